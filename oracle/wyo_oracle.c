@@ -1,0 +1,386 @@
+/*
+ * wyo_oracle.c -- plain fp64 CPU oracle (TEST INFRASTRUCTURE ONLY; see wyo_oracle.h).
+ *
+ * Every routine is the definition written out with plain loops: no blocking, fusion or
+ * reordering beyond what the cited passage states.  Sums run in ascending index order.
+ * Threads only split the list of independent units; they never change the arithmetic.
+ *
+ * Pages cited: [Inv] "TileLang 实战：单位下三角矩阵求逆"; [QLA] the FlashQLA announcement.
+ */
+#include "wyo_oracle.h"
+
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- input decoding ------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32; widening to double is exact. */
+static double decode_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load_elem(const void* base, int32_t dtype, int64_t idx)
+{
+    if (dtype == WYO_BF16) return decode_bf16(((const uint16_t*)base)[idx]);
+    return (double)((const float*)base)[idx];
+}
+
+/* ---- work map: chunks restart at each sequence start ([QLA] usage: cu_seqlens) ----------- */
+
+static int problem_ok(const wyo_problem* p, const int32_t* cu)
+{
+    if (!p) return 0;
+    if (p->batch < 0 || p->seqlen < 0 || p->num_qk_heads <= 0 || p->num_v_heads <= 0) return 0;
+    if (p->num_v_heads % p->num_qk_heads != 0) return 0;
+    if (p->head_dim_k <= 0 || p->head_dim_v <= 0 || p->chunk_size <= 0) return 0;
+    if (p->kv_dtype != WYO_BF16 && p->kv_dtype != WYO_F32) return 0;
+    if (cu) {
+        if (p->batch != 1 || p->num_seqs < 0) return 0;
+        if (cu[0] != 0 || cu[p->num_seqs] != p->seqlen) return 0;
+        for (int32_t s = 0; s < p->num_seqs; ++s)
+            if (cu[s + 1] < cu[s]) return 0;
+    }
+    return 1;
+}
+
+int64_t wyo_list_chunks(const wyo_problem* p, const int32_t* cu, int64_t* chunk_start,
+                        int32_t* chunk_len, int64_t cap)
+{
+    if (!problem_ok(p, cu)) return -1;
+    const int64_t C = p->chunk_size;
+    int64_t count = 0;
+    const int64_t nseq = cu ? p->num_seqs : p->batch;
+    for (int64_t s = 0; s < nseq; ++s) {
+        const int64_t s0 = cu ? cu[s] : s * (int64_t)p->seqlen;
+        const int64_t s1 = cu ? cu[s + 1] : (s + 1) * (int64_t)p->seqlen;
+        for (int64_t t0 = s0; t0 < s1; t0 += C) {
+            if (chunk_start) {
+                if (count >= cap) return -1;
+                chunk_start[count] = t0;
+                chunk_len[count] = (int32_t)((s1 - t0) < C ? (s1 - t0) : C);
+            }
+            ++count;
+        }
+    }
+    return count;
+}
+
+int64_t wyo_count_chunks(const wyo_problem* p, const int32_t* cu)
+{
+    return wyo_list_chunks(p, cu, NULL, NULL, 0);
+}
+
+/* ---- [Inv] section 2.1: X = L^{-1} row by row ------------------------------------------- */
+/* X[k,:] = e_k^T - sum_{j<k} L[k,j] X[j,:].  X[j,:] is zero right of column j, so the update
+ * of row k from row j touches columns 0..j only.  The product with X[j,j] = 1 (column i = j)
+ * is free; the counted ("necessary") products are those with i < j < k. */
+int64_t wyo_row_forward_inverse(int32_t n, const double* L, int32_t ldl, double* X, int32_t ldx)
+{
+    int64_t fma = 0;
+    for (int32_t k = 0; k < n; ++k) {
+        double* xk = X + (int64_t)k * ldx;
+        for (int32_t i = 0; i < n; ++i) xk[i] = (i == k) ? 1.0 : 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            const double lkj = L[(int64_t)k * ldl + j];
+            const double* xj = X + (int64_t)j * ldx;
+            for (int32_t i = 0; i <= j; ++i) {
+                xk[i] -= lkj * xj[i];
+                if (i < j) ++fma;
+            }
+        }
+    }
+    return fma;
+}
+
+/* ---- [Inv] section 2.2: the 2x2 block identity, applied recursively ----------------------
+ * L = [[L00, 0], [L10, L11]]  =>  L^{-1} = [[L00^{-1}, 0], [-L11^{-1} L10 L00^{-1}, L11^{-1}]].
+ * The two diagonal inverses are independent; the coupling is two dense products. */
+int64_t wyo_block_recursive_inverse(int32_t n, int32_t base, const double* L, int32_t ldl,
+                                    double* X, int32_t ldx, int32_t* depth)
+{
+    if (n <= base || n < 2) {
+        if (depth) *depth = n > 0 ? n - 1 : 0;
+        return wyo_row_forward_inverse(n, L, ldl, X, ldx);
+    }
+    const int32_t h = n / 2, m = n - h;
+    int32_t d0 = 0, d1 = 0;
+    int64_t fma = wyo_block_recursive_inverse(h, base, L, ldl, X, ldx, &d0);
+    fma += wyo_block_recursive_inverse(m, base, L + (int64_t)h * ldl + h, ldl,
+                                       X + (int64_t)h * ldx + h, ldx, &d1);
+    for (int32_t i = 0; i < h; ++i)
+        for (int32_t j = h; j < n; ++j) X[(int64_t)i * ldx + j] = 0.0;
+
+    /* tmp = L10 X00  (m x h) */
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)m * (size_t)h);
+    for (int32_t i = 0; i < m; ++i)
+        for (int32_t j = 0; j < h; ++j) {
+            double s = 0.0;
+            for (int32_t q = 0; q < h; ++q) {
+                s += L[(int64_t)(h + i) * ldl + q] * X[(int64_t)q * ldx + j];
+                ++fma;
+            }
+            tmp[(int64_t)i * h + j] = s;
+        }
+    /* X10 = -(X11 tmp)  (m x h) */
+    for (int32_t i = 0; i < m; ++i)
+        for (int32_t j = 0; j < h; ++j) {
+            double s = 0.0;
+            for (int32_t q = 0; q < m; ++q) {
+                s += X[(int64_t)(h + i) * ldx + (h + q)] * tmp[(int64_t)q * h + j];
+                ++fma;
+            }
+            X[(int64_t)(h + i) * ldx + j] = -s;
+        }
+    free(tmp);
+    if (depth) *depth = (d0 > d1 ? d0 : d1) + 2;
+    return fma;
+}
+
+/* ---- one unit: ([Inv] section 1 equations, section 3.2 for the diagonal rule) ------------ */
+
+typedef struct {
+    double* K;  /* n x dk */
+    double* V;  /* n x dv */
+    double* b;  /* n */
+    double* A;  /* n x n */
+    double* X;  /* n x n */
+} unit_scratch;
+
+static int scratch_alloc(unit_scratch* s, const wyo_problem* p)
+{
+    const size_t C = (size_t)p->chunk_size;
+    s->K = (double*)malloc(sizeof(double) * C * (size_t)p->head_dim_k);
+    s->V = (double*)malloc(sizeof(double) * C * (size_t)p->head_dim_v);
+    s->b = (double*)malloc(sizeof(double) * C);
+    s->A = (double*)malloc(sizeof(double) * C * C);
+    s->X = (double*)malloc(sizeof(double) * C * C);
+    return s->K && s->V && s->b && s->A && s->X;
+}
+
+static void scratch_free(unit_scratch* s)
+{
+    free(s->K); free(s->V); free(s->b); free(s->A); free(s->X);
+}
+
+/* Computes T (n x n, into s->X), and W, U (n x dk, n x dv) for the chunk [tok0, tok0 + n) of
+ * value head hv.  Returns the forward-substitution count. */
+static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                          int64_t tok0, int32_t n, int32_t hv, unit_scratch* s, double* W,
+                          double* U)
+{
+    const int32_t dk = p->head_dim_k, dv = p->head_dim_v;
+    const int32_t Hq = p->num_qk_heads, Hv = p->num_v_heads;
+    const int32_t hk = hv / (Hv / Hq);
+
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t tok = tok0 + i;
+        for (int32_t d = 0; d < dk; ++d)
+            s->K[(int64_t)i * dk + d] = load_elem(k, p->kv_dtype, (tok * Hq + hk) * dk + d);
+        if (v)
+            for (int32_t e = 0; e < dv; ++e)
+                s->V[(int64_t)i * dv + e] = load_elem(v, p->kv_dtype, (tok * Hv + hv) * dv + e);
+        s->b[i] = (double)beta[tok * Hv + hv];
+    }
+
+    /* A = I + strictLower(diag(beta) K K^T): beta scales row i; the diagonal is 1. */
+    for (int32_t i = 0; i < n; ++i)
+        for (int32_t j = 0; j < n; ++j) {
+            double a;
+            if (j < i) {
+                double g = 0.0;
+                for (int32_t d = 0; d < dk; ++d)
+                    g += s->K[(int64_t)i * dk + d] * s->K[(int64_t)j * dk + d];
+                a = s->b[i] * g;
+            } else {
+                a = (i == j) ? 1.0 : 0.0;
+            }
+            s->A[(int64_t)i * n + j] = a;
+        }
+
+    /* T = A^{-1} */
+    const int64_t fma = wyo_row_forward_inverse(n, s->A, n, s->X, n);
+
+    /* W = T diag(beta) K, U = T diag(beta) V  (full products over j = 0..n-1) */
+    if (W) {
+        for (int32_t i = 0; i < n; ++i) {
+            for (int32_t d = 0; d < dk; ++d) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < n; ++j)
+                    acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->K[(int64_t)j * dk + d];
+                W[(int64_t)i * dk + d] = acc;
+            }
+            for (int32_t e = 0; e < dv; ++e) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < n; ++j)
+                    acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->V[(int64_t)j * dv + e];
+                U[(int64_t)i * dv + e] = acc;
+            }
+        }
+    }
+    return fma;
+}
+
+/* ---- threading over independent units ------------------------------------------------- */
+
+typedef struct {
+    const wyo_problem* p;
+    const void* k;
+    const void* v;
+    const float* beta;
+    const int64_t* start;
+    const int32_t* len;
+    const int32_t* heads;  /* NULL: unit u = (chunk u / Hv, head u % Hv) */
+    int64_t num_units;
+    int compact;           /* 1: compact [M,C,*] outputs; 0: scatter into [B,T,Hv,*] */
+    double* T;
+    double* W;
+    double* U;
+    int32_t tid, nthreads;
+    int64_t fma;
+    int ok;
+} job;
+
+static void* job_run(void* arg)
+{
+    job* jb = (job*)arg;
+    const wyo_problem* p = jb->p;
+    const int32_t C = p->chunk_size, dk = p->head_dim_k, dv = p->head_dim_v;
+    const int32_t Hv = p->num_v_heads;
+    unit_scratch s;
+    double* W = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dk);
+    double* U = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dv);
+    jb->ok = scratch_alloc(&s, p) && W && U;
+    jb->fma = 0;
+    if (jb->ok) {
+        for (int64_t u = jb->tid; u < jb->num_units; u += jb->nthreads) {
+            const int64_t c = jb->heads ? u : u / Hv;
+            const int32_t hv = jb->heads ? jb->heads[u] : (int32_t)(u % Hv);
+            const int64_t tok0 = jb->start[c];
+            const int32_t n = jb->len[c];
+            const int want_wu = jb->W != NULL;
+            jb->fma += unit_solve(p, jb->k, want_wu ? jb->v : NULL, jb->beta, tok0, n, hv, &s,
+                                  want_wu ? W : NULL, want_wu ? U : NULL);
+            for (int32_t i = 0; i < n; ++i) {
+                double* trow;
+                double* wrow = NULL;
+                double* urow = NULL;
+                if (jb->compact) {
+                    trow = jb->T + (u * C + i) * (int64_t)C;
+                    if (want_wu) {
+                        wrow = jb->W + (u * C + i) * (int64_t)dk;
+                        urow = jb->U + (u * C + i) * (int64_t)dv;
+                    }
+                } else {
+                    const int64_t row = (tok0 + i) * Hv + hv;
+                    trow = jb->T + row * C;
+                    if (want_wu) {
+                        wrow = jb->W + row * dk;
+                        urow = jb->U + row * dv;
+                    }
+                }
+                for (int32_t j = 0; j < C; ++j) trow[j] = (j < n) ? s.X[(int64_t)i * n + j] : 0.0;
+                if (want_wu) {
+                    memcpy(wrow, W + (int64_t)i * dk, sizeof(double) * (size_t)dk);
+                    memcpy(urow, U + (int64_t)i * dv, sizeof(double) * (size_t)dv);
+                }
+            }
+        }
+    }
+    scratch_free(&s);
+    free(W);
+    free(U);
+    return NULL;
+}
+
+static int run_jobs(job* proto, int32_t nthreads)
+{
+    if (nthreads <= 0) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    job* jobs = (job*)calloc((size_t)nthreads, sizeof(job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return 0; }
+    for (int32_t t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].tid = t;
+        jobs[t].nthreads = nthreads;
+    }
+    int32_t started = 0;
+    for (int32_t t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, job_run, &jobs[t]) != 0) break;
+        started = t;
+    }
+    /* threads that failed to start: run their share here */
+    for (int32_t t = started + 1; t < nthreads; ++t) job_run(&jobs[t]);
+    job_run(&jobs[0]);
+    for (int32_t t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    int ok = 1;
+    proto->fma = 0;
+    for (int32_t t = 0; t < nthreads; ++t) {
+        ok = ok && jobs[t].ok;
+        proto->fma += jobs[t].fma;
+    }
+    free(jobs);
+    free(th);
+    return ok;
+}
+
+int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                       const int32_t* cu, double* T_out, double* W_out, double* U_out,
+                       int32_t nthreads, int64_t* fma_out)
+{
+    if (!problem_ok(p, cu) || !k || !beta || !T_out) return 1;
+    if ((W_out == NULL) != (U_out == NULL) || (W_out && !v)) return 1;
+    const int64_t nchunks = wyo_count_chunks(p, cu);
+    if (nchunks < 0) return 1;
+    int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nchunks + 1));
+    int32_t* len = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nchunks + 1));
+    if (!start || !len) { free(start); free(len); return 2; }
+    wyo_list_chunks(p, cu, start, len, nchunks);
+    job proto;
+    memset(&proto, 0, sizeof proto);
+    proto.p = p; proto.k = k; proto.v = v; proto.beta = beta;
+    proto.start = start; proto.len = len; proto.heads = NULL;
+    proto.num_units = nchunks * p->num_v_heads;
+    proto.compact = 0;
+    proto.T = T_out; proto.W = W_out; proto.U = U_out;
+    const int ok = run_jobs(&proto, nthreads);
+    if (fma_out) *fma_out = proto.fma;
+    free(start);
+    free(len);
+    return ok ? 0 : 2;
+}
+
+int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                  int64_t num_units, const int64_t* chunk_start, const int32_t* chunk_len,
+                  const int32_t* v_head, double* T_out, double* W_out, double* U_out,
+                  int32_t nthreads)
+{
+    if (!problem_ok(p, NULL) || !k || !beta || !T_out || num_units < 0) return 1;
+    if (!chunk_start || !chunk_len || !v_head) return 1;
+    if ((W_out == NULL) != (U_out == NULL) || (W_out && !v)) return 1;
+    const int64_t total_tokens = (int64_t)p->batch * p->seqlen;
+    for (int64_t u = 0; u < num_units; ++u)
+        if (chunk_len[u] < 1 || chunk_len[u] > p->chunk_size || v_head[u] < 0 ||
+            v_head[u] >= p->num_v_heads || chunk_start[u] < 0 ||
+            chunk_start[u] + chunk_len[u] > total_tokens)
+            return 1;
+    const int64_t C = p->chunk_size;
+    memset(T_out, 0, sizeof(double) * (size_t)(num_units * C * C));
+    if (W_out) {
+        memset(W_out, 0, sizeof(double) * (size_t)(num_units * C * p->head_dim_k));
+        memset(U_out, 0, sizeof(double) * (size_t)(num_units * C * p->head_dim_v));
+    }
+    job proto;
+    memset(&proto, 0, sizeof proto);
+    proto.p = p; proto.k = k; proto.v = v; proto.beta = beta;
+    proto.start = chunk_start; proto.len = chunk_len; proto.heads = v_head;
+    proto.num_units = num_units;
+    proto.compact = 1;
+    proto.T = T_out; proto.W = W_out; proto.U = U_out;
+    return run_jobs(&proto, nthreads) ? 0 : 2;
+}

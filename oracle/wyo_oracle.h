@@ -1,0 +1,98 @@
+/*
+ * wyo_oracle.h -- plain fp64 CPU oracle for the per-chunk WY/UT preparation of chunkwise
+ * (Gated) DeltaNet.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline load this library.  It shares no code, header, table or helper with the HIP path
+ * under chunkwise_gated_deltanet_amd/ and never includes a HIP header.
+ *
+ * Pages cited (by title and section):
+ *   [Inv]  "TileLang 实战：单位下三角矩阵求逆" (TileLang in practice: inverting a unit
+ *          lower-triangular matrix), sections 1, 2.1-2.4, 3.2, 4.
+ *   [QLA]  The FlashQLA announcement, section "使用方式" (usage): tensor shapes of k, v, beta
+ *          and the optional cu_seqlens.
+ *
+ * What it computes, for every chunk of C tokens of every sequence and every value head
+ * ([Inv] section 1, first equation and the W / U equations):
+ *     A = I + strictLower(diag(beta) K K^T)
+ *     T = A^{-1}                      (row-wise forward substitution, [Inv] section 2.1)
+ *     W = T diag(beta) K,  U = T diag(beta) V
+ * All arithmetic is IEEE double; inputs are decoded exactly from the caller's bf16 / fp32 data.
+ *
+ * Conventions (readings of the pages; each one is listed in the design notes):
+ *   - Token-major layouts as in [QLA] usage: k [B,T,Hq,dk], v [B,T,Hv,dv], beta [B,T,Hv].
+ *   - Value head h reads key head h / (Hv/Hq) (contiguous groups).
+ *   - With cu_seqlens (B must be 1) chunks restart at every sequence start; the last chunk of
+ *     a sequence may hold n < C tokens and is solved as an n x n system.
+ *   - T is returned as [B,T,Hv,C]: row t holds row (t - chunk start) of its chunk's T, with
+ *     chunk-relative columns; columns >= n of a short chunk are 0.
+ *   - W [B,T,Hv,dk], U [B,T,Hv,dv].
+ * All pointers are host pointers owned by the caller.
+ */
+#ifndef WYO_ORACLE_H
+#define WYO_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { WYO_BF16 = 0, WYO_F32 = 1 };
+
+typedef struct {
+    int32_t batch;        /* B (1 when cu_seqlens is given) */
+    int32_t seqlen;       /* T per batch row, or total packed tokens with cu_seqlens */
+    int32_t num_qk_heads; /* Hq */
+    int32_t num_v_heads;  /* Hv, a multiple of Hq */
+    int32_t head_dim_k;   /* dk */
+    int32_t head_dim_v;   /* dv */
+    int32_t chunk_size;   /* C */
+    int32_t num_seqs;     /* N, used only with cu_seqlens */
+    int32_t kv_dtype;     /* WYO_BF16 (k, v given as raw bf16 bit patterns) or WYO_F32 */
+} wyo_problem;
+
+/* Number of chunks (over all sequences); -1 on invalid arguments. */
+int64_t wyo_count_chunks(const wyo_problem* p, const int32_t* cu_seqlens);
+
+/* Writes the first-token index (flattened b*T + t) and the length of every chunk, in
+ * sequence order; returns the count, or -1 if it exceeds cap or the arguments are invalid. */
+int64_t wyo_list_chunks(const wyo_problem* p, const int32_t* cu_seqlens, int64_t* chunk_start,
+                        int32_t* chunk_len, int64_t cap);
+
+/* Row-wise forward substitution ([Inv] section 2.1): X = L^{-1} for the n x n unit lower
+ * triangular L (only the strict lower part of L is read; its diagonal is taken as 1).
+ * Returns the number of necessary multiply-adds: products L[k,j] * X[j,i] with i < j < k. */
+int64_t wyo_row_forward_inverse(int32_t n, const double* L, int32_t ldl, double* X,
+                                int32_t ldx);
+
+/* Independent second algorithm, used only to pin the 2x2 block identity ([Inv] section 2.2):
+ * X = L^{-1} by halving recursion down to blocks of at most `base` rows, each solved by
+ * wyo_row_forward_inverse, coupled by X10 = -X11 L10 X00 (two dense products).
+ * Returns the multiply-add count (dense products counted in full); *depth receives the
+ * dependency depth in steps: n-1 for a leaf, +2 per recursion level. */
+int64_t wyo_block_recursive_inverse(int32_t n, int32_t base, const double* L, int32_t ldl,
+                                    double* X, int32_t ldx, int32_t* depth);
+
+/* Whole-tensor oracle.  T_out [B,T,Hv,C], W_out [B,T,Hv,dk], U_out [B,T,Hv,dv] (fp64).
+ * v / W_out / U_out may be NULL together (T only).  nthreads <= 0 means 1.
+ * *fma_out (may be NULL) receives the summed forward-substitution count.
+ * Returns 0 on success, nonzero on invalid arguments. */
+int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                       const int32_t* cu_seqlens, double* T_out, double* W_out, double* U_out,
+                       int32_t nthreads, int64_t* fma_out);
+
+/* Selected units only: unit u is the chunk starting at flattened token chunk_start[u] with
+ * chunk_len[u] tokens, for value head v_head[u].  Outputs are compact and zero-padded:
+ * T_out [M,C,C], W_out [M,C,dk], U_out [M,C,dv] (W_out / U_out may be NULL with v).
+ * Returns 0 on success. */
+int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                  int64_t num_units, const int64_t* chunk_start, const int32_t* chunk_len,
+                  const int32_t* v_head, double* T_out, double* W_out, double* U_out,
+                  int32_t nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WYO_ORACLE_H */

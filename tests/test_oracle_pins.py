@@ -1,0 +1,409 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix (CPU only).
+
+Pages: "TileLang 实战：单位下三角矩阵求逆" (cited [Inv]) and the FlashQLA announcement.
+
+Each pin_* function raises AssertionError when the oracle library it is given is wrong.  The
+same pins run against deliberately broken copies of the oracle (test_mutants_are_caught), so a
+dropped term, a wrong sign or index, or a transposed operand anywhere in it fails at least one.
+"""
+import math
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+from chunkwise_gated_deltanet_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------------------------
+# helpers (test side: plain numpy statements of the definitions, used only as cross-checks)
+
+def unit_keys(rng, n, dk=128):
+    k = rng.standard_normal((n, dk)).astype(np.float32)
+    return (k / np.linalg.norm(k, axis=1, keepdims=True)).astype(np.float32)
+
+
+def one_unit(lib, K, V, beta, C=None):
+    """Runs the oracle on one chunk [0, n) of a single-head problem (fp32 inputs)."""
+    n = K.shape[0]
+    C = C or n
+    k = np.ascontiguousarray(K[None, :, None, :], np.float32)
+    v = np.ascontiguousarray(V[None, :, None, :], np.float32)
+    b = np.ascontiguousarray(beta[None, :, None], np.float32)
+    T, W, U = oracle.units(k, b, C, [0], [n], [0], v=v, lib=lib, nthreads=1)
+    return T[0, :n, :n], W[0, :n], U[0, :n]
+
+
+def a_matrix(K, beta):
+    """A = I + strictLower(diag(beta) K K^T) in fp64 ([Inv] section 1)."""
+    K = K.astype(np.float64)
+    G = K @ K.T
+    return np.eye(len(K)) + np.tril(beta.astype(np.float64)[:, None] * G, -1)
+
+
+def read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------------------------------------
+# pins
+
+def pin_closed_form_2(lib):
+    """C = 2: A = [[1,0],[b1 k1.k0, 1]] so T = [[1,0],[-b1 k1.k0, 1]] (2x2 inverse)."""
+    rng = np.random.default_rng(11)
+    K = unit_keys(rng, 2)
+    V = rng.standard_normal((2, 128)).astype(np.float32)
+    beta = np.array([0.3, 0.8], np.float32)
+    T, W, U = one_unit(lib, K, V, beta)
+    K64, V64, b = K.astype(np.float64), V.astype(np.float64), beta.astype(np.float64)
+    g = float(K64[1] @ K64[0])
+    assert T[0, 0] == 1 and T[1, 1] == 1 and T[0, 1] == 0
+    assert abs(T[1, 0] - (-b[1] * g)) <= 1e-15
+    W_exp = np.stack([b[0] * K64[0], -b[1] * g * b[0] * K64[0] + b[1] * K64[1]])
+    U_exp = np.stack([b[0] * V64[0], -b[1] * g * b[0] * V64[0] + b[1] * V64[1]])
+    assert np.max(np.abs(W - W_exp)) <= 1e-14
+    assert np.max(np.abs(U - U_exp)) <= 1e-14
+
+
+def pin_orthogonal(lib):
+    """Distinct one-hot keys: K K^T = I so A = I, T = I, W = diag(b) K, U = diag(b) V exactly."""
+    rng = np.random.default_rng(12)
+    n = 32
+    K = np.zeros((n, 128), np.float32)
+    K[np.arange(n), rng.permutation(128)[:n]] = 1.0
+    V = rng.standard_normal((n, 128)).astype(np.float32)
+    beta = rng.uniform(0.05, 0.95, n).astype(np.float32)
+    T, W, U = one_unit(lib, K, V, beta)
+    b = beta.astype(np.float64)[:, None]
+    assert np.array_equal(T, np.eye(n))
+    assert np.array_equal(W, b * K.astype(np.float64))
+    assert np.array_equal(U, b * V.astype(np.float64))
+
+
+def pin_residual_structure(lib):
+    """T A = A T = I to 1e-12; unit diagonal and zero strict upper triangle exactly."""
+    rng = np.random.default_rng(13)
+    for n in (32, 64, 128):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = (1 / (1 + np.exp(-rng.standard_normal(n)))).astype(np.float32)
+        T, _, _ = one_unit(lib, K, V, beta)
+        A = a_matrix(K, beta)
+        assert np.max(np.abs(T @ A - np.eye(n))) <= 1e-12
+        assert np.max(np.abs(A @ T - np.eye(n))) <= 1e-12
+        assert np.all(np.diag(T) == 1.0)
+        assert np.all(np.triu(T, 1) == 0.0)
+
+
+def pin_lapack_inverse(lib):
+    """Brute force: LAPACK's dense inverse of A (np.linalg.inv) within 1e-12."""
+    rng = np.random.default_rng(14)
+    for n in (2, 5, 16, 17, 32, 64, 128):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        T, _, _ = one_unit(lib, K, V, beta)
+        assert np.max(np.abs(T - np.linalg.inv(a_matrix(K, beta)))) <= 1e-12
+
+
+def pin_block_identity(lib):
+    """[Inv] section 2.2: lower-left of L^{-1} is -L11^{-1} L10 L00^{-1}; the recursive and the
+    row-wise inverses agree; block residual L10 X00 + L11 X10 = 0."""
+    rng = np.random.default_rng(15)
+    for n in (32, 64, 128):
+        K = unit_keys(rng, n)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        A = a_matrix(K, beta)
+        X, _ = oracle.row_forward_inverse(A, lib=lib)
+        Xr, _, _ = oracle.block_recursive_inverse(A, 16, lib=lib)
+        assert np.max(np.abs(X - Xr)) <= 1e-12
+        h = n // 2
+        X00, X11, X10 = X[:h, :h], X[h:, h:], X[h:, :h]
+        L10, L11 = A[h:, :h], A[h:, h:]
+        assert np.max(np.abs(X10 - (-X11 @ L10 @ X00))) <= 1e-12
+        assert np.max(np.abs(L10 @ X00 + L11 @ X10)) <= 1e-12
+        assert np.all(X[:h, h:] == 0)
+
+
+def pin_beta_zero(lib):
+    """[Inv] section 4, degenerate check 1: beta -> 0 gives T = I (and W = U = 0)."""
+    rng = np.random.default_rng(16)
+    for n in (32, 64, 128):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        T, W, U = one_unit(lib, K, V, np.zeros(n, np.float32))
+        assert np.array_equal(T, np.eye(n))
+        assert np.all(W == 0) and np.all(U == 0)
+
+
+def subdiag_keys(n, half):
+    """Keys making A's two diagonal half-blocks the identity while the lower-left block is not:
+    rows i < half are e_i; rows half + i are c (e_i + e_{half+i}) with c = 1/sqrt(2) in fp32."""
+    c = np.float32(1 / math.sqrt(2))
+    K = np.zeros((n, 128), np.float32)
+    for i in range(half):
+        K[i, i] = 1
+        K[half + i, i] = c
+        K[half + i, half + i] = c
+    return K
+
+
+def pin_subdiag_only(lib):
+    """[Inv] section 4, degenerate check 2: with L00 = L11 = I the lower-left of T is exactly
+    -L10 (checks the sign of the coupling on its own)."""
+    rng = np.random.default_rng(17)
+    for n in (32, 64, 128):
+        h = n // 2
+        K = subdiag_keys(n, h)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.05, 0.95, n).astype(np.float32)
+        T, _, _ = one_unit(lib, K, V, beta)
+        A = a_matrix(K, beta)
+        assert np.array_equal(A[:h, :h], np.eye(h)) and np.array_equal(A[h:, h:], np.eye(h))
+        assert np.any(A[h:, :h] != 0)
+        assert np.array_equal(T[h:, :h], -A[h:, :h])
+        assert np.array_equal(T[:h, :h], np.eye(h)) and np.array_equal(T[h:, h:], np.eye(h))
+
+
+def pin_identical_keys(lib):
+    """All keys equal (k.k = s): A[i,j] = s b_i for i > j, and
+    T[i,j] = -s b_i prod_{m=j+1}^{i-1} (1 - s b_m)  (derived from [Inv] section 1 by
+    eliminating row i with row i-1)."""
+    rng = np.random.default_rng(18)
+    for n in (32, 64):
+        k = unit_keys(rng, 1)[0]
+        K = np.repeat(k[None, :], n, axis=0)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        T, _, _ = one_unit(lib, K, V, beta)
+        s = float(k.astype(np.float64) @ k.astype(np.float64))
+        b = beta.astype(np.float64)
+        E = np.eye(n)
+        for i in range(n):
+            for j in range(i):
+                E[i, j] = -s * b[i] * np.prod(1 - s * b[j + 1:i])
+        assert np.max(np.abs(T - E)) <= 1e-13
+
+
+def pin_fma_counts(lib):
+    """Necessary multiply-adds and depths printed in [Inv] sections 2.2-2.4."""
+    rng = np.random.default_rng(19)
+    for n in range(1, 131):
+        L = np.tril(rng.uniform(-0.3, 0.3, (n, n)), -1) + np.eye(n)
+        _, fma = oracle.row_forward_inverse(L, lib=lib)
+        assert fma == n * (n - 1) * (n - 2) // 6, n
+    for C, row_fma, rec_fma, rec_depth, row_depth, per_tok in read_table("fma_counts.txt"):
+        C = int(C)
+        L = np.tril(rng.uniform(-0.3, 0.3, (C, C)), -1) + np.eye(C)
+        _, fma = oracle.row_forward_inverse(L, lib=lib)
+        if row_fma != "-":
+            assert fma == int(row_fma)
+        _, rfma, depth = oracle.block_recursive_inverse(L, 16, lib=lib)
+        assert rfma == int(rec_fma) and depth == int(rec_depth)
+        assert C - 1 == int(row_depth)
+        assert round(rfma / C) == int(per_tok)
+    # the whole-tensor oracle reports the sum of C(n,3) over its units
+    inp = synth.custom(1, 0, 1, 2, 32, dtype="f32", seed=3, seqlens=[40, 17, 64])
+    _, _, _, fma = oracle.wy_prepare(inp["k"], inp["beta"], 32, v=inp["v"],
+                                     cu_seqlens=inp["cu_seqlens"], lib=lib, nthreads=2)
+    expect = 2 * sum(n * (n - 1) * (n - 2) // 6 for n in (32, 8, 17, 32, 32))
+    assert fma == expect
+
+
+def pin_householder_product(lib):
+    """W pins: prod_{t=1..n} (I - b_t k_t k_t^T), t = 1 leftmost, equals I - W^T K -- the
+    product of the chunk's Householder-like transforms that the UT transform arranges into the
+    triangular system ([Inv] section 1)."""
+    rng = np.random.default_rng(20)
+    for n in (32, 37, 64, 128):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        _, W, _ = one_unit(lib, K, V, beta)
+        K64 = K.astype(np.float64)
+        P = np.eye(128)
+        for t in range(n):
+            P = P @ (np.eye(128) - float(beta[t]) * np.outer(K64[t], K64[t]))
+        assert np.max(np.abs(P - (np.eye(128) - W.T @ K64))) <= 1e-12
+
+
+def pin_delta_rule(lib):
+    """U pins: the delta rule S_t = S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T from S_0 = 0 ends
+    at S_n = U^T K (the chunk's contribution that U carries)."""
+    rng = np.random.default_rng(21)
+    for n in (32, 45, 64):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        _, _, U = one_unit(lib, K, V, beta)
+        K64, V64 = K.astype(np.float64), V.astype(np.float64)
+        S = np.zeros((128, 128))
+        for t in range(n):
+            b = float(beta[t])
+            S = S @ (np.eye(128) - b * np.outer(K64[t], K64[t])) + b * np.outer(V64[t], K64[t])
+        assert np.max(np.abs(S - U.T @ K64)) <= 1e-12
+
+
+def pin_tail_padding(lib):
+    """A short chunk (n < C) equals the top-left of the zero-padded chunk with beta = 0 on the
+    padding: A = blockdiag(A_n, I) gives T = blockdiag(T_n, I)."""
+    rng = np.random.default_rng(22)
+    n, C = 37, 64
+    K = unit_keys(rng, C)
+    V = rng.standard_normal((C, 128)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, C).astype(np.float32)
+    K[n:] = 0
+    beta[n:] = 0
+    Tn, Wn, Un = one_unit(lib, K[:n], V[:n], beta[:n], C=C)
+    Tp, Wp, Up = one_unit(lib, K, V, beta)
+    assert np.array_equal(Tp[:n, :n], Tn)
+    assert np.array_equal(Tp[n:, n:], np.eye(C - n)) and np.all(Tp[n:, :n] == 0)
+    assert np.array_equal(Wp[:n], Wn) and np.array_equal(Up[:n], Un)
+
+
+def pin_layout(lib):
+    """Whole-tensor scatter: row t of T_out / W_out / U_out holds row (t - chunk start) of its
+    chunk's T / W / U, with chunk-relative columns; packed chunks restart at sequence starts."""
+    inp = synth.custom(1, 0, 2, 4, 32, dtype="bf16", seed=4, seqlens=[70, 5, 33])
+    k, v, beta, cu = inp["k"], inp["v"], inp["beta"], inp["cu_seqlens"]
+    T, W, U, _ = oracle.wy_prepare(k, beta, 32, v=v, cu_seqlens=cu, lib=lib, nthreads=3)
+    starts, lens = oracle.list_chunks(1, int(cu[-1]), 32, cu, lib=lib)
+    assert list(starts) == [0, 32, 64, 70, 75, 107] and list(lens) == [32, 32, 6, 5, 32, 1]
+    for c in range(len(starts)):
+        for h in range(4):
+            Tu, Wu, Uu = oracle.units(k, beta, 32, [starts[c]], [lens[c]], [h], v=v, lib=lib)
+            rows = slice(starts[c], starts[c] + lens[c])
+            assert np.array_equal(T[0, rows, h], Tu[0, :lens[c]])
+            assert np.array_equal(W[0, rows, h], Wu[0, :lens[c]])
+            assert np.array_equal(U[0, rows, h], Uu[0, :lens[c]])
+            assert np.all(T[0, rows, h, lens[c]:] == 0)
+
+
+def pin_head_grouping(lib):
+    """Value head h reads key head h // (Hv/Hq) (contiguous groups; the pages fix only the
+    shapes, so this is a stated convention)."""
+    inp = synth.custom(1, 64, 2, 4, 64, dtype="f32", seed=5)
+    k, v, beta = inp["k"], inp["v"], inp["beta"]
+    # value head 2 of 4 with 2 key heads reads key head 1 (2 // 2), not key head 0 (2 % 2)
+    T, W, U = oracle.units(k, beta, 64, [0], [64], [2], v=v, lib=lib)
+    k1 = np.ascontiguousarray(k[:, :, 1:2])
+    T1, W1, U1 = oracle.units(k1, np.ascontiguousarray(beta[:, :, 2:3]), 64, [0], [64], [0],
+                              v=np.ascontiguousarray(v[:, :, 2:3]), lib=lib)
+    assert np.array_equal(T, T1) and np.array_equal(W, W1) and np.array_equal(U, U1)
+
+
+PINS = [pin_closed_form_2, pin_orthogonal, pin_residual_structure, pin_lapack_inverse,
+        pin_block_identity, pin_beta_zero, pin_subdiag_only, pin_identical_keys,
+        pin_fma_counts, pin_householder_product, pin_delta_rule, pin_tail_padding, pin_layout,
+        pin_head_grouping]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+# ---------------------------------------------------------------------------------------------
+# magnitudes and the generator's conditioning (pages' measured numbers)
+
+def test_error_magnitudes(oracle_lib):
+    """[Inv] section 4 results table: real A errors against np.linalg.inv are ~1e-16, and an
+    fp16-stored T carries ~5.7e-5 relative error."""
+    table = {r[0]: float(r[1]) for r in read_table("error_magnitudes.txt")}
+    rng = np.random.default_rng(23)
+    worst, rel16 = 0.0, []
+    for _ in range(200):
+        K = unit_keys(rng, 32)
+        beta = (1 / (1 + np.exp(-rng.standard_normal(32)))).astype(np.float32)
+        A = a_matrix(K, beta)
+        T, _ = oracle.row_forward_inverse(A, lib=oracle_lib)
+        worst = max(worst, float(np.max(np.abs(T - np.linalg.inv(A)))))
+        T16 = T.astype(np.float16).astype(np.float64)
+        rel16.append(np.linalg.norm(T16 - T) / np.linalg.norm(T))
+    assert worst <= 100 * table["real_A_200_samples"]
+    assert table["fp16_stored_T_relative"] / 10 <= max(rel16) <= table["fp16_stored_T_relative"] * 10
+    # the general 16x16 / 32x32 cases of the table stay within 10x of their printed values
+    Lg = np.tril(rng.uniform(-1, 1, (16, 16)), -1) + np.eye(16)
+    X, _ = oracle.row_forward_inverse(Lg, lib=oracle_lib)
+    assert np.max(np.abs(X - np.linalg.inv(Lg))) <= 10 * table["row_wise_16x16"]
+    Lg = np.tril(rng.uniform(-1, 1, (32, 32)), -1) + np.eye(32)
+    X, _, _ = oracle.block_recursive_inverse(Lg, 16, lib=oracle_lib)
+    assert np.max(np.abs(X - np.linalg.inv(Lg))) <= 10 * table["recursive_32x32"]
+
+
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_generator_conditioning(C):
+    """[Inv] section 2.4 cost table: measured cond(A) upper bounds 2.0 / 2.6 / 3.6 for C = 32 /
+    64 / 128 and strict-lower entries within 0.358 ([Inv] section 4), on the workloads' input
+    distribution (L2-normalised bf16 keys, beta = sigmoid(N(0, 1)))."""
+    bound = {int(r[0]): (float(r[1]), float(r[2])) for r in read_table("conditioning.txt")}[C]
+    inp = synth.custom(1, 200 * C, 1, 1, C, dtype="bf16", seed=100 + C)
+    K = synth.bf16_bits_to_f32(inp["k"])[0, :, 0].astype(np.float64)
+    b = inp["beta"][0, :, 0].astype(np.float64)
+    cmax, lmax = 0.0, 0.0
+    for c in range(200):
+        A = a_matrix(K[c * C:(c + 1) * C], b[c * C:(c + 1) * C])
+        cmax = max(cmax, float(np.linalg.cond(A)))
+        lmax = max(lmax, float(np.max(np.abs(np.tril(A, -1)))))
+    assert cmax <= bound[0]
+    assert lmax <= bound[1]
+
+
+# ---------------------------------------------------------------------------------------------
+# planted mistakes: each mutant copy of the oracle must fail at least one pin
+
+MUTANTS = {
+    "beta_dropped": ("a = s->b[i] * g;", "a = g;"),
+    "beta_on_columns": ("a = s->b[i] * g;", "a = s->b[j] * g;"),
+    "gram_term_dropped": ("for (int32_t d = 0; d < dk; ++d)\n                    g +=",
+                          "for (int32_t d = 1; d < dk; ++d)\n                    g +="),
+    "gram_wrong_index": ("* s->K[(int64_t)j * dk + d];\n                a = ",
+                         "* s->K[(int64_t)i * dk + d];\n                a = "),
+    "substitution_sign": ("xk[i] -= lkj * xj[i];", "xk[i] += lkj * xj[i];"),
+    "substitution_unit_term_dropped": ("for (int32_t i = 0; i <= j; ++i) {",
+                                       "for (int32_t i = 0; i < j; ++i) {"),
+    "substitution_transposed": ("const double lkj = L[(int64_t)k * ldl + j];",
+                                "const double lkj = L[(int64_t)j * ldl + k];"),
+    "wu_t_transposed": ("acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->K",
+                        "acc += (s->X[(int64_t)j * n + i] * s->b[j]) * s->K"),
+    "wu_beta_index": ("acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->V",
+                      "acc += (s->X[(int64_t)i * n + j] * s->b[i]) * s->V"),
+    "u_uses_keys": ("* s->V[(int64_t)j * dv + e];", "* s->K[(int64_t)j * dk + e];"),
+    "head_map_modulo": ("const int32_t hk = hv / (Hv / Hq);", "const int32_t hk = hv % Hq;"),
+    "coupling_sign": ("X[(int64_t)(h + i) * ldx + j] = -s;", "X[(int64_t)(h + i) * ldx + j] = s;"),
+    "tail_columns_leak": ("trow[j] = (j < n) ? s.X[(int64_t)i * n + j] : 0.0;",
+                          "trow[j] = (j < n) ? s.X[(int64_t)i * n + j] : 1.0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants_are_caught(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCES[0]).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mutated = src.replace(old, new)
+    path = tmp_path / "wyo_oracle.c"
+    path.write_text(mutated)
+    shutil.copy(os.path.join(os.path.dirname(oracle.SOURCES[0]), "wyo_oracle.h"), tmp_path)
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(lib_path, sources=[str(path)], extra_flags=("-w",))
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
