@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-chunk WY/UT preparation (kkt_solve + W/U) on one MI355X.
+
+One step = one wy_prepare launch over the whole workload: every (chunk, value head) unit of
+B=1, T=8192, Hq=Hv=16, d=128, C=64, bf16 k/v (fp32 beta, T out fp32, W/U out bf16).  Inputs
+are seeded synthetic data, resident in HBM before the timed region.  Several copies of the
+input/output buffers are rotated so that consecutive steps do not hit the 256 MB Infinity
+Cache with the previous step's data.
+
+Prints one JSON line.  value = units (chunk x value head) per second.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunks/s (tokens/s) for kkt_solve+W/U at C=64; achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 768 << 20  # rotated footprint: three times the Infinity Cache
+KERNEL_SOURCE = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc", "wyprep_kernels.hip")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "wy_prepare_bf16_c64_b1t8192h16_counters.md")
+
+
+def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz):
+    """K read once per key head, V and beta read once, T (fp32), W and U written once."""
+    per_token = hq * dk * esz + hv * (dv * esz + 4 + 4 * C + dk * esz + dv * esz)
+    return tokens * per_token
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    if not os.path.exists(COUNTER_SUMMARY):
+        return None
+    text = open(COUNTER_SUMMARY).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m_b or not m_h or m_h.group(1) != kernel_source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
+    """The fp64 oracle, as it stands, on the same workload: whole passes until ~`seconds`."""
+    import oracle
+    threads = cpu_threads()
+    lib = oracle.load()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.wy_prepare(inp["k"], inp["beta"], inp["chunk_size"], v=inp["v"],
+                          cu_seqlens=inp["cu_seqlens"], nthreads=threads, lib=lib)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": units_per_pass * passes / el, "unit": "chunks/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload ({units_per_pass} units, {tokens_per_pass} tokens) x "
+                      f"{passes} passes, {el:.1f} s wall, fp64",
+            "tokens_per_s": tokens_per_pass * passes / el}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="seeded workload index (2 = the headline C=64 workload)")
+    ap.add_argument("--chunk-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the step has no cross-GPU exchange, and this "
+              "build measures a single GPU's share (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    from chunkwise_gated_deltanet_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    lib = cg.load_library()
+
+    w = synth.workload(args.workload, chunk_size=args.chunk_size)
+    inp = synth.generate(w)
+    B, T = inp["batch"], inp["seqlen"]
+    Hq, Hv, C = w.num_qk_heads, w.num_v_heads, w.chunk_size
+    dk = dv = 128
+    esz = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if inp["cu_seqlens"] is not None:
+        lens = np.diff(inp["cu_seqlens"].astype(np.int64))
+        nchunks = int(np.sum((lens + C - 1) // C))
+    else:
+        nchunks = B * ((T + C - 1) // C)
+    units = nchunks * Hv
+    tokens = B * T
+    alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz)
+    nsets = max(1, math.ceil(ROTATE_BYTES / alg))  # every byte of a step is touched once
+
+    def dev_tensor(a, dt):
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        return (t.view(torch.bfloat16) if dt == torch.bfloat16 else t).to(dev)
+
+    k0 = dev_tensor(inp["k"], tdt)
+    v0 = dev_tensor(inp["v"], tdt)
+    b0 = torch.from_numpy(inp["beta"]).to(dev)
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(k=k0.clone(), v=v0.clone(), beta=b0.clone(),
+                         T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev),
+                         W=torch.empty(B, T, Hv, dk, dtype=tdt, device=dev),
+                         U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev)))
+    prob = cg.Problem(B, T, Hq, Hv, dk, dv, C, 0 if cu is None else cu.numel() - 1,
+                      0 if w.dtype == "bf16" else 1)
+    import ctypes
+    pprob = ctypes.byref(prob)
+    cu_ptr = None if cu is None else cu.data_ptr()
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(s["k"].data_ptr(), s["v"].data_ptr(), s["beta"].data_ptr(), s["T"].data_ptr(),
+              s["W"].data_ptr(), s["U"].data_ptr()) for s in sets]
+
+    def step(i):
+        kp, vp, bp, tp, wp, up = calls[i % nsets]
+        st = lib.wyp_wy_prepare(pprob, kp, vp, bp, cu_ptr, tp, wp, up, sptr)
+        if st != 0:
+            raise RuntimeError(lib.wyp_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+
+    # Timed region: exactly `steps` steps; events around each launch on the launch stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # seconds per launch
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg = float(np.mean(durs))
+
+    achieved = alg / kern_avg / 1e9
+    traffic = counter_traffic()
+    out = {
+        "metric": METRIC,
+        "value": units / (ms_per_step * 1e-3),
+        "unit": "chunks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seqlen": T, "num_qk_heads": Hq,
+                   "num_v_heads": Hv, "head_dim": dk, "chunk_size": C,
+                   "units_per_step": units, "tokens_per_step": tokens,
+                   "rotated_buffer_sets": nsets},
+        "tokens_per_s": tokens / (ms_per_step * 1e-3),
+        "kernel_us": {"mean": kern_avg * 1e6, "p10": float(np.percentile(durs, 10)) * 1e6,
+                      "p50": float(np.median(durs)) * 1e6,
+                      "p90": float(np.percentile(durs, 90)) * 1e6},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes": alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+"""MI355X (gfx950) per-chunk WY/UT preparation of chunkwise (Gated) DeltaNet.
+
+Thin Python binding over the C ABI in ``include/wyprep.h`` (libwyprep.so, built in-tree by
+``chunkwise_gated_deltanet_amd.build``).  This module only checks and marshals arguments:
+every step of the computation runs in the library's HIP kernels.  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if the library is missing the calls
+raise.
+
+Page cited: "TileLang 实战：单位下三角矩阵求逆" (TileLang in practice: inverting a unit
+lower-triangular matrix), section 1 -- for every chunk of C tokens and value head:
+A = I + strictLower(diag(beta) K K^T), T = A^{-1}, W = T diag(beta) K, U = T diag(beta) V.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["wy_prepare", "kkt_solve", "wyp_wy_prepare", "wyp_kkt_solve", "load_library",
+           "Problem", "LIB_PATH", "WyprepError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.so")
+
+WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
+WYP_BF16, WYP_F32 = 0, 1
+
+
+class WyprepError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_STATUS = {0: "WYP_OK", 1: "WYP_ERR_INVALID_ARGUMENT", 2: "WYP_ERR_UNSUPPORTED", 3: "WYP_ERR_HIP"}
+
+
+class Problem(ctypes.Structure):
+    """Mirror of wyp_problem."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seqlen", "num_qk_heads", "num_v_heads", "head_dim_k", "head_dim_v",
+        "chunk_size", "num_seqs", "kv_dtype")]
+
+
+_P = ctypes.c_void_p
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Loads libwyprep.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with chunkwise_gated_deltanet_amd.build "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(p)
+    lib.wyp_abi_version.restype = ctypes.c_int32
+    lib.wyp_abi_version.argtypes = []
+    lib.wyp_status_string.restype = ctypes.c_char_p
+    lib.wyp_status_string.argtypes = [ctypes.c_int32]
+    lib.wyp_last_error.restype = ctypes.c_char_p
+    lib.wyp_last_error.argtypes = []
+    lib.wyp_kkt_solve.restype = ctypes.c_int32
+    lib.wyp_kkt_solve.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P]
+    lib.wyp_wy_prepare.restype = ctypes.c_int32
+    lib.wyp_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != WYP_OK:
+        detail = lib.wyp_last_error().decode(errors="replace")
+        if status in (WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED):
+            raise ValueError(f"{_STATUS[status]}: {detail}")
+        raise WyprepError(status, detail)
+
+
+def _kv_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return WYP_BF16
+    if t.dtype == torch.float32:
+        return WYP_F32
+    raise TypeError(f"k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _require(t, name, ndim, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _problem(k, beta, chunk_size, cu_seqlens, v=None):
+    import torch
+    device = k.device
+    _require(k, "k", 4, device)
+    _require(beta, "beta", 3, device)
+    if beta.dtype != torch.float32:
+        raise TypeError("beta must be float32")
+    B, T, Hq, dk = k.shape
+    if beta.shape[:2] != (B, T):
+        raise ValueError(f"beta shape {tuple(beta.shape)} does not match k {tuple(k.shape)}")
+    Hv = beta.shape[2]
+    dv = dk
+    if v is not None:
+        _require(v, "v", 4, device)
+        if v.dtype != k.dtype:
+            raise TypeError("k and v must share a dtype")
+        if v.shape[:3] != (B, T, Hv):
+            raise ValueError(f"v shape {tuple(v.shape)} does not match beta {tuple(beta.shape)}")
+        dv = v.shape[3]
+    n = 0
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", 1, device)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        n = cu_seqlens.numel() - 1
+    return Problem(B, T, Hq, Hv, dk, dv, int(chunk_size), n, _kv_dtype(k))
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _out(t, shape, dtype, device, name):
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _require(t, name, len(shape), device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}")
+    return t
+
+
+def kkt_solve(k, beta, chunk_size, cu_seqlens=None, T_out=None):
+    """T [B,T,Hv,C] (float32) from k [B,T,Hq,128] and beta [B,T,Hv]; see wyp_kkt_solve."""
+    import torch
+    lib = load_library()
+    p = _problem(k, beta, chunk_size, cu_seqlens)
+    B, T = k.shape[:2]
+    T_out = _out(T_out, (B, T, p.num_v_heads, p.chunk_size), torch.float32, k.device, "T_out")
+    st = lib.wyp_kkt_solve(ctypes.byref(p), k.data_ptr(), beta.data_ptr(),
+                           cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                           T_out.data_ptr(), _stream(k.device))
+    _check(lib, st)
+    return T_out
+
+
+def wy_prepare(k, v, beta, chunk_size, cu_seqlens=None, T_out=None, W_out=None, U_out=None):
+    """(T, W, U): T [B,T,Hv,C] float32, W [B,T,Hv,128] and U [B,T,Hv,128] in k's dtype."""
+    import torch
+    lib = load_library()
+    p = _problem(k, beta, chunk_size, cu_seqlens, v=v)
+    B, T = k.shape[:2]
+    Hv = p.num_v_heads
+    T_out = _out(T_out, (B, T, Hv, p.chunk_size), torch.float32, k.device, "T_out")
+    W_out = _out(W_out, (B, T, Hv, p.head_dim_k), k.dtype, k.device, "W_out")
+    U_out = _out(U_out, (B, T, Hv, p.head_dim_v), k.dtype, k.device, "U_out")
+    st = lib.wyp_wy_prepare(ctypes.byref(p), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                            cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                            T_out.data_ptr(), W_out.data_ptr(), U_out.data_ptr(),
+                            _stream(k.device))
+    _check(lib, st)
+    return T_out, W_out, U_out
+
+
+# The C-ABI names, for callers that mirror the header.
+wyp_kkt_solve = kkt_solve
+wyp_wy_prepare = wy_prepare

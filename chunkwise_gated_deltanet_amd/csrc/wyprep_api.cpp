@@ -1,0 +1,147 @@
+// C-ABI front end of libwyprep: argument validation (before any HIP call), status codes and
+// the per-thread error text.  The arithmetic lives in wyprep_kernels.hip.
+#include "wyprep.h"
+#include "wyprep_launch.h"
+
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+wyp_status fail(wyp_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Host-side checks shared by both entry points.  Touches no HIP API.
+wyp_status validate(const wyp_problem* p, const void* k, const void* v, const float* beta,
+                    const int32_t* cu, const float* T, const void* W, const void* U,
+                    bool want_wu, wyp::LaunchArgs* out, bool* empty)
+{
+    *empty = false;
+    if (!p) return fail(WYP_ERR_INVALID_ARGUMENT, "problem is NULL");
+    if (p->batch < 1) return fail(WYP_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
+    if (p->seqlen < 0) return fail(WYP_ERR_INVALID_ARGUMENT, "seqlen must be >= 0 (got %d)", p->seqlen);
+    if (p->num_qk_heads < 1 || p->num_v_heads < 1)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hv=%d)",
+                    p->num_qk_heads, p->num_v_heads);
+    if (p->num_v_heads % p->num_qk_heads != 0)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "Hv (%d) must be a multiple of Hq (%d)",
+                    p->num_v_heads, p->num_qk_heads);
+    if (p->kv_dtype != WYP_BF16 && p->kv_dtype != WYP_F32)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "kv_dtype %d is not a wyp_dtype", p->kv_dtype);
+    if (p->head_dim_k != 128 || (want_wu && p->head_dim_v != 128))
+        return fail(WYP_ERR_UNSUPPORTED, "only head_dim_k = head_dim_v = 128 is built (got %d, %d)",
+                    p->head_dim_k, p->head_dim_v);
+    if (p->chunk_size != 32 && p->chunk_size != 64 && p->chunk_size != 128)
+        return fail(WYP_ERR_UNSUPPORTED, "chunk_size must be 32, 64 or 128 (got %d)",
+                    p->chunk_size);
+    if (want_wu && p->kv_dtype == WYP_F32 && p->chunk_size == 128)
+        return fail(WYP_ERR_UNSUPPORTED, "fp32 k/v with C = 128 is built for kkt_solve only");
+    if (cu) {
+        if (p->batch != 1)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)", p->batch);
+        if (p->num_seqs < 0)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", p->num_seqs);
+        if (p->num_seqs == 0 && p->seqlen != 0)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "num_seqs == 0 with %d tokens", p->seqlen);
+        if (!aligned(cu, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    }
+    const int64_t C = p->chunk_size;
+    const int64_t tokens = static_cast<int64_t>(p->batch) * p->seqlen;
+    if (tokens == 0) {  // nothing to read or write; pointers of empty tensors may be NULL
+        *empty = true;
+        return WYP_OK;
+    }
+    if (!k || !beta || !T) return fail(WYP_ERR_INVALID_ARGUMENT, "k, beta and T_out must be non-NULL");
+    if (want_wu && (!v || !W || !U))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "v, W_out and U_out must be non-NULL");
+    if (!aligned(k, 16) || !aligned(T, 16) || (want_wu && (!aligned(v, 16) || !aligned(W, 16) ||
+                                                           !aligned(U, 16))))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "k, v, T_out, W_out and U_out must be 16-byte aligned");
+    if (!aligned(beta, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "beta is not 4-byte aligned");
+
+    int64_t slots;
+    if (cu) slots = (p->seqlen + C - 1) / C + p->num_seqs - 1;  // >= sum of per-sequence chunks
+    else slots = static_cast<int64_t>(p->batch) * ((p->seqlen + C - 1) / C);
+    // the launch grid is slots x (Hv or Hq) workgroups, rounded up to a multiple of 8
+    const int64_t units = slots * p->num_v_heads;
+    if (units + 8 > INT32_MAX)
+        return fail(WYP_ERR_UNSUPPORTED, "problem has %lld units, more than one launch holds",
+                    static_cast<long long>(units));
+
+    out->k = k;
+    out->v = want_wu ? v : nullptr;
+    out->beta = beta;
+    out->cu_seqlens = cu;
+    out->T = const_cast<float*>(T);
+    out->W = want_wu ? const_cast<void*>(W) : nullptr;
+    out->U = want_wu ? const_cast<void*>(U) : nullptr;
+    out->batch = p->batch;
+    out->seqlen = p->seqlen;
+    out->num_qk_heads = p->num_qk_heads;
+    out->num_v_heads = p->num_v_heads;
+    out->num_seqs = cu ? p->num_seqs : p->batch;
+    out->chunk_size = p->chunk_size;
+    out->kv_dtype = p->kv_dtype;
+    out->chunk_slots = slots;
+    return WYP_OK;
+}
+
+wyp_status run(const wyp_problem* p, const void* k, const void* v, const float* beta,
+               const int32_t* cu, float* T, void* W, void* U, bool want_wu, void* stream)
+{
+    g_last_error[0] = '\0';
+    wyp::LaunchArgs args{};
+    bool empty = false;
+    const wyp_status st = validate(p, k, v, beta, cu, T, W, U, want_wu, &args, &empty);
+    if (st != WYP_OK || empty) return st;
+    char msg[256] = "";
+    if (wyp::launch(args, stream, msg, sizeof msg) != 0)
+        return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
+    return WYP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wyp_abi_version(void) { return WYP_ABI_VERSION; }
+
+const char* wyp_status_string(int32_t status)
+{
+    switch (status) {
+    case WYP_OK: return "WYP_OK";
+    case WYP_ERR_INVALID_ARGUMENT: return "WYP_ERR_INVALID_ARGUMENT";
+    case WYP_ERR_UNSUPPORTED: return "WYP_ERR_UNSUPPORTED";
+    case WYP_ERR_HIP: return "WYP_ERR_HIP";
+    default: return "WYP_ERR_UNKNOWN";
+    }
+}
+
+const char* wyp_last_error(void) { return g_last_error; }
+
+wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* beta,
+                         const int32_t* cu_seqlens, float* T_out, void* stream)
+{
+    return run(problem, k, nullptr, beta, cu_seqlens, T_out, nullptr, nullptr, false, stream);
+}
+
+wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void* v,
+                          const float* beta, const int32_t* cu_seqlens, float* T_out,
+                          void* W_out, void* U_out, void* stream)
+{
+    return run(problem, k, v, beta, cu_seqlens, T_out, W_out, U_out, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal interface between the C-ABI front end (wyprep_api.cpp) and the HIP kernels
+// (wyprep_kernels.hip).  Not installed; the public boundary is include/wyprep.h.
+#pragma once
+
+#include <cstdint>
+
+namespace wyp {
+
+// Validated problem, ready to launch.
+struct LaunchArgs {
+    const void* k;
+    const void* v;            // nullptr for kkt_solve
+    const float* beta;
+    const int32_t* cu_seqlens;  // nullptr: B x T layout
+    float* T;
+    void* W;                  // nullptr for kkt_solve
+    void* U;
+    int32_t batch;
+    int32_t seqlen;
+    int32_t num_qk_heads;
+    int32_t num_v_heads;
+    int32_t num_seqs;
+    int32_t chunk_size;
+    int32_t kv_dtype;         // 0 bf16, 1 f32
+    int64_t chunk_slots;      // chunks (B x T) or an upper bound on them (packed)
+};
+
+// Enqueues the kernel on `stream`.  Returns 0 or the hipError_t value; fills `msg` on error.
+int launch(const LaunchArgs& a, void* stream, char* msg, int msg_len);
+
+}  // namespace wyp

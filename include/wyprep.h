@@ -1,0 +1,115 @@
+/*
+ * wyprep.h -- C ABI of the MI355X (gfx950) per-chunk WY/UT preparation of chunkwise
+ * (Gated) DeltaNet.
+ *
+ * Pages cited (by title and section):
+ *   [Inv]  "TileLang 实战：单位下三角矩阵求逆" (TileLang in practice: inverting a unit
+ *          lower-triangular matrix).
+ *   [QLA]  The FlashQLA announcement (FlashQLA: a TileLang GDN chunked-prefill operator
+ *          library), section "使用方式" (usage).
+ *
+ * For every chunk of C tokens of every sequence and every value head h the library computes
+ * ([Inv] section 1, the coefficient-matrix equation and the W / U equations):
+ *     A = I + strictLower(diag(beta) K K^T)       (beta scales rows; diagonal 1, [Inv] 3.2)
+ *     T = A^{-1}                                  (block recursion of [Inv] section 2.2:
+ *                                                  independent 16x16 forward substitutions,
+ *                                                  then the coupling -X11 L10 X00 per level)
+ *     W = T diag(beta) K,   U = T diag(beta) V
+ * K is the chunk's keys of key head h / (Hv/Hq), V its values of value head h.
+ *
+ * Layouts (row-major, contiguous, token-major as in [QLA] usage):
+ *   k      [B, T, Hq, dk]    dtype kv_dtype
+ *   v      [B, T, Hv, dv]    dtype kv_dtype
+ *   beta   [B, T, Hv]        float32
+ *   T_out  [B, T, Hv, C]     float32; row t holds row (t - chunk start) of its chunk's T with
+ *                            chunk-relative columns; every entry right of the diagonal
+ *                            (including columns >= n of a short chunk) is written as 0.0 and
+ *                            the diagonal as 1.0.
+ *   W_out  [B, T, Hv, dk]    dtype kv_dtype
+ *   U_out  [B, T, Hv, dv]    dtype kv_dtype
+ *   cu_seqlens  int32 [N+1] (device) or NULL.  With it, B must be 1, T is the total packed
+ *               token count, and chunks restart at every sequence start ([QLA] usage lists
+ *               cu_seqlens as the variable-length option).  The last chunk of a sequence may
+ *               hold n < C tokens; it is solved as an n x n system (the same result as padding
+ *               k with zero rows and beta = 0).
+ *
+ * Ownership: every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ * never allocates, frees or synchronises device memory, keeps no per-call state and needs no
+ * workspace.  k, v, T_out, W_out and U_out must be 16-byte aligned; beta and cu_seqlens
+ * 4-byte aligned.
+ *
+ * Streams: work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ * call returns without waiting for it.
+ *
+ * Errors: problems detectable on the host return WYP_ERR_INVALID_ARGUMENT or
+ * WYP_ERR_UNSUPPORTED before any HIP call and launch nothing; a failed launch returns
+ * WYP_ERR_HIP.  wyp_last_error() then describes the failure (per calling thread).  No C++
+ * exception crosses this boundary.  A problem with T == 0 tokens is a no-op returning WYP_OK.
+ * The device contents of cu_seqlens are trusted, not checked (that would need a
+ * synchronisation): cu[0] = 0, non-decreasing, cu[N] = T.
+ *
+ * Supported: dk = dv = 128; C in {32, 64, 128}; kv_dtype WYP_BF16 (bf16 MFMA, fp32
+ * accumulation) or WYP_F32 (fp32 MFMA; wyp_wy_prepare at C = 32 or 64 only, since the fp32
+ * K, V and T tiles of C = 128 exceed one workgroup's 160 KiB of LDS); Hv a multiple of Hq.
+ * Anything else returns WYP_ERR_UNSUPPORTED.
+ */
+#ifndef WYPREP_H
+#define WYPREP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WYP_ABI_VERSION 1
+
+typedef enum {
+    WYP_OK = 0,
+    WYP_ERR_INVALID_ARGUMENT = 1,
+    WYP_ERR_UNSUPPORTED = 2,
+    WYP_ERR_HIP = 3
+} wyp_status;
+
+typedef enum { WYP_BF16 = 0, WYP_F32 = 1 } wyp_dtype;
+
+/* Problem sizes.  The struct is read, never kept. */
+typedef struct {
+    int32_t batch;        /* B (must be 1 when cu_seqlens is given)                     */
+    int32_t seqlen;       /* T per batch row; total packed tokens with cu_seqlens        */
+    int32_t num_qk_heads; /* Hq: key heads                                               */
+    int32_t num_v_heads;  /* Hv: value heads, a multiple of Hq                          */
+    int32_t head_dim_k;   /* dk (128)                                                   */
+    int32_t head_dim_v;   /* dv (128)                                                   */
+    int32_t chunk_size;   /* C: 32, 64 or 128                                           */
+    int32_t num_seqs;     /* N: number of packed sequences (only with cu_seqlens)        */
+    int32_t kv_dtype;     /* wyp_dtype of k, v, W_out, U_out                             */
+} wyp_problem;
+
+/* Version of this ABI (WYP_ABI_VERSION of the build). */
+int32_t wyp_abi_version(void);
+
+/* Static text for a status code. */
+const char* wyp_status_string(int32_t status);
+
+/* Detail of the calling thread's last non-OK return ("" if none).  Valid until the thread's
+ * next call into the library. */
+const char* wyp_last_error(void);
+
+/* kkt_solve ([Inv] section 3: takes only K and beta, produces only T): writes T_out for every
+ * chunk and value head.  k [B,T,Hq,dk], beta [B,T,Hv], T_out [B,T,Hv,C]. */
+wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* beta,
+                         const int32_t* cu_seqlens, float* T_out, void* stream);
+
+/* The full preparation step ([Inv] section 1: T is materialised because both W and U reuse
+ * it): writes T_out, W_out = T diag(beta) K and U_out = T diag(beta) V in one pass over K
+ * and V. */
+wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void* v,
+                          const float* beta, const int32_t* cu_seqlens, float* T_out,
+                          void* W_out, void* U_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WYPREP_H */

@@ -1,0 +1,113 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects bad
+arguments before any HIP call (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_gated_deltanet_amd as cg
+from chunkwise_gated_deltanet_amd import build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "wyprep.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cg.LIB_PATH):
+        build.build_library()
+    return cg.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wyp_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
+                          "wyp_kkt_solve", "wyp_wy_prepare"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.wyp_abi_version() == 1
+    assert lib.wyp_status_string(0) == b"WYP_OK"
+    assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
+    assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation or is empty
+
+
+def good(**kw):
+    d = dict(batch=1, seqlen=128, num_qk_heads=2, num_v_heads=4, head_dim_k=128,
+             head_dim_v=128, chunk_size=64, num_seqs=0, kv_dtype=0)
+    d.update(kw)
+    return cg.Problem(*[d[n] for n, _ in cg.Problem._fields_])
+
+
+def call_wy(lib, p, k=FAKE, v=FAKE, beta=FAKE, cu=None, T=FAKE, W=FAKE, U=FAKE):
+    return lib.wyp_wy_prepare(ctypes.byref(p) if p is not None else None, k, v, beta, cu, T, W,
+                              U, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(chunk_size=48), 2, "chunk_size"),
+    (dict(chunk_size=16), 2, "chunk_size"),
+    (dict(head_dim_k=64), 2, "head_dim"),
+    (dict(head_dim_v=256), 2, "head_dim"),
+    (dict(num_v_heads=3), 1, "multiple"),
+    (dict(num_qk_heads=0), 1, "head counts"),
+    (dict(batch=0), 1, "batch"),
+    (dict(seqlen=-1), 1, "seqlen"),
+    (dict(kv_dtype=7), 1, "kv_dtype"),
+    (dict(kv_dtype=1, chunk_size=128), 2, "C = 128"),
+])
+def test_rejects_bad_problem(lib, kw, code, needle):
+    assert call_wy(lib, good(**kw)) == code
+    assert needle in lib.wyp_last_error().decode()
+
+
+def test_rejects_null_and_misaligned(lib):
+    assert call_wy(lib, None) == 1
+    assert call_wy(lib, good(), k=None) == 1
+    assert call_wy(lib, good(), U=None) == 1
+    assert call_wy(lib, good(), T=FAKE + 4) == 1
+    assert "16-byte" in lib.wyp_last_error().decode()
+    assert call_wy(lib, good(), beta=FAKE + 2) == 1
+    assert lib.wyp_kkt_solve(ctypes.byref(good()), FAKE, FAKE, None, None, None) == 1
+
+
+def test_rejects_bad_packing(lib):
+    assert call_wy(lib, good(batch=2, num_seqs=2), cu=FAKE) == 1
+    assert "batch" in lib.wyp_last_error().decode()
+    assert call_wy(lib, good(num_seqs=-1), cu=FAKE) == 1
+    assert call_wy(lib, good(num_seqs=0, seqlen=5), cu=FAKE) == 1
+    assert call_wy(lib, good(num_seqs=2), cu=FAKE + 2) == 1
+
+
+def test_empty_problem_is_a_noop(lib):
+    assert call_wy(lib, good(seqlen=0)) == 0
+    assert lib.wyp_last_error() == b""
+    assert call_wy(lib, good(seqlen=0, num_seqs=0), cu=FAKE) == 0
+    assert lib.wyp_kkt_solve(ctypes.byref(good(seqlen=0)), FAKE, FAKE, None, FAKE, None) == 0
+
+
+def test_error_text_is_per_call(lib):
+    assert call_wy(lib, good(chunk_size=3)) == 2
+    assert lib.wyp_last_error() != b""
+    assert call_wy(lib, good(seqlen=0)) == 0
+    assert lib.wyp_last_error() == b""
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    k = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    beta = torch.zeros(1, 4, 1)
+    with pytest.raises(ValueError):
+        cg.kkt_solve(k, beta, 64)
