@@ -95,6 +95,9 @@ def main(argv=None):
     ap.add_argument("--chunk-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +209,13 @@ def main(argv=None):
                      "traffic": traffic, "algorithmic_bytes": alg},
         "cpu_baseline": None,
     }
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -6,34 +6,43 @@
 //         lower-triangular matrix).
 //   [QLA] The FlashQLA announcement, section "使用方式" (usage).
 //
-// One workgroup of 256 threads (four wave64s) owns one unit = (sequence, chunk, value head):
-//   a0  map the workgroup to its unit (packed batches: scan cu_seqlens on the device);
-//   a1  stage the chunk's K (n x 128), V (n x 128) and beta (n) in LDS with 16-byte loads;
-//       rows n..C-1 of a short chunk are zero with beta = 0 ([Inv] leaves tails open; this is
-//       the padded reading: A = blockdiag(A_n, I) so T = blockdiag(T_n, I));
+// A unit is one (sequence, chunk, value head).  Workgroups of 256 threads (four wave64s) are
+// persistent: the grid holds one resident round, and each workgroup walks a strided list of
+// units.  While it computes one unit, the next unit's K, V and beta are already in flight
+// into registers, so HBM traffic never waits for the arithmetic.  Per unit:
+//   a0  map the unit to (first token, length n, value head); packed batches scan cu_seqlens
+//       on the device;
+//   a1  K (n x 128), V (n x 128) and beta (n) arrive through bounded buffer loads: rows
+//       n..C-1 of a short chunk read as zero with beta = 0 ([Inv] leaves tails open; this is
+//       the padded reading, A = blockdiag(A_n, I), so T = blockdiag(T_n, I)).  K and beta go
+//       to LDS at once; V stays in registers until the T tile is free (LDS per unit is
+//       K + T, 34 KiB at C = 64, so four workgroups share a CU);
 //   a2  Gram G = K K^T, lower 16x16 tiles only, on bf16 MFMA (fp32 MFMA for fp32 inputs);
 //   a3  A = I + strictLower(diag(beta) G): beta scales rows, the diagonal is 1 ([Inv] 3.2);
-//   a4  the A matrix stays in one fp32 LDS tile; its diagonal 16x16 blocks are inverted in
-//       place and each coupling level overwrites its sub-diagonal block ([Inv] 3.3-3.6);
-//   a5  C/16 independent 16x16 forward substitutions, one lane per column, 15 dependent
-//       steps ([Inv] 2.1 and 3.4);
+//   a4  A lives in one fp32 LDS tile; its diagonal 16x16 blocks are inverted in place and
+//       each coupling level overwrites its sub-diagonal block ([Inv] 3.3-3.6);
+//   a5  C/16 independent 16x16 forward substitutions, one lane per column ([Inv] 2.1, 3.4);
 //   a6  coupling levels s = 16, 32, 64: X10 = -X11 L10 X00 as two fp32 MFMA products, the
 //       first product's accumulator feeding the second as its B operand ([Inv] 2.2, 3.5);
-//   a7  store T (fp32, upper triangle 0, diagonal 1);
-//   a8  T' = T diag(beta) as a hi + lo pair of bf16 values, W = T' K and U = T' V on bf16
-//       MFMA (T' is lower triangular, so k-tiles right of the diagonal are skipped), staged
-//       in LDS and stored with 16-byte writes.
+//   a7  store T (fp32; upper triangle 0, diagonal 1), then overwrite the T tile in place with
+//       T' = T diag(beta) as a hi + lo pair of bf16 values;
+//   a8  W^T = K^T T'^T and U^T = V^T T'^T on 16x16x16 bf16 MFMA, hi and lo parts of T'
+//       accumulated in turn (T' is lower triangular, so k-tiles right of the diagonal are
+//       skipped); the transposed accumulators hold four consecutive output columns per lane,
+//       staged in LDS and stored with 16-byte writes.
 //
-// MFMA operand convention used throughout: for a 16x16 output tile, lane l = 16*g + c holds
-// row/column c and k-group g.  In __builtin_amdgcn_mfma_f32_16x16x4f32 sub-step q the lane
-// supplies true k = 16*kt + 4*g + q; in __builtin_amdgcn_mfma_f32_16x16x32_bf16 element j
-// supplies true k = 32*kt + 8*g + j.  A and B use the same map, so the contraction is exact
-// in any hardware k order.  Accumulator element r of lane 16*g + c is D[4*g + r][c]; with the
-// k map above that is exactly the B operand a following 16x16x4 product needs.
+// MFMA operand convention: for a 16x16 output tile, lane l = 16*g + c holds row/column c and
+// k-group g.  In __builtin_amdgcn_mfma_f32_16x16x4f32 sub-step q the lane supplies true
+// k = 16*kt + 4*g + q; in __builtin_amdgcn_mfma_f32_16x16x32_bf16 element j supplies true
+// k = 32*kt + 8*g + j.  A and B use the same map, so the contraction is exact in any hardware
+// k order.  Accumulator element r of lane 16*g + c is D[4*g + r][c]; with the k map above that
+// is exactly the B operand a following 16x16x4 product needs.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
+#include <type_traits>
 
 #include "wyprep_launch.h"
 
@@ -41,11 +50,15 @@ namespace wyp {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kD = 128;        // head dim of k and v
 constexpr int kThreads = 256;  // four wave64s
 constexpr int kWaves = kThreads / 64;
+constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bounds checked
 
 struct Params {
     const void* k;
@@ -62,8 +75,11 @@ struct Params {
     int32_t num_seqs;
 };
 
-// LDS plan of one workgroup.  K and V rows carry 16 bytes of padding so that 16-byte reads of
-// one column chunk by 16 consecutive rows spread over all banks; T rows carry 4 floats.
+// LDS plan of one workgroup.  K and V rows carry 16 bytes of padding and T rows 4 floats, so
+// 16-byte reads of one column chunk by 16 consecutive rows spread over all banks.  V never
+// has its own region: it waits in registers until the T tile has been read for the last time
+// and then takes its place, so one unit needs K + max(T, V) bytes (34 KiB at C = 64: four
+// workgroups per CU).
 template <int C, int DT, bool WU>
 struct Lds {
     static constexpr int ESZ = DT == 0 ? 2 : 4;
@@ -71,36 +87,57 @@ struct Lds {
     static constexpr int KBYTES = C * KROW * ESZ;
     static constexpr int TROW = C + 4;           // floats per T row
     static constexpr int TBYTES = C * TROW * 4;
+    static constexpr int TVBYTES = WU && KBYTES > TBYTES ? KBYTES : TBYTES;
     static constexpr int OFF_K = 0;
-    static constexpr int OFF_V = KBYTES;
-    static constexpr int OFF_T = WU ? 2 * KBYTES : KBYTES;
-    static constexpr int OFF_B = OFF_T + TBYTES;
+    static constexpr int OFF_T = KBYTES;         // T, later V and the U staging
+    static constexpr int OFF_B = OFF_T + TVBYTES;
     static constexpr int OFF_INFO = OFF_B + C * 4;
     static constexpr int TOTAL = OFF_INFO + 16;
 };
 
+// Waves per SIMD the LDS plan allows (one wave of each resident workgroup per SIMD); the
+// register allocator is held to that budget.
+template <int C, int DT, bool WU>
+struct WavesPerEu {
+    static constexpr int by_lds = (160 * 1024) / Lds<C, DT, WU>::TOTAL;
+    static constexpr int value = by_lds < 1 ? 1 : (by_lds > 4 ? 4 : by_lds);
+};
+
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// a0: unit -> (first token, chunk length, value head).  Returns false for surplus workgroups.
-template <int C>
-__device__ bool map_unit(const Params& p, int* info, int64_t* tok0, int* n, int* hv)
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
 {
-    const uint32_t G = gridDim.x;  // a multiple of 8
-    const uint32_t bid = blockIdx.x;
-    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of
-    // units so that value heads sharing a key head, and neighbouring chunks, meet in one L2.
-    const int64_t logical = static_cast<int64_t>(bid & 7u) * (G >> 3) + (bid >> 3);
-    if (logical >= p.units) return false;
-    *hv = static_cast<int>(logical % p.hv);
-    const int64_t slot = logical / p.hv;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferConfig);
+}
+
+struct Unit {
+    int64_t tok0;  // first token (flattened b*T + t)
+    int n;         // tokens in the chunk (1..C); 0 = no unit
+    int hv;        // value head
+};
+
+// a0: logical unit index -> Unit (n == 0 past the end).  Packed batches: wave 0 scans
+// cu_seqlens 64 sequences at a time; the result goes through LDS (one barrier).
+template <int C>
+__device__ Unit map_unit(const Params& p, int* info, int64_t logical64, int tid)
+{
+    Unit u{0, 0, 0};
+    if (logical64 >= p.units) return u;
+    // units < 2^31 (checked on the host), so 32-bit arithmetic suffices here
+    const uint32_t logical = static_cast<uint32_t>(logical64);
+    const uint32_t hvn = static_cast<uint32_t>(p.hv);
+    u.hv = static_cast<int>(logical % hvn);
+    const uint32_t slot = logical / hvn;
     if (p.cu == nullptr) {
-        const int64_t cps = (p.seqlen + C - 1) / C;
-        const int64_t b = slot / cps, c = slot % cps;
-        *tok0 = b * p.seqlen + c * C;
-        *n = static_cast<int>(min<int64_t>(C, p.seqlen - c * C));
-        return true;
+        const uint32_t cps = static_cast<uint32_t>((p.seqlen + C - 1) / C);
+        const uint32_t b = slot / cps, c = slot % cps;
+        u.tok0 = static_cast<int64_t>(b) * p.seqlen + static_cast<int64_t>(c) * C;
+        u.n = min(C, p.seqlen - static_cast<int>(c) * C);
+        return u;
     }
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = tid & 63;
     if (tid < 64) {
         int64_t run = 0;
         int found_s = -1, found_c = 0;
@@ -115,12 +152,13 @@ __device__ bool map_unit(const Params& p, int* info, int64_t* tok0, int* n, int*
                 if (lane >= d) incl += t;
             }
             const int excl = incl - cnt;
-            const bool hit = cnt > 0 && slot >= run + excl && slot < run + incl;
+            const bool hit = cnt > 0 && static_cast<int64_t>(slot) >= run + excl &&
+                             static_cast<int64_t>(slot) < run + incl;
             const unsigned long long m = __ballot(hit);
             if (m) {
                 const int src = __ffsll(m) - 1;
                 found_s = __shfl(s, src);
-                found_c = static_cast<int>(slot - run - __shfl(excl, src));
+                found_c = static_cast<int>(static_cast<int64_t>(slot) - run - __shfl(excl, src));
                 break;
             }
             run += __shfl(incl, 63);
@@ -131,155 +169,280 @@ __device__ bool map_unit(const Params& p, int* info, int64_t* tok0, int* n, int*
         }
     }
     __syncthreads();
-    const int s = info[0];
-    if (s < 0) return false;
-    const int64_t s0 = p.cu[s], s1 = p.cu[s + 1];
-    *tok0 = s0 + static_cast<int64_t>(info[1]) * C;
-    *n = static_cast<int>(min<int64_t>(C, s1 - *tok0));
-    return true;
+    const int s = uniform(info[0]);
+    const int c = uniform(info[1]);
+    if (s < 0) return u;
+    const int s0 = uniform(p.cu[s]), s1 = uniform(p.cu[s + 1]);
+    u.tok0 = s0 + static_cast<int64_t>(c) * C;
+    u.n = min(C, s1 - static_cast<int>(u.tok0));
+    return u;
 }
 
-// a1: C rows of 128 elements from a [tokens, heads, 128] tensor into LDS (zero rows >= n).
-template <int C, int ESZ, int KROW>
-__device__ void stage_rows(unsigned char* dst, const void* src, int64_t tok0, int n, int heads,
-                           int head)
-{
-    constexpr int CPR = kD * ESZ / 16;  // 16-byte chunks per row
-    constexpr int NIT = C * CPR / kThreads;
+// a1: K, V and beta of one unit in flight to registers, then committed to LDS.  K and beta
+// are committed at the start of their unit; V only after that unit's T tile has been used.
+template <int C, int ESZ, int KROW, bool WU>
+struct Prefetch {
+    static constexpr int CPR = kD * ESZ / 16;  // 16-byte chunks per row
+    static constexpr int NIT = C * CPR / kThreads;
     static_assert(C * CPR % kThreads == 0, "row chunks must split evenly");
-    const int tid = threadIdx.x;
-    const unsigned char* base = static_cast<const unsigned char*>(src);
-    uint4 val[NIT];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int q = tid + it * kThreads;
-        const int r = q / CPR, c16 = q % CPR;
-        val[it] = uint4{0u, 0u, 0u, 0u};
-        if (r < n)
-            val[it] = *reinterpret_cast<const uint4*>(
-                base + ((tok0 + r) * heads + head) * (kD * ESZ) + c16 * 16);
+    u32x4 k[NIT];
+    u32x4 v[WU ? NIT : 1];
+    float b;
+
+    __device__ static __amdgpu_buffer_rsrc_t rows(const void* base, const Unit& u, int heads, int head)
+    {
+        const uint32_t stride = static_cast<uint32_t>(heads) * kD * ESZ;
+        const unsigned char* p = static_cast<const unsigned char*>(base) + (u.tok0 * heads + head) * (kD * ESZ);
+        return rsrc(p, (u.n - 1) * stride + kD * ESZ);
     }
+
+    __device__ void issue_k(const Params& p, const Unit& u, int tid)
+    {
+        const int hk = u.hv / (p.hv / p.hq);
+        const uint32_t kstride = static_cast<uint32_t>(p.hq) * kD * ESZ;
+        const __amdgpu_buffer_rsrc_t kr = rows(p.k, u, p.hq, hk);
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int q = tid + it * kThreads;
-        const int r = q / CPR, c16 = q % CPR;
-        *reinterpret_cast<uint4*>(dst + r * (KROW * ESZ) + c16 * 16) = val[it];
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kThreads;
+            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q / CPR) * kstride + (q % CPR) * 16, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t br =
+            rsrc(p.beta + u.tok0 * p.hv + u.hv, ((u.n - 1) * p.hv + 1) * 4);
+        b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (tid % C) * p.hv * 4, 0, 0));
     }
+
+    __device__ void issue_v(const Params& p, const Unit& u, int tid)
+    {
+        if constexpr (WU) {
+            const uint32_t vstride = static_cast<uint32_t>(p.hv) * kD * ESZ;
+            const __amdgpu_buffer_rsrc_t vr = rows(p.v, u, p.hv, u.hv);
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int q = tid + it * kThreads;
+                v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, (q / CPR) * vstride + (q % CPR) * 16, 0, 0);
+            }
+        }
+    }
+
+    __device__ void commit_k(unsigned char* Kraw, float* bs, int tid) const
+    {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kThreads;
+            *reinterpret_cast<u32x4*>(Kraw + (q / CPR) * (KROW * ESZ) + (q % CPR) * 16) = k[it];
+        }
+        if (tid < C) bs[tid] = b;
+    }
+
+    __device__ void commit_v(unsigned char* Vraw, int tid) const
+    {
+        if constexpr (WU) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int q = tid + it * kThreads;
+                *reinterpret_cast<u32x4*>(Vraw + (q / CPR) * (KROW * ESZ) + (q % CPR) * 16) = v[it];
+            }
+        }
+    }
+};
+
+// a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts; all C x C entries are written.
+// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4; upper tiles are zeroed with one
+// 16-byte write per lane.
+__device__ inline void tile_of(int t, int* I, int* J)
+{
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    *I = i;
+    *J = t - i * (i + 1) / 2;
 }
 
-// a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts (all C x C entries written).
-template <int C, int DT, int KROW, int TROW>
-__device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs)
-{
-    constexpr int NB = C / 16;
-    constexpr int NTILE = NB * (NB + 1) / 2;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    for (int t = wave; t < NTILE; t += kWaves) {
-        int I = 0;
-        while ((I + 1) * (I + 2) / 2 <= t) ++I;
-        const int J = t - I * (I + 1) / 2;
-        f32x4 acc = zero4();
+template <int DT, int KROW>
+struct GramFrags {
+    static constexpr int NS = DT == 0 ? kD / 32 : kD / 16;
+    typedef typename std::conditional<DT == 0, bf16x8, f32x4>::type frag;
+    frag a[NS], b[NS];
+
+    __device__ void load(const unsigned char* Kraw, int I, int J, int lr, int lg)
+    {
         if constexpr (DT == 0) {
             const __bf16* K = reinterpret_cast<const __bf16*>(Kraw);
 #pragma unroll
-            for (int s = 0; s < kD / 32; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                const bf16x8 b = *reinterpret_cast<const bf16x8*>(K + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+            for (int s = 0; s < NS; ++s) {
+                a[s] = *reinterpret_cast<const bf16x8*>(K + (16 * I + lr) * KROW + 32 * s + 8 * lg);
+                b[s] = *reinterpret_cast<const bf16x8*>(K + (16 * J + lr) * KROW + 32 * s + 8 * lg);
             }
         } else {
             const float* K = reinterpret_cast<const float*>(Kraw);
 #pragma unroll
-            for (int s = 0; s < kD / 16; ++s) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(K + (16 * I + lr) * KROW + 16 * s + 4 * lg);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(K + (16 * J + lr) * KROW + 16 * s + 4 * lg);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
+            for (int s = 0; s < NS; ++s) {
+                a[s] = *reinterpret_cast<const f32x4*>(K + (16 * I + lr) * KROW + 16 * s + 4 * lg);
+                b[s] = *reinterpret_cast<const f32x4*>(K + (16 * J + lr) * KROW + 16 * s + 4 * lg);
             }
         }
+    }
+
+    __device__ f32x4 product() const
+    {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if constexpr (DT == 0) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][q], b[s][q], acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+};
+
+template <int C, int DT, int KROW, int TROW>
+__device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
+{
+    constexpr int NB = C / 16;
+    constexpr int NTILE = NB * (NB + 1) / 2;
+    constexpr int PER = (NTILE + kWaves - 1) / kWaves;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    // Operands are loaded tile by tile: with four workgroups per CU, other waves cover the
+    // LDS latency, and a second operand buffer would cost 32 registers.
+    constexpr int NBUF = 1;
+    GramFrags<DT, KROW> f[NBUF];
+    int I = 0, J = 0;
+    if (wave < NTILE) {
+        tile_of(wave, &I, &J);
+        f[0].load(Kraw, I, J, lr, lg);
+    }
+#pragma unroll
+    for (int tt = 0; tt < PER; ++tt) {
+        const int t = tt * kWaves + wave;
+        if (t >= NTILE) break;
+        int In = 0, Jn = 0;
+        const int tn = t + kWaves;
+        if (NBUF == 2 && tt + 1 < PER && tn < NTILE) {
+            tile_of(tn, &In, &Jn);
+            f[(tt + 1) % NBUF].load(Kraw, In, Jn, lr, lg);
+        }
+        if (NBUF == 1 && tt > 0) f[0].load(Kraw, I, J, lr, lg);
+        const f32x4 acc = f[tt % NBUF].product();
+        const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
+        const float bcol = bs[16 * J + lr];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            // Diagonal tiles keep L^T in their upper triangle (G is symmetric, so entry (i, j),
+            // i < j, is beta_j G[j][i] = L[j][i]); the substitution reads columns of L there
+            // and overwrites it with zeros.
             const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
-            Ts[i * TROW + j] = (i > j) ? bs[i] * acc[r] : (i == j ? 1.f : 0.f);
+            Ts[i * TROW + j] = (i > j) ? bet[r] * acc[r] : (i == j ? 1.f : bcol * acc[r]);
+        }
+        if (NBUF == 2) {
+            I = In;
+            J = Jn;
+        } else if (tn < NTILE) {
+            tile_of(tn, &I, &J);
         }
     }
-    // strictly upper 16x16 tiles
-    for (int e = tid; e < C * C; e += kThreads) {
-        const int i = e / C, j = e % C;
-        if ((j >> 4) > (i >> 4)) Ts[i * TROW + j] = 0.f;
+    // strictly upper tiles (I < J), enumerated row-major, also dealt round-robin to waves
+    constexpr int NUP = NB * (NB - 1) / 2;
+#pragma unroll
+    for (int tt = 0; tt < (NUP + kWaves - 1) / kWaves; ++tt) {
+        const int t = tt * kWaves + wave;
+        if (t >= NUP) break;
+        int Iu = 0, rem = t;
+        while (rem >= NB - 1 - Iu) {
+            rem -= NB - 1 - Iu;
+            ++Iu;
+        }
+        const int Ju = Iu + 1 + rem;
+        *reinterpret_cast<f32x4*>(Ts + (16 * Iu + lr) * TROW + 16 * Ju + 4 * lg) = zero4();
+    }
+}
+
+// Step J of the right-looking substitution for lane (block, column i): X[J][i] is final
+// (1 for J = i, else -acc[J]; acc holds the negated partial sums, exactly +0 above i), it is
+// written back, and every later row k takes acc[k] -= L[k][J] X[J][i].  L[k][J] for k > J is
+// read from row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the
+// block read the same row (an LDS broadcast).  Row J's upper part is read before any lane
+// overwrites it with its X column.
+template <int J, int TROW>
+__device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
+{
+    const float x = (J == i) ? 1.f : acc[J];
+    float lrow[16];
+    if constexpr (J < 15) {
+#pragma unroll
+        for (int c4 = (J + 1) / 4; c4 < 4; ++c4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + J * TROW + 4 * c4);
+            lrow[4 * c4 + 0] = v[0];
+            lrow[4 * c4 + 1] = v[1];
+            lrow[4 * c4 + 2] = v[2];
+            lrow[4 * c4 + 3] = v[3];
+        }
+    }
+    blk[J * TROW + i] = x;
+    if constexpr (J < 15) {
+#pragma unroll
+        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-lrow[k], x, acc[k]);
+        substitution_step<J + 1, TROW>(acc, i, blk);
     }
 }
 
 // a5: invert the C/16 diagonal 16x16 blocks of Ts in place.  Lane (block b, column i) keeps
-// column i of X_b = L_b^{-1} in registers: X[k][i] = -sum_{j<k} L[k][j] X[j][i] for k > i,
-// with X[i][i] = 1 and X[j][i] = 0 for j < i.  All reads of a block precede its writes (one
-// wave per group of four blocks, LDS operations of a wave complete in order).
+// column i of X_b = L_b^{-1} in registers, right-looking: after X[j][i] is final, every later
+// row k takes its share L[k][j] X[j][i], so one multiply-add per step sits on the dependency
+// chain.  Blocks 0-3 run on wave 0, blocks 4-7 on wave 1.
 template <int C, int TROW>
-__device__ void invert_diagonal_blocks(float* Ts)
+__device__ void invert_diagonal_blocks(float* Ts, int tid)
 {
     constexpr int NB = C / 16;
-    const int tid = threadIdx.x;
     if (tid >= NB * 16) return;
     const int b = tid >> 4, i = tid & 15;
     float* blk = Ts + 16 * b * TROW + 16 * b;
-    float x[16];
+    float acc[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) x[k] = (k == i) ? 1.f : 0.f;
-#pragma unroll
-    for (int k = 1; k < 16; ++k) {
-        float row[16];
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + k * TROW + 4 * c4);
-            row[4 * c4 + 0] = v[0];
-            row[4 * c4 + 1] = v[1];
-            row[4 * c4 + 2] = v[2];
-            row[4 * c4 + 3] = v[3];
-        }
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < k; ++j) s = __builtin_fmaf(row[j], x[j], s);
-        x[k] = (k > i) ? -s : x[k];
-    }
-#pragma unroll
-    for (int k = 1; k < 16; ++k)
-        if (k > i) blk[k * TROW + i] = x[k];
+    for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+    substitution_step<0, TROW>(acc, i, blk);
 }
 
 // a6, one level: block size S.  Pair p covers rows/cols [2Sp, 2Sp + 2S); its sub-diagonal
 // block L10 (rows 2Sp+S.., cols 2Sp..) is replaced by X10 = -X11 (L10 X00).  Wave w owns pair
 // w / (S/16) and 16-column tile w % (S/16) of X10.
 template <int C, int S, int TROW>
-__device__ void coupling_level(float* Ts)
+__device__ void coupling_level(float* Ts, int tid)
 {
     constexpr int TS = S / 16;
     constexpr int NPAIR = C / (2 * S);
     constexpr int NTASK = NPAIR * TS;
     static_assert(NTASK <= kWaves, "one coupling task per wave");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const bool active = wave < NTASK;
     const int pr = wave / TS, nc = wave % TS;
     const int base = 2 * S * pr;
     f32x4 res[TS];
     if (active) {
-        // tmp[:, nc] = L10 X00[:, nc]; X00 is lower triangular, so k-tiles kt < nc vanish.
+        // tmp[:, nc] = L10 X00[:, nc].  X00 is lower triangular, so k-tiles kt < nc hold
+        // zeros; they are multiplied anyway, which keeps every operand load branch-free.
         f32x4 tmp[TS];
 #pragma unroll
-        for (int mr = 0; mr < TS; ++mr) {
-            f32x4 acc = zero4();
-            for (int kt = nc; kt < TS; ++kt) {
+        for (int mr = 0; mr < TS; ++mr) tmp[mr] = zero4();
+#pragma unroll
+        for (int kt = 0; kt < TS; ++kt) {
+            float bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bq[q] = Ts[(base + 16 * kt + 4 * lg + q) * TROW + base + 16 * nc + lr];
+#pragma unroll
+            for (int mr = 0; mr < TS; ++mr) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(
                     Ts + (base + S + 16 * mr + lr) * TROW + base + 16 * kt + 4 * lg);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float bq = Ts[(base + 16 * kt + 4 * lg + q) * TROW + base + 16 * nc + lr];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], bq, acc, 0, 0, 0);
-                }
+                for (int q = 0; q < 4; ++q)
+                    tmp[mr] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], bq[q], tmp[mr], 0, 0, 0);
             }
-            tmp[mr] = acc;
         }
         // X10[:, nc] = -X11 tmp[:, nc]; X11 is lower triangular, so kt <= mr.
 #pragma unroll
@@ -307,121 +470,172 @@ __device__ void coupling_level(float* Ts)
     __syncthreads();
 }
 
-// a7: T rows [0, n) to T_out[(tok0 + r) * Hv + hv][0:C].
-template <int C, int TROW>
-__device__ void store_t(const float* Ts, float* Tout, int64_t tok0, int n, int Hv, int hv)
+// a7: T rows [0, n) to T_out[(tok0 + r) * Hv + hv][0:C]; rows >= n fall outside the buffer
+// range and are dropped by the hardware.  With PACK, each thread then overwrites the 16-byte
+// chunk it just stored with T' = T diag(beta) for the W/U products: four bf16 "hi" values
+// followed by four bf16 "lo" values (lo = T' - hi, rounded), i.e. the same bytes per element.
+template <int C, int TROW, bool PACK>
+__device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, int Hv, int tid)
 {
-    constexpr int TCH = C / 4;
-    for (int q = threadIdx.x; q < n * TCH; q += kThreads) {
+    constexpr int TCH = C / 4;                 // 16-byte chunks per row
+    constexpr int NIT = C * TCH / kThreads;    // 1 / 4 / 16 for C = 32 / 64 / 128
+    static_assert(C * TCH % kThreads == 0, "T rows must split evenly");
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t rstride = static_cast<uint32_t>(Hv) * C * 4;
+    const __amdgpu_buffer_rsrc_t tr = rsrc(Tout + (u.tok0 * Hv + u.hv) * C, (u.n - 1) * rstride + C * 4);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int q = tid + it * kThreads;
         const int r = q / TCH, c = q % TCH;
-        const f32x4 val = *reinterpret_cast<const f32x4*>(Ts + r * TROW + 4 * c);
-        *reinterpret_cast<f32x4*>(Tout + ((tok0 + r) * Hv + hv) * C + 4 * c) = val;
+        f32x4* chunk = reinterpret_cast<f32x4*>(Ts + r * TROW + 4 * c);
+        const f32x4 val = *chunk;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, 0);
+        if constexpr (PACK) {
+            const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 4 * c);
+            bf16x4 h, l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float tp = val[e] * b[e];
+                h[e] = static_cast<__bf16>(tp);
+                l[e] = static_cast<__bf16>(tp - static_cast<float>(h[e]));
+            }
+            const u32x2 hp = __builtin_bit_cast(u32x2, h), lp = __builtin_bit_cast(u32x2, l);
+            *reinterpret_cast<u32x4*>(chunk) = u32x4{hp[0], hp[1], lp[0], lp[1]};
+        }
     }
 }
 
-// a8 (bf16): W = T' K and U = T' V with T' = T diag(beta).  T' enters the bf16 MFMA as a
-// hi + lo pair of bf16 values (T' - hi - lo is below 2^-17 |T'|), so the only rounding left
-// in W and U is the final bf16 store.  The B operand (8 consecutive tokens of one K / V
-// column) is gathered with two LDS transpose reads: within each 16-lane group, lane i of
-// ds_read_tr16_b64 receives element (i mod 4) of the 64-bit rows addressed by lanes
-// 4e + i/4, e = 0..3.  16 column tiles of 16 (8 of W, 8 of U); wave w owns tiles w, w+4,
-// w+8, w+12.
-template <int C, int KROW, int TROW>
-__device__ void wu_bf16(unsigned char* Kraw, unsigned char* Vraw, const float* Ts, const float* bs,
-                        void* Wout, void* Uout, int64_t tok0, int n, int Hv, int hv)
+// Stores n rows of 128 elements staged in LDS (row stride KROW elements) to a
+// [tokens, Hv, 128] output.  Rows >= n are dropped by the buffer range.
+template <int C, int ESZ, int KROW>
+__device__ void store_rows(const unsigned char* src, void* out, const Unit& u, int Hv, int tid)
 {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    constexpr int CPR = kD * ESZ / 16;
+    constexpr int NIT = C * CPR / kThreads;
+    const uint32_t rstride = static_cast<uint32_t>(Hv) * kD * ESZ;
+    const __amdgpu_buffer_rsrc_t r_out = rsrc(static_cast<unsigned char*>(out) + (u.tok0 * Hv + u.hv) * (kD * ESZ),
+                                              (u.n - 1) * rstride + kD * ESZ);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int q = tid + it * kThreads;
+        const int r = q / CPR, c16 = q % CPR;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * (KROW * ESZ) + c16 * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(val, r_out, r * rstride + c16 * 16, 0, 0);
+    }
+}
+
+// a8 (bf16): W^T = K^T T'^T and U^T = V^T T'^T with T' = T diag(beta), read from the T tile
+// as packed chunks of four hi and four lo bf16 values (see store_t): one chunk is exactly the
+// hi and the lo operand of a 16x16x16 MFMA, and hi + lo carries T' to within 2^-17 |T'|, so
+// the only rounding left in W and U is the final bf16 store.  k-tiles of 16 tokens right of
+// the diagonal (zeros of T') are skipped.  The K^T / V^T operand (4 consecutive tokens of one
+// column) is one LDS transpose read: within each 16-lane group, lane i of ds_read_tr16_b64
+// receives element (i mod 4) of the 64-bit rows addressed by lanes 4e + i/4, e = 0..3.  Wave w
+// owns column tiles w and w + 4 of W, then of U.  Accumulator element r of lane 16g + c is
+// X[16mi + c][16ni + 4g + r]; the result leaves as bf16.
+template <int C, int KROW>
+__device__ inline void wu_tiles(const unsigned char* src, const u32x4 (&tp)[C / 16][C / 16], int wave,
+                                int lr, int lg, bf16x4 (&out)[2][C / 16])
+{
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     constexpr int NB = C / 16;
-    constexpr int KT = C / 32;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-
-    bf16x8 ahi[NB][KT], alo[NB][KT];
+    const __bf16* base = reinterpret_cast<const __bf16*>(src);
 #pragma unroll
-    for (int mi = 0; mi < NB; ++mi)
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            if (2 * kt > mi) continue;
-            const float* trow = Ts + (16 * mi + lr) * TROW + 32 * kt + 8 * lg;
-            const f32x4 t0 = *reinterpret_cast<const f32x4*>(trow);
-            const f32x4 t1 = *reinterpret_cast<const f32x4*>(trow + 4);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + 32 * kt + 8 * lg);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + 32 * kt + 8 * lg + 4);
-            const float tp[8] = {t0[0] * b0[0], t0[1] * b0[1], t0[2] * b0[2], t0[3] * b0[3],
-                                 t1[0] * b1[0], t1[1] * b1[1], t1[2] * b1[2], t1[3] * b1[3]};
-            bf16x8 h, l;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                h[j] = static_cast<__bf16>(tp[j]);
-                l[j] = static_cast<__bf16>(tp[j] - static_cast<float>(h[j]));
-            }
-            ahi[mi][kt] = h;
-            alo[mi][kt] = l;
-        }
-
-    __bf16 out[4][NB][4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int ct = wave + 4 * c;
-        const __bf16* src = reinterpret_cast<const __bf16*>(ct < 8 ? Kraw : Vraw);
-        const int ni = ct & 7;
+    for (int c = 0; c < 2; ++c) {
+        const int ni = wave + 4 * c;
         f32x4 acc[NB];
 #pragma unroll
         for (int mi = 0; mi < NB; ++mi) acc[mi] = zero4();
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            // lane 16g + L addresses row 32kt + 8g + 4h + L/4, columns 16ni + 4(L%4) .. +3
-            const __bf16* p0 = src + (32 * kt + 8 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
-            const bf16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
-            const bf16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * KROW));
-            const bf16x8 bfr = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int kt = 0; kt < NB; ++kt) {
+            // lane 16g + L addresses row 16kt + 4g + L/4, columns 16ni + 4(L%4) .. +3
+            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
+            const i16x4 kfr = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
 #pragma unroll
-            for (int mi = 0; mi < NB; ++mi)
-                if (2 * kt <= mi) {
-                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mi][kt], bfr, acc[mi], 0, 0, 0);
-                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mi][kt], bfr, acc[mi], 0, 0, 0);
-                }
+            for (int mi = kt; mi < NB; ++mi) {
+                const i16x4 hi = __builtin_bit_cast(i16x4, u32x2{tp[mi][kt][0], tp[mi][kt][1]});
+                const i16x4 lo = __builtin_bit_cast(i16x4, u32x2{tp[mi][kt][2], tp[mi][kt][3]});
+                acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, hi, acc[mi], 0, 0, 0);
+                acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, lo, acc[mi], 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int mi = 0; mi < NB; ++mi)
+        for (int mi = 0; mi < NB; ++mi) {
+            bf16x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[c][mi][r] = static_cast<__bf16>(acc[mi][r]);
-    }
-    __syncthreads();  // all waves are done reading K and V; reuse them as output staging
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int ct = wave + 4 * c;
-        __bf16* dst = reinterpret_cast<__bf16*>(ct < 8 ? Kraw : Vraw);
-        const int ni = ct & 7;
-#pragma unroll
-        for (int mi = 0; mi < NB; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * mi + 4 * lg + r) * KROW + 16 * ni + lr] = out[c][mi][r];
-    }
-    __syncthreads();
-    constexpr int CPR = kD * 2 / 16;  // 16 chunks of 16 bytes per output row
-    const int per = n * CPR;
-    for (int q = tid; q < 2 * per; q += kThreads) {
-        const int which = q >= per;
-        const int rem = q - which * per;
-        const int r = rem / CPR, c16 = rem % CPR;
-        const unsigned char* s = (which ? Vraw : Kraw) + r * (KROW * 2) + c16 * 16;
-        unsigned char* d = static_cast<unsigned char*>(which ? Uout : Wout) +
-                           ((tok0 + r) * Hv + hv) * (kD * 2) + c16 * 16;
-        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+            for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[mi][r]);
+            out[c][mi] = o;
+        }
     }
 }
 
-// a8 (fp32 inputs): the same products on fp32 MFMA, T' kept in fp32.
-template <int C, int KROW, int TROW>
-__device__ void wu_f32(unsigned char* Kraw, unsigned char* Vraw, const float* Ts, const float* bs,
-                       void* Wout, void* Uout, int64_t tok0, int n, int Hv, int hv)
+template <int C, int KROW>
+__device__ inline void stage_tiles(unsigned char* dst, const bf16x4 (&out)[2][C / 16], int wave, int lr, int lg)
+{
+    __bf16* d = reinterpret_cast<__bf16*>(dst);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int mi = 0; mi < C / 16; ++mi)
+            *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + 4 * c) + 4 * lg) = out[c][mi];
+}
+
+// Every wave first takes its T' chunks (lower-triangular 16x16 blocks) into registers; then V,
+// waiting in registers, takes the T tile's place.  W is staged over K while U is computed.
+template <int C, int KROW, int TROW, class PF>
+__device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p, const Unit& u, int tid)
 {
     constexpr int NB = C / 16;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    float out[4][NB][4];
+    u32x4 tp[NB][NB];
+#pragma unroll
+    for (int mi = 0; mi < NB; ++mi)
+#pragma unroll
+        for (int kt = 0; kt <= mi; ++kt)
+            tp[mi][kt] = *reinterpret_cast<const u32x4*>(Ts + (16 * mi + lr) * TROW + 16 * kt + 4 * lg);
+    __syncthreads();  // the T tile is no longer read: V takes its place
+    unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
+    pf.commit_v(Vraw, tid);
+    __syncthreads();
+
+    bf16x4 out[2][NB];
+    wu_tiles<C, KROW>(Kraw, tp, wave, lr, lg, out);
+    __syncthreads();  // every wave is done reading K: W is staged over it
+    stage_tiles<C, KROW>(Kraw, out, wave, lr, lg);
+    wu_tiles<C, KROW>(Vraw, tp, wave, lr, lg, out);
+    __syncthreads();  // every wave is done reading V: U is staged over it
+    stage_tiles<C, KROW>(Vraw, out, wave, lr, lg);
+    __syncthreads();
+    store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
+    store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
+}
+
+// a8 (fp32 inputs): the same transposed products on fp32 MFMA, T' = T diag(beta) kept in fp32
+// registers before V takes the T tile's place.
+template <int C, int KROW, int TROW, class PF>
+__device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, const Params& p,
+                       const Unit& u, int tid)
+{
+    constexpr int NB = C / 16;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 tfr[NB][NB];
+#pragma unroll
+    for (int mi = 0; mi < NB; ++mi)
+#pragma unroll
+        for (int kt = 0; kt <= mi; ++kt) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(Ts + (16 * mi + lr) * TROW + 16 * kt + 4 * lg);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 16 * kt + 4 * lg);
+            tfr[mi][kt] = t * b;
+        }
+    __syncthreads();  // the T tile is no longer read: V takes its place
+    unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
+    pf.commit_v(Vraw, tid);
+    __syncthreads();
+
+    f32x4 out[4][NB];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int ct = wave + 4 * c;
@@ -432,16 +646,13 @@ __device__ void wu_f32(unsigned char* Kraw, unsigned char* Vraw, const float* Ts
             f32x4 acc = zero4();
 #pragma unroll
             for (int kt = 0; kt <= mi; ++kt) {
-                const f32x4 t = *reinterpret_cast<const f32x4*>(Ts + (16 * mi + lr) * TROW + 16 * kt + 4 * lg);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 16 * kt + 4 * lg);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float bq = src[(16 * kt + 4 * lg + q) * KROW + 16 * ni + lr];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(t[q] * b[q], bq, acc, 0, 0, 0);
+                    const float kq = src[(16 * kt + 4 * lg + q) * KROW + 16 * ni + lr];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kq, tfr[mi][kt][q], acc, 0, 0, 0);
                 }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) out[c][mi][r] = acc[r];
+            out[c][mi] = acc;
         }
     }
     __syncthreads();
@@ -452,63 +663,104 @@ __device__ void wu_f32(unsigned char* Kraw, unsigned char* Vraw, const float* Ts
         const int ni = ct & 7;
 #pragma unroll
         for (int mi = 0; mi < NB; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * mi + 4 * lg + r) * KROW + 16 * ni + lr] = out[c][mi][r];
+            *reinterpret_cast<f32x4*>(dst + (16 * mi + lr) * KROW + 16 * ni + 4 * lg) = out[c][mi];
     }
     __syncthreads();
-    constexpr int CPR = kD * 4 / 16;
-    const int per = n * CPR;
-    for (int q = tid; q < 2 * per; q += kThreads) {
-        const int which = q >= per;
-        const int rem = q - which * per;
-        const int r = rem / CPR, c16 = rem % CPR;
-        const unsigned char* s = (which ? Vraw : Kraw) + r * (KROW * 4) + c16 * 16;
-        unsigned char* d = static_cast<unsigned char*>(which ? Uout : Wout) +
-                           ((tok0 + r) * Hv + hv) * (kD * 4) + c16 * 16;
-        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
-    }
+    store_rows<C, 4, KROW>(Kraw, p.W, u, p.hv, tid);
+    store_rows<C, 4, KROW>(Vraw, p.U, u, p.hv, tid);
 }
 
-template <int C, int DT, bool WU>
-__global__ __launch_bounds__(kThreads) void wy_prepare_kernel(Params p)
+// One unit, from committing its prefetched K to storing its outputs; its own V and the next
+// unit's K are issued on the way.  Returns the next unit.
+template <int C, int DT, bool WU, class PF>
+__device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, PF& pf, const Unit& cur,
+                                         int64_t next)
 {
     using L = Lds<C, DT, WU>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char* Kraw = smem + L::OFF_K;
-    unsigned char* Vraw = smem + L::OFF_V;
     float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
     float* bs = reinterpret_cast<float*>(smem + L::OFF_B);
     int* info = reinterpret_cast<int*>(smem + L::OFF_INFO);
-
-    int64_t tok0;
-    int n, hv;
-    if (!map_unit<C>(p, info, &tok0, &n, &hv)) return;  // uniform per workgroup
-    const int hk = hv / (p.hv / p.hq);
-
-    stage_rows<C, L::ESZ, L::KROW>(Kraw, p.k, tok0, n, p.hq, hk);
-    if constexpr (WU) stage_rows<C, L::ESZ, L::KROW>(Vraw, p.v, tok0, n, p.hv, hv);
-    if (threadIdx.x < C)
-        bs[threadIdx.x] = threadIdx.x < n ? p.beta[(tok0 + threadIdx.x) * p.hv + hv] : 0.f;
+    // A fresh copy of the thread index per unit: per-lane addresses are then recomputed for
+    // each unit instead of being hoisted out of the loop and held in registers.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    pf.commit_k(Kraw, bs, tid);
     __syncthreads();
+    // This unit's V is needed only after its inversion; the next unit's K at the next unit's
+    // start.  Issued in that order, a wait for either never waits for the other.
+    pf.issue_v(p, cur, tid);
+    const Unit nxt = map_unit<C>(p, info, next, tid);
+    if (nxt.n > 0) pf.issue_k(p, nxt, tid);
 
-    form_a<C, DT, L::KROW, L::TROW>(Kraw, Ts, bs);
+    form_a<C, DT, L::KROW, L::TROW>(Kraw, Ts, bs, tid);
     __syncthreads();
-
-    invert_diagonal_blocks<C, L::TROW>(Ts);
+    invert_diagonal_blocks<C, L::TROW>(Ts, tid);
     __syncthreads();
-
-    if constexpr (C >= 32) coupling_level<C, 16, L::TROW>(Ts);
-    if constexpr (C >= 64) coupling_level<C, 32, L::TROW>(Ts);
-    if constexpr (C >= 128) coupling_level<C, 64, L::TROW>(Ts);
-
-    store_t<C, L::TROW>(Ts, p.T, tok0, n, p.hv, hv);
-
+    if constexpr (C >= 32) coupling_level<C, 16, L::TROW>(Ts, tid);
+    if constexpr (C >= 64) coupling_level<C, 32, L::TROW>(Ts, tid);
+    if constexpr (C >= 128) coupling_level<C, 64, L::TROW>(Ts, tid);
+    store_t<C, L::TROW, DT == 0 && WU>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
+        __syncthreads();  // T (packed T' for bf16) of all threads is in place
         if constexpr (DT == 0)
-            wu_bf16<C, L::KROW, L::TROW>(Kraw, Vraw, Ts, bs, p.W, p.U, tok0, n, p.hv, hv);
+            wu_bf16<C, L::KROW, L::TROW>(Kraw, Ts, pf, p, cur, tid);
         else
-            wu_f32<C, L::KROW, L::TROW>(Kraw, Vraw, Ts, bs, p.W, p.U, tok0, n, p.hv, hv);
+            wu_f32<C, L::KROW, L::TROW>(Kraw, Ts, bs, pf, p, cur, tid);
     }
+    __syncthreads();  // LDS is rewritten by the next unit
+    return nxt;
+}
+
+template <int C, int DT, bool WU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEu<C, DT, WU>::value))) void wy_prepare_kernel(Params p)
+{
+    using L = Lds<C, DT, WU>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int* info = reinterpret_cast<int*>(smem + L::OFF_INFO);
+
+    // Workgroups are dealt round-robin to the 8 XCDs; in every round give each XCD a
+    // contiguous range of units, so value heads sharing a key head meet in one L2.
+    const uint32_t G = gridDim.x;  // a multiple of 8
+    const int64_t first = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
+
+    Unit cur = map_unit<C>(p, info, first, threadIdx.x);
+    if (cur.n <= 0) return;  // uniform per workgroup
+    Prefetch<C, L::ESZ, L::KROW, WU> pf;
+    pf.issue_k(p, cur, threadIdx.x);
+    // The first unit is peeled off the loop: the loop head is then reached only from the end
+    // of a unit, so the memory-counter waits inside see one issue history.
+    int64_t next = first + G;
+    cur = run_unit<C, DT, WU>(p, smem, pf, cur, next);
+    while (cur.n > 0) {  // uniform
+        next += G;
+        cur = run_unit<C, DT, WU>(p, smem, pf, cur, next);
+    }
+}
+
+// Resident workgroups per CU for one kernel instance, cached per device.
+template <int C, int DT, bool WU>
+int resident_grid(int device, hipError_t* err)
+{
+    constexpr int kMaxDevices = 64;
+    static int cached[kMaxDevices] = {};
+    static std::mutex mu;
+    if (device < 0 || device >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return 0;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[device] == 0) {
+        using L = Lds<C, DT, WU>;
+        int cus = 0, per_cu = 0;
+        *err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+        if (*err != hipSuccess) return 0;
+        *err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(wy_prepare_kernel<C, DT, WU>), kThreads, L::TOTAL);
+        if (*err != hipSuccess) return 0;
+        cached[device] = (per_cu > 0 ? per_cu : 1) * cus;
+    }
+    return cached[device];
 }
 
 template <int C, int DT, bool WU>
@@ -529,13 +781,19 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     p.hq = a.num_qk_heads;
     p.hv = a.num_v_heads;
     p.num_seqs = a.num_seqs;
-    const int64_t grid = (p.units + 7) / 8 * 8;
     auto kern = wy_prepare_kernel<C, DT, WU>;
     hipError_t e = hipSuccess;
     if (L::TOTAL > 64 * 1024)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+    int device = 0;
+    if (e == hipSuccess) e = hipGetDevice(&device);
+    int resident = 0;
+    if (e == hipSuccess) resident = resident_grid<C, DT, WU>(device, &e);
     if (e == hipSuccess) {
+        int64_t grid = (p.units + 7) / 8 * 8;
+        const int64_t cap = static_cast<int64_t>(resident) / 8 * 8;
+        if (cap >= 8 && grid > cap) grid = cap;
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), L::TOTAL,
                            stream, p);
         e = hipGetLastError();
