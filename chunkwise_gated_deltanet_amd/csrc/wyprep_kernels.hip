@@ -59,6 +59,11 @@ constexpr int kD = 128;        // head dim of k and v
 constexpr int kThreads = 256;  // four wave64s
 constexpr int kWaves = kThreads / 64;
 constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bounds checked
+// Cache policy of the streaming loads and stores: nt (non-temporal).  Every byte of K, V,
+// T, W and U is touched once per launch (K once per value head of its group, by units that
+// run side by side on one XCD), so keeping these lines in L2 / MALL only evicts useful ones.
+// Measured on the C = 64 workload: 41 us with the default policy, 34 us with nt.
+constexpr int kStream = 2;
 
 struct Params {
     const void* k;
@@ -204,7 +209,7 @@ struct Prefetch {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int q = tid + it * kThreads;
-            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q / CPR) * kstride + (q % CPR) * 16, 0, 0);
+            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q / CPR) * kstride + (q % CPR) * 16, 0, kStream);
         }
         const __amdgpu_buffer_rsrc_t br =
             rsrc(p.beta + u.tok0 * p.hv + u.hv, ((u.n - 1) * p.hv + 1) * 4);
@@ -219,7 +224,7 @@ struct Prefetch {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int q = tid + it * kThreads;
-                v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, (q / CPR) * vstride + (q % CPR) * 16, 0, 0);
+                v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, (q / CPR) * vstride + (q % CPR) * 16, 0, kStream);
             }
         }
     }
@@ -489,7 +494,7 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
         const int r = q / TCH, c = q % TCH;
         f32x4* chunk = reinterpret_cast<f32x4*>(Ts + r * TROW + 4 * c);
         const f32x4 val = *chunk;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, kStream);
         if constexpr (PACK) {
             const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 4 * c);
             bf16x4 h, l;
@@ -520,7 +525,7 @@ __device__ void store_rows(const unsigned char* src, void* out, const Unit& u, i
         const int q = tid + it * kThreads;
         const int r = q / CPR, c16 = q % CPR;
         const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * (KROW * ESZ) + c16 * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(val, r_out, r * rstride + c16 * 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(val, r_out, r * rstride + c16 * 16, 0, kStream);
     }
 }
 

@@ -19,7 +19,7 @@
  *     W = T diag(beta) K,  U = T diag(beta) V
  * All arithmetic is IEEE double; inputs are decoded exactly from the caller's bf16 / fp32 data.
  *
- * Conventions (readings of the pages; each one is listed in the design notes):
+ * Conventions (readings of the pages where they leave a choice open):
  *   - Token-major layouts as in [QLA] usage: k [B,T,Hq,dk], v [B,T,Hv,dv], beta [B,T,Hv].
  *   - Value head h reads key head h / (Hv/Hq) (contiguous groups).
  *   - With cu_seqlens (B must be 1) chunks restart at every sequence start; the last chunk of
