@@ -102,6 +102,8 @@ def main(argv=None):
                     help="seeded workload index (2 = the headline C=64 workload)")
     ap.add_argument("--chunk-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each timed step from Python instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
@@ -159,44 +161,67 @@ def main(argv=None):
                       0 if w.dtype == "bf16" else 1)
     import ctypes
     pprob = ctypes.byref(prob)
-    cu_ptr = None if cu is None else cu.data_ptr()
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    calls = [(s["k"].data_ptr(), s["v"].data_ptr(), s["beta"].data_ptr(), s["T"].data_ptr(),
-              s["W"].data_ptr(), s["U"].data_ptr()) for s in sets]
+    calls = [tuple(ctypes.c_void_p(t.data_ptr()) for t in
+                   (s["k"], s["v"], s["beta"], s["T"], s["W"], s["U"])) for s in sets]
+    cu_ptr = ctypes.c_void_p(None if cu is None else cu.data_ptr())
 
-    def step(i):
+    def step(i, sp):
         kp, vp, bp, tp, wp, up = calls[i % nsets]
-        st = lib.wyp_wy_prepare(pprob, kp, vp, bp, cu_ptr, tp, wp, up, sptr)
+        st = lib.wyp_wy_prepare(pprob, kp, vp, bp, cu_ptr, tp, wp, up, sp)
         if st != 0:
             raise RuntimeError(lib.wyp_last_error().decode())
 
     for i in range(args.warmup):
-        step(i)
+        step(i, sptr)
     torch.cuda.synchronize(dev)
 
-    # Timed region: exactly `steps` back-to-back launches, one event pair around them on the
-    # launch stream (an event pair per launch would add its own few microseconds to each).
+    # The K launches of the timed region are captured once into a HIP graph (unless --eager):
+    # one host call then submits all of them, so the host's per-launch cost (ctypes, argument
+    # checks, hipLaunchKernel) cannot leave the GPU idle between these ~30 us kernels.
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream(dev)):
+            csp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+            for i in range(args.steps):
+                step(i, csp)
+        graph.replay()  # untimed: the first replay also uploads the graph
+        torch.cuda.synchronize(dev)
+
+    # Timed region: exactly `steps` launches, one event pair around them on the launch stream
+    # (an event pair per launch would add its own few microseconds to each).
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i, sptr)
     e1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = e0.elapsed_time(e1) * 1e-3 / args.steps  # seconds per launch, gaps included
 
-    # Diagnostic only (after the timed region): spread of single launches, each between its
-    # own pair of events, so every figure carries one event pair's overhead.
+    # The graph did the work: the last buffer set it wrote equals a fresh eager launch.
+    last = (args.steps - 1) % nsets
+    ref = {n: sets[last][n].clone() for n in ("T", "W", "U")}
+    step(last, sptr)
+    torch.cuda.synchronize(dev)
+    replay_ok = all(torch.equal(ref[n], sets[last][n]) for n in ref)
+
+    # Diagnostic only (after the timed region): spread of single eager launches, each between
+    # its own pair of events, so every figure carries one event pair's overhead.
     nd = min(args.steps, 50)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(nd)]
     for i in range(nd):
         ev[i][0].record(stream)
-        step(i)
+        step(i, sptr)
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
@@ -219,7 +244,9 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": B, "seqlen": T, "num_qk_heads": Hq,
                    "num_v_heads": Hv, "head_dim": dk, "chunk_size": C,
                    "units_per_step": units, "tokens_per_step": tokens,
-                   "rotated_buffer_sets": nsets},
+                   "rotated_buffer_sets": nsets,
+                   "launch": "eager" if graph is None else "hip graph of the timed launches",
+                   "replay_matches_eager": replay_ok},
         "tokens_per_s": tokens / (ms_per_step * 1e-3),
         "kernel_us": {"mean": kern_avg * 1e6,
                       "single_launch_p10": float(np.percentile(durs, 10)) * 1e6,

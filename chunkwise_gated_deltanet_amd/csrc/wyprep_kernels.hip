@@ -59,10 +59,12 @@ constexpr int kD = 128;        // head dim of k and v
 constexpr int kThreads = 256;  // four wave64s
 constexpr int kWaves = kThreads / 64;
 constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bounds checked
-// Cache policy of the streaming loads and stores: nt (non-temporal).  Every byte of K, V,
-// T, W and U is touched once per launch (K once per value head of its group, by units that
-// run side by side on one XCD), so keeping these lines in L2 / MALL only evicts useful ones.
-// Measured on the C = 64 workload: 41 us with the default policy, 34 us with nt.
+// Cache policy of the streaming loads and stores: nt (non-temporal).  V, beta, T, W and U
+// are touched once per launch, so keeping their lines in L2 / MALL only evicts useful ones
+// (B=1 T=8192 H=16 C=64: 41 us per launch with the default policy, 33 us with nt).  K keeps
+// the default policy: with grouped value heads every key row is read once per value head of
+// its group, by units running side by side on one XCD, and those re-reads hit in L2 (8
+// packed sequences, Hq=16 Hv=64 C=64: 1.32 ms with nt K loads, 1.11 ms without).
 constexpr int kStream = 2;
 
 struct Params {
@@ -209,7 +211,7 @@ struct Prefetch {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int q = tid + it * kThreads;
-            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q / CPR) * kstride + (q % CPR) * 16, 0, kStream);
+            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q / CPR) * kstride + (q % CPR) * 16, 0, 0);
         }
         const __amdgpu_buffer_rsrc_t br =
             rsrc(p.beta + u.tok0 * p.hv + u.hv, ((u.n - 1) * p.hv + 1) * 4);
@@ -743,7 +745,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     }
 }
 
-// Resident workgroups per CU for one kernel instance, cached per device.
+// Resident workgroups (occupancy x CUs) for one kernel instance, cached per device.  The first
+// call on a device also raises the instance's dynamic LDS limit where its plan needs more than
+// the default 64 KiB, so later launches (including ones under stream capture) make no
+// attribute calls.
 template <int C, int DT, bool WU>
 int resident_grid(int device, hipError_t* err)
 {
@@ -757,11 +762,15 @@ int resident_grid(int device, hipError_t* err)
     std::lock_guard<std::mutex> lock(mu);
     if (cached[device] == 0) {
         using L = Lds<C, DT, WU>;
+        const void* kern = reinterpret_cast<const void*>(wy_prepare_kernel<C, DT, WU>);
+        if (L::TOTAL > 64 * 1024) {
+            *err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+            if (*err != hipSuccess) return 0;
+        }
         int cus = 0, per_cu = 0;
         *err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
         if (*err != hipSuccess) return 0;
-        *err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(wy_prepare_kernel<C, DT, WU>), kThreads, L::TOTAL);
+        *err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, L::TOTAL);
         if (*err != hipSuccess) return 0;
         cached[device] = (per_cu > 0 ? per_cu : 1) * cus;
     }
@@ -787,12 +796,8 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     p.hv = a.num_v_heads;
     p.num_seqs = a.num_seqs;
     auto kern = wy_prepare_kernel<C, DT, WU>;
-    hipError_t e = hipSuccess;
-    if (L::TOTAL > 64 * 1024)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
     int device = 0;
-    if (e == hipSuccess) e = hipGetDevice(&device);
+    hipError_t e = hipGetDevice(&device);
     int resident = 0;
     if (e == hipSuccess) resident = resident_grid<C, DT, WU>(device, &e);
     if (e == hipSuccess) {
