@@ -87,13 +87,40 @@ struct Params {
 // has its own region: it waits in registers until the T tile has been read for the last time
 // and then takes its place, so one unit needs K + max(T, V) bytes (34 KiB at C = 64: four
 // workgroups per CU).
+// Placement of the fp32 C x C tile (A, then T, then T') in LDS; off(r, c) is the float offset
+// of entry (r, c).  Up to C = 64 it is row-major with rows padded by 4 floats.  At C = 128 only
+// the 36 lower 16x16 tiles (diagonal ones included) are kept, tile (I, J) at position
+// I(I+1)/2 + J, each 16 rows of 20 floats: 46 KB instead of 68 KB, so two workgroups share a
+// CU.  Every access below stays inside one 16x16 tile, and with either padding the rows of a
+// 16-lane group start on different banks.
+template <int C, bool TILED = (C > 64)>
+struct TLayout {
+    static constexpr bool kTiled = false;
+    static constexpr int RS = C + 4;  // floats per row
+    static constexpr int BYTES = C * RS * 4;
+    __device__ static constexpr int off(int r, int c) { return r * RS + c; }
+};
+
+template <int C>
+struct TLayout<C, true> {
+    static constexpr bool kTiled = true;
+    static constexpr int RS = 20;  // floats per tile row
+    static constexpr int TILE = 16 * RS;
+    static constexpr int NB = C / 16;
+    static constexpr int BYTES = NB * (NB + 1) / 2 * TILE * 4;
+    __device__ static constexpr int off(int r, int c)
+    {
+        return ((r >> 4) * ((r >> 4) + 1) / 2 + (c >> 4)) * TILE + (r & 15) * RS + (c & 15);
+    }
+};
+
 template <int C, int DT, bool WU>
 struct Lds {
     static constexpr int ESZ = DT == 0 ? 2 : 4;
     static constexpr int KROW = kD + 16 / ESZ;   // elements per staged K / V row
     static constexpr int KBYTES = C * KROW * ESZ;
-    static constexpr int TROW = C + 4;           // floats per T row
-    static constexpr int TBYTES = C * TROW * 4;
+    using TL = TLayout<C>;
+    static constexpr int TBYTES = TL::BYTES;
     static constexpr int TVBYTES = WU && KBYTES > TBYTES ? KBYTES : TBYTES;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_T = KBYTES;         // T, later V and the U staging
@@ -306,7 +333,7 @@ struct GramFrags {
     }
 };
 
-template <int C, int DT, int KROW, int TROW>
+template <int C, int DT, int KROW, class TL>
 __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
     constexpr int NB = C / 16;
@@ -343,7 +370,7 @@ __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, in
             // i < j, is beta_j G[j][i] = L[j][i]); the substitution reads columns of L there
             // and overwrites it with zeros.
             const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
-            Ts[i * TROW + j] = (i > j) ? bet[r] * acc[r] : (i == j ? 1.f : bcol * acc[r]);
+            Ts[TL::off(i, j)] = (i > j) ? bet[r] * acc[r] : (i == j ? 1.f : bcol * acc[r]);
         }
         if (NBUF == 2) {
             I = In;
@@ -353,18 +380,21 @@ __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, in
         }
     }
     // strictly upper tiles (I < J), enumerated row-major, also dealt round-robin to waves
-    constexpr int NUP = NB * (NB - 1) / 2;
+    // (the tile-packed layout has none)
+    if constexpr (!TL::kTiled) {
+        constexpr int NUP = NB * (NB - 1) / 2;
 #pragma unroll
-    for (int tt = 0; tt < (NUP + kWaves - 1) / kWaves; ++tt) {
-        const int t = tt * kWaves + wave;
-        if (t >= NUP) break;
-        int Iu = 0, rem = t;
-        while (rem >= NB - 1 - Iu) {
-            rem -= NB - 1 - Iu;
-            ++Iu;
+        for (int tt = 0; tt < (NUP + kWaves - 1) / kWaves; ++tt) {
+            const int t = tt * kWaves + wave;
+            if (t >= NUP) break;
+            int Iu = 0, rem = t;
+            while (rem >= NB - 1 - Iu) {
+                rem -= NB - 1 - Iu;
+                ++Iu;
+            }
+            const int Ju = Iu + 1 + rem;
+            *reinterpret_cast<f32x4*>(Ts + TL::off(16 * Iu + lr, 16 * Ju + 4 * lg)) = zero4();
         }
-        const int Ju = Iu + 1 + rem;
-        *reinterpret_cast<f32x4*>(Ts + (16 * Iu + lr) * TROW + 16 * Ju + 4 * lg) = zero4();
     }
 }
 
@@ -374,7 +404,7 @@ __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, in
 // read from row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the
 // block read the same row (an LDS broadcast).  Row J's upper part is read before any lane
 // overwrites it with its X column.
-template <int J, int TROW>
+template <int J, int RS>
 __device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
 {
     const float x = (J == i) ? 1.f : acc[J];
@@ -382,18 +412,18 @@ __device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
     if constexpr (J < 15) {
 #pragma unroll
         for (int c4 = (J + 1) / 4; c4 < 4; ++c4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + J * TROW + 4 * c4);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + J * RS + 4 * c4);
             lrow[4 * c4 + 0] = v[0];
             lrow[4 * c4 + 1] = v[1];
             lrow[4 * c4 + 2] = v[2];
             lrow[4 * c4 + 3] = v[3];
         }
     }
-    blk[J * TROW + i] = x;
+    blk[J * RS + i] = x;
     if constexpr (J < 15) {
 #pragma unroll
         for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-lrow[k], x, acc[k]);
-        substitution_step<J + 1, TROW>(acc, i, blk);
+        substitution_step<J + 1, RS>(acc, i, blk);
     }
 }
 
@@ -401,23 +431,23 @@ __device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
 // column i of X_b = L_b^{-1} in registers, right-looking: after X[j][i] is final, every later
 // row k takes its share L[k][j] X[j][i], so one multiply-add per step sits on the dependency
 // chain.  Blocks 0-3 run on wave 0, blocks 4-7 on wave 1.
-template <int C, int TROW>
+template <int C, class TL>
 __device__ void invert_diagonal_blocks(float* Ts, int tid)
 {
     constexpr int NB = C / 16;
     if (tid >= NB * 16) return;
     const int b = tid >> 4, i = tid & 15;
-    float* blk = Ts + 16 * b * TROW + 16 * b;
+    float* blk = Ts + TL::off(16 * b, 16 * b);
     float acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] = 0.f;
-    substitution_step<0, TROW>(acc, i, blk);
+    substitution_step<0, TL::RS>(acc, i, blk);
 }
 
 // a6, one level: block size S.  Pair p covers rows/cols [2Sp, 2Sp + 2S); its sub-diagonal
 // block L10 (rows 2Sp+S.., cols 2Sp..) is replaced by X10 = -X11 (L10 X00).  Wave w owns pair
 // w / (S/16) and 16-column tile w % (S/16) of X10.
-template <int C, int S, int TROW>
+template <int C, int S, class TL>
 __device__ void coupling_level(float* Ts, int tid)
 {
     constexpr int TS = S / 16;
@@ -432,20 +462,22 @@ __device__ void coupling_level(float* Ts, int tid)
     f32x4 res[TS];
     if (active) {
         // tmp[:, nc] = L10 X00[:, nc].  X00 is lower triangular, so k-tiles kt < nc hold
-        // zeros; they are multiplied anyway, which keeps every operand load branch-free.
+        // zeros.  The row-major layout multiplies them anyway, which keeps every operand load
+        // branch-free; the tile-packed layout does not store them and skips them.
         f32x4 tmp[TS];
 #pragma unroll
         for (int mr = 0; mr < TS; ++mr) tmp[mr] = zero4();
 #pragma unroll
         for (int kt = 0; kt < TS; ++kt) {
+            if (TL::kTiled && kt < nc) continue;  // uniform per wave
             float bq[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                bq[q] = Ts[(base + 16 * kt + 4 * lg + q) * TROW + base + 16 * nc + lr];
+                bq[q] = Ts[TL::off(base + 16 * kt + 4 * lg + q, base + 16 * nc + lr)];
 #pragma unroll
             for (int mr = 0; mr < TS; ++mr) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(
-                    Ts + (base + S + 16 * mr + lr) * TROW + base + 16 * kt + 4 * lg);
+                    Ts + TL::off(base + S + 16 * mr + lr, base + 16 * kt + 4 * lg));
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     tmp[mr] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], bq[q], tmp[mr], 0, 0, 0);
@@ -458,7 +490,7 @@ __device__ void coupling_level(float* Ts, int tid)
 #pragma unroll
             for (int kt = 0; kt <= mr; ++kt) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(
-                    Ts + (base + S + 16 * mr + lr) * TROW + base + S + 16 * kt + 4 * lg);
+                    Ts + TL::off(base + S + 16 * mr + lr, base + S + 16 * kt + 4 * lg));
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], tmp[kt][q], acc, 0, 0, 0);
@@ -472,7 +504,7 @@ __device__ void coupling_level(float* Ts, int tid)
         for (int mr = 0; mr < TS; ++mr)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Ts[(base + S + 16 * mr + 4 * lg + r) * TROW + base + 16 * nc + lr] = res[mr][r];
+                Ts[TL::off(base + S + 16 * mr + 4 * lg + r, base + 16 * nc + lr)] = res[mr][r];
     }
     __syncthreads();
 }
@@ -481,7 +513,7 @@ __device__ void coupling_level(float* Ts, int tid)
 // range and are dropped by the hardware.  With PACK, each thread then overwrites the 16-byte
 // chunk it just stored with T' = T diag(beta) for the W/U products: four bf16 "hi" values
 // followed by four bf16 "lo" values (lo = T' - hi, rounded), i.e. the same bytes per element.
-template <int C, int TROW, bool PACK>
+template <int C, class TL, bool PACK>
 __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, int Hv, int tid)
 {
     constexpr int TCH = C / 4;                 // 16-byte chunks per row
@@ -494,10 +526,13 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
     for (int it = 0; it < NIT; ++it) {
         const int q = tid + it * kThreads;
         const int r = q / TCH, c = q % TCH;
-        f32x4* chunk = reinterpret_cast<f32x4*>(Ts + r * TROW + 4 * c);
-        const f32x4 val = *chunk;
+        // tile-packed layout: chunks right of the diagonal tile are zeros that are not stored
+        const bool upper = TL::kTiled && (c >> 2) > (r >> 4);
+        f32x4* chunk = reinterpret_cast<f32x4*>(Ts + TL::off(r, 4 * c));
+        f32x4 val = zero4();
+        if (!upper) val = *chunk;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, kStream);
-        if constexpr (PACK) {
+        if (PACK && !upper) {
             const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 4 * c);
             bf16x4 h, l;
 #pragma unroll
@@ -588,40 +623,117 @@ __device__ inline void stage_tiles(unsigned char* dst, const bf16x4 (&out)[2][C 
             *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + 4 * c) + 4 * lg) = out[c][mi];
 }
 
+// The same products at C = 128, split by rows: all 36 lower T' blocks would take 144 registers
+// per lane in every wave, so wave w owns row tiles mA = w and mB = NB - 1 - w (nine T' blocks
+// between them, the same count for every wave) across all eight column tiles.  Accumulator
+// element r of lane 16g + c is X[16m + c][16ni + 4g + r] as above.
+template <int C, int KROW>
+__device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA)[C / 16],
+                                     const u32x4 (&tpB)[C / 16], int mA, int mB, int lr, int lg,
+                                     bf16x4 (&out)[C / 16][2])
+{
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int NB = C / 16;
+    const __bf16* base = reinterpret_cast<const __bf16*>(src);
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) {
+        f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+        for (int kt = 0; kt < NB; ++kt) {
+            if (kt > mB) break;  // uniform; mA < mB
+            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
+            const i16x4 kfr = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
+            a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpB[kt][0], tpB[kt][1]}), a1, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpB[kt][2], tpB[kt][3]}), a1, 0, 0, 0);
+            if (kt <= mA) {
+                a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpA[kt][0], tpA[kt][1]}), a0, 0, 0, 0);
+                a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpA[kt][2], tpA[kt][3]}), a0, 0, 0, 0);
+            }
+        }
+        bf16x4 o0, o1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            o0[r] = static_cast<__bf16>(a0[r]);
+            o1[r] = static_cast<__bf16>(a1[r]);
+        }
+        out[ni][0] = o0;
+        out[ni][1] = o1;
+    }
+}
+
+template <int C, int KROW>
+__device__ inline void stage_tiles_rows(unsigned char* dst, const bf16x4 (&out)[C / 16][2], int mA, int mB,
+                                        int lr, int lg)
+{
+    __bf16* d = reinterpret_cast<__bf16*>(dst);
+#pragma unroll
+    for (int ni = 0; ni < C / 16; ++ni) {
+        *reinterpret_cast<bf16x4*>(d + (16 * mA + lr) * KROW + 16 * ni + 4 * lg) = out[ni][0];
+        *reinterpret_cast<bf16x4*>(d + (16 * mB + lr) * KROW + 16 * ni + 4 * lg) = out[ni][1];
+    }
+}
+
 // Every wave first takes its T' chunks (lower-triangular 16x16 blocks) into registers; then V,
 // waiting in registers, takes the T tile's place.  W is staged over K while U is computed.
-template <int C, int KROW, int TROW, class PF>
+template <int C, int KROW, class TL, class PF>
 __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p, const Unit& u, int tid)
 {
     constexpr int NB = C / 16;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    u32x4 tp[NB][NB];
+    if constexpr (NB == 2 * kWaves) {
+        const int mA = wave, mB = NB - 1 - wave;
+        u32x4 tpA[NB], tpB[NB];
 #pragma unroll
-    for (int mi = 0; mi < NB; ++mi)
+        for (int kt = 0; kt < NB; ++kt) {
+            tpA[kt] = u32x4{0u, 0u, 0u, 0u};
+            tpB[kt] = u32x4{0u, 0u, 0u, 0u};
+            if (kt <= mA) tpA[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mA + lr, 16 * kt + 4 * lg));
+            if (kt <= mB) tpB[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mB + lr, 16 * kt + 4 * lg));
+        }
+        __syncthreads();  // the T tile is no longer read: V takes its place
+        unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
+        pf.commit_v(Vraw, tid);
+        __syncthreads();
+        bf16x4 out[NB][2];
+        wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, mA, mB, lr, lg, out);
+        __syncthreads();  // every wave is done reading K: W is staged over it
+        stage_tiles_rows<C, KROW>(Kraw, out, mA, mB, lr, lg);
+        wu_tiles_rows<C, KROW>(Vraw, tpA, tpB, mA, mB, lr, lg, out);
+        __syncthreads();  // every wave is done reading V: U is staged over it
+        stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, lr, lg);
+        __syncthreads();
+        store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
+        store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
+    } else {
+        u32x4 tp[NB][NB];
 #pragma unroll
-        for (int kt = 0; kt <= mi; ++kt)
-            tp[mi][kt] = *reinterpret_cast<const u32x4*>(Ts + (16 * mi + lr) * TROW + 16 * kt + 4 * lg);
-    __syncthreads();  // the T tile is no longer read: V takes its place
-    unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
-    pf.commit_v(Vraw, tid);
-    __syncthreads();
+        for (int mi = 0; mi < NB; ++mi)
+#pragma unroll
+            for (int kt = 0; kt <= mi; ++kt)
+                tp[mi][kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mi + lr, 16 * kt + 4 * lg));
+        __syncthreads();  // the T tile is no longer read: V takes its place
+        unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
+        pf.commit_v(Vraw, tid);
+        __syncthreads();
 
-    bf16x4 out[2][NB];
-    wu_tiles<C, KROW>(Kraw, tp, wave, lr, lg, out);
-    __syncthreads();  // every wave is done reading K: W is staged over it
-    stage_tiles<C, KROW>(Kraw, out, wave, lr, lg);
-    wu_tiles<C, KROW>(Vraw, tp, wave, lr, lg, out);
-    __syncthreads();  // every wave is done reading V: U is staged over it
-    stage_tiles<C, KROW>(Vraw, out, wave, lr, lg);
-    __syncthreads();
-    store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
-    store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
+        bf16x4 out[2][NB];
+        wu_tiles<C, KROW>(Kraw, tp, wave, lr, lg, out);
+        __syncthreads();  // every wave is done reading K: W is staged over it
+        stage_tiles<C, KROW>(Kraw, out, wave, lr, lg);
+        wu_tiles<C, KROW>(Vraw, tp, wave, lr, lg, out);
+        __syncthreads();  // every wave is done reading V: U is staged over it
+        stage_tiles<C, KROW>(Vraw, out, wave, lr, lg);
+        __syncthreads();
+        store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
+        store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
+    }
 }
 
 // a8 (fp32 inputs): the same transposed products on fp32 MFMA, T' = T diag(beta) kept in fp32
 // registers before V takes the T tile's place.
-template <int C, int KROW, int TROW, class PF>
+template <int C, int KROW, class TL, class PF>
 __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, const Params& p,
                        const Unit& u, int tid)
 {
@@ -633,7 +745,7 @@ __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, 
     for (int mi = 0; mi < NB; ++mi)
 #pragma unroll
         for (int kt = 0; kt <= mi; ++kt) {
-            const f32x4 t = *reinterpret_cast<const f32x4*>(Ts + (16 * mi + lr) * TROW + 16 * kt + 4 * lg);
+            const f32x4 t = *reinterpret_cast<const f32x4*>(Ts + TL::off(16 * mi + lr, 16 * kt + 4 * lg));
             const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 16 * kt + 4 * lg);
             tfr[mi][kt] = t * b;
         }
@@ -700,20 +812,21 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     const Unit nxt = map_unit<C>(p, info, next, tid);
     if (nxt.n > 0) pf.issue_k(p, nxt, tid);
 
-    form_a<C, DT, L::KROW, L::TROW>(Kraw, Ts, bs, tid);
+    using TL = typename L::TL;
+    form_a<C, DT, L::KROW, TL>(Kraw, Ts, bs, tid);
     __syncthreads();
-    invert_diagonal_blocks<C, L::TROW>(Ts, tid);
+    invert_diagonal_blocks<C, TL>(Ts, tid);
     __syncthreads();
-    if constexpr (C >= 32) coupling_level<C, 16, L::TROW>(Ts, tid);
-    if constexpr (C >= 64) coupling_level<C, 32, L::TROW>(Ts, tid);
-    if constexpr (C >= 128) coupling_level<C, 64, L::TROW>(Ts, tid);
-    store_t<C, L::TROW, DT == 0 && WU>(Ts, bs, p.T, cur, p.hv, tid);
+    if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
+    if constexpr (C >= 64) coupling_level<C, 32, TL>(Ts, tid);
+    if constexpr (C >= 128) coupling_level<C, 64, TL>(Ts, tid);
+    store_t<C, TL, DT == 0 && WU>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
         __syncthreads();  // T (packed T' for bf16) of all threads is in place
         if constexpr (DT == 0)
-            wu_bf16<C, L::KROW, L::TROW>(Kraw, Ts, pf, p, cur, tid);
+            wu_bf16<C, L::KROW, TL>(Kraw, Ts, pf, p, cur, tid);
         else
-            wu_f32<C, L::KROW, L::TROW>(Kraw, Ts, bs, pf, p, cur, tid);
+            wu_f32<C, L::KROW, TL>(Kraw, Ts, bs, pf, p, cur, tid);
     }
     __syncthreads();  // LDS is rewritten by the next unit
     return nxt;
