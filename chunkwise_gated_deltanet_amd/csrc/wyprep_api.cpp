@@ -46,8 +46,6 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
     if (p->chunk_size != 32 && p->chunk_size != 64 && p->chunk_size != 128)
         return fail(WYP_ERR_UNSUPPORTED, "chunk_size must be 32, 64 or 128 (got %d)",
                     p->chunk_size);
-    if (want_wu && p->kv_dtype == WYP_F32 && p->chunk_size == 128)
-        return fail(WYP_ERR_UNSUPPORTED, "fp32 k/v with C = 128 is built for kkt_solve only");
     if (cu) {
         if (p->batch != 1)
             return fail(WYP_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)", p->batch);

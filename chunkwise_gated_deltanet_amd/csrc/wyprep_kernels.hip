@@ -935,13 +935,7 @@ int launch_c(const LaunchArgs& a, hipStream_t s, char* msg, int len)
     switch (a.chunk_size) {
     case 32: return launch_t<32, DT, WU>(a, s, msg, len);
     case 64: return launch_t<64, DT, WU>(a, s, msg, len);
-    default:
-        if constexpr (DT == 1 && WU) {
-            std::snprintf(msg, len, "fp32 wy_prepare at C=128 is not built");
-            return static_cast<int>(hipErrorInvalidValue);
-        } else {
-            return launch_t<128, DT, WU>(a, s, msg, len);
-        }
+    default: return launch_t<128, DT, WU>(a, s, msg, len);
     }
 }
 

@@ -49,9 +49,8 @@
  * synchronisation): cu[0] = 0, non-decreasing, cu[N] = T.
  *
  * Supported: dk = dv = 128; C in {32, 64, 128}; kv_dtype WYP_BF16 (bf16 MFMA, fp32
- * accumulation) or WYP_F32 (fp32 MFMA; wyp_wy_prepare at C = 32 or 64 only, since the fp32
- * K, V and T tiles of C = 128 exceed one workgroup's 160 KiB of LDS); Hv a multiple of Hq.
- * Anything else returns WYP_ERR_UNSUPPORTED.
+ * accumulation) or WYP_F32 (fp32 MFMA throughout); Hv a multiple of Hq.  Anything else
+ * returns WYP_ERR_UNSUPPORTED.
  */
 #ifndef WYPREP_H
 #define WYPREP_H

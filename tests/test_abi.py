@@ -66,7 +66,7 @@ def call_wy(lib, p, k=FAKE, v=FAKE, beta=FAKE, cu=None, T=FAKE, W=FAKE, U=FAKE):
     (dict(batch=0), 1, "batch"),
     (dict(seqlen=-1), 1, "seqlen"),
     (dict(kv_dtype=7), 1, "kv_dtype"),
-    (dict(kv_dtype=1, chunk_size=128), 2, "C = 128"),
+    (dict(kv_dtype=1, chunk_size=96), 2, "chunk_size"),
 ])
 def test_rejects_bad_problem(lib, kw, code, needle):
     assert call_wy(lib, good(**kw)) == code

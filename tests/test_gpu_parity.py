@@ -33,6 +33,8 @@ SMALL = {
                             seed=7, seqlens=[127, 129, 1, 300, 17]),
     "fp32_C64": dict(batch=1, seqlen=200, num_qk_heads=2, num_v_heads=2, chunk_size=64,
                      dtype="f32", seed=8),
+    "fp32_packed_gva_C128": dict(batch=1, seqlen=0, num_qk_heads=1, num_v_heads=2,
+                                 chunk_size=128, dtype="f32", seed=9, seqlens=[300, 1, 128]),
 }
 
 
@@ -73,12 +75,13 @@ def test_kkt_solve_matches_wy_prepare(gpu):
 
 
 # Full sizes, in the launch configuration the benchmark times: sampled units against the
-# oracle, plus properties checked on every output entry.
-FULL = [(1, None), (2, None), (3, 32), (3, 64), (3, 128), (4, None), (5, None)]
+# oracle, plus properties checked on every output entry.  Every workload runs at C = 32, 64
+# and 128 (its own C among them).
+FULL = [(i, c) for i in (1, 2, 3, 4, 5) for c in (32, 64, 128)]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("idx,C", FULL, ids=[f"w{i}_C{c or 'default'}" for i, c in FULL])
+@pytest.mark.parametrize("idx,C", FULL, ids=[f"w{i}_C{c}" for i, c in FULL])
 def test_wy_prepare_full_size(idx, C, gpu):
     import torch
     w = synth.workload(idx, chunk_size=C)
