@@ -30,12 +30,16 @@ METRIC = "chunks/s (tokens/s) for kkt_solve+W/U at C=64; achieved HBM GB/s vs pe
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 768 << 20  # rotated footprint: three times the Infinity Cache
 KERNEL_SOURCE = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc", "wyprep_kernels.hip")
-COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "wy_prepare_bf16_c64_b1t8192h16_counters.md")
+ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve"}
 
 
-def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz):
-    """K read once per key head, V and beta read once, T (fp32), W and U written once."""
-    per_token = hq * dk * esz + hv * (dv * esz + 4 + 4 * C + dk * esz + dv * esz)
+def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy"):
+    """K read once per key head, beta read once; wy: V read, T (fp32), W and U written once;
+    wu: the same without T; kkt: T only."""
+    if entry == "kkt":
+        return tokens * (hq * dk * esz + hv * (4 + 4 * C))
+    t_bytes = 4 * C if entry == "wy" else 0
+    per_token = hq * dk * esz + hv * (dv * esz + 4 + t_bytes + dk * esz + dv * esz)
     return tokens * per_token
 
 
@@ -44,12 +48,25 @@ def kernel_source_sha():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source; else None."""
-    if not os.path.exists(COUNTER_SUMMARY):
+def profile_name(entry, w, batch, seqlen, num_seqs):
+    """Name of the profiles/ summaries for one entry point and workload, e.g.
+    wy_prepare_bf16_c64_b1t8192h16 or wy_prepare_bf16_c64_packed8_hq16hv64."""
+    if num_seqs:
+        shape = f"packed{num_seqs}_hq{w.num_qk_heads}hv{w.num_v_heads}"
+    elif w.num_qk_heads == w.num_v_heads:
+        shape = f"b{batch}t{seqlen}h{w.num_v_heads}"
+    else:
+        shape = f"b{batch}t{seqlen}hq{w.num_qk_heads}hv{w.num_v_heads}"
+    return f"{ENTRY_NAMES[entry]}_{w.dtype}_c{w.chunk_size}_{shape}"
+
+
+def counter_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this entry point
+    and workload, if there is one and it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", name + "_counters.md")
+    if not os.path.exists(path):
         return None
-    text = open(COUNTER_SUMMARY).read()
+    text = open(path).read()
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     if not m_b or not m_h or m_h.group(1) != kernel_source_sha():
@@ -96,12 +113,18 @@ def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--ramp-ms", type=float, default=100.0,
+                    help="untimed launches for at least this long before the warm-up steps, so "
+                         "the GPU clocks are steady (0 = none)")
     ap.add_argument("--workload", type=int, default=2,
                     help="seeded workload index (2 = the headline C=64 workload)")
     ap.add_argument("--chunk-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry", choices=("wy", "wu", "kkt"), default="wy",
+                    help="wy: wyp_wy_prepare (T, W, U; the headline); wu: wyp_wu_prepare "
+                         "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only)")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -140,7 +163,7 @@ def main(argv=None):
         nchunks = B * ((T + C - 1) // C)
     units = nchunks * Hv
     tokens = B * T
-    alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz)
+    alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, args.entry)
     nsets = max(1, math.ceil(ROTATE_BYTES / alg))  # every byte of a step is touched once
 
     def dev_tensor(a, dt):
@@ -169,10 +192,24 @@ def main(argv=None):
 
     def step(i, sp):
         kp, vp, bp, tp, wp, up = calls[i % nsets]
-        st = lib.wyp_wy_prepare(pprob, kp, vp, bp, cu_ptr, tp, wp, up, sp)
+        if args.entry == "wy":
+            st = lib.wyp_wy_prepare(pprob, kp, vp, bp, cu_ptr, tp, wp, up, sp)
+        elif args.entry == "wu":
+            st = lib.wyp_wu_prepare(pprob, kp, vp, bp, cu_ptr, wp, up, sp)
+        else:
+            st = lib.wyp_kkt_solve(pprob, kp, bp, cu_ptr, tp, sp)
         if st != 0:
             raise RuntimeError(lib.wyp_last_error().decode())
 
+    # Clock ramp: the GPU needs ~20 ms of sustained work to reach steady clocks (measured on
+    # this kernel: 43 us per launch in the first 4 ms, 30 us from 20 ms on).  The step runs
+    # untimed for at least --ramp-ms before the counted warm-up steps; the count is reported.
+    ramp_launches, t_end = 0, time.perf_counter() + args.ramp_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            step(ramp_launches, sptr)
+            ramp_launches += 1
+        torch.cuda.synchronize(dev)
     for i in range(args.warmup):
         step(i, sptr)
     torch.cuda.synchronize(dev)
@@ -227,7 +264,8 @@ def main(argv=None):
     durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
     achieved = alg / kern_avg / 1e9
-    traffic = counter_traffic()
+    pname = profile_name(args.entry, w, B, T, 0 if cu is None else cu.numel() - 1)
+    traffic = counter_traffic(pname)
     out = {
         "metric": METRIC,
         "value": units / (ms_per_step * 1e-3),
@@ -241,11 +279,13 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "seqlen": T, "num_qk_heads": Hq,
+        "config": {"workload": w.name, "entry": ENTRY_NAMES[args.entry],
+                   "batch": B, "seqlen": T, "num_qk_heads": Hq,
                    "num_v_heads": Hv, "head_dim": dk, "chunk_size": C,
                    "units_per_step": units, "tokens_per_step": tokens,
                    "rotated_buffer_sets": nsets,
                    "launch": "eager" if graph is None else "hip graph of the timed launches",
+                   "clock_ramp_launches": ramp_launches,
                    "replay_matches_eager": replay_ok},
         "tokens_per_s": tokens / (ms_per_step * 1e-3),
         "kernel_us": {"mean": kern_avg * 1e6,

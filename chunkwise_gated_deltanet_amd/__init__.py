@@ -15,8 +15,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["wy_prepare", "kkt_solve", "wyp_wy_prepare", "wyp_kkt_solve", "load_library",
-           "Problem", "LIB_PATH", "WyprepError"]
+__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "wyp_wy_prepare", "wyp_kkt_solve",
+           "wyp_wu_prepare", "load_library", "Problem", "LIB_PATH", "WyprepError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.so")
 
@@ -64,6 +64,8 @@ def load_library(path: str | None = None):
     lib.wyp_kkt_solve.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P]
     lib.wyp_wy_prepare.restype = ctypes.c_int32
     lib.wyp_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.wyp_wu_prepare.restype = ctypes.c_int32
+    lib.wyp_wu_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P]
     if path is None:
         _lib = lib
     return lib
@@ -172,6 +174,23 @@ def wy_prepare(k, v, beta, chunk_size, cu_seqlens=None, T_out=None, W_out=None, 
     return T_out, W_out, U_out
 
 
+def wu_prepare(k, v, beta, chunk_size, cu_seqlens=None, W_out=None, U_out=None):
+    """(W, U) without T in HBM: the same values as wy_prepare's W and U; see wyp_wu_prepare."""
+    import torch
+    lib = load_library()
+    p = _problem(k, beta, chunk_size, cu_seqlens, v=v)
+    B, T = k.shape[:2]
+    Hv = p.num_v_heads
+    W_out = _out(W_out, (B, T, Hv, p.head_dim_k), k.dtype, k.device, "W_out")
+    U_out = _out(U_out, (B, T, Hv, p.head_dim_v), k.dtype, k.device, "U_out")
+    st = lib.wyp_wu_prepare(ctypes.byref(p), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                            cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                            W_out.data_ptr(), U_out.data_ptr(), _stream(k.device))
+    _check(lib, st)
+    return W_out, U_out
+
+
 # The C-ABI names, for callers that mirror the header.
 wyp_kkt_solve = kkt_solve
 wyp_wy_prepare = wy_prepare
+wyp_wu_prepare = wu_prepare

@@ -23,10 +23,10 @@ wyp_status fail(wyp_status st, const char* fmt, ...)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Host-side checks shared by both entry points.  Touches no HIP API.
+// Host-side checks shared by the entry points.  Touches no HIP API.
 wyp_status validate(const wyp_problem* p, const void* k, const void* v, const float* beta,
                     const int32_t* cu, const float* T, const void* W, const void* U,
-                    bool want_wu, wyp::LaunchArgs* out, bool* empty)
+                    bool want_t, bool want_wu, wyp::LaunchArgs* out, bool* empty)
 {
     *empty = false;
     if (!p) return fail(WYP_ERR_INVALID_ARGUMENT, "problem is NULL");
@@ -61,11 +61,12 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
         *empty = true;
         return WYP_OK;
     }
-    if (!k || !beta || !T) return fail(WYP_ERR_INVALID_ARGUMENT, "k, beta and T_out must be non-NULL");
+    if (!k || !beta) return fail(WYP_ERR_INVALID_ARGUMENT, "k and beta must be non-NULL");
+    if (want_t && !T) return fail(WYP_ERR_INVALID_ARGUMENT, "T_out must be non-NULL");
     if (want_wu && (!v || !W || !U))
         return fail(WYP_ERR_INVALID_ARGUMENT, "v, W_out and U_out must be non-NULL");
-    if (!aligned(k, 16) || !aligned(T, 16) || (want_wu && (!aligned(v, 16) || !aligned(W, 16) ||
-                                                           !aligned(U, 16))))
+    if (!aligned(k, 16) || (want_t && !aligned(T, 16)) ||
+        (want_wu && (!aligned(v, 16) || !aligned(W, 16) || !aligned(U, 16))))
         return fail(WYP_ERR_INVALID_ARGUMENT, "k, v, T_out, W_out and U_out must be 16-byte aligned");
     if (!aligned(beta, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "beta is not 4-byte aligned");
 
@@ -82,7 +83,7 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
     out->v = want_wu ? v : nullptr;
     out->beta = beta;
     out->cu_seqlens = cu;
-    out->T = const_cast<float*>(T);
+    out->T = want_t ? const_cast<float*>(T) : nullptr;
     out->W = want_wu ? const_cast<void*>(W) : nullptr;
     out->U = want_wu ? const_cast<void*>(U) : nullptr;
     out->batch = p->batch;
@@ -97,12 +98,13 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
 }
 
 wyp_status run(const wyp_problem* p, const void* k, const void* v, const float* beta,
-               const int32_t* cu, float* T, void* W, void* U, bool want_wu, void* stream)
+               const int32_t* cu, float* T, void* W, void* U, bool want_t, bool want_wu,
+               void* stream)
 {
     g_last_error[0] = '\0';
     wyp::LaunchArgs args{};
     bool empty = false;
-    const wyp_status st = validate(p, k, v, beta, cu, T, W, U, want_wu, &args, &empty);
+    const wyp_status st = validate(p, k, v, beta, cu, T, W, U, want_t, want_wu, &args, &empty);
     if (st != WYP_OK || empty) return st;
     char msg[256] = "";
     if (wyp::launch(args, stream, msg, sizeof msg) != 0)
@@ -132,14 +134,21 @@ const char* wyp_last_error(void) { return g_last_error; }
 wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* beta,
                          const int32_t* cu_seqlens, float* T_out, void* stream)
 {
-    return run(problem, k, nullptr, beta, cu_seqlens, T_out, nullptr, nullptr, false, stream);
+    return run(problem, k, nullptr, beta, cu_seqlens, T_out, nullptr, nullptr, true, false, stream);
 }
 
 wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void* v,
                           const float* beta, const int32_t* cu_seqlens, float* T_out,
                           void* W_out, void* U_out, void* stream)
 {
-    return run(problem, k, v, beta, cu_seqlens, T_out, W_out, U_out, true, stream);
+    return run(problem, k, v, beta, cu_seqlens, T_out, W_out, U_out, true, true, stream);
+}
+
+wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void* v,
+                          const float* beta, const int32_t* cu_seqlens, void* W_out, void* U_out,
+                          void* stream)
+{
+    return run(problem, k, v, beta, cu_seqlens, nullptr, W_out, U_out, false, true, stream);
 }
 
 }  // extern "C"

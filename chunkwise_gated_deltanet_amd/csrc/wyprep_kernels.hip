@@ -67,6 +67,10 @@ constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bo
 // packed sequences, Hq=16 Hv=64 C=64: 1.32 ms with nt K loads, 1.11 ms without).
 constexpr int kStream = 2;
 
+// What one launch writes: T (kkt_solve, wy_prepare), W and U (wy_prepare, wu_prepare).
+constexpr int kModeT = 1;
+constexpr int kModeWU = 2;
+
 struct Params {
     const void* k;
     const void* v;
@@ -509,11 +513,12 @@ __device__ void coupling_level(float* Ts, int tid)
     __syncthreads();
 }
 
-// a7: T rows [0, n) to T_out[(tok0 + r) * Hv + hv][0:C]; rows >= n fall outside the buffer
-// range and are dropped by the hardware.  With PACK, each thread then overwrites the 16-byte
+// a7: T rows [0, n) to T_out[(tok0 + r) * Hv + hv][0:C] (with STORE; wu_prepare forms T but
+// does not write it); rows >= n fall outside the buffer range and are dropped by the
+// hardware.  With PACK, each thread then overwrites the 16-byte
 // chunk it just stored with T' = T diag(beta) for the W/U products: four bf16 "hi" values
 // followed by four bf16 "lo" values (lo = T' - hi, rounded), i.e. the same bytes per element.
-template <int C, class TL, bool PACK>
+template <int C, class TL, bool PACK, bool STORE>
 __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, int Hv, int tid)
 {
     constexpr int TCH = C / 4;                 // 16-byte chunks per row
@@ -521,7 +526,8 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
     static_assert(C * TCH % kThreads == 0, "T rows must split evenly");
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const uint32_t rstride = static_cast<uint32_t>(Hv) * C * 4;
-    const __amdgpu_buffer_rsrc_t tr = rsrc(Tout + (u.tok0 * Hv + u.hv) * C, (u.n - 1) * rstride + C * 4);
+    const __amdgpu_buffer_rsrc_t tr =
+        rsrc(STORE ? Tout + (u.tok0 * Hv + u.hv) * C : nullptr, STORE ? (u.n - 1) * rstride + C * 4 : 0);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int q = tid + it * kThreads;
@@ -531,7 +537,8 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
         f32x4* chunk = reinterpret_cast<f32x4*>(Ts + TL::off(r, 4 * c));
         f32x4 val = zero4();
         if (!upper) val = *chunk;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, kStream);
+        if constexpr (STORE)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, kStream);
         if (PACK && !upper) {
             const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 4 * c);
             bf16x4 h, l;
@@ -791,10 +798,11 @@ __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, 
 
 // One unit, from committing its prefetched K to storing its outputs; its own V and the next
 // unit's K are issued on the way.  Returns the next unit.
-template <int C, int DT, bool WU, class PF>
+template <int C, int DT, int M, class PF>
 __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, PF& pf, const Unit& cur,
                                          int64_t next)
 {
+    constexpr bool WU = (M & kModeWU) != 0;
     using L = Lds<C, DT, WU>;
     unsigned char* Kraw = smem + L::OFF_K;
     float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
@@ -820,7 +828,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
     if constexpr (C >= 64) coupling_level<C, 32, TL>(Ts, tid);
     if constexpr (C >= 128) coupling_level<C, 64, TL>(Ts, tid);
-    store_t<C, TL, DT == 0 && WU>(Ts, bs, p.T, cur, p.hv, tid);
+    store_t<C, TL, DT == 0 && WU, (M & kModeT) != 0>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
         __syncthreads();  // T (packed T' for bf16) of all threads is in place
         if constexpr (DT == 0)
@@ -832,9 +840,10 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     return nxt;
 }
 
-template <int C, int DT, bool WU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEu<C, DT, WU>::value))) void wy_prepare_kernel(Params p)
+template <int C, int DT, int M>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEu<C, DT, (M & kModeWU) != 0>::value))) void wy_prepare_kernel(Params p)
 {
+    constexpr bool WU = (M & kModeWU) != 0;
     using L = Lds<C, DT, WU>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int* info = reinterpret_cast<int*>(smem + L::OFF_INFO);
@@ -851,10 +860,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     // The first unit is peeled off the loop: the loop head is then reached only from the end
     // of a unit, so the memory-counter waits inside see one issue history.
     int64_t next = first + G;
-    cur = run_unit<C, DT, WU>(p, smem, pf, cur, next);
+    cur = run_unit<C, DT, M>(p, smem, pf, cur, next);
     while (cur.n > 0) {  // uniform
         next += G;
-        cur = run_unit<C, DT, WU>(p, smem, pf, cur, next);
+        cur = run_unit<C, DT, M>(p, smem, pf, cur, next);
     }
 }
 
@@ -862,7 +871,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
 // call on a device also raises the instance's dynamic LDS limit where its plan needs more than
 // the default 64 KiB, so later launches (including ones under stream capture) make no
 // attribute calls.
-template <int C, int DT, bool WU>
+template <int C, int DT, int M>
 int resident_grid(int device, hipError_t* err)
 {
     constexpr int kMaxDevices = 64;
@@ -874,8 +883,8 @@ int resident_grid(int device, hipError_t* err)
     }
     std::lock_guard<std::mutex> lock(mu);
     if (cached[device] == 0) {
-        using L = Lds<C, DT, WU>;
-        const void* kern = reinterpret_cast<const void*>(wy_prepare_kernel<C, DT, WU>);
+        using L = Lds<C, DT, (M & kModeWU) != 0>;
+        const void* kern = reinterpret_cast<const void*>(wy_prepare_kernel<C, DT, M>);
         if (L::TOTAL > 64 * 1024) {
             *err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
             if (*err != hipSuccess) return 0;
@@ -890,10 +899,10 @@ int resident_grid(int device, hipError_t* err)
     return cached[device];
 }
 
-template <int C, int DT, bool WU>
+template <int C, int DT, int M>
 int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
 {
-    using L = Lds<C, DT, WU>;
+    using L = Lds<C, DT, (M & kModeWU) != 0>;
     static_assert(L::TOTAL <= 160 * 1024, "LDS plan exceeds 160 KiB");
     Params p;
     p.k = a.k;
@@ -908,11 +917,11 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     p.hq = a.num_qk_heads;
     p.hv = a.num_v_heads;
     p.num_seqs = a.num_seqs;
-    auto kern = wy_prepare_kernel<C, DT, WU>;
+    auto kern = wy_prepare_kernel<C, DT, M>;
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     int resident = 0;
-    if (e == hipSuccess) resident = resident_grid<C, DT, WU>(device, &e);
+    if (e == hipSuccess) resident = resident_grid<C, DT, M>(device, &e);
     if (e == hipSuccess) {
         int64_t grid = (p.units + 7) / 8 * 8;
         const int64_t cap = static_cast<int64_t>(resident) / 8 * 8;
@@ -922,21 +931,29 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
         e = hipGetLastError();
     }
     if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (C=%d, dtype=%d, wu=%d)", hipGetErrorString(e), C, DT,
-                      static_cast<int>(WU));
+        std::snprintf(msg, msg_len, "%s (C=%d, dtype=%d, mode=%d)", hipGetErrorString(e), C, DT, M);
         return static_cast<int>(e);
     }
     return 0;
 }
 
-template <int DT, bool WU>
+template <int DT, int M>
 int launch_c(const LaunchArgs& a, hipStream_t s, char* msg, int len)
 {
     switch (a.chunk_size) {
-    case 32: return launch_t<32, DT, WU>(a, s, msg, len);
-    case 64: return launch_t<64, DT, WU>(a, s, msg, len);
-    default: return launch_t<128, DT, WU>(a, s, msg, len);
+    case 32: return launch_t<32, DT, M>(a, s, msg, len);
+    case 64: return launch_t<64, DT, M>(a, s, msg, len);
+    default: return launch_t<128, DT, M>(a, s, msg, len);
     }
+}
+
+template <int DT>
+int launch_m(const LaunchArgs& a, hipStream_t s, char* msg, int len)
+{
+    const bool wu = a.W != nullptr, t = a.T != nullptr;
+    if (wu && t) return launch_c<DT, kModeT | kModeWU>(a, s, msg, len);
+    if (wu) return launch_c<DT, kModeWU>(a, s, msg, len);
+    return launch_c<DT, kModeT>(a, s, msg, len);
 }
 
 }  // namespace
@@ -944,9 +961,7 @@ int launch_c(const LaunchArgs& a, hipStream_t s, char* msg, int len)
 int launch(const LaunchArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool wu = a.W != nullptr;
-    if (a.kv_dtype == 0) return wu ? launch_c<0, true>(a, s, msg, msg_len) : launch_c<0, false>(a, s, msg, msg_len);
-    return wu ? launch_c<1, true>(a, s, msg, msg_len) : launch_c<1, false>(a, s, msg, msg_len);
+    return a.kv_dtype == 0 ? launch_m<0>(a, s, msg, msg_len) : launch_m<1>(a, s, msg, msg_len);
 }
 
 }  // namespace wyp

@@ -12,7 +12,7 @@ struct LaunchArgs {
     const void* v;            // nullptr for kkt_solve
     const float* beta;
     const int32_t* cu_seqlens;  // nullptr: B x T layout
-    float* T;
+    float* T;                 // nullptr for wu_prepare
     void* W;                  // nullptr for kkt_solve
     void* U;
     int32_t batch;

@@ -107,6 +107,14 @@ wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void*
                           const float* beta, const int32_t* cu_seqlens, float* T_out,
                           void* W_out, void* U_out, void* stream);
 
+/* W and U without T in HBM ([Inv] section 1: T exists to be reused for W and U; section 2.4:
+ * writing T back costs C values per token, the standalone kernel's bottleneck): the same
+ * W_out and U_out as wyp_wy_prepare, bit for bit, with T formed on chip and never written.
+ * Arguments as in wyp_wy_prepare without T_out; saves 4 C bytes per token and value head. */
+wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void* v,
+                          const float* beta, const int32_t* cu_seqlens, void* W_out,
+                          void* U_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

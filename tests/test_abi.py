@@ -29,7 +29,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
-                          "wyp_kkt_solve", "wyp_wy_prepare"}
+                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -81,6 +81,10 @@ def test_rejects_null_and_misaligned(lib):
     assert "16-byte" in lib.wyp_last_error().decode()
     assert call_wy(lib, good(), beta=FAKE + 2) == 1
     assert lib.wyp_kkt_solve(ctypes.byref(good()), FAKE, FAKE, None, None, None) == 1
+    # wu_prepare takes no T_out, but needs W_out and U_out
+    assert lib.wyp_wu_prepare(ctypes.byref(good()), FAKE, FAKE, FAKE, None, FAKE, None, None) == 1
+    assert lib.wyp_wu_prepare(ctypes.byref(good()), FAKE, FAKE, FAKE, None, FAKE + 8, FAKE, None) == 1
+    assert "16-byte" in lib.wyp_last_error().decode()
 
 
 def test_rejects_bad_packing(lib):
@@ -96,6 +100,8 @@ def test_empty_problem_is_a_noop(lib):
     assert lib.wyp_last_error() == b""
     assert call_wy(lib, good(seqlen=0, num_seqs=0), cu=FAKE) == 0
     assert lib.wyp_kkt_solve(ctypes.byref(good(seqlen=0)), FAKE, FAKE, None, FAKE, None) == 0
+    assert lib.wyp_wu_prepare(ctypes.byref(good(seqlen=0)), None, None, None, None, None, None,
+                              None) == 0
 
 
 def test_error_text_is_per_call(lib):
