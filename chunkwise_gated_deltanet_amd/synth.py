@@ -11,7 +11,13 @@ Recipe (one numpy PCG64 generator per workload, seeded with the workload's seed)
   3. v ~ N(0, 1) in float32, shape [B, T, Hv, dv], drawn the same way;
   4. z ~ N(0, 1) in float32, shape [B, T, Hv]; beta = sigmoid(sigma * z) in float32;
   5. bf16 workloads: k and v rounded to bf16 (round to nearest, ties to even).  bf16 data is
-     carried as uint16 bit patterns on the host.
+     carried as uint16 bit patterns on the host;
+  6. gated inputs only: y ~ N(0, 1) in float32, shape [B, T, Hv], and the log gate
+     g = log sigmoid(mu + y) = -log(1 + exp(-(mu + y))) in float32, so every decay
+     alpha = exp(g) lies in (0, 1).  mu = 4 puts alpha near 0.98 (0.88 .. 0.9975 within two
+     standard deviations): a chunk of 64 tokens decays by about e^-1.6, and 6-8 chunks by
+     e^-10 or more, the regime in which the FlashQLA page reports its gate warm-up working.
+     Drawn last, so k, v and beta do not depend on whether gates are drawn.
 
 Workload shapes follow the head configurations the pages benchmark GDN on (value heads 64 down
 to 8 at d_k = d_v = 128) and the page's chunk sizes C in {32, 64, 128}.
@@ -55,6 +61,7 @@ class Workload:
     beta_sigma: float
     seed: int
     seq_range: tuple | None = None   # (lo, hi, count) for packed sequences
+    gate_mu: float | None = None     # None: no gates; else g = log sigmoid(gate_mu + N(0,1))
     note: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -128,21 +135,26 @@ def generate(w: Workload) -> dict:
     z = rng.standard_normal((B, T, w.num_v_heads), dtype=np.float32)
     beta = (1.0 / (1.0 + np.exp(-np.float32(w.beta_sigma) * z, dtype=np.float32))).astype(
         np.float32)
+    g = None
+    if w.gate_mu is not None:
+        y = rng.standard_normal((B, T, w.num_v_heads), dtype=np.float32)
+        g = (-np.logaddexp(np.float32(0), -(np.float32(w.gate_mu) + y))).astype(np.float32)
     if w.dtype == "bf16":
         k = f32_to_bf16_bits(k)
         v = f32_to_bf16_bits(v)
     elif w.dtype != "f32":
         raise ValueError(w.dtype)
-    return dict(k=k, v=v, beta=beta, cu_seqlens=cu, batch=B, seqlen=T,
+    return dict(k=k, v=v, beta=beta, g=g, cu_seqlens=cu, batch=B, seqlen=T,
                 chunk_size=w.chunk_size, num_qk_heads=w.num_qk_heads,
                 num_v_heads=w.num_v_heads, dtype=w.dtype, name=w.name)
 
 
 def custom(batch, seqlen, num_qk_heads, num_v_heads, chunk_size, dtype="bf16", seed=0,
-           beta_sigma=1.0, seqlens=None, head_dim=128) -> dict:
-    """Inputs for an arbitrary shape, same recipe.  `seqlens` (list) makes a packed batch."""
+           beta_sigma=1.0, seqlens=None, head_dim=128, gate_mu=None) -> dict:
+    """Inputs for an arbitrary shape, same recipe.  `seqlens` (list) makes a packed batch;
+    `gate_mu` (float) adds log gates g."""
     w = Workload("custom", batch, seqlen, num_qk_heads, num_v_heads, head_dim, head_dim,
-                 chunk_size, dtype, beta_sigma, seed)
+                 chunk_size, dtype, beta_sigma, seed, gate_mu=gate_mu)
     if seqlens is not None:
         rng_lens = np.asarray(seqlens, np.int64)
         w.batch, w.seqlen = 1, int(rng_lens.sum())

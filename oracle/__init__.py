@@ -16,6 +16,9 @@ Parity status of each function (what pins it is listed in tests/test_oracle_pins
   block_recursive_inverse    pinned (agrees with the row-wise inverse; FMA / depth counts)
   wy_prepare / units         pinned (Householder-product and delta-rule identities, closed
                              forms, degenerate cases, tail padding)
+  the same with gates g      pinned (gated delta-rule recurrence from zero and from an
+                             identity state, the 2-token closed form, g = 0 against no gates,
+                             Gamma o T_ungated, chunk restarts)
   head grouping (v-head h reads k-head h // (Hv/Hq)) and the T layout [B,T,Hv,C]:
                              parity unpinned -- a stated convention, not fixed by the pages.
 """
@@ -39,7 +42,7 @@ def build(out_path: str = LIB_PATH, sources=None, extra_flags=()) -> str:
     srcs = list(sources or SOURCES)
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
            "-Wall", "-Wextra", "-I", _HERE, *extra_flags, *srcs, "-o", out_path + ".tmp",
-           "-lpthread"]
+           "-lpthread", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out_path + ".tmp", out_path)
     return out_path
@@ -66,11 +69,11 @@ def _bind(lib):
     lib.wyo_block_recursive_inverse.argtypes = [ctypes.c_int32, ctypes.c_int32, _P,
                                                 ctypes.c_int32, _P, ctypes.c_int32, _P]
     lib.wyo_wy_prepare.restype = ctypes.c_int32
-    lib.wyo_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P,
+    lib.wyo_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_int32, _P]
     lib.wyo_units.restype = ctypes.c_int32
-    lib.wyo_units.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int64, _P, _P, _P,
-                              _P, _P, _P, ctypes.c_int32]
+    lib.wyo_units.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.c_int64, _P, _P,
+                              _P, _P, _P, _P, ctypes.c_int32]
     return lib
 
 
@@ -113,6 +116,16 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
+def _gate(g, beta):
+    """Log gates g [B,T,Hv] float32 (log alpha per token and value head) or None."""
+    if g is None:
+        return None
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    if g.shape != beta.shape:
+        raise ValueError(f"g shape {g.shape} must match beta {beta.shape}")
+    return g
+
+
 def list_chunks(batch, seqlen, chunk_size, cu_seqlens=None, lib=None):
     """(chunk_start[int64], chunk_len[int32]) in sequence order."""
     lib = lib or load()
@@ -149,16 +162,18 @@ def block_recursive_inverse(L, base=16, lib=None):
 
 
 def wy_prepare(k, beta, chunk_size, v=None, cu_seqlens=None, nthreads=None, lib=None,
-               want_wu=True):
+               want_wu=True, g=None):
     """Whole-tensor oracle.
 
     k: [B,T,Hq,dk] uint16 (bf16 bits) or float32; v: [B,T,Hv,dv] same dtype; beta: [B,T,Hv]
-    float32; cu_seqlens: int32 [N+1] or None.  Returns (T, W, U, fma) as float64 arrays
-    T [B,T,Hv,C], W [B,T,Hv,dk], U [B,T,Hv,dv] (W, U None when v is None or not want_wu).
+    float32; cu_seqlens: int32 [N+1] or None; g: [B,T,Hv] float32 log gates or None (no
+    gates).  Returns (T, W, U, fma) as float64 arrays T [B,T,Hv,C], W [B,T,Hv,dk],
+    U [B,T,Hv,dv] (W, U None when v is None or not want_wu).
     """
     lib = lib or load()
     k = np.ascontiguousarray(k)
     beta = _c(beta, np.float32)
+    g = _gate(g, beta)
     cu = _c(cu_seqlens, np.int32)
     p = _problem(k, v, beta, chunk_size, cu)
     B, T, Hq, dk = k.shape
@@ -171,18 +186,20 @@ def wy_prepare(k, beta, chunk_size, v=None, cu_seqlens=None, nthreads=None, lib=
         U = np.zeros((B, T, Hv, v.shape[3]), np.float64)
     fma = ctypes.c_int64(0)
     rc = lib.wyo_wy_prepare(ctypes.byref(p), _ptr(k), _ptr(v if W is not None else None),
-                            _ptr(beta), _ptr(cu), _ptr(Tm), _ptr(W), _ptr(U),
+                            _ptr(g), _ptr(beta), _ptr(cu), _ptr(Tm), _ptr(W), _ptr(U),
                             nthreads or os.cpu_count() or 1, ctypes.byref(fma))
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return Tm, W, U, int(fma.value)
 
 
-def units(k, beta, chunk_size, chunk_start, chunk_len, v_head, v=None, nthreads=None, lib=None):
+def units(k, beta, chunk_size, chunk_start, chunk_len, v_head, v=None, nthreads=None, lib=None,
+          g=None):
     """Selected units (compact outputs): T [M,C,C], W [M,C,dk], U [M,C,dv], zero-padded rows."""
     lib = lib or load()
     k = np.ascontiguousarray(k)
     beta = _c(beta, np.float32)
+    g = _gate(g, beta)
     p = _problem(k, v, beta, chunk_size, None)
     cs = _c(chunk_start, np.int64)
     cl = _c(chunk_len, np.int32)
@@ -196,7 +213,7 @@ def units(k, beta, chunk_size, chunk_start, chunk_len, v_head, v=None, nthreads=
         v = np.ascontiguousarray(v)
         W = np.zeros((M, C, dk), np.float64)
         U = np.zeros((M, C, v.shape[3]), np.float64)
-    rc = lib.wyo_units(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(beta), M, _ptr(cs), _ptr(cl),
+    rc = lib.wyo_units(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), M, _ptr(cs), _ptr(cl),
                        _ptr(vh), _ptr(Tm), _ptr(W), _ptr(U), nthreads or os.cpu_count() or 1)
     if rc != 0:
         raise ValueError(f"oracle rejected the units (code {rc})")

@@ -9,6 +9,7 @@
  */
 #include "wyo_oracle.h"
 
+#include <math.h>
 #include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
@@ -147,6 +148,8 @@ typedef struct {
     double* K;  /* n x dk */
     double* V;  /* n x dv */
     double* b;  /* n */
+    double* G;  /* n: chunk-local inclusive prefix sums of the log gates (0 without gates) */
+    double* E;  /* n: exp(G), the decay from the chunk start through token j */
     double* A;  /* n x n */
     double* X;  /* n x n */
 } unit_scratch;
@@ -157,21 +160,32 @@ static int scratch_alloc(unit_scratch* s, const wyo_problem* p)
     s->K = (double*)malloc(sizeof(double) * C * (size_t)p->head_dim_k);
     s->V = (double*)malloc(sizeof(double) * C * (size_t)p->head_dim_v);
     s->b = (double*)malloc(sizeof(double) * C);
+    s->G = (double*)malloc(sizeof(double) * C);
+    s->E = (double*)malloc(sizeof(double) * C);
     s->A = (double*)malloc(sizeof(double) * C * C);
     s->X = (double*)malloc(sizeof(double) * C * C);
-    return s->K && s->V && s->b && s->A && s->X;
+    return s->K && s->V && s->b && s->G && s->E && s->A && s->X;
 }
 
 static void scratch_free(unit_scratch* s)
 {
-    free(s->K); free(s->V); free(s->b); free(s->A); free(s->X);
+    free(s->K); free(s->V); free(s->b); free(s->G); free(s->E); free(s->A); free(s->X);
 }
 
 /* Computes T (n x n, into s->X), and W, U (n x dk, n x dv) for the chunk [tok0, tok0 + n) of
- * value head hv.  Returns the forward-substitution count. */
+ * value head hv.  Returns the forward-substitution count.
+ *
+ * Gates (g != NULL; [Inv] section 5, item 12: with gating the coefficient is
+ * diag(beta)(Gamma o K K^T)): g holds log alpha_t per token and value head.  G_i is the sum of
+ * g over the chunk's tokens 0..i, Gamma[i][j] = exp(G_i - G_j) is the decay from token j to
+ * token i, and W takes the decay from the chunk start, W = T diag(beta exp(G)) K, while
+ * U = T diag(beta) V keeps its form.  (Those two W / U forms are what the gated delta rule
+ * S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T needs; the FlashQLA page
+ * names the recurrence and its alpha_i in (0, 1), but its formula did not survive.)
+ * Without gates G = 0, every exp() below is exactly 1 and the result is the ungated one. */
 static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, const float* beta,
-                          int64_t tok0, int32_t n, int32_t hv, unit_scratch* s, double* W,
-                          double* U)
+                          const float* gate, int64_t tok0, int32_t n, int32_t hv,
+                          unit_scratch* s, double* W, double* U)
 {
     const int32_t dk = p->head_dim_k, dv = p->head_dim_v;
     const int32_t Hq = p->num_qk_heads, Hv = p->num_v_heads;
@@ -185,9 +199,12 @@ static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, co
             for (int32_t e = 0; e < dv; ++e)
                 s->V[(int64_t)i * dv + e] = load_elem(v, p->kv_dtype, (tok * Hv + hv) * dv + e);
         s->b[i] = (double)beta[tok * Hv + hv];
+        const double gi = gate ? (double)gate[tok * Hv + hv] : 0.0;
+        s->G[i] = (i == 0 ? 0.0 : s->G[i - 1]) + gi;
+        s->E[i] = exp(s->G[i]);
     }
 
-    /* A = I + strictLower(diag(beta) K K^T): beta scales row i; the diagonal is 1. */
+    /* A = I + strictLower(diag(beta) (Gamma o K K^T)): beta scales row i; the diagonal is 1. */
     for (int32_t i = 0; i < n; ++i)
         for (int32_t j = 0; j < n; ++j) {
             double a;
@@ -195,7 +212,8 @@ static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, co
                 double g = 0.0;
                 for (int32_t d = 0; d < dk; ++d)
                     g += s->K[(int64_t)i * dk + d] * s->K[(int64_t)j * dk + d];
-                a = s->b[i] * g;
+                const double decay = exp(s->G[i] - s->G[j]);
+                a = s->b[i] * decay * g;
             } else {
                 a = (i == j) ? 1.0 : 0.0;
             }
@@ -205,13 +223,13 @@ static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, co
     /* T = A^{-1} */
     const int64_t fma = wyo_row_forward_inverse(n, s->A, n, s->X, n);
 
-    /* W = T diag(beta) K, U = T diag(beta) V  (full products over j = 0..n-1) */
+    /* W = T diag(beta exp(G)) K, U = T diag(beta) V  (full products over j = 0..n-1) */
     if (W) {
         for (int32_t i = 0; i < n; ++i) {
             for (int32_t d = 0; d < dk; ++d) {
                 double acc = 0.0;
                 for (int32_t j = 0; j < n; ++j)
-                    acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->K[(int64_t)j * dk + d];
+                    acc += (s->X[(int64_t)i * n + j] * s->b[j] * s->E[j]) * s->K[(int64_t)j * dk + d];
                 W[(int64_t)i * dk + d] = acc;
             }
             for (int32_t e = 0; e < dv; ++e) {
@@ -232,6 +250,7 @@ typedef struct {
     const void* k;
     const void* v;
     const float* beta;
+    const float* gate;     /* NULL: no gates */
     const int64_t* start;
     const int32_t* len;
     const int32_t* heads;  /* NULL: unit u = (chunk u / Hv, head u % Hv) */
@@ -263,8 +282,8 @@ static void* job_run(void* arg)
             const int64_t tok0 = jb->start[c];
             const int32_t n = jb->len[c];
             const int want_wu = jb->W != NULL;
-            jb->fma += unit_solve(p, jb->k, want_wu ? jb->v : NULL, jb->beta, tok0, n, hv, &s,
-                                  want_wu ? W : NULL, want_wu ? U : NULL);
+            jb->fma += unit_solve(p, jb->k, want_wu ? jb->v : NULL, jb->beta, jb->gate, tok0, n,
+                                  hv, &s, want_wu ? W : NULL, want_wu ? U : NULL);
             for (int32_t i = 0; i < n; ++i) {
                 double* trow;
                 double* wrow = NULL;
@@ -329,9 +348,9 @@ static int run_jobs(job* proto, int32_t nthreads)
     return ok;
 }
 
-int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const float* beta,
-                       const int32_t* cu, double* T_out, double* W_out, double* U_out,
-                       int32_t nthreads, int64_t* fma_out)
+int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const float* g,
+                       const float* beta, const int32_t* cu, double* T_out, double* W_out,
+                       double* U_out, int32_t nthreads, int64_t* fma_out)
 {
     if (!problem_ok(p, cu) || !k || !beta || !T_out) return 1;
     if ((W_out == NULL) != (U_out == NULL) || (W_out && !v)) return 1;
@@ -343,7 +362,7 @@ int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const
     wyo_list_chunks(p, cu, start, len, nchunks);
     job proto;
     memset(&proto, 0, sizeof proto);
-    proto.p = p; proto.k = k; proto.v = v; proto.beta = beta;
+    proto.p = p; proto.k = k; proto.v = v; proto.beta = beta; proto.gate = g;
     proto.start = start; proto.len = len; proto.heads = NULL;
     proto.num_units = nchunks * p->num_v_heads;
     proto.compact = 0;
@@ -355,8 +374,8 @@ int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const
     return ok ? 0 : 2;
 }
 
-int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const float* beta,
-                  int64_t num_units, const int64_t* chunk_start, const int32_t* chunk_len,
+int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const float* g,
+                  const float* beta, int64_t num_units, const int64_t* chunk_start, const int32_t* chunk_len,
                   const int32_t* v_head, double* T_out, double* W_out, double* U_out,
                   int32_t nthreads)
 {
@@ -377,7 +396,7 @@ int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const floa
     }
     job proto;
     memset(&proto, 0, sizeof proto);
-    proto.p = p; proto.k = k; proto.v = v; proto.beta = beta;
+    proto.p = p; proto.k = k; proto.v = v; proto.beta = beta; proto.gate = g;
     proto.start = chunk_start; proto.len = chunk_len; proto.heads = v_head;
     proto.num_units = num_units;
     proto.compact = 1;

@@ -17,10 +17,16 @@
  *     A = I + strictLower(diag(beta) K K^T)
  *     T = A^{-1}                      (row-wise forward substitution, [Inv] section 2.1)
  *     W = T diag(beta) K,  U = T diag(beta) V
+ * With per-token log gates g ([Inv] section 5, item 12 for the gated coefficient; [QLA] usage
+ * for g [B,T,Hv]): G_i = g_0 + ... + g_i over the chunk's tokens, Gamma[i][j] = exp(G_i - G_j),
+ *     A = I + strictLower(diag(beta) (Gamma o K K^T))
+ *     W = T diag(beta exp(G)) K,  U = T diag(beta) V
+ * (the W / U forms of the gated delta rule; without gates G = 0 and this is the line above).
  * All arithmetic is IEEE double; inputs are decoded exactly from the caller's bf16 / fp32 data.
  *
  * Conventions (readings of the pages where they leave a choice open):
- *   - Token-major layouts as in [QLA] usage: k [B,T,Hq,dk], v [B,T,Hv,dv], beta [B,T,Hv].
+ *   - Token-major layouts as in [QLA] usage: k [B,T,Hq,dk], v [B,T,Hv,dv], beta [B,T,Hv],
+ *     g [B,T,Hv] (float32 log alpha_t, or NULL for no gates).
  *   - Value head h reads key head h / (Hv/Hq) (contiguous groups).
  *   - With cu_seqlens (B must be 1) chunks restart at every sequence start; the last chunk of
  *     a sequence may hold n < C tokens and is solved as an n x n system.
@@ -75,19 +81,20 @@ int64_t wyo_block_recursive_inverse(int32_t n, int32_t base, const double* L, in
                                     double* X, int32_t ldx, int32_t* depth);
 
 /* Whole-tensor oracle.  T_out [B,T,Hv,C], W_out [B,T,Hv,dk], U_out [B,T,Hv,dv] (fp64).
- * v / W_out / U_out may be NULL together (T only).  nthreads <= 0 means 1.
- * *fma_out (may be NULL) receives the summed forward-substitution count.
+ * v / W_out / U_out may be NULL together (T only); g may be NULL (no gates).  nthreads <= 0
+ * means 1.  *fma_out (may be NULL) receives the summed forward-substitution count.
  * Returns 0 on success, nonzero on invalid arguments. */
-int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const float* beta,
-                       const int32_t* cu_seqlens, double* T_out, double* W_out, double* U_out,
-                       int32_t nthreads, int64_t* fma_out);
+int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const float* g,
+                       const float* beta, const int32_t* cu_seqlens, double* T_out,
+                       double* W_out, double* U_out, int32_t nthreads, int64_t* fma_out);
 
 /* Selected units only: unit u is the chunk starting at flattened token chunk_start[u] with
  * chunk_len[u] tokens, for value head v_head[u].  Outputs are compact and zero-padded:
  * T_out [M,C,C], W_out [M,C,dk], U_out [M,C,dv] (W_out / U_out may be NULL with v).
  * Returns 0 on success. */
-int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const float* beta,
-                  int64_t num_units, const int64_t* chunk_start, const int32_t* chunk_len,
+int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const float* g,
+                  const float* beta, int64_t num_units, const int64_t* chunk_start,
+                  const int32_t* chunk_len,
                   const int32_t* v_head, double* T_out, double* W_out, double* U_out,
                   int32_t nthreads);
 

@@ -27,14 +27,16 @@ def unit_keys(rng, n, dk=128):
     return (k / np.linalg.norm(k, axis=1, keepdims=True)).astype(np.float32)
 
 
-def one_unit(lib, K, V, beta, C=None):
-    """Runs the oracle on one chunk [0, n) of a single-head problem (fp32 inputs)."""
+def one_unit(lib, K, V, beta, C=None, g=None):
+    """Runs the oracle on one chunk [0, n) of a single-head problem (fp32 inputs; g: optional
+    log gates of the n tokens)."""
     n = K.shape[0]
     C = C or n
     k = np.ascontiguousarray(K[None, :, None, :], np.float32)
     v = np.ascontiguousarray(V[None, :, None, :], np.float32)
     b = np.ascontiguousarray(beta[None, :, None], np.float32)
-    T, W, U = oracle.units(k, b, C, [0], [n], [0], v=v, lib=lib, nthreads=1)
+    gg = None if g is None else np.ascontiguousarray(g[None, :, None], np.float32)
+    T, W, U = oracle.units(k, b, C, [0], [n], [0], v=v, lib=lib, nthreads=1, g=gg)
     return T[0, :n, :n], W[0, :n], U[0, :n]
 
 
@@ -302,10 +304,118 @@ def pin_head_grouping(lib):
     assert np.array_equal(T, T1) and np.array_equal(W, W1) and np.array_equal(U, U1)
 
 
+# ---------------------------------------------------------------------------------------------
+# gated pins.  [Inv] section 5 item 12 gives the gated coefficient diag(beta)(Gamma o K K^T);
+# g [B,T,Hv] is the per-token log gate of [QLA] usage, alpha_t = exp(g_t) in (0, 1) the decay
+# of the GDN recurrence the FlashQLA page recalls.  Reading: G_i = g_0 + ... + g_i within the
+# chunk, Gamma[i][j] = exp(G_i - G_j).  The W / U forms are fixed here by the gated delta rule
+# itself, stepped token by token (S_t = S_{t-1} alpha_t (I - b_t k_t k_t^T) + b_t v_t k_t^T).
+
+def unit_gates(rng, n, mu=2.0):
+    """Log gates with real decay: log sigmoid(mu + N(0,1)), plus one alpha = 1 token."""
+    y = rng.standard_normal(n)
+    g = -np.logaddexp(0.0, -(mu + y))
+    g[n // 3] = 0.0
+    return g.astype(np.float32)
+
+
+def pin_gate_zero(lib):
+    """g = 0 everywhere (alpha = 1) is the ungated method, bit for bit."""
+    rng = np.random.default_rng(30)
+    for n in (17, 64):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        T0, W0, U0 = one_unit(lib, K, V, beta)
+        Tz, Wz, Uz = one_unit(lib, K, V, beta, g=np.zeros(n, np.float32))
+        assert np.array_equal(T0, Tz) and np.array_equal(W0, Wz) and np.array_equal(U0, Uz)
+
+
+def pin_gated_closed_form_2(lib):
+    """Two tokens: A[1,0] = b1 exp(g1) k1.k0 (the decay from token 0 to token 1 is alpha_1), so
+    T[1,0] = -b1 exp(g1) k1.k0; W rows b0 e^{g0} k0 and T[1,0] b0 e^{g0} k0 + b1 e^{g0+g1} k1;
+    U rows b0 v0 and T[1,0] b0 v0 + b1 v1 (one step of the gated delta rule per row)."""
+    rng = np.random.default_rng(31)
+    K = unit_keys(rng, 2)
+    V = rng.standard_normal((2, 128)).astype(np.float32)
+    beta = np.array([0.3, 0.8], np.float32)
+    g = np.array([-0.25, -0.6], np.float32)
+    T, W, U = one_unit(lib, K, V, beta, g=g)
+    K64, V64, b, g64 = K.astype(np.float64), V.astype(np.float64), beta.astype(np.float64), \
+        g.astype(np.float64)
+    t10 = -b[1] * math.exp(g64[1]) * float(K64[1] @ K64[0])
+    assert T[0, 0] == 1 and T[1, 1] == 1 and T[0, 1] == 0
+    assert abs(T[1, 0] - t10) <= 1e-15
+    e0, e01 = math.exp(g64[0]), math.exp(g64[0] + g64[1])
+    W_exp = np.stack([b[0] * e0 * K64[0], t10 * b[0] * e0 * K64[0] + b[1] * e01 * K64[1]])
+    U_exp = np.stack([b[0] * V64[0], t10 * b[0] * V64[0] + b[1] * V64[1]])
+    assert np.max(np.abs(W - W_exp)) <= 1e-14
+    assert np.max(np.abs(U - U_exp)) <= 1e-14
+
+
+def pin_gated_recurrence(lib):
+    """The gated delta rule stepped token by token pins both outputs: from S_0 = 0 it ends at
+    S_n = U^T diag(exp(G_n - G)) K, and its transition prod_t alpha_t (I - b_t k_t k_t^T)
+    (t = 1 leftmost) equals exp(G_n) I - W^T diag(exp(G_n - G)) K."""
+    rng = np.random.default_rng(32)
+    for n, mu in ((32, 2.0), (45, 0.5), (64, 4.0), (128, 3.0)):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        g = unit_gates(rng, n, mu)
+        _, W, U = one_unit(lib, K, V, beta, g=g)
+        K64, V64 = K.astype(np.float64), V.astype(np.float64)
+        S = np.zeros((128, 128))
+        P = np.eye(128)
+        for t in range(n):
+            a, b = math.exp(float(g[t])), float(beta[t])
+            M = a * (np.eye(128) - b * np.outer(K64[t], K64[t]))
+            S = S @ M + b * np.outer(V64[t], K64[t])
+            P = P @ M
+        G = np.cumsum(g.astype(np.float64))
+        d = np.exp(G[-1] - G)[:, None]
+        assert np.max(np.abs(S - U.T @ (d * K64))) <= 1e-12
+        assert np.max(np.abs(P - (math.exp(G[-1]) * np.eye(128) - W.T @ (d * K64)))) <= 1e-12
+
+
+def pin_gated_similarity(lib):
+    """Gamma[i][j] = e^{G_i} / e^{G_j}, so the gated A is D A_0 D^{-1} with D = diag(exp(G)) and
+    A_0 the ungated matrix: T = Gamma o T_0 entry by entry and W = D W_0 row by row (T_0, W_0
+    from the ungated oracle on the same keys and beta)."""
+    rng = np.random.default_rng(33)
+    for n, mu in ((32, 1.0), (64, 3.0), (128, 4.0)):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        g = unit_gates(rng, n, mu)
+        T0, W0, _ = one_unit(lib, K, V, beta)
+        T, W, _ = one_unit(lib, K, V, beta, g=g)
+        G = np.cumsum(g.astype(np.float64))
+        Gam = np.tril(np.exp(G[:, None] - G[None, :]))
+        assert np.max(np.abs(T - Gam * T0)) <= 1e-13
+        assert np.max(np.abs(W - np.exp(G)[:, None] * W0)) <= 1e-13
+
+
+def pin_gated_chunk_restart(lib):
+    """Gates restart at every chunk: the whole-tensor oracle's chunk c equals the one-unit
+    oracle run on that chunk's tokens alone (packed sequences and a ragged tail included)."""
+    inp = synth.custom(1, 0, 1, 2, 32, dtype="f32", seed=34, seqlens=[70, 33], gate_mu=1.0)
+    k, v, beta, g, cu = inp["k"], inp["v"], inp["beta"], inp["g"], inp["cu_seqlens"]
+    T, W, U, _ = oracle.wy_prepare(k, beta, 32, v=v, cu_seqlens=cu, lib=lib, nthreads=2, g=g)
+    for t0, n in ((0, 32), (32, 32), (64, 6), (70, 32), (102, 1)):
+        for h in range(2):
+            Tu, Wu, Uu = one_unit(lib, k[0, t0:t0 + n, 0], v[0, t0:t0 + n, h],
+                                  beta[0, t0:t0 + n, h], C=32, g=g[0, t0:t0 + n, h])
+            assert np.array_equal(T[0, t0:t0 + n, h, :n], Tu)
+            assert np.array_equal(W[0, t0:t0 + n, h], Wu)
+            assert np.array_equal(U[0, t0:t0 + n, h], Uu)
+
+
 PINS = [pin_closed_form_2, pin_orthogonal, pin_residual_structure, pin_lapack_inverse,
         pin_block_identity, pin_beta_zero, pin_subdiag_only, pin_identical_keys,
         pin_fma_counts, pin_householder_product, pin_delta_rule, pin_tail_padding, pin_layout,
-        pin_head_grouping]
+        pin_head_grouping, pin_gate_zero, pin_gated_closed_form_2, pin_gated_recurrence,
+        pin_gated_similarity, pin_gated_chunk_restart]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -363,19 +473,19 @@ def test_generator_conditioning(C):
 # planted mistakes: each mutant copy of the oracle must fail at least one pin
 
 MUTANTS = {
-    "beta_dropped": ("a = s->b[i] * g;", "a = g;"),
-    "beta_on_columns": ("a = s->b[i] * g;", "a = s->b[j] * g;"),
+    "beta_dropped": ("a = s->b[i] * decay * g;", "a = decay * g;"),
+    "beta_on_columns": ("a = s->b[i] * decay * g;", "a = s->b[j] * decay * g;"),
     "gram_term_dropped": ("for (int32_t d = 0; d < dk; ++d)\n                    g +=",
                           "for (int32_t d = 1; d < dk; ++d)\n                    g +="),
-    "gram_wrong_index": ("* s->K[(int64_t)j * dk + d];\n                a = ",
-                         "* s->K[(int64_t)i * dk + d];\n                a = "),
+    "gram_wrong_index": ("* s->K[(int64_t)j * dk + d];\n                const double decay",
+                         "* s->K[(int64_t)i * dk + d];\n                const double decay"),
     "substitution_sign": ("xk[i] -= lkj * xj[i];", "xk[i] += lkj * xj[i];"),
     "substitution_unit_term_dropped": ("for (int32_t i = 0; i <= j; ++i) {",
                                        "for (int32_t i = 0; i < j; ++i) {"),
     "substitution_transposed": ("const double lkj = L[(int64_t)k * ldl + j];",
                                 "const double lkj = L[(int64_t)j * ldl + k];"),
-    "wu_t_transposed": ("acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->K",
-                        "acc += (s->X[(int64_t)j * n + i] * s->b[j]) * s->K"),
+    "wu_t_transposed": ("acc += (s->X[(int64_t)i * n + j] * s->b[j] * s->E[j]) * s->K",
+                        "acc += (s->X[(int64_t)j * n + i] * s->b[j] * s->E[j]) * s->K"),
     "wu_beta_index": ("acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->V",
                       "acc += (s->X[(int64_t)i * n + j] * s->b[i]) * s->V"),
     "u_uses_keys": ("* s->V[(int64_t)j * dv + e];", "* s->K[(int64_t)j * dk + e];"),
@@ -383,6 +493,18 @@ MUTANTS = {
     "coupling_sign": ("X[(int64_t)(h + i) * ldx + j] = -s;", "X[(int64_t)(h + i) * ldx + j] = s;"),
     "tail_columns_leak": ("trow[j] = (j < n) ? s.X[(int64_t)i * n + j] : 0.0;",
                           "trow[j] = (j < n) ? s.X[(int64_t)i * n + j] : 1.0;"),
+    # gates
+    "gate_dropped_in_a": ("a = s->b[i] * decay * g;", "a = s->b[i] * g;"),
+    "gate_transposed": ("exp(s->G[i] - s->G[j])", "exp(s->G[j] - s->G[i])"),
+    "gate_sign": ("s->G[i - 1]) + gi;", "s->G[i - 1]) - gi;"),
+    "gate_exclusive_in_w": ("s->E[i] = exp(s->G[i]);", "s->E[i] = exp(s->G[i] - gi);"),
+    "gate_dropped_in_w": ("acc += (s->X[(int64_t)i * n + j] * s->b[j] * s->E[j]) * s->K",
+                          "acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->K"),
+    "gate_on_u": ("acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->V",
+                  "acc += (s->X[(int64_t)i * n + j] * s->b[j] * s->E[j]) * s->V"),
+    "gate_not_restarted": ("s->G[i] = (i == 0 ? 0.0 : s->G[i - 1]) + gi;",
+                           "s->G[i] = (i == 0 ? (gate && tok0 > 0 ? (double)gate[(tok0 - 1) * Hv + hv] "
+                           ": 0.0) : s->G[i - 1]) + gi;"),
 }
 
 
