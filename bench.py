@@ -33,13 +33,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc", "wypr
 ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve"}
 
 
-def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy"):
-    """K read once per key head, beta read once; wy: V read, T (fp32), W and U written once;
-    wu: the same without T; kkt: T only."""
+def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy", gated=False):
+    """K read once per key head, beta (and g when gated) read once; wy: V read, T (fp32), W and
+    U written once; wu: the same without T; kkt: T only."""
+    gb = 4 if gated else 0
     if entry == "kkt":
-        return tokens * (hq * dk * esz + hv * (4 + 4 * C))
+        return tokens * (hq * dk * esz + hv * (4 + gb + 4 * C))
     t_bytes = 4 * C if entry == "wy" else 0
-    per_token = hq * dk * esz + hv * (dv * esz + 4 + t_bytes + dk * esz + dv * esz)
+    per_token = hq * dk * esz + hv * (dv * esz + 4 + gb + t_bytes + dk * esz + dv * esz)
     return tokens * per_token
 
 
@@ -50,14 +51,16 @@ def kernel_source_sha():
 
 def profile_name(entry, w, batch, seqlen, num_seqs):
     """Name of the profiles/ summaries for one entry point and workload, e.g.
-    wy_prepare_bf16_c64_b1t8192h16 or wy_prepare_bf16_c64_packed8_hq16hv64."""
+    wy_prepare_bf16_c64_b1t8192h16, wy_prepare_bf16_c64_packed8_hq16hv64 or, with log gates,
+    wy_prepare_gated_bf16_c64_b1t8192h16."""
     if num_seqs:
         shape = f"packed{num_seqs}_hq{w.num_qk_heads}hv{w.num_v_heads}"
     elif w.num_qk_heads == w.num_v_heads:
         shape = f"b{batch}t{seqlen}h{w.num_v_heads}"
     else:
         shape = f"b{batch}t{seqlen}hq{w.num_qk_heads}hv{w.num_v_heads}"
-    return f"{ENTRY_NAMES[entry]}_{w.dtype}_c{w.chunk_size}_{shape}"
+    gated = "_gated" if w.gate_mu is not None else ""
+    return f"{ENTRY_NAMES[entry]}{gated}_{w.dtype}_c{w.chunk_size}_{shape}"
 
 
 def counter_traffic(name):
@@ -92,7 +95,8 @@ def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
         passes, t0 = 0, time.perf_counter()
         while True:
             oracle.wy_prepare(inp["k"], inp["beta"], inp["chunk_size"], v=inp["v"],
-                              cu_seqlens=inp["cu_seqlens"], nthreads=threads, lib=lib)
+                              cu_seqlens=inp["cu_seqlens"], nthreads=threads, lib=lib,
+                              g=inp["g"])
             passes += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -125,6 +129,9 @@ def main(argv=None):
     ap.add_argument("--entry", choices=("wy", "wu", "kkt"), default="wy",
                     help="wy: wyp_wy_prepare (T, W, U; the headline); wu: wyp_wu_prepare "
                          "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only)")
+    ap.add_argument("--gate-mu", type=float, default=None,
+                    help="add per-token log gates g = log sigmoid(mu + N(0,1)) (the gated "
+                         "coefficient diag(beta)(Gamma o K K^T)); 4 is the seeded gated recipe")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -149,8 +156,11 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     lib = cg.load_library()
 
-    w = synth.workload(args.workload, chunk_size=args.chunk_size)
+    w = synth.workload(args.workload, chunk_size=args.chunk_size, gate_mu=args.gate_mu)
+    if args.gate_mu is not None:
+        w.name += f" gated (g = log sigmoid({args.gate_mu:g} + N(0,1)))"
     inp = synth.generate(w)
+    gated = inp["g"] is not None
     B, T = inp["batch"], inp["seqlen"]
     Hq, Hv, C = w.num_qk_heads, w.num_v_heads, w.chunk_size
     dk = dv = 128
@@ -163,7 +173,7 @@ def main(argv=None):
         nchunks = B * ((T + C - 1) // C)
     units = nchunks * Hv
     tokens = B * T
-    alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, args.entry)
+    alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, args.entry, gated)
     nsets = max(1, math.ceil(ROTATE_BYTES / alg))  # every byte of a step is touched once
 
     def dev_tensor(a, dt):
@@ -173,10 +183,12 @@ def main(argv=None):
     k0 = dev_tensor(inp["k"], tdt)
     v0 = dev_tensor(inp["v"], tdt)
     b0 = torch.from_numpy(inp["beta"]).to(dev)
+    g0 = torch.from_numpy(inp["g"]).to(dev) if gated else None
     cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
     sets = []
     for _ in range(nsets):
         sets.append(dict(k=k0.clone(), v=v0.clone(), beta=b0.clone(),
+                         g=g0.clone() if gated else None,
                          T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev),
                          W=torch.empty(B, T, Hv, dk, dtype=tdt, device=dev),
                          U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev)))
@@ -186,18 +198,18 @@ def main(argv=None):
     pprob = ctypes.byref(prob)
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    calls = [tuple(ctypes.c_void_p(t.data_ptr()) for t in
-                   (s["k"], s["v"], s["beta"], s["T"], s["W"], s["U"])) for s in sets]
+    calls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
+                   (s["k"], s["v"], s["g"], s["beta"], s["T"], s["W"], s["U"])) for s in sets]
     cu_ptr = ctypes.c_void_p(None if cu is None else cu.data_ptr())
 
     def step(i, sp):
-        kp, vp, bp, tp, wp, up = calls[i % nsets]
+        kp, vp, gp, bp, tp, wp, up = calls[i % nsets]
         if args.entry == "wy":
-            st = lib.wyp_wy_prepare(pprob, kp, vp, bp, cu_ptr, tp, wp, up, sp)
+            st = lib.wyp_wy_prepare(pprob, kp, vp, gp, bp, cu_ptr, tp, wp, up, sp)
         elif args.entry == "wu":
-            st = lib.wyp_wu_prepare(pprob, kp, vp, bp, cu_ptr, wp, up, sp)
+            st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
         else:
-            st = lib.wyp_kkt_solve(pprob, kp, bp, cu_ptr, tp, sp)
+            st = lib.wyp_kkt_solve(pprob, kp, gp, bp, cu_ptr, tp, sp)
         if st != 0:
             raise RuntimeError(lib.wyp_last_error().decode())
 
@@ -279,7 +291,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "entry": ENTRY_NAMES[args.entry],
+        "config": {"workload": w.name, "entry": ENTRY_NAMES[args.entry], "gated": gated,
                    "batch": B, "seqlen": T, "num_qk_heads": Hq,
                    "num_v_heads": Hv, "head_dim": dk, "chunk_size": C,
                    "units_per_step": units, "tokens_per_step": tokens,

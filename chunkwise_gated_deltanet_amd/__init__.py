@@ -8,7 +8,10 @@ raise.
 
 Page cited: "TileLang 实战：单位下三角矩阵求逆" (TileLang in practice: inverting a unit
 lower-triangular matrix), section 1 -- for every chunk of C tokens and value head:
-A = I + strictLower(diag(beta) K K^T), T = A^{-1}, W = T diag(beta) K, U = T diag(beta) V.
+A = I + strictLower(diag(beta) K K^T), T = A^{-1}, W = T diag(beta) K, U = T diag(beta) V;
+section 5, item 12 for the gated coefficient diag(beta)(Gamma o K K^T).  With log gates g
+[B,T,Hv] (the FlashQLA usage section passes g beside beta): G_i = g_0 + ... + g_i within the
+chunk, Gamma[i][j] = exp(G_i - G_j), and W = T diag(beta exp(G)) K.
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.s
 
 WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
 WYP_BF16, WYP_F32 = 0, 1
+ABI_VERSION = 2
 
 
 class WyprepError(RuntimeError):
@@ -61,11 +65,14 @@ def load_library(path: str | None = None):
     lib.wyp_last_error.restype = ctypes.c_char_p
     lib.wyp_last_error.argtypes = []
     lib.wyp_kkt_solve.restype = ctypes.c_int32
-    lib.wyp_kkt_solve.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P]
+    lib.wyp_kkt_solve.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P]
     lib.wyp_wy_prepare.restype = ctypes.c_int32
-    lib.wyp_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.wyp_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.wyp_wu_prepare.restype = ctypes.c_int32
-    lib.wyp_wu_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P]
+    lib.wyp_wu_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P]
+    if lib.wyp_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{p} has ABI version {lib.wyp_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it")
     if path is None:
         _lib = lib
     return lib
@@ -97,6 +104,19 @@ def _require(t, name, ndim, device):
         raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _gate_ptr(g, beta):
+    """Device pointer of the log gates g [B,T,Hv] float32 (shape of beta), or None."""
+    import torch
+    if g is None:
+        return None
+    _require(g, "g", 3, beta.device)
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32")
+    if g.shape != beta.shape:
+        raise ValueError(f"g shape {tuple(g.shape)} must match beta {tuple(beta.shape)}")
+    return g.data_ptr()
 
 
 def _problem(k, beta, chunk_size, cu_seqlens, v=None):
@@ -142,31 +162,36 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
-def kkt_solve(k, beta, chunk_size, cu_seqlens=None, T_out=None):
-    """T [B,T,Hv,C] (float32) from k [B,T,Hq,128] and beta [B,T,Hv]; see wyp_kkt_solve."""
+def kkt_solve(k, beta, chunk_size, cu_seqlens=None, T_out=None, g=None):
+    """T [B,T,Hv,C] (float32) from k [B,T,Hq,128], beta [B,T,Hv] and optional log gates g
+    [B,T,Hv]; see wyp_kkt_solve."""
     import torch
     lib = load_library()
     p = _problem(k, beta, chunk_size, cu_seqlens)
+    gp = _gate_ptr(g, beta)
     B, T = k.shape[:2]
     T_out = _out(T_out, (B, T, p.num_v_heads, p.chunk_size), torch.float32, k.device, "T_out")
-    st = lib.wyp_kkt_solve(ctypes.byref(p), k.data_ptr(), beta.data_ptr(),
+    st = lib.wyp_kkt_solve(ctypes.byref(p), k.data_ptr(), gp, beta.data_ptr(),
                            cu_seqlens.data_ptr() if cu_seqlens is not None else None,
                            T_out.data_ptr(), _stream(k.device))
     _check(lib, st)
     return T_out
 
 
-def wy_prepare(k, v, beta, chunk_size, cu_seqlens=None, T_out=None, W_out=None, U_out=None):
-    """(T, W, U): T [B,T,Hv,C] float32, W [B,T,Hv,128] and U [B,T,Hv,128] in k's dtype."""
+def wy_prepare(k, v, beta, chunk_size, cu_seqlens=None, T_out=None, W_out=None, U_out=None,
+               g=None):
+    """(T, W, U): T [B,T,Hv,C] float32, W [B,T,Hv,128] and U [B,T,Hv,128] in k's dtype.
+    g: optional log gates [B,T,Hv] float32."""
     import torch
     lib = load_library()
     p = _problem(k, beta, chunk_size, cu_seqlens, v=v)
+    gp = _gate_ptr(g, beta)
     B, T = k.shape[:2]
     Hv = p.num_v_heads
     T_out = _out(T_out, (B, T, Hv, p.chunk_size), torch.float32, k.device, "T_out")
     W_out = _out(W_out, (B, T, Hv, p.head_dim_k), k.dtype, k.device, "W_out")
     U_out = _out(U_out, (B, T, Hv, p.head_dim_v), k.dtype, k.device, "U_out")
-    st = lib.wyp_wy_prepare(ctypes.byref(p), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+    st = lib.wyp_wy_prepare(ctypes.byref(p), k.data_ptr(), v.data_ptr(), gp, beta.data_ptr(),
                             cu_seqlens.data_ptr() if cu_seqlens is not None else None,
                             T_out.data_ptr(), W_out.data_ptr(), U_out.data_ptr(),
                             _stream(k.device))
@@ -174,16 +199,17 @@ def wy_prepare(k, v, beta, chunk_size, cu_seqlens=None, T_out=None, W_out=None, 
     return T_out, W_out, U_out
 
 
-def wu_prepare(k, v, beta, chunk_size, cu_seqlens=None, W_out=None, U_out=None):
+def wu_prepare(k, v, beta, chunk_size, cu_seqlens=None, W_out=None, U_out=None, g=None):
     """(W, U) without T in HBM: the same values as wy_prepare's W and U; see wyp_wu_prepare."""
     import torch
     lib = load_library()
     p = _problem(k, beta, chunk_size, cu_seqlens, v=v)
+    gp = _gate_ptr(g, beta)
     B, T = k.shape[:2]
     Hv = p.num_v_heads
     W_out = _out(W_out, (B, T, Hv, p.head_dim_k), k.dtype, k.device, "W_out")
     U_out = _out(U_out, (B, T, Hv, p.head_dim_v), k.dtype, k.device, "U_out")
-    st = lib.wyp_wu_prepare(ctypes.byref(p), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+    st = lib.wyp_wu_prepare(ctypes.byref(p), k.data_ptr(), v.data_ptr(), gp, beta.data_ptr(),
                             cu_seqlens.data_ptr() if cu_seqlens is not None else None,
                             W_out.data_ptr(), U_out.data_ptr(), _stream(k.device))
     _check(lib, st)

@@ -24,9 +24,9 @@ wyp_status fail(wyp_status st, const char* fmt, ...)
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Host-side checks shared by the entry points.  Touches no HIP API.
-wyp_status validate(const wyp_problem* p, const void* k, const void* v, const float* beta,
-                    const int32_t* cu, const float* T, const void* W, const void* U,
-                    bool want_t, bool want_wu, wyp::LaunchArgs* out, bool* empty)
+wyp_status validate(const wyp_problem* p, const void* k, const void* v, const float* g,
+                    const float* beta, const int32_t* cu, const float* T, const void* W,
+                    const void* U, bool want_t, bool want_wu, wyp::LaunchArgs* out, bool* empty)
 {
     *empty = false;
     if (!p) return fail(WYP_ERR_INVALID_ARGUMENT, "problem is NULL");
@@ -69,6 +69,7 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
         (want_wu && (!aligned(v, 16) || !aligned(W, 16) || !aligned(U, 16))))
         return fail(WYP_ERR_INVALID_ARGUMENT, "k, v, T_out, W_out and U_out must be 16-byte aligned");
     if (!aligned(beta, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "beta is not 4-byte aligned");
+    if (g && !aligned(g, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "g is not 4-byte aligned");
 
     int64_t slots;
     if (cu) slots = (p->seqlen + C - 1) / C + p->num_seqs - 1;  // >= sum of per-sequence chunks
@@ -82,6 +83,7 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
     out->k = k;
     out->v = want_wu ? v : nullptr;
     out->beta = beta;
+    out->g = g;
     out->cu_seqlens = cu;
     out->T = want_t ? const_cast<float*>(T) : nullptr;
     out->W = want_wu ? const_cast<void*>(W) : nullptr;
@@ -97,14 +99,14 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
     return WYP_OK;
 }
 
-wyp_status run(const wyp_problem* p, const void* k, const void* v, const float* beta,
-               const int32_t* cu, float* T, void* W, void* U, bool want_t, bool want_wu,
-               void* stream)
+wyp_status run(const wyp_problem* p, const void* k, const void* v, const float* g,
+               const float* beta, const int32_t* cu, float* T, void* W, void* U, bool want_t,
+               bool want_wu, void* stream)
 {
     g_last_error[0] = '\0';
     wyp::LaunchArgs args{};
     bool empty = false;
-    const wyp_status st = validate(p, k, v, beta, cu, T, W, U, want_t, want_wu, &args, &empty);
+    const wyp_status st = validate(p, k, v, g, beta, cu, T, W, U, want_t, want_wu, &args, &empty);
     if (st != WYP_OK || empty) return st;
     char msg[256] = "";
     if (wyp::launch(args, stream, msg, sizeof msg) != 0)
@@ -131,24 +133,25 @@ const char* wyp_status_string(int32_t status)
 
 const char* wyp_last_error(void) { return g_last_error; }
 
-wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* beta,
-                         const int32_t* cu_seqlens, float* T_out, void* stream)
+wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, float* T_out, void* stream)
 {
-    return run(problem, k, nullptr, beta, cu_seqlens, T_out, nullptr, nullptr, true, false, stream);
+    return run(problem, k, nullptr, g, beta, cu_seqlens, T_out, nullptr, nullptr, true, false,
+               stream);
 }
 
 wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void* v,
-                          const float* beta, const int32_t* cu_seqlens, float* T_out,
-                          void* W_out, void* U_out, void* stream)
+                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                          float* T_out, void* W_out, void* U_out, void* stream)
 {
-    return run(problem, k, v, beta, cu_seqlens, T_out, W_out, U_out, true, true, stream);
+    return run(problem, k, v, g, beta, cu_seqlens, T_out, W_out, U_out, true, true, stream);
 }
 
 wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void* v,
-                          const float* beta, const int32_t* cu_seqlens, void* W_out, void* U_out,
-                          void* stream)
+                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                          void* W_out, void* U_out, void* stream)
 {
-    return run(problem, k, v, beta, cu_seqlens, nullptr, W_out, U_out, false, true, stream);
+    return run(problem, k, v, g, beta, cu_seqlens, nullptr, W_out, U_out, false, true, stream);
 }
 
 }  // extern "C"

@@ -30,6 +30,14 @@
 //       accumulated in turn (T' is lower triangular, so k-tiles right of the diagonal are
 //       skipped); the transposed accumulators hold four consecutive output columns per lane,
 //       staged in LDS and stored with 16-byte writes.
+// Gated instances ([Inv] section 5, item 12: with gating the coefficient is
+// diag(beta)(Gamma o K K^T); g [B,T,Hv] is the per-token log gate of [QLA] usage) also read g:
+//   a1' wave 0 forms the chunk-local inclusive prefix sums G_i = g_0 + ... + g_i in fp64 (one
+//       shuffle scan) and parks G_i and exp(G_i) in the 16 padding bytes of staged K row i;
+//   a3' every A entry below the diagonal takes the decay Gamma[i][j] = exp(G_i - G_j);
+//   a8' W takes T diag(beta exp(G)): each wave rescales its T' chunks column by column by
+//       exp(G_j) in registers (exp(G_j) <= 1 for decaying gates, so nothing overflows) before
+//       the W product, and U keeps T' = T diag(beta).
 //
 // MFMA operand convention: for a 16x16 output tile, lane l = 16*g + c holds row/column c and
 // k-group g.  In __builtin_amdgcn_mfma_f32_16x16x4f32 sub-step q the lane supplies true
@@ -67,14 +75,17 @@ constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bo
 // packed sequences, Hq=16 Hv=64 C=64: 1.32 ms with nt K loads, 1.11 ms without).
 constexpr int kStream = 2;
 
-// What one launch writes: T (kkt_solve, wy_prepare), W and U (wy_prepare, wu_prepare).
+// What one launch writes: T (kkt_solve, wy_prepare), W and U (wy_prepare, wu_prepare); and
+// whether it reads log gates g.
 constexpr int kModeT = 1;
 constexpr int kModeWU = 2;
+constexpr int kModeGate = 4;
 
 struct Params {
     const void* k;
     const void* v;
     const float* beta;
+    const float* g;  // log gates, gated instances only
     const int32_t* cu;
     float* T;
     void* W;
@@ -121,7 +132,10 @@ struct TLayout<C, true> {
 template <int C, int DT, bool WU>
 struct Lds {
     static constexpr int ESZ = DT == 0 ? 2 : 4;
-    static constexpr int KROW = kD + 16 / ESZ;   // elements per staged K / V row
+    // Elements per staged K / V row: 128 plus 16 bytes of padding.  No K / V / W / U access
+    // touches the padding; gated instances keep row i's G_i (fp64) and exp(G_i) (fp32) there
+    // (see GateRow), so the gates cost no LDS.
+    static constexpr int KROW = kD + 16 / ESZ;
     static constexpr int KBYTES = C * KROW * ESZ;
     using TL = TLayout<C>;
     static constexpr int TBYTES = TL::BYTES;
@@ -142,6 +156,28 @@ struct WavesPerEu {
 };
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Gate values of token row r of the unit, in the padding after the 128 elements of staged K
+// row r: G_r (chunk-local inclusive prefix sum of the log gates, fp64) and exp(G_r) (fp32).
+template <int KROW, int ESZ>
+struct GateRow {
+    __device__ static double* Gp(unsigned char* Kraw, int r)
+    {
+        return reinterpret_cast<double*>(Kraw + r * (KROW * ESZ) + kD * ESZ);
+    }
+    __device__ static float* Ep(unsigned char* Kraw, int r)
+    {
+        return reinterpret_cast<float*>(Kraw + r * (KROW * ESZ) + kD * ESZ + 8);
+    }
+    __device__ static double G(const unsigned char* Kraw, int r)
+    {
+        return *reinterpret_cast<const double*>(Kraw + r * (KROW * ESZ) + kD * ESZ);
+    }
+    __device__ static float E(const unsigned char* Kraw, int r)
+    {
+        return *reinterpret_cast<const float*>(Kraw + r * (KROW * ESZ) + kD * ESZ + 8);
+    }
+};
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -218,14 +254,16 @@ __device__ Unit map_unit(const Params& p, int* info, int64_t logical64, int tid)
 
 // a1: K, V and beta of one unit in flight to registers, then committed to LDS.  K and beta
 // are committed at the start of their unit; V only after that unit's T tile has been used.
-template <int C, int ESZ, int KROW, bool WU>
+template <int C, int ESZ, int KROW, bool WU, bool GT>
 struct Prefetch {
     static constexpr int CPR = kD * ESZ / 16;  // 16-byte chunks per row
     static constexpr int NIT = C * CPR / kThreads;
+    static constexpr int NG = C > 64 ? 2 : 1;  // log gates per lane of wave 0
     static_assert(C * CPR % kThreads == 0, "row chunks must split evenly");
     u32x4 k[NIT];
     u32x4 v[WU ? NIT : 1];
     float b;
+    float g[NG];  // gated: wave 0 lane l holds g of rows l and l + 64
 
     __device__ static __amdgpu_buffer_rsrc_t rows(const void* base, const Unit& u, int heads, int head)
     {
@@ -247,6 +285,17 @@ struct Prefetch {
         const __amdgpu_buffer_rsrc_t br =
             rsrc(p.beta + u.tok0 * p.hv + u.hv, ((u.n - 1) * p.hv + 1) * 4);
         b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (tid % C) * p.hv * 4, 0, 0));
+        if constexpr (GT) {
+            // rows >= n read as 0, so G stays flat over a short chunk's padding
+            if (tid < 64) {
+                const __amdgpu_buffer_rsrc_t gr =
+                    rsrc(p.g + u.tok0 * p.hv + u.hv, ((u.n - 1) * p.hv + 1) * 4);
+#pragma unroll
+                for (int e = 0; e < NG; ++e)
+                    g[e] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(gr, (tid + 64 * e) * p.hv * 4, 0, kStream));
+            }
+        }
     }
 
     __device__ void issue_v(const Params& p, const Unit& u, int tid)
@@ -270,6 +319,30 @@ struct Prefetch {
             *reinterpret_cast<u32x4*>(Kraw + (q / CPR) * (KROW * ESZ) + (q % CPR) * 16) = k[it];
         }
         if (tid < C) bs[tid] = b;
+        if constexpr (GT) {
+            // a1': G = inclusive prefix sums of g over the chunk, in fp64, by wave 0
+            if (tid < 64) {
+                const int lane = tid;
+                double run = 0.0;
+#pragma unroll
+                for (int e = 0; e < NG; ++e) {
+                    double x = static_cast<double>(g[e]);
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const double t = __shfl_up(x, d);
+                        if (lane >= d) x += t;
+                    }
+                    x += run;
+                    const int r = lane + 64 * e;
+                    if (r < C) {
+                        *GateRow<KROW, ESZ>::Gp(Kraw, r) = x;
+                        // fp32 exp: e^G only scales W's columns, whose output is bf16
+                        *GateRow<KROW, ESZ>::Ep(Kraw, r) = __expf(static_cast<float>(x));
+                    }
+                    run = __shfl(x, 63);
+                }
+            }
+        }
     }
 
     __device__ void commit_v(unsigned char* Vraw, int tid) const
@@ -337,9 +410,10 @@ struct GramFrags {
     }
 };
 
-template <int C, int DT, int KROW, class TL>
+template <int C, int DT, int KROW, class TL, bool GT>
 __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
+    constexpr int ESZ = DT == 0 ? 2 : 4;
     constexpr int NB = C / 16;
     constexpr int NTILE = NB * (NB + 1) / 2;
     constexpr int PER = (NTILE + kWaves - 1) / kWaves;
@@ -368,13 +442,21 @@ __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, in
         const f32x4 acc = f[tt % NBUF].product();
         const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
         const float bcol = bs[16 * J + lr];
+        double gcol = 0.0;
+        if constexpr (GT) gcol = GateRow<KROW, ESZ>::G(Kraw, 16 * J + lr);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             // Diagonal tiles keep L^T in their upper triangle (G is symmetric, so entry (i, j),
             // i < j, is beta_j G[j][i] = L[j][i]); the substitution reads columns of L there
             // and overwrites it with zeros.
             const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
-            Ts[TL::off(i, j)] = (i > j) ? bet[r] * acc[r] : (i == j ? 1.f : bcol * acc[r]);
+            float a = acc[r];
+            if constexpr (GT) {
+                // a3': decay Gamma between the later and the earlier token of the pair
+                const double d = GateRow<KROW, ESZ>::G(Kraw, i) - gcol;
+                a *= __expf(static_cast<float>(i > j ? d : -d));
+            }
+            Ts[TL::off(i, j)] = (i > j) ? bet[r] * a : (i == j ? 1.f : bcol * a);
         }
         if (NBUF == 2) {
             I = In;
@@ -681,15 +763,105 @@ __device__ inline void stage_tiles_rows(unsigned char* dst, const bf16x4 (&out)[
     }
 }
 
+// a8' (gated): one packed T' chunk (four hi bf16, four lo bf16; see store_t) rescaled column
+// by column, T' diag(e): hi + lo is T' to within 2^-17 |T'|, the product is rounded once in
+// fp32, and the result is split into a new hi / lo pair the same way store_t splits T'.
+__device__ inline u32x4 scale_chunk(u32x4 c, f32x4 e)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const bf16x4 h = __builtin_bit_cast(bf16x4, u32x2{c[0], c[1]});
+    const bf16x4 l = __builtin_bit_cast(bf16x4, u32x2{c[2], c[3]});
+    bf16x4 h2, l2;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float f = (static_cast<float>(h[k]) + static_cast<float>(l[k])) * e[k];
+        h2[k] = static_cast<__bf16>(f);
+        l2[k] = static_cast<__bf16>(f - static_cast<float>(h2[k]));
+    }
+    const u32x2 hp = __builtin_bit_cast(u32x2, h2), lp = __builtin_bit_cast(u32x2, l2);
+    return u32x4{hp[0], hp[1], lp[0], lp[1]};
+}
+
+// exp(G_j) of the four T' columns 16 kt + 4 lg + 0..3 that one lane's chunks hold.
+template <int KROW>
+__device__ inline f32x4 gate_cols(const unsigned char* Kraw, int kt, int lg)
+{
+    f32x4 e;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) e[q] = GateRow<KROW, 2>::E(Kraw, 16 * kt + 4 * lg + q);
+    return e;
+}
+
 // Every wave first takes its T' chunks (lower-triangular 16x16 blocks) into registers; then V,
 // waiting in registers, takes the T tile's place.  W is staged over K while U is computed.
-template <int C, int KROW, class TL, class PF>
+// Gated: U is formed first with T' = T diag(beta) and staged over V; the same registers are
+// then rescaled column by column to T' diag(exp(G)) for W, whose K rows (and gate values) are
+// still in LDS.
+template <int C, int KROW, class TL, bool GT, class PF>
 __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p, const Unit& u, int tid)
 {
     constexpr int NB = C / 16;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    if constexpr (NB == 2 * kWaves) {
+    if constexpr (GT && NB == 2 * kWaves) {
+        const int mA = wave, mB = NB - 1 - wave;
+        u32x4 tpA[NB], tpB[NB];
+#pragma unroll
+        for (int kt = 0; kt < NB; ++kt) {
+            tpA[kt] = u32x4{0u, 0u, 0u, 0u};
+            tpB[kt] = u32x4{0u, 0u, 0u, 0u};
+            if (kt <= mA) tpA[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mA + lr, 16 * kt + 4 * lg));
+            if (kt <= mB) tpB[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mB + lr, 16 * kt + 4 * lg));
+        }
+        __syncthreads();  // the T tile is no longer read: V takes its place
+        unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
+        pf.commit_v(Vraw, tid);
+        __syncthreads();
+        bf16x4 out[NB][2];
+        wu_tiles_rows<C, KROW>(Vraw, tpA, tpB, mA, mB, lr, lg, out);
+        __syncthreads();  // every wave is done reading V: U is staged over it
+        stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, lr, lg);
+#pragma unroll
+        for (int kt = 0; kt < NB; ++kt) {
+            if (kt > mB) continue;  // uniform; the zero chunks above the diagonal stay zero
+            const f32x4 e = gate_cols<KROW>(Kraw, kt, lg);
+            if (kt <= mA) tpA[kt] = scale_chunk(tpA[kt], e);
+            tpB[kt] = scale_chunk(tpB[kt], e);
+        }
+        wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, mA, mB, lr, lg, out);
+        __syncthreads();  // every wave is done reading K: W is staged over it
+        stage_tiles_rows<C, KROW>(Kraw, out, mA, mB, lr, lg);
+        __syncthreads();
+        store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
+        store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
+    } else if constexpr (GT) {
+        u32x4 tp[NB][NB];
+#pragma unroll
+        for (int mi = 0; mi < NB; ++mi)
+#pragma unroll
+            for (int kt = 0; kt <= mi; ++kt)
+                tp[mi][kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mi + lr, 16 * kt + 4 * lg));
+        __syncthreads();  // the T tile is no longer read: V takes its place
+        unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
+        pf.commit_v(Vraw, tid);
+        __syncthreads();
+        bf16x4 out[2][NB];
+        wu_tiles<C, KROW>(Vraw, tp, wave, lr, lg, out);
+        __syncthreads();  // every wave is done reading V: U is staged over it
+        stage_tiles<C, KROW>(Vraw, out, wave, lr, lg);
+#pragma unroll
+        for (int kt = 0; kt < NB; ++kt) {
+            const f32x4 e = gate_cols<KROW>(Kraw, kt, lg);
+#pragma unroll
+            for (int mi = kt; mi < NB; ++mi) tp[mi][kt] = scale_chunk(tp[mi][kt], e);
+        }
+        wu_tiles<C, KROW>(Kraw, tp, wave, lr, lg, out);
+        __syncthreads();  // every wave is done reading K: W is staged over it
+        stage_tiles<C, KROW>(Kraw, out, wave, lr, lg);
+        __syncthreads();
+        store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
+        store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
+    } else if constexpr (NB == 2 * kWaves) {
         const int mA = wave, mB = NB - 1 - wave;
         u32x4 tpA[NB], tpB[NB];
 #pragma unroll
@@ -740,7 +912,7 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
 
 // a8 (fp32 inputs): the same transposed products on fp32 MFMA, T' = T diag(beta) kept in fp32
 // registers before V takes the T tile's place.
-template <int C, int KROW, class TL, class PF>
+template <int C, int KROW, class TL, bool GT, class PF>
 __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, const Params& p,
                        const Unit& u, int tid)
 {
@@ -763,7 +935,20 @@ __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, 
 
     f32x4 out[4][NB];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int cc = 0; cc < 4; ++cc) {
+        // gated: the U tiles (c = 2, 3) first, then T diag(beta) becomes T diag(beta exp(G))
+        // in place for the W tiles
+        const int c = GT ? (cc + 2) % 4 : cc;
+        if (GT && cc == 2) {
+#pragma unroll
+            for (int kt = 0; kt < NB; ++kt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float e = GateRow<KROW, 4>::E(Kraw, 16 * kt + 4 * lg + q);
+#pragma unroll
+                    for (int mi = kt; mi < NB; ++mi) tfr[mi][kt][q] *= e;
+                }
+        }
         const int ct = wave + 4 * c;
         const float* src = reinterpret_cast<const float*>(ct < 8 ? Kraw : Vraw);
         const int ni = ct & 7;
@@ -803,6 +988,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
                                          int64_t next)
 {
     constexpr bool WU = (M & kModeWU) != 0;
+    constexpr bool GT = (M & kModeGate) != 0;
     using L = Lds<C, DT, WU>;
     unsigned char* Kraw = smem + L::OFF_K;
     float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
@@ -821,7 +1007,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     if (nxt.n > 0) pf.issue_k(p, nxt, tid);
 
     using TL = typename L::TL;
-    form_a<C, DT, L::KROW, TL>(Kraw, Ts, bs, tid);
+    form_a<C, DT, L::KROW, TL, GT>(Kraw, Ts, bs, tid);
     __syncthreads();
     invert_diagonal_blocks<C, TL>(Ts, tid);
     __syncthreads();
@@ -832,9 +1018,9 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     if constexpr (WU) {
         __syncthreads();  // T (packed T' for bf16) of all threads is in place
         if constexpr (DT == 0)
-            wu_bf16<C, L::KROW, TL>(Kraw, Ts, pf, p, cur, tid);
+            wu_bf16<C, L::KROW, TL, GT>(Kraw, Ts, pf, p, cur, tid);
         else
-            wu_f32<C, L::KROW, TL>(Kraw, Ts, bs, pf, p, cur, tid);
+            wu_f32<C, L::KROW, TL, GT>(Kraw, Ts, bs, pf, p, cur, tid);
     }
     __syncthreads();  // LDS is rewritten by the next unit
     return nxt;
@@ -855,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
 
     Unit cur = map_unit<C>(p, info, first, threadIdx.x);
     if (cur.n <= 0) return;  // uniform per workgroup
-    Prefetch<C, L::ESZ, L::KROW, WU> pf;
+    Prefetch<C, L::ESZ, L::KROW, WU, (M & kModeGate) != 0> pf;
     pf.issue_k(p, cur, threadIdx.x);
     // The first unit is peeled off the loop: the loop head is then reached only from the end
     // of a unit, so the memory-counter waits inside see one issue history.
@@ -908,6 +1094,7 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     p.k = a.k;
     p.v = a.v;
     p.beta = a.beta;
+    p.g = a.g;
     p.cu = a.cu_seqlens;
     p.T = a.T;
     p.W = a.W;
@@ -947,13 +1134,19 @@ int launch_c(const LaunchArgs& a, hipStream_t s, char* msg, int len)
     }
 }
 
-template <int DT>
+template <int DT, int G>
 int launch_m(const LaunchArgs& a, hipStream_t s, char* msg, int len)
 {
     const bool wu = a.W != nullptr, t = a.T != nullptr;
-    if (wu && t) return launch_c<DT, kModeT | kModeWU>(a, s, msg, len);
-    if (wu) return launch_c<DT, kModeWU>(a, s, msg, len);
-    return launch_c<DT, kModeT>(a, s, msg, len);
+    if (wu && t) return launch_c<DT, kModeT | kModeWU | G>(a, s, msg, len);
+    if (wu) return launch_c<DT, kModeWU | G>(a, s, msg, len);
+    return launch_c<DT, kModeT | G>(a, s, msg, len);
+}
+
+template <int DT>
+int launch_g(const LaunchArgs& a, hipStream_t s, char* msg, int len)
+{
+    return a.g != nullptr ? launch_m<DT, kModeGate>(a, s, msg, len) : launch_m<DT, 0>(a, s, msg, len);
 }
 
 }  // namespace
@@ -961,7 +1154,7 @@ int launch_m(const LaunchArgs& a, hipStream_t s, char* msg, int len)
 int launch(const LaunchArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return a.kv_dtype == 0 ? launch_m<0>(a, s, msg, msg_len) : launch_m<1>(a, s, msg, msg_len);
+    return a.kv_dtype == 0 ? launch_g<0>(a, s, msg, msg_len) : launch_g<1>(a, s, msg, msg_len);
 }
 
 }  // namespace wyp

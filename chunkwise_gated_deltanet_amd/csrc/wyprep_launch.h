@@ -11,6 +11,7 @@ struct LaunchArgs {
     const void* k;
     const void* v;            // nullptr for kkt_solve
     const float* beta;
+    const float* g;           // nullptr: no gates
     const int32_t* cu_seqlens;  // nullptr: B x T layout
     float* T;                 // nullptr for wu_prepare
     void* W;                  // nullptr for kkt_solve

@@ -17,10 +17,23 @@
  *     W = T diag(beta) K,   U = T diag(beta) V
  * K is the chunk's keys of key head h / (Hv/Hq), V its values of value head h.
  *
+ * Gates (optional; g == NULL means alpha = 1 everywhere and gives exactly the lines above).
+ * [Inv] section 5, item 12 states the gated coefficient diag(beta)(Gamma o K K^T); [QLA]
+ * usage passes g [B,T,Hv] beside beta.  g_t = log alpha_t is the per-token log decay of the
+ * value head (finite; alpha_t in (0, 1] is the decaying regime the tolerances are stated for).
+ * With G_i = g_0 + ... + g_i summed over the chunk's own tokens (restarting at every chunk)
+ * and Gamma[i][j] = exp(G_i - G_j), the decay from token j to token i:
+ *     A = I + strictLower(diag(beta) (Gamma o K K^T)),   T = A^{-1}
+ *     W = T diag(beta exp(G)) K,   U = T diag(beta) V
+ * These W and U are the ones the gated delta rule S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T)
+ * + beta_t v_t k_t^T needs to advance a chunk in one step (the recurrence the FlashQLA page
+ * recalls, with alpha_i in (0, 1)).
+ *
  * Layouts (row-major, contiguous, token-major as in [QLA] usage):
  *   k      [B, T, Hq, dk]    dtype kv_dtype
  *   v      [B, T, Hv, dv]    dtype kv_dtype
  *   beta   [B, T, Hv]        float32
+ *   g      [B, T, Hv]        float32 log gates, or NULL
  *   T_out  [B, T, Hv, C]     float32; row t holds row (t - chunk start) of its chunk's T with
  *                            chunk-relative columns; every entry right of the diagonal
  *                            (including columns >= n of a short chunk) is written as 0.0 and
@@ -35,7 +48,7 @@
  *
  * Ownership: every tensor pointer is a DEVICE pointer owned by the caller.  The library
  * never allocates, frees or synchronises device memory, keeps no per-call state and needs no
- * workspace.  k, v, T_out, W_out and U_out must be 16-byte aligned; beta and cu_seqlens
+ * workspace.  k, v, T_out, W_out and U_out must be 16-byte aligned; beta, g and cu_seqlens
  * 4-byte aligned.
  *
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
@@ -61,7 +74,7 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 1
+#define WYP_ABI_VERSION 2  /* 2: log gates g on every entry point */
 
 typedef enum {
     WYP_OK = 0,
@@ -96,24 +109,26 @@ const char* wyp_status_string(int32_t status);
 const char* wyp_last_error(void);
 
 /* kkt_solve ([Inv] section 3: takes only K and beta, produces only T): writes T_out for every
- * chunk and value head.  k [B,T,Hq,dk], beta [B,T,Hv], T_out [B,T,Hv,C]. */
-wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* beta,
-                         const int32_t* cu_seqlens, float* T_out, void* stream);
+ * chunk and value head.  k [B,T,Hq,dk], g [B,T,Hv] or NULL, beta [B,T,Hv],
+ * T_out [B,T,Hv,C]. */
+wyp_status wyp_kkt_solve(const wyp_problem* problem, const void* k, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, float* T_out,
+                         void* stream);
 
 /* The full preparation step ([Inv] section 1: T is materialised because both W and U reuse
- * it): writes T_out, W_out = T diag(beta) K and U_out = T diag(beta) V in one pass over K
- * and V. */
+ * it): writes T_out, W_out = T diag(beta) K (T diag(beta exp(G)) K with gates) and
+ * U_out = T diag(beta) V in one pass over K and V. */
 wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void* v,
-                          const float* beta, const int32_t* cu_seqlens, float* T_out,
-                          void* W_out, void* U_out, void* stream);
+                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                          float* T_out, void* W_out, void* U_out, void* stream);
 
 /* W and U without T in HBM ([Inv] section 1: T exists to be reused for W and U; section 2.4:
  * writing T back costs C values per token, the standalone kernel's bottleneck): the same
  * W_out and U_out as wyp_wy_prepare, bit for bit, with T formed on chip and never written.
  * Arguments as in wyp_wy_prepare without T_out; saves 4 C bytes per token and value head. */
 wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void* v,
-                          const float* beta, const int32_t* cu_seqlens, void* W_out,
-                          void* U_out, void* stream);
+                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                          void* W_out, void* U_out, void* stream);
 
 #ifdef __cplusplus
 }

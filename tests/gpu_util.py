@@ -28,10 +28,18 @@ def to_device(inp, device):
     return k.to(device), v.to(device), beta.to(device), cu
 
 
+def gate_of(inp, device):
+    """The inputs' log gates g on the device, or None (ungated)."""
+    import torch
+    g = inp.get("g")
+    return None if g is None else torch.from_numpy(g).to(device)
+
+
 def run_wy(inp, device, sentinel=True, kkt_only=False, stream=None):
     """Runs the HIP path on `inp`; outputs are pre-filled with NaN so unwritten entries show."""
     import torch
     k, v, beta, cu = to_device(inp, device)
+    g = gate_of(inp, device)
     B, T, Hq, dk = k.shape
     Hv = beta.shape[2]
     C = inp["chunk_size"]
@@ -39,13 +47,13 @@ def run_wy(inp, device, sentinel=True, kkt_only=False, stream=None):
     T_out = torch.full((B, T, Hv, C), fill, dtype=torch.float32, device=device)
     if kkt_only:
         with torch.cuda.stream(stream or torch.cuda.current_stream(device)):
-            cg.kkt_solve(k, beta, C, cu_seqlens=cu, T_out=T_out)
+            cg.kkt_solve(k, beta, C, cu_seqlens=cu, T_out=T_out, g=g)
         torch.cuda.synchronize(device)
         return T_out, None, None
     W_out = torch.full((B, T, Hv, dk), fill, dtype=k.dtype, device=device)
     U_out = torch.full((B, T, Hv, v.shape[3]), fill, dtype=k.dtype, device=device)
     with torch.cuda.stream(stream or torch.cuda.current_stream(device)):
-        cg.wy_prepare(k, v, beta, C, cu_seqlens=cu, T_out=T_out, W_out=W_out, U_out=U_out)
+        cg.wy_prepare(k, v, beta, C, cu_seqlens=cu, T_out=T_out, W_out=W_out, U_out=U_out, g=g)
     torch.cuda.synchronize(device)
     return T_out, W_out, U_out
 
@@ -89,7 +97,7 @@ def to_f64(t):
 def compare_full(inp, T_gpu, W_gpu, U_gpu, label=""):
     """Whole-tensor comparison with the oracle; returns the metrics."""
     Tr, Wr, Ur, _ = oracle.wy_prepare(inp["k"], inp["beta"], inp["chunk_size"], v=inp["v"],
-                                      cu_seqlens=inp["cu_seqlens"])
+                                      cu_seqlens=inp["cu_seqlens"], g=inp.get("g"))
     Tg = to_f64(T_gpu)
     assert not np.isnan(Tg).any(), "unwritten T entries"
     dT = float(np.max(np.abs(Tg - Tr))) if Tg.size else 0.0
@@ -125,7 +133,7 @@ def compare_sampled(inp, T_gpu, W_gpu, U_gpu, m=256, label=""):
     starts, lens, heads = sample_units(inp, m)
     C = inp["chunk_size"]
     Tr, Wr, Ur = oracle.units(inp["k"], inp["beta"], C, starts, lens, heads,
-                              v=inp["v"] if W_gpu is not None else None)
+                              v=inp["v"] if W_gpu is not None else None, g=inp.get("g"))
     B, T = inp["batch"], inp["seqlen"]
     Hv = inp["beta"].shape[2]
     Tf = T_gpu.reshape(B * T, Hv, C)

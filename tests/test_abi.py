@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 1
+    assert lib.wyp_abi_version() == 2 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -51,9 +51,9 @@ def good(**kw):
     return cg.Problem(*[d[n] for n, _ in cg.Problem._fields_])
 
 
-def call_wy(lib, p, k=FAKE, v=FAKE, beta=FAKE, cu=None, T=FAKE, W=FAKE, U=FAKE):
-    return lib.wyp_wy_prepare(ctypes.byref(p) if p is not None else None, k, v, beta, cu, T, W,
-                              U, None)
+def call_wy(lib, p, k=FAKE, v=FAKE, beta=FAKE, cu=None, T=FAKE, W=FAKE, U=FAKE, g=None):
+    return lib.wyp_wy_prepare(ctypes.byref(p) if p is not None else None, k, v, g, beta, cu, T,
+                              W, U, None)
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -80,10 +80,15 @@ def test_rejects_null_and_misaligned(lib):
     assert call_wy(lib, good(), T=FAKE + 4) == 1
     assert "16-byte" in lib.wyp_last_error().decode()
     assert call_wy(lib, good(), beta=FAKE + 2) == 1
-    assert lib.wyp_kkt_solve(ctypes.byref(good()), FAKE, FAKE, None, None, None) == 1
+    assert call_wy(lib, good(), g=FAKE + 2) == 1
+    assert "g is not 4-byte" in lib.wyp_last_error().decode()
+    assert lib.wyp_kkt_solve(ctypes.byref(good()), FAKE, None, FAKE, None, None, None) == 1
+    assert lib.wyp_kkt_solve(ctypes.byref(good()), FAKE, FAKE + 1, FAKE, None, FAKE, None) == 1
     # wu_prepare takes no T_out, but needs W_out and U_out
-    assert lib.wyp_wu_prepare(ctypes.byref(good()), FAKE, FAKE, FAKE, None, FAKE, None, None) == 1
-    assert lib.wyp_wu_prepare(ctypes.byref(good()), FAKE, FAKE, FAKE, None, FAKE + 8, FAKE, None) == 1
+    assert lib.wyp_wu_prepare(ctypes.byref(good()), FAKE, FAKE, None, FAKE, None, FAKE, None,
+                              None) == 1
+    assert lib.wyp_wu_prepare(ctypes.byref(good()), FAKE, FAKE, None, FAKE, None, FAKE + 8, FAKE,
+                              None) == 1
     assert "16-byte" in lib.wyp_last_error().decode()
 
 
@@ -99,9 +104,10 @@ def test_empty_problem_is_a_noop(lib):
     assert call_wy(lib, good(seqlen=0)) == 0
     assert lib.wyp_last_error() == b""
     assert call_wy(lib, good(seqlen=0, num_seqs=0), cu=FAKE) == 0
-    assert lib.wyp_kkt_solve(ctypes.byref(good(seqlen=0)), FAKE, FAKE, None, FAKE, None) == 0
+    assert lib.wyp_kkt_solve(ctypes.byref(good(seqlen=0)), FAKE, None, FAKE, None, FAKE,
+                             None) == 0
     assert lib.wyp_wu_prepare(ctypes.byref(good(seqlen=0)), None, None, None, None, None, None,
-                              None) == 0
+                              None, None) == 0
 
 
 def test_error_text_is_per_call(lib):
@@ -117,3 +123,5 @@ def test_binding_rejects_cpu_tensors(lib):
     beta = torch.zeros(1, 4, 1)
     with pytest.raises(ValueError):
         cg.kkt_solve(k, beta, 64)
+    with pytest.raises(ValueError):
+        cg.kkt_solve(k, beta, 64, g=torch.zeros(1, 4, 1))

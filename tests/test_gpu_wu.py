@@ -7,7 +7,7 @@ within the W/U tolerance.
 import pytest
 
 from chunkwise_gated_deltanet_amd import synth
-from gpu_util import compare_full, compare_sampled, run_wy, say, to_device
+from gpu_util import compare_full, compare_sampled, gate_of, run_wy, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,8 @@ def run_wu(inp, device):
     Hv = beta.shape[2]
     W = torch.full((B, T, Hv, dk), float("nan"), dtype=k.dtype, device=device)
     U = torch.full((B, T, Hv, v.shape[3]), float("nan"), dtype=k.dtype, device=device)
-    cg.wu_prepare(k, v, beta, inp["chunk_size"], cu_seqlens=cu, W_out=W, U_out=U)
+    cg.wu_prepare(k, v, beta, inp["chunk_size"], cu_seqlens=cu, W_out=W, U_out=U,
+                  g=gate_of(inp, device))
     torch.cuda.synchronize(device)
     return W, U
 
