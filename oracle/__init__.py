@@ -19,6 +19,9 @@ Parity status of each function (what pins it is listed in tests/test_oracle_pins
   the same with gates g      pinned (gated delta-rule recurrence from zero and from an
                              identity state, the 2-token closed form, g = 0 against no gates,
                              Gamma o T_ungated, chunk restarts)
+  gdn_forward                pinned (delta-rule read-back, beta = 0 decay of h0, orthogonal
+                             keys = linear attention, the chunk form through the pinned W / U,
+                             sequences independent)
   head grouping (v-head h reads k-head h // (Hv/Hq)) and the T layout [B,T,Hv,C]:
                              parity unpinned -- a stated convention, not fixed by the pages.
 """
@@ -71,6 +74,9 @@ def _bind(lib):
     lib.wyo_wy_prepare.restype = ctypes.c_int32
     lib.wyo_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_int32, _P]
+    lib.wyo_gdn_forward.restype = ctypes.c_int32
+    lib.wyo_gdn_forward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_double, _P, _P, _P, _P, ctypes.c_int32]
     lib.wyo_units.restype = ctypes.c_int32
     lib.wyo_units.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.c_int64, _P, _P,
                               _P, _P, _P, _P, ctypes.c_int32]
@@ -218,3 +224,43 @@ def units(k, beta, chunk_size, chunk_start, chunk_len, v_head, v=None, nthreads=
     if rc != 0:
         raise ValueError(f"oracle rejected the units (code {rc})")
     return Tm, W, U
+
+
+def gdn_forward(q, k, v, beta, g=None, h0=None, scale=None, cu_seqlens=None, pairs=None,
+                nthreads=None, lib=None):
+    """The gated delta rule token by token (fp64): returns (o [B,T,Hv,dv], hT [N,Hv,dk,dv]).
+
+    q, k: [B,T,Hq,dk] uint16 (bf16 bits) or float32; v: [B,T,Hv,dv]; beta, g: [B,T,Hv]
+    float32 (g None: alpha = 1); h0: [N,Hv,dk,dv] float32 or None (zeros); scale defaults to
+    dk ** -0.5; pairs: optional iterable of (seq, value head) to compute (others stay 0).
+    """
+    lib = lib or load()
+    k = np.ascontiguousarray(k)
+    q = np.ascontiguousarray(q)
+    v = np.ascontiguousarray(v)
+    if q.dtype != k.dtype or q.shape != k.shape:
+        raise ValueError("q must match k in shape and dtype")
+    beta = _c(beta, np.float32)
+    g = _gate(g, beta)
+    cu = _c(cu_seqlens, np.int32)
+    p = _problem(k, v, beta, 64, cu)
+    B, T, Hq, dk = k.shape
+    Hv, dv = beta.shape[2], v.shape[3]
+    N = B if cu is None else len(cu) - 1
+    if h0 is not None:
+        h0 = np.ascontiguousarray(h0, dtype=np.float32)
+        if h0.shape != (N, Hv, dk, dv):
+            raise ValueError(f"h0 must be {(N, Hv, dk, dv)}")
+    mask = None
+    if pairs is not None:
+        mask = np.zeros(N * Hv, np.uint8)
+        for s, h in pairs:
+            mask[int(s) * Hv + int(h)] = 1
+    o = np.zeros((B, T, Hv, dv), np.float64)
+    hT = np.zeros((N, Hv, dk, dv), np.float64)
+    rc = lib.wyo_gdn_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(h0), float(dk ** -0.5 if scale is None else scale), _ptr(cu),
+                             _ptr(o), _ptr(hT), _ptr(mask), nthreads or os.cpu_count() or 1)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return o, hT

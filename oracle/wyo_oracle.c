@@ -403,3 +403,106 @@ int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const floa
     proto.T = T_out; proto.W = W_out; proto.U = U_out;
     return run_jobs(&proto, nthreads) ? 0 : 2;
 }
+
+/* ---- the gated delta rule, token by token (see wyo_oracle.h) ----------------------------- */
+
+typedef struct {
+    const wyo_problem* p;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* h0;
+    double scale;
+    const int32_t* cu;
+    double* o;
+    double* hT;
+    const uint8_t* mask;
+    int32_t tid, nthreads;
+    int ok;
+} gdn_job;
+
+static void* gdn_run(void* arg)
+{
+    gdn_job* jb = (gdn_job*)arg;
+    const wyo_problem* p = jb->p;
+    const int32_t dk = p->head_dim_k, dv = p->head_dim_v;
+    const int32_t Hq = p->num_qk_heads, Hv = p->num_v_heads;
+    const int64_t nseq = jb->cu ? p->num_seqs : p->batch;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+    jb->ok = S && kt && qt && e;
+    if (jb->ok) {
+        for (int64_t pair = jb->tid; pair < nseq * Hv; pair += jb->nthreads) {
+            if (jb->mask && !jb->mask[pair]) continue;
+            const int64_t seq = pair / Hv;
+            const int32_t hv = (int32_t)(pair % Hv), hk = hv / (Hv / Hq);
+            const int64_t s0 = jb->cu ? jb->cu[seq] : seq * (int64_t)p->seqlen;
+            const int64_t s1 = jb->cu ? jb->cu[seq + 1] : (seq + 1) * (int64_t)p->seqlen;
+            const float* h0 = jb->h0 ? jb->h0 + pair * (int64_t)dk * dv : NULL;
+            for (int64_t i = 0; i < (int64_t)dk * dv; ++i) S[i] = h0 ? (double)h0[i] : 0.0;
+            for (int64_t t = s0; t < s1; ++t) {
+                const double alpha = jb->g ? exp((double)jb->g[t * Hv + hv]) : 1.0;
+                const double b = (double)jb->beta[t * Hv + hv];
+                for (int32_t d = 0; d < dk; ++d) {
+                    kt[d] = load_elem(jb->k, p->kv_dtype, (t * Hq + hk) * dk + d);
+                    qt[d] = load_elem(jb->q, p->kv_dtype, (t * Hq + hk) * dk + d);
+                }
+                /* S <- alpha S; e = beta (v_t - S^T k_t); S <- S + k_t e^T */
+                for (int64_t i = 0; i < (int64_t)dk * dv; ++i) S[i] *= alpha;
+                for (int32_t c = 0; c < dv; ++c) {
+                    double r = 0.0;
+                    for (int32_t d = 0; d < dk; ++d) r += kt[d] * S[(int64_t)d * dv + c];
+                    e[c] = b * (load_elem(jb->v, p->kv_dtype, (t * Hv + hv) * dv + c) - r);
+                }
+                for (int32_t d = 0; d < dk; ++d)
+                    for (int32_t c = 0; c < dv; ++c) S[(int64_t)d * dv + c] += kt[d] * e[c];
+                /* o_t = scale S^T q_t */
+                for (int32_t c = 0; c < dv; ++c) {
+                    double r = 0.0;
+                    for (int32_t d = 0; d < dk; ++d) r += qt[d] * S[(int64_t)d * dv + c];
+                    jb->o[(t * Hv + hv) * (int64_t)dv + c] = jb->scale * r;
+                }
+            }
+            if (jb->hT)
+                memcpy(jb->hT + pair * (int64_t)dk * dv, S, sizeof(double) * (size_t)dk * (size_t)dv);
+        }
+    }
+    free(S); free(kt); free(qt); free(e);
+    return NULL;
+}
+
+int32_t wyo_gdn_forward(const wyo_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, double scale,
+                        const int32_t* cu, double* o_out, double* hT_out,
+                        const uint8_t* pair_mask, int32_t nthreads)
+{
+    if (!problem_ok(p, cu) || !q || !k || !v || !beta || !o_out) return 1;
+    if (nthreads <= 0) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    gdn_job* jobs = (gdn_job*)calloc((size_t)nthreads, sizeof(gdn_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return 2; }
+    for (int32_t t = 0; t < nthreads; ++t) {
+        gdn_job* jb = &jobs[t];
+        jb->p = p; jb->q = q; jb->k = k; jb->v = v; jb->g = g; jb->beta = beta; jb->h0 = h0;
+        jb->scale = scale; jb->cu = cu; jb->o = o_out; jb->hT = hT_out; jb->mask = pair_mask;
+        jb->tid = t; jb->nthreads = nthreads;
+    }
+    int32_t started = 0;
+    for (int32_t t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, gdn_run, &jobs[t]) != 0) break;
+        started = t;
+    }
+    for (int32_t t = started + 1; t < nthreads; ++t) gdn_run(&jobs[t]);
+    gdn_run(&jobs[0]);
+    for (int32_t t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    int ok = 1;
+    for (int32_t t = 0; t < nthreads; ++t) ok = ok && jobs[t].ok;
+    free(jobs);
+    free(th);
+    return ok ? 0 : 2;
+}

@@ -98,6 +98,23 @@ int32_t wyo_units(const wyo_problem* p, const void* k, const void* v, const floa
                   const int32_t* v_head, double* T_out, double* W_out, double* U_out,
                   int32_t nthreads);
 
+/* The gated delta rule itself, token by token -- the recurrence whose chunk form the WY / UT
+ * preparation serves ([Inv] section 1: the chunk's C Householder transforms; [QLA] gate section:
+ * the GDN recurrence with alpha_i in (0, 1), whose formula did not survive extraction; [QLA]
+ * usage: o, final_state = chunk_gated_delta_rule(q, k, v, g, beta, scale, initial_state, ...)
+ * with initial_state [B, Hv, K, V]).  Per sequence and value head h (key / query head
+ * h / (Hv/Hq)), with S the dk x dv state:
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   alpha_t = exp(g_t)
+ *     o_t = scale * S_t^T q_t                      (read after token t's own write)
+ * S_{-1} = h0[seq][h] (zeros when h0 is NULL).  q, k [B,T,Hq,dk]; v [B,T,Hv,dv]; g, beta
+ * [B,T,Hv]; h0, hT_out [N,Hv,dk,dv] with N = num_seqs (cu_seqlens) or B; o_out [B,T,Hv,dv].
+ * Outputs fp64.  pair_mask [N*Hv] (may be NULL = all): only pairs (seq, head) with a nonzero
+ * byte are computed; the rest of o_out / hT_out is left untouched.  Returns 0 on success. */
+int32_t wyo_gdn_forward(const wyo_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, double scale,
+                        const int32_t* cu_seqlens, double* o_out, double* hT_out,
+                        const uint8_t* pair_mask, int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif

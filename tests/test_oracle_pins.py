@@ -411,11 +411,119 @@ def pin_gated_chunk_restart(lib):
             assert np.array_equal(U[0, t0:t0 + n, h], Uu)
 
 
+# ---------------------------------------------------------------------------------------------
+# the gated delta rule, token by token (oracle.gdn_forward): the recurrence the chunk step
+# serves.  S_t = alpha_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T, o_t = scale S_t^T q_t.
+
+def seq_inputs(rng, T, Hq=1, Hv=1, dk=128, dv=128):
+    k = rng.standard_normal((1, T, Hq, dk))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    q = rng.standard_normal((1, T, Hq, dk)).astype(np.float32)
+    v = rng.standard_normal((1, T, Hv, dv)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (1, T, Hv)).astype(np.float32)
+    return q, k, v, beta
+
+
+def pin_gdn_read_back(lib):
+    """The delta rule stores v_t under key k_t: with beta_t = 1 and |k_t| = 1, reading the
+    state with q_t = k_t right after token t's write returns exactly v_t."""
+    rng = np.random.default_rng(40)
+    _, k, v, _ = seq_inputs(rng, 50)
+    k64 = k.astype(np.float64)
+    k = (k64 / np.linalg.norm(k64, axis=-1, keepdims=True)).astype(np.float32)
+    beta = np.ones((1, 50, 1), np.float32)
+    o, _ = oracle.gdn_forward(k, k, v, beta, scale=0.5, lib=lib, nthreads=1)
+    kk = np.sum(k.astype(np.float64) ** 2, axis=-1)  # |k|^2 in fp64 (1 up to fp32 rounding)
+    # exact: S_t^T k_t = S'^T k_t (1 - |k|^2) + v_t |k|^2
+    assert np.max(np.abs(o - 0.5 * v.astype(np.float64) * kk[..., None])) <= 1e-6
+    assert np.max(np.abs(o - 0.5 * v)) <= 1e-5
+
+
+def pin_gdn_beta_zero(lib):
+    """beta = 0: nothing is written, the initial state only decays, S_t = exp(G_t) h0 with G the
+    running sum of g over the whole sequence; o_t = scale exp(G_t) h0^T q_t.  A non-symmetric
+    h0 fixes its layout [dk][dv]."""
+    rng = np.random.default_rng(41)
+    T, dk, dv = 40, 128, 64
+    q, k, v, _ = seq_inputs(rng, T, dv=dv)
+    beta = np.zeros((1, T, 1), np.float32)
+    g = (-rng.uniform(0, 0.2, (1, T, 1))).astype(np.float32)
+    h0 = rng.standard_normal((1, 1, dk, dv)).astype(np.float32)
+    o, hT = oracle.gdn_forward(q, k, v, beta, g=g, h0=h0, scale=0.3, lib=lib, nthreads=1)
+    G = np.cumsum(g[0, :, 0].astype(np.float64))
+    H = h0[0, 0].astype(np.float64)
+    expect = 0.3 * np.exp(G)[:, None] * (q[0, :, 0].astype(np.float64) @ H)
+    assert np.max(np.abs(o[0, :, 0] - expect)) <= 1e-12
+    assert np.max(np.abs(hT[0, 0] - math.exp(G[-1]) * H)) <= 1e-12
+
+
+def pin_gdn_linear_attention(lib):
+    """Orthonormal keys, no decay, zero initial state: every k_t^T S_{t-1} is 0, so the rule
+    is plain linear attention, o_t = scale sum_{i <= t} b_i (q_t . k_i) v_i, and the final state
+    is sum_i b_i k_i v_i^T."""
+    rng = np.random.default_rng(42)
+    T = 96
+    q, _, v, beta = seq_inputs(rng, T)
+    k = np.zeros((1, T, 1, 128), np.float32)
+    k[0, np.arange(T), 0, rng.permutation(128)[:T]] = 1.0
+    o, hT = oracle.gdn_forward(q, k, v, beta, scale=0.7, lib=lib, nthreads=1)
+    Q, K, V = (a[0, :, 0].astype(np.float64) for a in (q, k, v))
+    b = beta[0, :, 0].astype(np.float64)
+    expect = 0.7 * np.tril(Q @ K.T) @ (b[:, None] * V)
+    assert np.max(np.abs(o[0, :, 0] - expect)) <= 1e-12
+    assert np.max(np.abs(hT[0, 0] - K.T @ (b[:, None] * V))) <= 1e-12
+
+
+def pin_gdn_chunk_form(lib):
+    """The recurrence agrees with its chunk form built from the (separately pinned) W and U:
+    per chunk with start state S, V' = U - W S, o_i = scale (e^{G_i} q_i^T S +
+    sum_{j <= i} Gamma[i][j] (q_i . k_j) V'_j) and the next state e^{G_n} S +
+    K^T diag(e^{G_n - G}) V'.  Grouped value heads, gates, a nonzero initial state."""
+    rng = np.random.default_rng(43)
+    T, C, Hq, Hv = 150, 64, 2, 4
+    q, k, v, beta = seq_inputs(rng, T, Hq=Hq, Hv=Hv)
+    g = np.stack([unit_gates(rng, T, mu) for mu in (3.0, 1.0, 4.0, 2.0)], -1)[None]
+    g = g.astype(np.float32)
+    h0 = (0.3 * rng.standard_normal((1, Hv, 128, 128))).astype(np.float32)
+    o, hT = oracle.gdn_forward(q, k, v, beta, g=g, h0=h0, scale=0.25, lib=lib, nthreads=2)
+    for h in range(Hv):
+        hk = h // (Hv // Hq)
+        S = h0[0, h].astype(np.float64)
+        for t0 in range(0, T, C):
+            n = min(C, T - t0)
+            sl = slice(t0, t0 + n)
+            _, W, U = one_unit(lib, k[0, sl, hk], v[0, sl, h], beta[0, sl, h], C=C,
+                               g=g[0, sl, h])
+            Q, K = q[0, sl, hk].astype(np.float64), k[0, sl, hk].astype(np.float64)
+            G = np.cumsum(g[0, sl, h].astype(np.float64))
+            Vn = U - W @ S
+            Gam = np.tril(np.exp(G[:, None] - G[None, :]))
+            oc = 0.25 * (np.exp(G)[:, None] * (Q @ S) + (Gam * (Q @ K.T)) @ Vn)
+            assert np.max(np.abs(o[0, sl, h] - oc)) <= 1e-11
+            S = math.exp(G[-1]) * S + K.T @ (np.exp(G[-1] - G)[:, None] * Vn)
+        assert np.max(np.abs(hT[0, h] - S)) <= 1e-11
+
+
+def pin_gdn_sequences_independent(lib):
+    """Packed sequences each start from their own initial state (zeros here): the packed run
+    equals each sequence run alone."""
+    rng = np.random.default_rng(44)
+    lens = [37, 64, 5]
+    q, k, v, beta = seq_inputs(rng, sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o, hT = oracle.gdn_forward(q, k, v, beta, cu_seqlens=cu, lib=lib, nthreads=1)
+    for s in range(3):
+        sl = slice(cu[s], cu[s + 1])
+        o1, h1 = oracle.gdn_forward(q[:, sl], k[:, sl], v[:, sl], beta[:, sl], lib=lib, nthreads=1)
+        assert np.array_equal(o[:, sl], o1) and np.array_equal(hT[s], h1[0])
+
+
 PINS = [pin_closed_form_2, pin_orthogonal, pin_residual_structure, pin_lapack_inverse,
         pin_block_identity, pin_beta_zero, pin_subdiag_only, pin_identical_keys,
         pin_fma_counts, pin_householder_product, pin_delta_rule, pin_tail_padding, pin_layout,
         pin_head_grouping, pin_gate_zero, pin_gated_closed_form_2, pin_gated_recurrence,
-        pin_gated_similarity, pin_gated_chunk_restart]
+        pin_gated_similarity, pin_gated_chunk_restart, pin_gdn_read_back, pin_gdn_beta_zero,
+        pin_gdn_linear_attention, pin_gdn_chunk_form, pin_gdn_sequences_independent]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -502,6 +610,18 @@ MUTANTS = {
                           "acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->K"),
     "gate_on_u": ("acc += (s->X[(int64_t)i * n + j] * s->b[j]) * s->V",
                   "acc += (s->X[(int64_t)i * n + j] * s->b[j] * s->E[j]) * s->V"),
+    # the token-by-token recurrence
+    "gdn_delta_sign": ("S[(int64_t)d * dv + c] += kt[d] * e[c];",
+                       "S[(int64_t)d * dv + c] -= kt[d] * e[c];"),
+    "gdn_beta_dropped": ("e[c] = b * (load_elem", "e[c] = (load_elem"),
+    "gdn_decay_dropped": ("S[i] *= alpha;", "S[i] *= 1.0;"),
+    "gdn_q_head_modulo": ("hk = hv / (Hv / Hq);\n            const int64_t s0",
+                          "hk = hv % Hq;\n            const int64_t s0"),
+    "gdn_h0_transposed": ("S[i] = h0 ? (double)h0[i] : 0.0;",
+                          "S[i] = h0 ? (double)h0[(i % dv) * dk + i / dv] : 0.0;"),
+    "gdn_scale_dropped": ("= jb->scale * r;", "= r;"),
+    "gdn_state_not_reset": ("for (int64_t i = 0; i < (int64_t)dk * dv; ++i) S[i] = h0 ?",
+                            "if (seq == 0) for (int64_t i = 0; i < (int64_t)dk * dv; ++i) S[i] = h0 ?"),
     "gate_not_restarted": ("s->G[i] = (i == 0 ? 0.0 : s->G[i - 1]) + gi;",
                            "s->G[i] = (i == 0 ? (gate && tok0 > 0 ? (double)gate[(tok0 - 1) * Hv + hv] "
                            ": 0.0) : s->G[i - 1]) + gi;"),
