@@ -18,14 +18,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "wyp_wy_prepare", "wyp_kkt_solve",
-           "wyp_wu_prepare", "load_library", "Problem", "LIB_PATH", "WyprepError"]
+__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "chunk_fwd", "chunk_gated_delta_rule",
+           "wyp_wy_prepare", "wyp_kkt_solve", "wyp_wu_prepare", "wyp_chunk_fwd", "load_library",
+           "Problem", "LIB_PATH", "WyprepError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.so")
 
 WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
 WYP_BF16, WYP_F32 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class WyprepError(RuntimeError):
@@ -70,6 +71,9 @@ def load_library(path: str | None = None):
     lib.wyp_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.wyp_wu_prepare.restype = ctypes.c_int32
     lib.wyp_wu_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.wyp_chunk_fwd.restype = ctypes.c_int32
+    lib.wyp_chunk_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                  _P, _P, _P, _P]
     if lib.wyp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{p} has ABI version {lib.wyp_abi_version()}, this binding expects "
                            f"{ABI_VERSION}: rebuild it")
@@ -216,7 +220,73 @@ def wu_prepare(k, v, beta, chunk_size, cu_seqlens=None, W_out=None, U_out=None, 
     return W_out, U_out
 
 
+def chunk_fwd(q, k, w, u, chunk_size=64, g=None, initial_state=None, scale=None,
+              cu_seqlens=None, output_final_state=False, o_out=None, final_state=None):
+    """(o, final_state) of the gated delta rule from q, k and the chunk's W, U (as returned by
+    wy_prepare / wu_prepare for the same k, beta, g); see wyp_chunk_fwd.  q, k [B,T,Hq,128],
+    w, u [B,T,Hv,128] bf16; g [B,T,Hv] float32 or None; initial_state [N,Hv,128,128] float32
+    or None.  final_state is None unless output_final_state (or a final_state buffer)."""
+    import torch
+    lib = load_library()
+    device = k.device
+    _require(q, "q", 4, device)
+    _require(k, "k", 4, device)
+    _require(w, "w", 4, device)
+    _require(u, "u", 4, device)
+    if q.shape != k.shape or q.dtype != k.dtype or w.dtype != k.dtype or u.dtype != k.dtype:
+        raise ValueError("q must match k; w, u must share k's dtype")
+    B, T, Hq, dk = k.shape
+    Hv = w.shape[2]
+    if w.shape[:2] != (B, T) or u.shape[:3] != (B, T, Hv):
+        raise ValueError(f"w {tuple(w.shape)} / u {tuple(u.shape)} do not match k {tuple(k.shape)}")
+    dv = u.shape[3]
+    n = 0
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", 1, device)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        n = cu_seqlens.numel() - 1
+    N = n if cu_seqlens is not None else B
+    gp = None
+    if g is not None:
+        _require(g, "g", 3, device)
+        if g.dtype != torch.float32 or tuple(g.shape) != (B, T, Hv):
+            raise ValueError(f"g must be float32 of shape {(B, T, Hv)}")
+        gp = g.data_ptr()
+    h0p = None
+    if initial_state is not None:
+        _require(initial_state, "initial_state", 4, device)
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (N, Hv, dk, dv):
+            raise ValueError(f"initial_state must be float32 of shape {(N, Hv, dk, dv)}")
+        h0p = initial_state.data_ptr()
+    p = Problem(B, T, Hq, Hv, dk, dv, int(chunk_size), n, _kv_dtype(k))
+    o_out = _out(o_out, (B, T, Hv, dv), k.dtype, device, "o_out")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=device)
+    elif final_state is not None:
+        final_state = _out(final_state, (N, Hv, dk, dv), torch.float32, device, "final_state")
+    sc = float(dk ** -0.5 if scale is None else scale)
+    st = lib.wyp_chunk_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), w.data_ptr(),
+                           u.data_ptr(), gp, h0p, sc,
+                           cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                           o_out.data_ptr(), final_state.data_ptr() if final_state is not None else None,
+                           _stream(device))
+    _check(lib, st)
+    return o_out, final_state
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
+                           output_final_state=False, cu_seqlens=None, chunk_size=64):
+    """The gated DeltaNet chunked forward with the argument list of the FlashQLA usage section:
+    wu_prepare (W, U for every chunk; T stays on chip) followed by chunk_fwd.  g may be None
+    (no gates).  Returns (o, final_state); final_state is None unless output_final_state."""
+    w, u = wu_prepare(k, v, beta, chunk_size, cu_seqlens=cu_seqlens, g=g)
+    return chunk_fwd(q, k, w, u, chunk_size, g=g, initial_state=initial_state, scale=scale,
+                     cu_seqlens=cu_seqlens, output_final_state=output_final_state)
+
+
 # The C-ABI names, for callers that mirror the header.
 wyp_kkt_solve = kkt_solve
 wyp_wy_prepare = wy_prepare
 wyp_wu_prepare = wu_prepare
+wyp_chunk_fwd = chunk_fwd

@@ -114,6 +114,75 @@ wyp_status run(const wyp_problem* p, const void* k, const void* v, const float* 
     return WYP_OK;
 }
 
+wyp_status validate_fwd(const wyp_problem* p, const void* q, const void* k, const void* w,
+                        const void* u, const float* g, const float* h0, float scale,
+                        const int32_t* cu, const void* o, const float* hT, wyp::FwdArgs* out,
+                        bool* empty)
+{
+    *empty = false;
+    if (!p) return fail(WYP_ERR_INVALID_ARGUMENT, "problem is NULL");
+    if (p->batch < 1) return fail(WYP_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
+    if (p->seqlen < 0) return fail(WYP_ERR_INVALID_ARGUMENT, "seqlen must be >= 0 (got %d)", p->seqlen);
+    if (p->num_qk_heads < 1 || p->num_v_heads < 1)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Hq=%d, Hv=%d)",
+                    p->num_qk_heads, p->num_v_heads);
+    if (p->num_v_heads % p->num_qk_heads != 0)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "Hv (%d) must be a multiple of Hq (%d)",
+                    p->num_v_heads, p->num_qk_heads);
+    if (p->kv_dtype != WYP_BF16 && p->kv_dtype != WYP_F32)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "kv_dtype %d is not a wyp_dtype", p->kv_dtype);
+    if (p->kv_dtype != WYP_BF16)
+        return fail(WYP_ERR_UNSUPPORTED, "wyp_chunk_fwd is built for bf16 q, k, W, U only");
+    if (p->head_dim_k != 128 || p->head_dim_v != 128)
+        return fail(WYP_ERR_UNSUPPORTED, "only head_dim_k = head_dim_v = 128 is built (got %d, %d)",
+                    p->head_dim_k, p->head_dim_v);
+    if (p->chunk_size != 64)
+        return fail(WYP_ERR_UNSUPPORTED, "wyp_chunk_fwd is built for chunk_size 64 (got %d)",
+                    p->chunk_size);
+    if (!(scale == scale) || scale == 1.0f / 0.0f || scale == -1.0f / 0.0f)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (cu) {
+        if (p->batch != 1)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)", p->batch);
+        if (p->num_seqs < 0)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", p->num_seqs);
+        if (p->num_seqs == 0 && p->seqlen != 0)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "num_seqs == 0 with %d tokens", p->seqlen);
+        if (!aligned(cu, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    }
+    const int64_t nseq = cu ? p->num_seqs : p->batch;
+    const int64_t work = nseq * p->num_v_heads * 4;  // (sequence, value head, dv slice)
+    if (work + 8 > INT32_MAX)
+        return fail(WYP_ERR_UNSUPPORTED, "problem has %lld work items, more than one launch holds",
+                    static_cast<long long>(work));
+    const int64_t tokens = static_cast<int64_t>(p->batch) * p->seqlen;
+    if (nseq == 0 || (tokens == 0 && !hT)) {  // nothing to read or write
+        *empty = true;
+        return WYP_OK;
+    }
+    if (tokens > 0 && (!q || !k || !w || !u || !o))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "q, k, W, U and o_out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 16) || !aligned(u, 16) || !aligned(o, 16))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "q, k, W, U and o_out must be 16-byte aligned");
+    if ((g && !aligned(g, 4)) || (h0 && !aligned(h0, 4)) || (hT && !aligned(hT, 4)))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "g, initial_state and final_state must be 4-byte aligned");
+    out->q = q;
+    out->k = k;
+    out->w = w;
+    out->u = u;
+    out->g = g;
+    out->h0 = h0;
+    out->cu_seqlens = cu;
+    out->o = const_cast<void*>(o);
+    out->hT = const_cast<float*>(hT);
+    out->scale = scale;
+    out->seqlen = p->seqlen;
+    out->num_qk_heads = p->num_qk_heads;
+    out->num_v_heads = p->num_v_heads;
+    out->num_seqs = static_cast<int32_t>(nseq);
+    return WYP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,3 +224,21 @@ wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void*
 }
 
 }  // extern "C"
+
+extern "C" wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* k,
+                                    const void* w, const void* u, const float* g,
+                                    const float* initial_state, float scale,
+                                    const int32_t* cu_seqlens, void* o_out, float* final_state,
+                                    void* stream)
+{
+    g_last_error[0] = '\0';
+    wyp::FwdArgs args{};
+    bool empty = false;
+    const wyp_status st = validate_fwd(problem, q, k, w, u, g, initial_state, scale, cu_seqlens,
+                                       o_out, final_state, &args, &empty);
+    if (st != WYP_OK || empty) return st;
+    char msg[256] = "";
+    if (wyp::launch_fwd(args, stream, msg, sizeof msg) != 0)
+        return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
+    return WYP_OK;
+}

@@ -29,4 +29,24 @@ struct LaunchArgs {
 // Enqueues the kernel on `stream`.  Returns 0 or the hipError_t value; fills `msg` on error.
 int launch(const LaunchArgs& a, void* stream, char* msg, int msg_len);
 
+// Validated chunked forward (state recurrence and output), ready to launch.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* w;
+    const void* u;
+    const float* g;            // nullptr: no gates
+    const float* h0;           // nullptr: zero initial state
+    const int32_t* cu_seqlens;
+    void* o;
+    float* hT;                 // nullptr: final state not written
+    float scale;
+    int32_t seqlen;
+    int32_t num_qk_heads;
+    int32_t num_v_heads;
+    int32_t num_seqs;          // sequences (cu_seqlens) or batch rows
+};
+
+int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len);
+
 }  // namespace wyp

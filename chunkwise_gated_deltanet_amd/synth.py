@@ -17,7 +17,10 @@ Recipe (one numpy PCG64 generator per workload, seeded with the workload's seed)
      alpha = exp(g) lies in (0, 1).  mu = 4 puts alpha near 0.98 (0.88 .. 0.9975 within two
      standard deviations): a chunk of 64 tokens decays by about e^-1.6, and 6-8 chunks by
      e^-10 or more, the regime in which the FlashQLA page reports its gate warm-up working.
-     Drawn last, so k, v and beta do not depend on whether gates are drawn.
+     Drawn after beta, so k, v and beta do not depend on whether gates are drawn;
+  7. forward inputs only: q ~ N(0, 1) in float32, shape [B, T, Hq, dk], drawn like k and
+     L2-normalised per (token, head) like k, then rounded to bf16 (bf16 workloads).  Drawn
+     last.
 
 Workload shapes follow the head configurations the pages benchmark GDN on (value heads 64 down
 to 8 at d_k = d_v = 128) and the page's chunk sizes C in {32, 64, 128}.
@@ -62,6 +65,7 @@ class Workload:
     seed: int
     seq_range: tuple | None = None   # (lo, hi, count) for packed sequences
     gate_mu: float | None = None     # None: no gates; else g = log sigmoid(gate_mu + N(0,1))
+    with_q: bool = False             # also draw the queries q (the chunked forward's input)
     note: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -139,22 +143,28 @@ def generate(w: Workload) -> dict:
     if w.gate_mu is not None:
         y = rng.standard_normal((B, T, w.num_v_heads), dtype=np.float32)
         g = (-np.logaddexp(np.float32(0), -(np.float32(w.gate_mu) + y))).astype(np.float32)
+    q = None
+    if w.with_q:
+        q = _draw_normal(rng, (B, T, w.num_qk_heads, w.head_dim_k))
+        qn = np.sqrt(np.sum(q * q, axis=-1, keepdims=True, dtype=np.float32), dtype=np.float32)
+        q = (q / qn).astype(np.float32)
     if w.dtype == "bf16":
         k = f32_to_bf16_bits(k)
         v = f32_to_bf16_bits(v)
+        q = None if q is None else f32_to_bf16_bits(q)
     elif w.dtype != "f32":
         raise ValueError(w.dtype)
-    return dict(k=k, v=v, beta=beta, g=g, cu_seqlens=cu, batch=B, seqlen=T,
+    return dict(k=k, v=v, beta=beta, g=g, q=q, cu_seqlens=cu, batch=B, seqlen=T,
                 chunk_size=w.chunk_size, num_qk_heads=w.num_qk_heads,
                 num_v_heads=w.num_v_heads, dtype=w.dtype, name=w.name)
 
 
 def custom(batch, seqlen, num_qk_heads, num_v_heads, chunk_size, dtype="bf16", seed=0,
-           beta_sigma=1.0, seqlens=None, head_dim=128, gate_mu=None) -> dict:
+           beta_sigma=1.0, seqlens=None, head_dim=128, gate_mu=None, with_q=False) -> dict:
     """Inputs for an arbitrary shape, same recipe.  `seqlens` (list) makes a packed batch;
-    `gate_mu` (float) adds log gates g."""
+    `gate_mu` (float) adds log gates g; `with_q` adds queries q."""
     w = Workload("custom", batch, seqlen, num_qk_heads, num_v_heads, head_dim, head_dim,
-                 chunk_size, dtype, beta_sigma, seed, gate_mu=gate_mu)
+                 chunk_size, dtype, beta_sigma, seed, gate_mu=gate_mu, with_q=with_q)
     if seqlens is not None:
         rng_lens = np.asarray(seqlens, np.int64)
         w.batch, w.seqlen = 1, int(rng_lens.sum())

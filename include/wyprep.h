@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 2  /* 2: log gates g on every entry point */
+#define WYP_ABI_VERSION 3  /* 2: log gates g on every entry point; 3: wyp_chunk_fwd */
 
 typedef enum {
     WYP_OK = 0,
@@ -129,6 +129,36 @@ wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void*
 wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void* v,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           void* W_out, void* U_out, void* stream);
+
+/* The chunked forward that consumes W and U ([QLA] "FLA GDN Chunked Prefill 面临的主要问题":
+ * after the WY step the pipeline carries the state across chunks and forms the output; [QLA]
+ * usage: o, final_state = chunk_gated_delta_rule(q, k, v, g, beta, scale, initial_state,
+ * output_final_state, cu_seqlens)).  Per sequence and value head h (key / query head
+ * h / (Hv/Hq)) it advances the dk x dv state S of the gated delta rule
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale S_t^T q_t
+ * one chunk at a time: with G, Gamma as above and S the state at the chunk start,
+ *     V' = U - W S,   O = scale (diag(exp(G)) Q S + (Gamma o tril(Q K^T)) V'),
+ *     S <- exp(G_{C-1}) S + K^T diag(exp(G_{C-1} - G)) V'.
+ * W and U must be what wyp_wy_prepare / wyp_wu_prepare returned for the same k, beta, g,
+ * cu_seqlens and chunk size (g NULL there and here, or the same g in both).
+ *   q, k             [B, T, Hq, dk]   kv_dtype
+ *   w_in, u_in       [B, T, Hv, dk] / [B, T, Hv, dv]   kv_dtype
+ *   g                [B, T, Hv] float32 log gates, or NULL
+ *   initial_state    [N, Hv, dk, dv] float32 (row dk, column dv), or NULL for zeros;
+ *                    N = num_seqs with cu_seqlens, else B
+ *   scale            finite float multiplying every output (dk^-1/2 is the usual choice)
+ *   o_out            [B, T, Hv, dv]   kv_dtype
+ *   final_state      [N, Hv, dk, dv] float32, or NULL (not written)
+ * The state stays fp32 on chip for the whole sequence; its products with W and Q take it
+ * rounded to bf16.  Work is split over (sequence, value head, 32-column slice of dv).
+ * Supported: kv_dtype WYP_BF16, chunk_size 64, dk = dv = 128 (else WYP_ERR_UNSUPPORTED).
+ * q, k, w_in, u_in and o_out must be 16-byte aligned; g, the states 4-byte aligned.
+ * initial_state and final_state may be the same buffer (an in-place state update): each
+ * workgroup reads its own slice of the initial state first and writes only that slice last. */
+wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* k,
+                         const void* w_in, const void* u_in, const float* g,
+                         const float* initial_state, float scale, const int32_t* cu_seqlens,
+                         void* o_out, float* final_state, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,13 +29,13 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
-                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare"}
+                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_chunk_fwd"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 2 == cg.ABI_VERSION
+    assert lib.wyp_abi_version() == 3 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -125,3 +125,42 @@ def test_binding_rejects_cpu_tensors(lib):
         cg.kkt_solve(k, beta, 64)
     with pytest.raises(ValueError):
         cg.kkt_solve(k, beta, 64, g=torch.zeros(1, 4, 1))
+
+
+def call_fwd(lib, p, q=FAKE, k=FAKE, w=FAKE, u=FAKE, g=None, h0=None, scale=0.5, cu=None,
+             o=FAKE, hT=None):
+    return lib.wyp_chunk_fwd(ctypes.byref(p) if p is not None else None, q, k, w, u, g, h0,
+                             scale, cu, o, hT, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(chunk_size=32), 2, "chunk_size"),
+    (dict(chunk_size=128), 2, "chunk_size"),
+    (dict(kv_dtype=1), 2, "bf16"),
+    (dict(head_dim_v=64), 2, "head_dim"),
+    (dict(num_v_heads=3), 1, "multiple"),
+    (dict(batch=0), 1, "batch"),
+])
+def test_chunk_fwd_rejects_bad_problem(lib, kw, code, needle):
+    assert call_fwd(lib, good(**kw)) == code
+    assert needle in lib.wyp_last_error().decode()
+
+
+def test_chunk_fwd_rejects_bad_arguments(lib):
+    assert call_fwd(lib, None) == 1
+    assert call_fwd(lib, good(), q=None) == 1
+    assert call_fwd(lib, good(), o=None) == 1
+    assert call_fwd(lib, good(), w=FAKE + 8) == 1
+    assert "16-byte" in lib.wyp_last_error().decode()
+    assert call_fwd(lib, good(), hT=FAKE + 2) == 1
+    assert call_fwd(lib, good(), scale=float("nan")) == 1
+    assert "scale" in lib.wyp_last_error().decode()
+    assert call_fwd(lib, good(), scale=float("inf")) == 1
+    assert call_fwd(lib, good(batch=2, num_seqs=2), cu=FAKE) == 1
+
+
+def test_chunk_fwd_empty_is_a_noop(lib):
+    # no tokens and no final state requested: nothing to do, no pointer is touched
+    assert call_fwd(lib, good(seqlen=0), q=None, k=None, w=None, u=None, o=None) == 0
+    assert call_fwd(lib, good(seqlen=0, num_seqs=0), cu=FAKE, q=None, k=None, w=None, u=None,
+                    o=None, hT=FAKE) == 0
