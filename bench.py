@@ -29,8 +29,11 @@ if ROOT not in sys.path:
 METRIC = "chunks/s (tokens/s) for kkt_solve+W/U at C=64; achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 768 << 20  # rotated footprint: three times the Infinity Cache
-KERNEL_SOURCE = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc", "wyprep_kernels.hip")
-ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve"}
+CSRC = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "wyprep_kernels.hip")
+FWD_SOURCE = os.path.join(CSRC, "chunk_fwd.hip")
+ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve", "fwd": "chunk_fwd",
+               "gdn": "gdn_forward"}
 
 
 def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy", gated=False):
@@ -44,8 +47,16 @@ def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy", gated=False):
     return tokens * per_token
 
 
-def kernel_source_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
+def fwd_bytes(tokens, num_states, hq, hv, dk, dv, esz, gated=False):
+    """chunk_fwd: q and k read once per key head; W, U (and g) read, o written once per value
+    head; the final state (fp32, dk x dv per sequence and value head) written once."""
+    gb = 4 if gated else 0
+    return tokens * (2 * hq * dk * esz + hv * (dk * esz + dv * esz + gb + dv * esz)) + \
+        num_states * hv * dk * dv * 4
+
+
+def kernel_source_sha(entry="wy"):
+    with open(FWD_SOURCE if entry == "fwd" else KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -63,7 +74,7 @@ def profile_name(entry, w, batch, seqlen, num_seqs):
     return f"{ENTRY_NAMES[entry]}{gated}_{w.dtype}_c{w.chunk_size}_{shape}"
 
 
-def counter_traffic(name):
+def counter_traffic(name, entry="wy"):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this entry point
     and workload, if there is one and it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", name + "_counters.md")
@@ -72,7 +83,7 @@ def counter_traffic(name):
     text = open(path).read()
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    if not m_b or not m_h or m_h.group(1) != kernel_source_sha():
+    if not m_b or not m_h or m_h.group(1) != kernel_source_sha(entry):
         return None
     return float(m_b.group(1))
 
@@ -114,6 +125,37 @@ def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
             "value_one_core": units_per_pass * passes1 / el1}
 
 
+def cpu_baseline_fwd(inp, seconds=10.0):
+    """The token-by-token fp64 recurrence oracle, as it stands, on a bounded sample of the
+    workload: the first (sequence, value head) pairs, one per usable host core, repeated until
+    ~`seconds`; reported per chunk x value head of those pairs."""
+    import oracle
+    lib = oracle.load()
+    threads = cpu_threads()
+    B, T, C = inp["batch"], inp["seqlen"], inp["chunk_size"]
+    Hv = inp["beta"].shape[2]
+    cu = inp["cu_seqlens"]
+    N = B if cu is None else len(cu) - 1
+    lens = np.full(N, T) if cu is None else np.diff(cu.astype(np.int64))
+    pairs = [(p // Hv, p % Hv) for p in range(min(threads, N * Hv))]
+    units = int(sum((lens[s] + C - 1) // C for s, _ in pairs))
+    toks = int(sum(lens[s] for s, _ in pairs))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"],
+                           cu_seqlens=cu, pairs=pairs, nthreads=threads, lib=lib)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": units * passes / el, "unit": "chunks/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(pairs)} (sequence, value head) pairs ({units} chunk x head units, "
+                      f"{toks} tokens each pass) x {passes} passes, {el:.1f} s wall, fp64 "
+                      "token-by-token recurrence",
+            "tokens_per_s": toks * passes / el}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,9 +168,11 @@ def main(argv=None):
                     help="seeded workload index (2 = the headline C=64 workload)")
     ap.add_argument("--chunk-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--entry", choices=("wy", "wu", "kkt"), default="wy",
+    ap.add_argument("--entry", choices=("wy", "wu", "kkt", "fwd", "gdn"), default="wy",
                     help="wy: wyp_wy_prepare (T, W, U; the headline); wu: wyp_wu_prepare "
-                         "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only)")
+                         "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only); fwd: wyp_chunk_fwd "
+                         "(state recurrence and output from prepared W, U; C = 64); gdn: the "
+                         "whole forward, wyp_wu_prepare then wyp_chunk_fwd")
     ap.add_argument("--gate-mu", type=float, default=None,
                     help="add per-token log gates g = log sigmoid(mu + N(0,1)) (the gated "
                          "coefficient diag(beta)(Gamma o K K^T)); 4 is the seeded gated recipe")
@@ -156,7 +200,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     lib = cg.load_library()
 
-    w = synth.workload(args.workload, chunk_size=args.chunk_size, gate_mu=args.gate_mu)
+    fwd_entry = args.entry in ("fwd", "gdn")
+    w = synth.workload(args.workload, chunk_size=args.chunk_size, gate_mu=args.gate_mu,
+                       with_q=fwd_entry)
     if args.gate_mu is not None:
         w.name += f" gated (g = log sigmoid({args.gate_mu:g} + N(0,1)))"
     inp = synth.generate(w)
@@ -173,7 +219,14 @@ def main(argv=None):
         nchunks = B * ((T + C - 1) // C)
     units = nchunks * Hv
     tokens = B * T
-    alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, args.entry, gated)
+    nstates = B if inp["cu_seqlens"] is None else len(inp["cu_seqlens"]) - 1
+    if args.entry == "fwd":
+        alg = fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
+    elif args.entry == "gdn":
+        alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, "wu", gated) + \
+            fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
+    else:
+        alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, args.entry, gated)
     nsets = max(1, math.ceil(ROTATE_BYTES / alg))  # every byte of a step is touched once
 
     def dev_tensor(a, dt):
@@ -185,13 +238,19 @@ def main(argv=None):
     b0 = torch.from_numpy(inp["beta"]).to(dev)
     g0 = torch.from_numpy(inp["g"]).to(dev) if gated else None
     cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    q0 = dev_tensor(inp["q"], tdt) if fwd_entry else None
     sets = []
     for _ in range(nsets):
         sets.append(dict(k=k0.clone(), v=v0.clone(), beta=b0.clone(),
                          g=g0.clone() if gated else None,
-                         T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev),
+                         T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev)
+                         if args.entry in ("wy", "kkt") else None,
                          W=torch.empty(B, T, Hv, dk, dtype=tdt, device=dev),
-                         U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev)))
+                         U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev),
+                         q=q0.clone() if fwd_entry else None,
+                         o=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev) if fwd_entry else None,
+                         hT=torch.empty(nstates, Hv, dk, dv, dtype=torch.float32, device=dev)
+                         if fwd_entry else None))
     prob = cg.Problem(B, T, Hq, Hv, dk, dv, C, 0 if cu is None else cu.numel() - 1,
                       0 if w.dtype == "bf16" else 1)
     import ctypes
@@ -199,19 +258,34 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
     calls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
-                   (s["k"], s["v"], s["g"], s["beta"], s["T"], s["W"], s["U"])) for s in sets]
+                   (s["k"], s["v"], s["g"], s["beta"], s["T"], s["W"], s["U"], s["q"], s["o"],
+                    s["hT"])) for s in sets]
     cu_ptr = ctypes.c_void_p(None if cu is None else cu.data_ptr())
+    scale = ctypes.c_float(dk ** -0.5)
 
     def step(i, sp):
-        kp, vp, gp, bp, tp, wp, up = calls[i % nsets]
+        kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i % nsets]
         if args.entry == "wy":
             st = lib.wyp_wy_prepare(pprob, kp, vp, gp, bp, cu_ptr, tp, wp, up, sp)
         elif args.entry == "wu":
             st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
-        else:
+        elif args.entry == "kkt":
             st = lib.wyp_kkt_solve(pprob, kp, gp, bp, cu_ptr, tp, sp)
+        else:
+            st = 0
+            if args.entry == "gdn":
+                st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
+            if st == 0:
+                st = lib.wyp_chunk_fwd(pprob, qp, kp, wp, up, gp, None, scale, cu_ptr, op, hp, sp)
         if st != 0:
             raise RuntimeError(lib.wyp_last_error().decode())
+
+    if args.entry == "fwd":  # W and U of every buffer set, prepared once, untimed
+        for i in range(nsets):
+            kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i]
+            if lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sptr) != 0:
+                raise RuntimeError(lib.wyp_last_error().decode())
+        torch.cuda.synchronize(dev)
 
     # Clock ramp: the GPU needs ~20 ms of sustained work to reach steady clocks (measured on
     # this kernel: 43 us per launch in the first 4 ms, 30 us from 20 ms on).  The step runs
@@ -258,7 +332,9 @@ def main(argv=None):
 
     # The graph did the work: the last buffer set it wrote equals a fresh eager launch.
     last = (args.steps - 1) % nsets
-    ref = {n: sets[last][n].clone() for n in ("T", "W", "U")}
+    outs = {"wy": ("T", "W", "U"), "wu": ("W", "U"), "kkt": ("T",), "fwd": ("o", "hT"),
+            "gdn": ("W", "U", "o", "hT")}[args.entry]
+    ref = {n: sets[last][n].clone() for n in outs}
     step(last, sptr)
     torch.cuda.synchronize(dev)
     replay_ok = all(torch.equal(ref[n], sets[last][n]) for n in ref)
@@ -277,9 +353,9 @@ def main(argv=None):
 
     achieved = alg / kern_avg / 1e9
     pname = profile_name(args.entry, w, B, T, 0 if cu is None else cu.numel() - 1)
-    traffic = counter_traffic(pname)
+    traffic = counter_traffic(pname, args.entry) if args.entry != "gdn" else None
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.entry == "wy" else f"chunks/s (tokens/s) for {ENTRY_NAMES[args.entry]} at C={C}; achieved HBM GB/s vs peak",
         "value": units / (ms_per_step * 1e-3),
         "unit": "chunks/s",
         "n_gpus": 1,
@@ -316,8 +392,14 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize(dev)
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+    if args.entry == "gdn":
+        out["roofline"]["note"] = ("two kernels per step (wu_prepare, chunk_fwd): achieved is "
+                                   "their summed algorithmic bytes over the step time")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds)
+        if fwd_entry:
+            out["cpu_baseline"] = cpu_baseline_fwd(inp, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
