@@ -19,6 +19,9 @@ Parity status of each function (what pins it is listed in tests/test_oracle_pins
   the same with gates g      pinned (gated delta-rule recurrence from zero and from an
                              identity state, the 2-token closed form, g = 0 against no gates,
                              Gamma o T_ungated, chunk restarts)
+  wy_backward                pinned (central finite differences of <dT,T> + <dW,W> + <dU,U>
+                             on a grid where every perturbation is exact; zero upstream;
+                             g = 0 against no gates)
   gdn_forward                pinned (delta-rule read-back, beta = 0 decay of h0, orthogonal
                              keys = linear attention, the chunk form through the pinned W / U,
                              sequences independent)
@@ -77,6 +80,9 @@ def _bind(lib):
     lib.wyo_gdn_forward.restype = ctypes.c_int32
     lib.wyo_gdn_forward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P,
                                     ctypes.c_double, _P, _P, _P, _P, ctypes.c_int32]
+    lib.wyo_wy_backward.restype = ctypes.c_int32
+    lib.wyo_wy_backward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, ctypes.c_int32]
     lib.wyo_units.restype = ctypes.c_int32
     lib.wyo_units.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.c_int64, _P, _P,
                               _P, _P, _P, _P, ctypes.c_int32]
@@ -264,3 +270,40 @@ def gdn_forward(q, k, v, beta, g=None, h0=None, scale=None, cu_seqlens=None, pai
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return o, hT
+
+
+def wy_backward(k, v, beta, chunk_size, dW, dU, dT=None, g=None, cu_seqlens=None, nthreads=None,
+                lib=None):
+    """Gradient of <dT,T> + <dW,W> + <dU,U> with respect to k, v, beta, g (fp64).
+
+    k [B,T,Hq,dk], v [B,T,Hv,dv], dW [B,T,Hv,dk], dU [B,T,Hv,dv]: uint16 (bf16 bits) or float32,
+    all of one dtype; beta, g [B,T,Hv] float32 (g None: no gates); dT [B,T,Hv,C] float32 or
+    None.  Returns (dk [B,T,Hq,dk], dv, dbeta [B,T,Hv], dg or None).
+    """
+    lib = lib or load()
+    k, v = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    dW, dU = np.ascontiguousarray(dW), np.ascontiguousarray(dU)
+    if not (k.dtype == v.dtype == dW.dtype == dU.dtype):
+        raise TypeError("k, v, dW, dU must share a dtype")
+    beta = _c(beta, np.float32)
+    g = _gate(g, beta)
+    cu = _c(cu_seqlens, np.int32)
+    p = _problem(k, v, beta, chunk_size, cu)
+    B, T, Hq, dk = k.shape
+    Hv, dv = beta.shape[2], v.shape[3]
+    if dW.shape != (B, T, Hv, dk) or dU.shape != (B, T, Hv, dv):
+        raise ValueError("dW / dU shapes do not match")
+    if dT is not None:
+        dT = np.ascontiguousarray(dT, dtype=np.float32)
+        if dT.shape != (B, T, Hv, chunk_size):
+            raise ValueError("dT shape does not match")
+    dko = np.zeros((B, T, Hq, dk))
+    dvo = np.zeros((B, T, Hv, dv))
+    dbo = np.zeros((B, T, Hv))
+    dgo = np.zeros((B, T, Hv)) if g is not None else None
+    rc = lib.wyo_wy_backward(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu),
+                             _ptr(dT), _ptr(dW), _ptr(dU), _ptr(dko), _ptr(dvo), _ptr(dbo),
+                             _ptr(dgo), nthreads or os.cpu_count() or 1)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return dko, dvo, dbo, dgo

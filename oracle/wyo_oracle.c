@@ -506,3 +506,209 @@ int32_t wyo_gdn_forward(const wyo_problem* p, const void* q, const void* k, cons
     free(th);
     return ok ? 0 : 2;
 }
+
+/* ---- backward of the preparation step (see wyo_oracle.h) ------------------------------------
+ * Forward, per chunk and value head (D = diag(beta), E = diag(exp(G)), Gamma[i][j] =
+ * exp(G_i - G_j)):  L = strictLower(D (Gamma o K K^T)),  A = I + L,  T = A^{-1},
+ * W = T D E K,  U = T D V.  Reverse, for the upstream dT, dW, dU:
+ *   dT_tot = dT + dW (D E K)^T + dU (D V)^T
+ *   d(D E K) = T^T dW  ->  dK += D E (T^T dW),  dbeta_i += sum_d (T^T dW)[i][d] e^{G_i} K[i][d],
+ *                          dG_i += sum_d (T^T dW)[i][d] beta_i e^{G_i} K[i][d]
+ *   d(D V)   = T^T dU  ->  dV = D (T^T dU),      dbeta_i += sum_d (T^T dU)[i][d] V[i][d]
+ *   dA = -T^T dT_tot T^T  (the derivative of the inverse); M = strictLower(dA)
+ *   L_ij = beta_i Gamma_ij (k_i . k_j), i > j:
+ *       dbeta_i += M_ij Gamma_ij (k_i . k_j);  dK_i += M_ij beta_i Gamma_ij k_j,
+ *       dK_j += M_ij beta_i Gamma_ij k_i;      dG_i += Z_ij, dG_j -= Z_ij with
+ *       Z_ij = M_ij beta_i Gamma_ij (k_i . k_j)
+ *   G_i = g_0 + ... + g_i  ->  dg_t = sum_{i >= t} dG_i.
+ */
+typedef struct {
+    const wyo_problem* p;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* dT;
+    const void* dW;
+    const void* dU;
+    const int64_t* start;
+    const int32_t* len;
+    int64_t nchunks;
+    double* dk;
+    double* dv;
+    double* db;
+    double* dg;
+    int32_t tid, nthreads;
+    int ok;
+} bwd_job;
+
+static void* bwd_run(void* arg)
+{
+    bwd_job* jb = (bwd_job*)arg;
+    const wyo_problem* p = jb->p;
+    const int32_t C = p->chunk_size, dk = p->head_dim_k, dv = p->head_dim_v;
+    const int32_t Hq = p->num_qk_heads, Hv = p->num_v_heads, r = Hv / Hq;
+    unit_scratch s;
+    const size_t CC = (size_t)C * (size_t)C;
+    double* dTt = (double*)malloc(sizeof(double) * CC);   /* dT_tot */
+    double* Y = (double*)malloc(sizeof(double) * CC);     /* dT_tot T^T */
+    double* M = (double*)malloc(sizeof(double) * CC);     /* strictLower(dA) */
+    double* TdW = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dk);
+    double* TdU = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dv);
+    double* dWc = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dk);
+    double* dUc = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dv);
+    double* dK = (double*)malloc(sizeof(double) * (size_t)C * (size_t)dk);
+    double* dG = (double*)malloc(sizeof(double) * (size_t)C);
+    jb->ok = scratch_alloc(&s, p) && dTt && Y && M && TdW && TdU && dWc && dUc && dK && dG;
+    if (jb->ok) {
+        for (int64_t job = jb->tid; job < jb->nchunks * Hq; job += jb->nthreads) {
+            const int64_t c = job / Hq;
+            const int32_t hk = (int32_t)(job % Hq);
+            const int64_t tok0 = jb->start[c];
+            const int32_t n = jb->len[c];
+            for (int64_t i = 0; i < (int64_t)n * dk; ++i) dK[i] = 0.0;
+            for (int32_t hv = hk * r; hv < (hk + 1) * r; ++hv) {
+                /* forward: K, V, beta, G, E and T = A^{-1} (into s.X) */
+                unit_solve(p, jb->k, jb->v, jb->beta, jb->g, tok0, n, hv, &s, NULL, NULL);
+                const double* K = s.K;
+                const double* V = s.V;
+                const double* b = s.b;
+                const double* E = s.E;
+                const double* T = s.X;
+                for (int32_t i = 0; i < n; ++i) {
+                    const int64_t row = (tok0 + i) * Hv + hv;
+                    for (int32_t d = 0; d < dk; ++d)
+                        dWc[(int64_t)i * dk + d] = load_elem(jb->dW, p->kv_dtype, row * dk + d);
+                    for (int32_t d = 0; d < dv; ++d)
+                        dUc[(int64_t)i * dv + d] = load_elem(jb->dU, p->kv_dtype, row * dv + d);
+                }
+                /* dT_tot[i][j] = dT[i][j] + sum_d dW[i][d] beta_j e^{G_j} K[j][d]
+                 *                         + sum_d dU[i][d] beta_j V[j][d] */
+                for (int32_t i = 0; i < n; ++i)
+                    for (int32_t j = 0; j < n; ++j) {
+                        double a = jb->dT ? (double)jb->dT[((tok0 + i) * Hv + hv) * (int64_t)C + j] : 0.0;
+                        double w = 0.0, u = 0.0;
+                        for (int32_t d = 0; d < dk; ++d) w += dWc[(int64_t)i * dk + d] * K[(int64_t)j * dk + d];
+                        for (int32_t d = 0; d < dv; ++d) u += dUc[(int64_t)i * dv + d] * V[(int64_t)j * dv + d];
+                        dTt[(int64_t)i * n + j] = a + w * b[j] * E[j] + u * b[j];
+                    }
+                /* T^T dW and T^T dU */
+                for (int32_t i = 0; i < n; ++i) {
+                    for (int32_t d = 0; d < dk; ++d) {
+                        double acc = 0.0;
+                        for (int32_t m = 0; m < n; ++m) acc += T[(int64_t)m * n + i] * dWc[(int64_t)m * dk + d];
+                        TdW[(int64_t)i * dk + d] = acc;
+                    }
+                    for (int32_t d = 0; d < dv; ++d) {
+                        double acc = 0.0;
+                        for (int32_t m = 0; m < n; ++m) acc += T[(int64_t)m * n + i] * dUc[(int64_t)m * dv + d];
+                        TdU[(int64_t)i * dv + d] = acc;
+                    }
+                }
+                double* dbrow = jb->db;
+                for (int32_t i = 0; i < n; ++i) {
+                    const int64_t row = (tok0 + i) * Hv + hv;
+                    double dbi = 0.0, dgi = 0.0;
+                    for (int32_t d = 0; d < dk; ++d) {
+                        const double t = TdW[(int64_t)i * dk + d];
+                        dK[(int64_t)i * dk + d] += b[i] * E[i] * t;
+                        dbi += t * E[i] * K[(int64_t)i * dk + d];
+                        dgi += t * b[i] * E[i] * K[(int64_t)i * dk + d];
+                    }
+                    for (int32_t d = 0; d < dv; ++d) {
+                        const double t = TdU[(int64_t)i * dv + d];
+                        jb->dv[row * dv + d] = b[i] * t;
+                        dbi += t * V[(int64_t)i * dv + d];
+                    }
+                    dbrow[row] = dbi;
+                    dG[i] = dgi;
+                }
+                /* dA = -T^T dT_tot T^T:  Y = dT_tot T^T, M = strictLower(-T^T Y) */
+                for (int32_t i = 0; i < n; ++i)
+                    for (int32_t j = 0; j < n; ++j) {
+                        double acc = 0.0;
+                        for (int32_t m = 0; m < n; ++m) acc += dTt[(int64_t)i * n + m] * T[(int64_t)j * n + m];
+                        Y[(int64_t)i * n + j] = acc;
+                    }
+                for (int32_t i = 0; i < n; ++i)
+                    for (int32_t j = 0; j < n; ++j) {
+                        double acc = 0.0;
+                        if (j < i)
+                            for (int32_t m = 0; m < n; ++m) acc += T[(int64_t)m * n + i] * Y[(int64_t)m * n + j];
+                        M[(int64_t)i * n + j] = -acc;
+                    }
+                /* through L_ij = beta_i Gamma_ij (k_i . k_j), i > j */
+                for (int32_t i = 0; i < n; ++i)
+                    for (int32_t j = 0; j < i; ++j) {
+                        const double mij = M[(int64_t)i * n + j];
+                        const double gam = exp(s.G[i] - s.G[j]);
+                        double kk = 0.0;
+                        for (int32_t d = 0; d < dk; ++d) kk += K[(int64_t)i * dk + d] * K[(int64_t)j * dk + d];
+                        const int64_t row = (tok0 + i) * Hv + hv;
+                        dbrow[row] += mij * gam * kk;
+                        const double rr = mij * b[i] * gam;
+                        for (int32_t d = 0; d < dk; ++d) {
+                            dK[(int64_t)i * dk + d] += rr * K[(int64_t)j * dk + d];
+                            dK[(int64_t)j * dk + d] += rr * K[(int64_t)i * dk + d];
+                        }
+                        const double z = rr * kk;
+                        dG[i] += z;
+                        dG[j] -= z;
+                    }
+                /* dg_t = sum_{i >= t} dG_i */
+                if (jb->dg) {
+                    double run = 0.0;
+                    for (int32_t t = n - 1; t >= 0; --t) {
+                        run += dG[t];
+                        jb->dg[(tok0 + t) * Hv + hv] = run;
+                    }
+                }
+            }
+            for (int32_t i = 0; i < n; ++i)
+                memcpy(jb->dk + ((tok0 + i) * Hq + hk) * (int64_t)dk, dK + (int64_t)i * dk,
+                       sizeof(double) * (size_t)dk);
+        }
+    }
+    scratch_free(&s);
+    free(dTt); free(Y); free(M); free(TdW); free(TdU); free(dWc); free(dUc); free(dK); free(dG);
+    return NULL;
+}
+
+int32_t wyo_wy_backward(const wyo_problem* p, const void* k, const void* v, const float* g,
+                        const float* beta, const int32_t* cu, const float* dT, const void* dW,
+                        const void* dU, double* dk_out, double* dv_out, double* dbeta_out,
+                        double* dg_out, int32_t nthreads)
+{
+    if (!problem_ok(p, cu) || !k || !v || !beta || !dW || !dU) return 1;
+    if (!dk_out || !dv_out || !dbeta_out || (g && !dg_out)) return 1;
+    const int64_t nchunks = wyo_count_chunks(p, cu);
+    if (nchunks < 0) return 1;
+    int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nchunks + 1));
+    int32_t* len = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nchunks + 1));
+    if (!start || !len) { free(start); free(len); return 2; }
+    wyo_list_chunks(p, cu, start, len, nchunks);
+    if (nthreads <= 0) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    bwd_job* jobs = (bwd_job*)calloc((size_t)nthreads, sizeof(bwd_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); free(start); free(len); return 2; }
+    for (int32_t t = 0; t < nthreads; ++t) {
+        bwd_job* jb = &jobs[t];
+        jb->p = p; jb->k = k; jb->v = v; jb->g = g; jb->beta = beta; jb->dT = dT; jb->dW = dW;
+        jb->dU = dU; jb->start = start; jb->len = len; jb->nchunks = nchunks; jb->dk = dk_out;
+        jb->dv = dv_out; jb->db = dbeta_out; jb->dg = g ? dg_out : NULL;
+        jb->tid = t; jb->nthreads = nthreads;
+    }
+    int32_t started = 0;
+    for (int32_t t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, bwd_run, &jobs[t]) != 0) break;
+        started = t;
+    }
+    for (int32_t t = started + 1; t < nthreads; ++t) bwd_run(&jobs[t]);
+    bwd_run(&jobs[0]);
+    for (int32_t t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    int ok = 1;
+    for (int32_t t = 0; t < nthreads; ++t) ok = ok && jobs[t].ok;
+    free(jobs); free(th); free(start); free(len);
+    return ok ? 0 : 2;
+}

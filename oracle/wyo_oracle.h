@@ -115,6 +115,21 @@ int32_t wyo_gdn_forward(const wyo_problem* p, const void* q, const void* k, cons
                         const int32_t* cu_seqlens, double* o_out, double* hT_out,
                         const uint8_t* pair_mask, int32_t nthreads);
 
+/* Backward of the preparation step: the gradient of
+ *     L = <dT, T> + <dW, W> + <dU, U>
+ * (sums over every chunk and value head) with respect to k, v, beta and g, for upstream
+ * gradients dT [B,T,Hv,C] (float32, may be NULL = 0; only its entries left of the diagonal of
+ * each chunk matter), dW [B,T,Hv,dk] and dU [B,T,Hv,dv] (kv_dtype).  T, W, U are the
+ * functions of k, v, beta, g that wyo_wy_prepare computes; the oracle takes the derivative of
+ * its steps in reverse order (chain rule, fp64 plain loops; see wyo_oracle.c).  Outputs (fp64):
+ * dk [B,T,Hq,dk] (summed over the value heads that read each key head), dv [B,T,Hv,dv],
+ * dbeta [B,T,Hv], dg [B,T,Hv] (written only when g is given; may then be NULL).
+ * Returns 0 on success. */
+int32_t wyo_wy_backward(const wyo_problem* p, const void* k, const void* v, const float* g,
+                        const float* beta, const int32_t* cu_seqlens, const float* dT,
+                        const void* dW, const void* dU, double* dk_out, double* dv_out,
+                        double* dbeta_out, double* dg_out, int32_t nthreads);
+
 #ifdef __cplusplus
 }
 #endif

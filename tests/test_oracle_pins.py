@@ -518,12 +518,84 @@ def pin_gdn_sequences_independent(lib):
         assert np.array_equal(o[:, sl], o1) and np.array_equal(hT[s], h1[0])
 
 
+# ---------------------------------------------------------------------------------------------
+# backward of the preparation step: the gradient of <dT,T> + <dW,W> + <dU,U>
+
+def grid(rng, shape, scale):
+    """fp32 values on the 2^-12 grid, so x +- 2^-12 is exact in fp32."""
+    return (np.round(rng.standard_normal(shape) * scale * 4096) / 4096).astype(np.float32)
+
+
+def bwd_problem(seed, gated=True):
+    rng = np.random.default_rng(seed)
+    T, Hq, Hv, d, C = 11, 1, 2, 8, 8  # two chunks: 8 tokens and a ragged tail of 3
+    k = grid(rng, (1, T, Hq, d), 0.4)
+    v = grid(rng, (1, T, Hv, d), 1.0)
+    beta = (np.round(rng.uniform(0.1, 0.9, (1, T, Hv)) * 4096) / 4096).astype(np.float32)
+    g = grid(rng, (1, T, Hv), 0.2) - np.float32(0.125) if gated else None
+    dT = rng.standard_normal((1, T, Hv, C)).astype(np.float32)
+    dW = rng.standard_normal((1, T, Hv, d)).astype(np.float32)
+    dU = rng.standard_normal((1, T, Hv, d)).astype(np.float32)
+    return dict(k=k, v=v, beta=beta, g=g, dT=dT, dW=dW, dU=dU, C=C)
+
+
+def bwd_loss(lib, P, k=None, v=None, beta=None, g=None):
+    k = P["k"] if k is None else k
+    v = P["v"] if v is None else v
+    beta = P["beta"] if beta is None else beta
+    g = P["g"] if g is None else g
+    T, W, U, _ = oracle.wy_prepare(k, beta, P["C"], v=v, lib=lib, nthreads=1, g=g)
+    # only entries of T left of or on the diagonal exist; the rest is 0 in T_out
+    return float(np.sum(P["dT"] * T) + np.sum(P["dW"] * W) + np.sum(P["dU"] * U))
+
+
+def pin_bwd_finite_differences(lib):
+    """Every component of the analytic gradient (k, v, beta, g; a key head read by two value
+    heads; two chunks with a ragged tail; gates; dT given) equals the central difference
+    (L(x + h) - L(x - h)) / 2h with h = 2^-12, every perturbed input exact in fp32."""
+    P = bwd_problem(50)
+    dk, dv, db, dg = oracle.wy_backward(P["k"], P["v"], P["beta"], P["C"], P["dW"], P["dU"],
+                                        dT=P["dT"], g=P["g"], lib=lib, nthreads=1)
+    h = np.float32(2.0 ** -12)
+    worst = 0.0
+    for name, grad in (("k", dk), ("v", dv), ("beta", db), ("g", dg)):
+        x = P[name]
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd = (bwd_loss(lib, P, **{name: xp}) - bwd_loss(lib, P, **{name: xm})) / (2 * float(h))
+            worst = max(worst, abs(fd - grad[idx]) / max(1.0, abs(fd)))
+    assert worst <= 1e-7, worst  # measured: 1e-11 (k, v, beta), 1e-8 (g: h^2 through exp)
+
+
+def pin_bwd_zero_upstream(lib):
+    """No upstream gradient, no gradient: every output is exactly 0."""
+    P = bwd_problem(51)
+    z = np.zeros_like(P["dW"])
+    dk, dv, db, dg = oracle.wy_backward(P["k"], P["v"], P["beta"], P["C"], z, z,
+                                        dT=np.zeros_like(P["dT"]), g=P["g"], lib=lib)
+    assert not dk.any() and not dv.any() and not db.any() and not dg.any()
+
+
+def pin_bwd_gate_zero(lib):
+    """g = 0 gives the ungated dk, dv, dbeta bit for bit (and a gradient for g)."""
+    P = bwd_problem(52, gated=False)
+    a = oracle.wy_backward(P["k"], P["v"], P["beta"], P["C"], P["dW"], P["dU"], dT=P["dT"],
+                           lib=lib)
+    b = oracle.wy_backward(P["k"], P["v"], P["beta"], P["C"], P["dW"], P["dU"], dT=P["dT"],
+                           g=np.zeros_like(P["beta"]), lib=lib)
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] is None
+    assert np.any(b[3] != 0)
+
+
 PINS = [pin_closed_form_2, pin_orthogonal, pin_residual_structure, pin_lapack_inverse,
         pin_block_identity, pin_beta_zero, pin_subdiag_only, pin_identical_keys,
         pin_fma_counts, pin_householder_product, pin_delta_rule, pin_tail_padding, pin_layout,
         pin_head_grouping, pin_gate_zero, pin_gated_closed_form_2, pin_gated_recurrence,
         pin_gated_similarity, pin_gated_chunk_restart, pin_gdn_read_back, pin_gdn_beta_zero,
-        pin_gdn_linear_attention, pin_gdn_chunk_form, pin_gdn_sequences_independent]
+        pin_gdn_linear_attention, pin_gdn_chunk_form, pin_gdn_sequences_independent,
+        pin_bwd_finite_differences, pin_bwd_zero_upstream, pin_bwd_gate_zero]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -622,6 +694,15 @@ MUTANTS = {
     "gdn_scale_dropped": ("= jb->scale * r;", "= r;"),
     "gdn_state_not_reset": ("for (int64_t i = 0; i < (int64_t)dk * dv; ++i) S[i] = h0 ?",
                             "if (seq == 0) for (int64_t i = 0; i < (int64_t)dk * dv; ++i) S[i] = h0 ?"),
+    # the backward
+    "bwd_dA_sign": ("M[(int64_t)i * n + j] = -acc;", "M[(int64_t)i * n + j] = acc;"),
+    "bwd_TdW_untransposed": ("acc += T[(int64_t)m * n + i] * dWc", "acc += T[(int64_t)i * n + m] * dWc"),
+    "bwd_rt_term_dropped": ("dK[(int64_t)j * dk + d] += rr * K[(int64_t)i * dk + d];", "(void)0;"),
+    "bwd_dg_forward_sum": ("for (int32_t t = n - 1; t >= 0; --t) {", "for (int32_t t = 0; t < n; ++t) {"),
+    "bwd_group_overwrite": ("dK[(int64_t)i * dk + d] += b[i] * E[i] * t;",
+                            "dK[(int64_t)i * dk + d] = b[i] * E[i] * t;"),
+    "bwd_dbeta_gram_dropped": ("dbrow[row] += mij * gam * kk;", "dbrow[row] += 0.0;"),
+    "bwd_dT_ignored": ("double a = jb->dT ?", "double a = 0.0 * (double)(jb->dT != NULL) + 0 ?"),
     "gate_not_restarted": ("s->G[i] = (i == 0 ? 0.0 : s->G[i - 1]) + gi;",
                            "s->G[i] = (i == 0 ? (gate && tok0 > 0 ? (double)gate[(tok0 - 1) * Hv + hv] "
                            ": 0.0) : s->G[i - 1]) + gi;"),
