@@ -18,15 +18,16 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "chunk_fwd", "chunk_gated_delta_rule",
-           "wyp_wy_prepare", "wyp_kkt_solve", "wyp_wu_prepare", "wyp_chunk_fwd", "load_library",
-           "Problem", "LIB_PATH", "WyprepError"]
+__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "wy_backward", "chunk_fwd",
+           "chunk_gated_delta_rule", "wyp_wy_prepare", "wyp_kkt_solve", "wyp_wu_prepare",
+           "wyp_wy_backward", "wyp_chunk_fwd", "load_library", "Problem", "LIB_PATH",
+           "WyprepError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.so")
 
 WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
 WYP_BF16, WYP_F32 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class WyprepError(RuntimeError):
@@ -74,6 +75,8 @@ def load_library(path: str | None = None):
     lib.wyp_chunk_fwd.restype = ctypes.c_int32
     lib.wyp_chunk_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                   _P, _P, _P, _P]
+    lib.wyp_wy_backward.restype = ctypes.c_int32
+    lib.wyp_wy_backward.argtypes = [ctypes.POINTER(Problem)] + [_P] * 13
     if lib.wyp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{p} has ABI version {lib.wyp_abi_version()}, this binding expects "
                            f"{ABI_VERSION}: rebuild it")
@@ -220,6 +223,37 @@ def wu_prepare(k, v, beta, chunk_size, cu_seqlens=None, W_out=None, U_out=None, 
     return W_out, U_out
 
 
+def wy_backward(k, v, beta, chunk_size, dW, dU, dT=None, g=None, cu_seqlens=None):
+    """(dk, dv, dbeta, dg): the gradient of <dT,T> + <dW,W> + <dU,U> through wy_prepare with
+    respect to k, v, beta and g (dg None without gates); see wyp_wy_backward.  dW, dU in k's
+    dtype with W / U's shapes; dT [B,T,Hv,C] float32 or None."""
+    import torch
+    lib = load_library()
+    p = _problem(k, beta, chunk_size, cu_seqlens, v=v)
+    gp = _gate_ptr(g, beta)
+    B, T = k.shape[:2]
+    Hv = p.num_v_heads
+    for t, name, shape in ((dW, "dW", (B, T, Hv, p.head_dim_k)), (dU, "dU", (B, T, Hv, p.head_dim_v))):
+        _require(t, name, 4, k.device)
+        if tuple(t.shape) != shape or t.dtype != k.dtype:
+            raise ValueError(f"{name} must be {k.dtype} of shape {shape}")
+    if dT is not None:
+        _require(dT, "dT", 4, k.device)
+        if dT.dtype != torch.float32 or tuple(dT.shape) != (B, T, Hv, p.chunk_size):
+            raise ValueError(f"dT must be float32 of shape {(B, T, Hv, p.chunk_size)}")
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    db = torch.empty_like(beta)
+    dg = torch.empty_like(beta) if g is not None else None
+    st = lib.wyp_wy_backward(ctypes.byref(p), k.data_ptr(), v.data_ptr(), gp, beta.data_ptr(),
+                             cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                             dT.data_ptr() if dT is not None else None, dW.data_ptr(),
+                             dU.data_ptr(), dk.data_ptr(), dv.data_ptr(), db.data_ptr(),
+                             dg.data_ptr() if dg is not None else None, _stream(k.device))
+    _check(lib, st)
+    return dk, dv, db, dg
+
+
 def chunk_fwd(q, k, w, u, chunk_size=64, g=None, initial_state=None, scale=None,
               cu_seqlens=None, output_final_state=False, o_out=None, final_state=None):
     """(o, final_state) of the gated delta rule from q, k and the chunk's W, U (as returned by
@@ -290,3 +324,4 @@ wyp_kkt_solve = kkt_solve
 wyp_wy_prepare = wy_prepare
 wyp_wu_prepare = wu_prepare
 wyp_chunk_fwd = chunk_fwd
+wyp_wy_backward = wy_backward

@@ -183,6 +183,50 @@ wyp_status validate_fwd(const wyp_problem* p, const void* q, const void* k, cons
     return WYP_OK;
 }
 
+wyp_status validate_bwd(const wyp_problem* p, const void* k, const void* v, const float* g,
+                        const float* beta, const int32_t* cu, const float* dT, const void* dW,
+                        const void* dU, const void* dk, const void* dv, const float* dbeta,
+                        const float* dg, wyp::BwdArgs* out, bool* empty)
+{
+    wyp::LaunchArgs la{};
+    // the problem checks of the forward (with W, U standing for dW, dU)
+    wyp_status st = validate(p, k, v, g, beta, cu, nullptr, dW, dU, false, true, &la, empty);
+    if (st != WYP_OK || *empty) return st;
+    if (p->kv_dtype != WYP_BF16)
+        return fail(WYP_ERR_UNSUPPORTED, "wyp_wy_backward is built for bf16 k, v only");
+    if (p->chunk_size != 64)
+        return fail(WYP_ERR_UNSUPPORTED, "wyp_wy_backward is built for chunk_size 64 (got %d)",
+                    p->chunk_size);
+    if (!dk || !dv || !dbeta) return fail(WYP_ERR_INVALID_ARGUMENT, "dk, dv and dbeta must be non-NULL");
+    if (g && !dg) return fail(WYP_ERR_INVALID_ARGUMENT, "dg must be non-NULL when g is given");
+    if (!aligned(dk, 16) || !aligned(dv, 16))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "dk and dv must be 16-byte aligned");
+    if (!aligned(dbeta, 4) || (dg && !aligned(dg, 4)) || (dT && !aligned(dT, 4)))
+        return fail(WYP_ERR_INVALID_ARGUMENT, "dT, dbeta and dg must be 4-byte aligned");
+    const int64_t units = la.chunk_slots * p->num_qk_heads;
+    if (units > INT32_MAX)
+        return fail(WYP_ERR_UNSUPPORTED, "problem has %lld units, more than one launch holds",
+                    static_cast<long long>(units));
+    out->k = k;
+    out->v = v;
+    out->beta = beta;
+    out->g = g;
+    out->cu_seqlens = cu;
+    out->dT = dT;
+    out->dW = dW;
+    out->dU = dU;
+    out->dk = const_cast<void*>(dk);
+    out->dv = const_cast<void*>(dv);
+    out->dbeta = const_cast<float*>(dbeta);
+    out->dg = g ? const_cast<float*>(dg) : nullptr;
+    out->seqlen = p->seqlen;
+    out->num_qk_heads = p->num_qk_heads;
+    out->num_v_heads = p->num_v_heads;
+    out->num_seqs = la.num_seqs;
+    out->chunk_slots = la.chunk_slots;
+    return WYP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +283,24 @@ extern "C" wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, c
     if (st != WYP_OK || empty) return st;
     char msg[256] = "";
     if (wyp::launch_fwd(args, stream, msg, sizeof msg) != 0)
+        return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
+    return WYP_OK;
+}
+
+extern "C" wyp_status wyp_wy_backward(const wyp_problem* problem, const void* k, const void* v,
+                                      const float* g, const float* beta, const int32_t* cu_seqlens,
+                                      const float* dT, const void* dW, const void* dU,
+                                      void* dk_out, void* dv_out, float* dbeta_out, float* dg_out,
+                                      void* stream)
+{
+    g_last_error[0] = '\0';
+    wyp::BwdArgs args{};
+    bool empty = false;
+    const wyp_status st = validate_bwd(problem, k, v, g, beta, cu_seqlens, dT, dW, dU, dk_out,
+                                       dv_out, dbeta_out, dg_out, &args, &empty);
+    if (st != WYP_OK || empty) return st;
+    char msg[256] = "";
+    if (wyp::launch_bwd(args, stream, msg, sizeof msg) != 0)
         return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
     return WYP_OK;
 }

@@ -49,4 +49,27 @@ struct FwdArgs {
 
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len);
 
+// Validated backward of the preparation step, ready to launch.
+struct BwdArgs {
+    const void* k;
+    const void* v;
+    const float* beta;
+    const float* g;            // nullptr: no gates (dg not written)
+    const int32_t* cu_seqlens;
+    const float* dT;           // nullptr: dT = 0
+    const void* dW;
+    const void* dU;
+    void* dk;
+    void* dv;
+    float* dbeta;
+    float* dg;
+    int32_t seqlen;
+    int32_t num_qk_heads;
+    int32_t num_v_heads;
+    int32_t num_seqs;
+    int64_t chunk_slots;
+};
+
+int launch_bwd(const BwdArgs& a, void* stream, char* msg, int msg_len);
+
 }  // namespace wyp

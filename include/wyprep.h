@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 3  /* 2: log gates g on every entry point; 3: wyp_chunk_fwd */
+#define WYP_ABI_VERSION 4  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward */
 
 typedef enum {
     WYP_OK = 0,
@@ -159,6 +159,33 @@ wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* 
                          const void* w_in, const void* u_in, const float* g,
                          const float* initial_state, float scale, const int32_t* cu_seqlens,
                          void* o_out, float* final_state, void* stream);
+
+/* Backward of the preparation step (the training path; [QLA] "反向" (backward): FlashQLA fuses
+ * bwd_wy with the other backward kernels).  For upstream gradients dT, dW, dU of wyp_wy_prepare's
+ * outputs it returns the gradient of  L = <dT, T> + <dW, W> + <dU, U>  with respect to k, v,
+ * beta and g.  With D = diag(beta), E = diag(exp(G)), H = Gamma o K K^T (strict lower part):
+ *     X  = strictLower(dT + (dW K^T) D E + (dU V^T) D),   M = strictLower(-T^T X T^T)
+ *     dk = D E T^T dW + (R + R^T) K   with R = D (Gamma o M)   (summed over the value heads
+ *                                                               that read each key head)
+ *     dv = D T^T dU
+ *     dbeta_i = sum_d [ (T^T dW)_id e^{G_i} K_id + (T^T dU)_id V_id ] + sum_j M_ij H_ij
+ *     dG_i = beta_i e^{G_i} sum_d (T^T dW)_id K_id + sum_j (Z_ij - Z_ji),  Z = M o D H
+ *     dg_t = sum of dG_i over the chunk's tokens i >= t.
+ * T is recomputed on chip by the same steps as wyp_wy_prepare.
+ *   k, v, g, beta, cu_seqlens   as for wyp_wy_prepare (the forward's inputs)
+ *   dT      [B, T, Hv, C] float32, or NULL (zero); entries on or right of each chunk's
+ *           diagonal are ignored (T is constant there)
+ *   dW, dU  [B, T, Hv, dk] / [B, T, Hv, dv]   kv_dtype
+ *   dk_out  [B, T, Hq, dk], dv_out [B, T, Hv, dv]   kv_dtype
+ *   dbeta_out [B, T, Hv] float32;  dg_out [B, T, Hv] float32, required when g is given (else
+ *           ignored)
+ * Supported: kv_dtype WYP_BF16, chunk_size 64, dk = dv = 128.  Alignment: k, v, dW, dU, dk_out,
+ * dv_out 16 bytes; beta, g, dT, dbeta_out, dg_out 4 bytes.  Results are deterministic (fixed
+ * reduction order, no atomics). */
+wyp_status wyp_wy_backward(const wyp_problem* problem, const void* k, const void* v,
+                           const float* g, const float* beta, const int32_t* cu_seqlens,
+                           const float* dT, const void* dW, const void* dU, void* dk_out,
+                           void* dv_out, float* dbeta_out, float* dg_out, void* stream);
 
 #ifdef __cplusplus
 }

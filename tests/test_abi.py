@@ -29,13 +29,14 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
-                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_chunk_fwd"}
+                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_chunk_fwd",
+                          "wyp_wy_backward"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 3 == cg.ABI_VERSION
+    assert lib.wyp_abi_version() == 4 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -164,3 +165,24 @@ def test_chunk_fwd_empty_is_a_noop(lib):
     assert call_fwd(lib, good(seqlen=0), q=None, k=None, w=None, u=None, o=None) == 0
     assert call_fwd(lib, good(seqlen=0, num_seqs=0), cu=FAKE, q=None, k=None, w=None, u=None,
                     o=None, hT=FAKE) == 0
+
+
+def call_bwd(lib, p, k=FAKE, v=FAKE, g=None, beta=FAKE, cu=None, dT=None, dW=FAKE, dU=FAKE,
+             dk=FAKE, dv=FAKE, db=FAKE, dg=None):
+    return lib.wyp_wy_backward(ctypes.byref(p) if p is not None else None, k, v, g, beta, cu, dT,
+                               dW, dU, dk, dv, db, dg, None)
+
+
+def test_wy_backward_rejects(lib):
+    assert call_bwd(lib, good(chunk_size=32)) == 2
+    assert "chunk_size" in lib.wyp_last_error().decode()
+    assert call_bwd(lib, good(kv_dtype=1)) == 2
+    assert call_bwd(lib, good(chunk_size=48)) == 2
+    assert call_bwd(lib, good(), dW=None) == 1
+    assert call_bwd(lib, good(), dk=None) == 1
+    assert call_bwd(lib, good(), g=FAKE) == 1          # gates given, dg missing
+    assert "dg" in lib.wyp_last_error().decode()
+    assert call_bwd(lib, good(), dv=FAKE + 4) == 1
+    assert call_bwd(lib, good(), dT=FAKE + 2) == 1
+    assert call_bwd(lib, good(seqlen=0), k=None, v=None, beta=None, dW=None, dU=None, dk=None,
+                    dv=None, db=None) == 0

@@ -1,0 +1,115 @@
+"""Backward of the preparation step (wyp_wy_backward) against the fp64 oracle's gradient of
+<dT,T> + <dW,W> + <dU,U>, through the C ABI (needs a GPU).
+
+The oracle is pinned by central finite differences.  Bar (derived from the arithmetic: T and
+R + R^T enter the bf16 products as hi + lo pairs, so the only coarse rounding is the bf16 output
+of dk and dv; a simulation of this arithmetic gives 1.7e-3 for dk, dv and 1e-6 for dbeta, dg):
+dk and dv within 1e-2 relative Frobenius, dbeta and dg within 1e-4.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from chunkwise_gated_deltanet_amd import synth
+from gpu_util import gate_of, rel_fro, say, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+KV_TOL = 1e-2
+BG_TOL = 1e-4
+
+CASES = {
+    "B2_T333_H4": dict(batch=2, seqlen=333, num_qk_heads=4, num_v_heads=4, seed=120),
+    "B2_T333_H4_mu4_dT": dict(batch=2, seqlen=333, num_qk_heads=4, num_v_heads=4, seed=121,
+                              gate_mu=4.0, dT=True),
+    "packed_gva_mu4_dT": dict(batch=1, seqlen=0, num_qk_heads=4, num_v_heads=16, seed=122,
+                              gate_mu=4.0, dT=True, seqlens=[300, 517, 64, 1, 129, 250, 63, 65]),
+    "packed_gva_mu0": dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=8, seed=123,
+                           gate_mu=0.0, seqlens=[31, 33, 1, 95, 200]),
+    "T700_H2_dT": dict(batch=1, seqlen=700, num_qk_heads=2, num_v_heads=2, seed=124, dT=True,
+                       beta_sigma=1.5),
+}
+
+
+def make_inputs(spec):
+    spec = dict(spec)
+    want_dT = spec.pop("dT", False)
+    inp = synth.custom(chunk_size=64, **spec)
+    rng = np.random.default_rng(spec["seed"] + 2000)
+    B, T, Hv = inp["beta"].shape
+    dW = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
+    dU = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
+    dT = rng.standard_normal((B, T, Hv, 64)).astype(np.float32) if want_dT else None
+    return inp, dW, dU, dT
+
+
+def run_bwd(inp, dW, dU, dT, device):
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    k, v, beta, cu = to_device(inp, device)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    out = cg.wy_backward(k, v, beta, 64, bf(dW), bf(dU),
+                         dT=None if dT is None else torch.from_numpy(dT).to(device),
+                         g=gate_of(inp, device), cu_seqlens=cu)
+    torch.cuda.synchronize(device)
+    return out
+
+
+def check(inp, dW, dU, dT, out, label):
+    dk, dv, db, dg = out
+    rk, rv, rb, rg = oracle.wy_backward(inp["k"], inp["v"], inp["beta"], 64, dW, dU, dT=dT,
+                                        g=inp.get("g"), cu_seqlens=inp["cu_seqlens"])
+    m = {"dk": rel_fro(to_f64(dk), rk), "dv": rel_fro(to_f64(dv), rv),
+         "dbeta": rel_fro(to_f64(db), rb)}
+    if rg is not None:
+        m["dg"] = rel_fro(to_f64(dg), rg)
+    say(f"[{label}] " + ", ".join(f"{k} {v:.3e}" for k, v in m.items()))
+    assert m["dk"] <= KV_TOL and m["dv"] <= KV_TOL, m
+    assert m["dbeta"] <= BG_TOL and m.get("dg", 0.0) <= BG_TOL, m
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_wy_backward_small(name, gpu):
+    inp, dW, dU, dT = make_inputs(CASES[name])
+    say(f"wy_backward {name}")
+    out = run_bwd(inp, dW, dU, dT, gpu)
+    check(inp, dW, dU, dT, out, name)
+
+
+def test_wy_backward_identical_keys(gpu):
+    """All keys of a chunk equal: the cancellation case that makes a single bf16 rounding of T
+    miss the W tolerance in the forward."""
+    inp, dW, dU, dT = make_inputs(dict(batch=1, seqlen=128, num_qk_heads=1, num_v_heads=2,
+                                       seed=125, dT=True, gate_mu=4.0))
+    inp["k"][0, :64] = inp["k"][0, 0]
+    inp["k"][0, 64:] = inp["k"][0, 64]
+    say("wy_backward identical keys")
+    out = run_bwd(inp, dW, dU, dT, gpu)
+    check(inp, dW, dU, dT, out, "identical keys")
+
+
+def test_wy_backward_deterministic(gpu):
+    import torch
+    inp, dW, dU, dT = make_inputs(CASES["packed_gva_mu4_dT"])
+    a = run_bwd(inp, dW, dU, dT, gpu)
+    b = run_bwd(inp, dW, dU, dT, gpu)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mu", [None, 4.0])
+def test_wy_backward_full_size(mu, gpu):
+    """B=1 T=8192 H=16/16 C=64, whole tensors against the oracle."""
+    import torch
+    w = synth.workload(2, chunk_size=64, gate_mu=mu)
+    inp = synth.generate(w)
+    rng = np.random.default_rng(7)
+    B, T, Hv = inp["beta"].shape
+    dW = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
+    dU = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
+    dT = rng.standard_normal((B, T, Hv, 64)).astype(np.float32)
+    say(f"wy_backward full {w.name} gate_mu={mu}")
+    out = run_bwd(inp, dW, dU, dT, gpu)
+    check(inp, dW, dU, dT, out, f"full {w.name} mu={mu}")
+    del out
+    torch.cuda.empty_cache()
