@@ -59,7 +59,11 @@ constexpr int kDVS = 32;       // dv columns per workgroup
 constexpr int kSlices = kD / kDVS;
 constexpr int kThreads = 256;
 constexpr int kBufferConfig = 0x00020000;
-constexpr int kStream = 2;     // non-temporal: read or written once per launch
+// Non-temporal policy for what one workgroup alone reads or writes (its U slice, g, o).  Q, K
+// and W keep the default policy: the four dv-slice workgroups of a head each read them, and
+// the later readers hit the XCD's L2 (with nt W loads the packed Hq=16 Hv=64 workload moved
+// 1.71x its algorithmic bytes).
+constexpr int kStream = 2;
 
 struct Params {
     const __bf16* q;
@@ -127,7 +131,7 @@ struct Chunk {
             const int pc = tid + it * kThreads;  // row pc / 16, piece pc % 16
             q[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
             k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
-            w[it] = __builtin_amdgcn_raw_buffer_load_b128(wr, (pc >> 4) * wstride + (pc & 15) * 16, 0, kStream);
+            w[it] = __builtin_amdgcn_raw_buffer_load_b128(wr, (pc >> 4) * wstride + (pc & 15) * 16, 0, 0);
         }
         const __amdgpu_buffer_rsrc_t ur =
             rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * kDVS, (n - 1) * wstride + kDVS * 2);

@@ -1213,20 +1213,32 @@ struct Params {
     int32_t num_seqs;
 };
 
-// Rows [0, n) of a [tokens, heads, 128] bf16 tensor into LDS rows of KROW elements (rows >= n
-// read as 0 through the buffer range).
-__device__ inline void load_rows(unsigned char* dst, const __bf16* base, int64_t tok0, int n, int heads,
-                                 int head, int tid)
-{
-    const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
-    const __amdgpu_buffer_rsrc_t r = rsrc(base + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
+// Rows [0, n) of a [tokens, heads, 128] bf16 tensor in flight to registers (four 16-byte
+// pieces per thread; rows >= n read as 0 through the buffer range), then into LDS rows of KROW
+// elements.  All of a value head's rows are issued before any is waited for.
+struct Rows {
+    u32x4 x[4];
+
+    __device__ void issue(const __bf16* base, int64_t tok0, int n, int heads, int head, int tid)
+    {
+        const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
+        const __amdgpu_buffer_rsrc_t r = rsrc(base + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int q = tid + it * kThreads;
-        const u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
-        *reinterpret_cast<u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16) = val;
+        for (int it = 0; it < 4; ++it) {
+            const int q = tid + it * kThreads;
+            x[it] = __builtin_amdgcn_raw_buffer_load_b128(r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
+        }
     }
-}
+
+    __device__ void commit(unsigned char* dst, int tid) const
+    {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int q = tid + it * kThreads;
+            *reinterpret_cast<u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16) = x[it];
+        }
+    }
+};
 
 __device__ inline u32x4 pack_hilo(f32x4 x)
 {
@@ -1354,7 +1366,8 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
     const int64_t tok0 = u.tok0;
     const int n = u.n;
 
-    load_rows(Kraw, p.k, tok0, n, p.hq, hk, tid);
+    Rows kin;
+    kin.issue(p.k, tok0, n, p.hq, hk, tid);
     f32x4 dk_acc[2][kNB];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -1362,16 +1375,26 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
         for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
 
     for (int hv = hk * r; hv < (hk + 1) * r; ++hv) {  // uniform
-        // ---- inputs of this value head
-        load_rows(Vraw, p.v, tok0, n, p.hv, hv, tid);
-        load_rows(dWraw, p.dW, tok0, n, p.hv, hv, tid);
-        load_rows(dUraw, p.dU, tok0, n, p.hv, hv, tid);
+        // ---- inputs of this value head: every load issued before the first wait
+        Rows vin, dwin, duin;
+        vin.issue(p.v, tok0, n, p.hv, hv, tid);
+        dwin.issue(p.dW, tok0, n, p.hv, hv, tid);
+        duin.issue(p.dU, tok0, n, p.hv, hv, tid);
         const __amdgpu_buffer_rsrc_t brs = rsrc(p.beta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-        if (tid < kC) bs[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, tid * p.hv * 4, 0, 0));
+        const float bval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, (tid & 63) * p.hv * 4, 0, 0));
+        float gval = 0.f;
+        if constexpr (GT) {
+            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
+            gval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, (tid & 63) * p.hv * 4, 0, 0));
+        }
+        if (hv == hk * r) kin.commit(Kraw, tid);
+        vin.commit(Vraw, tid);
+        dwin.commit(dWraw, tid);
+        duin.commit(dUraw, tid);
+        if (tid < kC) bs[tid] = bval;
         if constexpr (GT) {
             if (tid < 64) {  // G = inclusive prefix sums of g in fp64 (as the forward)
-                const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-                double x = static_cast<double>(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, tid * p.hv * 4, 0, 0)));
+                double x = static_cast<double>(gval);
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
                     const double t = __shfl_up(x, d);
