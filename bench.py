@@ -33,7 +33,7 @@ CSRC = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "wyprep_kernels.hip")
 FWD_SOURCE = os.path.join(CSRC, "chunk_fwd.hip")
 ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve", "fwd": "chunk_fwd",
-               "gdn": "gdn_forward"}
+               "gdn": "gdn_forward", "bwd": "wy_backward"}
 
 
 def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy", gated=False):
@@ -53,6 +53,13 @@ def fwd_bytes(tokens, num_states, hq, hv, dk, dv, esz, gated=False):
     gb = 4 if gated else 0
     return tokens * (2 * hq * dk * esz + hv * (dk * esz + dv * esz + gb + dv * esz)) + \
         num_states * hv * dk * dv * 4
+
+
+def bwd_bytes(tokens, hq, hv, dk, dv, esz, gated=False):
+    """wy_backward without dT: k read and dk written once per key head; v, beta, dW, dU (and g)
+    read, dv and dbeta (and dg) written once per value head."""
+    gb = 8 if gated else 0
+    return tokens * (2 * hq * dk * esz + hv * (3 * dv * esz + dk * esz + 8 + gb))
 
 
 def kernel_source_sha(entry="wy"):
@@ -125,6 +132,32 @@ def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
             "value_one_core": units_per_pass * passes1 / el1}
 
 
+def cpu_baseline_bwd(inp, units_per_pass, tokens_per_pass, workload, seconds=10.0):
+    """The fp64 backward oracle, as it stands, on the whole workload (the same seeded dW, dU):
+    whole passes until ~`seconds` on every usable host core."""
+    import oracle
+    from chunkwise_gated_deltanet_amd import synth
+    lib = oracle.load()
+    threads = cpu_threads()
+    B, T, Hv = inp["beta"].shape
+    grng = np.random.default_rng(1000 + workload)
+    dW = synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, 128), dtype=np.float32))
+    dU = synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, 128), dtype=np.float32))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.wy_backward(inp["k"], inp["v"], inp["beta"], inp["chunk_size"], dW, dU,
+                           g=inp["g"], cu_seqlens=inp["cu_seqlens"], nthreads=threads, lib=lib)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": units_per_pass * passes / el, "unit": "chunks/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload ({units_per_pass} units, {tokens_per_pass} tokens) x "
+                      f"{passes} passes, {el:.1f} s wall, fp64 backward",
+            "tokens_per_s": tokens_per_pass * passes / el}
+
+
 def cpu_baseline_fwd(inp, seconds=10.0):
     """The token-by-token fp64 recurrence oracle, as it stands, on a bounded sample of the
     workload: the first (sequence, value head) pairs, one per usable host core, repeated until
@@ -168,14 +201,19 @@ def main(argv=None):
                     help="seeded workload index (2 = the headline C=64 workload)")
     ap.add_argument("--chunk-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--entry", choices=("wy", "wu", "kkt", "fwd", "gdn"), default="wy",
+    ap.add_argument("--entry", choices=("wy", "wu", "kkt", "fwd", "gdn", "bwd"), default="wy",
                     help="wy: wyp_wy_prepare (T, W, U; the headline); wu: wyp_wu_prepare "
                          "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only); fwd: wyp_chunk_fwd "
                          "(state recurrence and output from prepared W, U; C = 64); gdn: the "
-                         "whole forward, wyp_wu_prepare then wyp_chunk_fwd")
+                         "whole forward, wyp_wu_prepare then wyp_chunk_fwd; bwd: "
+                         "wyp_wy_backward (dk, dv, dbeta, dg from dW, dU; no dT; C = 64)")
     ap.add_argument("--gate-mu", type=float, default=None,
                     help="add per-token log gates g = log sigmoid(mu + N(0,1)) (the gated "
                          "coefficient diag(beta)(Gamma o K K^T)); 4 is the seeded gated recipe")
+    ap.add_argument("--segment-chunks", default=None,
+                    help="fwd / gdn entries: split each sequence into segments of this many "
+                         "chunks run in parallel (wyp_chunk_fwd_cp); 'auto' picks it from the "
+                         "shape")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -220,7 +258,9 @@ def main(argv=None):
     units = nchunks * Hv
     tokens = B * T
     nstates = B if inp["cu_seqlens"] is None else len(inp["cu_seqlens"]) - 1
-    if args.entry == "fwd":
+    if args.entry == "bwd":
+        alg = bwd_bytes(tokens, Hq, Hv, dk, dv, esz, gated)
+    elif args.entry == "fwd":
         alg = fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
     elif args.entry == "gdn":
         alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, "wu", gated) + \
@@ -239,6 +279,11 @@ def main(argv=None):
     g0 = torch.from_numpy(inp["g"]).to(dev) if gated else None
     cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
     q0 = dev_tensor(inp["q"], tdt) if fwd_entry else None
+    bwd_entry = args.entry == "bwd"
+    if bwd_entry:  # upstream gradients dW, dU: seeded N(0, 1), bf16
+        grng = np.random.default_rng(1000 + args.workload)
+        dW0 = dev_tensor(synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, dk), dtype=np.float32)), tdt)
+        dU0 = dev_tensor(synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, dv), dtype=np.float32)), tdt)
     sets = []
     for _ in range(nsets):
         sets.append(dict(k=k0.clone(), v=v0.clone(), beta=b0.clone(),
@@ -250,7 +295,13 @@ def main(argv=None):
                          q=q0.clone() if fwd_entry else None,
                          o=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev) if fwd_entry else None,
                          hT=torch.empty(nstates, Hv, dk, dv, dtype=torch.float32, device=dev)
-                         if fwd_entry else None))
+                         if fwd_entry else None,
+                         dW=dW0.clone() if bwd_entry else None,
+                         dU=dU0.clone() if bwd_entry else None,
+                         dk=torch.empty_like(k0) if bwd_entry else None,
+                         dv=torch.empty_like(v0) if bwd_entry else None,
+                         db=torch.empty_like(b0) if bwd_entry else None,
+                         dg=torch.empty_like(b0) if bwd_entry and gated else None))
     prob = cg.Problem(B, T, Hq, Hv, dk, dv, C, 0 if cu is None else cu.numel() - 1,
                       0 if w.dtype == "bf16" else 1)
     import ctypes
@@ -260,8 +311,19 @@ def main(argv=None):
     calls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
                    (s["k"], s["v"], s["g"], s["beta"], s["T"], s["W"], s["U"], s["q"], s["o"],
                     s["hT"])) for s in sets]
+    bcalls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
+                    (s["dW"], s["dU"], s["dk"], s["dv"], s["db"], s["dg"])) for s in sets]
     cu_ptr = ctypes.c_void_p(None if cu is None else cu.data_ptr())
     scale = ctypes.c_float(dk ** -0.5)
+    seg_chunks = None
+    if fwd_entry and args.segment_chunks is not None:
+        if cu is not None:
+            raise SystemExit("--segment-chunks needs a [B, T] workload (no packed sequences)")
+        seg_chunks = (cg.cp_segment_chunks(B, T, Hv, C) if args.segment_chunks == "auto"
+                      else int(args.segment_chunks))
+        ws_bytes = lib.wyp_chunk_fwd_cp_workspace_bytes(pprob, seg_chunks)
+        ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
+        ws_ptr, ws_n = ctypes.c_void_p(ws.data_ptr()), ctypes.c_int64(ws_bytes)
 
     def step(i, sp):
         kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i % nsets]
@@ -271,11 +333,18 @@ def main(argv=None):
             st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
         elif args.entry == "kkt":
             st = lib.wyp_kkt_solve(pprob, kp, gp, bp, cu_ptr, tp, sp)
+        elif args.entry == "bwd":
+            dwp, dup, dkp, dvp, dbp, dgp = bcalls[i % nsets]
+            st = lib.wyp_wy_backward(pprob, kp, vp, gp, bp, cu_ptr, None, dwp, dup, dkp, dvp, dbp,
+                                     dgp, sp)
         else:
             st = 0
             if args.entry == "gdn":
                 st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
-            if st == 0:
+            if st == 0 and seg_chunks is not None:
+                st = lib.wyp_chunk_fwd_cp(pprob, qp, kp, wp, up, gp, None, scale, seg_chunks,
+                                          ws_ptr, ws_n, op, hp, sp)
+            elif st == 0:
                 st = lib.wyp_chunk_fwd(pprob, qp, kp, wp, up, gp, None, scale, cu_ptr, op, hp, sp)
         if st != 0:
             raise RuntimeError(lib.wyp_last_error().decode())
@@ -333,7 +402,8 @@ def main(argv=None):
     # The graph did the work: the last buffer set it wrote equals a fresh eager launch.
     last = (args.steps - 1) % nsets
     outs = {"wy": ("T", "W", "U"), "wu": ("W", "U"), "kkt": ("T",), "fwd": ("o", "hT"),
-            "gdn": ("W", "U", "o", "hT")}[args.entry]
+            "gdn": ("W", "U", "o", "hT"),
+            "bwd": ("dk", "dv", "db") + (("dg",) if gated else ())}[args.entry]
     ref = {n: sets[last][n].clone() for n in outs}
     step(last, sptr)
     torch.cuda.synchronize(dev)
@@ -368,6 +438,7 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "entry": ENTRY_NAMES[args.entry], "gated": gated,
+                   "segment_chunks": seg_chunks if fwd_entry else None,
                    "batch": B, "seqlen": T, "num_qk_heads": Hq,
                    "num_v_heads": Hv, "head_dim": dk, "chunk_size": C,
                    "units_per_step": units, "tokens_per_step": tokens,
@@ -398,6 +469,9 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         if fwd_entry:
             out["cpu_baseline"] = cpu_baseline_fwd(inp, args.cpu_seconds)
+        elif bwd_entry:
+            out["cpu_baseline"] = cpu_baseline_bwd(inp, units, tokens, args.workload,
+                                                   args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -32,6 +32,17 @@
 //   2. O tile += (Gamma o P) V'; S tiles = exp(G_last) S + K^T V'_dec (K^T fragments by
 //      ds_read_tr16_b64); the new bf16 S^T goes to LDS; O is staged and stored as 16-byte rows.
 // The state stays fp32 in the MFMA accumulators for the whole sequence.
+//
+// Sequence parallelism (wyp_chunk_fwd_cp; [QLA] "兼顾访存开销与序列并行的解法": the state
+// kernel's thread blocks number only batch x heads, so the pages split each sequence and fix
+// the split up with a correction computed per segment).  The state after a segment is linear in
+// the state before it, S_end = M S_start + A, so with segments of L chunks:
+//   pass 1 (LOCAL): per (sequence, segment, head), A = the segment's end state from a zero state
+//          and M = its transition (the same recurrence with U = 0 from the identity), as eight
+//          32-column slices; no output;
+//   pass 2 (combine): S_start of segment s + 1 = M_s S_start(s) + A_s, in fp32, per head;
+//   pass 3: the kernel above per (sequence, segment, head) from its true S_start, writing o.
+// Exact, not the gate-decay warm-up approximation the pages also describe.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -79,8 +90,12 @@ struct Params {
     int32_t seqlen;
     int32_t hq;
     int32_t hv;
-    int32_t num_seqs;  // sequences (cu_seqlens) or batch rows
-    int32_t work;      // num_seqs * hv * kSlices
+    int32_t num_seqs;    // sequences (cu_seqlens) or batch rows
+    int32_t work;        // work items: sequences x segments x value heads x slices
+    int32_t nseg;        // segments per sequence (1: the whole sequence)
+    int32_t seg_chunks;  // chunks per segment (nseg > 1)
+    float* ws_a;         // [pair][nseg - 1][dk][dv]: A_s (pass 1), then S_start(s + 1) (pass 2)
+    float* ws_m;         // [pair][nseg - 1][dk][dk]: M_s
 };
 
 // LDS plan (bytes).  Rows of Q, K, W carry 16 bytes of padding (row stride 272 B) so 16-byte
@@ -119,7 +134,8 @@ struct Chunk {
     u32x4 u;
     float g;
 
-    __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, int slice, int tid)
+    __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, int slice, int tid,
+                          bool want_q = true, bool want_u = true)
     {
         const uint32_t qstride = static_cast<uint32_t>(p.hq) * kD * 2;
         const uint32_t wstride = static_cast<uint32_t>(p.hv) * kD * 2;
@@ -129,13 +145,15 @@ struct Chunk {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int pc = tid + it * kThreads;  // row pc / 16, piece pc % 16
-            q[it] = __builtin_amdgcn_raw_buffer_load_b128(qr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
+            q[it] = want_q ? __builtin_amdgcn_raw_buffer_load_b128(qr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0)
+                           : u32x4{0u, 0u, 0u, 0u};
             k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
             w[it] = __builtin_amdgcn_raw_buffer_load_b128(wr, (pc >> 4) * wstride + (pc & 15) * 16, 0, 0);
         }
         const __amdgpu_buffer_rsrc_t ur =
             rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * kDVS, (n - 1) * wstride + kDVS * 2);
-        u = __builtin_amdgcn_raw_buffer_load_b128(ur, (tid >> 2) * wstride + (tid & 3) * 16, 0, kStream);
+        u = want_u ? __builtin_amdgcn_raw_buffer_load_b128(ur, (tid >> 2) * wstride + (tid & 3) * 16, 0, kStream)
+                   : u32x4{0u, 0u, 0u, 0u};
         g = 0.f;
         if (p.g != nullptr && tid < 64) {
             const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
@@ -183,21 +201,34 @@ __device__ inline void seq_range(const Params& p, int seq, int64_t* s0, int64_t*
     }
 }
 
-template <bool GT>
+template <bool GT, bool LOCAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous range of work
-    // items, so the four dv slices of a head (and the heads sharing a key head) meet in one L2.
+    // items, so the dv slices of a head (and the heads sharing a key head) meet in one L2.
     const uint32_t Gsz = gridDim.x;  // a multiple of 8
     const int item = static_cast<int>((blockIdx.x & 7u) * (Gsz >> 3) + (blockIdx.x >> 3));
     if (item >= p.work) return;  // uniform
-    const int slice = item % kSlices;
-    const int pair = item / kSlices;
-    const int hv = pair % p.hv, seq = pair / p.hv;
+    // item = ((seq * nsegw + seg) * Hv + hv) * NSL + slice; pass 1 (LOCAL) has 8 slices (four of
+    // A, four of M) and no item for the last segment
+    constexpr int NSL = LOCAL ? 2 * kSlices : kSlices;
+    const int nsegw = LOCAL ? p.nseg - 1 : p.nseg;
+    const int slice8 = item % NSL;
+    int rest = item / NSL;
+    const int hv = rest % p.hv;
+    rest /= p.hv;
+    const int seg = rest % nsegw, seq = rest / nsegw;
+    const int pair = seq * p.hv + hv;
+    const bool mcols = LOCAL && slice8 >= kSlices;  // a slice of the transition M
+    const int slice = slice8 % kSlices;
     const int hk = hv / (p.hv / p.hq);
     int64_t s0, s1;
     seq_range(p, seq, &s0, &s1);
+    const int nchunks_seq = static_cast<int>((s1 - s0 + kC - 1) / kC);
+    const int c_begin = p.nseg > 1 ? seg * p.seg_chunks : 0;
+    const int c_end = p.nseg > 1 ? min(c_begin + p.seg_chunks, nchunks_seq) : nchunks_seq;
+    const int64_t wsslot = static_cast<int64_t>(pair) * (p.nseg - 1);  // first workspace slot
 
     int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
@@ -213,15 +244,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float* Gs = reinterpret_cast<const float*>(smem + OFF_G);
 
     // State tiles of this wave: S[16 mt + 4 lg + r][16 nt + lr], mt = 2 wave + m, in fp32.
+    // Start: pass 1 from zero (A) or from the identity's columns (M); otherwise the sequence's
+    // initial state (segment 0) or the S_start the combine left in the workspace.
     f32x4 sacc[2][2];
-    const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kDVS : nullptr;
+    const float* h0 = nullptr;
+    if (!LOCAL) {
+        if (seg == 0)
+            h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD : nullptr;
+        else
+            h0 = p.ws_a + (wsslot + seg - 1) * kD * kD;
+    }
+    if (h0) h0 += slice * kDVS;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[m][nt][r] = h0 ? h0[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * (2 * wave + m) + 4 * lg + r, col = 16 * nt + lr;
+                sacc[m][nt][r] = h0 ? h0[row * kD + col] : (mcols && row == slice * kDVS + col ? 1.f : 0.f);
+            }
 
     // S^T (bf16) for the first chunk's products: row = dv column, 4 consecutive dk per lane
     auto write_st = [&]() {
@@ -237,17 +279,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
     write_st();
 
-    const int nchunks = static_cast<int>((s1 - s0 + kC - 1) / kC);
     Chunk cur;
-    if (nchunks > 0) cur.issue(p, s0, static_cast<int>(s1 - s0 < kC ? s1 - s0 : kC), hk, hv, slice, tid);
-    for (int c = 0; c < nchunks; ++c) {  // uniform
+    const bool want_q = !LOCAL, want_u = !mcols;
+    if (c_begin < c_end) {
+        const int64_t t0 = s0 + static_cast<int64_t>(c_begin) * kC;
+        cur.issue(p, t0, static_cast<int>(s1 - t0 < kC ? s1 - t0 : kC), hk, hv, slice, tid, want_q, want_u);
+    }
+    for (int c = c_begin; c < c_end; ++c) {  // uniform
         const int64_t tok0 = s0 + static_cast<int64_t>(c) * kC;
         const int n = static_cast<int>(s1 - tok0 < kC ? s1 - tok0 : kC);
         cur.commit<GT>(smem, tid);
         __syncthreads();  // B1: the chunk (and the state's S^T) is in LDS
-        if (c + 1 < nchunks) {
+        if (c + 1 < c_end) {
             const int64_t nt0 = tok0 + kC;
-            cur.issue(p, nt0, static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC), hk, hv, slice, tid);
+            cur.issue(p, nt0, static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC), hk, hv, slice, tid, want_q, want_u);
         }
         const int I = wave;  // row tile of V' and O
         const float glast = GT ? Gs[kC - 1] : 0.f;
@@ -265,12 +310,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int s = 0; s < kD / 32; ++s) {
             const bf16x8 wa = *reinterpret_cast<const bf16x8*>(Ws + (16 * I + lr) * QROW + 32 * s + 8 * lg);
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (16 * I + lr) * QROW + 32 * s + 8 * lg);
+            bf16x8 qa;
+            if constexpr (!LOCAL) qa = *reinterpret_cast<const bf16x8*>(Qs + (16 * I + lr) * QROW + 32 * s + 8 * lg);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const bf16x8 sb = *reinterpret_cast<const bf16x8*>(St + (16 * nt + lr) * SROW + 32 * s + 8 * lg);
                 vacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, sb, vacc[nt], 0, 0, 0);
-                oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sb, oacc[nt], 0, 0, 0);
+                if constexpr (!LOCAL) oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sb, oacc[nt], 0, 0, 0);
             }
         }
         // V' = U - W S: element r of lane 16 lg + lr is row 16 I + 4 lg + r, column 16 nt + lr
@@ -283,9 +329,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 const float x = uu - vacc[nt][r];
                 vn[r] = static_cast<__bf16>(x);
                 vd[r] = static_cast<__bf16>(GT ? x * __expf(glast - grow[r]) : x);
-                if constexpr (GT) oacc[nt][r] *= __expf(grow[r]);
+                if constexpr (GT && !LOCAL) oacc[nt][r] *= __expf(grow[r]);
             }
-            *reinterpret_cast<bf16x4*>(Vn + (16 * nt + lr) * VROW + 16 * I + 4 * lg) = vn;
+            if constexpr (!LOCAL) *reinterpret_cast<bf16x4*>(Vn + (16 * nt + lr) * VROW + 16 * I + 4 * lg) = vn;
             *reinterpret_cast<bf16x4*>(Vd + (16 * nt + lr) * VROW + 16 * I + 4 * lg) = vd;
         }
         // P^T tiles K_J Q_I^T, J <= I.  Accumulator element r of lane 16 lg + lr is
@@ -296,7 +342,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if constexpr (GT) gi = Gs[16 * I + lr];
 #pragma unroll
         for (int J = 0; J < kNB; ++J) {
-            if (J > I) break;  // uniform
+            if (LOCAL || J > I) break;  // uniform
             f32x4 pt = zero4();
 #pragma unroll
             for (int s = 0; s < kD / 32; ++s) {
@@ -319,7 +365,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // 2a. O += (Gamma o P) V' over the causal k tiles (16x16x16 bf16)
 #pragma unroll
         for (int J = 0; J < kNB; ++J) {
-            if (J > I) break;
+            if (LOCAL || J > I) break;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const bf16x4 vb = *reinterpret_cast<const bf16x4*>(Vn + (16 * nt + lr) * VROW + 16 * J + 4 * lg);
@@ -351,13 +397,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         write_st();
         // O rows of tile I, scaled, staged row-major for 16-byte stores
+        if constexpr (!LOCAL) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Os[(16 * I + 4 * lg + r) * UROW + 16 * nt + lr] = static_cast<__bf16>(p.scale * oacc[nt][r]);
+                for (int r = 0; r < 4; ++r)
+                    Os[(16 * I + 4 * lg + r) * UROW + 16 * nt + lr] = static_cast<__bf16>(p.scale * oacc[nt][r]);
+        }
         __syncthreads();  // B3: O staged, the new S^T in place; Q, K, W, U, V' free
-        {
+        if constexpr (!LOCAL) {
             const uint32_t ostride = static_cast<uint32_t>(p.hv) * kD * 2;
             const __amdgpu_buffer_rsrc_t orr =
                 rsrc(p.o + (tok0 * p.hv + hv) * kD + slice * kDVS, (n - 1) * ostride + kDVS * 2);
@@ -365,8 +413,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             __builtin_amdgcn_raw_buffer_store_b128(val, orr, (tid >> 2) * ostride + (tid & 3) * 16, 0, kStream);
         }
     }
-    if (p.hT != nullptr) {
-        float* hT = p.hT + static_cast<int64_t>(pair) * kD * kD + slice * kDVS;
+    float* out = nullptr;  // where this work item's end state goes
+    if (LOCAL)
+        out = (mcols ? p.ws_m : p.ws_a) + (wsslot + seg) * kD * kD + slice * kDVS;
+    else if (p.hT != nullptr && seg == p.nseg - 1)
+        out = p.hT + static_cast<int64_t>(pair) * kD * kD + slice * kDVS;
+    if (out != nullptr) {
+        float* hT = out;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -374,6 +427,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     hT[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] = sacc[m][nt][r];
+    }
+}
+
+// Pass 2 of the sequence-parallel forward: per (sequence, value head, 32-column dv slice),
+// S_start(0) = the initial state and S_start(s + 1) = M_s S_start(s) + A_s for s = 0 .. nseg - 2,
+// each written over A_s (it is read there by pass 3).  fp32 MFMA 16x16x4; wave w owns row tiles
+// 2w, 2w + 1 of the 128 x 32 slice; S^T sits in LDS so every B operand is one 16-byte read.
+__global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
+{
+    __shared__ __attribute__((aligned(16))) float St[kDVS][kD + 4];
+    const int slice = blockIdx.x % kSlices, pair = blockIdx.x / kSlices;
+    if (pair >= p.num_seqs * p.hv) return;  // uniform
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kDVS : nullptr;
+    for (int idx = tid; idx < kD * kDVS; idx += kThreads) {
+        const int row = idx / kDVS, col = idx % kDVS;
+        St[col][row] = h0 ? h0[row * kD + col] : 0.f;
+    }
+    __syncthreads();
+    const int64_t slot0 = static_cast<int64_t>(pair) * (p.nseg - 1);
+    for (int sg = 0; sg + 1 < p.nseg; ++sg) {  // uniform
+        float* A = p.ws_a + (slot0 + sg) * kD * kD + slice * kDVS;
+        const float* M = p.ws_m + (slot0 + sg) * kD * kD;
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][nt][r] = A[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr];
+#pragma unroll
+                for (int kt = 0; kt < kD / 16; ++kt) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (16 * (2 * wave + m) + lr) * kD + 16 * kt + 4 * lg);
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(&St[16 * nt + lr][16 * kt + 4 * lg]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc[m][nt], 0, 0, 0);
+                }
+            }
+        __syncthreads();  // every read of S_start(s) done
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                *reinterpret_cast<f32x4*>(&St[16 * nt + lr][16 * (2 * wave + m) + 4 * lg]) = acc[m][nt];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) A[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] = acc[m][nt][r];
+            }
+        __syncthreads();
     }
 }
 
@@ -387,8 +492,11 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
     if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
     if (e == hipSuccess) {
         std::call_once(once[device], [&] {
-            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT>),
+            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, false>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+            if (attr_err[device] == hipSuccess)
+                attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, true>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
         });
         e = attr_err[device];
     }
@@ -408,13 +516,31 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.hq = a.num_qk_heads;
         p.hv = a.num_v_heads;
         p.num_seqs = a.num_seqs;
-        p.work = a.num_seqs * a.num_v_heads * kSlices;
-        const uint32_t grid = static_cast<uint32_t>((p.work + 7) / 8 * 8);
-        hipLaunchKernelGGL(chunk_fwd_kernel<GT>, dim3(grid), dim3(kThreads), LDS_TOTAL, stream, p);
-        e = hipGetLastError();
+        p.nseg = a.nseg > 1 ? a.nseg : 1;
+        p.seg_chunks = a.seg_chunks;
+        p.ws_a = a.ws;
+        p.ws_m = a.ws ? a.ws + static_cast<int64_t>(a.num_seqs) * a.num_v_heads * (p.nseg - 1) * kD * kD : nullptr;
+        const int pairs = a.num_seqs * a.num_v_heads;
+        if (p.nseg > 1) {
+            p.work = pairs * (p.nseg - 1) * 2 * kSlices;  // pass 1
+            hipLaunchKernelGGL((chunk_fwd_kernel<GT, true>), dim3(static_cast<uint32_t>((p.work + 7) / 8 * 8)),
+                               dim3(kThreads), LDS_TOTAL, stream, p);
+            e = hipGetLastError();
+            if (e == hipSuccess) {  // pass 2
+                hipLaunchKernelGGL(cp_combine_kernel, dim3(static_cast<uint32_t>(pairs * kSlices)), dim3(kThreads), 0,
+                                   stream, p);
+                e = hipGetLastError();
+            }
+        }
+        if (e == hipSuccess) {  // pass 3 (the whole forward when nseg = 1)
+            p.work = pairs * p.nseg * kSlices;
+            hipLaunchKernelGGL((chunk_fwd_kernel<GT, false>), dim3(static_cast<uint32_t>((p.work + 7) / 8 * 8)),
+                               dim3(kThreads), LDS_TOTAL, stream, p);
+            e = hipGetLastError();
+        }
     }
     if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d)", hipGetErrorString(e), GT ? 1 : 0);
+        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d, segments=%d)", hipGetErrorString(e), GT ? 1 : 0, a.nseg);
         return static_cast<int>(e);
     }
     return 0;

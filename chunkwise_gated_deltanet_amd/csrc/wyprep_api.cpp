@@ -304,3 +304,62 @@ extern "C" wyp_status wyp_wy_backward(const wyp_problem* problem, const void* k,
         return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
     return WYP_OK;
 }
+
+namespace {
+
+// Segments of `segment_chunks` chunks per batch row, or -1 if the arguments are invalid.
+int64_t cp_segments(const wyp_problem* p, int32_t segment_chunks)
+{
+    if (!p || segment_chunks < 1 || p->chunk_size != 64 || p->seqlen < 0) return -1;
+    const int64_t nchunks = (static_cast<int64_t>(p->seqlen) + 63) / 64;
+    return nchunks == 0 ? 1 : (nchunks + segment_chunks - 1) / segment_chunks;
+}
+
+int64_t cp_workspace(const wyp_problem* p, int64_t nseg)
+{
+    return 2 * static_cast<int64_t>(p->batch) * p->num_v_heads * (nseg - 1) * 128 * 128 * 4;
+}
+
+}  // namespace
+
+extern "C" int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t segment_chunks)
+{
+    const int64_t nseg = cp_segments(problem, segment_chunks);
+    if (nseg < 0 || problem->batch < 1 || problem->num_v_heads < 1) return -1;
+    return cp_workspace(problem, nseg);
+}
+
+extern "C" wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
+                                       const void* w, const void* u, const float* g,
+                                       const float* initial_state, float scale,
+                                       int32_t segment_chunks, void* workspace,
+                                       int64_t workspace_bytes, void* o_out, float* final_state,
+                                       void* stream)
+{
+    g_last_error[0] = '\0';
+    wyp::FwdArgs args{};
+    bool empty = false;
+    wyp_status st = validate_fwd(problem, q, k, w, u, g, initial_state, scale, nullptr, o_out,
+                                 final_state, &args, &empty);
+    if (st != WYP_OK || empty) return st;
+    const int64_t nseg = cp_segments(problem, segment_chunks);
+    if (nseg < 1)
+        return fail(WYP_ERR_INVALID_ARGUMENT, "segment_chunks must be >= 1 (got %d)", segment_chunks);
+    if (nseg > 1) {
+        const int64_t need = cp_workspace(problem, nseg);
+        if (!workspace || workspace_bytes < need)
+            return fail(WYP_ERR_INVALID_ARGUMENT, "workspace of %lld bytes needed (%lld given)",
+                        static_cast<long long>(need), static_cast<long long>(workspace_bytes));
+        if (!aligned(workspace, 16))
+            return fail(WYP_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+        if (static_cast<int64_t>(problem->batch) * problem->num_v_heads * nseg * 8 + 8 > INT32_MAX)
+            return fail(WYP_ERR_UNSUPPORTED, "too many segments for one launch");
+    }
+    args.nseg = static_cast<int32_t>(nseg);
+    args.seg_chunks = segment_chunks;
+    args.ws = nseg > 1 ? static_cast<float*>(workspace) : nullptr;
+    char msg[256] = "";
+    if (wyp::launch_fwd(args, stream, msg, sizeof msg) != 0)
+        return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
+    return WYP_OK;
+}

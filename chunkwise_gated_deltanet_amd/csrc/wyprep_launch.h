@@ -45,6 +45,9 @@ struct FwdArgs {
     int32_t num_qk_heads;
     int32_t num_v_heads;
     int32_t num_seqs;          // sequences (cu_seqlens) or batch rows
+    int32_t nseg;              // segments per sequence (<= 1: sequential)
+    int32_t seg_chunks;        // chunks per segment (nseg > 1)
+    float* ws;                 // nseg > 1: 2 x num_seqs x Hv x (nseg - 1) x dk x dk floats
 };
 
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len);

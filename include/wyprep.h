@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 4  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward */
+#define WYP_ABI_VERSION 5  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp */
 
 typedef enum {
     WYP_OK = 0,
@@ -159,6 +159,35 @@ wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* 
                          const void* w_in, const void* u_in, const float* g,
                          const float* initial_state, float scale, const int32_t* cu_seqlens,
                          void* o_out, float* final_state, void* stream);
+
+/* The same forward, split along the sequence ([QLA] "兼顾访存开销与序列并行的解法": the state
+ * recurrence's kernel has only batch x heads thread blocks; the pages split each sequence and
+ * repair the split with a per-segment correction).  The state after a segment of
+ * `segment_chunks` chunks is linear in the state before it, S_end = M S_start + A, so the library
+ * runs three passes on `stream`: (1) every segment's A (from a zero state) and transition M (the
+ * same recurrence with U = 0, from the identity), in parallel; (2) S_start of each segment from
+ * the previous one, S_start(s+1) = M_s S_start(s) + A_s, in fp32; (3) wyp_chunk_fwd's work per
+ * segment from its S_start, writing o (and the final state from the last segment).  Exact up
+ * to rounding (not the pages' gate-decay warm-up approximation).
+ * Arguments as for wyp_chunk_fwd, without cu_seqlens (each batch row is one sequence of T
+ * tokens), plus:
+ *   segment_chunks   chunks per segment, >= 1; a value covering all ceil(T / 64) chunks gives
+ *                    one segment, which is wyp_chunk_fwd itself and needs no workspace
+ *   workspace        caller-owned device memory of at least
+ *                    wyp_chunk_fwd_cp_workspace_bytes(problem, segment_chunks) bytes,
+ *                    16-byte aligned; its contents on entry do not matter and on return are
+ *                    unspecified.  Calls that share a workspace must not overlap.
+ * Supported as wyp_chunk_fwd (bf16, C = 64, dk = dv = 128). */
+wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
+                            const void* w_in, const void* u_in, const float* g,
+                            const float* initial_state, float scale, int32_t segment_chunks,
+                            void* workspace, int64_t workspace_bytes, void* o_out,
+                            float* final_state, void* stream);
+
+/* Workspace bytes wyp_chunk_fwd_cp needs: 2 x B x Hv x (segments - 1) x dk x dk x 4 (A and M
+ * of every segment but the last); 0 for a single segment; -1 for invalid arguments
+ * (segment_chunks < 1, chunk_size other than 64, NULL problem). */
+int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t segment_chunks);
 
 /* Backward of the preparation step (the training path; [QLA] "反向" (backward): FlashQLA fuses
  * bwd_wy with the other backward kernels).  For upstream gradients dT, dW, dU of wyp_wy_prepare's

@@ -30,13 +30,14 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
                           "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_chunk_fwd",
-                          "wyp_wy_backward"}
+                          "wyp_wy_backward", "wyp_chunk_fwd_cp",
+                          "wyp_chunk_fwd_cp_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 4 == cg.ABI_VERSION
+    assert lib.wyp_abi_version() == 5 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -186,3 +187,21 @@ def test_wy_backward_rejects(lib):
     assert call_bwd(lib, good(), dT=FAKE + 2) == 1
     assert call_bwd(lib, good(seqlen=0), k=None, v=None, beta=None, dW=None, dU=None, dk=None,
                     dv=None, db=None) == 0
+
+
+def test_chunk_fwd_cp_workspace_and_rejects(lib):
+    p = good(batch=2, seqlen=1000, num_v_heads=4)       # 16 chunks per row
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 16) == 0   # one segment
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 5) == 2 * 2 * 4 * 3 * 128 * 128 * 4
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 0) == -1
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(good(chunk_size=32)), 4) == -1
+    need = lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 4)
+
+    def call(seg=4, ws=FAKE, nbytes=need, **kw):
+        return lib.wyp_chunk_fwd_cp(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0.5, seg,
+                                    ws, nbytes, FAKE, None, None)
+    assert call(ws=None) == 1
+    assert "workspace" in lib.wyp_last_error().decode()
+    assert call(nbytes=need - 1) == 1
+    assert call(ws=FAKE + 4) == 1
+    assert call(seg=0) == 1

@@ -151,3 +151,68 @@ def test_chunk_fwd_full_size(idx, mu, gpu):
     assert worst <= FWD_TOL, worst
     del o, hT
     torch.cuda.empty_cache()
+
+
+# Sequence-parallel forward (wyp_chunk_fwd_cp): per-segment transitions, an fp32 combine, then
+# the forward per segment.  Same oracle, same bar; segment lengths cover a single chunk, a
+# ragged last segment and a single segment.
+CP_CASES = {
+    "B1_T1000_H2_seg1": (dict(batch=1, seqlen=1000, num_qk_heads=2, num_v_heads=2, seed=130), 1),
+    "B2_T700_H2_mu4_h0_seg3": (dict(batch=2, seqlen=700, num_qk_heads=1, num_v_heads=2, seed=131,
+                                    gate_mu=4.0, h0=True), 3),
+    "B1_T2048_H4_mu0_seg5": (dict(batch=1, seqlen=2048, num_qk_heads=4, num_v_heads=4, seed=132,
+                                  gate_mu=0.0), 5),
+    "B1_T2048_H2_ungated_h0_seg8": (dict(batch=1, seqlen=2048, num_qk_heads=2, num_v_heads=2,
+                                         seed=133, h0=True), 8),
+    "B1_T333_H2_one_segment": (dict(batch=1, seqlen=333, num_qk_heads=2, num_v_heads=2, seed=134), 6),
+}
+
+
+def run_fwd_cp(inp, h0, device, seg):
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    k, v, beta, _ = to_device(inp, device)
+    q = q_of(inp, device)
+    g = gate_of(inp, device)
+    W, U = cg.wu_prepare(k, v, beta, 64, g=g)
+    o = torch.full(v.shape, float("nan"), dtype=v.dtype, device=device)
+    h0d = None if h0 is None else torch.from_numpy(h0).to(device)
+    o, hT = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=h0d, o_out=o,
+                         output_final_state=True, segment_chunks=seg)
+    torch.cuda.synchronize(device)
+    return o, hT
+
+
+@pytest.mark.parametrize("name", sorted(CP_CASES))
+def test_chunk_fwd_cp(name, gpu):
+    import torch
+    spec, seg = CP_CASES[name]
+    inp, h0 = make_inputs(spec)
+    say(f"chunk_fwd_cp {name} segment_chunks={seg}")
+    o, hT = run_fwd_cp(inp, h0, gpu, seg)
+    assert not torch.isnan(o).any(), "unwritten o entries"
+    o_ref, h_ref = oracle_fwd(inp, h0)
+    ro, rh = rel_fro(to_f64(o), o_ref), rel_fro(to_f64(hT), h_ref)
+    say(f"[cp {name}] o rel fro {ro:.3e}, final state rel fro {rh:.3e}")
+    assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mu", [None, 4.0])
+def test_chunk_fwd_cp_full_size(mu, gpu):
+    """B=1 T=8192 H=16/16 C=64 with the automatic segment length, sampled heads."""
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    w = synth.workload(2, chunk_size=64, gate_mu=mu, with_q=True)
+    inp = synth.generate(w)
+    seg = cg.cp_segment_chunks(1, 8192, 16)
+    say(f"chunk_fwd_cp full {w.name} gate_mu={mu} segment_chunks={seg}")
+    o, hT = run_fwd_cp(inp, None, gpu, seg)
+    assert not torch.isnan(o).any()
+    pairs = [(0, 0), (0, 7), (0, 15)]
+    o_ref, h_ref = oracle_fwd(inp, None, pairs=pairs)
+    for s, h in pairs:
+        ro = rel_fro(to_f64(o[0, :, h]), o_ref[0, :, h])
+        rh = rel_fro(to_f64(hT[s, h]), h_ref[s, h])
+        say(f"  head {h}: o rel fro {ro:.3e}, final state rel fro {rh:.3e}")
+        assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
