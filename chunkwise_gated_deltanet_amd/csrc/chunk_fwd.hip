@@ -98,24 +98,25 @@ struct Params {
     float* ws_m;         // [pair][nseg - 1][dk][dk]: M_s
 };
 
-// LDS plan (bytes).  Rows of Q, K, W carry 16 bytes of padding (row stride 272 B) so 16-byte
-// reads of one column chunk by 16 consecutive rows spread over the banks; the transposed bf16
-// tiles (S^T, V'^T) are padded the same way.
-constexpr int QROW = kD + 8;          // bf16 per Q / K / W row
+// LDS plan (bytes).  Only what several waves read goes through LDS: K (rows padded by 16 bytes,
+// row stride 272 B, so 16-byte reads of one column chunk by 16 consecutive rows spread over the
+// banks), the U slice, the staged O slice, the bf16 S^T and V'^T tiles (padded the same way) and
+// G.  Q and W rows of row tile w are read by wave w alone, so they go from HBM straight into its
+// MFMA operand registers: this halves the LDS traffic of a chunk step and lets three workgroups
+// share a CU (45.8 KB each).
+constexpr int QROW = kD + 8;          // bf16 per K row
 constexpr int UROW = kDVS + 8;        // bf16 per U / O slice row
 constexpr int SROW = kD + 8;          // bf16 per S^T row (one dv column of S)
 constexpr int VROW = kC + 8;          // bf16 per V'^T row (one dv column of V')
-constexpr int OFF_Q = 0;
-constexpr int OFF_K = OFF_Q + kC * QROW * 2;
-constexpr int OFF_W = OFF_K + kC * QROW * 2;
-constexpr int OFF_U = OFF_W + kC * QROW * 2;
+constexpr int OFF_K = 0;
+constexpr int OFF_U = OFF_K + kC * QROW * 2;
 constexpr int OFF_O = OFF_U + kC * UROW * 2;
 constexpr int OFF_S = OFF_O + kC * UROW * 2;
 constexpr int OFF_VN = OFF_S + kDVS * SROW * 2;
 constexpr int OFF_VD = OFF_VN + kDVS * VROW * 2;
 constexpr int OFF_G = OFF_VD + kDVS * VROW * 2;
 constexpr int LDS_TOTAL = OFF_G + kC * 4;
-static_assert(2 * LDS_TOTAL <= 160 * 1024, "two workgroups per CU");
+static_assert(3 * LDS_TOTAL <= 160 * 1024, "three workgroups per CU");
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -126,30 +127,47 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferConfig);
 }
 
-// One chunk's rows in flight to registers: Q, K, W (64 rows x 256 B: four 16-byte pieces per
-// thread each), the U slice (64 rows x 64 B: one piece per thread) and g (wave 0, one per lane).
-// Rows past the chunk's n tokens read as 0 through the buffer range.
+// One chunk's data in flight to registers: K (64 rows x 256 B: four 16-byte pieces per thread),
+// the U slice (64 rows x 64 B: one piece per thread), g (wave 0, one per lane), and for wave w
+// its own Q and W rows 16 w .. 16 w + 15 as 16x16x32 MFMA operands: lane 16 lg + lr holds
+// elements 32 s + 8 lg .. + 7 of row 16 w + lr, s = 0..3.  Rows past the chunk's n tokens read
+// as 0 through the buffer range.
 struct Chunk {
     u32x4 q[4], k[4], w[4];
     u32x4 u;
     float g;
 
-    __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, int slice, int tid,
-                          bool want_q = true, bool want_u = true)
+    // This wave's Q and W operands (issued separately: the current chunk's copies must be dead
+    // first).
+    __device__ void issue_qw(const Params& p, int64_t tok0, int n, int hk, int hv, int tid, bool want_q)
     {
         const uint32_t qstride = static_cast<uint32_t>(p.hq) * kD * 2;
         const uint32_t wstride = static_cast<uint32_t>(p.hv) * kD * 2;
         const __amdgpu_buffer_rsrc_t qr = rsrc(p.q + (tok0 * p.hq + hk) * kD, (n - 1) * qstride + kD * 2);
-        const __amdgpu_buffer_rsrc_t kr = rsrc(p.k + (tok0 * p.hq + hk) * kD, (n - 1) * qstride + kD * 2);
         const __amdgpu_buffer_rsrc_t wr = rsrc(p.w + (tok0 * p.hv + hv) * kD, (n - 1) * wstride + kD * 2);
+        const int lane = tid & 63, row = 16 * (tid >> 6) + (lane & 15), lg = lane >> 4;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const uint32_t col = (32 * it + 8 * lg) * 2;
+            q[it] = want_q ? __builtin_amdgcn_raw_buffer_load_b128(qr, row * qstride + col, 0, 0)
+                           : u32x4{0u, 0u, 0u, 0u};
+            w[it] = __builtin_amdgcn_raw_buffer_load_b128(wr, row * wstride + col, 0, 0);
+        }
+    }
+
+    // K, U and g (all of them, or without Q / W when `qw` is false).
+    __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, int slice, int tid,
+                          bool want_q = true, bool want_u = true, bool qw = true)
+    {
+        const uint32_t qstride = static_cast<uint32_t>(p.hq) * kD * 2;
+        const uint32_t wstride = static_cast<uint32_t>(p.hv) * kD * 2;
+        const __amdgpu_buffer_rsrc_t kr = rsrc(p.k + (tok0 * p.hq + hk) * kD, (n - 1) * qstride + kD * 2);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int pc = tid + it * kThreads;  // row pc / 16, piece pc % 16
-            q[it] = want_q ? __builtin_amdgcn_raw_buffer_load_b128(qr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0)
-                           : u32x4{0u, 0u, 0u, 0u};
             k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
-            w[it] = __builtin_amdgcn_raw_buffer_load_b128(wr, (pc >> 4) * wstride + (pc & 15) * 16, 0, 0);
         }
+        if (qw) issue_qw(p, tok0, n, hk, hv, tid, want_q);
         const __amdgpu_buffer_rsrc_t ur =
             rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * kDVS, (n - 1) * wstride + kDVS * 2);
         u = want_u ? __builtin_amdgcn_raw_buffer_load_b128(ur, (tid >> 2) * wstride + (tid & 3) * 16, 0, kStream)
@@ -161,18 +179,15 @@ struct Chunk {
         }
     }
 
-    // Q, K, W, U to LDS; wave 0 turns g into the chunk-local inclusive prefix sums G (fp64
-    // shuffle scan, stored as fp32).
+    // K and U to LDS; wave 0 turns g into the chunk-local inclusive prefix sums G (fp64 shuffle
+    // scan, stored as fp32).  Q and W stay in registers.
     template <bool GT>
     __device__ void commit(unsigned char* smem, int tid) const
     {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int pc = tid + it * kThreads;
-            const int off = (pc >> 4) * (QROW * 2) + (pc & 15) * 16;
-            *reinterpret_cast<u32x4*>(smem + OFF_Q + off) = q[it];
-            *reinterpret_cast<u32x4*>(smem + OFF_K + off) = k[it];
-            *reinterpret_cast<u32x4*>(smem + OFF_W + off) = w[it];
+            *reinterpret_cast<u32x4*>(smem + OFF_K + (pc >> 4) * (QROW * 2) + (pc & 15) * 16) = k[it];
         }
         *reinterpret_cast<u32x4*>(smem + OFF_U + (tid >> 2) * (UROW * 2) + (tid & 3) * 16) = u;
         if constexpr (GT) {
@@ -202,7 +217,7 @@ __device__ inline void seq_range(const Params& p, int seq, int64_t* s0, int64_t*
 }
 
 template <bool GT, bool LOCAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_fwd_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous range of work
@@ -233,9 +248,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + OFF_Q);
     const __bf16* Ks = reinterpret_cast<const __bf16*>(smem + OFF_K);
-    const __bf16* Ws = reinterpret_cast<const __bf16*>(smem + OFF_W);
     const __bf16* Us = reinterpret_cast<const __bf16*>(smem + OFF_U);
     __bf16* Os = reinterpret_cast<__bf16*>(smem + OFF_O);
     __bf16* St = reinterpret_cast<__bf16*>(smem + OFF_S);
@@ -289,11 +302,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int64_t tok0 = s0 + static_cast<int64_t>(c) * kC;
         const int n = static_cast<int>(s1 - tok0 < kC ? s1 - tok0 : kC);
         cur.commit<GT>(smem, tid);
-        __syncthreads();  // B1: the chunk (and the state's S^T) is in LDS
-        if (c + 1 < c_end) {
-            const int64_t nt0 = tok0 + kC;
-            cur.issue(p, nt0, static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC), hk, hv, slice, tid, want_q, want_u);
+        // this wave's Q and W operands leave the prefetch registers before they are reused
+        bf16x8 qa[kD / 32], wa[kD / 32];
+#pragma unroll
+        for (int s = 0; s < kD / 32; ++s) {
+            qa[s] = __builtin_bit_cast(bf16x8, cur.q[s]);
+            wa[s] = __builtin_bit_cast(bf16x8, cur.w[s]);
         }
+        __syncthreads();  // B1: the chunk (and the state's S^T) is in LDS
+        const int64_t nt0 = tok0 + kC;
+        const int nn = static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC);
+        if (c + 1 < c_end) cur.issue(p, nt0, nn, hk, hv, slice, tid, want_q, want_u, false);
         const int I = wave;  // row tile of V' and O
         const float glast = GT ? Gs[kC - 1] : 0.f;
         float grow[4];
@@ -309,14 +328,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
 #pragma unroll
         for (int s = 0; s < kD / 32; ++s) {
-            const bf16x8 wa = *reinterpret_cast<const bf16x8*>(Ws + (16 * I + lr) * QROW + 32 * s + 8 * lg);
-            bf16x8 qa;
-            if constexpr (!LOCAL) qa = *reinterpret_cast<const bf16x8*>(Qs + (16 * I + lr) * QROW + 32 * s + 8 * lg);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const bf16x8 sb = *reinterpret_cast<const bf16x8*>(St + (16 * nt + lr) * SROW + 32 * s + 8 * lg);
-                vacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, sb, vacc[nt], 0, 0, 0);
-                if constexpr (!LOCAL) oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, sb, oacc[nt], 0, 0, 0);
+                vacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], sb, vacc[nt], 0, 0, 0);
+                if constexpr (!LOCAL) oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], sb, oacc[nt], 0, 0, 0);
             }
         }
         // V' = U - W S: element r of lane 16 lg + lr is row 16 I + 4 lg + r, column 16 nt + lr
@@ -347,8 +363,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int s = 0; s < kD / 32; ++s) {
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (16 * J + lr) * QROW + 32 * s + 8 * lg);
-                const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qs + (16 * I + lr) * QROW + 32 * s + 8 * lg);
-                pt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, pt, 0, 0, 0);
+                pt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qa[s], pt, 0, 0, 0);
             }
             bf16x4 a;
 #pragma unroll
@@ -361,6 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             pa[J] = a;
         }
         __syncthreads();  // B2: V'^T and V'_dec^T complete; every read of S^T and U is done
+        if (c + 1 < c_end) cur.issue_qw(p, nt0, nn, hk, hv, tid, want_q);  // qa, wa are dead
 
         // 2a. O += (Gamma o P) V' over the causal k tiles (16x16x16 bf16)
 #pragma unroll
