@@ -40,7 +40,8 @@
 //   pass 1 (LOCAL): per (sequence, segment, head), A = the segment's end state from a zero state
 //          and M = its transition (the same recurrence with U = 0 from the identity), as eight
 //          32-column slices; no output;
-//   pass 2 (combine): S_start of segment s + 1 = M_s S_start(s) + A_s, in fp32, per head;
+//   pass 2 (combine): S_start of segment s + 1 = M_s S_start(s) + A_s, in fp32, per head and
+//          16-column slice;
 //   pass 3: the kernel above per (sequence, segment, head) from its true S_start, writing o.
 // Exact, not the gate-decay warm-up approximation the pages also describe.
 #include <hip/hip_runtime.h>
@@ -446,55 +447,77 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 }
 
-// Pass 2 of the sequence-parallel forward: per (sequence, value head, 32-column dv slice),
+// Pass 2 of the sequence-parallel forward: per (sequence, value head, 16-column dv slice),
 // S_start(0) = the initial state and S_start(s + 1) = M_s S_start(s) + A_s for s = 0 .. nseg - 2,
-// each written over A_s (it is read there by pass 3).  fp32 MFMA 16x16x4; wave w owns row tiles
-// 2w, 2w + 1 of the 128 x 32 slice; S^T sits in LDS so every B operand is one 16-byte read.
+// each written over A_s (it is read there by pass 3).  Each step is 128 x 128 x 16 fp32
+// multiply-adds on fp32 MFMA 16x16x4, bound by that unit's throughput, so the slices are 16
+// columns wide (eight workgroups per head); wave w owns row tiles 2w, 2w + 1; S^T sits in LDS so
+// every B operand is one 16-byte read.  M_{s+1} and A_{s+1} do not depend on S and are in
+// flight while step s computes.
+constexpr int kCombCols = 16;
+constexpr int kCombSlices = kD / kCombCols;
+
+struct CombineOperands {
+    f32x4 m[2][kD / 16];  // M rows 16 mt + lr, columns 16 kt + 4 lg .. + 3 (A operands)
+    f32x4 a[2];           // A elements [16 mt + 4 lg + r][lr] of the slice (accumulator start)
+
+    __device__ void load(const Params& p, int64_t slot, int slice, int wave, int lr, int lg)
+    {
+        const float* A = p.ws_a + slot * kD * kD + slice * kCombCols;
+        const float* M = p.ws_m + slot * kD * kD;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            const int mt = 2 * wave + mm;
+#pragma unroll
+            for (int kt = 0; kt < kD / 16; ++kt)
+                m[mm][kt] = *reinterpret_cast<const f32x4*>(M + (16 * mt + lr) * kD + 16 * kt + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[mm][r] = A[(16 * mt + 4 * lg + r) * kD + lr];
+        }
+    }
+};
+
 __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(16))) float St[kDVS][kD + 4];
-    const int slice = blockIdx.x % kSlices, pair = blockIdx.x / kSlices;
+    __shared__ __attribute__((aligned(16))) float St[kCombCols][kD + 4];
+    const int slice = blockIdx.x % kCombSlices, pair = blockIdx.x / kCombSlices;
     if (pair >= p.num_seqs * p.hv) return;  // uniform
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kDVS : nullptr;
-    for (int idx = tid; idx < kD * kDVS; idx += kThreads) {
-        const int row = idx / kDVS, col = idx % kDVS;
+    const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kCombCols : nullptr;
+    const int64_t slot0 = static_cast<int64_t>(pair) * (p.nseg - 1);
+    CombineOperands cur, nxt;
+    if (p.nseg > 1) cur.load(p, slot0, slice, wave, lr, lg);
+    for (int idx = tid; idx < kD * kCombCols; idx += kThreads) {
+        const int row = idx / kCombCols, col = idx % kCombCols;
         St[col][row] = h0 ? h0[row * kD + col] : 0.f;
     }
     __syncthreads();
-    const int64_t slot0 = static_cast<int64_t>(pair) * (p.nseg - 1);
     for (int sg = 0; sg + 1 < p.nseg; ++sg) {  // uniform
-        float* A = p.ws_a + (slot0 + sg) * kD * kD + slice * kDVS;
-        const float* M = p.ws_m + (slot0 + sg) * kD * kD;
-        f32x4 acc[2][2];
+        if (sg + 2 < p.nseg) nxt.load(p, slot0 + sg + 1, slice, wave, lr, lg);
+        f32x4 acc[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int mm = 0; mm < 2; ++mm) {
+            acc[mm] = cur.a[mm];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int kt = 0; kt < kD / 16; ++kt) {
+                const f32x4 b = *reinterpret_cast<const f32x4*>(&St[lr][16 * kt + 4 * lg]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[m][nt][r] = A[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr];
-#pragma unroll
-                for (int kt = 0; kt < kD / 16; ++kt) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (16 * (2 * wave + m) + lr) * kD + 16 * kt + 4 * lg);
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(&St[16 * nt + lr][16 * kt + 4 * lg]);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc[m][nt], 0, 0, 0);
-                }
+                for (int q = 0; q < 4; ++q)
+                    acc[mm] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.m[mm][kt][q], b[q], acc[mm], 0, 0, 0);
             }
+        }
         __syncthreads();  // every read of S_start(s) done
+        float* A = p.ws_a + (slot0 + sg) * kD * kD + slice * kCombCols;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int mm = 0; mm < 2; ++mm) {
+            *reinterpret_cast<f32x4*>(&St[lr][16 * (2 * wave + mm) + 4 * lg]) = acc[mm];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                *reinterpret_cast<f32x4*>(&St[16 * nt + lr][16 * (2 * wave + m) + 4 * lg]) = acc[m][nt];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) A[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] = acc[m][nt][r];
-            }
+            for (int r = 0; r < 4; ++r) A[(16 * (2 * wave + mm) + 4 * lg + r) * kD + lr] = acc[mm][r];
+        }
         __syncthreads();
+        cur = nxt;
     }
 }
 
@@ -543,8 +566,8 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
                                dim3(kThreads), LDS_TOTAL, stream, p);
             e = hipGetLastError();
             if (e == hipSuccess) {  // pass 2
-                hipLaunchKernelGGL(cp_combine_kernel, dim3(static_cast<uint32_t>(pairs * kSlices)), dim3(kThreads), 0,
-                                   stream, p);
+                hipLaunchKernelGGL(cp_combine_kernel, dim3(static_cast<uint32_t>(pairs * kCombSlices)), dim3(kThreads),
+                                   0, stream, p);
                 e = hipGetLastError();
             }
         }
