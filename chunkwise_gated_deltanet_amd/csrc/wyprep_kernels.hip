@@ -1171,6 +1171,13 @@ namespace bwd {
 
 constexpr int kC = 64;
 constexpr int kNB = kC / 16;
+// Eight waves per workgroup: LDS (140 KB) holds one workgroup per CU, and with one wave per SIMD
+// every LDS, MFMA and VALU latency of the unit's long serial chain would be exposed.  Phases
+// that tile over waves run twice as wide; the forward's Gram / substitution / coupling steps
+// keep their four-wave mapping.
+constexpr int kBT = 512;
+constexpr int kBW = kBT / 64;
+constexpr int kCW = kD / 16 / kBW;  // dk column tiles per wave in the transposed products
 constexpr int KROW = kD + 8;                 // bf16 per staged K / V / dW / dU row
 constexpr int TRS = kC + 4;                  // floats per n x n tile row
 constexpr int KB = kC * KROW * 2;            // 17408
@@ -1184,8 +1191,8 @@ constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, strict lower 
 constexpr int OFF_X = OFF_H + TB;            // X -> Y^T -> M (fp32)
 constexpr int OFF_TT = OFF_X + TB;           // T^T as hi / lo chunks
 constexpr int OFF_B = OFF_TT + TB;           // beta (64 floats)
-constexpr int OFF_PART = OFF_B + kC * 4;     // per-wave row partials: 4 waves x 3 x 64 floats
-constexpr int OFF_RED = OFF_PART + 4 * 3 * kC * 4;  // dbeta, dG of this value head (2 x 64)
+constexpr int OFF_PART = OFF_B + kC * 4;     // per-wave row partials: kBW waves x 2 x 64 floats
+constexpr int OFF_RED = OFF_PART + kBW * 2 * kC * 4;  // dbeta, dG of this value head (2 x 64)
 constexpr int OFF_INFO = OFF_RED + 2 * kC * 4;
 constexpr int LDS_TOTAL = OFF_INFO + 16;
 static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
@@ -1213,19 +1220,20 @@ struct Params {
     int32_t num_seqs;
 };
 
-// Rows [0, n) of a [tokens, heads, 128] bf16 tensor in flight to registers (four 16-byte
-// pieces per thread; rows >= n read as 0 through the buffer range), then into LDS rows of KROW
+// Rows [0, n) of a [tokens, heads, 128] bf16 tensor in flight to registers (two 16-byte pieces
+// per thread; rows >= n read as 0 through the buffer range), then into LDS rows of KROW
 // elements.  All of a value head's rows are issued before any is waited for.
 struct Rows {
-    u32x4 x[4];
+    static constexpr int NIT = kC * 16 / kBT;
+    u32x4 x[NIT];
 
     __device__ void issue(const __bf16* base, int64_t tok0, int n, int heads, int head, int tid)
     {
         const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
         const __amdgpu_buffer_rsrc_t r = rsrc(base + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int q = tid + it * kThreads;
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kBT;
             x[it] = __builtin_amdgcn_raw_buffer_load_b128(r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
         }
     }
@@ -1233,8 +1241,8 @@ struct Rows {
     __device__ void commit(unsigned char* dst, int tid) const
     {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int q = tid + it * kThreads;
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kBT;
             *reinterpret_cast<u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16) = x[it];
         }
     }
@@ -1264,37 +1272,35 @@ __device__ inline f32x4 unpack_hilo(u32x4 c)
     return x;
 }
 
-// Transposed products over tokens: acc[ni][mi] (+)= sum_kt X^T(ni, kt) B(kt, mi) for the two
-// dk column tiles ni = wave, wave + 4 and the four token tiles mi, where X^T fragments come from
-// the staged bf16 rows of `src` by transposed LDS reads and B(kt, mi) is the packed hi / lo chunk
-// of row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed chunks).  KT_GE_MI
+// Transposed products over tokens: acc[c][mi] (+)= sum_kt X^T(ni, kt) B(kt, mi) for the dk
+// column tile ni = wave + 8 c and the four token tiles mi, where X^T fragments come from the
+// staged bf16 rows of `src` by transposed LDS reads and B(kt, mi) is the packed hi / lo chunk of
+// row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed chunks).  KT_GE_MI
 // skips the k tiles kt < mi (B = T^T is zero there).  Accumulator element r of lane 16 g + c is
 // (.)[16 ni + 4 g + r][16 mi + c].
 template <bool KT_GE_MI>
 __device__ inline void tr_products(const unsigned char* src, const float* bp, int wave, int lr, int lg,
-                                   f32x4 (&acc)[2][kNB])
+                                   f32x4 (&acc)[kCW][kNB])
 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const __bf16* base = reinterpret_cast<const __bf16*>(src);
-    u32x4 bch[kNB][kNB];
 #pragma unroll
-    for (int mi = 0; mi < kNB; ++mi)
+    for (int kt = 0; kt < kNB; ++kt) {
+        u32x4 bch[kNB];
 #pragma unroll
-        for (int kt = 0; kt < kNB; ++kt)
-            bch[mi][kt] = (KT_GE_MI && kt < mi) ? u32x4{0u, 0u, 0u, 0u}
-                                                : *reinterpret_cast<const u32x4*>(bp + (16 * mi + lr) * TRS + 16 * kt + 4 * lg);
+        for (int mi = 0; mi < kNB; ++mi)
+            bch[mi] = (KT_GE_MI && kt < mi) ? u32x4{0u, 0u, 0u, 0u}
+                                            : *reinterpret_cast<const u32x4*>(bp + (16 * mi + lr) * TRS + 16 * kt + 4 * lg);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int ni = wave + 4 * c;
-#pragma unroll
-        for (int kt = 0; kt < kNB; ++kt) {
+        for (int c = 0; c < kCW; ++c) {
+            const int ni = wave + kBW * c;
             const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
             const i16x4 xf = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
                 if (KT_GE_MI && kt < mi) continue;
-                const u32x4 ch = bch[mi][kt];
+                const u32x4 ch = bch[mi];
                 acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                     xf, __builtin_bit_cast(i16x4, u32x2{ch[0], ch[1]}), acc[c][mi], 0, 0, 0);
                 acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
@@ -1306,32 +1312,32 @@ __device__ inline void tr_products(const unsigned char* src, const float* bp, in
 
 // Stages transposed accumulators (element r of lane 16 g + c = X[16 mi + c][16 ni + 4 g + r])
 // as bf16 rows of `dst` and stores rows [0, n) to a [tokens, heads, 128] tensor.
-__device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[2][kNB], __bf16* out, int64_t tok0,
+__device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][kNB], __bf16* out, int64_t tok0,
                                    int n, int heads, int head, int wave, int lr, int lg, int tid)
 {
     __bf16* d = reinterpret_cast<__bf16*>(dst);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kCW; ++c)
 #pragma unroll
         for (int mi = 0; mi < kNB; ++mi) {
             bf16x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[c][mi][r]);
-            *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + 4 * c) + 4 * lg) = o;
+            *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + kBW * c) + 4 * lg) = o;
         }
     __syncthreads();
     const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
     const __amdgpu_buffer_rsrc_t r = rsrc(out + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int q = tid + it * kThreads;
+    for (int it = 0; it < Rows::NIT; ++it) {
+        const int q = tid + it * kBT;
         const u32x4 val = *reinterpret_cast<const u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16);
         __builtin_amdgcn_raw_buffer_store_b128(val, r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
     }
 }
 
 template <bool GT>
-__global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
+__global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char* Kraw = smem + OFF_K;
@@ -1368,9 +1374,9 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
 
     Rows kin;
     kin.issue(p.k, tok0, n, p.hq, hk, tid);
-    f32x4 dk_acc[2][kNB];
+    f32x4 dk_acc[kCW][kNB];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kCW; ++c)
 #pragma unroll
         for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
 
@@ -1408,10 +1414,10 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
 
         // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs): the forward's form_a
         // with H kept
-        form_a<kC, 0, KROW, TL, GT>(Kraw, Ts, bs, tid);
+        if (tid < kThreads) form_a<kC, 0, KROW, TL, GT>(Kraw, Ts, bs, tid);  // its four-wave map
         {
             constexpr int NTILE = kNB * (kNB + 1) / 2;
-            for (int t = wave; t < NTILE; t += kWaves) {  // uniform
+            for (int t = wave; t < NTILE; t += kBW) {  // uniform
                 int I = 0, J = 0;
                 tile_of(t, &I, &J);
                 GramFrags<0, KROW> f;
@@ -1427,7 +1433,7 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                     Hs[i * TRS + j] = i > j ? h : 0.f;
                 }
             }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kWaves) {  // strict upper tiles
+            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {  // strict upper tiles
                 int Iu = 0, rem = t;
                 while (rem >= kNB - 1 - Iu) {
                     rem -= kNB - 1 - Iu;
@@ -1445,8 +1451,8 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
 
         // ---- T^T as hi / lo chunks: chunk (i, c4) holds T[4 c4 + e][i], e = 0..3
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int q = tid + it * kThreads;
+        for (int it = 0; it < kC * 16 / kBT; ++it) {
+            const int q = tid + it * kBT;
             const int i = q >> 4, c4 = q & 15;
             f32x4 x;
 #pragma unroll
@@ -1459,7 +1465,7 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                 rsrc(p.dT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
                      p.dT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0);
             constexpr int NTILE = kNB * (kNB + 1) / 2;
-            for (int t = wave; t < NTILE; t += kWaves) {  // uniform
+            for (int t = wave; t < NTILE; t += kBW) {  // uniform
                 int I = 0, J = 0;
                 tile_of(t, &I, &J);
                 f32x4 pw = zero4(), pu = zero4();
@@ -1492,7 +1498,7 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                     Xs[i * TRS + j] = x;
                 }
             }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kWaves) {
+            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
                 int Iu = 0, rem = t;
                 while (rem >= kNB - 1 - Iu) {
                     rem -= kNB - 1 - Iu;
@@ -1508,11 +1514,12 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
         // stored transposed over X
         {
             constexpr int NTILE = kNB * (kNB + 1) / 2;
-            f32x4 y[3];
+            constexpr int NT = (NTILE + kBW - 1) / kBW;
+            f32x4 y[NT];
 #pragma unroll
-            for (int tt = 0; tt < 3; ++tt) {
+            for (int tt = 0; tt < NT; ++tt) {
                 y[tt] = zero4();
-                const int t = wave + kWaves * tt;
+                const int t = wave + kBW * tt;
                 if (t >= NTILE) break;
                 int Mt = 0, J = 0;
                 tile_of(t, &Mt, &J);
@@ -1525,8 +1532,8 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
             }
             __syncthreads();  // every read of X done
 #pragma unroll
-            for (int tt = 0; tt < 3; ++tt) {
-                const int t = wave + kWaves * tt;
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = wave + kBW * tt;
                 if (t >= NTILE) break;
                 int Mt = 0, J = 0;
                 tile_of(t, &Mt, &J);
@@ -1540,11 +1547,12 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
         // the hi / lo chunks (hi + lo), Y from Y^T rows
         {
             constexpr int NTILE = kNB * (kNB + 1) / 2;
-            f32x4 m[3];
+            constexpr int NT = (NTILE + kBW - 1) / kBW;
+            f32x4 m[NT];
 #pragma unroll
-            for (int tt = 0; tt < 3; ++tt) {
+            for (int tt = 0; tt < NT; ++tt) {
                 m[tt] = zero4();
-                const int t = wave + kWaves * tt;
+                const int t = wave + kBW * tt;
                 if (t >= NTILE) break;
                 int I = 0, J = 0;
                 tile_of(t, &I, &J);
@@ -1557,8 +1565,8 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
             }
             __syncthreads();  // every read of Y^T done
 #pragma unroll
-            for (int tt = 0; tt < 3; ++tt) {
-                const int t = wave + kWaves * tt;
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t = wave + kBW * tt;
                 if (t >= NTILE) break;
                 int I = 0, J = 0;
                 tile_of(t, &I, &J);
@@ -1568,7 +1576,7 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                     Xs[i * TRS + j] = i > j ? -m[tt][rr] : 0.f;
                 }
             }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kWaves) {
+            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
                 int Iu = 0, rem = t;
                 while (rem >= kNB - 1 - Iu) {
                     rem -= kNB - 1 - Iu;
@@ -1584,17 +1592,17 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
         // row sums sum_j M_ij H_ij and sum_j Z_ij, column sums sum_i Z_ij (Z = M o D H; H
         // already carries Gamma)
         {
-            const int i = tid >> 2, seg = tid & 3;
+            const int i = tid >> 3, seg = tid & 7;  // row i, columns 8 seg .. 8 seg + 7
             const float bi = bs[i];
             double gi = 0.0;
             if constexpr (GT) gi = GR::G(Kraw, i);
             float rowMH = 0.f, rowZ = 0.f, colZ = 0.f;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
+            for (int c4 = 0; c4 < 2; ++c4) {
                 f32x4 sv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int j = 16 * seg + 4 * c4 + e;
+                    const int j = 8 * seg + 4 * c4 + e;
                     float rij = 0.f, rji = 0.f;
                     if (j < i) {
                         const float mij = Xs[i * TRS + j];
@@ -1615,11 +1623,11 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                     }
                     sv[e] = rij + rji;
                 }
-                *reinterpret_cast<u32x4*>(Ts + i * TRS + 16 * seg + 4 * c4) = pack_hilo(sv);
+                *reinterpret_cast<u32x4*>(Ts + i * TRS + 8 * seg + 4 * c4) = pack_hilo(sv);
             }
-            // reduce over the four threads of row i (consecutive lanes), in a fixed order
+            // reduce over the eight threads of row i (consecutive lanes), in a fixed order
 #pragma unroll
-            for (int d = 1; d < 4; d <<= 1) {
+            for (int d = 1; d < 8; d <<= 1) {
                 rowMH += __shfl_xor(rowMH, d);
                 rowZ += __shfl_xor(rowZ, d);
                 colZ += __shfl_xor(colZ, d);
@@ -1634,9 +1642,9 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
         // ---- T^T dW and T^T dU (bf16 MFMA, T^T hi / lo): dK += D E T^T dW, dV = D T^T dU, and
         // the per-row sums for dbeta and dG
         {
-            f32x4 acc[2][kNB];
+            f32x4 acc[kCW][kNB];
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < kCW; ++c)
 #pragma unroll
                 for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
             tr_products<true>(dWraw, TT, wave, lr, lg, acc);
@@ -1650,8 +1658,8 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                 const float ei = GT ? GR::E(Kraw, i) : 1.f;
                 float sk = 0.f;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * (wave + 4 * c) + 4 * lg);
+                for (int c = 0; c < kCW; ++c) {
+                    const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * (wave + kBW * c) + 4 * lg);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         sk += acc[c][mi][rr] * static_cast<float>(kv[rr]);
@@ -1660,10 +1668,10 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                 }
                 sk += __shfl_xor(sk, 16);
                 sk += __shfl_xor(sk, 32);
-                if (lg == 0) part[(wave * 3 + 0) * kC + i] = sk;
+                if (lg == 0) part[(wave * 2 + 0) * kC + i] = sk;
             }
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < kCW; ++c)
 #pragma unroll
                 for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
             tr_products<true>(dUraw, TT, wave, lr, lg, acc);
@@ -1673,8 +1681,8 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                 const float bi = bs[i];
                 float sv = 0.f;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const bf16x4 vv = *reinterpret_cast<const bf16x4*>(Vb + i * KROW + 16 * (wave + 4 * c) + 4 * lg);
+                for (int c = 0; c < kCW; ++c) {
+                    const bf16x4 vv = *reinterpret_cast<const bf16x4*>(Vb + i * KROW + 16 * (wave + kBW * c) + 4 * lg);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         sv += acc[c][mi][rr] * static_cast<float>(vv[rr]);
@@ -1683,7 +1691,7 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
                 }
                 sv += __shfl_xor(sv, 16);
                 sv += __shfl_xor(sv, 32);
-                if (lg == 0) part[(wave * 3 + 1) * kC + i] = sv;
+                if (lg == 0) part[(wave * 2 + 1) * kC + i] = sv;
             }
             __syncthreads();  // every read of dU (and V) done: dV is staged over dU
             stage_store(dUraw, acc, p.dv, tok0, n, p.hv, hv, wave, lr, lg, tid);
@@ -1697,9 +1705,9 @@ __global__ __launch_bounds__(kThreads) void wy_backward_kernel(Params p)
             const int i = tid;
             float sk = 0.f, sv = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                sk += part[(w * 3 + 0) * kC + i];
-                sv += part[(w * 3 + 1) * kC + i];
+            for (int w = 0; w < kBW; ++w) {
+                sk += part[(w * 2 + 0) * kC + i];
+                sv += part[(w * 2 + 1) * kC + i];
             }
             const float ei = GT ? GR::E(Kraw, i) : 1.f;
             const float db = sk * ei + sv + red[i];
@@ -1757,7 +1765,7 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.hq = a.num_qk_heads;
         p.hv = a.num_v_heads;
         p.num_seqs = a.num_seqs;
-        hipLaunchKernelGGL(wy_backward_kernel<GT>, dim3(static_cast<uint32_t>(p.units)), dim3(kThreads),
+        hipLaunchKernelGGL(wy_backward_kernel<GT>, dim3(static_cast<uint32_t>(p.units)), dim3(kBT),
                            LDS_TOTAL, stream, p);
         e = hipGetLastError();
     }
