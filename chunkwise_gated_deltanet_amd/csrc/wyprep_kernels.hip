@@ -1336,6 +1336,48 @@ __device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][k
     }
 }
 
+// A = I + strictLower(D H) into Ts exactly as the forward's form_a writes it (diagonal tiles
+// keep L^T in their upper triangle for the substitution), and H = Gamma o K K^T (strict lower,
+// zeros elsewhere) into Hs, from one Gram per lower tile, over the eight waves.
+template <bool GT>
+__device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const float* bs, int wave, int lr,
+                         int lg)
+{
+    constexpr int NTILE = kNB * (kNB + 1) / 2;
+    for (int t = wave; t < NTILE; t += kBW) {  // uniform
+        int I = 0, J = 0;
+        tile_of(t, &I, &J);
+        GramFrags<0, KROW> f;
+        f.load(Kraw, I, J, lr, lg);
+        const f32x4 acc = f.product();
+        const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
+        const float bcol = bs[16 * J + lr];
+        double gcol = 0.0;
+        if constexpr (GT) gcol = GR::G(Kraw, 16 * J + lr);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
+            float a = acc[rr];
+            if constexpr (GT) {
+                const double d = GR::G(Kraw, i) - gcol;
+                a *= __expf(static_cast<float>(i > j ? d : -d));
+            }
+            Ts[i * TRS + j] = (i > j) ? bet[rr] * a : (i == j ? 1.f : bcol * a);
+            Hs[i * TRS + j] = i > j ? a : 0.f;
+        }
+    }
+    for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {  // strict upper tiles
+        int Iu = 0, rem = t;
+        while (rem >= kNB - 1 - Iu) {
+            rem -= kNB - 1 - Iu;
+            ++Iu;
+        }
+        const int Ju = Iu + 1 + rem;
+        *reinterpret_cast<f32x4*>(Ts + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
+        *reinterpret_cast<f32x4*>(Hs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
+    }
+}
+
 template <bool GT>
 __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
 {
@@ -1412,37 +1454,8 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         }
         __syncthreads();
 
-        // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs): the forward's form_a
-        // with H kept
-        if (tid < kThreads) form_a<kC, 0, KROW, TL, GT>(Kraw, Ts, bs, tid);  // its four-wave map
-        {
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            for (int t = wave; t < NTILE; t += kBW) {  // uniform
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-                GramFrags<0, KROW> f;
-                f.load(Kraw, I, J, lr, lg);
-                const f32x4 acc = f.product();
-                double gcol = 0.0;
-                if constexpr (GT) gcol = GR::G(Kraw, 16 * J + lr);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
-                    float h = acc[rr];
-                    if constexpr (GT) h *= __expf(static_cast<float>(GR::G(Kraw, i) - gcol));
-                    Hs[i * TRS + j] = i > j ? h : 0.f;
-                }
-            }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {  // strict upper tiles
-                int Iu = 0, rem = t;
-                while (rem >= kNB - 1 - Iu) {
-                    rem -= kNB - 1 - Iu;
-                    ++Iu;
-                }
-                const int Ju = Iu + 1 + rem;
-                *reinterpret_cast<f32x4*>(Hs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-            }
-        }
+        // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs)
+        form_a_h<GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
         __syncthreads();
         invert_diagonal_blocks<kC, TL>(Ts, tid);
         __syncthreads();
