@@ -30,8 +30,13 @@ METRIC = "chunks/s (tokens/s) for kkt_solve+W/U at C=64; achieved HBM GB/s vs pe
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 768 << 20  # rotated footprint: three times the Infinity Cache
 CSRC = os.path.join(ROOT, "chunkwise_gated_deltanet_amd", "csrc")
-KERNEL_SOURCE = os.path.join(CSRC, "wyprep_kernels.hip")
-FWD_SOURCE = os.path.join(CSRC, "chunk_fwd.hip")
+# Kernel sources behind each entry point; a committed counter summary is used only while the
+# hash of these files matches the one it was taken on.
+KERNEL_SOURCES = {
+    "wy": ("wyprep_device.h", "wyprep_kernels.hip"),
+    "fwd": ("chunk_fwd.hip",),
+    "bwd": ("wyprep_device.h", "wy_backward.hip"),
+}
 ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve", "fwd": "chunk_fwd",
                "gdn": "gdn_forward", "bwd": "wy_backward"}
 
@@ -63,8 +68,12 @@ def bwd_bytes(tokens, hq, hv, dk, dv, esz, gated=False):
 
 
 def kernel_source_sha(entry="wy"):
-    with open(FWD_SOURCE if entry == "fwd" else KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the kernel sources of an entry point (wu, kkt, gdn: those of wy), in order."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(entry, KERNEL_SOURCES["wy"]):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def profile_name(entry, w, batch, seqlen, num_seqs):

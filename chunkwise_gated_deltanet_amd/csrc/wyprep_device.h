@@ -1,0 +1,349 @@
+// Device-side pieces shared by the WY/UT preparation kernel (wyprep_kernels.hip) and its
+// backward (wy_backward.hip): vector types, buffer resources, the unit map (a0), the gate
+// values parked in staged K rows, the placement of the C x C tile, the Gram fragments, and
+// the block inversion of a unit lower-triangular tile (a5: 16x16 substitutions; a6:
+// coupling levels).  Step labels a0..a8 are those of wyprep_kernels.hip.
+//
+// Pages cited (by title and section):
+//   [Inv] "TileLang 实战：单位下三角矩阵求逆" (TileLang in practice: inverting a unit
+//         lower-triangular matrix).
+//   [QLA] The FlashQLA announcement, section "使用方式" (usage).
+//
+// MFMA operand convention: for a 16x16 output tile, lane l = 16*g + c holds row/column c and
+// k-group g.  In __builtin_amdgcn_mfma_f32_16x16x4f32 sub-step q the lane supplies true
+// k = 16*kt + 4*g + q; in __builtin_amdgcn_mfma_f32_16x16x32_bf16 element j supplies true
+// k = 32*kt + 8*g + j.  A and B use the same map, so the contraction is exact in any hardware
+// k order.  Accumulator element r of lane 16*g + c is D[4*g + r][c]; with the k map above that
+// is exactly the B operand a following 16x16x4 product needs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+namespace wyp {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int kD = 128;        // head dim of k and v
+constexpr int kThreads = 256;  // four wave64s
+constexpr int kWaves = kThreads / 64;
+constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bounds checked
+// Cache policy of the streaming loads and stores: nt (non-temporal).  V, beta, T, W and U
+// are touched once per launch, so keeping their lines in L2 / MALL only evicts useful ones
+// (B=1 T=8192 H=16 C=64: 41 us per launch with the default policy, 33 us with nt).  K keeps
+// the default policy: with grouped value heads every key row is read once per value head of
+// its group, by units running side by side on one XCD, and those re-reads hit in L2 (8
+// packed sequences, Hq=16 Hv=64 C=64: 1.32 ms with nt K loads, 1.11 ms without).
+constexpr int kStream = 2;
+
+struct Params {
+    const void* k;
+    const void* v;
+    const float* beta;
+    const float* g;  // log gates, gated instances only
+    const int32_t* cu;
+    float* T;
+    void* W;
+    void* U;
+    int64_t units;
+    int32_t seqlen;
+    int32_t hq;
+    int32_t hv;
+    int32_t num_seqs;
+};
+
+// Placement of the fp32 C x C tile (A, then T, then T') in LDS; off(r, c) is the float offset
+// of entry (r, c).  Up to C = 64 it is row-major with rows padded by 4 floats.  At C = 128 only
+// the 36 lower 16x16 tiles (diagonal ones included) are kept, tile (I, J) at position
+// I(I+1)/2 + J, each 16 rows of 20 floats: 46 KB instead of 68 KB, so two workgroups share a
+// CU.  Every access below stays inside one 16x16 tile, and with either padding the rows of a
+// 16-lane group start on different banks.
+template <int C, bool TILED = (C > 64)>
+struct TLayout {
+    static constexpr bool kTiled = false;
+    static constexpr int RS = C + 4;  // floats per row
+    static constexpr int BYTES = C * RS * 4;
+    __device__ static constexpr int off(int r, int c) { return r * RS + c; }
+};
+
+template <int C>
+struct TLayout<C, true> {
+    static constexpr bool kTiled = true;
+    static constexpr int RS = 20;  // floats per tile row
+    static constexpr int TILE = 16 * RS;
+    static constexpr int NB = C / 16;
+    static constexpr int BYTES = NB * (NB + 1) / 2 * TILE * 4;
+    __device__ static constexpr int off(int r, int c)
+    {
+        return ((r >> 4) * ((r >> 4) + 1) / 2 + (c >> 4)) * TILE + (r & 15) * RS + (c & 15);
+    }
+};
+
+__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Gate values of token row r of the unit, in the padding after the 128 elements of staged K
+// row r: G_r (chunk-local inclusive prefix sum of the log gates, fp64) and exp(G_r) (fp32).
+template <int KROW, int ESZ>
+struct GateRow {
+    __device__ static double* Gp(unsigned char* Kraw, int r)
+    {
+        return reinterpret_cast<double*>(Kraw + r * (KROW * ESZ) + kD * ESZ);
+    }
+    __device__ static float* Ep(unsigned char* Kraw, int r)
+    {
+        return reinterpret_cast<float*>(Kraw + r * (KROW * ESZ) + kD * ESZ + 8);
+    }
+    __device__ static double G(const unsigned char* Kraw, int r)
+    {
+        return *reinterpret_cast<const double*>(Kraw + r * (KROW * ESZ) + kD * ESZ);
+    }
+    __device__ static float E(const unsigned char* Kraw, int r)
+    {
+        return *reinterpret_cast<const float*>(Kraw + r * (KROW * ESZ) + kD * ESZ + 8);
+    }
+};
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferConfig);
+}
+
+struct Unit {
+    int64_t tok0;  // first token (flattened b*T + t)
+    int n;         // tokens in the chunk (1..C); 0 = no unit
+    int hv;        // value head
+};
+
+// a0: logical unit index -> Unit (n == 0 past the end).  Packed batches: wave 0 scans
+// cu_seqlens 64 sequences at a time; the result goes through LDS (one barrier).
+template <int C>
+__device__ Unit map_unit(const Params& p, int* info, int64_t logical64, int tid)
+{
+    Unit u{0, 0, 0};
+    if (logical64 >= p.units) return u;
+    // units < 2^31 (checked on the host), so 32-bit arithmetic suffices here
+    const uint32_t logical = static_cast<uint32_t>(logical64);
+    const uint32_t hvn = static_cast<uint32_t>(p.hv);
+    u.hv = static_cast<int>(logical % hvn);
+    const uint32_t slot = logical / hvn;
+    if (p.cu == nullptr) {
+        const uint32_t cps = static_cast<uint32_t>((p.seqlen + C - 1) / C);
+        const uint32_t b = slot / cps, c = slot % cps;
+        u.tok0 = static_cast<int64_t>(b) * p.seqlen + static_cast<int64_t>(c) * C;
+        u.n = min(C, p.seqlen - static_cast<int>(c) * C);
+        return u;
+    }
+    const int lane = tid & 63;
+    if (tid < 64) {
+        int64_t run = 0;
+        int found_s = -1, found_c = 0;
+        for (int base = 0; base < p.num_seqs; base += 64) {
+            const int s = base + lane;
+            int cnt = 0;
+            if (s < p.num_seqs) cnt = (p.cu[s + 1] - p.cu[s] + C - 1) / C;
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(incl, d);
+                if (lane >= d) incl += t;
+            }
+            const int excl = incl - cnt;
+            const bool hit = cnt > 0 && static_cast<int64_t>(slot) >= run + excl &&
+                             static_cast<int64_t>(slot) < run + incl;
+            const unsigned long long m = __ballot(hit);
+            if (m) {
+                const int src = __ffsll(m) - 1;
+                found_s = __shfl(s, src);
+                found_c = static_cast<int>(static_cast<int64_t>(slot) - run - __shfl(excl, src));
+                break;
+            }
+            run += __shfl(incl, 63);
+        }
+        if (lane == 0) {
+            info[0] = found_s;
+            info[1] = found_c;
+        }
+    }
+    __syncthreads();
+    const int s = uniform(info[0]);
+    const int c = uniform(info[1]);
+    if (s < 0) return u;
+    const int s0 = uniform(p.cu[s]), s1 = uniform(p.cu[s + 1]);
+    u.tok0 = s0 + static_cast<int64_t>(c) * C;
+    u.n = min(C, s1 - static_cast<int>(u.tok0));
+    return u;
+}
+
+// Lower 16x16 tile t (row-major over I >= J) -> (I, J).
+__device__ inline void tile_of(int t, int* I, int* J)
+{
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    *I = i;
+    *J = t - i * (i + 1) / 2;
+}
+
+template <int DT, int KROW>
+struct GramFrags {
+    static constexpr int NS = DT == 0 ? kD / 32 : kD / 16;
+    typedef typename std::conditional<DT == 0, bf16x8, f32x4>::type frag;
+    frag a[NS], b[NS];
+
+    __device__ void load(const unsigned char* Kraw, int I, int J, int lr, int lg)
+    {
+        if constexpr (DT == 0) {
+            const __bf16* K = reinterpret_cast<const __bf16*>(Kraw);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                a[s] = *reinterpret_cast<const bf16x8*>(K + (16 * I + lr) * KROW + 32 * s + 8 * lg);
+                b[s] = *reinterpret_cast<const bf16x8*>(K + (16 * J + lr) * KROW + 32 * s + 8 * lg);
+            }
+        } else {
+            const float* K = reinterpret_cast<const float*>(Kraw);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                a[s] = *reinterpret_cast<const f32x4*>(K + (16 * I + lr) * KROW + 16 * s + 4 * lg);
+                b[s] = *reinterpret_cast<const f32x4*>(K + (16 * J + lr) * KROW + 16 * s + 4 * lg);
+            }
+        }
+    }
+
+    __device__ f32x4 product() const
+    {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if constexpr (DT == 0) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][q], b[s][q], acc, 0, 0, 0);
+            }
+        }
+        return acc;
+    }
+};
+
+// Step J of the right-looking substitution for lane (block, column i): X[J][i] is final
+// (1 for J = i, else -acc[J]; acc holds the negated partial sums, exactly +0 above i), it is
+// written back, and every later row k takes acc[k] -= L[k][J] X[J][i].  L[k][J] for k > J is
+// read from row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the
+// block read the same row (an LDS broadcast).  Row J's upper part is read before any lane
+// overwrites it with its X column.
+template <int J, int RS>
+__device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
+{
+    const float x = (J == i) ? 1.f : acc[J];
+    float lrow[16];
+    if constexpr (J < 15) {
+#pragma unroll
+        for (int c4 = (J + 1) / 4; c4 < 4; ++c4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + J * RS + 4 * c4);
+            lrow[4 * c4 + 0] = v[0];
+            lrow[4 * c4 + 1] = v[1];
+            lrow[4 * c4 + 2] = v[2];
+            lrow[4 * c4 + 3] = v[3];
+        }
+    }
+    blk[J * RS + i] = x;
+    if constexpr (J < 15) {
+#pragma unroll
+        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-lrow[k], x, acc[k]);
+        substitution_step<J + 1, RS>(acc, i, blk);
+    }
+}
+
+// a5: invert the C/16 diagonal 16x16 blocks of Ts in place.  Lane (block b, column i) keeps
+// column i of X_b = L_b^{-1} in registers, right-looking: after X[j][i] is final, every later
+// row k takes its share L[k][j] X[j][i], so one multiply-add per step sits on the dependency
+// chain.  Blocks 0-3 run on wave 0, blocks 4-7 on wave 1.
+template <int C, class TL>
+__device__ void invert_diagonal_blocks(float* Ts, int tid)
+{
+    constexpr int NB = C / 16;
+    if (tid >= NB * 16) return;
+    const int b = tid >> 4, i = tid & 15;
+    float* blk = Ts + TL::off(16 * b, 16 * b);
+    float acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+    substitution_step<0, TL::RS>(acc, i, blk);
+}
+
+// a6, one level: block size S.  Pair p covers rows/cols [2Sp, 2Sp + 2S); its sub-diagonal
+// block L10 (rows 2Sp+S.., cols 2Sp..) is replaced by X10 = -X11 (L10 X00).  Wave w owns pair
+// w / (S/16) and 16-column tile w % (S/16) of X10.
+template <int C, int S, class TL>
+__device__ void coupling_level(float* Ts, int tid)
+{
+    constexpr int TS = S / 16;
+    constexpr int NPAIR = C / (2 * S);
+    constexpr int NTASK = NPAIR * TS;
+    static_assert(NTASK <= kWaves, "one coupling task per wave");
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const bool active = wave < NTASK;
+    const int pr = wave / TS, nc = wave % TS;
+    const int base = 2 * S * pr;
+    f32x4 res[TS];
+    if (active) {
+        // tmp[:, nc] = L10 X00[:, nc].  X00 is lower triangular, so k-tiles kt < nc hold
+        // zeros.  The row-major layout multiplies them anyway, which keeps every operand load
+        // branch-free; the tile-packed layout does not store them and skips them.
+        f32x4 tmp[TS];
+#pragma unroll
+        for (int mr = 0; mr < TS; ++mr) tmp[mr] = zero4();
+#pragma unroll
+        for (int kt = 0; kt < TS; ++kt) {
+            if (TL::kTiled && kt < nc) continue;  // uniform per wave
+            float bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bq[q] = Ts[TL::off(base + 16 * kt + 4 * lg + q, base + 16 * nc + lr)];
+#pragma unroll
+            for (int mr = 0; mr < TS; ++mr) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(
+                    Ts + TL::off(base + S + 16 * mr + lr, base + 16 * kt + 4 * lg));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    tmp[mr] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], bq[q], tmp[mr], 0, 0, 0);
+            }
+        }
+        // X10[:, nc] = -X11 tmp[:, nc]; X11 is lower triangular, so kt <= mr.
+#pragma unroll
+        for (int mr = 0; mr < TS; ++mr) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kt = 0; kt <= mr; ++kt) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(
+                    Ts + TL::off(base + S + 16 * mr + lr, base + S + 16 * kt + 4 * lg));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], tmp[kt][q], acc, 0, 0, 0);
+            }
+            res[mr] = -acc;
+        }
+    }
+    __syncthreads();  // every wave has read L10 before any X10 overwrites it
+    if (active) {
+#pragma unroll
+        for (int mr = 0; mr < TS; ++mr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Ts[TL::off(base + S + 16 * mr + 4 * lg + r, base + 16 * nc + lr)] = res[mr][r];
+    }
+    __syncthreads();
+}
+
+}  // namespace
+}  // namespace wyp

@@ -44,7 +44,8 @@
 // k = 16*kt + 4*g + q; in __builtin_amdgcn_mfma_f32_16x16x32_bf16 element j supplies true
 // k = 32*kt + 8*g + j.  A and B use the same map, so the contraction is exact in any hardware
 // k order.  Accumulator element r of lane 16*g + c is D[4*g + r][c]; with the k map above that
-// is exactly the B operand a following 16x16x4 product needs.
+// is exactly the B operand a following 16x16x4 product needs.  The helpers shared with the
+// backward (a0, a5, a6, the T-tile layout, Gram fragments) live in wyprep_device.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -52,28 +53,11 @@
 #include <mutex>
 #include <type_traits>
 
+#include "wyprep_device.h"
 #include "wyprep_launch.h"
 
 namespace wyp {
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-constexpr int kD = 128;        // head dim of k and v
-constexpr int kThreads = 256;  // four wave64s
-constexpr int kWaves = kThreads / 64;
-constexpr int kBufferConfig = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, bounds checked
-// Cache policy of the streaming loads and stores: nt (non-temporal).  V, beta, T, W and U
-// are touched once per launch, so keeping their lines in L2 / MALL only evicts useful ones
-// (B=1 T=8192 H=16 C=64: 41 us per launch with the default policy, 33 us with nt).  K keeps
-// the default policy: with grouped value heads every key row is read once per value head of
-// its group, by units running side by side on one XCD, and those re-reads hit in L2 (8
-// packed sequences, Hq=16 Hv=64 C=64: 1.32 ms with nt K loads, 1.11 ms without).
-constexpr int kStream = 2;
 
 // What one launch writes: T (kkt_solve, wy_prepare), W and U (wy_prepare, wu_prepare); and
 // whether it reads log gates g.
@@ -81,54 +65,11 @@ constexpr int kModeT = 1;
 constexpr int kModeWU = 2;
 constexpr int kModeGate = 4;
 
-struct Params {
-    const void* k;
-    const void* v;
-    const float* beta;
-    const float* g;  // log gates, gated instances only
-    const int32_t* cu;
-    float* T;
-    void* W;
-    void* U;
-    int64_t units;
-    int32_t seqlen;
-    int32_t hq;
-    int32_t hv;
-    int32_t num_seqs;
-};
-
 // LDS plan of one workgroup.  K and V rows carry 16 bytes of padding and T rows 4 floats, so
 // 16-byte reads of one column chunk by 16 consecutive rows spread over all banks.  V never
 // has its own region: it waits in registers until the T tile has been read for the last time
 // and then takes its place, so one unit needs K + max(T, V) bytes (34 KiB at C = 64: four
-// workgroups per CU).
-// Placement of the fp32 C x C tile (A, then T, then T') in LDS; off(r, c) is the float offset
-// of entry (r, c).  Up to C = 64 it is row-major with rows padded by 4 floats.  At C = 128 only
-// the 36 lower 16x16 tiles (diagonal ones included) are kept, tile (I, J) at position
-// I(I+1)/2 + J, each 16 rows of 20 floats: 46 KB instead of 68 KB, so two workgroups share a
-// CU.  Every access below stays inside one 16x16 tile, and with either padding the rows of a
-// 16-lane group start on different banks.
-template <int C, bool TILED = (C > 64)>
-struct TLayout {
-    static constexpr bool kTiled = false;
-    static constexpr int RS = C + 4;  // floats per row
-    static constexpr int BYTES = C * RS * 4;
-    __device__ static constexpr int off(int r, int c) { return r * RS + c; }
-};
-
-template <int C>
-struct TLayout<C, true> {
-    static constexpr bool kTiled = true;
-    static constexpr int RS = 20;  // floats per tile row
-    static constexpr int TILE = 16 * RS;
-    static constexpr int NB = C / 16;
-    static constexpr int BYTES = NB * (NB + 1) / 2 * TILE * 4;
-    __device__ static constexpr int off(int r, int c)
-    {
-        return ((r >> 4) * ((r >> 4) + 1) / 2 + (c >> 4)) * TILE + (r & 15) * RS + (c & 15);
-    }
-};
-
+// workgroups per CU).  The T tile's placement is TLayout (wyprep_device.h).
 template <int C, int DT, bool WU>
 struct Lds {
     static constexpr int ESZ = DT == 0 ? 2 : 4;
@@ -154,103 +95,6 @@ struct WavesPerEu {
     static constexpr int by_lds = (160 * 1024) / Lds<C, DT, WU>::TOTAL;
     static constexpr int value = by_lds < 1 ? 1 : (by_lds > 4 ? 4 : by_lds);
 };
-
-__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Gate values of token row r of the unit, in the padding after the 128 elements of staged K
-// row r: G_r (chunk-local inclusive prefix sum of the log gates, fp64) and exp(G_r) (fp32).
-template <int KROW, int ESZ>
-struct GateRow {
-    __device__ static double* Gp(unsigned char* Kraw, int r)
-    {
-        return reinterpret_cast<double*>(Kraw + r * (KROW * ESZ) + kD * ESZ);
-    }
-    __device__ static float* Ep(unsigned char* Kraw, int r)
-    {
-        return reinterpret_cast<float*>(Kraw + r * (KROW * ESZ) + kD * ESZ + 8);
-    }
-    __device__ static double G(const unsigned char* Kraw, int r)
-    {
-        return *reinterpret_cast<const double*>(Kraw + r * (KROW * ESZ) + kD * ESZ);
-    }
-    __device__ static float E(const unsigned char* Kraw, int r)
-    {
-        return *reinterpret_cast<const float*>(Kraw + r * (KROW * ESZ) + kD * ESZ + 8);
-    }
-};
-
-__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferConfig);
-}
-
-struct Unit {
-    int64_t tok0;  // first token (flattened b*T + t)
-    int n;         // tokens in the chunk (1..C); 0 = no unit
-    int hv;        // value head
-};
-
-// a0: logical unit index -> Unit (n == 0 past the end).  Packed batches: wave 0 scans
-// cu_seqlens 64 sequences at a time; the result goes through LDS (one barrier).
-template <int C>
-__device__ Unit map_unit(const Params& p, int* info, int64_t logical64, int tid)
-{
-    Unit u{0, 0, 0};
-    if (logical64 >= p.units) return u;
-    // units < 2^31 (checked on the host), so 32-bit arithmetic suffices here
-    const uint32_t logical = static_cast<uint32_t>(logical64);
-    const uint32_t hvn = static_cast<uint32_t>(p.hv);
-    u.hv = static_cast<int>(logical % hvn);
-    const uint32_t slot = logical / hvn;
-    if (p.cu == nullptr) {
-        const uint32_t cps = static_cast<uint32_t>((p.seqlen + C - 1) / C);
-        const uint32_t b = slot / cps, c = slot % cps;
-        u.tok0 = static_cast<int64_t>(b) * p.seqlen + static_cast<int64_t>(c) * C;
-        u.n = min(C, p.seqlen - static_cast<int>(c) * C);
-        return u;
-    }
-    const int lane = tid & 63;
-    if (tid < 64) {
-        int64_t run = 0;
-        int found_s = -1, found_c = 0;
-        for (int base = 0; base < p.num_seqs; base += 64) {
-            const int s = base + lane;
-            int cnt = 0;
-            if (s < p.num_seqs) cnt = (p.cu[s + 1] - p.cu[s] + C - 1) / C;
-            int incl = cnt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int t = __shfl_up(incl, d);
-                if (lane >= d) incl += t;
-            }
-            const int excl = incl - cnt;
-            const bool hit = cnt > 0 && static_cast<int64_t>(slot) >= run + excl &&
-                             static_cast<int64_t>(slot) < run + incl;
-            const unsigned long long m = __ballot(hit);
-            if (m) {
-                const int src = __ffsll(m) - 1;
-                found_s = __shfl(s, src);
-                found_c = static_cast<int>(static_cast<int64_t>(slot) - run - __shfl(excl, src));
-                break;
-            }
-            run += __shfl(incl, 63);
-        }
-        if (lane == 0) {
-            info[0] = found_s;
-            info[1] = found_c;
-        }
-    }
-    __syncthreads();
-    const int s = uniform(info[0]);
-    const int c = uniform(info[1]);
-    if (s < 0) return u;
-    const int s0 = uniform(p.cu[s]), s1 = uniform(p.cu[s + 1]);
-    u.tok0 = s0 + static_cast<int64_t>(c) * C;
-    u.n = min(C, s1 - static_cast<int>(u.tok0));
-    return u;
-}
 
 // a1: K, V and beta of one unit in flight to registers, then committed to LDS.  K and beta
 // are committed at the start of their unit; V only after that unit's T tile has been used.
@@ -360,56 +204,6 @@ struct Prefetch {
 // a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts; all C x C entries are written.
 // Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4; upper tiles are zeroed with one
 // 16-byte write per lane.
-__device__ inline void tile_of(int t, int* I, int* J)
-{
-    int i = 0;
-    while ((i + 1) * (i + 2) / 2 <= t) ++i;
-    *I = i;
-    *J = t - i * (i + 1) / 2;
-}
-
-template <int DT, int KROW>
-struct GramFrags {
-    static constexpr int NS = DT == 0 ? kD / 32 : kD / 16;
-    typedef typename std::conditional<DT == 0, bf16x8, f32x4>::type frag;
-    frag a[NS], b[NS];
-
-    __device__ void load(const unsigned char* Kraw, int I, int J, int lr, int lg)
-    {
-        if constexpr (DT == 0) {
-            const __bf16* K = reinterpret_cast<const __bf16*>(Kraw);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                a[s] = *reinterpret_cast<const bf16x8*>(K + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                b[s] = *reinterpret_cast<const bf16x8*>(K + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-            }
-        } else {
-            const float* K = reinterpret_cast<const float*>(Kraw);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                a[s] = *reinterpret_cast<const f32x4*>(K + (16 * I + lr) * KROW + 16 * s + 4 * lg);
-                b[s] = *reinterpret_cast<const f32x4*>(K + (16 * J + lr) * KROW + 16 * s + 4 * lg);
-            }
-        }
-    }
-
-    __device__ f32x4 product() const
-    {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if constexpr (DT == 0) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][q], b[s][q], acc, 0, 0, 0);
-            }
-        }
-        return acc;
-    }
-};
-
 template <int C, int DT, int KROW, class TL, bool GT>
 __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
@@ -482,117 +276,6 @@ __device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, in
             *reinterpret_cast<f32x4*>(Ts + TL::off(16 * Iu + lr, 16 * Ju + 4 * lg)) = zero4();
         }
     }
-}
-
-// Step J of the right-looking substitution for lane (block, column i): X[J][i] is final
-// (1 for J = i, else -acc[J]; acc holds the negated partial sums, exactly +0 above i), it is
-// written back, and every later row k takes acc[k] -= L[k][J] X[J][i].  L[k][J] for k > J is
-// read from row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the
-// block read the same row (an LDS broadcast).  Row J's upper part is read before any lane
-// overwrites it with its X column.
-template <int J, int RS>
-__device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
-{
-    const float x = (J == i) ? 1.f : acc[J];
-    float lrow[16];
-    if constexpr (J < 15) {
-#pragma unroll
-        for (int c4 = (J + 1) / 4; c4 < 4; ++c4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + J * RS + 4 * c4);
-            lrow[4 * c4 + 0] = v[0];
-            lrow[4 * c4 + 1] = v[1];
-            lrow[4 * c4 + 2] = v[2];
-            lrow[4 * c4 + 3] = v[3];
-        }
-    }
-    blk[J * RS + i] = x;
-    if constexpr (J < 15) {
-#pragma unroll
-        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-lrow[k], x, acc[k]);
-        substitution_step<J + 1, RS>(acc, i, blk);
-    }
-}
-
-// a5: invert the C/16 diagonal 16x16 blocks of Ts in place.  Lane (block b, column i) keeps
-// column i of X_b = L_b^{-1} in registers, right-looking: after X[j][i] is final, every later
-// row k takes its share L[k][j] X[j][i], so one multiply-add per step sits on the dependency
-// chain.  Blocks 0-3 run on wave 0, blocks 4-7 on wave 1.
-template <int C, class TL>
-__device__ void invert_diagonal_blocks(float* Ts, int tid)
-{
-    constexpr int NB = C / 16;
-    if (tid >= NB * 16) return;
-    const int b = tid >> 4, i = tid & 15;
-    float* blk = Ts + TL::off(16 * b, 16 * b);
-    float acc[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.f;
-    substitution_step<0, TL::RS>(acc, i, blk);
-}
-
-// a6, one level: block size S.  Pair p covers rows/cols [2Sp, 2Sp + 2S); its sub-diagonal
-// block L10 (rows 2Sp+S.., cols 2Sp..) is replaced by X10 = -X11 (L10 X00).  Wave w owns pair
-// w / (S/16) and 16-column tile w % (S/16) of X10.
-template <int C, int S, class TL>
-__device__ void coupling_level(float* Ts, int tid)
-{
-    constexpr int TS = S / 16;
-    constexpr int NPAIR = C / (2 * S);
-    constexpr int NTASK = NPAIR * TS;
-    static_assert(NTASK <= kWaves, "one coupling task per wave");
-    const int lane = tid & 63, wave = uniform(tid >> 6);
-    const int lr = lane & 15, lg = lane >> 4;
-    const bool active = wave < NTASK;
-    const int pr = wave / TS, nc = wave % TS;
-    const int base = 2 * S * pr;
-    f32x4 res[TS];
-    if (active) {
-        // tmp[:, nc] = L10 X00[:, nc].  X00 is lower triangular, so k-tiles kt < nc hold
-        // zeros.  The row-major layout multiplies them anyway, which keeps every operand load
-        // branch-free; the tile-packed layout does not store them and skips them.
-        f32x4 tmp[TS];
-#pragma unroll
-        for (int mr = 0; mr < TS; ++mr) tmp[mr] = zero4();
-#pragma unroll
-        for (int kt = 0; kt < TS; ++kt) {
-            if (TL::kTiled && kt < nc) continue;  // uniform per wave
-            float bq[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bq[q] = Ts[TL::off(base + 16 * kt + 4 * lg + q, base + 16 * nc + lr)];
-#pragma unroll
-            for (int mr = 0; mr < TS; ++mr) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(
-                    Ts + TL::off(base + S + 16 * mr + lr, base + 16 * kt + 4 * lg));
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    tmp[mr] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], bq[q], tmp[mr], 0, 0, 0);
-            }
-        }
-        // X10[:, nc] = -X11 tmp[:, nc]; X11 is lower triangular, so kt <= mr.
-#pragma unroll
-        for (int mr = 0; mr < TS; ++mr) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kt = 0; kt <= mr; ++kt) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(
-                    Ts + TL::off(base + S + 16 * mr + lr, base + S + 16 * kt + 4 * lg));
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], tmp[kt][q], acc, 0, 0, 0);
-            }
-            res[mr] = -acc;
-        }
-    }
-    __syncthreads();  // every wave has read L10 before any X10 overwrites it
-    if (active) {
-#pragma unroll
-        for (int mr = 0; mr < TS; ++mr)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Ts[TL::off(base + S + 16 * mr + 4 * lg + r, base + 16 * nc + lr)] = res[mr][r];
-    }
-    __syncthreads();
 }
 
 // a7: T rows [0, n) to T_out[(tok0 + r) * Hv + hv][0:C] (with STORE; wu_prepare forms T but
@@ -1149,664 +832,12 @@ int launch_g(const LaunchArgs& a, hipStream_t s, char* msg, int len)
     return a.g != nullptr ? launch_m<DT, kModeGate>(a, s, msg, len) : launch_m<DT, 0>(a, s, msg, len);
 }
 
-
-// ==========================================================================================
-// Backward of the preparation step (bf16 k / v, C = 64): the gradient of
-//     L = <dT, T> + <dW, W> + <dU, U>
-// with respect to k, v, beta and g.  Forward per chunk and value head (D = diag(beta),
-// E = diag(exp(G)), Gamma[i][j] = exp(G_i - G_j), H = Gamma o K K^T on the strict lower
-// triangle):  A = I + D H,  T = A^{-1},  W = T D E K,  U = T D V.  Reverse:
-//   X  = strictLower(dT + (dW K^T) D E + (dU V^T) D)     (only this part of dT_tot reaches A)
-//   Y  = X T^T,  M = strictLower(-T^T Y)                   (the derivative of the inverse)
-//   dK = D E (T^T dW) + (R + R^T) K,  R = D (Gamma o M)   (both key rows of each Gram entry)
-//   dV = D (T^T dU)
-//   dbeta_i = sum_d (T^T dW)_id e^{G_i} K_id + sum_d (T^T dU)_id V_id + sum_j M_ij H_ij
-//   dG_i = beta_i e^{G_i} sum_d (T^T dW)_id K_id + sum_j Z_ij - sum_j Z_ji,  Z = M o D H
-//   dg_t = sum_{i >= t} dG_i
-// One workgroup per (chunk, key head) handles the value heads of that key head in turn and
-// sums their dK in registers, so dk is written once, without atomics.  T is recomputed with
-// the forward's own steps (bit-identical to the T that wy_prepare returns).  T and R + R^T
-// enter the bf16 products as hi + lo pairs, so dbeta and dg keep fp32 accuracy.
-namespace bwd {
-
-constexpr int kC = 64;
-constexpr int kNB = kC / 16;
-// Eight waves per workgroup: LDS (140 KB) holds one workgroup per CU, and with one wave per SIMD
-// every LDS, MFMA and VALU latency of the unit's long serial chain would be exposed.  Phases
-// that tile over waves run twice as wide; the forward's Gram / substitution / coupling steps
-// keep their four-wave mapping.
-constexpr int kBT = 512;
-constexpr int kBW = kBT / 64;
-constexpr int kCW = kD / 16 / kBW;  // dk column tiles per wave in the transposed products
-constexpr int KROW = kD + 8;                 // bf16 per staged K / V / dW / dU row
-constexpr int TRS = kC + 4;                  // floats per n x n tile row
-constexpr int KB = kC * KROW * 2;            // 17408
-constexpr int TB = kC * TRS * 4;             // 17408
-constexpr int OFF_K = 0;
-constexpr int OFF_V = OFF_K + KB;
-constexpr int OFF_DW = OFF_V + KB;
-constexpr int OFF_DU = OFF_DW + KB;
-constexpr int OFF_T = OFF_DU + KB;           // A -> T (fp32) -> S = R + R^T (hi / lo)
-constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, strict lower (fp32)
-constexpr int OFF_X = OFF_H + TB;            // X -> Y^T -> M (fp32)
-constexpr int OFF_TT = OFF_X + TB;           // T^T as hi / lo chunks
-constexpr int OFF_B = OFF_TT + TB;           // beta (64 floats)
-constexpr int OFF_PART = OFF_B + kC * 4;     // per-wave row partials: kBW waves x 2 x 64 floats
-constexpr int OFF_RED = OFF_PART + kBW * 2 * kC * 4;  // dbeta, dG of this value head (2 x 64)
-constexpr int OFF_INFO = OFF_RED + 2 * kC * 4;
-constexpr int LDS_TOTAL = OFF_INFO + 16;
-static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
-
-using TL = TLayout<kC>;
-using GR = GateRow<KROW, 2>;
-
-struct Params {
-    const __bf16* k;
-    const __bf16* v;
-    const float* beta;
-    const float* g;
-    const int32_t* cu;
-    const float* dT;
-    const __bf16* dW;
-    const __bf16* dU;
-    __bf16* dk;
-    __bf16* dv;
-    float* dbeta;
-    float* dg;
-    int64_t units;    // chunk slots x Hq
-    int32_t seqlen;
-    int32_t hq;
-    int32_t hv;
-    int32_t num_seqs;
-};
-
-// Rows [0, n) of a [tokens, heads, 128] bf16 tensor in flight to registers (two 16-byte pieces
-// per thread; rows >= n read as 0 through the buffer range), then into LDS rows of KROW
-// elements.  All of a value head's rows are issued before any is waited for.
-struct Rows {
-    static constexpr int NIT = kC * 16 / kBT;
-    u32x4 x[NIT];
-
-    __device__ void issue(const __bf16* base, int64_t tok0, int n, int heads, int head, int tid)
-    {
-        const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
-        const __amdgpu_buffer_rsrc_t r = rsrc(base + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int q = tid + it * kBT;
-            x[it] = __builtin_amdgcn_raw_buffer_load_b128(r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
-        }
-    }
-
-    __device__ void commit(unsigned char* dst, int tid) const
-    {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int q = tid + it * kBT;
-            *reinterpret_cast<u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16) = x[it];
-        }
-    }
-};
-
-__device__ inline u32x4 pack_hilo(f32x4 x)
-{
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    bf16x4 h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        h[e] = static_cast<__bf16>(x[e]);
-        l[e] = static_cast<__bf16>(x[e] - static_cast<float>(h[e]));
-    }
-    const u32x2 hp = __builtin_bit_cast(u32x2, h), lp = __builtin_bit_cast(u32x2, l);
-    return u32x4{hp[0], hp[1], lp[0], lp[1]};
-}
-
-__device__ inline f32x4 unpack_hilo(u32x4 c)
-{
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const bf16x4 h = __builtin_bit_cast(bf16x4, u32x2{c[0], c[1]});
-    const bf16x4 l = __builtin_bit_cast(bf16x4, u32x2{c[2], c[3]});
-    f32x4 x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = static_cast<float>(h[e]) + static_cast<float>(l[e]);
-    return x;
-}
-
-// Transposed products over tokens: acc[c][mi] (+)= sum_kt X^T(ni, kt) B(kt, mi) for the dk
-// column tile ni = wave + 8 c and the four token tiles mi, where X^T fragments come from the
-// staged bf16 rows of `src` by transposed LDS reads and B(kt, mi) is the packed hi / lo chunk of
-// row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed chunks).  KT_GE_MI
-// skips the k tiles kt < mi (B = T^T is zero there).  Accumulator element r of lane 16 g + c is
-// (.)[16 ni + 4 g + r][16 mi + c].
-template <bool KT_GE_MI>
-__device__ inline void tr_products(const unsigned char* src, const float* bp, int wave, int lr, int lg,
-                                   f32x4 (&acc)[kCW][kNB])
-{
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const __bf16* base = reinterpret_cast<const __bf16*>(src);
-#pragma unroll
-    for (int kt = 0; kt < kNB; ++kt) {
-        u32x4 bch[kNB];
-#pragma unroll
-        for (int mi = 0; mi < kNB; ++mi)
-            bch[mi] = (KT_GE_MI && kt < mi) ? u32x4{0u, 0u, 0u, 0u}
-                                            : *reinterpret_cast<const u32x4*>(bp + (16 * mi + lr) * TRS + 16 * kt + 4 * lg);
-#pragma unroll
-        for (int c = 0; c < kCW; ++c) {
-            const int ni = wave + kBW * c;
-            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
-            const i16x4 xf = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
-#pragma unroll
-            for (int mi = 0; mi < kNB; ++mi) {
-                if (KT_GE_MI && kt < mi) continue;
-                const u32x4 ch = bch[mi];
-                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    xf, __builtin_bit_cast(i16x4, u32x2{ch[0], ch[1]}), acc[c][mi], 0, 0, 0);
-                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    xf, __builtin_bit_cast(i16x4, u32x2{ch[2], ch[3]}), acc[c][mi], 0, 0, 0);
-            }
-        }
-    }
-}
-
-// Stages transposed accumulators (element r of lane 16 g + c = X[16 mi + c][16 ni + 4 g + r])
-// as bf16 rows of `dst` and stores rows [0, n) to a [tokens, heads, 128] tensor.
-__device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][kNB], __bf16* out, int64_t tok0,
-                                   int n, int heads, int head, int wave, int lr, int lg, int tid)
-{
-    __bf16* d = reinterpret_cast<__bf16*>(dst);
-#pragma unroll
-    for (int c = 0; c < kCW; ++c)
-#pragma unroll
-        for (int mi = 0; mi < kNB; ++mi) {
-            bf16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[c][mi][r]);
-            *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + kBW * c) + 4 * lg) = o;
-        }
-    __syncthreads();
-    const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
-    const __amdgpu_buffer_rsrc_t r = rsrc(out + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
-#pragma unroll
-    for (int it = 0; it < Rows::NIT; ++it) {
-        const int q = tid + it * kBT;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(val, r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
-    }
-}
-
-// A = I + strictLower(D H) into Ts exactly as the forward's form_a writes it (diagonal tiles
-// keep L^T in their upper triangle for the substitution), and H = Gamma o K K^T (strict lower,
-// zeros elsewhere) into Hs, from one Gram per lower tile, over the eight waves.
-template <bool GT>
-__device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const float* bs, int wave, int lr,
-                         int lg)
-{
-    constexpr int NTILE = kNB * (kNB + 1) / 2;
-    for (int t = wave; t < NTILE; t += kBW) {  // uniform
-        int I = 0, J = 0;
-        tile_of(t, &I, &J);
-        GramFrags<0, KROW> f;
-        f.load(Kraw, I, J, lr, lg);
-        const f32x4 acc = f.product();
-        const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
-        const float bcol = bs[16 * J + lr];
-        double gcol = 0.0;
-        if constexpr (GT) gcol = GR::G(Kraw, 16 * J + lr);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
-            float a = acc[rr];
-            if constexpr (GT) {
-                const double d = GR::G(Kraw, i) - gcol;
-                a *= __expf(static_cast<float>(i > j ? d : -d));
-            }
-            Ts[i * TRS + j] = (i > j) ? bet[rr] * a : (i == j ? 1.f : bcol * a);
-            Hs[i * TRS + j] = i > j ? a : 0.f;
-        }
-    }
-    for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {  // strict upper tiles
-        int Iu = 0, rem = t;
-        while (rem >= kNB - 1 - Iu) {
-            rem -= kNB - 1 - Iu;
-            ++Iu;
-        }
-        const int Ju = Iu + 1 + rem;
-        *reinterpret_cast<f32x4*>(Ts + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-        *reinterpret_cast<f32x4*>(Hs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-    }
-}
-
-template <bool GT>
-__global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned char* Kraw = smem + OFF_K;
-    unsigned char* Vraw = smem + OFF_V;
-    unsigned char* dWraw = smem + OFF_DW;
-    unsigned char* dUraw = smem + OFF_DU;
-    float* Ts = reinterpret_cast<float*>(smem + OFF_T);
-    float* Hs = reinterpret_cast<float*>(smem + OFF_H);
-    float* Xs = reinterpret_cast<float*>(smem + OFF_X);
-    float* TT = reinterpret_cast<float*>(smem + OFF_TT);
-    float* bs = reinterpret_cast<float*>(smem + OFF_B);
-    float* part = reinterpret_cast<float*>(smem + OFF_PART);
-    float* red = reinterpret_cast<float*>(smem + OFF_RED);
-    int* info = reinterpret_cast<int*>(smem + OFF_INFO);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = uniform(tid >> 6);
-    const int lr = lane & 15, lg = lane >> 4;
-
-    // unit -> (first token, n, key head): the forward's map with key heads in place of value heads
-    wyp::Params mp{};
-    mp.cu = p.cu;
-    mp.units = p.units;
-    mp.seqlen = p.seqlen;
-    mp.hq = p.hq;
-    mp.hv = p.hq;
-    mp.num_seqs = p.num_seqs;
-    const Unit u = map_unit<kC>(mp, info, blockIdx.x, tid);
-    if (u.n <= 0) return;  // uniform
-    const int hk = u.hv;
-    const int r = p.hv / p.hq;
-    const int64_t tok0 = u.tok0;
-    const int n = u.n;
-
-    Rows kin;
-    kin.issue(p.k, tok0, n, p.hq, hk, tid);
-    f32x4 dk_acc[kCW][kNB];
-#pragma unroll
-    for (int c = 0; c < kCW; ++c)
-#pragma unroll
-        for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
-
-    for (int hv = hk * r; hv < (hk + 1) * r; ++hv) {  // uniform
-        // ---- inputs of this value head: every load issued before the first wait
-        Rows vin, dwin, duin;
-        vin.issue(p.v, tok0, n, p.hv, hv, tid);
-        dwin.issue(p.dW, tok0, n, p.hv, hv, tid);
-        duin.issue(p.dU, tok0, n, p.hv, hv, tid);
-        const __amdgpu_buffer_rsrc_t brs = rsrc(p.beta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-        const float bval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, (tid & 63) * p.hv * 4, 0, 0));
-        float gval = 0.f;
-        if constexpr (GT) {
-            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-            gval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, (tid & 63) * p.hv * 4, 0, 0));
-        }
-        if (hv == hk * r) kin.commit(Kraw, tid);
-        vin.commit(Vraw, tid);
-        dwin.commit(dWraw, tid);
-        duin.commit(dUraw, tid);
-        if (tid < kC) bs[tid] = bval;
-        if constexpr (GT) {
-            if (tid < 64) {  // G = inclusive prefix sums of g in fp64 (as the forward)
-                double x = static_cast<double>(gval);
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const double t = __shfl_up(x, d);
-                    if (tid >= d) x += t;
-                }
-                *GR::Gp(Kraw, tid) = x;
-                *GR::Ep(Kraw, tid) = __expf(static_cast<float>(x));
-            }
-        }
-        __syncthreads();
-
-        // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs)
-        form_a_h<GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
-        __syncthreads();
-        invert_diagonal_blocks<kC, TL>(Ts, tid);
-        __syncthreads();
-        coupling_level<kC, 16, TL>(Ts, tid);
-        coupling_level<kC, 32, TL>(Ts, tid);
-
-        // ---- T^T as hi / lo chunks: chunk (i, c4) holds T[4 c4 + e][i], e = 0..3
-#pragma unroll
-        for (int it = 0; it < kC * 16 / kBT; ++it) {
-            const int q = tid + it * kBT;
-            const int i = q >> 4, c4 = q & 15;
-            f32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = Ts[(4 * c4 + e) * TRS + i];
-            *reinterpret_cast<u32x4*>(TT + i * TRS + 4 * c4) = pack_hilo(x);
-        }
-        // ---- X = strictLower(dT + (dW K^T) D E + (dU V^T) D), lower tiles on bf16 MFMA
-        {
-            const __amdgpu_buffer_rsrc_t dtr =
-                rsrc(p.dT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
-                     p.dT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0);
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            for (int t = wave; t < NTILE; t += kBW) {  // uniform
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-                f32x4 pw = zero4(), pu = zero4();
-                const __bf16* dWb = reinterpret_cast<const __bf16*>(dWraw);
-                const __bf16* dUb = reinterpret_cast<const __bf16*>(dUraw);
-                const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
-                const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
-#pragma unroll
-                for (int s = 0; s < kD / 32; ++s) {
-                    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dWb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                    const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(dUb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                    const bf16x8 b2 = *reinterpret_cast<const bf16x8*>(Vb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                    pw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, pw, 0, 0, 0);
-                    pu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, pu, 0, 0, 0);
-                }
-                const int j = 16 * J + lr;
-                const float bj = bs[j];
-                const float ej = GT ? GR::E(Kraw, j) : 1.f;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr;
-                    float x = 0.f;
-                    if (i > j) {
-                        const float dt = p.dT ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                    dtr, i * p.hv * kC * 4 + j * 4, 0, 0))
-                                              : 0.f;
-                        x = dt + pw[rr] * bj * ej + pu[rr] * bj;
-                    }
-                    Xs[i * TRS + j] = x;
-                }
-            }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
-                int Iu = 0, rem = t;
-                while (rem >= kNB - 1 - Iu) {
-                    rem -= kNB - 1 - Iu;
-                    ++Iu;
-                }
-                const int Ju = Iu + 1 + rem;
-                *reinterpret_cast<f32x4*>(Xs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-            }
-        }
-        __syncthreads();
-
-        // ---- Y = X T^T on the lower tiles (fp32 MFMA): Y(M, J) = sum_{L <= J} X(M, L) T(J, L)^T;
-        // stored transposed over X
-        {
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            constexpr int NT = (NTILE + kBW - 1) / kBW;
-            f32x4 y[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                y[tt] = zero4();
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int Mt = 0, J = 0;
-                tile_of(t, &Mt, &J);
-                for (int L = 0; L <= J; ++L) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + (16 * Mt + lr) * TRS + 16 * L + 4 * lg);
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(Ts + (16 * J + lr) * TRS + 16 * L + 4 * lg);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) y[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], y[tt], 0, 0, 0);
-                }
-            }
-            __syncthreads();  // every read of X done
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int Mt = 0, J = 0;
-                tile_of(t, &Mt, &J);
-                // element r of lane 16 g + c is Y[16 Mt + 4 g + r][16 J + c] -> Y^T row 16 J + c
-                *reinterpret_cast<f32x4*>(Xs + (16 * J + lr) * TRS + 16 * Mt + 4 * lg) = y[tt];
-            }
-        }
-        __syncthreads();
-
-        // ---- M = strictLower(-T^T Y): M(I, J) = -sum_{Mt >= I} T^T(I, Mt) Y(Mt, J); T^T rows from
-        // the hi / lo chunks (hi + lo), Y from Y^T rows
-        {
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            constexpr int NT = (NTILE + kBW - 1) / kBW;
-            f32x4 m[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                m[tt] = zero4();
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-                for (int Mt = I; Mt < kNB; ++Mt) {
-                    const f32x4 a = unpack_hilo(*reinterpret_cast<const u32x4*>(TT + (16 * I + lr) * TRS + 16 * Mt + 4 * lg));
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(Xs + (16 * J + lr) * TRS + 16 * Mt + 4 * lg);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) m[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], m[tt], 0, 0, 0);
-                }
-            }
-            __syncthreads();  // every read of Y^T done
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
-                    Xs[i * TRS + j] = i > j ? -m[tt][rr] : 0.f;
-                }
-            }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
-                int Iu = 0, rem = t;
-                while (rem >= kNB - 1 - Iu) {
-                    rem -= kNB - 1 - Iu;
-                    ++Iu;
-                }
-                const int Ju = Iu + 1 + rem;
-                *reinterpret_cast<f32x4*>(Xs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-            }
-        }
-        __syncthreads();
-
-        // ---- elementwise: S = R + R^T (R = D (Gamma o M)) as hi / lo chunks over Ts;
-        // row sums sum_j M_ij H_ij and sum_j Z_ij, column sums sum_i Z_ij (Z = M o D H; H
-        // already carries Gamma)
-        {
-            const int i = tid >> 3, seg = tid & 7;  // row i, columns 8 seg .. 8 seg + 7
-            const float bi = bs[i];
-            double gi = 0.0;
-            if constexpr (GT) gi = GR::G(Kraw, i);
-            float rowMH = 0.f, rowZ = 0.f, colZ = 0.f;
-#pragma unroll
-            for (int c4 = 0; c4 < 2; ++c4) {
-                f32x4 sv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 8 * seg + 4 * c4 + e;
-                    float rij = 0.f, rji = 0.f;
-                    if (j < i) {
-                        const float mij = Xs[i * TRS + j];
-                        const float hij = Hs[i * TRS + j];
-                        float gam = 1.f;
-                        if constexpr (GT) gam = __expf(static_cast<float>(gi - GR::G(Kraw, j)));
-                        rij = mij * bi * gam;
-                        rowMH += mij * hij;
-                        rowZ += mij * bi * hij;  // Z_ij = M_ij beta_i Gamma_ij (k_i . k_j)
-                    } else if (j > i) {
-                        // this thread's column sum runs over column i: Z_ji for rows j > i
-                        const float mji = Xs[j * TRS + i];
-                        const float hji = Hs[j * TRS + i];
-                        float gam = 1.f;
-                        if constexpr (GT) gam = __expf(static_cast<float>(GR::G(Kraw, j) - gi));
-                        rji = mji * bs[j] * gam;
-                        colZ += mji * bs[j] * hji;
-                    }
-                    sv[e] = rij + rji;
-                }
-                *reinterpret_cast<u32x4*>(Ts + i * TRS + 8 * seg + 4 * c4) = pack_hilo(sv);
-            }
-            // reduce over the eight threads of row i (consecutive lanes), in a fixed order
-#pragma unroll
-            for (int d = 1; d < 8; d <<= 1) {
-                rowMH += __shfl_xor(rowMH, d);
-                rowZ += __shfl_xor(rowZ, d);
-                colZ += __shfl_xor(colZ, d);
-            }
-            if (seg == 0) {
-                red[i] = rowMH;            // dbeta part
-                red[kC + i] = rowZ - colZ;  // dG part
-            }
-        }
-        __syncthreads();
-
-        // ---- T^T dW and T^T dU (bf16 MFMA, T^T hi / lo): dK += D E T^T dW, dV = D T^T dU, and
-        // the per-row sums for dbeta and dG
-        {
-            f32x4 acc[kCW][kNB];
-#pragma unroll
-            for (int c = 0; c < kCW; ++c)
-#pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            tr_products<true>(dWraw, TT, wave, lr, lg, acc);
-            // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
-            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
-            const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
-#pragma unroll
-            for (int mi = 0; mi < kNB; ++mi) {
-                const int i = 16 * mi + lr;
-                const float bi = bs[i];
-                const float ei = GT ? GR::E(Kraw, i) : 1.f;
-                float sk = 0.f;
-#pragma unroll
-                for (int c = 0; c < kCW; ++c) {
-                    const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * (wave + kBW * c) + 4 * lg);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        sk += acc[c][mi][rr] * static_cast<float>(kv[rr]);
-                        dk_acc[c][mi][rr] += bi * ei * acc[c][mi][rr];
-                    }
-                }
-                sk += __shfl_xor(sk, 16);
-                sk += __shfl_xor(sk, 32);
-                if (lg == 0) part[(wave * 2 + 0) * kC + i] = sk;
-            }
-#pragma unroll
-            for (int c = 0; c < kCW; ++c)
-#pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            tr_products<true>(dUraw, TT, wave, lr, lg, acc);
-#pragma unroll
-            for (int mi = 0; mi < kNB; ++mi) {
-                const int i = 16 * mi + lr;
-                const float bi = bs[i];
-                float sv = 0.f;
-#pragma unroll
-                for (int c = 0; c < kCW; ++c) {
-                    const bf16x4 vv = *reinterpret_cast<const bf16x4*>(Vb + i * KROW + 16 * (wave + kBW * c) + 4 * lg);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        sv += acc[c][mi][rr] * static_cast<float>(vv[rr]);
-                        acc[c][mi][rr] *= bi;  // dV
-                    }
-                }
-                sv += __shfl_xor(sv, 16);
-                sv += __shfl_xor(sv, 32);
-                if (lg == 0) part[(wave * 2 + 1) * kC + i] = sv;
-            }
-            __syncthreads();  // every read of dU (and V) done: dV is staged over dU
-            stage_store(dUraw, acc, p.dv, tok0, n, p.hv, hv, wave, lr, lg, tid);
-        }
-        // ---- (R + R^T) K into dK (bf16 MFMA, S hi / lo; S symmetric, so its row chunks are
-        // also the column chunks the product needs)
-        tr_products<false>(Kraw, Ts, wave, lr, lg, dk_acc);
-
-        // ---- dbeta, dG, dg of this value head
-        if (tid < 64) {
-            const int i = tid;
-            float sk = 0.f, sv = 0.f;
-#pragma unroll
-            for (int w = 0; w < kBW; ++w) {
-                sk += part[(w * 2 + 0) * kC + i];
-                sv += part[(w * 2 + 1) * kC + i];
-            }
-            const float ei = GT ? GR::E(Kraw, i) : 1.f;
-            const float db = sk * ei + sv + red[i];
-            float dG = bs[i] * ei * sk + red[kC + i];
-            const __amdgpu_buffer_rsrc_t br = rsrc(p.dbeta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, db), br, i * p.hv * 4, 0, 0);
-            if constexpr (GT) {
-                // dg_t = sum_{i >= t} dG_i: a reverse inclusive scan over the 64 lanes
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const float t = __shfl_down(dG, d);
-                    if (i + d < 64) dG += t;
-                }
-                const __amdgpu_buffer_rsrc_t gr = rsrc(p.dg + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, dG), gr, i * p.hv * 4, 0, 0);
-            }
-        }
-        __syncthreads();  // LDS of this value head is rewritten by the next
-    }
-    // ---- dk, summed over the value heads of this key head
-    stage_store(Vraw, dk_acc, p.dk, tok0, n, p.hq, hk, wave, lr, lg, tid);
-}
-
-template <bool GT>
-int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
-{
-    static std::once_flag once[64];
-    static hipError_t attr_err[64];
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
-    if (e == hipSuccess) {
-        std::call_once(once[device], [&] {
-            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(wy_backward_kernel<GT>),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
-        });
-        e = attr_err[device];
-    }
-    if (e == hipSuccess) {
-        Params p;
-        p.k = static_cast<const __bf16*>(a.k);
-        p.v = static_cast<const __bf16*>(a.v);
-        p.beta = a.beta;
-        p.g = a.g;
-        p.cu = a.cu_seqlens;
-        p.dT = a.dT;
-        p.dW = static_cast<const __bf16*>(a.dW);
-        p.dU = static_cast<const __bf16*>(a.dU);
-        p.dk = static_cast<__bf16*>(a.dk);
-        p.dv = static_cast<__bf16*>(a.dv);
-        p.dbeta = a.dbeta;
-        p.dg = a.dg;
-        p.units = a.chunk_slots * a.num_qk_heads;
-        p.seqlen = a.seqlen;
-        p.hq = a.num_qk_heads;
-        p.hv = a.num_v_heads;
-        p.num_seqs = a.num_seqs;
-        hipLaunchKernelGGL(wy_backward_kernel<GT>, dim3(static_cast<uint32_t>(p.units)), dim3(kBT),
-                           LDS_TOTAL, stream, p);
-        e = hipGetLastError();
-    }
-    if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (wy_backward, gated=%d)", hipGetErrorString(e), GT ? 1 : 0);
-        return static_cast<int>(e);
-    }
-    return 0;
-}
-
-}  // namespace bwd
-
 }  // namespace
 
 int launch(const LaunchArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     return a.kv_dtype == 0 ? launch_g<0>(a, s, msg, msg_len) : launch_g<1>(a, s, msg, msg_len);
-}
-
-}  // namespace wyp
-
-namespace wyp {
-
-int launch_bwd(const BwdArgs& a, void* stream, char* msg, int msg_len)
-{
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return a.g != nullptr ? bwd::launch_t<true>(a, s, msg, msg_len) : bwd::launch_t<false>(a, s, msg, msg_len);
 }
 
 }  // namespace wyp
