@@ -100,7 +100,9 @@ struct Rows {
     __device__ void issue(const __bf16* base, int64_t tok0, int n, int heads, int head, int tid)
     {
         const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
-        const __amdgpu_buffer_rsrc_t r = rsrc(base + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
+        // n = 0 (no job): an empty range, every load reads 0 without touching memory
+        const __amdgpu_buffer_rsrc_t r =
+            rsrc(base + (tok0 * heads + head) * kD, n > 0 ? (n - 1) * stride + kD * 2 : 0u);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int q = tid + it * kBT;
@@ -114,6 +116,31 @@ struct Rows {
         for (int it = 0; it < NIT; ++it) {
             const int q = tid + it * kBT;
             *reinterpret_cast<u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16) = x[it];
+        }
+    }
+};
+
+// The inputs of one job (one value head hv of a unit: first token tok0, n tokens, key head hk)
+// in flight to registers: k (read only for the first value head of a unit), v, dW, dU, beta and
+// g.  n = 0 (past the last job) issues loads over empty ranges, so the issue has no branches.
+template <bool GT>
+struct JobIn {
+    Rows k, v, dw, du;
+    float b, g;
+
+    __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, bool with_k, int tid)
+    {
+        k.issue(p.k, tok0, with_k ? n : 0, p.hq, hk, tid);
+        v.issue(p.v, tok0, n, p.hv, hv, tid);
+        dw.issue(p.dW, tok0, n, p.hv, hv, tid);
+        du.issue(p.dU, tok0, n, p.hv, hv, tid);
+        const uint32_t bytes = n > 0 ? ((n - 1) * p.hv + 1) * 4 : 0u;
+        const __amdgpu_buffer_rsrc_t br = rsrc(p.beta + tok0 * p.hv + hv, bytes);
+        b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (tid & 63) * p.hv * 4, 0, 0));
+        g = 0.f;
+        if constexpr (GT) {
+            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, bytes);
+            g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, (tid & 63) * p.hv * 4, 0, 0));
         }
     }
 };
@@ -277,42 +304,38 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
     mp.hq = p.hq;
     mp.hv = p.hq;
     mp.num_seqs = p.num_seqs;
-    const Unit u = map_unit<kC>(mp, info, blockIdx.x, tid);
-    if (u.n <= 0) return;  // uniform
-    const int hk = u.hv;
     const int r = p.hv / p.hq;
-    const int64_t tok0 = u.tok0;
-    const int n = u.n;
-
-    Rows kin;
-    kin.issue(p.k, tok0, n, p.hq, hk, tid);
+    // Persistent: the grid holds one resident round, dealt round-robin to the 8 XCDs; each
+    // workgroup takes a contiguous range of units per round, so the value heads of a key head
+    // and neighbouring chunks meet in one L2.  Jobs (one value head of a unit) run in turn,
+    // and the next job's inputs are in flight while the current one computes.
+    const uint32_t G = gridDim.x;  // a multiple of 8
+    int64_t logical = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
+    Unit u = map_unit<kC>(mp, info, logical, tid);
+    if (u.n <= 0) return;  // uniform
+    int hv = u.hv * r;
+    bool new_unit = true;
+    JobIn<GT> in;
+    in.issue(p, u.tok0, u.n, u.hv, hv, true, tid);
     f32x4 dk_acc[kCW][kNB];
 #pragma unroll
     for (int c = 0; c < kCW; ++c)
 #pragma unroll
         for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
 
-    for (int hv = hk * r; hv < (hk + 1) * r; ++hv) {  // uniform
-        // ---- inputs of this value head: every load issued before the first wait
-        Rows vin, dwin, duin;
-        vin.issue(p.v, tok0, n, p.hv, hv, tid);
-        dwin.issue(p.dW, tok0, n, p.hv, hv, tid);
-        duin.issue(p.dU, tok0, n, p.hv, hv, tid);
-        const __amdgpu_buffer_rsrc_t brs = rsrc(p.beta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-        const float bval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, (tid & 63) * p.hv * 4, 0, 0));
-        float gval = 0.f;
-        if constexpr (GT) {
-            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
-            gval = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, (tid & 63) * p.hv * 4, 0, 0));
-        }
-        if (hv == hk * r) kin.commit(Kraw, tid);
-        vin.commit(Vraw, tid);
-        dwin.commit(dWraw, tid);
-        duin.commit(dUraw, tid);
-        if (tid < kC) bs[tid] = bval;
+    auto job = [&]() -> bool {
+        const int hk = u.hv;
+        const int64_t tok0 = u.tok0;
+        const int n = u.n;
+        // ---- this job's inputs to LDS
+        if (new_unit) in.k.commit(Kraw, tid);
+        in.v.commit(Vraw, tid);
+        in.dw.commit(dWraw, tid);
+        in.du.commit(dUraw, tid);
+        if (tid < kC) bs[tid] = in.b;
         if constexpr (GT) {
             if (tid < 64) {  // G = inclusive prefix sums of g in fp64 (as the forward)
-                double x = static_cast<double>(gval);
+                double x = static_cast<double>(in.g);
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
                     const double t = __shfl_up(x, d);
@@ -323,6 +346,18 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
             }
         }
         __syncthreads();
+        // ---- the next job (the next value head of this unit, else the first of the next unit)
+        // goes in flight now
+        Unit nu = u;
+        int nhv = hv + 1;
+        bool nnew = false;
+        if (nhv == (hk + 1) * r) {  // uniform
+            logical += G;
+            nu = map_unit<kC>(mp, info, logical, tid);
+            nhv = nu.hv * r;
+            nnew = true;
+        }
+        in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);
 
         // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs)
         form_a_h<GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
@@ -342,45 +377,55 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
             for (int e = 0; e < 4; ++e) x[e] = Ts[(4 * c4 + e) * TRS + i];
             *reinterpret_cast<u32x4*>(TT + i * TRS + 4 * c4) = pack_hilo(x);
         }
-        // ---- X = strictLower(dT + (dW K^T) D E + (dU V^T) D), lower tiles on bf16 MFMA
+        // ---- X = strictLower(dT + (dW K^T) D E + (dU V^T) D), lower tiles on bf16 MFMA.  The dT
+        // reads sit in their own instance of the tile loop: without dT the loop issues no memory
+        // operation, so nothing in it waits for the next job's loads in flight.
         {
-            const __amdgpu_buffer_rsrc_t dtr =
-                rsrc(p.dT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
-                     p.dT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0);
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            for (int t = wave; t < NTILE; t += kBW) {  // uniform
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-                f32x4 pw = zero4(), pu = zero4();
-                const __bf16* dWb = reinterpret_cast<const __bf16*>(dWraw);
-                const __bf16* dUb = reinterpret_cast<const __bf16*>(dUraw);
-                const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
-                const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
+            auto x_tiles = [&](auto with_dt) {
+                constexpr bool DT = decltype(with_dt)::value;
+                const __amdgpu_buffer_rsrc_t dtr =
+                    rsrc(DT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
+                         DT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0u);
+                constexpr int NTILE = kNB * (kNB + 1) / 2;
+                for (int t = wave; t < NTILE; t += kBW) {  // uniform
+                    int I = 0, J = 0;
+                    tile_of(t, &I, &J);
+                    f32x4 pw = zero4(), pu = zero4();
+                    const __bf16* dWb = reinterpret_cast<const __bf16*>(dWraw);
+                    const __bf16* dUb = reinterpret_cast<const __bf16*>(dUraw);
+                    const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+                    const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
 #pragma unroll
-                for (int s = 0; s < kD / 32; ++s) {
-                    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dWb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                    const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(dUb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                    const bf16x8 b2 = *reinterpret_cast<const bf16x8*>(Vb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                    pw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, pw, 0, 0, 0);
-                    pu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, pu, 0, 0, 0);
-                }
-                const int j = 16 * J + lr;
-                const float bj = bs[j];
-                const float ej = GT ? GR::E(Kraw, j) : 1.f;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr;
-                    float x = 0.f;
-                    if (i > j) {
-                        const float dt = p.dT ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                    dtr, i * p.hv * kC * 4 + j * 4, 0, 0))
-                                              : 0.f;
-                        x = dt + pw[rr] * bj * ej + pu[rr] * bj;
+                    for (int s = 0; s < kD / 32; ++s) {
+                        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dWb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
+                        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
+                        const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(dUb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
+                        const bf16x8 b2 = *reinterpret_cast<const bf16x8*>(Vb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
+                        pw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, pw, 0, 0, 0);
+                        pu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, pu, 0, 0, 0);
                     }
-                    Xs[i * TRS + j] = x;
+                    const int j = 16 * J + lr;
+                    const float bj = bs[j];
+                    const float ej = GT ? GR::E(Kraw, j) : 1.f;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = 16 * I + 4 * lg + rr;
+                        float x = 0.f;
+                        if (i > j) {
+                            float dt = 0.f;
+                            if constexpr (DT)
+                                dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                   dtr, i * p.hv * kC * 4 + j * 4, 0, 0));
+                            x = dt + pw[rr] * bj * ej + pu[rr] * bj;
+                        }
+                        Xs[i * TRS + j] = x;
+                    }
                 }
-            }
+            };
+            if (p.dT != nullptr)  // uniform
+                x_tiles(std::true_type{});
+            else
+                x_tiles(std::false_type{});
             for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
                 int Iu = 0, rem = t;
                 while (rem >= kNB - 1 - Iu) {
@@ -609,25 +654,50 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
             }
         }
         __syncthreads();  // LDS of this value head is rewritten by the next
+        if (hv == (hk + 1) * r - 1) {  // uniform: dk of this unit, summed over its value heads
+            stage_store(Vraw, dk_acc, p.dk, tok0, n, p.hq, hk, wave, lr, lg, tid);
+#pragma unroll
+            for (int c = 0; c < kCW; ++c)
+#pragma unroll
+                for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
+            __syncthreads();  // the staging rows (V) are rewritten by the next commit
+        }
+        u = nu;
+        hv = nhv;
+        new_unit = nnew;
+        return u.n > 0;
+    };
+    // The first job is peeled off the loop: the loop head is then reached only from the end of
+    // a job, so the memory-counter waits inside see one issue history.
+    if (job()) {
+        while (job()) {
+        }
     }
-    // ---- dk, summed over the value heads of this key head
-    stage_store(Vraw, dk_acc, p.dk, tok0, n, p.hq, hk, wave, lr, lg, tid);
 }
 
 template <bool GT>
 int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 {
-    static std::once_flag once[64];
-    static hipError_t attr_err[64];
+    // Per device, once: raise the kernel's dynamic LDS limit and count its resident workgroups
+    // (occupancy x CUs), so later launches (also under stream capture) make no attribute calls.
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t setup_err[kMaxDevices];
+    static int resident[kMaxDevices];
     int device = 0;
     hipError_t e = hipGetDevice(&device);
-    if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
+    if (e == hipSuccess && (device < 0 || device >= kMaxDevices)) e = hipErrorInvalidDevice;
     if (e == hipSuccess) {
         std::call_once(once[device], [&] {
-            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(wy_backward_kernel<GT>),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+            const void* kern = reinterpret_cast<const void*>(wy_backward_kernel<GT>);
+            hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+            int cus = 0, per_cu = 0;
+            if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+            if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBT, LDS_TOTAL);
+            resident[device] = (per_cu > 0 ? per_cu : 1) * cus;
+            setup_err[device] = err;
         });
-        e = attr_err[device];
+        e = setup_err[device];
     }
     if (e == hipSuccess) {
         Params p;
@@ -648,8 +718,12 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.hq = a.num_qk_heads;
         p.hv = a.num_v_heads;
         p.num_seqs = a.num_seqs;
-        hipLaunchKernelGGL(wy_backward_kernel<GT>, dim3(static_cast<uint32_t>(p.units)), dim3(kBT),
-                           LDS_TOTAL, stream, p);
+        // one resident round (a multiple of 8 workgroups, for the XCD mapping), or fewer
+        int64_t grid = (p.units + 7) / 8 * 8;
+        const int64_t cap = static_cast<int64_t>(resident[device]) / 8 * 8;
+        if (cap >= 8 && grid > cap) grid = cap;
+        hipLaunchKernelGGL(wy_backward_kernel<GT>, dim3(static_cast<uint32_t>(grid)), dim3(kBT), LDS_TOTAL,
+                           stream, p);
         e = hipGetLastError();
     }
     if (e != hipSuccess) {
