@@ -63,7 +63,8 @@ constexpr int OFF_TT = OFF_X + TB;           // T^T as hi / lo chunks
 constexpr int OFF_B = OFF_TT + TB;           // beta (64 floats)
 constexpr int OFF_PART = OFF_B + kC * 4;     // per-wave row partials: kBW waves x 2 x 64 floats
 constexpr int OFF_RED = OFF_PART + kBW * 2 * kC * 4;  // dbeta, dG of this value head (2 x 64)
-constexpr int OFF_INFO = OFF_RED + 2 * kC * 4;
+constexpr int OFF_GD = OFF_RED + 2 * kC * 4;  // G of the chunk's rows, fp64 (gated instances)
+constexpr int OFF_INFO = OFF_GD + kC * 8;
 constexpr int LDS_TOTAL = OFF_INFO + 16;
 static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
 
@@ -234,8 +235,10 @@ __device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][k
 }
 
 // A = I + strictLower(D H) into Ts exactly as the forward's form_a writes it (diagonal tiles
-// keep L^T in their upper triangle for the substitution), and H = Gamma o K K^T (strict lower,
-// zeros elsewhere) into Hs, from one Gram per lower tile, over the eight waves.
+// keep L^T in their upper triangle for the substitution), and H = Gamma o K K^T into Hs, from one
+// Gram per lower tile, over the eight waves.  Hs holds H below the diagonal and its transpose
+// above (Hs[j][i] = H[i][j] for i > j; 0 on the diagonal), so row i of Hs lists H_ij for j < i
+// and H_ji for j > i: the elementwise step then reads rows only.
 template <bool GT>
 __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const float* bs, int wave, int lr,
                          int lg)
@@ -251,6 +254,7 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
         const float bcol = bs[16 * J + lr];
         double gcol = 0.0;
         if constexpr (GT) gcol = GR::G(Kraw, 16 * J + lr);
+        f32x4 hv;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
@@ -260,8 +264,12 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
                 a *= __expf(static_cast<float>(i > j ? d : -d));
             }
             Ts[i * TRS + j] = (i > j) ? bet[rr] * a : (i == j ? 1.f : bcol * a);
-            Hs[i * TRS + j] = i > j ? a : 0.f;
+            // a diagonal tile above its diagonal holds Gram_ij Gamma_ji = H_ji already
+            Hs[i * TRS + j] = i != j ? a : 0.f;
+            hv[rr] = a;
         }
+        if (I > J)  // uniform: H^T of the tile into the upper tile (J, I), one 16-byte row chunk
+            *reinterpret_cast<f32x4*>(Hs + (16 * J + lr) * TRS + 16 * I + 4 * lg) = hv;
     }
     for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {  // strict upper tiles
         int Iu = 0, rem = t;
@@ -271,7 +279,6 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
         }
         const int Ju = Iu + 1 + rem;
         *reinterpret_cast<f32x4*>(Ts + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-        *reinterpret_cast<f32x4*>(Hs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
     }
 }
 
@@ -290,6 +297,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
     float* bs = reinterpret_cast<float*>(smem + OFF_B);
     float* part = reinterpret_cast<float*>(smem + OFF_PART);
     float* red = reinterpret_cast<float*>(smem + OFF_RED);
+    double* Gd = reinterpret_cast<double*>(smem + OFF_GD);
     int* info = reinterpret_cast<int*>(smem + OFF_INFO);
 
     const int tid = threadIdx.x;
@@ -343,6 +351,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
                 }
                 *GR::Gp(Kraw, tid) = x;
                 *GR::Ep(Kraw, tid) = __expf(static_cast<float>(x));
+                Gd[tid] = x;
             }
         }
         __syncthreads();
@@ -498,60 +507,59 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
                 if (t >= NTILE) break;
                 int I = 0, J = 0;
                 tile_of(t, &I, &J);
+                // M below the diagonal and M^T above it (Xs[j][i] = M[i][j] for i > j; 0 on the
+                // diagonal), so that row i of Xs lists M_ij for j < i and M_ji for j > i
+                if (I > J) {  // uniform
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
-                    Xs[i * TRS + j] = i > j ? -m[tt][rr] : 0.f;
+                    for (int rr = 0; rr < 4; ++rr) Xs[(16 * I + 4 * lg + rr) * TRS + 16 * J + lr] = -m[tt][rr];
+                    *reinterpret_cast<f32x4*>(Xs + (16 * J + lr) * TRS + 16 * I + 4 * lg) = -m[tt];
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
+                        if (i >= j) Xs[i * TRS + j] = i > j ? -m[tt][rr] : 0.f;
+                        if (i > j) Xs[j * TRS + i] = -m[tt][rr];
+                    }
                 }
-            }
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
-                int Iu = 0, rem = t;
-                while (rem >= kNB - 1 - Iu) {
-                    rem -= kNB - 1 - Iu;
-                    ++Iu;
-                }
-                const int Ju = Iu + 1 + rem;
-                *reinterpret_cast<f32x4*>(Xs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
             }
         }
         __syncthreads();
 
         // ---- elementwise: S = R + R^T (R = D (Gamma o M)) as hi / lo chunks over Ts;
         // row sums sum_j M_ij H_ij and sum_j Z_ij, column sums sum_i Z_ij (Z = M o D H; H
-        // already carries Gamma)
+        // already carries Gamma).  Row i of Xs and Hs holds M_ij, H_ij for j < i and M_ji, H_ji
+        // for j > i, so every read is a 16-byte row chunk.
         {
             const int i = tid >> 3, seg = tid & 7;  // row i, columns 8 seg .. 8 seg + 7
             const float bi = bs[i];
             double gi = 0.0;
-            if constexpr (GT) gi = GR::G(Kraw, i);
+            if constexpr (GT) gi = Gd[i];
             float rowMH = 0.f, rowZ = 0.f, colZ = 0.f;
 #pragma unroll
             for (int c4 = 0; c4 < 2; ++c4) {
+                const int j0 = 8 * seg + 4 * c4;
+                const f32x4 mv = *reinterpret_cast<const f32x4*>(Xs + i * TRS + j0);
+                const f32x4 hv = *reinterpret_cast<const f32x4*>(Hs + i * TRS + j0);
+                const f32x4 bj = *reinterpret_cast<const f32x4*>(bs + j0);
                 f32x4 sv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int j = 8 * seg + 4 * c4 + e;
-                    float rij = 0.f, rji = 0.f;
-                    if (j < i) {
-                        const float mij = Xs[i * TRS + j];
-                        const float hij = Hs[i * TRS + j];
-                        float gam = 1.f;
-                        if constexpr (GT) gam = __expf(static_cast<float>(gi - GR::G(Kraw, j)));
-                        rij = mij * bi * gam;
-                        rowMH += mij * hij;
-                        rowZ += mij * bi * hij;  // Z_ij = M_ij beta_i Gamma_ij (k_i . k_j)
-                    } else if (j > i) {
-                        // this thread's column sum runs over column i: Z_ji for rows j > i
-                        const float mji = Xs[j * TRS + i];
-                        const float hji = Hs[j * TRS + i];
-                        float gam = 1.f;
-                        if constexpr (GT) gam = __expf(static_cast<float>(GR::G(Kraw, j) - gi));
-                        rji = mji * bs[j] * gam;
-                        colZ += mji * bs[j] * hji;
+                    const int j = j0 + e;
+                    const bool below = j < i, above = j > i;
+                    float gam = 1.f;
+                    if constexpr (GT) {  // decay between the later and the earlier token
+                        const double d = Gd[j] - gi;
+                        gam = __expf(static_cast<float>(below ? -d : d));
                     }
-                    sv[e] = rij + rji;
+                    const float m = mv[e], h = hv[e];
+                    // R_ij (j < i) and R_ji (j > i); Z_ij = M_ij beta_i Gamma_ij (k_i . k_j), and
+                    // this thread's column sum runs over column i: Z_ji for rows j > i
+                    sv[e] = below ? m * bi * gam : (above ? m * bj[e] * gam : 0.f);
+                    rowMH += below ? m * h : 0.f;
+                    rowZ += below ? m * bi * h : 0.f;
+                    colZ += above ? m * bj[e] * h : 0.f;
                 }
-                *reinterpret_cast<u32x4*>(Ts + i * TRS + 8 * seg + 4 * c4) = pack_hilo(sv);
+                *reinterpret_cast<u32x4*>(Ts + i * TRS + j0) = pack_hilo(sv);
             }
             // reduce over the eight threads of row i (consecutive lanes), in a fixed order
 #pragma unroll
