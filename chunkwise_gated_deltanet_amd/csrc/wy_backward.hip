@@ -371,7 +371,71 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs)
         form_a_h<GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
         __syncthreads();
-        invert_diagonal_blocks<kC, TL>(Ts, tid);
+        // ---- wave 0 inverts the diagonal blocks of A (its substitutions are one long dependency
+        // chain); meanwhile waves 1-7 form X, which does not depend on T
+        if (wave == 0) {  // uniform
+            invert_diagonal_blocks<kC, TL>(Ts, tid);
+        } else {
+            // ---- X = strictLower(dT + (dW K^T) D E + (dU V^T) D), lower tiles on bf16 MFMA.  The dT
+            // reads sit in their own instance of the tile loop: without dT the loop issues no memory
+            // operation, so nothing in it waits for the next job's loads in flight.
+            {
+                auto x_tiles = [&](auto with_dt) {
+                    constexpr bool DT = decltype(with_dt)::value;
+                    const __amdgpu_buffer_rsrc_t dtr =
+                        rsrc(DT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
+                             DT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0u);
+                    constexpr int NTILE = kNB * (kNB + 1) / 2;
+                    for (int t = wave - 1; t < NTILE; t += kBW - 1) {  // uniform
+                        int I = 0, J = 0;
+                        tile_of(t, &I, &J);
+                        f32x4 pw = zero4(), pu = zero4();
+                        const __bf16* dWb = reinterpret_cast<const __bf16*>(dWraw);
+                        const __bf16* dUb = reinterpret_cast<const __bf16*>(dUraw);
+                        const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+                        const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
+#pragma unroll
+                        for (int s = 0; s < kD / 32; ++s) {
+                            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dWb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
+                            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
+                            const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(dUb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
+                            const bf16x8 b2 = *reinterpret_cast<const bf16x8*>(Vb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
+                            pw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, pw, 0, 0, 0);
+                            pu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, pu, 0, 0, 0);
+                        }
+                        const int j = 16 * J + lr;
+                        const float bj = bs[j];
+                        const float ej = GT ? GR::E(Kraw, j) : 1.f;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int i = 16 * I + 4 * lg + rr;
+                            float x = 0.f;
+                            if (i > j) {
+                                float dt = 0.f;
+                                if constexpr (DT)
+                                    dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                       dtr, i * p.hv * kC * 4 + j * 4, 0, 0));
+                                x = dt + pw[rr] * bj * ej + pu[rr] * bj;
+                            }
+                            Xs[i * TRS + j] = x;
+                        }
+                    }
+                };
+                if (p.dT != nullptr)  // uniform
+                    x_tiles(std::true_type{});
+                else
+                    x_tiles(std::false_type{});
+                for (int t = wave - 1; t < kNB * (kNB - 1) / 2; t += kBW - 1) {
+                    int Iu = 0, rem = t;
+                    while (rem >= kNB - 1 - Iu) {
+                        rem -= kNB - 1 - Iu;
+                        ++Iu;
+                    }
+                    const int Ju = Iu + 1 + rem;
+                    *reinterpret_cast<f32x4*>(Xs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
+                }
+            }
+        }
         __syncthreads();
         coupling_level<kC, 16, TL>(Ts, tid);
         coupling_level<kC, 32, TL>(Ts, tid);
@@ -385,65 +449,6 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = Ts[(4 * c4 + e) * TRS + i];
             *reinterpret_cast<u32x4*>(TT + i * TRS + 4 * c4) = pack_hilo(x);
-        }
-        // ---- X = strictLower(dT + (dW K^T) D E + (dU V^T) D), lower tiles on bf16 MFMA.  The dT
-        // reads sit in their own instance of the tile loop: without dT the loop issues no memory
-        // operation, so nothing in it waits for the next job's loads in flight.
-        {
-            auto x_tiles = [&](auto with_dt) {
-                constexpr bool DT = decltype(with_dt)::value;
-                const __amdgpu_buffer_rsrc_t dtr =
-                    rsrc(DT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
-                         DT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0u);
-                constexpr int NTILE = kNB * (kNB + 1) / 2;
-                for (int t = wave; t < NTILE; t += kBW) {  // uniform
-                    int I = 0, J = 0;
-                    tile_of(t, &I, &J);
-                    f32x4 pw = zero4(), pu = zero4();
-                    const __bf16* dWb = reinterpret_cast<const __bf16*>(dWraw);
-                    const __bf16* dUb = reinterpret_cast<const __bf16*>(dUraw);
-                    const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
-                    const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
-#pragma unroll
-                    for (int s = 0; s < kD / 32; ++s) {
-                        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dWb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                        const bf16x8 a2 = *reinterpret_cast<const bf16x8*>(dUb + (16 * I + lr) * KROW + 32 * s + 8 * lg);
-                        const bf16x8 b2 = *reinterpret_cast<const bf16x8*>(Vb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
-                        pw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, pw, 0, 0, 0);
-                        pu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b2, pu, 0, 0, 0);
-                    }
-                    const int j = 16 * J + lr;
-                    const float bj = bs[j];
-                    const float ej = GT ? GR::E(Kraw, j) : 1.f;
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int i = 16 * I + 4 * lg + rr;
-                        float x = 0.f;
-                        if (i > j) {
-                            float dt = 0.f;
-                            if constexpr (DT)
-                                dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                                   dtr, i * p.hv * kC * 4 + j * 4, 0, 0));
-                            x = dt + pw[rr] * bj * ej + pu[rr] * bj;
-                        }
-                        Xs[i * TRS + j] = x;
-                    }
-                }
-            };
-            if (p.dT != nullptr)  // uniform
-                x_tiles(std::true_type{});
-            else
-                x_tiles(std::false_type{});
-            for (int t = wave; t < kNB * (kNB - 1) / 2; t += kBW) {
-                int Iu = 0, rem = t;
-                while (rem >= kNB - 1 - Iu) {
-                    rem -= kNB - 1 - Iu;
-                    ++Iu;
-                }
-                const int Ju = Iu + 1 + rem;
-                *reinterpret_cast<f32x4*>(Xs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-            }
         }
         __syncthreads();
 
