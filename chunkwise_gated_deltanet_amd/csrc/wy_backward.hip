@@ -18,8 +18,10 @@
 //   dbeta_i = sum_d (T^T dW)_id e^{G_i} K_id + sum_d (T^T dU)_id V_id + sum_j M_ij H_ij
 //   dG_i = beta_i e^{G_i} sum_d (T^T dW)_id K_id + sum_j Z_ij - sum_j Z_ji,  Z = M o D H
 //   dg_t = sum_{i >= t} dG_i
-// One workgroup per (chunk, key head) handles the value heads of that key head in turn and
-// sums their dK in registers, so dk is written once, without atomics.  T is recomputed with
+// A unit is one (chunk, key head); a workgroup handles the value heads of a unit in turn (one
+// job each) and sums their dK in registers, so dk is written once, without atomics.  Workgroups
+// are persistent and walk a strided list of units; the next job's inputs are loaded while the
+// current job computes.  T is recomputed with
 // the forward's own steps (bit-identical to the T that wy_prepare returns).  T and R + R^T
 // enter the bf16 products as hi + lo pairs, so dbeta and dg keep fp32 accuracy.
 //
@@ -41,7 +43,7 @@ namespace bwd {
 
 constexpr int kC = 64;
 constexpr int kNB = kC / 16;
-// Eight waves per workgroup: LDS (140 KB) holds one workgroup per CU, and with one wave per SIMD
+// Eight waves per workgroup: LDS (141 KB) holds one workgroup per CU, and with one wave per SIMD
 // every LDS, MFMA and VALU latency of the unit's long serial chain would be exposed.  Phases
 // that tile over waves run twice as wide; the forward's Gram / substitution / coupling steps
 // keep their four-wave mapping.
