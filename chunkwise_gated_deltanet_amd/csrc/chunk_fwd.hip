@@ -487,15 +487,22 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
     const int lr = lane & 15, lg = lane >> 4;
     const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kCombCols : nullptr;
     const int64_t slot0 = static_cast<int64_t>(pair) * (p.nseg - 1);
-    CombineOperands cur, nxt;
-    if (p.nseg > 1) cur.load(p, slot0, slice, wave, lr, lg);
+    // Two operand sets take turns (the loop is unrolled by two), so the next step's M and A are
+    // loaded straight into the set that step uses, with no register copies that would wait for
+    // those loads early.
+    CombineOperands ops0, ops1;
+    ops0.load(p, slot0, slice, wave, lr, lg);  // launched only with nseg > 1
     for (int idx = tid; idx < kD * kCombCols; idx += kThreads) {
         const int row = idx / kCombCols, col = idx % kCombCols;
         St[col][row] = h0 ? h0[row * kD + col] : 0.f;
     }
     __syncthreads();
-    for (int sg = 0; sg + 1 < p.nseg; ++sg) {  // uniform
-        if (sg + 2 < p.nseg) nxt.load(p, slot0 + sg + 1, slice, wave, lr, lg);
+    auto step = [&](int sg, const CombineOperands& cur, CombineOperands& nxt) {
+        // M and A of the next step, in flight during this one.  The last step reloads its own
+        // slot (in bounds, unused) so that the issue has no branch: a branch around it makes the
+        // compiler's wait for `cur` conservative, and that wait would then cover these loads.
+        nxt.load(p, slot0 + (sg + 2 < p.nseg ? sg + 1 : sg), slice, wave, lr, lg);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of this step's products
         f32x4 acc[2];
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
@@ -517,7 +524,11 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
             for (int r = 0; r < 4; ++r) A[(16 * (2 * wave + mm) + 4 * lg + r) * kD + lr] = acc[mm][r];
         }
         __syncthreads();
-        cur = nxt;
+    };
+    for (int sg = 0; sg + 1 < p.nseg; sg += 2) {  // uniform
+        step(sg, ops0, ops1);
+        if (sg + 2 >= p.nseg) break;  // uniform
+        step(sg + 1, ops1, ops0);
     }
 }
 
