@@ -31,7 +31,9 @@
 //      operand of the 16x16x16 product P V' below, so P never goes through LDS;
 //   2. O tile += (Gamma o P) V'; S tiles = exp(G_last) S + K^T V'_dec (K^T fragments by
 //      ds_read_tr16_b64); the new bf16 S^T goes to LDS; O is staged and stored as 16-byte rows.
-// The state stays fp32 in the MFMA accumulators for the whole sequence.
+// The state stays fp32 in the MFMA accumulators for the whole sequence.  Every load of chunk
+// c + 1 (K, U, g and this wave's Q and W rows) is issued right after chunk c's first barrier into a
+// second register set; the two sets take turns.
 //
 // Sequence parallelism (wyp_chunk_fwd_cp; [QLA] "兼顾访存开销与序列并行的解法": the state
 // kernel's thread blocks number only batch x heads, so the pages split each sequence and fix
@@ -103,8 +105,8 @@ struct Params {
 // row stride 272 B, so 16-byte reads of one column chunk by 16 consecutive rows spread over the
 // banks), the U slice, the staged O slice, the bf16 S^T and V'^T tiles (padded the same way) and
 // G.  Q and W rows of row tile w are read by wave w alone, so they go from HBM straight into its
-// MFMA operand registers: this halves the LDS traffic of a chunk step and lets three workgroups
-// share a CU (45.8 KB each).
+// MFMA operand registers: this halves the LDS traffic of a chunk step.  45.8 KB each: LDS would
+// let three workgroups share a CU (registers allow three ungated, two gated).
 constexpr int QROW = kD + 8;          // bf16 per K row
 constexpr int UROW = kDVS + 8;        // bf16 per U / O slice row
 constexpr int SROW = kD + 8;          // bf16 per S^T row (one dv column of S)
@@ -117,7 +119,7 @@ constexpr int OFF_VN = OFF_S + kDVS * SROW * 2;
 constexpr int OFF_VD = OFF_VN + kDVS * VROW * 2;
 constexpr int OFF_G = OFF_VD + kDVS * VROW * 2;
 constexpr int LDS_TOTAL = OFF_G + kC * 4;
-static_assert(3 * LDS_TOTAL <= 160 * 1024, "three workgroups per CU");
+static_assert(3 * LDS_TOTAL <= 160 * 1024, "three workgroups per CU by LDS");
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -126,6 +128,14 @@ __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x);
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferConfig);
+}
+
+// Bytes spanned by rows [0, n) of a row-strided tensor (row stride `stride` bytes, `width` bytes
+// read per row); 0 for n <= 0, which puts every access out of range (loads read 0), so loads can
+// be issued without branches.
+__device__ inline uint32_t row_bytes(int n, uint32_t stride, uint32_t width)
+{
+    return n > 0 ? static_cast<uint32_t>(n - 1) * stride + width : 0u;
 }
 
 // One chunk's data in flight to registers: K (64 rows x 256 B: four 16-byte pieces per thread),
@@ -144,8 +154,8 @@ struct Chunk {
     {
         const uint32_t qstride = static_cast<uint32_t>(p.hq) * kD * 2;
         const uint32_t wstride = static_cast<uint32_t>(p.hv) * kD * 2;
-        const __amdgpu_buffer_rsrc_t qr = rsrc(p.q + (tok0 * p.hq + hk) * kD, (n - 1) * qstride + kD * 2);
-        const __amdgpu_buffer_rsrc_t wr = rsrc(p.w + (tok0 * p.hv + hv) * kD, (n - 1) * wstride + kD * 2);
+        const __amdgpu_buffer_rsrc_t qr = rsrc(p.q + (tok0 * p.hq + hk) * kD, row_bytes(n, qstride, kD * 2));
+        const __amdgpu_buffer_rsrc_t wr = rsrc(p.w + (tok0 * p.hv + hv) * kD, row_bytes(n, wstride, kD * 2));
         const int lane = tid & 63, row = 16 * (tid >> 6) + (lane & 15), lg = lane >> 4;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -156,28 +166,30 @@ struct Chunk {
         }
     }
 
-    // K, U and g (all of them, or without Q / W when `qw` is false).
+    // K, U, g, then Q and W: every load of one chunk, without branches (n = 0: nothing is read).
+    template <bool GT>
     __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, int slice, int tid,
-                          bool want_q = true, bool want_u = true, bool qw = true)
+                          bool want_q, bool want_u)
     {
         const uint32_t qstride = static_cast<uint32_t>(p.hq) * kD * 2;
         const uint32_t wstride = static_cast<uint32_t>(p.hv) * kD * 2;
-        const __amdgpu_buffer_rsrc_t kr = rsrc(p.k + (tok0 * p.hq + hk) * kD, (n - 1) * qstride + kD * 2);
+        const __amdgpu_buffer_rsrc_t kr = rsrc(p.k + (tok0 * p.hq + hk) * kD, row_bytes(n, qstride, kD * 2));
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int pc = tid + it * kThreads;  // row pc / 16, piece pc % 16
             k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
         }
-        if (qw) issue_qw(p, tok0, n, hk, hv, tid, want_q);
-        const __amdgpu_buffer_rsrc_t ur =
-            rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * kDVS, (n - 1) * wstride + kDVS * 2);
-        u = want_u ? __builtin_amdgcn_raw_buffer_load_b128(ur, (tid >> 2) * wstride + (tid & 3) * 16, 0, kStream)
-                   : u32x4{0u, 0u, 0u, 0u};
+        // the transition slices of the sequence-parallel pass read no U: an empty range
+        const __amdgpu_buffer_rsrc_t ur = rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * kDVS,
+                                               want_u ? row_bytes(n, wstride, kDVS * 2) : 0u);
+        u = __builtin_amdgcn_raw_buffer_load_b128(ur, (tid >> 2) * wstride + (tid & 3) * 16, 0, kStream);
         g = 0.f;
-        if (p.g != nullptr && tid < 64) {
-            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
+        if constexpr (GT) {
+            // every thread loads; rows tid >= n (all of waves 1-3) fall outside the range
+            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, row_bytes(n, p.hv * 4, 4));
             g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, tid * p.hv * 4, 0, kStream));
         }
+        issue_qw(p, tok0, n, hk, hv, tid, want_q);
     }
 
     // K and U to LDS; wave 0 turns g into the chunk-local inclusive prefix sums G (fp64 shuffle
@@ -218,7 +230,10 @@ __device__ inline void seq_range(const Params& p, int seq, int64_t* s0, int64_t*
 }
 
 template <bool GT, bool LOCAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_fwd_kernel(Params p)
+// Two waves per SIMD for the register allocator: the two register sets of the chunk pipeline take
+// 155 (gated: 177) VGPRs; with three the gated instance spills, and the ungated one is slower at
+// one workgroup per CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous range of work
@@ -293,17 +308,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     };
     write_st();
 
-    Chunk cur;
+    // Two register sets take turns (the loop is unrolled by two): chunk c + 1's loads go into the
+    // set chunk c does not use, right after chunk c's first barrier, so they have a whole chunk
+    // step to arrive, and no register copy makes the compiler wait for them early.
+    Chunk ch0, ch1;
     const bool want_q = !LOCAL, want_u = !mcols;
-    if (c_begin < c_end) {
+    {
         const int64_t t0 = s0 + static_cast<int64_t>(c_begin) * kC;
-        cur.issue(p, t0, static_cast<int>(s1 - t0 < kC ? s1 - t0 : kC), hk, hv, slice, tid, want_q, want_u);
+        const int n0 = c_begin < c_end ? static_cast<int>(s1 - t0 < kC ? s1 - t0 : kC) : 0;
+        ch0.issue<GT>(p, t0, n0, hk, hv, slice, tid, want_q, want_u);
+        // Each chunk step ends with its O store; the loop is entered after a store too (over an
+        // empty range: the hardware drops it), so both ways into the loop have the same memory
+        // history and the compiler's waits inside need not cover the youngest store.
+        if constexpr (!LOCAL)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rsrc(p.o, 0u), 0, 0, kStream);
     }
-    for (int c = c_begin; c < c_end; ++c) {  // uniform
+    auto step = [&](int c, const Chunk& cur, Chunk& nxt) {
         const int64_t tok0 = s0 + static_cast<int64_t>(c) * kC;
         const int n = static_cast<int>(s1 - tok0 < kC ? s1 - tok0 : kC);
         cur.commit<GT>(smem, tid);
-        // this wave's Q and W operands leave the prefetch registers before they are reused
+        // this wave's Q and W operands, straight from the registers they were loaded into
         bf16x8 qa[kD / 32], wa[kD / 32];
 #pragma unroll
         for (int s = 0; s < kD / 32; ++s) {
@@ -311,9 +335,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             wa[s] = __builtin_bit_cast(bf16x8, cur.w[s]);
         }
         __syncthreads();  // B1: the chunk (and the state's S^T) is in LDS
+        // every load of the next chunk goes in flight now, into the other register set
         const int64_t nt0 = tok0 + kC;
-        const int nn = static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC);
-        if (c + 1 < c_end) cur.issue(p, nt0, nn, hk, hv, slice, tid, want_q, want_u, false);
+        const int nn = c + 1 < c_end ? static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC) : 0;
+        nxt.issue<GT>(p, nt0, nn, hk, hv, slice, tid, want_q, want_u);
         const int I = wave;  // row tile of V' and O
         const float glast = GT ? Gs[kC - 1] : 0.f;
         float grow[4];
@@ -377,7 +402,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             pa[J] = a;
         }
         __syncthreads();  // B2: V'^T and V'_dec^T complete; every read of S^T and U is done
-        if (c + 1 < c_end) cur.issue_qw(p, nt0, nn, hk, hv, tid, want_q);  // qa, wa are dead
 
         // 2a. O += (Gamma o P) V' over the causal k tiles (16x16x16 bf16)
 #pragma unroll
@@ -429,6 +453,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const u32x4 val = *reinterpret_cast<const u32x4*>(smem + OFF_O + (tid >> 2) * (UROW * 2) + (tid & 3) * 16);
             __builtin_amdgcn_raw_buffer_store_b128(val, orr, (tid >> 2) * ostride + (tid & 3) * 16, 0, kStream);
         }
+    };
+    for (int c = c_begin; c < c_end; c += 2) {  // uniform
+        step(c, ch0, ch1);
+        if (c + 1 >= c_end) break;  // uniform
+        step(c + 1, ch1, ch0);
     }
     float* out = nullptr;  // where this work item's end state goes
     if (LOCAL)
