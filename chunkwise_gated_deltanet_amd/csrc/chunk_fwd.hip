@@ -479,10 +479,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // Pass 2 of the sequence-parallel forward: per (sequence, value head, 16-column dv slice),
 // S_start(0) = the initial state and S_start(s + 1) = M_s S_start(s) + A_s for s = 0 .. nseg - 2,
 // each written over A_s (it is read there by pass 3).  Each step is 128 x 128 x 16 fp32
-// multiply-adds on fp32 MFMA 16x16x4, bound by that unit's throughput, so the slices are 16
-// columns wide (eight workgroups per head); wave w owns row tiles 2w, 2w + 1; S^T sits in LDS so
-// every B operand is one 16-byte read.  M_{s+1} and A_{s+1} do not depend on S and are in
-// flight while step s computes.
+// multiply-adds on fp32 MFMA 16x16x4.  The steps of one slice form a chain, so the slices are
+// 16 columns wide (eight workgroups per head: more chains, each step shorter); wave w owns row
+// tiles 2w, 2w + 1; S^T sits in LDS so every B operand is one 16-byte read.  M_{s+1} and A_{s+1}
+// do not depend on S and are in flight while step s computes.
 constexpr int kCombCols = 16;
 constexpr int kCombSlices = kD / kCombCols;
 
