@@ -205,7 +205,7 @@ struct Prefetch {
 // Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4; upper tiles are zeroed with one
 // 16-byte write per lane.
 template <int C, int DT, int KROW, class TL, bool GT>
-__device__ void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
+__device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
     constexpr int ESZ = DT == 0 ? 2 : 4;
     constexpr int NB = C / 16;
@@ -293,15 +293,29 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
     const uint32_t rstride = static_cast<uint32_t>(Hv) * C * 4;
     const __amdgpu_buffer_rsrc_t tr =
         rsrc(STORE ? Tout + (u.tok0 * Hv + u.hv) * C : nullptr, STORE ? (u.n - 1) * rstride + C * 4 : 0);
+    // With more than four chunks per thread (C = 128), the chunks are read in batches of four
+    // ahead of the batch's T' writes: the compiler cannot move a read above a write to the same
+    // tile, so one chunk at a time would expose every read's latency.
+    constexpr int BATCH = NIT > 4 ? 4 : 1;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
+    for (int b0 = 0; b0 < NIT; b0 += BATCH) {
+    f32x4 vals[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+        const int q = tid + (b0 + j) * kThreads;
+        const int r = q / TCH, c = q % TCH;
+        const bool upper = TL::kTiled && (c >> 2) > (r >> 4);
+        vals[j] = upper ? zero4() : *reinterpret_cast<const f32x4*>(Ts + TL::off(r, 4 * c));
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+        const int it = b0 + j;
         const int q = tid + it * kThreads;
         const int r = q / TCH, c = q % TCH;
         // tile-packed layout: chunks right of the diagonal tile are zeros that are not stored
         const bool upper = TL::kTiled && (c >> 2) > (r >> 4);
         f32x4* chunk = reinterpret_cast<f32x4*>(Ts + TL::off(r, 4 * c));
-        f32x4 val = zero4();
-        if (!upper) val = *chunk;
+        const f32x4 val = vals[j];
         if constexpr (STORE)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, kStream);
         if (PACK && !upper) {
@@ -316,6 +330,7 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
             const u32x2 hp = __builtin_bit_cast(u32x2, h), lp = __builtin_bit_cast(u32x2, l);
             *reinterpret_cast<u32x4*>(chunk) = u32x4{hp[0], hp[1], lp[0], lp[1]};
         }
+    }
     }
 }
 
@@ -398,27 +413,28 @@ __device__ inline void stage_tiles(unsigned char* dst, const bf16x4 (&out)[2][C 
 // The same products at C = 128, split by rows: all 36 lower T' blocks would take 144 registers
 // per lane in every wave, so wave w owns row tiles mA = w and mB = NB - 1 - w (nine T' blocks
 // between them, the same count for every wave) across all eight column tiles.  Accumulator
-// element r of lane 16g + c is X[16m + c][16ni + 4g + r] as above.
-template <int C, int KROW>
-__device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA)[C / 16],
-                                     const u32x4 (&tpB)[C / 16], int mA, int mB, int lr, int lg,
-                                     bf16x4 (&out)[C / 16][2])
+// element r of lane 16g + c is X[16m + c][16ni + 4g + r] as above.  The row tiles are template
+// arguments (one instance per wave, picked by a uniform switch), so the k loops have fixed
+// bounds and no branches: the transposed reads of several k tiles can be in flight together.
+template <int C, int KROW, int MA>
+__device__ inline void wu_tiles_rows_w(const unsigned char* src, const u32x4 (&tpA)[C / 16],
+                                       const u32x4 (&tpB)[C / 16], int lr, int lg, bf16x4 (&out)[C / 16][2])
 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     constexpr int NB = C / 16;
+    constexpr int MB = NB - 1 - MA;
     const __bf16* base = reinterpret_cast<const __bf16*>(src);
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni) {
         f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
-        for (int kt = 0; kt < NB; ++kt) {
-            if (kt > mB) break;  // uniform; mA < mB
+        for (int kt = 0; kt <= MB; ++kt) {
             const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
             const i16x4 kfr = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
             a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpB[kt][0], tpB[kt][1]}), a1, 0, 0, 0);
             a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpB[kt][2], tpB[kt][3]}), a1, 0, 0, 0);
-            if (kt <= mA) {
+            if (kt <= MA) {  // folds away once the loop is unrolled
                 a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpA[kt][0], tpA[kt][1]}), a0, 0, 0, 0);
                 a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpA[kt][2], tpA[kt][3]}), a0, 0, 0, 0);
             }
@@ -431,6 +447,21 @@ __device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA
         }
         out[ni][0] = o0;
         out[ni][1] = o1;
+    }
+}
+
+template <int C, int KROW>
+__device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA)[C / 16],
+                                     const u32x4 (&tpB)[C / 16], int mA, int mB, int lr, int lg,
+                                     bf16x4 (&out)[C / 16][2])
+{
+    static_assert(C / 16 == 2 * kWaves, "one pair of row tiles per wave");
+    (void)mB;  // always C / 16 - 1 - mA
+    switch (mA) {  // uniform: the wave index
+    case 0: wu_tiles_rows_w<C, KROW, 0>(src, tpA, tpB, lr, lg, out); break;
+    case 1: wu_tiles_rows_w<C, KROW, 1>(src, tpA, tpB, lr, lg, out); break;
+    case 2: wu_tiles_rows_w<C, KROW, 2>(src, tpA, tpB, lr, lg, out); break;
+    default: wu_tiles_rows_w<C, KROW, 3>(src, tpA, tpB, lr, lg, out); break;
     }
 }
 
