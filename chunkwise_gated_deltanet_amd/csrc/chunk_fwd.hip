@@ -148,8 +148,7 @@ struct Chunk {
     u32x4 u;
     float g;
 
-    // This wave's Q and W operands (issued separately: the current chunk's copies must be dead
-    // first).
+    // This wave's Q and W operands.
     __device__ void issue_qw(const Params& p, int64_t tok0, int n, int hk, int hv, int tid, bool want_q)
     {
         const uint32_t qstride = static_cast<uint32_t>(p.hq) * kD * 2;

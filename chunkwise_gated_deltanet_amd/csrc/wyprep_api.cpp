@@ -1,5 +1,6 @@
 // C-ABI front end of libwyprep: argument validation (before any HIP call), status codes and
-// the per-thread error text.  The arithmetic lives in wyprep_kernels.hip.
+// the per-thread error text.  The arithmetic lives in the HIP sources (wyprep_kernels.hip,
+// chunk_fwd.hip, wy_backward.hip).
 #include "wyprep.h"
 #include "wyprep_launch.h"
 

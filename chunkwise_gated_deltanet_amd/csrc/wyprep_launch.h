@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front end (wyprep_api.cpp) and the HIP kernels
-// (wyprep_kernels.hip).  Not installed; the public boundary is include/wyprep.h.
+// (wyprep_kernels.hip: preparation; chunk_fwd.hip: chunked forward; wy_backward.hip: backward).
+// Not installed; the public boundary is include/wyprep.h.
 #pragma once
 
 #include <cstdint>
