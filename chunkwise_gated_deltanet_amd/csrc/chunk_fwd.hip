@@ -508,7 +508,11 @@ struct CombineOperands {
 __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
 {
     __shared__ __attribute__((aligned(16))) float St[kCombCols][kD + 4];
-    const int slice = blockIdx.x % kCombSlices, pair = blockIdx.x / kCombSlices;
+    // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous range of items,
+    // so the eight slices of a head read M_s through one L2 (M_s is 64 KB per step).
+    const uint32_t Gsz = gridDim.x;  // pairs x 8, a multiple of 8
+    const int item = static_cast<int>((blockIdx.x & 7u) * (Gsz >> 3) + (blockIdx.x >> 3));
+    const int slice = item % kCombSlices, pair = item / kCombSlices;
     if (pair >= p.num_seqs * p.hv) return;  // uniform
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
