@@ -410,18 +410,59 @@ __device__ inline void stage_tiles(unsigned char* dst, const bf16x4 (&out)[2][C 
             *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + 4 * c) + 4 * lg) = out[c][mi];
 }
 
+// a8' (gated): one packed T' chunk (four hi bf16, four lo bf16; see store_t) rescaled column
+// by column, T' diag(e): hi + lo is T' to within 2^-17 |T'|, the product is rounded once in
+// fp32, and the result is split into a new hi / lo pair the same way store_t splits T'.
+__device__ inline u32x4 scale_chunk(u32x4 c, f32x4 e)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const bf16x4 h = __builtin_bit_cast(bf16x4, u32x2{c[0], c[1]});
+    const bf16x4 l = __builtin_bit_cast(bf16x4, u32x2{c[2], c[3]});
+    bf16x4 h2, l2;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float f = (static_cast<float>(h[k]) + static_cast<float>(l[k])) * e[k];
+        h2[k] = static_cast<__bf16>(f);
+        l2[k] = static_cast<__bf16>(f - static_cast<float>(h2[k]));
+    }
+    const u32x2 hp = __builtin_bit_cast(u32x2, h2), lp = __builtin_bit_cast(u32x2, l2);
+    return u32x4{hp[0], hp[1], lp[0], lp[1]};
+}
+
+// tp_rows' operands of one k step (columns 32 kt + 8 lg .. + 7) rescaled column by column by
+// e^G, T' diag(e^G): hi + lo is rounded once in fp32 and split again, as in scale_chunk
+template <int KROW>
+__device__ inline void scale_rows(const unsigned char* Kraw, u32x4& hi, u32x4& lo, int kt, int lg)
+{
+    const bf16x8 h = __builtin_bit_cast(bf16x8, hi), l = __builtin_bit_cast(bf16x8, lo);
+    bf16x8 h2, l2;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float f = (static_cast<float>(h[q]) + static_cast<float>(l[q])) *
+                        GateRow<KROW, 2>::E(Kraw, 32 * kt + 8 * lg + q);
+        h2[q] = static_cast<__bf16>(f);
+        l2[q] = static_cast<__bf16>(f - static_cast<float>(h2[q]));
+    }
+    hi = __builtin_bit_cast(u32x4, h2);
+    lo = __builtin_bit_cast(u32x4, l2);
+}
+
 // The same products at C = 128, split by rows: all 36 lower T' blocks would take 144 registers
 // per lane in every wave, so wave w owns row tiles mA = w and mB = NB - 1 - w (nine T' blocks
-// between them, the same count for every wave) across all eight column tiles.  Accumulator
-// element r of lane 16g + c is X[16m + c][16ni + 4g + r] as above.  The row tiles are template
-// arguments (one instance per wave, picked by a uniform switch), so the k loops have fixed
-// bounds and no branches: the transposed reads of several k tiles can be in flight together.
+// between them, the same count for every wave) across all eight column tiles.  Here k runs in
+// steps of 32 tokens on 16x16x32 MFMA (twice the k of 16x16x16 at the same issue cost): element
+// j of a lane in group g is token 32 kt + 8 g + j, the K^T / V^T operand is two transposed reads
+// (tokens 8 g .. + 3 and 8 g + 4 .. + 7), and the T' operands are tp[2 kt] (hi) and tp[2 kt + 1]
+// (lo) as tp_rows lays them out.  Accumulator element r of lane 16g + c is
+// X[16m + c][16ni + 4g + r] as above.  The row tiles are template arguments (one instance per
+// wave, picked by a uniform switch), so the k loops have fixed bounds and no branches: several
+// transposed reads can be in flight together.  (Kept outside: the gate rescale of the operands;
+// inside the per-wave instances it raises the register count past two waves per SIMD.)
 template <int C, int KROW, int MA>
 __device__ inline void wu_tiles_rows_w(const unsigned char* src, const u32x4 (&tpA)[C / 16],
                                        const u32x4 (&tpB)[C / 16], int lr, int lg, bf16x4 (&out)[C / 16][2])
 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     constexpr int NB = C / 16;
     constexpr int MB = NB - 1 - MA;
     const __bf16* base = reinterpret_cast<const __bf16*>(src);
@@ -429,14 +470,16 @@ __device__ inline void wu_tiles_rows_w(const unsigned char* src, const u32x4 (&t
     for (int ni = 0; ni < NB; ++ni) {
         f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
-        for (int kt = 0; kt <= MB; ++kt) {
-            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
-            const i16x4 kfr = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
-            a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpB[kt][0], tpB[kt][1]}), a1, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpB[kt][2], tpB[kt][3]}), a1, 0, 0, 0);
-            if (kt <= MA) {  // folds away once the loop is unrolled
-                a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpA[kt][0], tpA[kt][1]}), a0, 0, 0, 0);
-                a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, u32x2{tpA[kt][2], tpA[kt][3]}), a0, 0, 0, 0);
+        for (int kt = 0; kt <= MB / 2; ++kt) {
+            const __bf16* p0 = base + (32 * kt + 8 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
+            const i16x4 f0 = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
+            const i16x4 f1 = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * KROW)));
+            const bf16x8 kfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7));
+            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, __builtin_bit_cast(bf16x8, tpB[2 * kt]), a1, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, __builtin_bit_cast(bf16x8, tpB[2 * kt + 1]), a1, 0, 0, 0);
+            if (kt <= MA / 2) {  // folds away once the loop is unrolled
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, __builtin_bit_cast(bf16x8, tpA[2 * kt]), a0, 0, 0, 0);
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr, __builtin_bit_cast(bf16x8, tpA[2 * kt + 1]), a0, 0, 0, 0);
             }
         }
         bf16x4 o0, o1;
@@ -450,10 +493,34 @@ __device__ inline void wu_tiles_rows_w(const unsigned char* src, const u32x4 (&t
     }
 }
 
+// T' of row tile m as the B operands of the row products above: for lane (lr, lg), tp[2 kt] holds
+// the hi halves and tp[2 kt + 1] the lo halves of row 16 m + lr, columns 32 kt + 8 lg .. + 7, in
+// column order.  Each half of a packed chunk (see store_t) is read straight into its place;
+// columns in 16x16 blocks right of the diagonal read as zero (the tile-packed layout does not
+// store them).
+template <int C, class TL>
+__device__ inline void tp_rows(const float* Ts, int m, int lr, int lg, u32x4 (&tp)[C / 16])
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int kt = 0; kt < C / 32; ++kt) {
+        u32x2 hi[2], lo[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = 32 * kt + 8 * lg + 4 * h;
+            const float* c = Ts + TL::off(16 * m + lr, col);
+            const bool in = (col >> 4) <= m;
+            hi[h] = in ? *reinterpret_cast<const u32x2*>(c) : u32x2{0u, 0u};
+            lo[h] = in ? *reinterpret_cast<const u32x2*>(c + 2) : u32x2{0u, 0u};
+        }
+        tp[2 * kt] = u32x4{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+        tp[2 * kt + 1] = u32x4{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+    }
+}
+
 template <int C, int KROW>
-__device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA)[C / 16],
-                                     const u32x4 (&tpB)[C / 16], int mA, int mB, int lr, int lg,
-                                     bf16x4 (&out)[C / 16][2])
+__device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA)[C / 16], const u32x4 (&tpB)[C / 16],
+                                     int mA, int mB, int lr, int lg, bf16x4 (&out)[C / 16][2])
 {
     static_assert(C / 16 == 2 * kWaves, "one pair of row tiles per wave");
     (void)mB;  // always C / 16 - 1 - mA
@@ -475,25 +542,6 @@ __device__ inline void stage_tiles_rows(unsigned char* dst, const bf16x4 (&out)[
         *reinterpret_cast<bf16x4*>(d + (16 * mA + lr) * KROW + 16 * ni + 4 * lg) = out[ni][0];
         *reinterpret_cast<bf16x4*>(d + (16 * mB + lr) * KROW + 16 * ni + 4 * lg) = out[ni][1];
     }
-}
-
-// a8' (gated): one packed T' chunk (four hi bf16, four lo bf16; see store_t) rescaled column
-// by column, T' diag(e): hi + lo is T' to within 2^-17 |T'|, the product is rounded once in
-// fp32, and the result is split into a new hi / lo pair the same way store_t splits T'.
-__device__ inline u32x4 scale_chunk(u32x4 c, f32x4 e)
-{
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const bf16x4 h = __builtin_bit_cast(bf16x4, u32x2{c[0], c[1]});
-    const bf16x4 l = __builtin_bit_cast(bf16x4, u32x2{c[2], c[3]});
-    bf16x4 h2, l2;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float f = (static_cast<float>(h[k]) + static_cast<float>(l[k])) * e[k];
-        h2[k] = static_cast<__bf16>(f);
-        l2[k] = static_cast<__bf16>(f - static_cast<float>(h2[k]));
-    }
-    const u32x2 hp = __builtin_bit_cast(u32x2, h2), lp = __builtin_bit_cast(u32x2, l2);
-    return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
 // exp(G_j) of the four T' columns 16 kt + 4 lg + 0..3 that one lane's chunks hold.
@@ -520,13 +568,8 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
     if constexpr (GT && NB == 2 * kWaves) {
         const int mA = wave, mB = NB - 1 - wave;
         u32x4 tpA[NB], tpB[NB];
-#pragma unroll
-        for (int kt = 0; kt < NB; ++kt) {
-            tpA[kt] = u32x4{0u, 0u, 0u, 0u};
-            tpB[kt] = u32x4{0u, 0u, 0u, 0u};
-            if (kt <= mA) tpA[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mA + lr, 16 * kt + 4 * lg));
-            if (kt <= mB) tpB[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mB + lr, 16 * kt + 4 * lg));
-        }
+        tp_rows<C, TL>(Ts, mA, lr, lg, tpA);
+        tp_rows<C, TL>(Ts, mB, lr, lg, tpB);
         __syncthreads();  // the T tile is no longer read: V takes its place
         unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
         pf.commit_v(Vraw, tid);
@@ -536,11 +579,10 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
         __syncthreads();  // every wave is done reading V: U is staged over it
         stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, lr, lg);
 #pragma unroll
-        for (int kt = 0; kt < NB; ++kt) {
-            if (kt > mB) continue;  // uniform; the zero chunks above the diagonal stay zero
-            const f32x4 e = gate_cols<KROW>(Kraw, kt, lg);
-            if (kt <= mA) tpA[kt] = scale_chunk(tpA[kt], e);
-            tpB[kt] = scale_chunk(tpB[kt], e);
+        for (int kt = 0; kt < NB / 2; ++kt) {
+            if (2 * kt > mB) continue;  // uniform; a k step wholly right of the diagonal stays zero
+            if (2 * kt <= mA) scale_rows<KROW>(Kraw, tpA[2 * kt], tpA[2 * kt + 1], kt, lg);
+            scale_rows<KROW>(Kraw, tpB[2 * kt], tpB[2 * kt + 1], kt, lg);
         }
         wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, mA, mB, lr, lg, out);
         __syncthreads();  // every wave is done reading K: W is staged over it
@@ -578,13 +620,8 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
     } else if constexpr (NB == 2 * kWaves) {
         const int mA = wave, mB = NB - 1 - wave;
         u32x4 tpA[NB], tpB[NB];
-#pragma unroll
-        for (int kt = 0; kt < NB; ++kt) {
-            tpA[kt] = u32x4{0u, 0u, 0u, 0u};
-            tpB[kt] = u32x4{0u, 0u, 0u, 0u};
-            if (kt <= mA) tpA[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mA + lr, 16 * kt + 4 * lg));
-            if (kt <= mB) tpB[kt] = *reinterpret_cast<const u32x4*>(Ts + TL::off(16 * mB + lr, 16 * kt + 4 * lg));
-        }
+        tp_rows<C, TL>(Ts, mA, lr, lg, tpA);
+        tp_rows<C, TL>(Ts, mB, lr, lg, tpB);
         __syncthreads();  // the T tile is no longer read: V takes its place
         unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
         pf.commit_v(Vraw, tid);
