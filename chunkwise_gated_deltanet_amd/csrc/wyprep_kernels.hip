@@ -26,10 +26,11 @@
 //       first product's accumulator feeding the second as its B operand ([Inv] 2.2, 3.5);
 //   a7  store T (fp32; upper triangle 0, diagonal 1), then overwrite the T tile in place with
 //       T' = T diag(beta) as a hi + lo pair of bf16 values;
-//   a8  W^T = K^T T'^T and U^T = V^T T'^T on 16x16x16 bf16 MFMA, hi and lo parts of T'
-//       accumulated in turn (T' is lower triangular, so k-tiles right of the diagonal are
-//       skipped); the transposed accumulators hold four consecutive output columns per lane,
-//       staged in LDS and stored with 16-byte writes.
+//   a8  W^T = K^T T'^T and U^T = V^T T'^T on bf16 MFMA (16x16x16; 16x16x32 at C = 128, where
+//       each wave owns two row tiles), hi and lo parts of T' accumulated in turn (T' is lower
+//       triangular, so k-tiles right of the diagonal are skipped); the transposed accumulators
+//       hold four consecutive output columns per lane, staged in LDS and stored with 16-byte
+//       writes.
 // Gated instances ([Inv] section 5, item 12: with gating the coefficient is
 // diag(beta)(Gamma o K K^T); g [B,T,Hv] is the per-token log gate of [QLA] usage) also read g:
 //   a1' wave 0 forms the chunk-local inclusive prefix sums G_i = g_0 + ... + g_i in fp64 (one
@@ -213,8 +214,9 @@ __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw,
     constexpr int PER = (NTILE + kWaves - 1) / kWaves;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    // Operands are loaded tile by tile: with four workgroups per CU, other waves cover the
-    // LDS latency, and a second operand buffer would cost 32 registers.
+    // Operands are loaded tile by tile: other resident workgroups cover the LDS latency.  A
+    // second operand buffer costs 32 registers and measured no faster even at C = 128, where
+    // only two workgroups share a CU.
     constexpr int NBUF = 1;
     GramFrags<DT, KROW> f[NBUF];
     int I = 0, J = 0;
