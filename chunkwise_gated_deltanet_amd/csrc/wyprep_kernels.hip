@@ -202,9 +202,78 @@ struct Prefetch {
     }
 };
 
+// a3 for one lower tile (I, J) of the Gram accumulator acc (element r of lane 16 lg + lr is
+// G[16 I + 4 lg + r][16 J + lr]): A below the diagonal, 1 on it.  Diagonal tiles keep L^T in
+// their upper triangle (G is symmetric, so entry (i, j), i < j, is beta_j G[j][i] = L[j][i]);
+// the substitution reads columns of L there and overwrites it with zeros.
+template <int KROW, int ESZ, class TL, bool GT>
+__device__ __attribute__((always_inline)) void a_tile_out(const f32x4& acc, const unsigned char* Kraw, float* Ts,
+                                                          const float* bs, int I, int J, int lr, int lg)
+{
+    const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
+    const float bcol = bs[16 * J + lr];
+    double gcol = 0.0;
+    if constexpr (GT) gcol = GateRow<KROW, ESZ>::G(Kraw, 16 * J + lr);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
+        float a = acc[r];
+        if constexpr (GT) {
+            // a3': decay Gamma between the later and the earlier token of the pair
+            const double d = GateRow<KROW, ESZ>::G(Kraw, i) - gcol;
+            a *= __expf(static_cast<float>(i > j ? d : -d));
+        }
+        Ts[TL::off(i, j)] = (i > j) ? bet[r] * a : (i == j ? 1.f : bcol * a);
+    }
+}
+
+// a2 + a3 at C = 128 (bf16 K, ungated): wave w forms the lower tiles of row blocks w and 7 - w,
+// nine tiles for every wave.  The K fragments of its two row blocks are read once, and each
+// column block's once for both rows, so a unit reads 26 blocks of 16 K rows from LDS instead of
+// the 72 that tile-by-tile products read (both blocks of every tile).  The gated instance keeps
+// the tile-by-tile order: with this one it needs 226 VGPRs, one workgroup per CU.
+template <int C, int KROW, class TL, bool GT, int MA>
+__device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char* Kraw, float* Ts, const float* bs,
+                                                             int lr, int lg)
+{
+    constexpr int NB = C / 16;
+    constexpr int MB = NB - 1 - MA;
+    constexpr int NS = kD / 32;
+    const __bf16* K = reinterpret_cast<const __bf16*>(Kraw);
+    // fragment of row block `blk`: lane 16 g + c holds row 16 blk + c, dk 32 s + 8 g .. + 7
+    auto frag = [&](int blk, bf16x8 (&f)[NS]) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) f[s] = *reinterpret_cast<const bf16x8*>(K + (16 * blk + lr) * KROW + 32 * s + 8 * lg);
+    };
+    auto tile = [&](const bf16x8 (&fi)[NS], const bf16x8 (&fj)[NS], int I, int J) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fi[s], fj[s], acc, 0, 0, 0);
+        a_tile_out<KROW, 2, TL, GT>(acc, Kraw, Ts, bs, I, J, lr, lg);
+    };
+    bf16x8 fa[NS], fb[NS];
+    frag(MA, fa);
+    frag(MB, fb);
+#pragma unroll
+    for (int J = 0; J <= MB; ++J) {  // unrolled: every test on J below is resolved at compile time
+        bf16x8 fj[NS];
+        if (J == MA) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) fj[s] = fa[s];
+        } else if (J == MB) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) fj[s] = fb[s];
+        } else {
+            frag(J, fj);
+        }
+        if (J <= MA) tile(fa, fj, MA, J);
+        tile(fb, fj, MB, J);
+    }
+}
+
 // a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts; all C x C entries are written.
-// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4; upper tiles are zeroed with one
-// 16-byte write per lane.
+// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4 (ungated at C = 128 with bf16 K: by
+// row blocks, form_a_rows_w); upper tiles are zeroed with one 16-byte write per lane.
 template <int C, int DT, int KROW, class TL, bool GT>
 __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
@@ -214,6 +283,16 @@ __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw,
     constexpr int PER = (NTILE + kWaves - 1) / kWaves;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
+    if constexpr (C == 128 && DT == 0 && TL::kTiled && !GT) {
+        static_assert(NB == 2 * kWaves, "one pair of row blocks per wave");
+        switch (wave) {  // uniform
+        case 0: form_a_rows_w<C, KROW, TL, GT, 0>(Kraw, Ts, bs, lr, lg); break;
+        case 1: form_a_rows_w<C, KROW, TL, GT, 1>(Kraw, Ts, bs, lr, lg); break;
+        case 2: form_a_rows_w<C, KROW, TL, GT, 2>(Kraw, Ts, bs, lr, lg); break;
+        default: form_a_rows_w<C, KROW, TL, GT, 3>(Kraw, Ts, bs, lr, lg); break;
+        }
+        return;  // the tile-packed layout stores no upper tiles
+    }
     // Operands are loaded tile by tile: other resident workgroups cover the LDS latency.  A
     // second operand buffer costs 32 registers and measured no faster even at C = 128, where
     // only two workgroups share a CU.
@@ -235,25 +314,7 @@ __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw,
             f[(tt + 1) % NBUF].load(Kraw, In, Jn, lr, lg);
         }
         if (NBUF == 1 && tt > 0) f[0].load(Kraw, I, J, lr, lg);
-        const f32x4 acc = f[tt % NBUF].product();
-        const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
-        const float bcol = bs[16 * J + lr];
-        double gcol = 0.0;
-        if constexpr (GT) gcol = GateRow<KROW, ESZ>::G(Kraw, 16 * J + lr);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // Diagonal tiles keep L^T in their upper triangle (G is symmetric, so entry (i, j),
-            // i < j, is beta_j G[j][i] = L[j][i]); the substitution reads columns of L there
-            // and overwrites it with zeros.
-            const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
-            float a = acc[r];
-            if constexpr (GT) {
-                // a3': decay Gamma between the later and the earlier token of the pair
-                const double d = GateRow<KROW, ESZ>::G(Kraw, i) - gcol;
-                a *= __expf(static_cast<float>(i > j ? d : -d));
-            }
-            Ts[TL::off(i, j)] = (i > j) ? bet[r] * a : (i == j ? 1.f : bcol * a);
-        }
+        a_tile_out<KROW, ESZ, TL, GT>(f[tt % NBUF].product(), Kraw, Ts, bs, I, J, lr, lg);
         if (NBUF == 2) {
             I = In;
             J = Jn;
