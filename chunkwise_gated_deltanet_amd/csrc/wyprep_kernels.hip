@@ -360,21 +360,41 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
     // ahead of the batch's T' writes: the compiler cannot move a read above a write to the same
     // tile, so one chunk at a time would expose every read's latency.
     constexpr int BATCH = NIT > 4 ? 4 : 1;
+    // Chunk (row r, 16-byte column chunk c) of thread tid in iteration it.  Row-major tiles: 16
+    // consecutive lanes take 16 consecutive chunks of one row, 64 distinct banks.  The
+    // tile-packed layout puts the tiles of a row 320 floats apart, on the same banks, so there
+    // one wave-wide access covers rows 16 I + rb + {0, 4, 8, 12} and tiles Jb .. Jb + 3 instead:
+    // each 16 lanes read one tile's four rows at 20-float pitch (disjoint banks), and every row
+    // still gets 256 contiguous bytes of the global store.
+    auto chunk_of = [&](int it, int* r, int* c) {
+        const int q = tid + it * kThreads;
+        if constexpr (TL::kTiled) {
+            static_assert(C == 128, "tile-packed T is used at C = 128 only");
+            const int n = it * kWaves + (tid >> 6), lane = tid & 63;  // n: which wave-wide access
+            // the half of the row (tiles 0-3 or 4-7) alternates with I, so every wave gets as
+            // many tiles right of the diagonal (reads and T' writes skipped) as the others
+            const int I = n >> 3, rb = (n >> 1) & 3, jb = 4 * ((n ^ I) & 1);
+            *r = 16 * I + rb + 4 * ((lane >> 2) & 3);
+            *c = 4 * (jb + (lane >> 4)) + (lane & 3);
+        } else {
+            *r = q / TCH;
+            *c = q % TCH;
+        }
+    };
 #pragma unroll
     for (int b0 = 0; b0 < NIT; b0 += BATCH) {
     f32x4 vals[BATCH];
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-        const int q = tid + (b0 + j) * kThreads;
-        const int r = q / TCH, c = q % TCH;
+        int r, c;
+        chunk_of(b0 + j, &r, &c);
         const bool upper = TL::kTiled && (c >> 2) > (r >> 4);
         vals[j] = upper ? zero4() : *reinterpret_cast<const f32x4*>(Ts + TL::off(r, 4 * c));
     }
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-        const int it = b0 + j;
-        const int q = tid + it * kThreads;
-        const int r = q / TCH, c = q % TCH;
+        int r, c;
+        chunk_of(b0 + j, &r, &c);
         // tile-packed layout: chunks right of the diagonal tile are zeros that are not stored
         const bool upper = TL::kTiled && (c >> 2) > (r >> 4);
         f32x4* chunk = reinterpret_cast<f32x4*>(Ts + TL::off(r, 4 * c));
