@@ -835,15 +835,24 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     pf.commit_k(Kraw, bs, tid);
     __syncthreads();
     // This unit's V is needed only after its inversion; the next unit's K at the next unit's
-    // start.  Issued in that order, a wait for either never waits for the other.
+    // start.  Issued in that order, a wait for either never waits for the other.  At C = 128 the
+    // unit's chain, not HBM, sets the pace: the next K is issued after the diagonal inversions
+    // (which two of the four waves run), not right behind V, where the two compete for the
+    // CU's address units (3-4% faster at B=4 T=4096 H=32; at C <= 64 it stays here, in flight
+    // as long as possible).
     pf.issue_v(p, cur, tid);
     const Unit nxt = map_unit<C>(p, info, next, tid);
-    if (nxt.n > 0) pf.issue_k(p, nxt, tid);
+    if constexpr (C != 128) {
+        if (nxt.n > 0) pf.issue_k(p, nxt, tid);
+    }
 
     using TL = typename L::TL;
     form_a<C, DT, L::KROW, TL, GT>(Kraw, Ts, bs, tid);
     __syncthreads();
     invert_diagonal_blocks<C, TL>(Ts, tid);
+    if constexpr (C == 128) {
+        if (nxt.n > 0) pf.issue_k(p, nxt, tid);
+    }
     __syncthreads();
     if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
     if constexpr (C >= 64) coupling_level<C, 32, TL>(Ts, tid);
