@@ -227,11 +227,11 @@ __device__ __attribute__((always_inline)) void a_tile_out(const f32x4& acc, cons
     }
 }
 
-// a2 + a3 at C = 128 (bf16 K, ungated): wave w forms the lower tiles of row blocks w and 7 - w,
-// nine tiles for every wave.  The K fragments of its two row blocks are read once, and each
-// column block's once for both rows, so a unit reads 26 blocks of 16 K rows from LDS instead of
-// the 72 that tile-by-tile products read (both blocks of every tile).  The gated instance keeps
-// the tile-by-tile order: with this one it needs 226 VGPRs, one workgroup per CU.
+// a2 + a3 at C = 128 (bf16 K): wave w forms the lower tiles of row blocks w and 7 - w, nine
+// tiles for every wave, one row block after the other.  A row block's K fragments are read once
+// for all its tiles, so a unit reads 36 blocks of 16 K rows from LDS instead of the 72 that
+// tile-by-tile products read (both blocks of every tile).  Sharing the column blocks between the
+// two rows as well (26 reads) measured no faster and holds 16 more registers.
 template <int C, int KROW, class TL, bool GT, int MA>
 __device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char* Kraw, float* Ts, const float* bs,
                                                              int lr, int lg)
@@ -250,30 +250,32 @@ __device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fi[s], fj[s], acc, 0, 0, 0);
         a_tile_out<KROW, 2, TL, GT>(acc, Kraw, Ts, bs, I, J, lr, lg);
+        // gated: the fp64 gates each tile's decay reads would otherwise be hoisted out of the
+        // unrolled tiles and held all at once
+        if constexpr (GT) __builtin_amdgcn_sched_barrier(0);
     };
-    bf16x8 fa[NS], fb[NS];
-    frag(MA, fa);
-    frag(MB, fb);
+    // one row block at a time, so only its fragments and one column block's are live
+    auto row = [&](int I) {
+        bf16x8 fi[NS];
+        frag(I, fi);
 #pragma unroll
-    for (int J = 0; J <= MB; ++J) {  // unrolled: every test on J below is resolved at compile time
-        bf16x8 fj[NS];
-        if (J == MA) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) fj[s] = fa[s];
-        } else if (J == MB) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) fj[s] = fb[s];
-        } else {
-            frag(J, fj);
+        for (int J = 0; J <= I; ++J) {  // unrolled: J == I is resolved at compile time
+            if (J == I) {
+                tile(fi, fi, I, J);
+            } else {
+                bf16x8 fj[NS];
+                frag(J, fj);
+                tile(fi, fj, I, J);
+            }
         }
-        if (J <= MA) tile(fa, fj, MA, J);
-        tile(fb, fj, MB, J);
-    }
+    };
+    row(MA);
+    row(MB);
 }
 
 // a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts; all C x C entries are written.
-// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4 (ungated at C = 128 with bf16 K: by
-// row blocks, form_a_rows_w); upper tiles are zeroed with one 16-byte write per lane.
+// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4 (at C = 128 with bf16 K: by row
+// blocks, form_a_rows_w); upper tiles are zeroed with one 16-byte write per lane.
 template <int C, int DT, int KROW, class TL, bool GT>
 __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
@@ -283,7 +285,7 @@ __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw,
     constexpr int PER = (NTILE + kWaves - 1) / kWaves;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    if constexpr (C == 128 && DT == 0 && TL::kTiled && !GT) {
+    if constexpr (C == 128 && DT == 0 && TL::kTiled) {
         static_assert(NB == 2 * kWaves, "one pair of row blocks per wave");
         switch (wave) {  // uniform
         case 0: form_a_rows_w<C, KROW, TL, GT, 0>(Kraw, Ts, bs, lr, lg); break;
