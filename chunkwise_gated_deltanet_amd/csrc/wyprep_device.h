@@ -234,32 +234,31 @@ struct GramFrags {
     }
 };
 
-// Step J of the right-looking substitution for lane (block, column i): X[J][i] is final
-// (1 for J = i, else -acc[J]; acc holds the negated partial sums, exactly +0 above i), it is
+// The right-looking substitution for lane (block, column i).  At step J, X[J][i] is final (1
+// for J = i, else -acc[J]; acc holds the negated partial sums, exactly +0 above i), it is
 // written back, and every later row k takes acc[k] -= L[k][J] X[J][i].  L[k][J] for k > J is
-// read from row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the
-// block read the same row (an LDS broadcast).  Row J's upper part is read before any lane
-// overwrites it with its X column.
-template <int J, int RS>
-__device__ inline void substitution_step(float (&acc)[16], int i, float* blk)
+// row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the block read
+// the same row (an LDS broadcast).  Row J is written only at step J, after it has been read, so
+// each row is read two steps ahead, before the writes of the rows in between: its LDS latency
+// then overlaps two steps of multiply-adds instead of sitting on the chain.
+template <int RS>
+__device__ __attribute__((always_inline)) void substitute(float (&acc)[16], int i, float* blk)
 {
-    const float x = (J == i) ? 1.f : acc[J];
-    float lrow[16];
-    if constexpr (J < 15) {
+    f32x4 rows[3][4];  // rows[J % 3][c4]: chunks c4 >= (J + 1) / 4 of row J
+    auto load_row = [&](int J, f32x4 (&r)[4]) {
 #pragma unroll
-        for (int c4 = (J + 1) / 4; c4 < 4; ++c4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(blk + J * RS + 4 * c4);
-            lrow[4 * c4 + 0] = v[0];
-            lrow[4 * c4 + 1] = v[1];
-            lrow[4 * c4 + 2] = v[2];
-            lrow[4 * c4 + 3] = v[3];
-        }
-    }
-    blk[J * RS + i] = x;
-    if constexpr (J < 15) {
+        for (int c4 = 0; c4 < 4; ++c4)
+            if (c4 >= (J + 1) / 4) r[c4] = *reinterpret_cast<const f32x4*>(blk + J * RS + 4 * c4);
+    };
+    load_row(0, rows[0]);
+    load_row(1, rows[1]);
 #pragma unroll
-        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-lrow[k], x, acc[k]);
-        substitution_step<J + 1, RS>(acc, i, blk);
+    for (int J = 0; J < 16; ++J) {  // unrolled: every index below is a compile-time constant
+        if (J + 2 < 15) load_row(J + 2, rows[(J + 2) % 3]);
+        const float x = (J == i) ? 1.f : acc[J];
+        blk[J * RS + i] = x;
+#pragma unroll
+        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-rows[J % 3][k / 4][k % 4], x, acc[k]);
     }
 }
 
@@ -277,7 +276,7 @@ __device__ void invert_diagonal_blocks(float* Ts, int tid)
     float acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] = 0.f;
-    substitution_step<0, TL::RS>(acc, i, blk);
+    substitute<TL::RS>(acc, i, blk);
 }
 
 // a6, one level: block size S.  Pair p covers rows/cols [2Sp, 2Sp + 2S); its sub-diagonal
