@@ -90,16 +90,20 @@ def test_orthogonal_keys(C, gpu):
     compare_full(inp, T, W, U, label=f"orthogonal C={C}")
 
 
-def test_identical_keys(gpu):
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_identical_keys(C, gpu):
+    """Every key the same unit vector: the densest T (no zero entry below the diagonal), at
+    each chunk size's own block and coupling layout."""
     rng = np.random.default_rng(62)
     k = rng.standard_normal(128).astype(np.float32)
     k /= np.linalg.norm(k)
-    K = np.repeat(k[None, None, :], 64, axis=0)
-    V = rng.standard_normal((64, 1, 128)).astype(np.float32)
-    beta = rng.uniform(0.0, 1.0, (64, 1)).astype(np.float32)
-    inp = make_inp(K, V, beta, 64)
+    K = np.repeat(k[None, None, :], C, axis=0)
+    V = rng.standard_normal((C, 1, 128)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (C, 1)).astype(np.float32)
+    inp = make_inp(K, V, beta, C)
+    say(f"identical keys C={C}")
     T, W, U = run_wy(inp, gpu)
-    compare_full(inp, T, W, U, label="identical keys")
+    compare_full(inp, T, W, U, label=f"identical keys C={C}")
 
 
 def test_head_grouping(gpu):
