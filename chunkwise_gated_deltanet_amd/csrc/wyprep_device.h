@@ -239,33 +239,36 @@ struct GramFrags {
 // written back, and every later row k takes acc[k] -= L[k][J] X[J][i].  L[k][J] for k > J is
 // row J of the block's upper triangle, where form_a left L^T; all 16 lanes of the block read
 // the same row (an LDS broadcast).  Row J is written only at step J, after it has been read, so
-// each row is read two steps ahead, before the writes of the rows in between: its LDS latency
-// then overlaps two steps of multiply-adds instead of sitting on the chain.
-template <int RS>
+// each row can be read D steps ahead, before the writes of the rows in between: its LDS latency
+// then overlaps D steps of multiply-adds instead of sitting on the chain (D = 0: read at its
+// own step).
+template <int RS, int D>
 __device__ __attribute__((always_inline)) void substitute(float (&acc)[16], int i, float* blk)
 {
-    f32x4 rows[3][4];  // rows[J % 3][c4]: chunks c4 >= (J + 1) / 4 of row J
+    f32x4 rows[D + 1][4];  // rows[J % (D + 1)][c4]: chunks c4 >= (J + 1) / 4 of row J
     auto load_row = [&](int J, f32x4 (&r)[4]) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
             if (c4 >= (J + 1) / 4) r[c4] = *reinterpret_cast<const f32x4*>(blk + J * RS + 4 * c4);
     };
-    load_row(0, rows[0]);
-    load_row(1, rows[1]);
+#pragma unroll
+    for (int J = 0; J < D; ++J) load_row(J, rows[J]);
 #pragma unroll
     for (int J = 0; J < 16; ++J) {  // unrolled: every index below is a compile-time constant
-        if (J + 2 < 15) load_row(J + 2, rows[(J + 2) % 3]);
+        if (J + D < 15) load_row(J + D, rows[(J + D) % (D + 1)]);
         const float x = (J == i) ? 1.f : acc[J];
         blk[J * RS + i] = x;
 #pragma unroll
-        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-rows[J % 3][k / 4][k % 4], x, acc[k]);
+        for (int k = J + 1; k < 16; ++k) acc[k] = __builtin_fmaf(-rows[J % (D + 1)][k / 4][k % 4], x, acc[k]);
     }
 }
 
 // a5: invert the C/16 diagonal 16x16 blocks of Ts in place.  Lane (block b, column i) keeps
 // column i of X_b = L_b^{-1} in registers, right-looking: after X[j][i] is final, every later
 // row k takes its share L[k][j] X[j][i], so one multiply-add per step sits on the dependency
-// chain.  Blocks 0-3 run on wave 0, blocks 4-7 on wave 1.
+// chain.  Blocks 0-3 run on wave 0, blocks 4-7 on wave 1.  Rows are read two steps ahead from
+// C = 64 on; at C = 32 the 32 extra registers would cost resident workgroups (seven to five per
+// CU), which the T-only step at C = 32 needs more than the shorter chain.
 template <int C, class TL>
 __device__ void invert_diagonal_blocks(float* Ts, int tid)
 {
@@ -276,7 +279,7 @@ __device__ void invert_diagonal_blocks(float* Ts, int tid)
     float acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] = 0.f;
-    substitute<TL::RS>(acc, i, blk);
+    substitute<TL::RS, (C >= 64 ? 2 : 0)>(acc, i, blk);
 }
 
 // a6, one level: block size S.  Pair p covers rows/cols [2Sp, 2Sp + 2S); its sub-diagonal

@@ -122,11 +122,13 @@ struct Prefetch {
         const int hk = u.hv / (p.hv / p.hq);
         const uint32_t kstride = static_cast<uint32_t>(p.hq) * kD * ESZ;
         const __amdgpu_buffer_rsrc_t kr = rows(p.k, u, p.hq, hk);
+        // thread tid takes row tid / CPR + it * (kThreads / CPR), chunk tid % CPR: one multiply
+        // per thread, then a scalar step per iteration (all of it in the range-checked offset)
+        const uint32_t koff = (tid / CPR) * kstride + (tid % CPR) * 16;
+        const uint32_t kstep = (kThreads / CPR) * kstride;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int q = tid + it * kThreads;
-            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q / CPR) * kstride + (q % CPR) * 16, 0, 0);
-        }
+        for (int it = 0; it < NIT; ++it)
+            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + it * kstep, 0, 0);
         const __amdgpu_buffer_rsrc_t br =
             rsrc(p.beta + u.tok0 * p.hv + u.hv, ((u.n - 1) * p.hv + 1) * 4);
         b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (tid % C) * p.hv * 4, 0, 0));
@@ -148,11 +150,11 @@ struct Prefetch {
         if constexpr (WU) {
             const uint32_t vstride = static_cast<uint32_t>(p.hv) * kD * ESZ;
             const __amdgpu_buffer_rsrc_t vr = rows(p.v, u, p.hv, u.hv);
+            const uint32_t voff = (tid / CPR) * vstride + (tid % CPR) * 16;
+            const uint32_t vstep = (kThreads / CPR) * vstride;
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                const int q = tid + it * kThreads;
-                v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, (q / CPR) * vstride + (q % CPR) * 16, 0, kStream);
-            }
+            for (int it = 0; it < NIT; ++it)
+                v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + it * vstep, 0, kStream);
         }
     }
 
@@ -368,20 +370,31 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
     // one wave-wide access covers rows 16 I + rb + {0, 4, 8, 12} and tiles Jb .. Jb + 3 instead:
     // each 16 lanes read one tile's four rows at 20-float pitch (disjoint banks), and every row
     // still gets 256 contiguous bytes of the global store.
+    // Wave-wide access n = 4 it + w (w the wave) covers, in the tile-packed layout, row block
+    // I = n / 8 = it / 2, rows rb = (n / 2) mod 4 = 2 (it mod 2) + w / 2 plus {0, 4, 8, 12}, tiles
+    // jb .. jb + 3; the half of the row (tiles 0-3 or 4-7) alternates with I, so every wave gets
+    // as many tiles right of the diagonal (reads and T' writes skipped) as the others.  Written
+    // with I and the row step known at compile time, every offset is a per-thread base plus a
+    // scalar: no per-chunk multiply.
+    const int wv = tid >> 6, lane = tid & 63;
     auto chunk_of = [&](int it, int* r, int* c) {
-        const int q = tid + it * kThreads;
         if constexpr (TL::kTiled) {
-            static_assert(C == 128, "tile-packed T is used at C = 128 only");
-            const int n = it * kWaves + (tid >> 6), lane = tid & 63;  // n: which wave-wide access
-            // the half of the row (tiles 0-3 or 4-7) alternates with I, so every wave gets as
-            // many tiles right of the diagonal (reads and T' writes skipped) as the others
-            const int I = n >> 3, rb = (n >> 1) & 3, jb = 4 * ((n ^ I) & 1);
-            *r = 16 * I + rb + 4 * ((lane >> 2) & 3);
+            static_assert(C == 128 && kWaves == 4, "tile-packed T is used at C = 128 only");
+            const int I = it >> 1, jb = 4 * ((wv ^ I) & 1);
+            *r = 16 * I + 2 * (it & 1) + (wv >> 1) + 4 * ((lane >> 2) & 3);
             *c = 4 * (jb + (lane >> 4)) + (lane & 3);
         } else {
-            *r = q / TCH;
-            *c = q % TCH;
+            *r = tid / TCH + it * (kThreads / TCH);
+            *c = tid % TCH;
         }
+    };
+    // global byte offset of chunk (r, c) of iteration it, without a per-chunk multiply
+    const uint32_t rowbase = TL::kTiled ? static_cast<uint32_t>((wv >> 1) + 4 * ((lane >> 2) & 3)) * rstride
+                                        : static_cast<uint32_t>(tid / TCH) * rstride;
+    auto store_off = [&](int it, int c) -> uint32_t {
+        const uint32_t rstep = TL::kTiled ? static_cast<uint32_t>(16 * (it >> 1) + 2 * (it & 1))
+                                          : static_cast<uint32_t>(it * (kThreads / TCH));
+        return rowbase + rstep * rstride + static_cast<uint32_t>(c) * 16;
     };
 #pragma unroll
     for (int b0 = 0; b0 < NIT; b0 += BATCH) {
@@ -402,7 +415,7 @@ __device__ void store_t(float* Ts, const float* bs, float* Tout, const Unit& u, 
         f32x4* chunk = reinterpret_cast<f32x4*>(Ts + TL::off(r, 4 * c));
         const f32x4 val = vals[j];
         if constexpr (STORE)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, r * rstride + c * 16, 0, kStream);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), tr, store_off(b0 + j, c), 0, kStream);
         if (PACK && !upper) {
             const f32x4 b = *reinterpret_cast<const f32x4*>(bs + 4 * c);
             bf16x4 h, l;
@@ -429,12 +442,14 @@ __device__ void store_rows(const unsigned char* src, void* out, const Unit& u, i
     const uint32_t rstride = static_cast<uint32_t>(Hv) * kD * ESZ;
     const __amdgpu_buffer_rsrc_t r_out = rsrc(static_cast<unsigned char*>(out) + (u.tok0 * Hv + u.hv) * (kD * ESZ),
                                               (u.n - 1) * rstride + kD * ESZ);
+    // one multiply per thread, then a scalar row step per iteration
+    const uint32_t off = (tid / CPR) * rstride + (tid % CPR) * 16, step = (kThreads / CPR) * rstride;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int q = tid + it * kThreads;
         const int r = q / CPR, c16 = q % CPR;
         const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * (KROW * ESZ) + c16 * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(val, r_out, r * rstride + c16 * 16, 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b128(val, r_out, off + it * step, 0, kStream);
     }
 }
 
