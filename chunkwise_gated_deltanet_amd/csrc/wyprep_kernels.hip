@@ -26,8 +26,8 @@
 //       first product's accumulator feeding the second as its B operand ([Inv] 2.2, 3.5);
 //   a7  store T (fp32; upper triangle 0, diagonal 1), then overwrite the T tile in place with
 //       T' = T diag(beta) as a hi + lo pair of bf16 values;
-//   a8  W^T = K^T T'^T and U^T = V^T T'^T on bf16 MFMA (16x16x16; 16x16x32 at C = 128, where
-//       each wave owns two row tiles), hi and lo parts of T' accumulated in turn (T' is lower
+//   a8  W^T = K^T T'^T and U^T = V^T T'^T on bf16 MFMA (16x16x16 at C = 32; from C = 64 on
+//       16x16x32, each wave owning two row tiles), hi and lo parts of T' accumulated in turn (T' is lower
 //       triangular, so k-tiles right of the diagonal are skipped); the transposed accumulators
 //       hold four consecutive output columns per lane, staged in LDS and stored with 16-byte
 //       writes.
@@ -461,7 +461,8 @@ __device__ void store_rows(const unsigned char* src, void* out, const Unit& u, i
 // column) is one LDS transpose read: within each 16-lane group, lane i of ds_read_tr16_b64
 // receives element (i mod 4) of the 64-bit rows addressed by lanes 4e + i/4, e = 0..3.  Wave w
 // owns column tiles w and w + 4 of W, then of U.  Accumulator element r of lane 16g + c is
-// X[16mi + c][16ni + 4g + r]; the result leaves as bf16.
+// X[16mi + c][16ni + 4g + r]; the result leaves as bf16.  Used at C = 32 (and for fp32 inputs,
+// whose path has its own products); from C = 64 on the row products below take over.
 template <int C, int KROW>
 __device__ inline void wu_tiles(const unsigned char* src, const u32x4 (&tp)[C / 16][C / 16], int wave,
                                 int lr, int lg, bf16x4 (&out)[2][C / 16])
@@ -547,9 +548,12 @@ __device__ inline void scale_rows(const unsigned char* Kraw, u32x4& hi, u32x4& l
     lo = __builtin_bit_cast(u32x4, l2);
 }
 
-// The same products at C = 128, split by rows: all 36 lower T' blocks would take 144 registers
-// per lane in every wave, so wave w owns row tiles mA = w and mB = NB - 1 - w (nine T' blocks
-// between them, the same count for every wave) across all eight column tiles.  Here k runs in
+// The same products split by rows, from C = 64 on.  At C = 128 all 36 lower T' blocks would take
+// 144 registers per lane in every wave, so wave w owns row tiles mA = w and mB = NB - 1 - w (nine
+// T' blocks between them, the same count for every wave) across all eight column tiles.  At
+// C = 64 waves w and w + 2 own row tiles w and 3 - w (five blocks) and split the column tiles:
+// each wave holds half the T' blocks of the all-blocks form and, gated, rescales only those
+// (gated C = 64 7% faster, ungated unchanged).  Here k runs in
 // steps of 32 tokens on 16x16x32 MFMA (twice the k of 16x16x16 at the same issue cost): element
 // j of a lane in group g is token 32 kt + 8 g + j, the K^T / V^T operand is two transposed reads
 // (tokens 8 g .. + 3 and 8 g + 4 .. + 7), and the T' operands are tp[2 kt] (hi) and tp[2 kt + 1]
@@ -558,16 +562,16 @@ __device__ inline void scale_rows(const unsigned char* Kraw, u32x4& hi, u32x4& l
 // wave, picked by a uniform switch), so the k loops have fixed bounds and no branches: several
 // transposed reads can be in flight together.  (Kept outside: the gate rescale of the operands;
 // inside the per-wave instances it raises the register count past two waves per SIMD.)
-template <int C, int KROW, int MA>
+template <int C, int KROW, int MA, int NI0, int NNI>
 __device__ inline void wu_tiles_rows_w(const unsigned char* src, const u32x4 (&tpA)[C / 16],
-                                       const u32x4 (&tpB)[C / 16], int lr, int lg, bf16x4 (&out)[C / 16][2])
+                                       const u32x4 (&tpB)[C / 16], int lr, int lg, bf16x4 (&out)[NNI][2])
 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     constexpr int NB = C / 16;
     constexpr int MB = NB - 1 - MA;
     const __bf16* base = reinterpret_cast<const __bf16*>(src);
 #pragma unroll
-    for (int ni = 0; ni < NB; ++ni) {
+    for (int ni = NI0; ni < NI0 + NNI; ++ni) {
         f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
         for (int kt = 0; kt <= MB / 2; ++kt) {
@@ -588,10 +592,16 @@ __device__ inline void wu_tiles_rows_w(const unsigned char* src, const u32x4 (&t
             o0[r] = static_cast<__bf16>(a0[r]);
             o1[r] = static_cast<__bf16>(a1[r]);
         }
-        out[ni][0] = o0;
-        out[ni][1] = o1;
+        out[ni - NI0][0] = o0;
+        out[ni - NI0][1] = o1;
     }
 }
+
+// Output column tiles (of kD / 16) per wave in the row products: all eight at C = 128 (four
+// waves, four row-tile pairs); four at C = 64, where waves w and w + 2 share row tiles w and
+// 3 - w and take column tiles 0-3 and 4-7.
+template <int C>
+constexpr int kRowNNI = C == 128 ? kD / 16 : kD / 32;
 
 // T' of row tile m as the B operands of the row products above: for lane (lr, lg), tp[2 kt] holds
 // the hi halves and tp[2 kt + 1] the lo halves of row 16 m + lr, columns 32 kt + 8 lg .. + 7, in
@@ -620,27 +630,37 @@ __device__ inline void tp_rows(const float* Ts, int m, int lr, int lg, u32x4 (&t
 
 template <int C, int KROW>
 __device__ inline void wu_tiles_rows(const unsigned char* src, const u32x4 (&tpA)[C / 16], const u32x4 (&tpB)[C / 16],
-                                     int mA, int mB, int lr, int lg, bf16x4 (&out)[C / 16][2])
+                                     int wave, int lr, int lg, bf16x4 (&out)[kRowNNI<C>][2])
 {
-    static_assert(C / 16 == 2 * kWaves, "one pair of row tiles per wave");
-    (void)mB;  // always C / 16 - 1 - mA
-    switch (mA) {  // uniform: the wave index
-    case 0: wu_tiles_rows_w<C, KROW, 0>(src, tpA, tpB, lr, lg, out); break;
-    case 1: wu_tiles_rows_w<C, KROW, 1>(src, tpA, tpB, lr, lg, out); break;
-    case 2: wu_tiles_rows_w<C, KROW, 2>(src, tpA, tpB, lr, lg, out); break;
-    default: wu_tiles_rows_w<C, KROW, 3>(src, tpA, tpB, lr, lg, out); break;
+    constexpr int N = kRowNNI<C>;
+    static_assert(kWaves == 4 && (C == 128 || C == 64), "four waves; row-tile pairs at C = 64, 128");
+    if constexpr (C == 128) {
+        switch (wave) {  // uniform
+        case 0: wu_tiles_rows_w<C, KROW, 0, 0, N>(src, tpA, tpB, lr, lg, out); break;
+        case 1: wu_tiles_rows_w<C, KROW, 1, 0, N>(src, tpA, tpB, lr, lg, out); break;
+        case 2: wu_tiles_rows_w<C, KROW, 2, 0, N>(src, tpA, tpB, lr, lg, out); break;
+        default: wu_tiles_rows_w<C, KROW, 3, 0, N>(src, tpA, tpB, lr, lg, out); break;
+        }
+    } else {
+        switch (wave) {  // uniform
+        case 0: wu_tiles_rows_w<C, KROW, 0, 0, N>(src, tpA, tpB, lr, lg, out); break;
+        case 1: wu_tiles_rows_w<C, KROW, 1, 0, N>(src, tpA, tpB, lr, lg, out); break;
+        case 2: wu_tiles_rows_w<C, KROW, 0, N, N>(src, tpA, tpB, lr, lg, out); break;
+        default: wu_tiles_rows_w<C, KROW, 1, N, N>(src, tpA, tpB, lr, lg, out); break;
+        }
     }
 }
 
 template <int C, int KROW>
-__device__ inline void stage_tiles_rows(unsigned char* dst, const bf16x4 (&out)[C / 16][2], int mA, int mB,
-                                        int lr, int lg)
+__device__ inline void stage_tiles_rows(unsigned char* dst, const bf16x4 (&out)[kRowNNI<C>][2], int mA, int mB,
+                                        int ni0, int lr, int lg)
 {
     __bf16* d = reinterpret_cast<__bf16*>(dst);
 #pragma unroll
-    for (int ni = 0; ni < C / 16; ++ni) {
-        *reinterpret_cast<bf16x4*>(d + (16 * mA + lr) * KROW + 16 * ni + 4 * lg) = out[ni][0];
-        *reinterpret_cast<bf16x4*>(d + (16 * mB + lr) * KROW + 16 * ni + 4 * lg) = out[ni][1];
+    for (int c = 0; c < kRowNNI<C>; ++c) {
+        const int ni = ni0 + c;
+        *reinterpret_cast<bf16x4*>(d + (16 * mA + lr) * KROW + 16 * ni + 4 * lg) = out[c][0];
+        *reinterpret_cast<bf16x4*>(d + (16 * mB + lr) * KROW + 16 * ni + 4 * lg) = out[c][1];
     }
 }
 
@@ -665,8 +685,9 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
     constexpr int NB = C / 16;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    if constexpr (GT && NB == 2 * kWaves) {
-        const int mA = wave, mB = NB - 1 - wave;
+    if constexpr (GT && C >= 64) {
+        const int mA = C == 128 ? wave : (wave & 1), mB = NB - 1 - mA;
+        const int ni0 = C == 128 ? 0 : (wave >> 1) * kRowNNI<C>;
         u32x4 tpA[NB], tpB[NB];
         tp_rows<C, TL>(Ts, mA, lr, lg, tpA);
         tp_rows<C, TL>(Ts, mB, lr, lg, tpB);
@@ -674,19 +695,19 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
         unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
         pf.commit_v(Vraw, tid);
         __syncthreads();
-        bf16x4 out[NB][2];
-        wu_tiles_rows<C, KROW>(Vraw, tpA, tpB, mA, mB, lr, lg, out);
+        bf16x4 out[kRowNNI<C>][2];
+        wu_tiles_rows<C, KROW>(Vraw, tpA, tpB, wave, lr, lg, out);
         __syncthreads();  // every wave is done reading V: U is staged over it
-        stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, lr, lg);
+        stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, ni0, lr, lg);
 #pragma unroll
         for (int kt = 0; kt < NB / 2; ++kt) {
             if (2 * kt > mB) continue;  // uniform; a k step wholly right of the diagonal stays zero
             if (2 * kt <= mA) scale_rows<KROW>(Kraw, tpA[2 * kt], tpA[2 * kt + 1], kt, lg);
             scale_rows<KROW>(Kraw, tpB[2 * kt], tpB[2 * kt + 1], kt, lg);
         }
-        wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, mA, mB, lr, lg, out);
+        wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, wave, lr, lg, out);
         __syncthreads();  // every wave is done reading K: W is staged over it
-        stage_tiles_rows<C, KROW>(Kraw, out, mA, mB, lr, lg);
+        stage_tiles_rows<C, KROW>(Kraw, out, mA, mB, ni0, lr, lg);
         __syncthreads();
         store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
         store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
@@ -717,8 +738,9 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
         __syncthreads();
         store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
         store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
-    } else if constexpr (NB == 2 * kWaves) {
-        const int mA = wave, mB = NB - 1 - wave;
+    } else if constexpr (C >= 64) {
+        const int mA = C == 128 ? wave : (wave & 1), mB = NB - 1 - mA;
+        const int ni0 = C == 128 ? 0 : (wave >> 1) * kRowNNI<C>;
         u32x4 tpA[NB], tpB[NB];
         tp_rows<C, TL>(Ts, mA, lr, lg, tpA);
         tp_rows<C, TL>(Ts, mB, lr, lg, tpB);
@@ -726,13 +748,13 @@ __device__ void wu_bf16(unsigned char* Kraw, float* Ts, PF& pf, const Params& p,
         unsigned char* Vraw = reinterpret_cast<unsigned char*>(Ts);
         pf.commit_v(Vraw, tid);
         __syncthreads();
-        bf16x4 out[NB][2];
-        wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, mA, mB, lr, lg, out);
+        bf16x4 out[kRowNNI<C>][2];
+        wu_tiles_rows<C, KROW>(Kraw, tpA, tpB, wave, lr, lg, out);
         __syncthreads();  // every wave is done reading K: W is staged over it
-        stage_tiles_rows<C, KROW>(Kraw, out, mA, mB, lr, lg);
-        wu_tiles_rows<C, KROW>(Vraw, tpA, tpB, mA, mB, lr, lg, out);
+        stage_tiles_rows<C, KROW>(Kraw, out, mA, mB, ni0, lr, lg);
+        wu_tiles_rows<C, KROW>(Vraw, tpA, tpB, wave, lr, lg, out);
         __syncthreads();  // every wave is done reading V: U is staged over it
-        stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, lr, lg);
+        stage_tiles_rows<C, KROW>(Vraw, out, mA, mB, ni0, lr, lg);
         __syncthreads();
         store_rows<C, 2, KROW>(Kraw, p.W, u, p.hv, tid);
         store_rows<C, 2, KROW>(Vraw, p.U, u, p.hv, tid);
