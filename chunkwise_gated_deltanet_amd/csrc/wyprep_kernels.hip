@@ -27,10 +27,10 @@
 //   a7  store T (fp32; upper triangle 0, diagonal 1), then overwrite the T tile in place with
 //       T' = T diag(beta) as a hi + lo pair of bf16 values;
 //   a8  W^T = K^T T'^T and U^T = V^T T'^T on bf16 MFMA (16x16x16 at C = 32; from C = 64 on
-//       16x16x32, each wave owning two row tiles), hi and lo parts of T' accumulated in turn (T' is lower
-//       triangular, so k-tiles right of the diagonal are skipped); the transposed accumulators
-//       hold four consecutive output columns per lane, staged in LDS and stored with 16-byte
-//       writes.
+//       16x16x32, each wave owning two row tiles), hi and lo parts of T' accumulated in turn
+//       (T' is lower triangular, so k-tiles right of the diagonal are skipped); the transposed
+//       accumulators hold four consecutive output columns per lane, staged in LDS and stored
+//       with 16-byte writes.
 // Gated instances ([Inv] section 5, item 12: with gating the coefficient is
 // diag(beta)(Gamma o K K^T); g [B,T,Hv] is the per-token log gate of [QLA] usage) also read g:
 //   a1' wave 0 forms the chunk-local inclusive prefix sums G_i = g_0 + ... + g_i in fp64 (one
@@ -461,8 +461,8 @@ __device__ void store_rows(const unsigned char* src, void* out, const Unit& u, i
 // column) is one LDS transpose read: within each 16-lane group, lane i of ds_read_tr16_b64
 // receives element (i mod 4) of the 64-bit rows addressed by lanes 4e + i/4, e = 0..3.  Wave w
 // owns column tiles w and w + 4 of W, then of U.  Accumulator element r of lane 16g + c is
-// X[16mi + c][16ni + 4g + r]; the result leaves as bf16.  Used at C = 32 (and for fp32 inputs,
-// whose path has its own products); from C = 64 on the row products below take over.
+// X[16mi + c][16ni + 4g + r]; the result leaves as bf16.  Used at C = 32; from C = 64 on the
+// row products below take over.
 template <int C, int KROW>
 __device__ inline void wu_tiles(const unsigned char* src, const u32x4 (&tp)[C / 16][C / 16], int wave,
                                 int lr, int lg, bf16x4 (&out)[2][C / 16])
