@@ -234,7 +234,11 @@ __device__ __attribute__((always_inline)) void a_tile_out(const f32x4& acc, cons
 // for all its tiles, so a unit reads 36 blocks of 16 K rows from LDS instead of the 72 that
 // tile-by-tile products read (both blocks of every tile).  Sharing the column blocks between the
 // two rows as well (26 reads) measured no faster and holds 16 more registers.
-template <int C, int KROW, class TL, bool GT, int MA>
+//
+// At C = 64 the two row-block pairs (0, 3) and (1, 2) are split over waves p and p + 2 (PART 0
+// and 1): wave p forms row p and the first 2 - p tiles of row 3 - p, wave p + 2 the rest of
+// row 3 - p (three, three, two and two tiles, as the tile-by-tile order deals them).
+template <int C, int KROW, class TL, bool GT, int MA, int PART = -1>
 __device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char* Kraw, float* Ts, const float* bs,
                                                              int lr, int lg)
 {
@@ -256,12 +260,13 @@ __device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char
         // unrolled tiles and held all at once
         if constexpr (GT) __builtin_amdgcn_sched_barrier(0);
     };
-    // one row block at a time, so only its fragments and one column block's are live
-    auto row = [&](int I) {
+    // tiles J0 .. J1 of row block I, one row block at a time, so only its fragments and one
+    // column block's are live
+    auto row = [&](int I, int J0, int J1) {
         bf16x8 fi[NS];
         frag(I, fi);
 #pragma unroll
-        for (int J = 0; J <= I; ++J) {  // unrolled: J == I is resolved at compile time
+        for (int J = J0; J <= J1; ++J) {  // unrolled: J == I is resolved at compile time
             if (J == I) {
                 tile(fi, fi, I, J);
             } else {
@@ -271,8 +276,15 @@ __device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char
             }
         }
     };
-    row(MA);
-    row(MB);
+    if constexpr (PART < 0) {
+        row(MA, 0, MA);
+        row(MB, 0, MB);
+    } else if constexpr (PART == 0) {
+        row(MA, 0, MA);
+        row(MB, 0, NB / 2 - 1 - MA);
+    } else {
+        row(MB, NB / 2 - MA, MB);
+    }
 }
 
 // a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts; all C x C entries are written.
@@ -297,6 +309,14 @@ __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw,
         }
         return;  // the tile-packed layout stores no upper tiles
     }
+    if constexpr (C == 64 && DT == 0) {
+        switch (wave) {  // uniform
+        case 0: form_a_rows_w<C, KROW, TL, GT, 0, 0>(Kraw, Ts, bs, lr, lg); break;
+        case 1: form_a_rows_w<C, KROW, TL, GT, 1, 0>(Kraw, Ts, bs, lr, lg); break;
+        case 2: form_a_rows_w<C, KROW, TL, GT, 0, 1>(Kraw, Ts, bs, lr, lg); break;
+        default: form_a_rows_w<C, KROW, TL, GT, 1, 1>(Kraw, Ts, bs, lr, lg); break;
+        }
+    } else {
     // Operands are loaded tile by tile: other resident workgroups cover the LDS latency.  A
     // second operand buffer costs 32 registers and measured no faster even at C = 128, where
     // only two workgroups share a CU.
@@ -325,6 +345,7 @@ __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw,
         } else if (tn < NTILE) {
             tile_of(tn, &I, &J);
         }
+    }
     }
     // strictly upper tiles (I < J), enumerated row-major, also dealt round-robin to waves
     // (the tile-packed layout has none)
