@@ -288,8 +288,8 @@ __device__ __attribute__((always_inline)) void form_a_rows_w(const unsigned char
 }
 
 // a2 + a3: A = I + strictLower(diag(beta) K K^T) into Ts; all C x C entries are written.
-// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4 (at C = 128 with bf16 K: by row
-// blocks, form_a_rows_w); upper tiles are zeroed with one 16-byte write per lane.
+// Lower tiles t = 0.. (row-major over I >= J) go to wave t % 4 (with bf16 K at C = 64 and 128:
+// by row blocks, form_a_rows_w); upper tiles are zeroed with one 16-byte write per lane.
 template <int C, int DT, int KROW, class TL, bool GT>
 __device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int tid)
 {
@@ -895,14 +895,13 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     pf.commit_k(Kraw, bs, tid);
     __syncthreads();
     // This unit's V is needed only after its inversion; the next unit's K at the next unit's
-    // start.  Issued in that order, a wait for either never waits for the other.  At C = 128 the
-    // unit's chain, not HBM, sets the pace: the next K is issued after the diagonal inversions
-    // (which two of the four waves run), not right behind V, where the two compete for the
-    // CU's address units (3-4% faster at B=4 T=4096 H=32; at C <= 64 it stays here, in flight
-    // as long as possible).
+    // start.  Issued in that order, a wait for either never waits for the other.  From C = 64
+    // on the next K is issued after the diagonal inversions (which one or two of the four waves
+    // run), not right behind V, where the two compete for the CU's address units: at C = 128
+    // 2-4% faster, at C = 64 3% on the headline, 5% on the packed workload and 7% for T alone.
     pf.issue_v(p, cur, tid);
     const Unit nxt = map_unit<C>(p, info, next, tid);
-    if constexpr (C != 128) {
+    if constexpr (C < 64) {
         if (nxt.n > 0) pf.issue_k(p, nxt, tid);
     }
 
@@ -910,7 +909,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     form_a<C, DT, L::KROW, TL, GT>(Kraw, Ts, bs, tid);
     __syncthreads();
     invert_diagonal_blocks<C, TL>(Ts, tid);
-    if constexpr (C == 128) {
+    if constexpr (C >= 64) {
         if (nxt.n > 0) pf.issue_k(p, nxt, tid);
     }
     __syncthreads();
