@@ -7,7 +7,10 @@ are seeded synthetic data, resident in HBM before the timed region.  Several cop
 input/output buffers are rotated so that consecutive steps do not hit the 256 MB Infinity
 Cache with the previous step's data.
 
-Prints one JSON line.  value = units (chunk x value head) per second.
+Prints one JSON line.  value = units (chunk x value head) per second, from the GPU time of the
+timed steps (one HIP event pair around them, on the launch stream); the roofline's achieved
+bandwidth comes from the same figure.  The same run also times the other C = 64 workloads and
+the chunk-size study (extra key "workloads"), each with its own roofline.
 """
 from __future__ import annotations
 
@@ -104,12 +107,18 @@ def counter_traffic(name, entry="wy"):
     return float(m_b.group(1))
 
 
-def cpu_threads():
+def host_cores():
+    """Host cores this process may run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def cpu_threads():
+    """Threads for the CPU baseline: every usable host core, at most 16 (one GPU's share of a
+    GPU machine's cores; the rest belong to the other GPUs of the machine)."""
+    return max(1, min(16, host_cores()))
 
 
 def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
@@ -133,7 +142,7 @@ def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
     passes, el = timed(threads, seconds)
     passes1, el1 = timed(1, seconds / 3)
     return {"value": units_per_pass * passes / el, "unit": "chunks/s", "cores": threads,
-            "kind": "oracle",
+            "host_cores": host_cores(), "kind": "oracle",
             "sample": f"whole workload ({units_per_pass} units, {tokens_per_pass} tokens) x "
                       f"{passes} passes, {el:.1f} s wall, fp64; one core: {passes1} passes, "
                       f"{el1:.1f} s",
@@ -161,7 +170,7 @@ def cpu_baseline_bwd(inp, units_per_pass, tokens_per_pass, workload, seconds=10.
         if el >= seconds:
             break
     return {"value": units_per_pass * passes / el, "unit": "chunks/s", "cores": threads,
-            "kind": "oracle",
+            "host_cores": host_cores(), "kind": "oracle",
             "sample": f"whole workload ({units_per_pass} units, {tokens_per_pass} tokens) x "
                       f"{passes} passes, {el:.1f} s wall, fp64 backward",
             "tokens_per_s": tokens_per_pass * passes / el}
@@ -191,11 +200,245 @@ def cpu_baseline_fwd(inp, seconds=10.0):
         if el >= seconds:
             break
     return {"value": units * passes / el, "unit": "chunks/s", "cores": threads,
-            "kind": "oracle",
+            "host_cores": host_cores(), "kind": "oracle",
             "sample": f"{len(pairs)} (sequence, value head) pairs ({units} chunk x head units, "
                       f"{toks} tokens each pass) x {passes} passes, {el:.1f} s wall, fp64 "
                       "token-by-token recurrence",
             "tokens_per_s": toks * passes / el}
+
+
+# Extra workloads timed after the headline (each with its own roofline): the other C = 64
+# configurations and the chunk-size study on B=4 T=4096 H=32.
+DEFAULT_EXTRAS = "3:32,3:64,3:128,5:64"
+
+
+def parse_extras(text):
+    """'3:32,5:64' -> [(3, 32), (5, 64)]; 'none' or '' -> []."""
+    if not text or text == "none":
+        return []
+    out = []
+    for item in text.split(","):
+        idx, c = item.split(":")
+        out.append((int(idx), int(c)))
+    return out
+
+
+def measure(args, entry, w, inp, dev, lib, ramp=True):
+    """Times `args.steps` steps of one entry point on one workload; returns the result fields
+    (and the timing details) as a dict."""
+    import ctypes
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    from chunkwise_gated_deltanet_amd import synth
+
+    fwd_entry = entry in ("fwd", "gdn")
+    bwd_entry = entry == "bwd"
+    gated = inp["g"] is not None
+    B, T = inp["batch"], inp["seqlen"]
+    Hq, Hv, C = w.num_qk_heads, w.num_v_heads, w.chunk_size
+    dk = dv = 128
+    esz = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if inp["cu_seqlens"] is not None:
+        lens = np.diff(inp["cu_seqlens"].astype(np.int64))
+        nchunks = int(np.sum((lens + C - 1) // C))
+    else:
+        nchunks = B * ((T + C - 1) // C)
+    units = nchunks * Hv
+    tokens = B * T
+    nstates = B if inp["cu_seqlens"] is None else len(inp["cu_seqlens"]) - 1
+    if entry == "bwd":
+        alg = bwd_bytes(tokens, Hq, Hv, dk, dv, esz, gated)
+    elif entry == "fwd":
+        alg = fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
+    elif entry == "gdn":
+        alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, "wu", gated) + \
+            fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
+    else:
+        alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, entry, gated)
+    nsets = max(1, math.ceil(ROTATE_BYTES / alg))  # every byte of a step is touched once
+
+    def dev_tensor(a, dt):
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        return (t.view(torch.bfloat16) if dt == torch.bfloat16 else t).to(dev)
+
+    k0 = dev_tensor(inp["k"], tdt)
+    v0 = dev_tensor(inp["v"], tdt)
+    b0 = torch.from_numpy(inp["beta"]).to(dev)
+    g0 = torch.from_numpy(inp["g"]).to(dev) if gated else None
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    q0 = dev_tensor(inp["q"], tdt) if fwd_entry else None
+    if bwd_entry:  # upstream gradients dW, dU: seeded N(0, 1), bf16
+        grng = np.random.default_rng(1000 + args.workload)
+        dW0 = dev_tensor(synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, dk), dtype=np.float32)), tdt)
+        dU0 = dev_tensor(synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, dv), dtype=np.float32)), tdt)
+    sets = []
+    for i in range(nsets):
+        first = i == 0  # set 0 uses the uploaded tensors themselves
+        sets.append(dict(k=k0 if first else k0.clone(), v=v0 if first else v0.clone(),
+                         beta=b0 if first else b0.clone(),
+                         g=(g0 if first else g0.clone()) if gated else None,
+                         T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev)
+                         if entry in ("wy", "kkt") else None,
+                         W=torch.empty(B, T, Hv, dk, dtype=tdt, device=dev)
+                         if entry != "kkt" else None,
+                         U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev)
+                         if entry != "kkt" else None,
+                         q=(q0 if first else q0.clone()) if fwd_entry else None,
+                         o=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev) if fwd_entry else None,
+                         hT=torch.empty(nstates, Hv, dk, dv, dtype=torch.float32, device=dev)
+                         if fwd_entry else None,
+                         dW=(dW0 if first else dW0.clone()) if bwd_entry else None,
+                         dU=(dU0 if first else dU0.clone()) if bwd_entry else None,
+                         dk=torch.empty_like(k0) if bwd_entry else None,
+                         dv=torch.empty_like(v0) if bwd_entry else None,
+                         db=torch.empty_like(b0) if bwd_entry else None,
+                         dg=torch.empty_like(b0) if bwd_entry and gated else None))
+    prob = cg.Problem(B, T, Hq, Hv, dk, dv, C, 0 if cu is None else cu.numel() - 1,
+                      0 if w.dtype == "bf16" else 1)
+    pprob = ctypes.byref(prob)
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
+                   (s["k"], s["v"], s["g"], s["beta"], s["T"], s["W"], s["U"], s["q"], s["o"],
+                    s["hT"])) for s in sets]
+    bcalls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
+                    (s["dW"], s["dU"], s["dk"], s["dv"], s["db"], s["dg"])) for s in sets]
+    cu_ptr = ctypes.c_void_p(None if cu is None else cu.data_ptr())
+    scale = ctypes.c_float(dk ** -0.5)
+    seg_chunks = None
+    if fwd_entry and args.segment_chunks is not None:
+        if cu is not None:
+            raise SystemExit("--segment-chunks needs a [B, T] workload (no packed sequences)")
+        seg_chunks = (cg.cp_segment_chunks(B, T, Hv, C) if args.segment_chunks == "auto"
+                      else int(args.segment_chunks))
+        ws_bytes = lib.wyp_chunk_fwd_cp_workspace_bytes(pprob, seg_chunks)
+        ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
+        ws_ptr, ws_n = ctypes.c_void_p(ws.data_ptr()), ctypes.c_int64(ws_bytes)
+
+    def step(i, sp):
+        kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i % nsets]
+        if entry == "wy":
+            st = lib.wyp_wy_prepare(pprob, kp, vp, gp, bp, cu_ptr, tp, wp, up, sp)
+        elif entry == "wu":
+            st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
+        elif entry == "kkt":
+            st = lib.wyp_kkt_solve(pprob, kp, gp, bp, cu_ptr, tp, sp)
+        elif entry == "bwd":
+            dwp, dup, dkp, dvp, dbp, dgp = bcalls[i % nsets]
+            st = lib.wyp_wy_backward(pprob, kp, vp, gp, bp, cu_ptr, None, dwp, dup, dkp, dvp, dbp,
+                                     dgp, sp)
+        else:
+            st = 0
+            if entry == "gdn":
+                st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
+            if st == 0 and seg_chunks is not None:
+                st = lib.wyp_chunk_fwd_cp(pprob, qp, kp, wp, up, gp, None, scale, seg_chunks,
+                                          ws_ptr, ws_n, op, hp, sp)
+            elif st == 0:
+                st = lib.wyp_chunk_fwd(pprob, qp, kp, wp, up, gp, None, scale, cu_ptr, op, hp, sp)
+        if st != 0:
+            raise RuntimeError(lib.wyp_last_error().decode())
+
+    if entry == "fwd":  # W and U of every buffer set, prepared once, untimed
+        for i in range(nsets):
+            kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i]
+            if lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sptr) != 0:
+                raise RuntimeError(lib.wyp_last_error().decode())
+        torch.cuda.synchronize(dev)
+
+    # Clock ramp: the GPU needs ~20 ms of sustained work to reach steady clocks (measured on
+    # this kernel: 43 us per launch in the first 4 ms, 30 us from 20 ms on).  The step runs
+    # untimed for at least --ramp-ms before the counted warm-up steps; the count is reported.
+    ramp_launches = 0
+    if ramp:
+        t_end = time.perf_counter() + args.ramp_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(50):
+                step(ramp_launches, sptr)
+                ramp_launches += 1
+            torch.cuda.synchronize(dev)
+    for i in range(args.warmup):
+        step(i, sptr)
+    torch.cuda.synchronize(dev)
+
+    # The K launches of the timed region are captured once into a HIP graph (unless --eager):
+    # one host call then submits all of them, so the host's per-launch cost (ctypes, argument
+    # checks, hipLaunchKernel) cannot leave the GPU idle between these ~30 us kernels.
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream(dev)):
+            csp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+            for i in range(args.steps):
+                step(i, csp)
+        graph.replay()  # untimed: the first replay also uploads the graph
+        torch.cuda.synchronize(dev)
+
+    # The outputs the last timed launch writes are filled with NaN first, so the check after
+    # the timed region fails if the timed launches did not write them.
+    last = (args.steps - 1) % nsets
+    outs = {"wy": ("T", "W", "U"), "wu": ("W", "U"), "kkt": ("T",), "fwd": ("o", "hT"),
+            "gdn": ("W", "U", "o", "hT"),
+            "bwd": ("dk", "dv", "db") + (("dg",) if gated else ())}[entry]
+    for n in outs:
+        sets[last][n].fill_(float("nan"))
+
+    # Timed region: exactly `steps` launches, one event pair around them on the launch stream
+    # (an event pair per launch would add its own few microseconds to each).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i, sptr)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    step_s = e0.elapsed_time(e1) * 1e-3 / args.steps  # GPU seconds per step, gaps included
+
+    # The timed launches did the work: the outputs of the last buffer set hold no NaN and equal
+    # a fresh eager launch bit for bit.
+    got = {n: sets[last][n].clone() for n in outs}
+    written = all(not torch.isnan(got[n]).any() for n in outs)
+    step(last, sptr)
+    torch.cuda.synchronize(dev)
+    replay_ok = written and all(torch.equal(got[n], sets[last][n]) for n in outs)
+
+    # Diagnostic only (after the timed region): spread of single eager launches, each between
+    # its own pair of events, so every figure carries one event pair's overhead.
+    nd = min(args.steps, 50)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(nd)]
+    for i in range(nd):
+        ev[i][0].record(stream)
+        step(i, sptr)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+
+    achieved = alg / step_s / 1e9
+    pname = profile_name(entry, w, B, T, 0 if cu is None else cu.numel() - 1)
+    traffic = counter_traffic(pname, entry) if entry != "gdn" else None
+    res = {
+        "units": units, "tokens": tokens, "alg": alg, "nsets": nsets, "seg_chunks": seg_chunks,
+        "ramp_launches": ramp_launches, "launch": "eager" if graph is None else
+        "hip graph of the timed launches", "replay_ok": replay_ok, "step_s": step_s,
+        "wall_s": wall,
+        "kernel_us": {"mean": step_s * 1e6,
+                      "single_launch_p10": float(np.percentile(durs, 10)) * 1e6,
+                      "single_launch_p50": float(np.median(durs)) * 1e6,
+                      "single_launch_p90": float(np.percentile(durs, 90)) * 1e6},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes": alg},
+    }
+    del sets, graph
+    torch.cuda.empty_cache()
+    return res
 
 
 def main(argv=None):
@@ -223,6 +466,10 @@ def main(argv=None):
                     help="fwd / gdn entries: split each sequence into segments of this many "
                          "chunks run in parallel (wyp_chunk_fwd_cp); 'auto' picks it from the "
                          "shape")
+    ap.add_argument("--extras", default=None,
+                    help="extra workloads timed after the main one with the same entry point, "
+                         "as workload:C pairs (default for the headline: "
+                         f"{DEFAULT_EXTRAS}; 'none' for none)")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -255,216 +502,66 @@ def main(argv=None):
     inp = synth.generate(w)
     gated = inp["g"] is not None
     B, T = inp["batch"], inp["seqlen"]
-    Hq, Hv, C = w.num_qk_heads, w.num_v_heads, w.chunk_size
-    dk = dv = 128
-    esz = 2 if w.dtype == "bf16" else 4
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    if inp["cu_seqlens"] is not None:
-        lens = np.diff(inp["cu_seqlens"].astype(np.int64))
-        nchunks = int(np.sum((lens + C - 1) // C))
-    else:
-        nchunks = B * ((T + C - 1) // C)
-    units = nchunks * Hv
-    tokens = B * T
-    nstates = B if inp["cu_seqlens"] is None else len(inp["cu_seqlens"]) - 1
-    if args.entry == "bwd":
-        alg = bwd_bytes(tokens, Hq, Hv, dk, dv, esz, gated)
-    elif args.entry == "fwd":
-        alg = fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
-    elif args.entry == "gdn":
-        alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, "wu", gated) + \
-            fwd_bytes(tokens, nstates, Hq, Hv, dk, dv, esz, gated)
-    else:
-        alg = algorithmic_bytes(tokens, Hq, Hv, dk, dv, C, esz, args.entry, gated)
-    nsets = max(1, math.ceil(ROTATE_BYTES / alg))  # every byte of a step is touched once
-
-    def dev_tensor(a, dt):
-        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
-        return (t.view(torch.bfloat16) if dt == torch.bfloat16 else t).to(dev)
-
-    k0 = dev_tensor(inp["k"], tdt)
-    v0 = dev_tensor(inp["v"], tdt)
-    b0 = torch.from_numpy(inp["beta"]).to(dev)
-    g0 = torch.from_numpy(inp["g"]).to(dev) if gated else None
-    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
-    q0 = dev_tensor(inp["q"], tdt) if fwd_entry else None
-    bwd_entry = args.entry == "bwd"
-    if bwd_entry:  # upstream gradients dW, dU: seeded N(0, 1), bf16
-        grng = np.random.default_rng(1000 + args.workload)
-        dW0 = dev_tensor(synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, dk), dtype=np.float32)), tdt)
-        dU0 = dev_tensor(synth.f32_to_bf16_bits(grng.standard_normal((B, T, Hv, dv), dtype=np.float32)), tdt)
-    sets = []
-    for _ in range(nsets):
-        sets.append(dict(k=k0.clone(), v=v0.clone(), beta=b0.clone(),
-                         g=g0.clone() if gated else None,
-                         T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev)
-                         if args.entry in ("wy", "kkt") else None,
-                         W=torch.empty(B, T, Hv, dk, dtype=tdt, device=dev),
-                         U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev),
-                         q=q0.clone() if fwd_entry else None,
-                         o=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev) if fwd_entry else None,
-                         hT=torch.empty(nstates, Hv, dk, dv, dtype=torch.float32, device=dev)
-                         if fwd_entry else None,
-                         dW=dW0.clone() if bwd_entry else None,
-                         dU=dU0.clone() if bwd_entry else None,
-                         dk=torch.empty_like(k0) if bwd_entry else None,
-                         dv=torch.empty_like(v0) if bwd_entry else None,
-                         db=torch.empty_like(b0) if bwd_entry else None,
-                         dg=torch.empty_like(b0) if bwd_entry and gated else None))
-    prob = cg.Problem(B, T, Hq, Hv, dk, dv, C, 0 if cu is None else cu.numel() - 1,
-                      0 if w.dtype == "bf16" else 1)
-    import ctypes
-    pprob = ctypes.byref(prob)
-    stream = torch.cuda.current_stream(dev)
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-    calls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
-                   (s["k"], s["v"], s["g"], s["beta"], s["T"], s["W"], s["U"], s["q"], s["o"],
-                    s["hT"])) for s in sets]
-    bcalls = [tuple(ctypes.c_void_p(None if t is None else t.data_ptr()) for t in
-                    (s["dW"], s["dU"], s["dk"], s["dv"], s["db"], s["dg"])) for s in sets]
-    cu_ptr = ctypes.c_void_p(None if cu is None else cu.data_ptr())
-    scale = ctypes.c_float(dk ** -0.5)
-    seg_chunks = None
-    if fwd_entry and args.segment_chunks is not None:
-        if cu is not None:
-            raise SystemExit("--segment-chunks needs a [B, T] workload (no packed sequences)")
-        seg_chunks = (cg.cp_segment_chunks(B, T, Hv, C) if args.segment_chunks == "auto"
-                      else int(args.segment_chunks))
-        ws_bytes = lib.wyp_chunk_fwd_cp_workspace_bytes(pprob, seg_chunks)
-        ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
-        ws_ptr, ws_n = ctypes.c_void_p(ws.data_ptr()), ctypes.c_int64(ws_bytes)
-
-    def step(i, sp):
-        kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i % nsets]
-        if args.entry == "wy":
-            st = lib.wyp_wy_prepare(pprob, kp, vp, gp, bp, cu_ptr, tp, wp, up, sp)
-        elif args.entry == "wu":
-            st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
-        elif args.entry == "kkt":
-            st = lib.wyp_kkt_solve(pprob, kp, gp, bp, cu_ptr, tp, sp)
-        elif args.entry == "bwd":
-            dwp, dup, dkp, dvp, dbp, dgp = bcalls[i % nsets]
-            st = lib.wyp_wy_backward(pprob, kp, vp, gp, bp, cu_ptr, None, dwp, dup, dkp, dvp, dbp,
-                                     dgp, sp)
-        else:
-            st = 0
-            if args.entry == "gdn":
-                st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
-            if st == 0 and seg_chunks is not None:
-                st = lib.wyp_chunk_fwd_cp(pprob, qp, kp, wp, up, gp, None, scale, seg_chunks,
-                                          ws_ptr, ws_n, op, hp, sp)
-            elif st == 0:
-                st = lib.wyp_chunk_fwd(pprob, qp, kp, wp, up, gp, None, scale, cu_ptr, op, hp, sp)
-        if st != 0:
-            raise RuntimeError(lib.wyp_last_error().decode())
-
-    if args.entry == "fwd":  # W and U of every buffer set, prepared once, untimed
-        for i in range(nsets):
-            kp, vp, gp, bp, tp, wp, up, qp, op, hp = calls[i]
-            if lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sptr) != 0:
-                raise RuntimeError(lib.wyp_last_error().decode())
-        torch.cuda.synchronize(dev)
-
-    # Clock ramp: the GPU needs ~20 ms of sustained work to reach steady clocks (measured on
-    # this kernel: 43 us per launch in the first 4 ms, 30 us from 20 ms on).  The step runs
-    # untimed for at least --ramp-ms before the counted warm-up steps; the count is reported.
-    ramp_launches, t_end = 0, time.perf_counter() + args.ramp_ms * 1e-3
-    while time.perf_counter() < t_end:
-        for _ in range(50):
-            step(ramp_launches, sptr)
-            ramp_launches += 1
-        torch.cuda.synchronize(dev)
-    for i in range(args.warmup):
-        step(i, sptr)
-    torch.cuda.synchronize(dev)
-
-    # The K launches of the timed region are captured once into a HIP graph (unless --eager):
-    # one host call then submits all of them, so the host's per-launch cost (ctypes, argument
-    # checks, hipLaunchKernel) cannot leave the GPU idle between these ~30 us kernels.
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=torch.cuda.Stream(dev)):
-            csp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-            for i in range(args.steps):
-                step(i, csp)
-        graph.replay()  # untimed: the first replay also uploads the graph
-        torch.cuda.synchronize(dev)
-
-    # Timed region: exactly `steps` launches, one event pair around them on the launch stream
-    # (an event pair per launch would add its own few microseconds to each).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i, sptr)
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    kern_avg = e0.elapsed_time(e1) * 1e-3 / args.steps  # seconds per launch, gaps included
-
-    # The graph did the work: the last buffer set it wrote equals a fresh eager launch.
-    last = (args.steps - 1) % nsets
-    outs = {"wy": ("T", "W", "U"), "wu": ("W", "U"), "kkt": ("T",), "fwd": ("o", "hT"),
-            "gdn": ("W", "U", "o", "hT"),
-            "bwd": ("dk", "dv", "db") + (("dg",) if gated else ())}[args.entry]
-    ref = {n: sets[last][n].clone() for n in outs}
-    step(last, sptr)
-    torch.cuda.synchronize(dev)
-    replay_ok = all(torch.equal(ref[n], sets[last][n]) for n in ref)
-
-    # Diagnostic only (after the timed region): spread of single eager launches, each between
-    # its own pair of events, so every figure carries one event pair's overhead.
-    nd = min(args.steps, 50)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(nd)]
-    for i in range(nd):
-        ev[i][0].record(stream)
-        step(i, sptr)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize(dev)
-    durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
-
-    achieved = alg / kern_avg / 1e9
-    pname = profile_name(args.entry, w, B, T, 0 if cu is None else cu.numel() - 1)
-    traffic = counter_traffic(pname, args.entry) if args.entry != "gdn" else None
+    C = w.chunk_size
+    r = measure(args, args.entry, w, inp, dev, lib, ramp=True)
+    units, tokens = r["units"], r["tokens"]
     out = {
         "metric": METRIC if args.entry == "wy" else f"chunks/s (tokens/s) for {ENTRY_NAMES[args.entry]} at C={C}; achieved HBM GB/s vs peak",
-        "value": units / (ms_per_step * 1e-3),
+        "value": units / r["step_s"],
         "unit": "chunks/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["step_s"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "entry": ENTRY_NAMES[args.entry], "gated": gated,
-                   "segment_chunks": seg_chunks if fwd_entry else None,
-                   "batch": B, "seqlen": T, "num_qk_heads": Hq,
-                   "num_v_heads": Hv, "head_dim": dk, "chunk_size": C,
+                   "segment_chunks": r["seg_chunks"] if fwd_entry else None,
+                   "batch": B, "seqlen": T, "num_qk_heads": w.num_qk_heads,
+                   "num_v_heads": w.num_v_heads, "head_dim": 128, "chunk_size": C,
                    "units_per_step": units, "tokens_per_step": tokens,
-                   "rotated_buffer_sets": nsets,
-                   "launch": "eager" if graph is None else "hip graph of the timed launches",
-                   "clock_ramp_launches": ramp_launches,
-                   "replay_matches_eager": replay_ok},
-        "tokens_per_s": tokens / (ms_per_step * 1e-3),
-        "kernel_us": {"mean": kern_avg * 1e6,
-                      "single_launch_p10": float(np.percentile(durs, 10)) * 1e6,
-                      "single_launch_p50": float(np.median(durs)) * 1e6,
-                      "single_launch_p90": float(np.percentile(durs, 90)) * 1e6},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": alg},
+                   "rotated_buffer_sets": r["nsets"], "launch": r["launch"],
+                   "clock_ramp_launches": r["ramp_launches"],
+                   "replay_matches_eager": r["replay_ok"],
+                   "timing": "ms_per_step, value and roofline.achieved come from one HIP event "
+                             "pair around the timed launches on the launch stream"},
+        "tokens_per_s": tokens / r["step_s"],
+        "host_wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "kernel_us": r["kernel_us"],
+        "roofline": r["roofline"],
         "cpu_baseline": None,
     }
+    if args.entry == "gdn":
+        out["roofline"]["note"] = ("two kernels per step (wu_prepare, chunk_fwd): achieved is "
+                                   "their summed algorithmic bytes over the step time")
+    extras = parse_extras(args.extras if args.extras is not None else
+                          (DEFAULT_EXTRAS if args.entry == "wy" and args.workload == 2 and
+                           args.chunk_size in (None, 64) and not gated else "none"))
+    if extras:
+        out["workloads"] = []
+        cache = {}
+        for idx, c in extras:
+            we = synth.workload(idx, chunk_size=c, gate_mu=args.gate_mu, with_q=fwd_entry)
+            # the chunk size changes only a packed workload's lengths
+            key = (idx, c if we.seq_range is not None else None)
+            if key not in cache:
+                cache.clear()
+                cache[key] = synth.generate(we)
+            ie = dict(cache[key], chunk_size=c)
+            # each gets its own clock ramp: the GPU idles while the host draws its inputs
+            re_ = measure(args, args.entry, we, ie, dev, lib, ramp=True)
+            out["workloads"].append({
+                "workload": we.name, "chunk_size": c, "units_per_step": re_["units"],
+                "tokens_per_step": re_["tokens"], "ms_per_step": re_["step_s"] * 1e3,
+                "value": re_["units"] / re_["step_s"], "unit": "chunks/s",
+                "tokens_per_s": re_["tokens"] / re_["step_s"],
+                "replay_matches_eager": re_["replay_ok"], "rotated_buffer_sets": re_["nsets"],
+                "clock_ramp_launches": re_["ramp_launches"],
+                "kernel_us": re_["kernel_us"], "roofline": re_["roofline"]})
+        cache.clear()
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -472,13 +569,10 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize(dev)
         out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
-    if args.entry == "gdn":
-        out["roofline"]["note"] = ("two kernels per step (wu_prepare, chunk_fwd): achieved is "
-                                   "their summed algorithmic bytes over the step time")
     if not args.no_cpu_baseline:
         if fwd_entry:
             out["cpu_baseline"] = cpu_baseline_fwd(inp, args.cpu_seconds)
-        elif bwd_entry:
+        elif args.entry == "bwd":
             out["cpu_baseline"] = cpu_baseline_bwd(inp, units, tokens, args.workload,
                                                    args.cpu_seconds)
         else:

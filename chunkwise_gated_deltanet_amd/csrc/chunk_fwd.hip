@@ -42,9 +42,10 @@
 //   pass 1 (LOCAL): per (sequence, segment, head), A = the segment's end state from a zero state
 //          and M = its transition (the same recurrence with U = 0 from the identity), as eight
 //          32-column slices; no output;
-//   pass 2 (combine): S_start of segment s + 1 = M_s S_start(s) + A_s, in fp32, per head and
-//          16-column slice;
-//   pass 3: the kernel above per (sequence, segment, head) from its true S_start, writing o.
+//   pass 2 (combine): S_start(0) = the initial state, copied into the workspace, and S_start of
+//          segment s + 1 = M_s S_start(s) + A_s, in fp32, per head and 16-column slice;
+//   pass 3: the kernel above per (sequence, segment, head) from its true S_start (always read
+//          from the workspace, so the initial state may be the final-state buffer), writing o.
 // Exact, not the gate-decay warm-up approximation the pages also describe.
 #include <hip/hip_runtime.h>
 
@@ -97,7 +98,8 @@ struct Params {
     int32_t work;        // work items: sequences x segments x value heads x slices
     int32_t nseg;        // segments per sequence (1: the whole sequence)
     int32_t seg_chunks;  // chunks per segment (nseg > 1)
-    float* ws_a;         // [pair][nseg - 1][dk][dv]: A_s (pass 1), then S_start(s + 1) (pass 2)
+    float* ws_a;         // [pair][nseg][dk][dv]: slot 0 S_start(0) (pass 2); slot s + 1 A_s
+                         // (pass 1), then S_start(s + 1) (pass 2)
     float* ws_m;         // [pair][nseg - 1][dk][dk]: M_s
 };
 
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int nchunks_seq = static_cast<int>((s1 - s0 + kC - 1) / kC);
     const int c_begin = p.nseg > 1 ? seg * p.seg_chunks : 0;
     const int c_end = p.nseg > 1 ? min(c_begin + p.seg_chunks, nchunks_seq) : nchunks_seq;
-    const int64_t wsslot = static_cast<int64_t>(pair) * (p.nseg - 1);  // first workspace slot
+    const int64_t mslot = static_cast<int64_t>(pair) * (p.nseg - 1);  // this pair's first M slot
+    const int64_t aslot = static_cast<int64_t>(pair) * p.nseg;        // this pair's S_start(0) slot
 
     int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
@@ -272,15 +275,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float* Gs = reinterpret_cast<const float*>(smem + OFF_G);
 
     // State tiles of this wave: S[16 mt + 4 lg + r][16 nt + lr], mt = 2 wave + m, in fp32.
-    // Start: pass 1 from zero (A) or from the identity's columns (M); otherwise the sequence's
-    // initial state (segment 0) or the S_start the combine left in the workspace.
+    // Start: pass 1 from zero (A) or from the identity's columns (M); unsplit, the sequence's
+    // initial state; split, the S_start the combine left in the workspace (segment 0 too: the
+    // combine copied the initial state there before this pass, so the last segment may write
+    // the final state over the initial state's buffer).
     f32x4 sacc[2][2];
     const float* h0 = nullptr;
     if (!LOCAL) {
-        if (seg == 0)
+        if (p.nseg == 1)
             h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD : nullptr;
-        else
-            h0 = p.ws_a + (wsslot + seg - 1) * kD * kD;
+        else if (seg > 0 || p.h0 != nullptr)
+            h0 = p.ws_a + (aslot + seg) * kD * kD;
     }
     if (h0) h0 += slice * kDVS;
 #pragma unroll
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     float* out = nullptr;  // where this work item's end state goes
     if (LOCAL)
-        out = (mcols ? p.ws_m : p.ws_a) + (wsslot + seg) * kD * kD + slice * kDVS;
+        out = (mcols ? p.ws_m + (mslot + seg) * kD * kD : p.ws_a + (aslot + seg + 1) * kD * kD) + slice * kDVS;
     else if (p.hT != nullptr && seg == p.nseg - 1)
         out = p.hT + static_cast<int64_t>(pair) * kD * kD + slice * kDVS;
     if (out != nullptr) {
@@ -476,8 +481,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // Pass 2 of the sequence-parallel forward: per (sequence, value head, 16-column dv slice),
-// S_start(0) = the initial state and S_start(s + 1) = M_s S_start(s) + A_s for s = 0 .. nseg - 2,
-// each written over A_s (it is read there by pass 3).  Each step is 128 x 128 x 16 fp32
+// S_start(0) = the initial state (copied to workspace slot 0) and S_start(s + 1) =
+// M_s S_start(s) + A_s for s = 0 .. nseg - 2, each written over A_s (pass 3 reads them there).  Each step is 128 x 128 x 16 fp32
 // multiply-adds on fp32 MFMA 16x16x4.  The steps of one slice form a chain, so the slices are
 // 16 columns wide (eight workgroups per head: more chains, each step shorter); wave w owns row
 // tiles 2w, 2w + 1; S^T sits in LDS so every B operand is one 16-byte read.  M_{s+1} and A_{s+1}
@@ -489,10 +494,11 @@ struct CombineOperands {
     f32x4 m[2][kD / 16];  // M rows 16 mt + lr, columns 16 kt + 4 lg .. + 3 (A operands)
     f32x4 a[2];           // A elements [16 mt + 4 lg + r][lr] of the slice (accumulator start)
 
-    __device__ void load(const Params& p, int64_t slot, int slice, int wave, int lr, int lg)
+    // Step s of pair `pair`: A_s sits in slot pair * nseg + s + 1, M_s in pair * (nseg - 1) + s.
+    __device__ void load(const Params& p, int pair, int s, int slice, int wave, int lr, int lg)
     {
-        const float* A = p.ws_a + slot * kD * kD + slice * kCombCols;
-        const float* M = p.ws_m + slot * kD * kD;
+        const float* A = p.ws_a + (static_cast<int64_t>(pair) * p.nseg + s + 1) * kD * kD + slice * kCombCols;
+        const float* M = p.ws_m + (static_cast<int64_t>(pair) * (p.nseg - 1) + s) * kD * kD;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
             const int mt = 2 * wave + mm;
@@ -518,22 +524,24 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kCombCols : nullptr;
-    const int64_t slot0 = static_cast<int64_t>(pair) * (p.nseg - 1);
+    float* s0 = p.ws_a + static_cast<int64_t>(pair) * p.nseg * kD * kD + slice * kCombCols;
     // Two operand sets take turns (the loop is unrolled by two), so the next step's M and A are
     // loaded straight into the set that step uses, with no register copies that would wait for
     // those loads early.
     CombineOperands ops0, ops1;
-    ops0.load(p, slot0, slice, wave, lr, lg);  // launched only with nseg > 1
+    ops0.load(p, pair, 0, slice, wave, lr, lg);  // launched only with nseg > 1
     for (int idx = tid; idx < kD * kCombCols; idx += kThreads) {
         const int row = idx / kCombCols, col = idx % kCombCols;
-        St[col][row] = h0 ? h0[row * kD + col] : 0.f;
+        const float x = h0 ? h0[row * kD + col] : 0.f;
+        St[col][row] = x;
+        if (h0) s0[row * kD + col] = x;  // pass 3's segment 0 starts from this copy
     }
     __syncthreads();
     auto step = [&](int sg, const CombineOperands& cur, CombineOperands& nxt) {
         // M and A of the next step, in flight during this one.  The last step reloads its own
         // slot (in bounds, unused) so that the issue has no branch: a branch around it makes the
         // compiler's wait for `cur` conservative, and that wait would then cover these loads.
-        nxt.load(p, slot0 + (sg + 2 < p.nseg ? sg + 1 : sg), slice, wave, lr, lg);
+        nxt.load(p, pair, sg + 2 < p.nseg ? sg + 1 : sg, slice, wave, lr, lg);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of this step's products
         f32x4 acc[2];
 #pragma unroll
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
             }
         }
         __syncthreads();  // every read of S_start(s) done
-        float* A = p.ws_a + (slot0 + sg) * kD * kD + slice * kCombCols;
+        float* A = s0 + (sg + 1) * kD * kD;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
             *reinterpret_cast<f32x4*>(&St[lr][16 * (2 * wave + mm) + 4 * lg]) = acc[mm];
@@ -601,7 +609,7 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.nseg = a.nseg > 1 ? a.nseg : 1;
         p.seg_chunks = a.seg_chunks;
         p.ws_a = a.ws;
-        p.ws_m = a.ws ? a.ws + static_cast<int64_t>(a.num_seqs) * a.num_v_heads * (p.nseg - 1) * kD * kD : nullptr;
+        p.ws_m = a.ws ? a.ws + static_cast<int64_t>(a.num_seqs) * a.num_v_heads * p.nseg * kD * kD : nullptr;
         const int pairs = a.num_seqs * a.num_v_heads;
         if (p.nseg > 1) {
             p.work = pairs * (p.nseg - 1) * 2 * kSlices;  // pass 1

@@ -316,9 +316,12 @@ int64_t cp_segments(const wyp_problem* p, int32_t segment_chunks)
     return nchunks == 0 ? 1 : (nchunks + segment_chunks - 1) / segment_chunks;
 }
 
+// A and M of every segment but the last, plus S_start(0), per (batch row, value head); none
+// for a single segment.
 int64_t cp_workspace(const wyp_problem* p, int64_t nseg)
 {
-    return 2 * static_cast<int64_t>(p->batch) * p->num_v_heads * (nseg - 1) * 128 * 128 * 4;
+    if (nseg <= 1) return 0;
+    return static_cast<int64_t>(p->batch) * p->num_v_heads * (2 * nseg - 1) * 128 * 128 * 4;
 }
 
 }  // namespace

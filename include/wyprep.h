@@ -168,7 +168,9 @@ wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* 
  * same recurrence with U = 0, from the identity), in parallel; (2) S_start of each segment from
  * the previous one, S_start(s+1) = M_s S_start(s) + A_s, in fp32; (3) wyp_chunk_fwd's work per
  * segment from its S_start, writing o (and the final state from the last segment).  Exact up
- * to rounding (not the pages' gate-decay warm-up approximation).
+ * to rounding (not the pages' gate-decay warm-up approximation).  Pass 2 copies the initial
+ * state into the workspace and pass 3 reads it only there, so initial_state and final_state
+ * may be the same buffer, as for wyp_chunk_fwd.
  * Arguments as for wyp_chunk_fwd, without cu_seqlens (each batch row is one sequence of T
  * tokens), plus:
  *   segment_chunks   chunks per segment, >= 1; a value covering all ceil(T / 64) chunks gives
@@ -184,9 +186,9 @@ wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const voi
                             void* workspace, int64_t workspace_bytes, void* o_out,
                             float* final_state, void* stream);
 
-/* Workspace bytes wyp_chunk_fwd_cp needs: 2 x B x Hv x (segments - 1) x dk x dk x 4 (A and M
- * of every segment but the last); 0 for a single segment; -1 for invalid arguments
- * (segment_chunks < 1, chunk_size other than 64, NULL problem). */
+/* Workspace bytes wyp_chunk_fwd_cp needs: B x Hv x (2 x segments - 1) x dk x dk x 4 (A and M
+ * of every segment but the last, and a copy of the initial state); 0 for a single segment; -1
+ * for invalid arguments (segment_chunks < 1, chunk_size other than 64, NULL problem). */
 int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t segment_chunks);
 
 /* Backward of the preparation step (the training path; [QLA] "反向" (backward): FlashQLA fuses

@@ -92,6 +92,16 @@ def _bind(lib):
 _LIB = None
 
 
+def default_threads() -> int:
+    """Worker threads when none are given: the usable host cores, at most 16 (the CPU share
+    of one GPU on a GPU machine)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def load(path: str | None = None):
     """Load the oracle library (building it first if it is missing)."""
     global _LIB
@@ -199,7 +209,7 @@ def wy_prepare(k, beta, chunk_size, v=None, cu_seqlens=None, nthreads=None, lib=
     fma = ctypes.c_int64(0)
     rc = lib.wyo_wy_prepare(ctypes.byref(p), _ptr(k), _ptr(v if W is not None else None),
                             _ptr(g), _ptr(beta), _ptr(cu), _ptr(Tm), _ptr(W), _ptr(U),
-                            nthreads or os.cpu_count() or 1, ctypes.byref(fma))
+                            nthreads or default_threads(), ctypes.byref(fma))
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return Tm, W, U, int(fma.value)
@@ -226,7 +236,7 @@ def units(k, beta, chunk_size, chunk_start, chunk_len, v_head, v=None, nthreads=
         W = np.zeros((M, C, dk), np.float64)
         U = np.zeros((M, C, v.shape[3]), np.float64)
     rc = lib.wyo_units(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), M, _ptr(cs), _ptr(cl),
-                       _ptr(vh), _ptr(Tm), _ptr(W), _ptr(U), nthreads or os.cpu_count() or 1)
+                       _ptr(vh), _ptr(Tm), _ptr(W), _ptr(U), nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle rejected the units (code {rc})")
     return Tm, W, U
@@ -266,7 +276,7 @@ def gdn_forward(q, k, v, beta, g=None, h0=None, scale=None, cu_seqlens=None, pai
     hT = np.zeros((N, Hv, dk, dv), np.float64)
     rc = lib.wyo_gdn_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(h0), float(dk ** -0.5 if scale is None else scale), _ptr(cu),
-                             _ptr(o), _ptr(hT), _ptr(mask), nthreads or os.cpu_count() or 1)
+                             _ptr(o), _ptr(hT), _ptr(mask), nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return o, hT
@@ -303,7 +313,7 @@ def wy_backward(k, v, beta, chunk_size, dW, dU, dT=None, g=None, cu_seqlens=None
     dgo = np.zeros((B, T, Hv)) if g is not None else None
     rc = lib.wyo_wy_backward(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu),
                              _ptr(dT), _ptr(dW), _ptr(dU), _ptr(dko), _ptr(dvo), _ptr(dbo),
-                             _ptr(dgo), nthreads or os.cpu_count() or 1)
+                             _ptr(dgo), nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return dko, dvo, dbo, dgo

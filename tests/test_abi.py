@@ -192,7 +192,8 @@ def test_wy_backward_rejects(lib):
 def test_chunk_fwd_cp_workspace_and_rejects(lib):
     p = good(batch=2, seqlen=1000, num_v_heads=4)       # 16 chunks per row
     assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 16) == 0   # one segment
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 5) == 2 * 2 * 4 * 3 * 128 * 128 * 4
+    # four segments: A and M of three, plus the initial-state copy, per (row, value head)
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 5) == 2 * 4 * 7 * 128 * 128 * 4
     assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 0) == -1
     assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(good(chunk_size=32)), 4) == -1
     need = lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 4)

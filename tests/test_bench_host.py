@@ -78,3 +78,14 @@ def test_committed_headline_counters_are_near_the_algorithmic_bytes():
         pytest.skip("headline counter summary was taken on another kernel source")
     alg = bench.algorithmic_bytes(8192, 16, 16, 128, 128, 64, 2)
     assert 0.99 * alg <= t <= 1.1 * alg
+
+
+def test_extra_workloads_cover_the_c64_configs_and_the_chunk_study():
+    extras = bench.parse_extras(bench.DEFAULT_EXTRAS)
+    assert (3, 64) in extras and (5, 64) in extras
+    assert {c for i, c in extras if i == 3} == {32, 64, 128}
+    assert bench.parse_extras("none") == [] and bench.parse_extras("2:32") == [(2, 32)]
+
+
+def test_cpu_threads_are_capped_and_host_cores_recorded():
+    assert 1 <= bench.cpu_threads() <= min(16, bench.host_cores())

@@ -1,0 +1,59 @@
+"""Every entry point of the preparation step at full size, whole tensors against the fp64 oracle
+(needs a GPU).
+
+Each seeded workload runs at C = 32, 64 and 128, ungated and with the seeded gate recipe
+(g = log sigmoid(4 + N(0,1))), through wy_prepare (T, W, U), kkt_solve (T) and wu_prepare (W, U)
+in the launch configuration the benchmark times.  Bar, over every stored entry: T within 1e-5
+max-abs of the oracle, with its diagonal exactly 1 and strict upper triangle exactly 0; W and U
+within 1e-2 relative Frobenius over the whole tensor; every output written (outputs are
+pre-filled with NaN).  kkt_solve's T and wu_prepare's W, U must also equal wy_prepare's bit for
+bit (one arithmetic).  The oracle runs one range of whole chunks at a time.
+"""
+import pytest
+
+from chunkwise_gated_deltanet_amd import synth
+from gpu_util import check_structure, compare_all, run_all, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check_entry_points(inp, gpu, label):
+    import torch
+    outs = run_all(inp, gpu)
+    check_structure(outs["T"], inp)
+    assert torch.equal(outs["T"], outs["T_kkt"]), "kkt_solve's T differs from wy_prepare's"
+    assert torch.equal(outs["W"], outs["W_wu"]) and torch.equal(outs["U"], outs["U_wu"]), \
+        "wu_prepare's W / U differ from wy_prepare's"
+    compare_all(inp, outs, label=label)
+    del outs
+    torch.cuda.empty_cache()
+
+
+# A mid-size packed-free shape with a ragged end whose unit count is at least three times the
+# resident workgroups of every instance (T only: up to 7 per CU), so each persistent workgroup
+# runs its loop over several units: 8000 tokens, Hq=12 / Hv=48 -> 12000 / 6000 / 3024 units.
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_mid_size_multi_unit(C, gpu):
+    inp = synth.custom(1, 8000, 12, 48, C, seed=60 + C)
+    say(f"mid size B=1 T=8000 H=12/48 C={C}")
+    check_entry_points(inp, gpu, f"mid C={C}")
+
+
+FULL = [(i, c) for i in (1, 2, 3, 4, 5) for c in (32, 64, 128)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx,C", FULL, ids=[f"w{i}_C{c}" for i, c in FULL])
+def test_full_size_every_entry(idx, C, gpu):
+    """Ungated, then gated: the gates are drawn after k, v and beta, so both runs see the same
+    k, v and beta (the ungated run drops g)."""
+    w = synth.workload(idx, chunk_size=C, gate_mu=4.0)
+    inp = synth.generate(w)
+    tokens = inp["batch"] * inp["seqlen"]
+    g = inp["g"]
+    inp["g"] = None
+    say(f"full size {w.name} C={C} ungated tokens={tokens}")
+    check_entry_points(inp, gpu, f"{w.name} C={C} ungated")
+    inp["g"] = g
+    say(f"full size {w.name} C={C} gated (mu=4) tokens={tokens}")
+    check_entry_points(inp, gpu, f"{w.name} C={C} gated")

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from chunkwise_gated_deltanet_amd import synth
-from gpu_util import gate_of, rel_fro, say, to_device, to_f64
+from gpu_util import gate_of, oracle_threads, rel_fro, say, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -118,9 +118,31 @@ def test_chunk_gated_delta_rule_api(gpu):
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
-# Full sizes, C = 64: sampled (sequence, value head) pairs against the oracle, and every output
-# entry written.
+# Full sizes, C = 64: every (sequence, value head) pair against the oracle, whole tensors, with
+# the worst pair reported; every output entry written.
 FULL = [(2, None), (2, 4.0), (3, None), (5, 4.0)]
+
+
+def compare_pairs(inp, o, hT, o_ref, h_ref, label):
+    """Whole-tensor relative Frobenius of o and the final state, plus the worst single pair."""
+    B, T = inp["batch"], inp["seqlen"]
+    Hv = inp["beta"].shape[2]
+    cu = inp["cu_seqlens"]
+    N = B if cu is None else len(cu) - 1
+    starts = (np.arange(N) * T if cu is None else cu[:-1]).astype(np.int64)
+    ends = (starts + T if cu is None else cu[1:]).astype(np.int64)
+    og, rf = to_f64(o).reshape(-1, Hv, 128), o_ref.reshape(-1, Hv, 128)
+    hg = to_f64(hT)
+    ro, rh = rel_fro(og, rf), rel_fro(hg, h_ref)
+    worst = 0.0
+    for s in range(N):
+        for h in range(Hv):
+            if ends[s] > starts[s]:
+                worst = max(worst, rel_fro(og[starts[s]:ends[s], h], rf[starts[s]:ends[s], h]))
+            worst = max(worst, rel_fro(hg[s, h], h_ref[s, h]))
+    say(f"[{label}] o rel fro {ro:.3e}, final state rel fro {rh:.3e}, worst pair {worst:.3e}")
+    assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
+    return worst
 
 
 @pytest.mark.slow
@@ -132,23 +154,9 @@ def test_chunk_fwd_full_size(idx, mu, gpu):
     say(f"chunk_fwd full {w.name} gate_mu={mu} tokens={inp['batch'] * inp['seqlen']}")
     o, hT = run_fwd(inp, None, gpu)
     assert not torch.isnan(o).any(), "unwritten o entries"
-    N = inp["batch"] if inp["cu_seqlens"] is None else len(inp["cu_seqlens"]) - 1
-    Hv = inp["beta"].shape[2]
-    rng = np.random.default_rng(idx)
-    pairs = {(0, 0), (N - 1, Hv - 1)} | {(int(rng.integers(N)), int(rng.integers(Hv))) for _ in range(2)}
-    o_ref, h_ref = oracle_fwd(inp, None, pairs=sorted(pairs))
-    og, hg = o.reshape(-1, Hv, 128), hT
-    B, T = inp["batch"], inp["seqlen"]
-    starts = (np.arange(N) * T if inp["cu_seqlens"] is None else inp["cu_seqlens"][:-1]).astype(np.int64)
-    ends = (starts + T if inp["cu_seqlens"] is None else inp["cu_seqlens"][1:]).astype(np.int64)
-    o_ref = o_ref.reshape(-1, Hv, 128)
-    worst = 0.0
-    for s, h in sorted(pairs):
-        ro = rel_fro(to_f64(og[starts[s]:ends[s], h]), o_ref[starts[s]:ends[s], h])
-        rh = rel_fro(to_f64(hg[s, h]), h_ref[s, h])
-        worst = max(worst, ro, rh)
-        say(f"  pair (seq {s}, head {h}): o rel fro {ro:.3e}, final state rel fro {rh:.3e}")
-    assert worst <= FWD_TOL, worst
+    o_ref, h_ref = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp.get("g"),
+                                      cu_seqlens=inp["cu_seqlens"], nthreads=oracle_threads())
+    compare_pairs(inp, o, hT, o_ref, h_ref, f"full {w.name} mu={mu}")
     del o, hT
     torch.cuda.empty_cache()
 
@@ -197,10 +205,38 @@ def test_chunk_fwd_cp(name, gpu):
     assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
 
 
+def test_chunk_fwd_cp_in_place_state(gpu):
+    """Split forward with final_state = initial_state: segment 0 starts from the combine's copy
+    of the initial state, so the last segment's write cannot reach it.  B=2 T=4096 H=8 with
+    4-chunk segments runs 1024 output-pass workgroups, more than one resident round (768), so
+    last segments do finish while first segments are still waiting to start."""
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    inp, h0 = make_inputs(dict(batch=2, seqlen=4096, num_qk_heads=4, num_v_heads=8, seed=135,
+                               gate_mu=4.0, h0=True))
+    say("chunk_fwd_cp in place, B=2 T=4096 H=4/8, segment_chunks=4")
+    k, v, beta, _ = to_device(inp, gpu)
+    q = q_of(inp, gpu)
+    g = gate_of(inp, gpu)
+    W, U = cg.wu_prepare(k, v, beta, 64, g=g)
+    o1, h1 = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=torch.from_numpy(h0).to(gpu),
+                          output_final_state=True, segment_chunks=4)
+    state = torch.from_numpy(h0).to(gpu)
+    o2, h2 = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=state, final_state=state,
+                          segment_chunks=4)
+    torch.cuda.synchronize(gpu)
+    assert h2.data_ptr() == state.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    o_ref, h_ref = oracle_fwd(inp, h0)
+    ro, rh = rel_fro(to_f64(o2), o_ref), rel_fro(to_f64(h2), h_ref)
+    say(f"[cp in place] o rel fro {ro:.3e}, final state rel fro {rh:.3e}")
+    assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("mu", [None, 4.0])
 def test_chunk_fwd_cp_full_size(mu, gpu):
-    """B=1 T=8192 H=16/16 C=64 with the automatic segment length, sampled heads."""
+    """B=1 T=8192 H=16/16 C=64 with the automatic segment length, every head."""
     import torch
     import chunkwise_gated_deltanet_amd as cg
     w = synth.workload(2, chunk_size=64, gate_mu=mu, with_q=True)
@@ -209,10 +245,6 @@ def test_chunk_fwd_cp_full_size(mu, gpu):
     say(f"chunk_fwd_cp full {w.name} gate_mu={mu} segment_chunks={seg}")
     o, hT = run_fwd_cp(inp, None, gpu, seg)
     assert not torch.isnan(o).any()
-    pairs = [(0, 0), (0, 7), (0, 15)]
-    o_ref, h_ref = oracle_fwd(inp, None, pairs=pairs)
-    for s, h in pairs:
-        ro = rel_fro(to_f64(o[0, :, h]), o_ref[0, :, h])
-        rh = rel_fro(to_f64(hT[s, h]), h_ref[s, h])
-        say(f"  head {h}: o rel fro {ro:.3e}, final state rel fro {rh:.3e}")
-        assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
+    o_ref, h_ref = oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp.get("g"),
+                                      nthreads=oracle_threads())
+    compare_pairs(inp, o, hT, o_ref, h_ref, f"cp full {w.name} mu={mu} segment_chunks={seg}")

@@ -7,7 +7,7 @@ within the W/U tolerance.
 import pytest
 
 from chunkwise_gated_deltanet_amd import synth
-from gpu_util import compare_full, compare_sampled, gate_of, run_wy, say, to_device
+from gpu_util import compare_full, gate_of, run_wy, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -47,16 +47,3 @@ def test_wu_prepare_matches_wy_prepare_and_oracle(name, gpu):
     T0, W0, U0 = run_wy(inp, gpu)
     assert torch.equal(W, W0) and torch.equal(U, U0)
     compare_full(inp, T0, W, U, label="wu " + name)
-
-
-@pytest.mark.slow
-@pytest.mark.parametrize("idx", [2, 5])
-def test_wu_prepare_full_size(idx, gpu):
-    import torch
-    inp = synth.generate(synth.workload(idx))
-    say(f"wu_prepare full workload {idx}")
-    W, U = run_wu(inp, gpu)
-    assert not torch.isnan(W).any() and not torch.isnan(U).any()
-    T0, W0, U0 = run_wy(inp, gpu, sentinel=False)
-    assert torch.equal(W, W0) and torch.equal(U, U0)
-    compare_sampled(inp, T0, W, U, m=128, label=f"wu workload {idx}")
