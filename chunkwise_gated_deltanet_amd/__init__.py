@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.s
 
 WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
 WYP_BF16, WYP_F32 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class WyprepError(RuntimeError):
@@ -79,6 +79,9 @@ def load_library(path: str | None = None):
     lib.wyp_chunk_fwd_cp.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P,
                                      ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
                                      _P]
+    lib.wyp_chunk_fwd_cp_noalloc.restype = ctypes.c_int32
+    lib.wyp_chunk_fwd_cp_noalloc.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_float, ctypes.c_int32, _P, _P, _P]
     lib.wyp_chunk_fwd_cp_workspace_bytes.restype = ctypes.c_int64
     lib.wyp_chunk_fwd_cp_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32]
     lib.wyp_wy_backward.restype = ctypes.c_int32

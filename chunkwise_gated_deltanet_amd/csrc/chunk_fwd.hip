@@ -53,7 +53,15 @@
 #include <cstdio>
 #include <mutex>
 
+#include "wyprep.h"
 #include "wyprep_launch.h"
+
+// Workspace of wyp_chunk_fwd_cp_noalloc, for callers that cannot allocate: A, M and the
+// initial-state copy of every segment, as wyp_chunk_fwd_cp keeps them in its caller's workspace.
+// Each GPU holds its own copy of the array for the life of the process.  Host code never passes
+// the array's name to a kernel (on the host it only stands in for the device object): it takes
+// the device address from hipGetSymbolAddress (cp_scratch below).
+static __device__ __align__(256) unsigned char scratch[WYP_CP_SCRATCH_BYTES];
 
 namespace wyp {
 namespace fwd {
@@ -638,6 +646,30 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 
 }  // namespace
 }  // namespace fwd
+
+int cp_scratch(void** ptr, char* msg, int msg_len)
+{
+    // Looked up once per device, on the first call made with that device current.
+    static std::once_flag once[64];
+    static void* addr[64];
+    static hipError_t err[64];
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
+    if (e == hipSuccess) {
+        std::call_once(once[device], [&] {
+            err[device] = hipGetSymbolAddress(&addr[device], HIP_SYMBOL(scratch));
+            if (err[device] == hipSuccess && addr[device] == nullptr) err[device] = hipErrorInvalidSymbol;
+        });
+        e = err[device];
+    }
+    if (e != hipSuccess) {
+        std::snprintf(msg, msg_len, "%s (device address of the split forward's scratch)", hipGetErrorString(e));
+        return static_cast<int>(e);
+    }
+    *ptr = addr[device];
+    return 0;
+}
 
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len)
 {

@@ -333,12 +333,14 @@ extern "C" int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, 
     return cp_workspace(problem, nseg);
 }
 
-extern "C" wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
-                                       const void* w, const void* u, const float* g,
-                                       const float* initial_state, float scale,
-                                       int32_t segment_chunks, void* workspace,
-                                       int64_t workspace_bytes, void* o_out, float* final_state,
-                                       void* stream)
+namespace {
+
+// The split forward: `workspace` is the caller's (wyp_chunk_fwd_cp) or, when `use_scratch`, the
+// library's static scratch (wyp_chunk_fwd_cp_noalloc, which allocates nothing).
+wyp_status run_cp(const wyp_problem* problem, const void* q, const void* k, const void* w,
+                  const void* u, const float* g, const float* initial_state, float scale,
+                  int32_t segment_chunks, void* workspace, int64_t workspace_bytes, bool use_scratch,
+                  void* o_out, float* final_state, void* stream)
 {
     g_last_error[0] = '\0';
     wyp::FwdArgs args{};
@@ -349,21 +351,54 @@ extern "C" wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q
     const int64_t nseg = cp_segments(problem, segment_chunks);
     if (nseg < 1)
         return fail(WYP_ERR_INVALID_ARGUMENT, "segment_chunks must be >= 1 (got %d)", segment_chunks);
+    char msg[256] = "";
     if (nseg > 1) {
         const int64_t need = cp_workspace(problem, nseg);
-        if (!workspace || workspace_bytes < need)
-            return fail(WYP_ERR_INVALID_ARGUMENT, "workspace of %lld bytes needed (%lld given)",
-                        static_cast<long long>(need), static_cast<long long>(workspace_bytes));
-        if (!aligned(workspace, 16))
-            return fail(WYP_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+        if (use_scratch) {
+            if (need > WYP_CP_SCRATCH_BYTES)
+                return fail(WYP_ERR_UNSUPPORTED,
+                            "the split needs %lld bytes of workspace, more than the %lld-byte scratch "
+                            "(use fewer segments or wyp_chunk_fwd_cp)",
+                            static_cast<long long>(need), static_cast<long long>(WYP_CP_SCRATCH_BYTES));
+        } else {
+            if (!workspace || workspace_bytes < need)
+                return fail(WYP_ERR_INVALID_ARGUMENT, "workspace of %lld bytes needed (%lld given)",
+                            static_cast<long long>(need), static_cast<long long>(workspace_bytes));
+            if (!aligned(workspace, 16))
+                return fail(WYP_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+        }
         if (static_cast<int64_t>(problem->batch) * problem->num_v_heads * nseg * 8 + 8 > INT32_MAX)
             return fail(WYP_ERR_UNSUPPORTED, "too many segments for one launch");
+        if (use_scratch && wyp::cp_scratch(&workspace, msg, sizeof msg) != 0)
+            return fail(WYP_ERR_HIP, "%s", msg);
     }
     args.nseg = static_cast<int32_t>(nseg);
     args.seg_chunks = segment_chunks;
     args.ws = nseg > 1 ? static_cast<float*>(workspace) : nullptr;
-    char msg[256] = "";
     if (wyp::launch_fwd(args, stream, msg, sizeof msg) != 0)
         return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
     return WYP_OK;
+}
+
+}  // namespace
+
+extern "C" wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
+                                       const void* w, const void* u, const float* g,
+                                       const float* initial_state, float scale,
+                                       int32_t segment_chunks, void* workspace,
+                                       int64_t workspace_bytes, void* o_out, float* final_state,
+                                       void* stream)
+{
+    return run_cp(problem, q, k, w, u, g, initial_state, scale, segment_chunks, workspace,
+                  workspace_bytes, false, o_out, final_state, stream);
+}
+
+extern "C" wyp_status wyp_chunk_fwd_cp_noalloc(const wyp_problem* problem, const void* q,
+                                               const void* k, const void* w, const void* u,
+                                               const float* g, const float* initial_state,
+                                               float scale, int32_t segment_chunks, void* o_out,
+                                               float* final_state, void* stream)
+{
+    return run_cp(problem, q, k, w, u, g, initial_state, scale, segment_chunks, nullptr, 0, true,
+                  o_out, final_state, stream);
 }

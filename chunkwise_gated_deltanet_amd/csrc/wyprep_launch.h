@@ -48,10 +48,14 @@ struct FwdArgs {
     int32_t num_seqs;          // sequences (cu_seqlens) or batch rows
     int32_t nseg;              // segments per sequence (<= 1: sequential)
     int32_t seg_chunks;        // chunks per segment (nseg > 1)
-    float* ws;                 // nseg > 1: 2 x num_seqs x Hv x (nseg - 1) x dk x dk floats
+    float* ws;                 // nseg > 1: num_seqs x Hv x (2 nseg - 1) x dk x dk floats
 };
 
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len);
+
+// Device address of the split forward's static scratch (WYP_CP_SCRATCH_BYTES) on the current
+// device.  Returns 0 or the hipError_t value; fills `msg` on error.
+int cp_scratch(void** ptr, char* msg, int msg_len);
 
 // Validated backward of the preparation step, ready to launch.
 struct BwdArgs {

@@ -74,7 +74,11 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 5  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp */
+#define WYP_ABI_VERSION 6  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp;
+                              6: wyp_chunk_fwd_cp_noalloc */
+
+/* Bytes of the static device scratch behind wyp_chunk_fwd_cp_noalloc (one array per GPU). */
+#define WYP_CP_SCRATCH_BYTES (32 * 1024 * 1024)
 
 typedef enum {
     WYP_OK = 0,
@@ -190,6 +194,26 @@ wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const voi
  * of every segment but the last, and a copy of the initial state); 0 for a single segment; -1
  * for invalid arguments (segment_chunks < 1, chunk_size other than 64, NULL problem). */
 int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t segment_chunks);
+
+/* wyp_chunk_fwd_cp for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same passes, results and
+ * arguments, without workspace / workspace_bytes.  The workspace is instead a static device array
+ * of WYP_CP_SCRATCH_BYTES (32 MiB) inside the library; each GPU the library runs on holds its own
+ * copy until the process ends.  The call allocates and frees nothing (no hipMalloc, hipFree or
+ * allocating library routine); on its first call on a device it looks up that device's address
+ * of the array once.
+ *   Limit: wyp_chunk_fwd_cp_workspace_bytes(problem, segment_chunks) must not exceed
+ *   WYP_CP_SCRATCH_BYTES, else WYP_ERR_UNSUPPORTED (checked on the host, nothing launched).
+ *   B = 1, T = 8192, Hv = 16 in 8 segments needs 15 MiB.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on different
+ *   streams or from different threads without ordering) race and must not be made; calls on one
+ *   stream are ordered.  Each call writes every part of the array it reads before reading it,
+ *   so nothing has to start at zero and no call sees an earlier call's contents. */
+wyp_status wyp_chunk_fwd_cp_noalloc(const wyp_problem* problem, const void* q, const void* k,
+                                    const void* w_in, const void* u_in, const float* g,
+                                    const float* initial_state, float scale,
+                                    int32_t segment_chunks, void* o_out, float* final_state,
+                                    void* stream);
 
 /* Backward of the preparation step (the training path; [QLA] "反向" (backward): FlashQLA fuses
  * bwd_wy with the other backward kernels).  For upstream gradients dT, dW, dU of wyp_wy_prepare's

@@ -30,14 +30,14 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
                           "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_chunk_fwd",
-                          "wyp_wy_backward", "wyp_chunk_fwd_cp",
+                          "wyp_wy_backward", "wyp_chunk_fwd_cp", "wyp_chunk_fwd_cp_noalloc",
                           "wyp_chunk_fwd_cp_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 5 == cg.ABI_VERSION
+    assert lib.wyp_abi_version() == 6 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -206,3 +206,21 @@ def test_chunk_fwd_cp_workspace_and_rejects(lib):
     assert call(nbytes=need - 1) == 1
     assert call(ws=FAKE + 4) == 1
     assert call(seg=0) == 1
+
+
+def test_chunk_fwd_cp_noalloc_rejects_before_any_hip_call(lib):
+    """The scratch limit and argument checks are host-side: nothing is launched."""
+    lim = 32 * 1024 * 1024
+    p = good(batch=1, seqlen=64 * 128, num_qk_heads=16, num_v_heads=16)   # 128 chunks
+
+    def call(prob, seg, **kw):
+        return lib.wyp_chunk_fwd_cp_noalloc(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, None, None,
+                                            0.5, seg, FAKE, None, None)
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 16) <= lim      # 8 segments
+    big = good(batch=4, seqlen=64 * 128, num_qk_heads=32, num_v_heads=32)
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(big), 16) > lim
+    assert call(big, 16) == 2
+    assert "scratch" in lib.wyp_last_error().decode()
+    assert call(p, 0) == 1
+    assert call(good(chunk_size=32), 4) == 2
+    assert call(good(seqlen=0), 4) == 0          # no tokens, no final state: a no-op
