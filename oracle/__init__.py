@@ -16,6 +16,9 @@ Parity status of each function (what pins it is listed in tests/test_oracle_pins
   block_recursive_inverse    pinned (agrees with the row-wise inverse; FMA / depth counts)
   wy_prepare / units         pinned (Householder-product and delta-rule identities, closed
                              forms, degenerate cases, tail padding)
+  solve_rhs                  pinned (residual A X = diag(beta) R against numpy's A, the
+                             delta rule from a zero state with R = V, orthogonal keys, beta = 0,
+                             agreement with the separately pinned T diag(beta) R)
   the same with gates g      pinned (gated delta-rule recurrence from zero and from an
                              identity state, the 2-token closed form, g = 0 against no gates,
                              Gamma o T_ungated, chunk restarts)
@@ -83,6 +86,8 @@ def _bind(lib):
     lib.wyo_wy_backward.restype = ctypes.c_int32
     lib.wyo_wy_backward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P, ctypes.c_int32]
+    lib.wyo_solve_rhs.restype = ctypes.c_int32
+    lib.wyo_solve_rhs.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, ctypes.c_int32]
     lib.wyo_units.restype = ctypes.c_int32
     lib.wyo_units.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.c_int64, _P, _P,
                               _P, _P, _P, _P, ctypes.c_int32]
@@ -213,6 +218,24 @@ def wy_prepare(k, beta, chunk_size, v=None, cu_seqlens=None, nthreads=None, lib=
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return Tm, W, U, int(fma.value)
+
+
+def solve_rhs(k, rhs, beta, chunk_size, cu_seqlens=None, g=None, nthreads=None, lib=None):
+    """X = A^{-1} diag(beta) R per chunk and value head by forward substitution on the right-hand
+    side (T never formed); rhs [B,T,Hv,dv] with k's dtype.  Returns X [B,T,Hv,dv] float64."""
+    lib = lib or load()
+    k = np.ascontiguousarray(k)
+    rhs = np.ascontiguousarray(rhs)
+    beta = _c(beta, np.float32)
+    g = _gate(g, beta)
+    cu = _c(cu_seqlens, np.int32)
+    p = _problem(k, rhs, beta, chunk_size, cu)
+    X = np.zeros(rhs.shape, np.float64)
+    rc = lib.wyo_solve_rhs(ctypes.byref(p), _ptr(k), _ptr(rhs), _ptr(g), _ptr(beta), _ptr(cu),
+                           _ptr(X), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return X
 
 
 def units(k, beta, chunk_size, chunk_start, chunk_len, v_head, v=None, nthreads=None, lib=None,

@@ -183,9 +183,10 @@ static void scratch_free(unit_scratch* s)
  * S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T needs; the FlashQLA page
  * names the recurrence and its alpha_i in (0, 1), but its formula did not survive.)
  * Without gates G = 0, every exp() below is exactly 1 and the result is the ungated one. */
-static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, const float* beta,
-                          const float* gate, int64_t tok0, int32_t n, int32_t hv,
-                          unit_scratch* s, double* W, double* U)
+/* Decodes K, V (when v != NULL), beta and the gates of the chunk into s and forms
+ * A = I + strictLower(diag(beta) (Gamma o K K^T)) in s->A (n x n). */
+static void unit_form_a(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                        const float* gate, int64_t tok0, int32_t n, int32_t hv, unit_scratch* s)
 {
     const int32_t dk = p->head_dim_k, dv = p->head_dim_v;
     const int32_t Hq = p->num_qk_heads, Hv = p->num_v_heads;
@@ -219,6 +220,14 @@ static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, co
             }
             s->A[(int64_t)i * n + j] = a;
         }
+}
+
+static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, const float* beta,
+                          const float* gate, int64_t tok0, int32_t n, int32_t hv,
+                          unit_scratch* s, double* W, double* U)
+{
+    const int32_t dk = p->head_dim_k, dv = p->head_dim_v;
+    unit_form_a(p, k, v, beta, gate, tok0, n, hv, s);
 
     /* T = A^{-1} */
     const int64_t fma = wyo_row_forward_inverse(n, s->A, n, s->X, n);
@@ -243,6 +252,26 @@ static int64_t unit_solve(const wyo_problem* p, const void* k, const void* v, co
     return fma;
 }
 
+/* The single right-hand side ([Inv] section 5, item 10: when T would be used only once, the
+ * forward substitution is applied straight to the right-hand side and T is never formed):
+ * X = A^{-1} diag(beta) R for the chunk's rows of R (the rhs, value-head layout, in s->V),
+ * row by row, X[i,:] = beta_i R[i,:] - sum_{j<i} A[i,j] X[j,:] (ascending j), into Xout (n x dv).
+ * With R = V this is U = T diag(beta) V. */
+static void unit_rhs_solve(const wyo_problem* p, const void* k, const void* rhs, const float* beta,
+                           const float* gate, int64_t tok0, int32_t n, int32_t hv,
+                           unit_scratch* s, double* Xout)
+{
+    const int32_t dv = p->head_dim_v;
+    unit_form_a(p, k, rhs, beta, gate, tok0, n, hv, s);
+    for (int32_t i = 0; i < n; ++i)
+        for (int32_t e = 0; e < dv; ++e) {
+            double x = s->b[i] * s->V[(int64_t)i * dv + e];
+            for (int32_t j = 0; j < i; ++j)
+                x -= s->A[(int64_t)i * n + j] * Xout[(int64_t)j * dv + e];
+            Xout[(int64_t)i * dv + e] = x;
+        }
+}
+
 /* ---- threading over independent units ------------------------------------------------- */
 
 typedef struct {
@@ -256,6 +285,7 @@ typedef struct {
     const int32_t* heads;  /* NULL: unit u = (chunk u / Hv, head u % Hv) */
     int64_t num_units;
     int compact;           /* 1: compact [M,C,*] outputs; 0: scatter into [B,T,Hv,*] */
+    int rhs_solve;         /* 1: v is a right-hand side R; only X = A^{-1} diag(beta) R, into U */
     double* T;
     double* W;
     double* U;
@@ -281,6 +311,13 @@ static void* job_run(void* arg)
             const int32_t hv = jb->heads ? jb->heads[u] : (int32_t)(u % Hv);
             const int64_t tok0 = jb->start[c];
             const int32_t n = jb->len[c];
+            if (jb->rhs_solve) {
+                unit_rhs_solve(p, jb->k, jb->v, jb->beta, jb->gate, tok0, n, hv, &s, U);
+                for (int32_t i = 0; i < n; ++i)
+                    memcpy(jb->U + ((tok0 + i) * Hv + hv) * dv, U + (int64_t)i * dv,
+                           sizeof(double) * (size_t)dv);
+                continue;
+            }
             const int want_wu = jb->W != NULL;
             jb->fma += unit_solve(p, jb->k, want_wu ? jb->v : NULL, jb->beta, jb->gate, tok0, n,
                                   hv, &s, want_wu ? W : NULL, want_wu ? U : NULL);
@@ -369,6 +406,30 @@ int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const
     proto.T = T_out; proto.W = W_out; proto.U = U_out;
     const int ok = run_jobs(&proto, nthreads);
     if (fma_out) *fma_out = proto.fma;
+    free(start);
+    free(len);
+    return ok ? 0 : 2;
+}
+
+int32_t wyo_solve_rhs(const wyo_problem* p, const void* k, const void* rhs, const float* g,
+                      const float* beta, const int32_t* cu, double* X_out, int32_t nthreads)
+{
+    if (!problem_ok(p, cu) || !k || !rhs || !beta || !X_out) return 1;
+    const int64_t nchunks = wyo_count_chunks(p, cu);
+    if (nchunks < 0) return 1;
+    int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nchunks + 1));
+    int32_t* len = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nchunks + 1));
+    if (!start || !len) { free(start); free(len); return 2; }
+    wyo_list_chunks(p, cu, start, len, nchunks);
+    job proto;
+    memset(&proto, 0, sizeof proto);
+    proto.p = p; proto.k = k; proto.v = rhs; proto.beta = beta; proto.gate = g;
+    proto.start = start; proto.len = len; proto.heads = NULL;
+    proto.num_units = nchunks * p->num_v_heads;
+    proto.compact = 0;
+    proto.rhs_solve = 1;
+    proto.U = X_out;
+    const int ok = run_jobs(&proto, nthreads);
     free(start);
     free(len);
     return ok ? 0 : 2;

@@ -88,6 +88,16 @@ int32_t wyo_wy_prepare(const wyo_problem* p, const void* k, const void* v, const
                        const float* beta, const int32_t* cu_seqlens, double* T_out,
                        double* W_out, double* U_out, int32_t nthreads, int64_t* fma_out);
 
+/* A single right-hand side, T never formed ([Inv] section 5, item 10: when T would be used only
+ * once, apply the forward substitution straight to the right-hand side instead of materialising
+ * it).  For every chunk and value head h: X = A^{-1} diag(beta) R, where R holds the chunk's rows
+ * of rhs for value head h and A is wyo_wy_prepare's (gates included), by row-wise forward
+ * substitution on the right-hand side: X[i,:] = beta_i R[i,:] - sum_{j<i} A[i,j] X[j,:].  With
+ * rhs = v, X is U.  rhs [B,T,Hv,dv] (kv_dtype), X_out [B,T,Hv,dv] (fp64).  Returns 0 on success. */
+int32_t wyo_solve_rhs(const wyo_problem* p, const void* k, const void* rhs, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, double* X_out,
+                      int32_t nthreads);
+
 /* Selected units only: unit u is the chunk starting at flattened token chunk_start[u] with
  * chunk_len[u] tokens, for value head v_head[u].  Outputs are compact and zero-padded:
  * T_out [M,C,C], W_out [M,C,dk], U_out [M,C,dv] (W_out / U_out may be NULL with v).

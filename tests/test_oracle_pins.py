@@ -589,13 +589,96 @@ def pin_bwd_gate_zero(lib):
     assert np.any(b[3] != 0)
 
 
+# ---------------------------------------------------------------------------------------------
+# the single right-hand-side solve ([Inv] section 5, item 10: T never formed)
+
+def solve_one(lib, K, R, beta, g=None, C=None):
+    """solve_rhs on one chunk [0, n) of a single-head problem (fp32 inputs)."""
+    n = K.shape[0]
+    k = np.ascontiguousarray(K[None, :, None, :], np.float32)
+    r = np.ascontiguousarray(R[None, :, None, :], np.float32)
+    b = np.ascontiguousarray(beta[None, :, None], np.float32)
+    gg = None if g is None else np.ascontiguousarray(g[None, :, None], np.float32)
+    return oracle.solve_rhs(k, r, b, C or n, g=gg, lib=lib, nthreads=1)[0, :, 0]
+
+
+def gated_a(K, beta, g):
+    """A = I + strictLower(diag(beta)(Gamma o K K^T)), Gamma[i][j] = exp(G_i - G_j), fp64."""
+    G = np.cumsum(g.astype(np.float64))
+    K = K.astype(np.float64)
+    gam = np.exp(G[:, None] - G[None, :])
+    return np.eye(len(K)) + np.tril(beta.astype(np.float64)[:, None] * gam * (K @ K.T), -1)
+
+
+def pin_solve_rhs_residual(lib):
+    """A X = diag(beta) R for A formed here in numpy, gated and ungated, several lengths."""
+    rng = np.random.default_rng(40)
+    for n, mu in ((32, None), (45, 2.0), (64, None), (100, 0.5), (128, 4.0)):
+        K = unit_keys(rng, n)
+        R = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        g = None if mu is None else unit_gates(rng, n, mu)
+        X = solve_one(lib, K, R, beta, g)
+        A = a_matrix(K, beta) if g is None else gated_a(K, beta, g)
+        res = A @ X - beta.astype(np.float64)[:, None] * R.astype(np.float64)
+        assert np.max(np.abs(res)) <= 1e-12
+
+
+def pin_solve_rhs_delta_rule(lib):
+    """With R = V the solve is U: the gated delta rule from S_0 = 0 ends at
+    S_n = X^T diag(exp(G_n - G)) K (g = 0: the plain delta rule, S_n = X^T K)."""
+    rng = np.random.default_rng(41)
+    for n, mu in ((40, None), (64, 3.0)):
+        K = unit_keys(rng, n)
+        V = rng.standard_normal((n, 128)).astype(np.float32)
+        beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        g = np.zeros(n, np.float32) if mu is None else unit_gates(rng, n, mu)
+        X = solve_one(lib, K, V, beta, None if mu is None else g)
+        K64, V64 = K.astype(np.float64), V.astype(np.float64)
+        S = np.zeros((128, 128))
+        for t in range(n):
+            a, b = math.exp(float(g[t])), float(beta[t])
+            S = S @ (a * (np.eye(128) - b * np.outer(K64[t], K64[t]))) + b * np.outer(V64[t], K64[t])
+        G = np.cumsum(g.astype(np.float64))
+        assert np.max(np.abs(S - X.T @ (np.exp(G[-1] - G)[:, None] * K64))) <= 1e-12
+
+
+def pin_solve_rhs_degenerate(lib):
+    """Orthogonal keys: A = I, so X = diag(beta) R exactly; beta = 0: X = 0 exactly."""
+    rng = np.random.default_rng(42)
+    n = 64
+    K = np.eye(128, dtype=np.float32)[rng.permutation(128)[:n]]
+    R = rng.standard_normal((n, 128)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+    X = solve_one(lib, K, R, beta)
+    assert np.array_equal(X, beta.astype(np.float64)[:, None] * R.astype(np.float64))
+    X0 = solve_one(lib, unit_keys(rng, n), R, np.zeros(n, np.float32))
+    assert np.array_equal(X0, np.zeros_like(X0))
+
+
+def pin_solve_rhs_matches_u(lib):
+    """Whole tensors of a packed, grouped-head, gated problem: X with rhs = v equals the separately
+    pinned U = T diag(beta) V, chunk by chunk and head by head."""
+    for C in (32, 64):
+        inp = synth.custom(1, 0, 2, 6, C, dtype="f32", seed=43 + C, gate_mu=2.0,
+                           seqlens=[3 * C + 5, 7, C])
+        X = oracle.solve_rhs(inp["k"], inp["v"], inp["beta"], C, cu_seqlens=inp["cu_seqlens"],
+                             g=inp["g"], lib=lib, nthreads=2)
+        _, _, U, _ = oracle.wy_prepare(inp["k"], inp["beta"], C, v=inp["v"],
+                                       cu_seqlens=inp["cu_seqlens"], g=inp["g"], lib=lib,
+                                       nthreads=2)
+        assert np.max(np.abs(X - U)) <= 1e-12 * max(1.0, float(np.max(np.abs(U))))
+
+
 PINS = [pin_closed_form_2, pin_orthogonal, pin_residual_structure, pin_lapack_inverse,
         pin_block_identity, pin_beta_zero, pin_subdiag_only, pin_identical_keys,
         pin_fma_counts, pin_householder_product, pin_delta_rule, pin_tail_padding, pin_layout,
         pin_head_grouping, pin_gate_zero, pin_gated_closed_form_2, pin_gated_recurrence,
         pin_gated_similarity, pin_gated_chunk_restart, pin_gdn_read_back, pin_gdn_beta_zero,
         pin_gdn_linear_attention, pin_gdn_chunk_form, pin_gdn_sequences_independent,
-        pin_bwd_finite_differences, pin_bwd_zero_upstream, pin_bwd_gate_zero]
+        pin_bwd_finite_differences, pin_bwd_zero_upstream, pin_bwd_gate_zero,
+        pin_solve_rhs_residual, pin_solve_rhs_delta_rule, pin_solve_rhs_degenerate,
+        pin_solve_rhs_matches_u]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -703,6 +786,13 @@ MUTANTS = {
                             "dK[(int64_t)i * dk + d] = b[i] * E[i] * t;"),
     "bwd_dbeta_gram_dropped": ("dbrow[row] += mij * gam * kk;", "dbrow[row] += 0.0;"),
     "bwd_dT_ignored": ("double a = jb->dT ?", "double a = 0.0 * (double)(jb->dT != NULL) + 0 ?"),
+    # the single right-hand-side solve
+    "rhs_beta_dropped": ("double x = s->b[i] * s->V[(int64_t)i * dv + e];",
+                         "double x = s->V[(int64_t)i * dv + e];"),
+    "rhs_sign": ("x -= s->A[(int64_t)i * n + j] * Xout", "x += s->A[(int64_t)i * n + j] * Xout"),
+    "rhs_a_transposed": ("x -= s->A[(int64_t)i * n + j] * Xout", "x -= s->A[(int64_t)j * n + i] * Xout"),
+    "rhs_head_scatter": ("memcpy(jb->U + ((tok0 + i) * Hv + hv) * dv",
+                         "memcpy(jb->U + ((tok0 + i) * Hv + (hv + 1) % Hv) * dv"),
     "gate_not_restarted": ("s->G[i] = (i == 0 ? 0.0 : s->G[i - 1]) + gi;",
                            "s->G[i] = (i == 0 ? (gate && tok0 > 0 ? (double)gate[(tok0 - 1) * Hv + hv] "
                            ": 0.0) : s->G[i - 1]) + gi;"),
