@@ -41,15 +41,18 @@ KERNEL_SOURCES = {
     "bwd": ("wyprep_device.h", "wy_backward.hip"),
 }
 ENTRY_NAMES = {"wy": "wy_prepare", "wu": "wu_prepare", "kkt": "kkt_solve", "fwd": "chunk_fwd",
-               "gdn": "gdn_forward", "bwd": "wy_backward"}
+               "gdn": "gdn_forward", "bwd": "wy_backward", "solve": "solve_rhs"}
 
 
 def algorithmic_bytes(tokens, hq, hv, dk, dv, C, esz, entry="wy", gated=False):
     """K read once per key head, beta (and g when gated) read once; wy: V read, T (fp32), W and
-    U written once; wu: the same without T; kkt: T only."""
+    U written once; wu: the same without T; kkt: T only; solve: one right-hand side R read and
+    X written (R and X in the value-head layout, like V and U)."""
     gb = 4 if gated else 0
     if entry == "kkt":
         return tokens * (hq * dk * esz + hv * (4 + gb + 4 * C))
+    if entry == "solve":
+        return tokens * (hq * dk * esz + hv * (dv * esz + 4 + gb + dv * esz))
     t_bytes = 4 * C if entry == "wy" else 0
     per_token = hq * dk * esz + hv * (dv * esz + 4 + gb + t_bytes + dk * esz + dv * esz)
     return tokens * per_token
@@ -121,18 +124,25 @@ def cpu_threads():
     return max(1, min(16, host_cores()))
 
 
-def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0):
+def cpu_baseline(inp, units_per_pass, tokens_per_pass, seconds=10.0, entry="wy"):
     """The fp64 oracle, as it stands, on the same workload: whole passes until ~`seconds` on
-    every usable host core, then until ~`seconds`/3 on one core."""
+    every usable host core, then until ~`seconds`/3 on one core.  entry "solve" times the
+    oracle's right-hand-side solve with v as the right-hand side; every other entry the whole
+    preparation (T, W, U)."""
     import oracle
     lib = oracle.load()
 
     def timed(threads, budget):
         passes, t0 = 0, time.perf_counter()
         while True:
-            oracle.wy_prepare(inp["k"], inp["beta"], inp["chunk_size"], v=inp["v"],
-                              cu_seqlens=inp["cu_seqlens"], nthreads=threads, lib=lib,
-                              g=inp["g"])
+            if entry == "solve":
+                oracle.solve_rhs(inp["k"], inp["v"], inp["beta"], inp["chunk_size"],
+                                 cu_seqlens=inp["cu_seqlens"], g=inp["g"], nthreads=threads,
+                                 lib=lib)
+            else:
+                oracle.wy_prepare(inp["k"], inp["beta"], inp["chunk_size"], v=inp["v"],
+                                  cu_seqlens=inp["cu_seqlens"], nthreads=threads, lib=lib,
+                                  g=inp["g"])
             passes += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -281,9 +291,9 @@ def measure(args, entry, w, inp, dev, lib, ramp=True):
                          T=torch.empty(B, T, Hv, C, dtype=torch.float32, device=dev)
                          if entry in ("wy", "kkt") else None,
                          W=torch.empty(B, T, Hv, dk, dtype=tdt, device=dev)
-                         if entry != "kkt" else None,
+                         if entry not in ("kkt", "solve") else None,
                          U=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev)
-                         if entry != "kkt" else None,
+                         if entry != "kkt" else None,  # solve: X
                          q=(q0 if first else q0.clone()) if fwd_entry else None,
                          o=torch.empty(B, T, Hv, dv, dtype=tdt, device=dev) if fwd_entry else None,
                          hT=torch.empty(nstates, Hv, dk, dv, dtype=torch.float32, device=dev)
@@ -324,6 +334,8 @@ def measure(args, entry, w, inp, dev, lib, ramp=True):
             st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
         elif entry == "kkt":
             st = lib.wyp_kkt_solve(pprob, kp, gp, bp, cu_ptr, tp, sp)
+        elif entry == "solve":  # the right-hand side is v, X goes to the U buffer
+            st = lib.wyp_solve_rhs(pprob, kp, vp, gp, bp, cu_ptr, up, sp)
         elif entry == "bwd":
             dwp, dup, dkp, dvp, dbp, dgp = bcalls[i % nsets]
             st = lib.wyp_wy_backward(pprob, kp, vp, gp, bp, cu_ptr, None, dwp, dup, dkp, dvp, dbp,
@@ -378,7 +390,8 @@ def measure(args, entry, w, inp, dev, lib, ramp=True):
     # The outputs the last timed launch writes are filled with NaN first, so the check after
     # the timed region fails if the timed launches did not write them.
     last = (args.steps - 1) % nsets
-    outs = {"wy": ("T", "W", "U"), "wu": ("W", "U"), "kkt": ("T",), "fwd": ("o", "hT"),
+    outs = {"wy": ("T", "W", "U"), "wu": ("W", "U"), "kkt": ("T",), "solve": ("U",),
+            "fwd": ("o", "hT"),
             "gdn": ("W", "U", "o", "hT"),
             "bwd": ("dk", "dv", "db") + (("dg",) if gated else ())}[entry]
     for n in outs:
@@ -453,9 +466,12 @@ def main(argv=None):
                     help="seeded workload index (2 = the headline C=64 workload)")
     ap.add_argument("--chunk-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--entry", choices=("wy", "wu", "kkt", "fwd", "gdn", "bwd"), default="wy",
+    ap.add_argument("--entry", choices=("wy", "wu", "kkt", "solve", "fwd", "gdn", "bwd"),
+                    default="wy",
                     help="wy: wyp_wy_prepare (T, W, U; the headline); wu: wyp_wu_prepare "
-                         "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only); fwd: wyp_chunk_fwd "
+                         "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only); solve: "
+                         "wyp_solve_rhs with v as the one right-hand side (X = U, T never "
+                         "formed); fwd: wyp_chunk_fwd "
                          "(state recurrence and output from prepared W, U; C = 64); gdn: the "
                          "whole forward, wyp_wu_prepare then wyp_chunk_fwd; bwd: "
                          "wyp_wy_backward (dk, dv, dbeta, dg from dW, dU; no dT; C = 64)")
@@ -576,7 +592,7 @@ def main(argv=None):
             out["cpu_baseline"] = cpu_baseline_bwd(inp, units, tokens, args.workload,
                                                    args.cpu_seconds)
         else:
-            out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds)
+            out["cpu_baseline"] = cpu_baseline(inp, units, tokens, args.cpu_seconds, args.entry)
     print(json.dumps(out), flush=True)
     return 0
 

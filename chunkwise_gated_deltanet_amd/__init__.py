@@ -18,8 +18,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "wy_backward", "chunk_fwd",
+__all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "solve_rhs", "wy_backward", "chunk_fwd",
            "chunk_gated_delta_rule", "wyp_wy_prepare", "wyp_kkt_solve", "wyp_wu_prepare",
+           "wyp_solve_rhs",
            "wyp_wy_backward", "wyp_chunk_fwd", "cp_segment_chunks", "load_library", "Problem",
            "LIB_PATH", "WyprepError"]
 
@@ -27,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.s
 
 WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
 WYP_BF16, WYP_F32 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class WyprepError(RuntimeError):
@@ -72,6 +73,8 @@ def load_library(path: str | None = None):
     lib.wyp_wy_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.wyp_wu_prepare.restype = ctypes.c_int32
     lib.wyp_wu_prepare.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.wyp_solve_rhs.restype = ctypes.c_int32
+    lib.wyp_solve_rhs.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P]
     lib.wyp_chunk_fwd.restype = ctypes.c_int32
     lib.wyp_chunk_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                   _P, _P, _P, _P]
@@ -232,6 +235,20 @@ def wu_prepare(k, v, beta, chunk_size, cu_seqlens=None, W_out=None, U_out=None, 
     return W_out, U_out
 
 
+def solve_rhs(k, rhs, beta, chunk_size, cu_seqlens=None, X_out=None, g=None):
+    """X = A^{-1} diag(beta) R per chunk and value head, T never formed (rhs = v gives U); see
+    wyp_solve_rhs.  rhs [B,T,Hv,128] in k's dtype; returns X of the same shape and dtype."""
+    lib = load_library()
+    p = _problem(k, beta, chunk_size, cu_seqlens, v=rhs)
+    gp = _gate_ptr(g, beta)
+    X_out = _out(X_out, tuple(rhs.shape), k.dtype, k.device, "X_out")
+    st = lib.wyp_solve_rhs(ctypes.byref(p), k.data_ptr(), rhs.data_ptr(), gp, beta.data_ptr(),
+                           cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                           X_out.data_ptr(), _stream(k.device))
+    _check(lib, st)
+    return X_out
+
+
 def wy_backward(k, v, beta, chunk_size, dW, dU, dT=None, g=None, cu_seqlens=None):
     """(dk, dv, dbeta, dg): the gradient of <dT,T> + <dW,W> + <dU,U> through wy_prepare with
     respect to k, v, beta and g (dg None without gates); see wyp_wy_backward.  dW, dU in k's
@@ -368,5 +385,6 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
 wyp_kkt_solve = kkt_solve
 wyp_wy_prepare = wy_prepare
 wyp_wu_prepare = wu_prepare
+wyp_solve_rhs = solve_rhs
 wyp_chunk_fwd = chunk_fwd
 wyp_wy_backward = wy_backward

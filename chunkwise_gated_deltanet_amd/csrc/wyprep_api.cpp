@@ -65,7 +65,7 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
     if (!k || !beta) return fail(WYP_ERR_INVALID_ARGUMENT, "k and beta must be non-NULL");
     if (want_t && !T) return fail(WYP_ERR_INVALID_ARGUMENT, "T_out must be non-NULL");
     if (want_wu && (!v || !W || !U))
-        return fail(WYP_ERR_INVALID_ARGUMENT, "v, W_out and U_out must be non-NULL");
+        return fail(WYP_ERR_INVALID_ARGUMENT, "v (rhs), W_out and U_out (X_out) must be non-NULL");
     if (!aligned(k, 16) || (want_t && !aligned(T, 16)) ||
         (want_wu && (!aligned(v, 16) || !aligned(W, 16) || !aligned(U, 16))))
         return fail(WYP_ERR_INVALID_ARGUMENT, "k, v, T_out, W_out and U_out must be 16-byte aligned");
@@ -266,6 +266,25 @@ wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void*
                           void* W_out, void* U_out, void* stream)
 {
     return run(problem, k, v, g, beta, cu_seqlens, nullptr, W_out, U_out, false, true, stream);
+}
+
+wyp_status wyp_solve_rhs(const wyp_problem* problem, const void* k, const void* rhs,
+                         const float* g, const float* beta, const int32_t* cu_seqlens,
+                         void* X_out, void* stream)
+{
+    g_last_error[0] = '\0';
+    wyp::LaunchArgs args{};
+    bool empty = false;
+    // the checks of wy_prepare's W / U path, with rhs in v's place and X_out in U's (and W's)
+    const wyp_status st = validate(problem, k, rhs, g, beta, cu_seqlens, nullptr, X_out, X_out,
+                                   false, true, &args, &empty);
+    if (st != WYP_OK || empty) return st;
+    args.W = nullptr;
+    args.solve = 1;
+    char msg[256] = "";
+    if (wyp::launch(args, stream, msg, sizeof msg) != 0)
+        return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
+    return WYP_OK;
 }
 
 }  // extern "C"

@@ -60,11 +60,12 @@
 namespace wyp {
 namespace {
 
-// What one launch writes: T (kkt_solve, wy_prepare), W and U (wy_prepare, wu_prepare); and
-// whether it reads log gates g.
+// What one launch writes: T (kkt_solve, wy_prepare), W and U (wy_prepare, wu_prepare), or X for
+// one right-hand side (solve_rhs); and whether it reads log gates g.
 constexpr int kModeT = 1;
 constexpr int kModeWU = 2;
 constexpr int kModeGate = 4;
+constexpr int kModeSolve = 8;
 
 // LDS plan of one workgroup.  K and V rows carry 16 bytes of padding and T rows 4 floats, so
 // 16-byte reads of one column chunk by 16 consecutive rows spread over all banks.  V never
@@ -99,8 +100,9 @@ struct WavesPerEu {
 
 // a1: K, V and beta of one unit in flight to registers, then committed to LDS.  K and beta
 // are committed at the start of their unit; V only after that unit's T tile has been used.
-template <int C, int ESZ, int KROW, bool WU, bool GT>
+template <int C, int ESZ, int KROW, bool RV, bool GT>
 struct Prefetch {
+    static constexpr bool WU = RV;  // V (or the right-hand side) is loaded
     static constexpr int CPR = kD * ESZ / 16;  // 16-byte chunks per row
     static constexpr int NIT = C * CPR / kThreads;
     static constexpr int NG = C > 64 ? 2 : 1;  // log gates per lane of wave 0
@@ -875,6 +877,69 @@ __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, 
     store_rows<C, 4, KROW>(Vraw, p.U, u, p.hv, tid);
 }
 
+// The single right-hand side ([Inv] section 5, item 10: T used once is not materialised; the
+// substitution is applied to the right-hand side): X = A^{-1} diag(beta) R by block forward
+// substitution over the C/16 row blocks,
+//     X_i = L_ii^{-1} (diag(beta_i) R_i - sum_{j<i} A_ij X_j),
+// with L_ii^{-1} the inverted diagonal blocks (a5) and A_ij the sub-diagonal blocks of A as
+// form_a left them; the coupling levels that would fill in T are never run.  Wave w owns the 32
+// columns 32 w .. 32 w + 31 of R and X (two column tiles) for every row block, so the waves never
+// wait for each other.  Both products run on fp32 MFMA 16x16x4: the accumulator of X_j (element r
+// of lane 16 g + c is X_j[4 g + r][c]) is exactly the B operand the later products take, so X
+// stays in registers; R_i is read from LDS in that layout and X_i written back over it (same
+// wave, same columns), as bf16 (or fp32) for the row store.
+template <int C, int DT, int KROW, class TL>
+__device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs, int tid)
+{
+    constexpr int NB = C / 16;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 X[NB][2];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+            // A_ij row 16 i + lr, columns 16 j + 4 lg .. + 3: the A operand of all four k steps
+            const f32x4 a = *reinterpret_cast<const f32x4*>(Ts + TL::off(16 * i + lr, 16 * j + 4 * lg));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], X[j][c][q], acc[c], 0, 0, 0);
+        }
+        const f32x4 inv = *reinterpret_cast<const f32x4*>(Ts + TL::off(16 * i + lr, 16 * i + 4 * lg));
+        const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * i + 4 * lg);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int col = 32 * wave + 16 * c + lr;
+            f32x4 y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * lg + r;
+                float rv;
+                if constexpr (DT == 0)
+                    rv = static_cast<float>(reinterpret_cast<const __bf16*>(Rraw)[row * KROW + col]);
+                else
+                    rv = reinterpret_cast<const float*>(Rraw)[row * KROW + col];
+                y[r] = bet[r] * rv - acc[c][r];
+            }
+            f32x4 x = zero4();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x = __builtin_amdgcn_mfma_f32_16x16x4f32(inv[q], y[q], x, 0, 0, 0);
+            X[i][c] = x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * lg + r;
+                if constexpr (DT == 0)
+                    reinterpret_cast<__bf16*>(Rraw)[row * KROW + col] = static_cast<__bf16>(x[r]);
+                else
+                    reinterpret_cast<float*>(Rraw)[row * KROW + col] = x[r];
+            }
+        }
+    }
+}
+
 // One unit, from committing its prefetched K to storing its outputs; its own V and the next
 // unit's K are issued on the way.  Returns the next unit.
 template <int C, int DT, int M, class PF>
@@ -883,6 +948,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
 {
     constexpr bool WU = (M & kModeWU) != 0;
     constexpr bool GT = (M & kModeGate) != 0;
+    constexpr bool SOLVE = (M & kModeSolve) != 0;
     using L = Lds<C, DT, WU>;
     unsigned char* Kraw = smem + L::OFF_K;
     float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
@@ -913,6 +979,17 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
         if (nxt.n > 0) pf.issue_k(p, nxt, tid);
     }
     __syncthreads();
+    if constexpr (SOLVE) {
+        // K is no longer read (form_a finished before the last barrier but one): the right-hand
+        // side takes its place, and X is staged over it
+        pf.commit_v(Kraw, tid);
+        __syncthreads();
+        solve_rhs<C, DT, L::KROW, TL>(Kraw, Ts, bs, tid);
+        __syncthreads();
+        store_rows<C, L::ESZ, L::KROW>(Kraw, p.U, cur, p.hv, tid);
+        __syncthreads();  // LDS is rewritten by the next unit
+        return nxt;
+    }
     if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
     if constexpr (C >= 64) coupling_level<C, 32, TL>(Ts, tid);
     if constexpr (C >= 128) coupling_level<C, 64, TL>(Ts, tid);
@@ -943,7 +1020,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
 
     Unit cur = map_unit<C>(p, info, first, threadIdx.x);
     if (cur.n <= 0) return;  // uniform per workgroup
-    Prefetch<C, L::ESZ, L::KROW, WU, (M & kModeGate) != 0> pf;
+    Prefetch<C, L::ESZ, L::KROW, WU || (M & kModeSolve) != 0, (M & kModeGate) != 0> pf;
     pf.issue_k(p, cur, threadIdx.x);
     // The first unit is peeled off the loop: the loop head is then reached only from the end
     // of a unit, so the memory-counter waits inside see one issue history.
@@ -985,7 +1062,7 @@ int resident_grid(int device, hipError_t* err)
         // With W and U, more than four resident workgroups per CU only add HBM streams: at C = 32
         // (seven fit) four were measured faster, e.g. 29.6 vs 34.6 us at B=1 T=8192 H=16, while
         // T alone gains from all seven.
-        constexpr int kMaxPerCu = (M & kModeWU) != 0 ? 4 : 1 << 10;
+        constexpr int kMaxPerCu = (M & (kModeWU | kModeSolve)) != 0 ? 4 : 1 << 10;
         if (per_cu > kMaxPerCu) per_cu = kMaxPerCu;
         cached[device] = (per_cu > 0 ? per_cu : 1) * cus;
     }
@@ -1044,6 +1121,7 @@ int launch_c(const LaunchArgs& a, hipStream_t s, char* msg, int len)
 template <int DT, int G>
 int launch_m(const LaunchArgs& a, hipStream_t s, char* msg, int len)
 {
+    if (a.solve) return launch_c<DT, kModeSolve | G>(a, s, msg, len);
     const bool wu = a.W != nullptr, t = a.T != nullptr;
     if (wu && t) return launch_c<DT, kModeT | kModeWU | G>(a, s, msg, len);
     if (wu) return launch_c<DT, kModeWU | G>(a, s, msg, len);

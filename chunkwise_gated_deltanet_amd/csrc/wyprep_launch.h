@@ -25,6 +25,7 @@ struct LaunchArgs {
     int32_t chunk_size;
     int32_t kv_dtype;         // 0 bf16, 1 f32
     int64_t chunk_slots;      // chunks (B x T) or an upper bound on them (packed)
+    int32_t solve;            // 1: single right-hand side (v holds R, U receives X)
 };
 
 // Enqueues the kernel on `stream`.  Returns 0 or the hipError_t value; fills `msg` on error.

@@ -74,8 +74,8 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 6  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp;
-                              6: wyp_chunk_fwd_cp_noalloc */
+#define WYP_ABI_VERSION 7  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp;
+                              6: wyp_chunk_fwd_cp_noalloc; 7: wyp_solve_rhs */
 
 /* Bytes of the static device scratch behind wyp_chunk_fwd_cp_noalloc (one array per GPU). */
 #define WYP_CP_SCRATCH_BYTES (32 * 1024 * 1024)
@@ -133,6 +133,24 @@ wyp_status wyp_wy_prepare(const wyp_problem* problem, const void* k, const void*
 wyp_status wyp_wu_prepare(const wyp_problem* problem, const void* k, const void* v,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           void* W_out, void* U_out, void* stream);
+
+/* One right-hand side, T never formed ([Inv] section 5 (summary), item 10: whether to
+ * materialise T depends on how often it is used; used once, the forward substitution is applied
+ * straight to the right-hand side).  For every chunk and value head h:
+ *     X = A^{-1} diag(beta) R        (A as above, gates included when g is given)
+ * where R holds the chunk's rows of rhs for value head h.  With rhs = v, X is U of
+ * wyp_wy_prepare (to rounding; a different order of operations).  Computed by block forward
+ * substitution over the chunk's 16-row blocks, X_i = L_ii^{-1} (diag(beta_i) R_i -
+ * sum_{j<i} A_ij X_j), with only the 16x16 diagonal blocks inverted on chip (fp32 throughout);
+ * nothing of T is written or formed beyond those blocks.
+ *   rhs    [B, T, Hv, dv]   kv_dtype (dv = 128)
+ *   X_out  [B, T, Hv, dv]   kv_dtype
+ *   k, g, beta, cu_seqlens, stream   as for wyp_wy_prepare
+ * Alignment: k, rhs, X_out 16 bytes; beta, g, cu_seqlens 4 bytes.  rhs and X_out must not
+ * overlap.  Supported as wyp_wy_prepare (C in {32, 64, 128}, bf16 or fp32). */
+wyp_status wyp_solve_rhs(const wyp_problem* problem, const void* k, const void* rhs,
+                         const float* g, const float* beta, const int32_t* cu_seqlens,
+                         void* X_out, void* stream);
 
 /* The chunked forward that consumes W and U ([QLA] "FLA GDN Chunked Prefill 面临的主要问题":
  * after the WY step the pipeline carries the state across chunks and forms the output; [QLA]

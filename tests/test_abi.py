@@ -29,7 +29,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"wyp_abi_version", "wyp_status_string", "wyp_last_error",
-                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_chunk_fwd",
+                          "wyp_kkt_solve", "wyp_wy_prepare", "wyp_wu_prepare", "wyp_solve_rhs",
+                          "wyp_chunk_fwd",
                           "wyp_wy_backward", "wyp_chunk_fwd_cp", "wyp_chunk_fwd_cp_noalloc",
                           "wyp_chunk_fwd_cp_workspace_bytes"}
     for name in names:
@@ -37,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 6 == cg.ABI_VERSION
+    assert lib.wyp_abi_version() == 7 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -224,3 +225,18 @@ def test_chunk_fwd_cp_noalloc_rejects_before_any_hip_call(lib):
     assert call(p, 0) == 1
     assert call(good(chunk_size=32), 4) == 2
     assert call(good(seqlen=0), 4) == 0          # no tokens, no final state: a no-op
+
+
+def test_solve_rhs_rejects_before_any_hip_call(lib):
+    def call(p, k=FAKE, rhs=FAKE, beta=FAKE, X=FAKE, g=None, cu=None):
+        return lib.wyp_solve_rhs(ctypes.byref(p) if p is not None else None, k, rhs, g, beta, cu,
+                                 X, None)
+    assert call(None) == 1
+    assert call(good(), rhs=None) == 1
+    assert call(good(), X=None) == 1
+    assert call(good(), X=FAKE + 8) == 1
+    assert call(good(), rhs=FAKE + 8) == 1
+    assert call(good(chunk_size=48)) == 2
+    assert call(good(head_dim_v=64)) == 2
+    assert call(good(num_v_heads=3)) == 1
+    assert call(good(seqlen=0), k=None, rhs=None, beta=None, X=None) == 0

@@ -89,3 +89,11 @@ def test_extra_workloads_cover_the_c64_configs_and_the_chunk_study():
 
 def test_cpu_threads_are_capped_and_host_cores_recorded():
     assert 1 <= bench.cpu_threads() <= min(16, bench.host_cores())
+
+
+def test_solve_bytes():
+    # one right-hand side: k once per key head; R, beta read and X written per value head
+    tok, hq, hv, d = 1000, 16, 64, 128
+    assert bench.algorithmic_bytes(tok, hq, hv, d, d, 64, 2, entry="solve") == \
+        tok * (hq * d * 2 + hv * (d * 2 + 4 + d * 2))
+    assert bench.profile_name("solve", synth.workload(2), 1, 8192, 0) == "solve_rhs_bf16_c64_b1t8192h16"
