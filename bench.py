@@ -218,8 +218,9 @@ def cpu_baseline_fwd(inp, seconds=10.0):
 
 
 # Extra workloads timed after the headline (each with its own roofline): the other C = 64
-# configurations and the chunk-size study on B=4 T=4096 H=32.
-DEFAULT_EXTRAS = "3:32,3:64,3:128,5:64"
+# configurations, the chunk-size study on B=4 T=4096 H=32, and 1024 short packed sequences (the
+# packed-sequence work map under load).
+DEFAULT_EXTRAS = "3:32,3:64,3:128,5:64,6:64"
 
 
 def parse_extras(text):

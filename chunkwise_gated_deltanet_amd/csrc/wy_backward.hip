@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
     // and the next job's inputs are in flight while the current one computes.
     const uint32_t G = gridDim.x;  // a multiple of 8
     int64_t logical = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
-    Unit u = map_unit<kC>(mp, info, logical, tid);
+    Unit u = map_unit<kC>(mp, info, logical, G, tid);
     if (u.n <= 0) return;  // uniform
     int hv = u.hv * r;
     bool new_unit = true;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         bool nnew = false;
         if (nhv == (hk + 1) * r) {  // uniform
             logical += G;
-            nu = map_unit<kC>(mp, info, logical, tid);
+            nu = map_unit<kC>(mp, info, logical, G, tid);
             nhv = nu.hv * r;
             nnew = true;
         }

@@ -73,7 +73,9 @@ wyp_status validate(const wyp_problem* p, const void* k, const void* v, const fl
     if (g && !aligned(g, 4)) return fail(WYP_ERR_INVALID_ARGUMENT, "g is not 4-byte aligned");
 
     int64_t slots;
-    if (cu) slots = (p->seqlen + C - 1) / C + p->num_seqs - 1;  // >= sum of per-sequence chunks
+    // packed: sequence s owns slots [floor(cu[s] / C) + s, floor(cu[s + 1] / C) + s + 1), room for
+    // its chunks and at most one empty slot (the kernels skip empty slots)
+    if (cu) slots = p->seqlen / C + p->num_seqs;
     else slots = static_cast<int64_t>(p->batch) * ((p->seqlen + C - 1) / C);
     // the launch grid is slots x (Hv or Hq) workgroups, rounded up to a multiple of 8
     const int64_t units = slots * p->num_v_heads;

@@ -123,18 +123,49 @@ struct Unit {
     int hv;        // value head
 };
 
-// a0: logical unit index -> Unit (n == 0 past the end).  Packed batches: wave 0 scans
-// cu_seqlens 64 sequences at a time; the result goes through LDS (one barrier).
+// a0: logical unit index -> Unit.  logical = slot * Hv + value head.  Batch rows: slot b * cps + c
+// is chunk c of row b (cps chunks per row).  Packed sequences: sequence s owns the slots
+// [B_s, B_{s+1}) with B_s = floor(cu[s] / C) + s.  B is strictly increasing and leaves room for all
+// ceil(len_s / C) chunks of sequence s (B_{s+1} - B_s - ceil(len_s / C) is 0 or 1), so a slot is
+// found from cu_seqlens alone, by a search over s, without prefix sums of chunk counts; a slot past
+// its sequence's last chunk is empty.  Host side: floor(T / C) + N slots.
+
+// Packed: wave 0 finds the sequence of `slot` by a 64-ary search over B (one round trip to
+// cu_seqlens while N <= 64, two while N <= 4096, ...) and returns (sequence, chunk); chunk = -1 for
+// an empty slot.  Every lane of wave 0 gets the same result; other waves must not call it.
 template <int C>
-__device__ Unit map_unit(const Params& p, int* info, int64_t logical64, int tid)
+__device__ inline void find_slot(const Params& p, uint32_t slot, int lane, int* seq, int* chunk)
 {
-    Unit u{0, 0, 0};
-    if (logical64 >= p.units) return u;
-    // units < 2^31 (checked on the host), so 32-bit arithmetic suffices here
-    const uint32_t logical = static_cast<uint32_t>(logical64);
-    const uint32_t hvn = static_cast<uint32_t>(p.hv);
-    u.hv = static_cast<int>(logical % hvn);
-    const uint32_t slot = logical / hvn;
+    int lo = 0, hi = p.num_seqs;  // B_lo <= slot (B_0 = 0), and s < hi
+    int cu_s = 0, cu_s1 = 0;
+    while (true) {  // uniform
+        const int span = hi - lo;
+        const int step = (span + 63) / 64;
+        const int s = lo + lane * step;
+        const bool in = s < hi;
+        const int c0 = in ? p.cu[s] : 0;
+        // in the last round (step 1) each lane also takes its sequence's end
+        const int c1 = (in && step == 1) ? p.cu[s + 1] : 0;
+        const bool below = in && static_cast<uint32_t>(c0 / C + s) <= slot;
+        const unsigned long long m = __ballot(below);  // lane 0 is always set
+        const int L = 63 - __clzll(m);
+        lo += L * step;
+        hi = min(lo + step, hi);
+        if (step == 1) {
+            cu_s = __shfl(c0, L);
+            cu_s1 = __shfl(c1, L);
+            break;
+        }
+    }
+    *seq = lo;
+    const int c = static_cast<int>(slot) - (cu_s / C + lo);
+    *chunk = c < (cu_s1 - cu_s + C - 1) / C ? c : -1;
+}
+
+template <int C>
+__device__ inline Unit unit_of_slot(const Params& p, uint32_t slot, int hv, int seq, int chunk)
+{
+    Unit u{0, 0, hv};
     if (p.cu == nullptr) {
         const uint32_t cps = static_cast<uint32_t>((p.seqlen + C - 1) / C);
         const uint32_t b = slot / cps, c = slot % cps;
@@ -142,45 +173,63 @@ __device__ Unit map_unit(const Params& p, int* info, int64_t logical64, int tid)
         u.n = min(C, p.seqlen - static_cast<int>(c) * C);
         return u;
     }
-    const int lane = tid & 63;
-    if (tid < 64) {
-        int64_t run = 0;
-        int found_s = -1, found_c = 0;
-        for (int base = 0; base < p.num_seqs; base += 64) {
-            const int s = base + lane;
-            int cnt = 0;
-            if (s < p.num_seqs) cnt = (p.cu[s + 1] - p.cu[s] + C - 1) / C;
-            int incl = cnt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int t = __shfl_up(incl, d);
-                if (lane >= d) incl += t;
-            }
-            const int excl = incl - cnt;
-            const bool hit = cnt > 0 && static_cast<int64_t>(slot) >= run + excl &&
-                             static_cast<int64_t>(slot) < run + incl;
-            const unsigned long long m = __ballot(hit);
-            if (m) {
-                const int src = __ffsll(m) - 1;
-                found_s = __shfl(s, src);
-                found_c = static_cast<int>(static_cast<int64_t>(slot) - run - __shfl(excl, src));
-                break;
-            }
-            run += __shfl(incl, 63);
-        }
-        if (lane == 0) {
-            info[0] = found_s;
-            info[1] = found_c;
-        }
-    }
-    __syncthreads();
-    const int s = uniform(info[0]);
-    const int c = uniform(info[1]);
-    if (s < 0) return u;
-    const int s0 = uniform(p.cu[s]), s1 = uniform(p.cu[s + 1]);
-    u.tok0 = s0 + static_cast<int64_t>(c) * C;
+    const int s0 = uniform(p.cu[seq]), s1 = uniform(p.cu[seq + 1]);
+    u.tok0 = s0 + static_cast<int64_t>(chunk) * C;
     u.n = min(C, s1 - static_cast<int>(u.tok0));
     return u;
+}
+
+// Packed, first half: wave 0 finds the first non-empty unit at logical, logical + stride, ... and
+// leaves it in info (info[0] = sequence or -1 past the end, info[1] = chunk, info[2..3] = its
+// logical index); the caller's next barrier publishes it.  Nothing to do for batch rows.
+template <int C>
+__device__ inline void map_search(const Params& p, int* info, int64_t logical, int64_t stride, int tid)
+{
+    if (p.cu == nullptr || tid >= 64) return;
+    int seq = -1, chunk = 0;
+    while (logical < p.units) {  // uniform in wave 0
+        // units < 2^31 (checked on the host), so 32-bit arithmetic suffices here
+        const uint32_t slot = static_cast<uint32_t>(logical) / static_cast<uint32_t>(p.hv);
+        find_slot<C>(p, slot, tid, &seq, &chunk);
+        if (chunk >= 0) break;
+        seq = -1;
+        logical += stride;
+    }
+    if (tid == 0) {
+        info[0] = seq;
+        info[1] = chunk;
+        info[2] = static_cast<int>(logical & 0xffffffff);
+        info[3] = static_cast<int>(logical >> 32);
+    }
+}
+
+// Second half, after that barrier: the unit (n == 0 past the end); `logical` moves to its index.
+template <int C>
+__device__ inline Unit map_read(const Params& p, const int* info, int64_t& logical)
+{
+    if (p.cu == nullptr) {
+        if (logical >= p.units) return Unit{0, 0, 0};
+        const uint32_t l32 = static_cast<uint32_t>(logical), hvn = static_cast<uint32_t>(p.hv);
+        return unit_of_slot<C>(p, l32 / hvn, static_cast<int>(l32 % hvn), 0, 0);
+    }
+    const int seq = uniform(info[0]);
+    logical = static_cast<int64_t>(static_cast<uint32_t>(uniform(info[2]))) |
+              (static_cast<int64_t>(uniform(info[3])) << 32);
+    if (seq < 0) return Unit{0, 0, 0};
+    const uint32_t l32 = static_cast<uint32_t>(logical), hvn = static_cast<uint32_t>(p.hv);
+    return unit_of_slot<C>(p, l32 / hvn, static_cast<int>(l32 % hvn), seq, uniform(info[1]));
+}
+
+// Both halves with their own barrier (packed only): the first non-empty unit at logical,
+// logical + stride, ...; `logical` moves to its index.
+template <int C>
+__device__ inline Unit map_unit(const Params& p, int* info, int64_t& logical, int64_t stride, int tid)
+{
+    if (p.cu != nullptr) {
+        map_search<C>(p, info, logical, stride, tid);
+        __syncthreads();
+    }
+    return map_read<C>(p, info, logical);
 }
 
 // Lower 16x16 tile t (row-major over I >= J) -> (I, J).

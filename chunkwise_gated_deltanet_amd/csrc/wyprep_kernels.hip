@@ -10,8 +10,8 @@
 // persistent: the grid holds one resident round, and each workgroup walks a strided list of
 // units.  While it computes one unit, the next unit's K, V and beta are already in flight
 // into registers, so HBM traffic never waits for the arithmetic.  Per unit:
-//   a0  map the unit to (first token, length n, value head); packed batches scan cu_seqlens
-//       on the device;
+//   a0  map the unit to (first token, length n, value head); packed batches search cu_seqlens
+//       on the device (wyprep_device.h);
 //   a1  K (n x 128), V (n x 128) and beta (n) arrive through bounded buffer loads: rows
 //       n..C-1 of a short chunk read as zero with beta = 0 ([Inv] leaves tails open; this is
 //       the padded reading, A = blockdiag(A_n, I), so T = blockdiag(T_n, I)).  K and beta go
@@ -944,7 +944,7 @@ __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs,
 // unit's K are issued on the way.  Returns the next unit.
 template <int C, int DT, int M, class PF>
 __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, PF& pf, const Unit& cur,
-                                         int64_t next)
+                                         int64_t& next, int64_t stride)
 {
     constexpr bool WU = (M & kModeWU) != 0;
     constexpr bool GT = (M & kModeGate) != 0;
@@ -959,14 +959,18 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     pf.commit_k(Kraw, bs, tid);
+    // a0 for the next unit (packed sequences: wave 0 searches cu_seqlens) before this unit's V is
+    // issued: loads complete in order, so a search issued behind V would wait for V, and with it,
+    // at the barrier, every wave would wait before forming A.
+    map_search<C>(p, info, next, stride, tid);
     __syncthreads();
+    const Unit nxt = map_read<C>(p, info, next);
     // This unit's V is needed only after its inversion; the next unit's K at the next unit's
     // start.  Issued in that order, a wait for either never waits for the other.  From C = 64
     // on the next K is issued after the diagonal inversions (which one or two of the four waves
     // run), not right behind V, where the two compete for the CU's address units: at C = 128
     // 2-4% faster, at C = 64 3% on the headline, 5% on the packed workload and 7% for T alone.
     pf.issue_v(p, cur, tid);
-    const Unit nxt = map_unit<C>(p, info, next, tid);
     if constexpr (C < 64) {
         if (nxt.n > 0) pf.issue_k(p, nxt, tid);
     }
@@ -1018,17 +1022,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     const uint32_t G = gridDim.x;  // a multiple of 8
     const int64_t first = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
 
-    Unit cur = map_unit<C>(p, info, first, threadIdx.x);
+    int64_t logical = first;
+    Unit cur = map_unit<C>(p, info, logical, G, threadIdx.x);
     if (cur.n <= 0) return;  // uniform per workgroup
+    __syncthreads();  // every wave has read info before the next unit's search rewrites it
     Prefetch<C, L::ESZ, L::KROW, WU || (M & kModeSolve) != 0, (M & kModeGate) != 0> pf;
     pf.issue_k(p, cur, threadIdx.x);
     // The first unit is peeled off the loop: the loop head is then reached only from the end
     // of a unit, so the memory-counter waits inside see one issue history.
-    int64_t next = first + G;
-    cur = run_unit<C, DT, M>(p, smem, pf, cur, next);
+    int64_t next = logical + G;
+    cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G);
     while (cur.n > 0) {  // uniform
         next += G;
-        cur = run_unit<C, DT, M>(p, smem, pf, cur, next);
+        cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G);
     }
 }
 

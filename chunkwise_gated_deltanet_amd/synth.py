@@ -71,7 +71,8 @@ class Workload:
 
 
 def workloads() -> dict:
-    """The five seeded workloads (sizes as stated by the hot path's target)."""
+    """The five seeded workloads (sizes as stated by the hot path's target), and a sixth that
+    stresses the packed-sequence work map: 1024 short sequences of 1..65 tokens."""
     return {
         1: Workload("tiny fp32: B=1 T=256 H=2/2 C=32", 1, 256, 2, 2, 128, 128, 32, "f32", 1.0, 1),
         2: Workload("B=1 T=8192 H=16/16 C=64 bf16", 1, 8192, 16, 16, 128, 128, 64, "bf16", 1.5,
@@ -82,6 +83,8 @@ def workloads() -> dict:
                     4),
         5: Workload("packed 8 seqs U[300,16384] Hq=16 Hv=64 C=64 bf16", 1, 0, 16, 64, 128, 128,
                     64, "bf16", 1.0, 5, seq_range=(300, 16384, 8)),
+        6: Workload("packed 1024 seqs U[1,65] Hq=16 Hv=16 C=64 bf16", 1, 0, 16, 16, 128, 128, 64,
+                    "bf16", 1.0, 6, seq_range=(1, 65, 1024)),
     }
 
 

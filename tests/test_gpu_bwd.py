@@ -88,6 +88,19 @@ def test_wy_backward_identical_keys(gpu):
     check(inp, dW, dU, dT, out, "identical keys")
 
 
+def test_wy_backward_many_short_sequences(gpu):
+    """1100 packed sequences of 1..65 tokens (a few empty): the work map's search and its empty
+    slots, on the key-head units of the backward."""
+    rng = np.random.default_rng(126)
+    lens = rng.integers(1, 66, size=1100)
+    lens[rng.random(1100) < 0.05] = 0
+    inp, dW, dU, dT = make_inputs(dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4, seed=126,
+                                       gate_mu=4.0, dT=True, seqlens=[int(x) for x in lens]))
+    say(f"wy_backward 1100 short sequences, tokens={int(lens.sum())}")
+    out = run_bwd(inp, dW, dU, dT, gpu)
+    check(inp, dW, dU, dT, out, "1100 short sequences")
+
+
 def test_wy_backward_deterministic(gpu):
     import torch
     inp, dW, dU, dT = make_inputs(CASES["packed_gva_mu4_dT"])

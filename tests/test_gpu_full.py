@@ -9,6 +9,7 @@ within 1e-2 relative Frobenius over the whole tensor; every output written (outp
 pre-filled with NaN).  kkt_solve's T and wu_prepare's W, U must also equal wy_prepare's bit for
 bit (one arithmetic).  The oracle runs one range of whole chunks at a time.
 """
+import numpy as np
 import pytest
 
 from chunkwise_gated_deltanet_amd import synth
@@ -37,6 +38,31 @@ def test_mid_size_multi_unit(C, gpu):
     inp = synth.custom(1, 8000, 12, 48, C, seed=60 + C)
     say(f"mid size B=1 T=8000 H=12/48 C={C}")
     check_entry_points(inp, gpu, f"mid C={C}")
+
+
+def short_lengths(seed, count, C, zero_frac=0.05):
+    """Lengths uniform in [1, C + 1], a few of them 0: most sequences are a single short chunk."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, C + 2, size=count)
+    lens[rng.random(count) < zero_frac] = 0
+    return [int(x) for x in lens]
+
+
+# Many short packed sequences: the work map searches cu_seqlens for every unit (two rounds of the
+# search for 1200 sequences, three for 5000) and skips the slots past each sequence's last chunk.
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_many_short_sequences(C, gpu):
+    lens = short_lengths(90 + C, 1200, C)
+    inp = synth.custom(1, 0, 4, 16, C, seed=95 + C, gate_mu=4.0, seqlens=lens)
+    say(f"1200 packed sequences, lengths 1..{C + 1}, C={C}, tokens={sum(lens)}")
+    check_entry_points(inp, gpu, f"1200 seqs C={C}")
+
+
+def test_five_thousand_sequences(gpu):
+    lens = short_lengths(99, 5000, 32)
+    inp = synth.custom(1, 0, 1, 2, 32, seed=98, seqlens=lens)
+    say(f"5000 packed sequences, lengths 1..33, C=32, tokens={sum(lens)}")
+    check_entry_points(inp, gpu, "5000 seqs C=32")
 
 
 FULL = [(i, c) for i in (1, 2, 3, 4, 5) for c in (32, 64, 128)]

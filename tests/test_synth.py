@@ -47,3 +47,10 @@ def test_workload_table():
     assert ws[1].dtype == "f32" and ws[1].chunk_size == 32
     assert ws[5].num_qk_heads == 16 and ws[5].num_v_heads == 64
     assert synth.workload(3, chunk_size=128).chunk_size == 128
+
+
+def test_short_sequence_workload():
+    inp = synth.generate(synth.workload(6))
+    lens = np.diff(inp["cu_seqlens"].astype(np.int64))
+    assert len(lens) == 1024 and lens.min() >= 1 and lens.max() <= 65 and np.all(lens % 64 != 0)
+    assert inp["seqlen"] == int(lens.sum())
