@@ -131,73 +131,70 @@ struct Unit {
 // its sequence's last chunk is empty.  Host side: floor(T / C) + N slots.
 
 // Packed: wave 0 finds the sequence of `slot` by a 64-ary search over B (one round trip to
-// cu_seqlens while N <= 64, two while N <= 4096, ...) and returns (sequence, chunk); chunk = -1 for
-// an empty slot.  Every lane of wave 0 gets the same result; other waves must not call it.
+// cu_seqlens while N <= 64, two while N <= 4096, ...) and returns the chunk's first token and
+// length (n = 0 for an empty slot).  With fewer than 64 sequences, lane l may pass cu[min(l, N)]
+// in cu_lane (cached = true, loaded once per launch): the search is then one ballot and two
+// shuffles, with no memory access.  Every lane of wave 0 gets the same result; other waves must
+// not call it.
 template <int C>
-__device__ inline void find_slot(const Params& p, uint32_t slot, int lane, int* seq, int* chunk)
+__device__ inline void find_slot(const Params& p, uint32_t slot, int lane, bool cached, int cu_lane,
+                                 int64_t* tok0, int* n)
 {
     int lo = 0, hi = p.num_seqs;  // B_lo <= slot (B_0 = 0), and s < hi
     int cu_s = 0, cu_s1 = 0;
-    while (true) {  // uniform
-        const int span = hi - lo;
-        const int step = (span + 63) / 64;
-        const int s = lo + lane * step;
-        const bool in = s < hi;
-        const int c0 = in ? p.cu[s] : 0;
-        // in the last round (step 1) each lane also takes its sequence's end
-        const int c1 = (in && step == 1) ? p.cu[s + 1] : 0;
-        const bool below = in && static_cast<uint32_t>(c0 / C + s) <= slot;
+    if (cached) {  // uniform
+        const bool below = lane < hi && static_cast<uint32_t>(cu_lane / C + lane) <= slot;
         const unsigned long long m = __ballot(below);  // lane 0 is always set
-        const int L = 63 - __clzll(m);
-        lo += L * step;
-        hi = min(lo + step, hi);
-        if (step == 1) {
-            cu_s = __shfl(c0, L);
-            cu_s1 = __shfl(c1, L);
-            break;
+        lo = 63 - __clzll(m);
+        cu_s = __shfl(cu_lane, lo);
+        cu_s1 = __shfl(cu_lane, lo + 1);
+    } else {
+        while (true) {  // uniform
+            const int span = hi - lo;
+            const int step = (span + 63) / 64;
+            const int s = lo + lane * step;
+            const bool in = s < hi;
+            const int c0 = in ? p.cu[s] : 0;
+            // in the last round (step 1) each lane also takes its sequence's end
+            const int c1 = (in && step == 1) ? p.cu[s + 1] : 0;
+            const bool below = in && static_cast<uint32_t>(c0 / C + s) <= slot;
+            const unsigned long long m = __ballot(below);  // lane 0 is always set
+            const int L = 63 - __clzll(m);
+            lo += L * step;
+            hi = min(lo + step, hi);
+            if (step == 1) {
+                cu_s = __shfl(c0, L);
+                cu_s1 = __shfl(c1, L);
+                break;
+            }
         }
     }
-    *seq = lo;
     const int c = static_cast<int>(slot) - (cu_s / C + lo);
-    *chunk = c < (cu_s1 - cu_s + C - 1) / C ? c : -1;
-}
-
-template <int C>
-__device__ inline Unit unit_of_slot(const Params& p, uint32_t slot, int hv, int seq, int chunk)
-{
-    Unit u{0, 0, hv};
-    if (p.cu == nullptr) {
-        const uint32_t cps = static_cast<uint32_t>((p.seqlen + C - 1) / C);
-        const uint32_t b = slot / cps, c = slot % cps;
-        u.tok0 = static_cast<int64_t>(b) * p.seqlen + static_cast<int64_t>(c) * C;
-        u.n = min(C, p.seqlen - static_cast<int>(c) * C);
-        return u;
-    }
-    const int s0 = uniform(p.cu[seq]), s1 = uniform(p.cu[seq + 1]);
-    u.tok0 = s0 + static_cast<int64_t>(chunk) * C;
-    u.n = min(C, s1 - static_cast<int>(u.tok0));
-    return u;
+    const bool valid = c < (cu_s1 - cu_s + C - 1) / C;
+    *tok0 = cu_s + static_cast<int64_t>(c) * C;
+    *n = valid ? min(C, cu_s1 - (cu_s + c * C)) : 0;
 }
 
 // Packed, first half: wave 0 finds the first non-empty unit at logical, logical + stride, ... and
-// leaves it in info (info[0] = sequence or -1 past the end, info[1] = chunk, info[2..3] = its
+// leaves it in info (info[0] = first token, info[1] = n, 0 past the end, info[2..3] = its
 // logical index); the caller's next barrier publishes it.  Nothing to do for batch rows.
 template <int C>
-__device__ inline void map_search(const Params& p, int* info, int64_t logical, int64_t stride, int tid)
+__device__ inline void map_search(const Params& p, int* info, int64_t logical, int64_t stride, int tid,
+                                  bool cached = false, int cu_lane = 0)
 {
     if (p.cu == nullptr || tid >= 64) return;
-    int seq = -1, chunk = 0;
+    int64_t tok0 = 0;
+    int n = 0;
     while (logical < p.units) {  // uniform in wave 0
         // units < 2^31 (checked on the host), so 32-bit arithmetic suffices here
         const uint32_t slot = static_cast<uint32_t>(logical) / static_cast<uint32_t>(p.hv);
-        find_slot<C>(p, slot, tid, &seq, &chunk);
-        if (chunk >= 0) break;
-        seq = -1;
+        find_slot<C>(p, slot, tid, cached, cu_lane, &tok0, &n);
+        if (n > 0) break;
         logical += stride;
     }
     if (tid == 0) {
-        info[0] = seq;
-        info[1] = chunk;
+        info[0] = static_cast<int>(tok0);  // packed tokens fit in int32 (the problem's T)
+        info[1] = n;
         info[2] = static_cast<int>(logical & 0xffffffff);
         info[3] = static_cast<int>(logical >> 32);
     }
@@ -207,26 +204,36 @@ __device__ inline void map_search(const Params& p, int* info, int64_t logical, i
 template <int C>
 __device__ inline Unit map_read(const Params& p, const int* info, int64_t& logical)
 {
+    const uint32_t hvn = static_cast<uint32_t>(p.hv);
     if (p.cu == nullptr) {
         if (logical >= p.units) return Unit{0, 0, 0};
-        const uint32_t l32 = static_cast<uint32_t>(logical), hvn = static_cast<uint32_t>(p.hv);
-        return unit_of_slot<C>(p, l32 / hvn, static_cast<int>(l32 % hvn), 0, 0);
+        const uint32_t l32 = static_cast<uint32_t>(logical);
+        const uint32_t slot = l32 / hvn;
+        const uint32_t cps = static_cast<uint32_t>((p.seqlen + C - 1) / C);
+        const uint32_t b = slot / cps, c = slot % cps;
+        Unit u;
+        u.tok0 = static_cast<int64_t>(b) * p.seqlen + static_cast<int64_t>(c) * C;
+        u.n = min(C, p.seqlen - static_cast<int>(c) * C);
+        u.hv = static_cast<int>(l32 % hvn);
+        return u;
     }
-    const int seq = uniform(info[0]);
     logical = static_cast<int64_t>(static_cast<uint32_t>(uniform(info[2]))) |
               (static_cast<int64_t>(uniform(info[3])) << 32);
-    if (seq < 0) return Unit{0, 0, 0};
-    const uint32_t l32 = static_cast<uint32_t>(logical), hvn = static_cast<uint32_t>(p.hv);
-    return unit_of_slot<C>(p, l32 / hvn, static_cast<int>(l32 % hvn), seq, uniform(info[1]));
+    Unit u;
+    u.tok0 = uniform(info[0]);
+    u.n = uniform(info[1]);
+    u.hv = static_cast<int>(static_cast<uint32_t>(logical) % hvn);
+    return u;
 }
 
 // Both halves with their own barrier (packed only): the first non-empty unit at logical,
 // logical + stride, ...; `logical` moves to its index.
 template <int C>
-__device__ inline Unit map_unit(const Params& p, int* info, int64_t& logical, int64_t stride, int tid)
+__device__ inline Unit map_unit(const Params& p, int* info, int64_t& logical, int64_t stride, int tid,
+                                bool cached = false, int cu_lane = 0)
 {
     if (p.cu != nullptr) {
-        map_search<C>(p, info, logical, stride, tid);
+        map_search<C>(p, info, logical, stride, tid, cached, cu_lane);
         __syncthreads();
     }
     return map_read<C>(p, info, logical);

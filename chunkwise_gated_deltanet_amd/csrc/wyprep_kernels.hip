@@ -944,7 +944,7 @@ __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs,
 // unit's K are issued on the way.  Returns the next unit.
 template <int C, int DT, int M, class PF>
 __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, PF& pf, const Unit& cur,
-                                         int64_t& next, int64_t stride)
+                                         int64_t& next, int64_t stride, bool cached, int cu_lane)
 {
     constexpr bool WU = (M & kModeWU) != 0;
     constexpr bool GT = (M & kModeGate) != 0;
@@ -962,7 +962,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     // a0 for the next unit (packed sequences: wave 0 searches cu_seqlens) before this unit's V is
     // issued: loads complete in order, so a search issued behind V would wait for V, and with it,
     // at the barrier, every wave would wait before forming A.
-    map_search<C>(p, info, next, stride, tid);
+    map_search<C>(p, info, next, stride, tid, cached, cu_lane);
     __syncthreads();
     const Unit nxt = map_read<C>(p, info, next);
     // This unit's V is needed only after its inversion; the next unit's K at the next unit's
@@ -1022,8 +1022,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     const uint32_t G = gridDim.x;  // a multiple of 8
     const int64_t first = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
 
+    // Fewer than 64 packed sequences: wave 0 keeps cu_seqlens in registers (lane l: cu[min(l, N)])
+    // for the whole launch, so every unit's search is a ballot and two shuffles.
+    const bool cached = p.cu != nullptr && p.num_seqs < 64;
+    const int cu_lane = cached && threadIdx.x < 64 ? p.cu[min(static_cast<int>(threadIdx.x), p.num_seqs)] : 0;
     int64_t logical = first;
-    Unit cur = map_unit<C>(p, info, logical, G, threadIdx.x);
+    Unit cur = map_unit<C>(p, info, logical, G, threadIdx.x, cached, cu_lane);
     if (cur.n <= 0) return;  // uniform per workgroup
     __syncthreads();  // every wave has read info before the next unit's search rewrites it
     Prefetch<C, L::ESZ, L::KROW, WU || (M & kModeSolve) != 0, (M & kModeGate) != 0> pf;
@@ -1031,10 +1035,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     // The first unit is peeled off the loop: the loop head is then reached only from the end
     // of a unit, so the memory-counter waits inside see one issue history.
     int64_t next = logical + G;
-    cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G);
+    cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G, cached, cu_lane);
     while (cur.n > 0) {  // uniform
         next += G;
-        cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G);
+        cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G, cached, cu_lane);
     }
 }
 
