@@ -245,14 +245,20 @@ template <bool GT, bool LOCAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous range of work
-    // items, so the dv slices of a head (and the heads sharing a key head) meet in one L2.
-    const uint32_t Gsz = gridDim.x;  // a multiple of 8
-    const int item = static_cast<int>((blockIdx.x & 7u) * (Gsz >> 3) + (blockIdx.x >> 3));
-    if (item >= p.work) return;  // uniform
     // item = ((seq * nsegw + seg) * Hv + hv) * NSL + slice; pass 1 (LOCAL) has 8 slices (four of
     // A, four of M) and no item for the last segment
     constexpr int NSL = LOCAL ? 2 * kSlices : kSlices;
+    // Workgroups are dealt round-robin to the 8 XCDs (block b to XCD b mod 8).  A group is one
+    // (sequence or segment, key head): its value heads' dv slices read the same Q, K and W rows, so
+    // the group stays on one XCD and they meet in its L2.  Consecutive groups go to consecutive
+    // XCDs, so every XCD gets an equal share of every sequence (a contiguous range of items per
+    // XCD gave each of 8 packed sequences an XCD of its own, and the XCD with the longest one set
+    // the time).  The grid is 8 x gsize x ceil(groups / 8) blocks.
+    const int gsize = (p.hv / p.hq) * NSL;
+    const uint32_t xcd = blockIdx.x & 7u, j = blockIdx.x >> 3;
+    const int item = static_cast<int>((8u * (j / static_cast<uint32_t>(gsize)) + xcd) * static_cast<uint32_t>(gsize) +
+                                      j % static_cast<uint32_t>(gsize));
+    if (item >= p.work) return;  // uniform
     const int nsegw = LOCAL ? p.nseg - 1 : p.nseg;
     const int slice8 = item % NSL;
     int rest = item / NSL;
@@ -619,9 +625,15 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.ws_a = a.ws;
         p.ws_m = a.ws ? a.ws + static_cast<int64_t>(a.num_seqs) * a.num_v_heads * p.nseg * kD * kD : nullptr;
         const int pairs = a.num_seqs * a.num_v_heads;
+        // blocks for `work` items in groups of gsize, dealt to 8 XCDs group by group
+        auto grid_of = [&](int work, int nsl) {
+            const int gsize = (a.num_v_heads / a.num_qk_heads) * nsl;
+            const int groups = work / gsize;
+            return static_cast<uint32_t>(8 * gsize * ((groups + 7) / 8));
+        };
         if (p.nseg > 1) {
             p.work = pairs * (p.nseg - 1) * 2 * kSlices;  // pass 1
-            hipLaunchKernelGGL((chunk_fwd_kernel<GT, true>), dim3(static_cast<uint32_t>((p.work + 7) / 8 * 8)),
+            hipLaunchKernelGGL((chunk_fwd_kernel<GT, true>), dim3(grid_of(p.work, 2 * kSlices)),
                                dim3(kThreads), LDS_TOTAL, stream, p);
             e = hipGetLastError();
             if (e == hipSuccess) {  // pass 2
@@ -632,7 +644,7 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         }
         if (e == hipSuccess) {  // pass 3 (the whole forward when nseg = 1)
             p.work = pairs * p.nseg * kSlices;
-            hipLaunchKernelGGL((chunk_fwd_kernel<GT, false>), dim3(static_cast<uint32_t>((p.work + 7) / 8 * 8)),
+            hipLaunchKernelGGL((chunk_fwd_kernel<GT, false>), dim3(grid_of(p.work, kSlices)),
                                dim3(kThreads), LDS_TOTAL, stream, p);
             e = hipGetLastError();
         }

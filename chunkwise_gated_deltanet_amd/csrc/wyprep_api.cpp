@@ -155,7 +155,10 @@ wyp_status validate_fwd(const wyp_problem* p, const void* q, const void* k, cons
     }
     const int64_t nseq = cu ? p->num_seqs : p->batch;
     const int64_t work = nseq * p->num_v_heads * 4;  // (sequence, value head, dv slice)
-    if (work + 8 > INT32_MAX)
+    // the grid rounds the (sequence, key head) groups up to a multiple of 8, each group
+    // Hv / Hq value heads x up to 8 slices
+    const int64_t pad = 64 * static_cast<int64_t>(p->num_v_heads / p->num_qk_heads);
+    if (work + pad > INT32_MAX)
         return fail(WYP_ERR_UNSUPPORTED, "problem has %lld work items, more than one launch holds",
                     static_cast<long long>(work));
     const int64_t tokens = static_cast<int64_t>(p->batch) * p->seqlen;
@@ -388,7 +391,8 @@ wyp_status run_cp(const wyp_problem* problem, const void* q, const void* k, cons
             if (!aligned(workspace, 16))
                 return fail(WYP_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
         }
-        if (static_cast<int64_t>(problem->batch) * problem->num_v_heads * nseg * 8 + 8 > INT32_MAX)
+        if (static_cast<int64_t>(problem->batch) * problem->num_v_heads * nseg * 8 +
+                64 * static_cast<int64_t>(problem->num_v_heads / problem->num_qk_heads) > INT32_MAX)
             return fail(WYP_ERR_UNSUPPORTED, "too many segments for one launch");
         if (use_scratch && wyp::cp_scratch(&workspace, msg, sizeof msg) != 0)
             return fail(WYP_ERR_HIP, "%s", msg);
