@@ -283,9 +283,12 @@ def wy_backward(k, v, beta, chunk_size, dW, dU, dT=None, g=None, cu_seqlens=None
 def cp_segment_chunks(batch, seqlen, num_v_heads, chunk_size=64, cus=256, target=512):
     """Chunks per segment for wyp_chunk_fwd_cp.  No split (all chunks in one segment) once the
     4 dv-slice workgroups per sequence and head give every CU one; otherwise enough segments for
-    about `target` workgroups in the output pass, at least 4 chunks each.  Measured on MI355X at
-    C = 64: B=1 T=8192 H=16 runs 312 us unsplit, 167 / 157 / 188 / 258 us with segments of
-    32 / 16 / 8 / 4 chunks; B=4 T=4096 H=32 (512 workgroups) is slower split."""
+    about `target` 32-column workgroups in the output pass (which the launch then runs as half
+    as many 64-column ones), at least 4 chunks each.  Measured on MI355X at C = 64: B=1 T=8192
+    H=16 runs 231 us unsplit, 198 / 142 / 108 / 127 / 178 us with segments of 64 / 32 / 16 / 8 /
+    4 chunks; B=1 T=32768 H=8 runs 859 us unsplit, 375 / 271 / 201 / 229 / 320 us at 128 / 64 /
+    32 / 16 / 8; B=2 T=8192 H=32 (256 workgroups unsplit) runs 256 us unsplit, 272 / 294 us at
+    64 / 32."""
     nchunks = max(1, -(-seqlen // chunk_size))
     items = batch * num_v_heads * 4
     if items >= cus:

@@ -78,8 +78,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int kD = 128;        // dk = dv
 constexpr int kC = 64;         // chunk size
 constexpr int kNB = kC / 16;   // row tiles per chunk (one per wave)
-constexpr int kDVS = 32;       // dv columns per workgroup
-constexpr int kSlices = kD / kDVS;
 constexpr int kThreads = 256;
 constexpr int kBufferConfig = 0x00020000;
 // Non-temporal policy for what one workgroup alone reads or writes (its U slice, g, o).  Q, K
@@ -111,25 +109,36 @@ struct Params {
     float* ws_m;         // [pair][nseg - 1][dk][dk]: M_s
 };
 
-// LDS plan (bytes).  Only what several waves read goes through LDS: K (rows padded by 16 bytes,
-// row stride 272 B, so 16-byte reads of one column chunk by 16 consecutive rows spread over the
-// banks), the U slice, the staged O slice, the bf16 S^T and V'^T tiles (padded the same way) and
-// G.  Q and W rows of row tile w are read by wave w alone, so they go from HBM straight into its
-// MFMA operand registers: this halves the LDS traffic of a chunk step.  45.8 KB each: LDS would
-// let three workgroups share a CU (registers allow three ungated, two gated).
 constexpr int QROW = kD + 8;          // bf16 per K row
-constexpr int UROW = kDVS + 8;        // bf16 per U / O slice row
 constexpr int SROW = kD + 8;          // bf16 per S^T row (one dv column of S)
 constexpr int VROW = kC + 8;          // bf16 per V'^T row (one dv column of V')
-constexpr int OFF_K = 0;
-constexpr int OFF_U = OFF_K + kC * QROW * 2;
-constexpr int OFF_O = OFF_U + kC * UROW * 2;
-constexpr int OFF_S = OFF_O + kC * UROW * 2;
-constexpr int OFF_VN = OFF_S + kDVS * SROW * 2;
-constexpr int OFF_VD = OFF_VN + kDVS * VROW * 2;
-constexpr int OFF_G = OFF_VD + kDVS * VROW * 2;
-constexpr int LDS_TOTAL = OFF_G + kC * 4;
-static_assert(3 * LDS_TOTAL <= 160 * 1024, "three workgroups per CU by LDS");
+
+// A workgroup owns DVS of its head's dv columns (a slice: 32 or 64).  LDS plan (bytes): only what
+// several waves read goes through LDS: K (rows padded by 16 bytes, row stride 272 B, so 16-byte
+// reads of one column chunk by 16 consecutive rows spread over the banks), the U slice, the staged
+// O slice, the bf16 S^T and V'^T tiles (padded the same way) and G.  Q and W rows of row tile w
+// are read by wave w alone, so they go from HBM straight into its MFMA operand registers: this
+// halves the LDS traffic of a chunk step.  45.8 KB at DVS = 32 (three workgroups per CU by LDS;
+// registers allow three ungated, two gated), 71.8 KB at DVS = 64 (two).
+template <int DVS>
+struct Slice {
+    static constexpr int NT = DVS / 16;        // 16-column tiles of the slice
+    static constexpr int COUNT = kD / DVS;     // slices per head
+    static constexpr int PIECES = DVS / 32;    // 16-byte pieces of the U / O slice per thread
+    static constexpr int RPC = DVS / 8;        // 16-byte pieces per row of the slice
+    static constexpr int UROW = DVS + 8;       // bf16 per U / O slice row
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_U = OFF_K + kC * QROW * 2;
+    static constexpr int OFF_O = OFF_U + kC * UROW * 2;
+    static constexpr int OFF_S = OFF_O + kC * UROW * 2;
+    static constexpr int OFF_VN = OFF_S + DVS * SROW * 2;
+    static constexpr int OFF_VD = OFF_VN + DVS * VROW * 2;
+    static constexpr int OFF_G = OFF_VD + DVS * VROW * 2;
+    static constexpr int LDS_TOTAL = OFF_G + kC * 4;
+    static_assert(kC * RPC == PIECES * kThreads, "the U / O slice splits evenly over the threads");
+};
+static_assert(3 * Slice<32>::LDS_TOTAL <= 160 * 1024, "three workgroups per CU by LDS");
+static_assert(2 * Slice<64>::LDS_TOTAL <= 160 * 1024, "two workgroups per CU by LDS");
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -153,9 +162,11 @@ __device__ inline uint32_t row_bytes(int n, uint32_t stride, uint32_t width)
 // its own Q and W rows 16 w .. 16 w + 15 as 16x16x32 MFMA operands: lane 16 lg + lr holds
 // elements 32 s + 8 lg .. + 7 of row 16 w + lr, s = 0..3.  Rows past the chunk's n tokens read
 // as 0 through the buffer range.
+template <int DVS>
 struct Chunk {
+    using F = Slice<DVS>;
     u32x4 q[4], k[4], w[4];
-    u32x4 u;
+    u32x4 u[F::PIECES];
     float g;
 
     // This wave's Q and W operands.
@@ -189,9 +200,13 @@ struct Chunk {
             k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
         }
         // the transition slices of the sequence-parallel pass read no U: an empty range
-        const __amdgpu_buffer_rsrc_t ur = rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * kDVS,
-                                               want_u ? row_bytes(n, wstride, kDVS * 2) : 0u);
-        u = __builtin_amdgcn_raw_buffer_load_b128(ur, (tid >> 2) * wstride + (tid & 3) * 16, 0, kStream);
+        const __amdgpu_buffer_rsrc_t ur = rsrc(p.u + (tok0 * p.hv + hv) * kD + slice * DVS,
+                                               want_u ? row_bytes(n, wstride, DVS * 2) : 0u);
+#pragma unroll
+        for (int it = 0; it < F::PIECES; ++it) {
+            const int pc = tid + it * kThreads;  // row pc / RPC, piece pc % RPC
+            u[it] = __builtin_amdgcn_raw_buffer_load_b128(ur, (pc / F::RPC) * wstride + (pc % F::RPC) * 16, 0, kStream);
+        }
         g = 0.f;
         if constexpr (GT) {
             // every thread loads; rows tid >= n (all of waves 1-3) fall outside the range
@@ -209,9 +224,13 @@ struct Chunk {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int pc = tid + it * kThreads;
-            *reinterpret_cast<u32x4*>(smem + OFF_K + (pc >> 4) * (QROW * 2) + (pc & 15) * 16) = k[it];
+            *reinterpret_cast<u32x4*>(smem + F::OFF_K + (pc >> 4) * (QROW * 2) + (pc & 15) * 16) = k[it];
         }
-        *reinterpret_cast<u32x4*>(smem + OFF_U + (tid >> 2) * (UROW * 2) + (tid & 3) * 16) = u;
+#pragma unroll
+        for (int it = 0; it < F::PIECES; ++it) {
+            const int pc = tid + it * kThreads;
+            *reinterpret_cast<u32x4*>(smem + F::OFF_U + (pc / F::RPC) * (F::UROW * 2) + (pc % F::RPC) * 16) = u[it];
+        }
         if constexpr (GT) {
             if (tid < 64) {
                 double x = static_cast<double>(g);
@@ -220,7 +239,7 @@ struct Chunk {
                     const double t = __shfl_up(x, d);
                     if (tid >= d) x += t;
                 }
-                reinterpret_cast<float*>(smem + OFF_G)[tid] = static_cast<float>(x);
+                reinterpret_cast<float*>(smem + F::OFF_G)[tid] = static_cast<float>(x);
             }
         }
     }
@@ -238,7 +257,7 @@ __device__ inline void seq_range(const Params& p, int seq, int64_t* s0, int64_t*
     }
 }
 
-template <bool GT, bool LOCAL>
+template <bool GT, bool LOCAL, int DVS>
 // Two waves per SIMD for the register allocator: the two register sets of the chunk pipeline take
 // 155 (gated: 177) VGPRs; with three the gated instance spills, and the ungated one is slower at
 // one workgroup per CU.
@@ -247,7 +266,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // item = ((seq * nsegw + seg) * Hv + hv) * NSL + slice; pass 1 (LOCAL) has 8 slices (four of
     // A, four of M) and no item for the last segment
-    constexpr int NSL = LOCAL ? 2 * kSlices : kSlices;
+    using F = Slice<DVS>;
+    constexpr int NT = F::NT;
+    constexpr int NSL = LOCAL ? 2 * F::COUNT : F::COUNT;
     // Workgroups are dealt round-robin to the 8 XCDs (block b to XCD b mod 8).  A group is one
     // (sequence or segment, key head): its value heads' dv slices read the same Q, K and W rows, so
     // the group stays on one XCD and they meet in its L2.  Consecutive groups go to consecutive
@@ -266,8 +287,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     rest /= p.hv;
     const int seg = rest % nsegw, seq = rest / nsegw;
     const int pair = seq * p.hv + hv;
-    const bool mcols = LOCAL && slice8 >= kSlices;  // a slice of the transition M
-    const int slice = slice8 % kSlices;
+    const bool mcols = LOCAL && slice8 >= F::COUNT;  // a slice of the transition M
+    const int slice = slice8 % F::COUNT;
     const int hk = hv / (p.hv / p.hq);
     int64_t s0, s1;
     seq_range(p, seq, &s0, &s1);
@@ -280,20 +301,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const __bf16* Ks = reinterpret_cast<const __bf16*>(smem + OFF_K);
-    const __bf16* Us = reinterpret_cast<const __bf16*>(smem + OFF_U);
-    __bf16* Os = reinterpret_cast<__bf16*>(smem + OFF_O);
-    __bf16* St = reinterpret_cast<__bf16*>(smem + OFF_S);
-    __bf16* Vn = reinterpret_cast<__bf16*>(smem + OFF_VN);
-    __bf16* Vd = reinterpret_cast<__bf16*>(smem + OFF_VD);
-    const float* Gs = reinterpret_cast<const float*>(smem + OFF_G);
+    const __bf16* Ks = reinterpret_cast<const __bf16*>(smem + F::OFF_K);
+    const __bf16* Us = reinterpret_cast<const __bf16*>(smem + F::OFF_U);
+    __bf16* Os = reinterpret_cast<__bf16*>(smem + F::OFF_O);
+    __bf16* St = reinterpret_cast<__bf16*>(smem + F::OFF_S);
+    __bf16* Vn = reinterpret_cast<__bf16*>(smem + F::OFF_VN);
+    __bf16* Vd = reinterpret_cast<__bf16*>(smem + F::OFF_VD);
+    const float* Gs = reinterpret_cast<const float*>(smem + F::OFF_G);
 
     // State tiles of this wave: S[16 mt + 4 lg + r][16 nt + lr], mt = 2 wave + m, in fp32.
     // Start: pass 1 from zero (A) or from the identity's columns (M); unsplit, the sequence's
     // initial state; split, the S_start the combine left in the workspace (segment 0 too: the
     // combine copied the initial state there before this pass, so the last segment may write
     // the final state over the initial state's buffer).
-    f32x4 sacc[2][2];
+    f32x4 sacc[2][NT];
     const float* h0 = nullptr;
     if (!LOCAL) {
         if (p.nseg == 1)
@@ -301,15 +322,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         else if (seg > 0 || p.h0 != nullptr)
             h0 = p.ws_a + (aslot + seg) * kD * kD;
     }
-    if (h0) h0 += slice * kDVS;
+    if (h0) h0 += slice * DVS;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * (2 * wave + m) + 4 * lg + r, col = 16 * nt + lr;
-                sacc[m][nt][r] = h0 ? h0[row * kD + col] : (mcols && row == slice * kDVS + col ? 1.f : 0.f);
+                sacc[m][nt][r] = h0 ? h0[row * kD + col] : (mcols && row == slice * DVS + col ? 1.f : 0.f);
             }
 
     // S^T (bf16) for the first chunk's products: row = dv column, 4 consecutive dk per lane
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 bf16x4 v;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[r] = static_cast<__bf16>(sacc[m][nt][r]);
@@ -329,22 +350,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // Two register sets take turns (the loop is unrolled by two): chunk c + 1's loads go into the
     // set chunk c does not use, right after chunk c's first barrier, so they have a whole chunk
     // step to arrive, and no register copy makes the compiler wait for them early.
-    Chunk ch0, ch1;
+    Chunk<DVS> ch0, ch1;
     const bool want_q = !LOCAL, want_u = !mcols;
     {
         const int64_t t0 = s0 + static_cast<int64_t>(c_begin) * kC;
         const int n0 = c_begin < c_end ? static_cast<int>(s1 - t0 < kC ? s1 - t0 : kC) : 0;
-        ch0.issue<GT>(p, t0, n0, hk, hv, slice, tid, want_q, want_u);
+        ch0.template issue<GT>(p, t0, n0, hk, hv, slice, tid, want_q, want_u);
         // Each chunk step ends with its O store; the loop is entered after a store too (over an
         // empty range: the hardware drops it), so both ways into the loop have the same memory
         // history and the compiler's waits inside need not cover the youngest store.
         if constexpr (!LOCAL)
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rsrc(p.o, 0u), 0, 0, kStream);
     }
-    auto step = [&](int c, const Chunk& cur, Chunk& nxt) {
+    auto step = [&](int c, const Chunk<DVS>& cur, Chunk<DVS>& nxt) {
         const int64_t tok0 = s0 + static_cast<int64_t>(c) * kC;
         const int n = static_cast<int>(s1 - tok0 < kC ? s1 - tok0 : kC);
-        cur.commit<GT>(smem, tid);
+        cur.template commit<GT>(smem, tid);
         // this wave's Q and W operands, straight from the registers they were loaded into
         bf16x8 qa[kD / 32], wa[kD / 32];
 #pragma unroll
@@ -356,7 +377,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // every load of the next chunk goes in flight now, into the other register set
         const int64_t nt0 = tok0 + kC;
         const int nn = c + 1 < c_end ? static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC) : 0;
-        nxt.issue<GT>(p, nt0, nn, hk, hv, slice, tid, want_q, want_u);
+        nxt.template issue<GT>(p, nt0, nn, hk, hv, slice, tid, want_q, want_u);
         const int I = wave;  // row tile of V' and O
         const float glast = GT ? Gs[kC - 1] : 0.f;
         float grow[4];
@@ -364,16 +385,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int r = 0; r < 4; ++r) grow[r] = GT ? Gs[16 * I + 4 * lg + r] : 0.f;
 
         // 1. V' = U - W S and O = exp(G) Q S for row tile I; 16x16x32 bf16 MFMA over dk
-        f32x4 vacc[2], oacc[2];
+        f32x4 vacc[NT], oacc[NT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             vacc[nt] = zero4();
             oacc[nt] = zero4();
         }
 #pragma unroll
         for (int s = 0; s < kD / 32; ++s) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const bf16x8 sb = *reinterpret_cast<const bf16x8*>(St + (16 * nt + lr) * SROW + 32 * s + 8 * lg);
                 vacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], sb, vacc[nt], 0, 0, 0);
                 if constexpr (!LOCAL) oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], sb, oacc[nt], 0, 0, 0);
@@ -381,11 +402,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         // V' = U - W S: element r of lane 16 lg + lr is row 16 I + 4 lg + r, column 16 nt + lr
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             bf16x4 vn, vd;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float uu = static_cast<float>(Us[(16 * I + 4 * lg + r) * UROW + 16 * nt + lr]);
+                const float uu = static_cast<float>(Us[(16 * I + 4 * lg + r) * F::UROW + 16 * nt + lr]);
                 const float x = uu - vacc[nt][r];
                 vn[r] = static_cast<__bf16>(x);
                 vd[r] = static_cast<__bf16>(GT ? x * __expf(glast - grow[r]) : x);
@@ -426,7 +447,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int J = 0; J < kNB; ++J) {
             if (LOCAL || J > I) break;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 const bf16x4 vb = *reinterpret_cast<const bf16x4*>(Vn + (16 * nt + lr) * VROW + 16 * J + 4 * lg);
                 oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                     __builtin_bit_cast(i16x4, pa[J]), __builtin_bit_cast(i16x4, vb), oacc[nt], 0, 0, 0);
@@ -440,14 +461,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             if constexpr (GT) {
                 const float e = __expf(glast);
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) sacc[m][nt] *= e;
+                for (int nt = 0; nt < NT; ++nt) sacc[m][nt] *= e;
             }
 #pragma unroll
             for (int kt = 0; kt < kNB; ++kt) {
                 const __bf16* p0 = Ks + (16 * kt + 4 * lg + (lr >> 2)) * QROW + 16 * mt + 4 * (lr & 3);
                 const i16x4 kfr = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < NT; ++nt) {
                     const bf16x4 vb = *reinterpret_cast<const bf16x4*>(Vd + (16 * nt + lr) * VROW + 16 * kt + 4 * lg);
                     sacc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kfr, __builtin_bit_cast(i16x4, vb),
                                                                            sacc[m][nt], 0, 0, 0);
@@ -458,18 +479,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // O rows of tile I, scaled, staged row-major for 16-byte stores
         if constexpr (!LOCAL) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Os[(16 * I + 4 * lg + r) * UROW + 16 * nt + lr] = static_cast<__bf16>(p.scale * oacc[nt][r]);
+                    Os[(16 * I + 4 * lg + r) * F::UROW + 16 * nt + lr] = static_cast<__bf16>(p.scale * oacc[nt][r]);
         }
         __syncthreads();  // B3: O staged, the new S^T in place; Q, K, W, U, V' free
         if constexpr (!LOCAL) {
             const uint32_t ostride = static_cast<uint32_t>(p.hv) * kD * 2;
             const __amdgpu_buffer_rsrc_t orr =
-                rsrc(p.o + (tok0 * p.hv + hv) * kD + slice * kDVS, (n - 1) * ostride + kDVS * 2);
-            const u32x4 val = *reinterpret_cast<const u32x4*>(smem + OFF_O + (tid >> 2) * (UROW * 2) + (tid & 3) * 16);
-            __builtin_amdgcn_raw_buffer_store_b128(val, orr, (tid >> 2) * ostride + (tid & 3) * 16, 0, kStream);
+                rsrc(p.o + (tok0 * p.hv + hv) * kD + slice * DVS, (n - 1) * ostride + DVS * 2);
+#pragma unroll
+            for (int it = 0; it < F::PIECES; ++it) {
+                const int pc = tid + it * kThreads;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(smem + F::OFF_O + (pc / F::RPC) * (F::UROW * 2) + (pc % F::RPC) * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(val, orr, (pc / F::RPC) * ostride + (pc % F::RPC) * 16, 0, kStream);
+            }
         }
     };
     for (int c = c_begin; c < c_end; c += 2) {  // uniform
@@ -479,15 +504,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     float* out = nullptr;  // where this work item's end state goes
     if (LOCAL)
-        out = (mcols ? p.ws_m + (mslot + seg) * kD * kD : p.ws_a + (aslot + seg + 1) * kD * kD) + slice * kDVS;
+        out = (mcols ? p.ws_m + (mslot + seg) * kD * kD : p.ws_a + (aslot + seg + 1) * kD * kD) + slice * DVS;
     else if (p.hT != nullptr && seg == p.nseg - 1)
-        out = p.hT + static_cast<int64_t>(pair) * kD * kD + slice * kDVS;
+        out = p.hT + static_cast<int64_t>(pair) * kD * kD + slice * DVS;
     if (out != nullptr) {
         float* hT = out;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     hT[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] = sacc[m][nt][r];
@@ -586,9 +611,10 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
     }
 }
 
-template <bool GT>
+template <bool GT, int DVS>
 int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 {
+    using F = Slice<DVS>;
     static std::once_flag once[64];
     static hipError_t attr_err[64];
     int device = 0;
@@ -596,11 +622,11 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
     if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
     if (e == hipSuccess) {
         std::call_once(once[device], [&] {
-            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, false>),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, false, DVS>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS_TOTAL);
             if (attr_err[device] == hipSuccess)
-                attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, true>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+                attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, true, DVS>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS_TOTAL);
         });
         e = attr_err[device];
     }
@@ -632,9 +658,9 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
             return static_cast<uint32_t>(8 * gsize * ((groups + 7) / 8));
         };
         if (p.nseg > 1) {
-            p.work = pairs * (p.nseg - 1) * 2 * kSlices;  // pass 1
-            hipLaunchKernelGGL((chunk_fwd_kernel<GT, true>), dim3(grid_of(p.work, 2 * kSlices)),
-                               dim3(kThreads), LDS_TOTAL, stream, p);
+            p.work = pairs * (p.nseg - 1) * 2 * F::COUNT;  // pass 1
+            hipLaunchKernelGGL((chunk_fwd_kernel<GT, true, DVS>), dim3(grid_of(p.work, 2 * F::COUNT)),
+                               dim3(kThreads), F::LDS_TOTAL, stream, p);
             e = hipGetLastError();
             if (e == hipSuccess) {  // pass 2
                 hipLaunchKernelGGL(cp_combine_kernel, dim3(static_cast<uint32_t>(pairs * kCombSlices)), dim3(kThreads),
@@ -643,17 +669,57 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
             }
         }
         if (e == hipSuccess) {  // pass 3 (the whole forward when nseg = 1)
-            p.work = pairs * p.nseg * kSlices;
-            hipLaunchKernelGGL((chunk_fwd_kernel<GT, false>), dim3(grid_of(p.work, kSlices)),
-                               dim3(kThreads), LDS_TOTAL, stream, p);
+            p.work = pairs * p.nseg * F::COUNT;
+            hipLaunchKernelGGL((chunk_fwd_kernel<GT, false, DVS>), dim3(grid_of(p.work, F::COUNT)),
+                               dim3(kThreads), F::LDS_TOTAL, stream, p);
             e = hipGetLastError();
         }
     }
     if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d, segments=%d)", hipGetErrorString(e), GT ? 1 : 0, a.nseg);
+        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d, segments=%d, slice=%d)", hipGetErrorString(e), GT ? 1 : 0,
+                      a.nseg, DVS);
         return static_cast<int>(e);
     }
     return 0;
+}
+
+// Compute units of the current device, read once per device.
+int cu_count(int* out)
+{
+    static std::once_flag once[64];
+    static int cus[64];
+    static hipError_t err[64];
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
+    if (e == hipSuccess) {
+        std::call_once(once[device], [&] {
+            err[device] = hipDeviceGetAttribute(&cus[device], hipDeviceAttributeMultiprocessorCount, device);
+        });
+        e = err[device];
+    }
+    if (e == hipSuccess) *out = cus[device];
+    return static_cast<int>(e);
+}
+
+// Slice width per launch.  A 64-column slice reads Q, K, W and the gates once for twice the
+// columns and forms P = Q K^T once for them, so it costs about 1.35x a 32-column slice per
+// workgroup instead of 2x; it wins once the 64-column workgroups (two per (sequence or segment,
+// value head)) give every CU one, and loses below that, where the 32-column grid fills twice as
+// many CUs.  Both widths do the same operations per column in the same order, so the results
+// are identical bit for bit.
+template <bool GT>
+int launch_s(const FwdArgs& a, hipStream_t s, char* msg, int len)
+{
+    int cus = 0;
+    const int e = cu_count(&cus);
+    if (e != 0) {
+        std::snprintf(msg, len, "%s (compute unit count for chunk_fwd)", hipGetErrorString(static_cast<hipError_t>(e)));
+        return e;
+    }
+    const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_v_heads * (a.nseg > 1 ? a.nseg : 1);
+    if (items * Slice<64>::COUNT >= cus) return launch_t<GT, 64>(a, s, msg, len);
+    return launch_t<GT, 32>(a, s, msg, len);
 }
 
 }  // namespace
@@ -686,7 +752,7 @@ int cp_scratch(void** ptr, char* msg, int msg_len)
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return a.g != nullptr ? fwd::launch_t<true>(a, s, msg, msg_len) : fwd::launch_t<false>(a, s, msg, msg_len);
+    return a.g != nullptr ? fwd::launch_s<true>(a, s, msg, msg_len) : fwd::launch_s<false>(a, s, msg, msg_len);
 }
 
 }  // namespace wyp

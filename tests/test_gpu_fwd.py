@@ -32,6 +32,14 @@ CASES = {
                                 h0=True),
     "packed_empty_seq_mu2_h0": dict(batch=1, seqlen=0, num_qk_heads=1, num_v_heads=2, seed=105,
                                     gate_mu=2.0, h0=True, seqlens=[100, 0, 70, 0]),
+    # 128 or more (sequence, value head) pairs: the launch takes 64-column slices of the state
+    # (two workgroups per pair) instead of 32-column ones once that gives every CU one.
+    "wide_B8_T321_H4_16_mu4_h0": dict(batch=8, seqlen=321, num_qk_heads=4, num_v_heads=16,
+                                      seed=106, gate_mu=4.0, h0=True),
+    "wide_B16_T130_H8_ungated": dict(batch=16, seqlen=130, num_qk_heads=8, num_v_heads=8, seed=107),
+    "wide_packed_40_mu0_h0": dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4, seed=108,
+                                  gate_mu=0.0, h0=True,
+                                  seqlens=[1, 0, 64, 65, 127, 129, 200, 31, 33, 63] * 4),
 }
 
 
@@ -173,6 +181,9 @@ CP_CASES = {
     "B1_T2048_H2_ungated_h0_seg8": (dict(batch=1, seqlen=2048, num_qk_heads=2, num_v_heads=2,
                                          seed=133, h0=True), 8),
     "B1_T333_H2_one_segment": (dict(batch=1, seqlen=333, num_qk_heads=2, num_v_heads=2, seed=134), 6),
+    # 17 segments x 8 value heads: 64-column slices in both kernel passes
+    "wide_B1_T2100_H2_8_mu4_h0_seg2": (dict(batch=1, seqlen=2100, num_qk_heads=2, num_v_heads=8,
+                                            seed=136, gate_mu=4.0, h0=True), 2),
 }
 
 
