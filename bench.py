@@ -319,11 +319,10 @@ def measure(args, entry, w, inp, dev, lib, ramp=True):
     scale = ctypes.c_float(dk ** -0.5)
     seg_chunks = None
     if fwd_entry and args.segment_chunks is not None:
-        if cu is not None:
-            raise SystemExit("--segment-chunks needs a [B, T] workload (no packed sequences)")
-        seg_chunks = (cg.cp_segment_chunks(B, T, Hv, C) if args.segment_chunks == "auto"
-                      else int(args.segment_chunks))
-        ws_bytes = lib.wyp_chunk_fwd_cp_workspace_bytes(pprob, seg_chunks)
+        seg_chunks = (cg.auto_segment_chunks(B, T, Hv, C, None if cu is None else cu.numel() - 1)
+                      if args.segment_chunks == "auto" else int(args.segment_chunks))
+    if seg_chunks is not None:
+        ws_bytes = lib.wyp_chunk_fwd_cp_workspace_bytes(pprob, cu_ptr, seg_chunks)
         ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
         ws_ptr, ws_n = ctypes.c_void_p(ws.data_ptr()), ctypes.c_int64(ws_bytes)
 
@@ -346,8 +345,8 @@ def measure(args, entry, w, inp, dev, lib, ramp=True):
             if entry == "gdn":
                 st = lib.wyp_wu_prepare(pprob, kp, vp, gp, bp, cu_ptr, wp, up, sp)
             if st == 0 and seg_chunks is not None:
-                st = lib.wyp_chunk_fwd_cp(pprob, qp, kp, wp, up, gp, None, scale, seg_chunks,
-                                          ws_ptr, ws_n, op, hp, sp)
+                st = lib.wyp_chunk_fwd_cp(pprob, qp, kp, wp, up, gp, None, scale, cu_ptr,
+                                          seg_chunks, ws_ptr, ws_n, op, hp, sp)
             elif st == 0:
                 st = lib.wyp_chunk_fwd(pprob, qp, kp, wp, up, gp, None, scale, cu_ptr, op, hp, sp)
         if st != 0:

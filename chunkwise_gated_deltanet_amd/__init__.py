@@ -20,15 +20,14 @@ import os
 
 __all__ = ["wy_prepare", "kkt_solve", "wu_prepare", "solve_rhs", "wy_backward", "chunk_fwd",
            "chunk_gated_delta_rule", "wyp_wy_prepare", "wyp_kkt_solve", "wyp_wu_prepare",
-           "wyp_solve_rhs",
-           "wyp_wy_backward", "wyp_chunk_fwd", "cp_segment_chunks", "load_library", "Problem",
-           "LIB_PATH", "WyprepError"]
+           "wyp_solve_rhs", "wyp_wy_backward", "wyp_chunk_fwd", "cp_segment_chunks",
+           "auto_segment_chunks", "load_library", "Problem", "LIB_PATH", "WyprepError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwyprep.so")
 
 WYP_OK, WYP_ERR_INVALID_ARGUMENT, WYP_ERR_UNSUPPORTED, WYP_ERR_HIP = 0, 1, 2, 3
 WYP_BF16, WYP_F32 = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class WyprepError(RuntimeError):
@@ -80,13 +79,13 @@ def load_library(path: str | None = None):
                                   _P, _P, _P, _P]
     lib.wyp_chunk_fwd_cp.restype = ctypes.c_int32
     lib.wyp_chunk_fwd_cp.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P,
-                                     ctypes.c_float, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
-                                     _P]
+                                     ctypes.c_float, _P, ctypes.c_int32, _P, ctypes.c_int64, _P,
+                                     _P, _P]
     lib.wyp_chunk_fwd_cp_noalloc.restype = ctypes.c_int32
     lib.wyp_chunk_fwd_cp_noalloc.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P,
-                                             ctypes.c_float, ctypes.c_int32, _P, _P, _P]
+                                             ctypes.c_float, _P, ctypes.c_int32, _P, _P, _P]
     lib.wyp_chunk_fwd_cp_workspace_bytes.restype = ctypes.c_int64
-    lib.wyp_chunk_fwd_cp_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32]
+    lib.wyp_chunk_fwd_cp_workspace_bytes.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32]
     lib.wyp_wy_backward.restype = ctypes.c_int32
     lib.wyp_wy_backward.argtypes = [ctypes.POINTER(Problem)] + [_P] * 13
     if lib.wyp_abi_version() != ABI_VERSION:
@@ -297,6 +296,20 @@ def cp_segment_chunks(batch, seqlen, num_v_heads, chunk_size=64, cus=256, target
     return -(-nchunks // nseg)
 
 
+def auto_segment_chunks(batch, seqlen, num_v_heads, chunk_size=64, num_seqs=None):
+    """segment_chunks for the automatic split of chunk_fwd, or None where cp_segment_chunks
+    would not split.  A packed batch (num_seqs sequences, `seqlen` tokens in all, batch 1)
+    counts as num_seqs rows of its mean length."""
+    C = int(chunk_size)
+    if num_seqs is None:
+        rows, mean = batch, seqlen
+    else:
+        rows = max(int(num_seqs), 1)
+        mean = -(-seqlen // rows)
+    L = cp_segment_chunks(rows, mean, num_v_heads, C)
+    return L if L < -(-mean // C) else None
+
+
 def chunk_fwd(q, k, w, u, chunk_size=64, g=None, initial_state=None, scale=None,
               cu_seqlens=None, output_final_state=False, o_out=None, final_state=None,
               segment_chunks=None):
@@ -304,8 +317,9 @@ def chunk_fwd(q, k, w, u, chunk_size=64, g=None, initial_state=None, scale=None,
     wy_prepare / wu_prepare for the same k, beta, g); see wyp_chunk_fwd.  q, k [B,T,Hq,128],
     w, u [B,T,Hv,128] bf16; g [B,T,Hv] float32 or None; initial_state [N,Hv,128,128] float32
     or None.  final_state is None unless output_final_state (or a final_state buffer).
-    segment_chunks (int, or "auto"; not with cu_seqlens) splits each sequence into segments of
-    that many chunks run in parallel (wyp_chunk_fwd_cp; the workspace comes from torch)."""
+    segment_chunks (int, or "auto") splits each sequence into segments of that many chunks run
+    in parallel (wyp_chunk_fwd_cp; the workspace comes from torch).  "auto" picks it with
+    auto_segment_chunks (no split where that gives None)."""
     import torch
     lib = load_library()
     device = k.device
@@ -347,23 +361,22 @@ def chunk_fwd(q, k, w, u, chunk_size=64, g=None, initial_state=None, scale=None,
         final_state = _out(final_state, (N, Hv, dk, dv), torch.float32, device, "final_state")
     sc = float(dk ** -0.5 if scale is None else scale)
     fsp = final_state.data_ptr() if final_state is not None else None
+    cup = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    if segment_chunks == "auto":
+        segment_chunks = auto_segment_chunks(B, T, Hv, chunk_size,
+                                             None if cu_seqlens is None else n)
     if segment_chunks is not None:
-        if cu_seqlens is not None:
-            raise ValueError("segment_chunks needs the [B, T] layout (no cu_seqlens)")
-        if segment_chunks == "auto":
-            segment_chunks = cp_segment_chunks(B, T, Hv, int(chunk_size))
-        nbytes = lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), int(segment_chunks))
+        nbytes = lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), cup, int(segment_chunks))
         if nbytes < 0:
             raise ValueError(f"invalid segment_chunks {segment_chunks}")
         ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=device)
         st = lib.wyp_chunk_fwd_cp(ctypes.byref(p), q.data_ptr(), k.data_ptr(), w.data_ptr(),
-                                  u.data_ptr(), gp, h0p, sc, int(segment_chunks), ws.data_ptr(),
-                                  nbytes, o_out.data_ptr(), fsp, _stream(device))
+                                  u.data_ptr(), gp, h0p, sc, cup, int(segment_chunks),
+                                  ws.data_ptr(), nbytes, o_out.data_ptr(), fsp, _stream(device))
     else:
         st = lib.wyp_chunk_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), w.data_ptr(),
-                               u.data_ptr(), gp, h0p, sc,
-                               cu_seqlens.data_ptr() if cu_seqlens is not None else None,
-                               o_out.data_ptr(), fsp, _stream(device))
+                               u.data_ptr(), gp, h0p, sc, cup, o_out.data_ptr(), fsp,
+                               _stream(device))
     _check(lib, st)
     return o_out, final_state
 
@@ -374,14 +387,10 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     wu_prepare (W, U for every chunk; T stays on chip) followed by chunk_fwd.  g may be None
     (no gates).  Returns (o, final_state); final_state is None unless output_final_state."""
     w, u = wu_prepare(k, v, beta, chunk_size, cu_seqlens=cu_seqlens, g=g)
-    seg = None
-    if cu_seqlens is None:  # in-GPU sequence parallelism when batch x heads is small
-        B, T = k.shape[:2]
-        L = cp_segment_chunks(B, T, w.shape[2], int(chunk_size))
-        seg = L if L < -(-T // int(chunk_size)) else None
+    # in-GPU sequence parallelism when sequences x heads is small
     return chunk_fwd(q, k, w, u, chunk_size, g=g, initial_state=initial_state, scale=scale,
                      cu_seqlens=cu_seqlens, output_final_state=output_final_state,
-                     segment_chunks=seg)
+                     segment_chunks="auto")
 
 
 # The C-ABI names, for callers that mirror the header.

@@ -39,13 +39,15 @@
 // kernel's thread blocks number only batch x heads, so the pages split each sequence and fix
 // the split up with a correction computed per segment).  The state after a segment is linear in
 // the state before it, S_end = M S_start + A, so with segments of L chunks:
-//   pass 1 (LOCAL): per (sequence, segment, head), A = the segment's end state from a zero state
-//          and M = its transition (the same recurrence with U = 0 from the identity), as eight
-//          32-column slices; no output;
+//   pass 1 (LOCAL): per (segment but a sequence's last, head), A = the segment's end state from
+//          a zero state and M = its transition (the same recurrence with U = 0 from the
+//          identity), as twice the slices of a head; no output;
 //   pass 2 (combine): S_start(0) = the initial state, copied into the workspace, and S_start of
-//          segment s + 1 = M_s S_start(s) + A_s, in fp32, per head and 16-column slice;
-//   pass 3: the kernel above per (sequence, segment, head) from its true S_start (always read
-//          from the workspace, so the initial state may be the final-state buffer), writing o.
+//          segment s + 1 = M_s S_start(s) + A_s, in fp32, per sequence, head and 16-column slice;
+//   pass 3: the kernel above per (segment, head) from its true S_start (for a sequence of two or
+//          more segments always read from the workspace, so the initial state may be the
+//          final-state buffer), writing o.
+// Segments start at each sequence's first chunk, for batch rows and packed sequences alike.
 // Exact, not the gate-decay warm-up approximation the pages also describe.
 #include <hip/hip_runtime.h>
 
@@ -101,12 +103,13 @@ struct Params {
     int32_t hq;
     int32_t hv;
     int32_t num_seqs;    // sequences (cu_seqlens) or batch rows
-    int32_t work;        // work items: sequences x segments x value heads x slices
-    int32_t nseg;        // segments per sequence (1: the whole sequence)
-    int32_t seg_chunks;  // chunks per segment (nseg > 1)
-    float* ws_a;         // [pair][nseg][dk][dv]: slot 0 S_start(0) (pass 2); slot s + 1 A_s
-                         // (pass 1), then S_start(s + 1) (pass 2)
-    float* ws_m;         // [pair][nseg - 1][dk][dk]: M_s
+    int32_t work;        // work items of this launch: slots x value heads x slices
+    int32_t split;       // 1: the sequence-parallel form
+    int32_t nseg;        // split batch rows: segments per row
+    int32_t seg_chunks;  // split: chunks per segment
+    float* ws_a;         // [a-slot][Hv][dk][dv]: a sequence's first a-slot S_start(0) (pass 2),
+                         // a-slot s + 1 A_s (pass 1), then S_start(s + 1) (pass 2)
+    float* ws_m;         // [m-slot][Hv][dk][dk]: M_s
 };
 
 constexpr int QROW = kD + 8;          // bf16 per K row
@@ -257,6 +260,88 @@ __device__ inline void seq_range(const Params& p, int seq, int64_t* s0, int64_t*
     }
 }
 
+// Where a work item's slot sits.  Unsplit, the slot is the sequence.  Split, a sequence of nseg_n
+// segments owns nseg_n consecutive a-slots from abase (the output pass runs segment s in a-slot
+// abase + s; the workspace keeps S_start(0) in a-slot abase and A_s, later S_start(s + 1), in
+// abase + s + 1) and nseg_n - 1 consecutive m-slots from mbase (pass 1 runs segment s in m-slot
+// mbase + s and keeps M_s there).  Batch rows: abase = row x nseg, mbase = row x (nseg - 1).
+// Packed sequences, with X = seg_chunks x C tokens per segment and segments aligned to each
+// sequence's first chunk: abase = floor(cu[n] / X) + n and mbase = floor(cu[n] / X).  Since
+// nseg_n = ceil(len_n / X) <= floor(cu[n + 1] / X) - floor(cu[n] / X) + 1, the ranges of
+// consecutive sequences never overlap: floor(T / X) + N a-slots and floor(T / X) m-slots hold
+// every packed batch, whatever its length mix.
+struct Seg {
+    int seq, seg, nseg, abase, mbase;
+    bool valid;
+};
+
+// Largest n < N with key(n) <= idx, key(n) = floor(cu[n] / X) (+ n for a-slots), which does not
+// decrease with n: a 64-ary search (one load per lane per level, two levels for 4096
+// sequences).  Every wave runs it; the result is wave-uniform.
+template <bool ASLOT>
+__device__ inline int packed_owner(const Params& p, int idx, int lane)
+{
+    const int X = p.seg_chunks * kC;
+    int lo = 0, span = p.num_seqs;
+    while (span > 1) {  // uniform
+        const int step = (span + 63) >> 6;
+        bool ok = false;
+        if (lane * step < span) {
+            const int n = lo + lane * step;
+            ok = p.cu[n] / X + (ASLOT ? n : 0) <= idx;
+        }
+        const unsigned long long b = __ballot(ok);
+        const int last = b ? 63 - __clzll(b) : 0;
+        lo += last * step;
+        span = min(step, span - last * step);
+    }
+    return uniform(lo);
+}
+
+// Segments and slot bases of sequence (or batch row) n of a split launch.
+__device__ inline Seg seq_slots(const Params& p, int n)
+{
+    Seg s;
+    s.seq = n;
+    s.seg = 0;
+    s.valid = true;
+    if (p.cu == nullptr) {
+        s.nseg = p.nseg;
+        s.abase = n * p.nseg;
+        s.mbase = n * (p.nseg - 1);
+    } else {
+        const int X = p.seg_chunks * kC;
+        const int c0 = p.cu[n], len = p.cu[n + 1] - c0;
+        s.nseg = len > X ? (len + X - 1) / X : 1;
+        s.mbase = c0 / X;
+        s.abase = s.mbase + n;
+    }
+    return s;
+}
+
+template <bool ASLOT>
+__device__ inline Seg locate(const Params& p, int slot, int lane)
+{
+    Seg s;
+    if (!p.split) {
+        s.seq = slot;
+        s.seg = 0;
+        s.nseg = 1;
+        s.abase = slot;
+        s.mbase = 0;
+        s.valid = true;
+    } else if (p.cu == nullptr) {
+        const int per = ASLOT ? p.nseg : p.nseg - 1;
+        s = seq_slots(p, slot / per);
+        s.seg = slot % per;
+    } else {
+        s = seq_slots(p, packed_owner<ASLOT>(p, slot, lane));
+        s.seg = slot - (ASLOT ? s.abase : s.mbase);
+        s.valid = s.seg >= 0 && s.seg < (ASLOT ? s.nseg : s.nseg - 1);  // else a spare slot
+    }
+    return s;
+}
+
 template <bool GT, bool LOCAL, int DVS>
 // Two waves per SIMD for the register allocator: the two register sets of the chunk pipeline take
 // 155 (gated: 177) VGPRs; with three the gated instance spills, and the ungated one is slower at
@@ -264,8 +349,9 @@ template <bool GT, bool LOCAL, int DVS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    // item = ((seq * nsegw + seg) * Hv + hv) * NSL + slice; pass 1 (LOCAL) has 8 slices (four of
-    // A, four of M) and no item for the last segment
+    // item = (slot * Hv + hv) * NSL + slice over the a-slots (unsplit: the sequences), or in
+    // pass 1 (LOCAL) over the m-slots with twice the slices (A's, then M's); no pass-1 item for
+    // a sequence's last segment
     using F = Slice<DVS>;
     constexpr int NT = F::NT;
     constexpr int NSL = LOCAL ? 2 * F::COUNT : F::COUNT;
@@ -280,12 +366,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int item = static_cast<int>((8u * (j / static_cast<uint32_t>(gsize)) + xcd) * static_cast<uint32_t>(gsize) +
                                       j % static_cast<uint32_t>(gsize));
     if (item >= p.work) return;  // uniform
-    const int nsegw = LOCAL ? p.nseg - 1 : p.nseg;
     const int slice8 = item % NSL;
-    int rest = item / NSL;
-    const int hv = rest % p.hv;
-    rest /= p.hv;
-    const int seg = rest % nsegw, seq = rest / nsegw;
+    const int hv = (item / NSL) % p.hv;
+    const Seg at = locate<!LOCAL>(p, item / NSL / p.hv, threadIdx.x & 63);
+    if (!at.valid) return;  // uniform: a spare slot
+    const int seg = at.seg, seq = at.seq;
     const int pair = seq * p.hv + hv;
     const bool mcols = LOCAL && slice8 >= F::COUNT;  // a slice of the transition M
     const int slice = slice8 % F::COUNT;
@@ -293,10 +378,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int64_t s0, s1;
     seq_range(p, seq, &s0, &s1);
     const int nchunks_seq = static_cast<int>((s1 - s0 + kC - 1) / kC);
-    const int c_begin = p.nseg > 1 ? seg * p.seg_chunks : 0;
-    const int c_end = p.nseg > 1 ? min(c_begin + p.seg_chunks, nchunks_seq) : nchunks_seq;
-    const int64_t mslot = static_cast<int64_t>(pair) * (p.nseg - 1);  // this pair's first M slot
-    const int64_t aslot = static_cast<int64_t>(pair) * p.nseg;        // this pair's S_start(0) slot
+    const int c_begin = p.split ? seg * p.seg_chunks : 0;
+    const int c_end = p.split ? min(c_begin + p.seg_chunks, nchunks_seq) : nchunks_seq;
+    const int64_t slot_floats = static_cast<int64_t>(p.hv) * kD * kD;  // one workspace slot
 
     int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
@@ -311,16 +395,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     // State tiles of this wave: S[16 mt + 4 lg + r][16 nt + lr], mt = 2 wave + m, in fp32.
     // Start: pass 1 from zero (A) or from the identity's columns (M); unsplit, the sequence's
-    // initial state; split, the S_start the combine left in the workspace (segment 0 too: the
-    // combine copied the initial state there before this pass, so the last segment may write
-    // the final state over the initial state's buffer).
+    // initial state (also a split launch's one-segment sequences); split, the S_start the combine
+    // left in the workspace (segment 0 too: the combine copied the initial state there before
+    // this pass, so the last segment may write the final state over the initial state's buffer).
     f32x4 sacc[2][NT];
     const float* h0 = nullptr;
     if (!LOCAL) {
-        if (p.nseg == 1)
+        if (at.nseg == 1)
             h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD : nullptr;
         else if (seg > 0 || p.h0 != nullptr)
-            h0 = p.ws_a + (aslot + seg) * kD * kD;
+            h0 = p.ws_a + (at.abase + seg) * slot_floats + static_cast<int64_t>(hv) * kD * kD;
     }
     if (h0) h0 += slice * DVS;
 #pragma unroll
@@ -504,8 +588,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     float* out = nullptr;  // where this work item's end state goes
     if (LOCAL)
-        out = (mcols ? p.ws_m + (mslot + seg) * kD * kD : p.ws_a + (aslot + seg + 1) * kD * kD) + slice * DVS;
-    else if (p.hT != nullptr && seg == p.nseg - 1)
+        out = (mcols ? p.ws_m + (at.mbase + seg) * slot_floats : p.ws_a + (at.abase + seg + 1) * slot_floats) +
+              static_cast<int64_t>(hv) * kD * kD + slice * DVS;
+    else if (p.hT != nullptr && seg == at.nseg - 1)
         out = p.hT + static_cast<int64_t>(pair) * kD * kD + slice * DVS;
     if (out != nullptr) {
         float* hT = out;
@@ -519,9 +604,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
-// Pass 2 of the sequence-parallel forward: per (sequence, value head, 16-column dv slice),
-// S_start(0) = the initial state (copied to workspace slot 0) and S_start(s + 1) =
-// M_s S_start(s) + A_s for s = 0 .. nseg - 2, each written over A_s (pass 3 reads them there).  Each step is 128 x 128 x 16 fp32
+// Pass 2 of the sequence-parallel forward: per (sequence of two or more segments, value head,
+// 16-column dv slice), S_start(0) = the initial state (copied to the sequence's first a-slot)
+// and S_start(s + 1) = M_s S_start(s) + A_s for s = 0 .. nseg_n - 2, each written over A_s
+// (pass 3 reads them there).  Each step is 128 x 128 x 16 fp32
 // multiply-adds on fp32 MFMA 16x16x4.  The steps of one slice form a chain, so the slices are
 // 16 columns wide (eight workgroups per head: more chains, each step shorter); wave w owns row
 // tiles 2w, 2w + 1; S^T sits in LDS so every B operand is one 16-byte read.  M_{s+1} and A_{s+1}
@@ -533,11 +619,13 @@ struct CombineOperands {
     f32x4 m[2][kD / 16];  // M rows 16 mt + lr, columns 16 kt + 4 lg .. + 3 (A operands)
     f32x4 a[2];           // A elements [16 mt + 4 lg + r][lr] of the slice (accumulator start)
 
-    // Step s of pair `pair`: A_s sits in slot pair * nseg + s + 1, M_s in pair * (nseg - 1) + s.
-    __device__ void load(const Params& p, int pair, int s, int slice, int wave, int lr, int lg)
+    // Step s of value head hv of a sequence: A_s sits in a-slot abase + s + 1, M_s in m-slot
+    // mbase + s.
+    __device__ void load(const Params& p, const Seg& at, int hv, int s, int slice, int wave, int lr, int lg)
     {
-        const float* A = p.ws_a + (static_cast<int64_t>(pair) * p.nseg + s + 1) * kD * kD + slice * kCombCols;
-        const float* M = p.ws_m + (static_cast<int64_t>(pair) * (p.nseg - 1) + s) * kD * kD;
+        const int64_t head = static_cast<int64_t>(hv) * kD * kD;
+        const float* A = p.ws_a + static_cast<int64_t>(at.abase + s + 1) * p.hv * kD * kD + head + slice * kCombCols;
+        const float* M = p.ws_m + static_cast<int64_t>(at.mbase + s) * p.hv * kD * kD + head;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
             const int mt = 2 * wave + mm;
@@ -555,20 +643,28 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
     __shared__ __attribute__((aligned(16))) float St[kCombCols][kD + 4];
     // Workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous range of items,
     // so the eight slices of a head read M_s through one L2 (M_s is 64 KB per step).
-    const uint32_t Gsz = gridDim.x;  // pairs x 8, a multiple of 8
-    const int item = static_cast<int>((blockIdx.x & 7u) * (Gsz >> 3) + (blockIdx.x >> 3));
-    const int slice = item % kCombSlices, pair = item / kCombSlices;
-    if (pair >= p.num_seqs * p.hv) return;  // uniform
+    // Items are (sequence, value head, slice).  The eight slices of one (sequence, value head)
+    // form a group on one XCD (block b runs on XCD b mod 8), so they read M_s through one L2;
+    // consecutive groups go to consecutive XCDs, so a few long sequences of a packed batch
+    // still spread over every XCD.  The grid is 64 x ceil(groups / 8) blocks.
+    const uint32_t xcd = blockIdx.x & 7u, j = blockIdx.x >> 3;
+    const int item = static_cast<int>((8u * (j / kCombSlices) + xcd) * kCombSlices + j % kCombSlices);
+    const int slice = item % kCombSlices, hv = (item / kCombSlices) % p.hv, seq = item / kCombSlices / p.hv;
+    if (seq >= p.num_seqs) return;  // uniform
+    const Seg at = seq_slots(p, seq);
+    if (at.nseg < 2) return;  // uniform: nothing to chain
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
+    const int pair = seq * p.hv + hv;
+    const int64_t slot_floats = static_cast<int64_t>(p.hv) * kD * kD;
     const float* h0 = p.h0 ? p.h0 + static_cast<int64_t>(pair) * kD * kD + slice * kCombCols : nullptr;
-    float* s0 = p.ws_a + static_cast<int64_t>(pair) * p.nseg * kD * kD + slice * kCombCols;
+    float* s0 = p.ws_a + at.abase * slot_floats + static_cast<int64_t>(hv) * kD * kD + slice * kCombCols;
     // Two operand sets take turns (the loop is unrolled by two), so the next step's M and A are
     // loaded straight into the set that step uses, with no register copies that would wait for
     // those loads early.
     CombineOperands ops0, ops1;
-    ops0.load(p, pair, 0, slice, wave, lr, lg);  // launched only with nseg > 1
+    ops0.load(p, at, hv, 0, slice, wave, lr, lg);  // the sequence has two or more segments
     for (int idx = tid; idx < kD * kCombCols; idx += kThreads) {
         const int row = idx / kCombCols, col = idx % kCombCols;
         const float x = h0 ? h0[row * kD + col] : 0.f;
@@ -580,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
         // M and A of the next step, in flight during this one.  The last step reloads its own
         // slot (in bounds, unused) so that the issue has no branch: a branch around it makes the
         // compiler's wait for `cur` conservative, and that wait would then cover these loads.
-        nxt.load(p, pair, sg + 2 < p.nseg ? sg + 1 : sg, slice, wave, lr, lg);
+        nxt.load(p, at, hv, sg + 2 < at.nseg ? sg + 1 : sg, slice, wave, lr, lg);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of this step's products
         f32x4 acc[2];
 #pragma unroll
@@ -595,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
             }
         }
         __syncthreads();  // every read of S_start(s) done
-        float* A = s0 + (sg + 1) * kD * kD;
+        float* A = s0 + (sg + 1) * slot_floats;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
             *reinterpret_cast<f32x4*>(&St[lr][16 * (2 * wave + mm) + 4 * lg]) = acc[mm];
@@ -604,9 +700,9 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
         }
         __syncthreads();
     };
-    for (int sg = 0; sg + 1 < p.nseg; sg += 2) {  // uniform
+    for (int sg = 0; sg + 1 < at.nseg; sg += 2) {  // uniform
         step(sg, ops0, ops1);
-        if (sg + 2 >= p.nseg) break;  // uniform
+        if (sg + 2 >= at.nseg) break;  // uniform
         step(sg + 1, ops1, ops0);
     }
 }
@@ -646,38 +742,40 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.hq = a.num_qk_heads;
         p.hv = a.num_v_heads;
         p.num_seqs = a.num_seqs;
-        p.nseg = a.nseg > 1 ? a.nseg : 1;
+        p.split = a.split;
+        p.nseg = a.nseg;
         p.seg_chunks = a.seg_chunks;
         p.ws_a = a.ws;
-        p.ws_m = a.ws ? a.ws + static_cast<int64_t>(a.num_seqs) * a.num_v_heads * p.nseg * kD * kD : nullptr;
-        const int pairs = a.num_seqs * a.num_v_heads;
+        p.ws_m = a.split ? a.ws + static_cast<int64_t>(a.a_slots) * a.num_v_heads * kD * kD : nullptr;
+        const int hv = a.num_v_heads;
         // blocks for `work` items in groups of gsize, dealt to 8 XCDs group by group
         auto grid_of = [&](int work, int nsl) {
             const int gsize = (a.num_v_heads / a.num_qk_heads) * nsl;
             const int groups = work / gsize;
             return static_cast<uint32_t>(8 * gsize * ((groups + 7) / 8));
         };
-        if (p.nseg > 1) {
-            p.work = pairs * (p.nseg - 1) * 2 * F::COUNT;  // pass 1
+        if (p.split) {
+            p.work = a.m_slots * hv * 2 * F::COUNT;  // pass 1
             hipLaunchKernelGGL((chunk_fwd_kernel<GT, true, DVS>), dim3(grid_of(p.work, 2 * F::COUNT)),
                                dim3(kThreads), F::LDS_TOTAL, stream, p);
             e = hipGetLastError();
             if (e == hipSuccess) {  // pass 2
-                hipLaunchKernelGGL(cp_combine_kernel, dim3(static_cast<uint32_t>(pairs * kCombSlices)), dim3(kThreads),
-                                   0, stream, p);
+                const int groups = a.num_seqs * hv;
+                hipLaunchKernelGGL(cp_combine_kernel, dim3(static_cast<uint32_t>(64 * ((groups + 7) / 8))),
+                                   dim3(kThreads), 0, stream, p);
                 e = hipGetLastError();
             }
         }
-        if (e == hipSuccess) {  // pass 3 (the whole forward when nseg = 1)
-            p.work = pairs * p.nseg * F::COUNT;
+        if (e == hipSuccess) {  // pass 3 (the whole forward when not split)
+            p.work = (p.split ? a.a_slots : a.num_seqs) * hv * F::COUNT;
             hipLaunchKernelGGL((chunk_fwd_kernel<GT, false, DVS>), dim3(grid_of(p.work, F::COUNT)),
                                dim3(kThreads), F::LDS_TOTAL, stream, p);
             e = hipGetLastError();
         }
     }
     if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d, segments=%d, slice=%d)", hipGetErrorString(e), GT ? 1 : 0,
-                      a.nseg, DVS);
+        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d, split=%d, slice=%d)", hipGetErrorString(e), GT ? 1 : 0,
+                      a.split, DVS);
         return static_cast<int>(e);
     }
     return 0;
@@ -717,7 +815,7 @@ int launch_s(const FwdArgs& a, hipStream_t s, char* msg, int len)
         std::snprintf(msg, len, "%s (compute unit count for chunk_fwd)", hipGetErrorString(static_cast<hipError_t>(e)));
         return e;
     }
-    const int64_t items = static_cast<int64_t>(a.num_seqs) * a.num_v_heads * (a.nseg > 1 ? a.nseg : 1);
+    const int64_t items = static_cast<int64_t>(a.split ? a.a_slots : a.num_seqs) * a.num_v_heads;
     if (items * Slice<64>::COUNT >= cus) return launch_t<GT, 64>(a, s, msg, len);
     return launch_t<GT, 32>(a, s, msg, len);
 }

@@ -332,29 +332,50 @@ extern "C" wyp_status wyp_wy_backward(const wyp_problem* problem, const void* k,
 
 namespace {
 
-// Segments of `segment_chunks` chunks per batch row, or -1 if the arguments are invalid.
-int64_t cp_segments(const wyp_problem* p, int32_t segment_chunks)
+// Slots of the split forward.  Batch rows: nseg = ceil(chunks / segment_chunks) segments per row,
+// B nseg a-slots and B (nseg - 1) m-slots.  Packed sequences (segments aligned to each
+// sequence's first chunk, X = 64 segment_chunks tokens each): floor(T / X) + N a-slots and
+// floor(T / X) m-slots, enough for any length mix.  No m-slot means no split.
+struct CpPlan {
+    int64_t nseg, a_slots, m_slots;
+};
+
+bool cp_plan(const wyp_problem* p, bool packed, int32_t segment_chunks, CpPlan* out)
 {
-    if (!p || segment_chunks < 1 || p->chunk_size != 64 || p->seqlen < 0) return -1;
-    const int64_t nchunks = (static_cast<int64_t>(p->seqlen) + 63) / 64;
-    return nchunks == 0 ? 1 : (nchunks + segment_chunks - 1) / segment_chunks;
+    if (!p || segment_chunks < 1 || p->chunk_size != 64 || p->seqlen < 0 || p->num_v_heads < 1)
+        return false;
+    if (packed) {
+        if (p->batch != 1 || p->num_seqs < 0) return false;
+        const int64_t e = p->seqlen / (64 * static_cast<int64_t>(segment_chunks));
+        out->nseg = 0;
+        out->m_slots = e;
+        out->a_slots = e > 0 ? e + p->num_seqs : 0;
+    } else {
+        if (p->batch < 1) return false;
+        const int64_t nchunks = (static_cast<int64_t>(p->seqlen) + 63) / 64;
+        const int64_t nseg = nchunks == 0 ? 1 : (nchunks + segment_chunks - 1) / segment_chunks;
+        out->nseg = nseg;
+        out->m_slots = nseg > 1 ? p->batch * (nseg - 1) : 0;
+        out->a_slots = nseg > 1 ? p->batch * nseg : 0;
+    }
+    return true;
 }
 
-// A and M of every segment but the last, plus S_start(0), per (batch row, value head); none
-// for a single segment.
-int64_t cp_workspace(const wyp_problem* p, int64_t nseg)
+// A and M of every segment but a sequence's last, plus its S_start(0): one dk x dv fp32 matrix per
+// slot and value head.
+int64_t cp_workspace(const wyp_problem* p, const CpPlan& plan)
 {
-    if (nseg <= 1) return 0;
-    return static_cast<int64_t>(p->batch) * p->num_v_heads * (2 * nseg - 1) * 128 * 128 * 4;
+    return (plan.a_slots + plan.m_slots) * p->num_v_heads * 128 * 128 * 4;
 }
 
 }  // namespace
 
-extern "C" int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t segment_chunks)
+extern "C" int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, const int32_t* cu_seqlens,
+                                                    int32_t segment_chunks)
 {
-    const int64_t nseg = cp_segments(problem, segment_chunks);
-    if (nseg < 0 || problem->batch < 1 || problem->num_v_heads < 1) return -1;
-    return cp_workspace(problem, nseg);
+    CpPlan plan;
+    if (!cp_plan(problem, cu_seqlens != nullptr, segment_chunks, &plan)) return -1;
+    return cp_workspace(problem, plan);
 }
 
 namespace {
@@ -363,21 +384,23 @@ namespace {
 // library's static scratch (wyp_chunk_fwd_cp_noalloc, which allocates nothing).
 wyp_status run_cp(const wyp_problem* problem, const void* q, const void* k, const void* w,
                   const void* u, const float* g, const float* initial_state, float scale,
-                  int32_t segment_chunks, void* workspace, int64_t workspace_bytes, bool use_scratch,
-                  void* o_out, float* final_state, void* stream)
+                  const int32_t* cu_seqlens, int32_t segment_chunks, void* workspace,
+                  int64_t workspace_bytes, bool use_scratch, void* o_out, float* final_state,
+                  void* stream)
 {
     g_last_error[0] = '\0';
     wyp::FwdArgs args{};
     bool empty = false;
-    wyp_status st = validate_fwd(problem, q, k, w, u, g, initial_state, scale, nullptr, o_out,
+    wyp_status st = validate_fwd(problem, q, k, w, u, g, initial_state, scale, cu_seqlens, o_out,
                                  final_state, &args, &empty);
-    if (st != WYP_OK || empty) return st;
-    const int64_t nseg = cp_segments(problem, segment_chunks);
-    if (nseg < 1)
+    if (st != WYP_OK) return st;
+    CpPlan plan;
+    if (!cp_plan(problem, cu_seqlens != nullptr, segment_chunks, &plan))
         return fail(WYP_ERR_INVALID_ARGUMENT, "segment_chunks must be >= 1 (got %d)", segment_chunks);
+    if (empty) return WYP_OK;
     char msg[256] = "";
-    if (nseg > 1) {
-        const int64_t need = cp_workspace(problem, nseg);
+    if (plan.m_slots > 0) {
+        const int64_t need = cp_workspace(problem, plan);
         if (use_scratch) {
             if (need > WYP_CP_SCRATCH_BYTES)
                 return fail(WYP_ERR_UNSUPPORTED,
@@ -391,15 +414,19 @@ wyp_status run_cp(const wyp_problem* problem, const void* q, const void* k, cons
             if (!aligned(workspace, 16))
                 return fail(WYP_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
         }
-        if (static_cast<int64_t>(problem->batch) * problem->num_v_heads * nseg * 8 +
+        // the largest grid: the combine's or pass 1's 8 blocks per (slot, value head), rounded up
+        if (plan.a_slots * problem->num_v_heads * 8 +
                 64 * static_cast<int64_t>(problem->num_v_heads / problem->num_qk_heads) > INT32_MAX)
             return fail(WYP_ERR_UNSUPPORTED, "too many segments for one launch");
         if (use_scratch && wyp::cp_scratch(&workspace, msg, sizeof msg) != 0)
             return fail(WYP_ERR_HIP, "%s", msg);
+        args.split = 1;
+        args.nseg = static_cast<int32_t>(plan.nseg);
+        args.seg_chunks = segment_chunks;
+        args.a_slots = static_cast<int32_t>(plan.a_slots);
+        args.m_slots = static_cast<int32_t>(plan.m_slots);
+        args.ws = static_cast<float*>(workspace);
     }
-    args.nseg = static_cast<int32_t>(nseg);
-    args.seg_chunks = segment_chunks;
-    args.ws = nseg > 1 ? static_cast<float*>(workspace) : nullptr;
     if (wyp::launch_fwd(args, stream, msg, sizeof msg) != 0)
         return fail(WYP_ERR_HIP, "kernel launch failed: %s", msg);
     return WYP_OK;
@@ -410,20 +437,21 @@ wyp_status run_cp(const wyp_problem* problem, const void* q, const void* k, cons
 extern "C" wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
                                        const void* w, const void* u, const float* g,
                                        const float* initial_state, float scale,
-                                       int32_t segment_chunks, void* workspace,
-                                       int64_t workspace_bytes, void* o_out, float* final_state,
-                                       void* stream)
+                                       const int32_t* cu_seqlens, int32_t segment_chunks,
+                                       void* workspace, int64_t workspace_bytes, void* o_out,
+                                       float* final_state, void* stream)
 {
-    return run_cp(problem, q, k, w, u, g, initial_state, scale, segment_chunks, workspace,
-                  workspace_bytes, false, o_out, final_state, stream);
+    return run_cp(problem, q, k, w, u, g, initial_state, scale, cu_seqlens, segment_chunks,
+                  workspace, workspace_bytes, false, o_out, final_state, stream);
 }
 
 extern "C" wyp_status wyp_chunk_fwd_cp_noalloc(const wyp_problem* problem, const void* q,
                                                const void* k, const void* w, const void* u,
                                                const float* g, const float* initial_state,
-                                               float scale, int32_t segment_chunks, void* o_out,
+                                               float scale, const int32_t* cu_seqlens,
+                                               int32_t segment_chunks, void* o_out,
                                                float* final_state, void* stream)
 {
-    return run_cp(problem, q, k, w, u, g, initial_state, scale, segment_chunks, nullptr, 0, true,
-                  o_out, final_state, stream);
+    return run_cp(problem, q, k, w, u, g, initial_state, scale, cu_seqlens, segment_chunks,
+                  nullptr, 0, true, o_out, final_state, stream);
 }

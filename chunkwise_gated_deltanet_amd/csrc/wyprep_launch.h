@@ -47,9 +47,12 @@ struct FwdArgs {
     int32_t num_qk_heads;
     int32_t num_v_heads;
     int32_t num_seqs;          // sequences (cu_seqlens) or batch rows
-    int32_t nseg;              // segments per sequence (<= 1: sequential)
-    int32_t seg_chunks;        // chunks per segment (nseg > 1)
-    float* ws;                 // nseg > 1: num_seqs x Hv x (2 nseg - 1) x dk x dk floats
+    int32_t split;             // 1: the sequence-parallel form (the fields below)
+    int32_t nseg;              // batch rows: segments per row
+    int32_t seg_chunks;        // chunks per segment
+    int32_t a_slots;           // batch rows: B nseg; packed: floor(T / (64 seg_chunks)) + N
+    int32_t m_slots;           // batch rows: B (nseg - 1); packed: floor(T / (64 seg_chunks))
+    float* ws;                 // (a_slots + m_slots) x Hv x dk x dk floats
 };
 
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len);

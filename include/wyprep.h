@@ -74,8 +74,9 @@
 extern "C" {
 #endif
 
-#define WYP_ABI_VERSION 7  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp;
-                              6: wyp_chunk_fwd_cp_noalloc; 7: wyp_solve_rhs */
+#define WYP_ABI_VERSION 8  /* 2: log gates g; 3: wyp_chunk_fwd; 4: wyp_wy_backward; 5: wyp_chunk_fwd_cp;
+                              6: wyp_chunk_fwd_cp_noalloc; 7: wyp_solve_rhs; 8: cu_seqlens in the
+                              split forward and its workspace query */
 
 /* Bytes of the static device scratch behind wyp_chunk_fwd_cp_noalloc (one array per GPU). */
 #define WYP_CP_SCRATCH_BYTES (32 * 1024 * 1024)
@@ -193,25 +194,35 @@ wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* 
  * to rounding (not the pages' gate-decay warm-up approximation).  Pass 2 copies the initial
  * state into the workspace and pass 3 reads it only there, so initial_state and final_state
  * may be the same buffer, as for wyp_chunk_fwd.
- * Arguments as for wyp_chunk_fwd, without cu_seqlens (each batch row is one sequence of T
- * tokens), plus:
- *   segment_chunks   chunks per segment, >= 1; a value covering all ceil(T / 64) chunks gives
- *                    one segment, which is wyp_chunk_fwd itself and needs no workspace
+ * Arguments as for wyp_chunk_fwd, cu_seqlens included, plus:
+ *   segment_chunks   chunks per segment, >= 1.  Segments start at a sequence's first chunk, so a
+ *                    sequence of n tokens has ceil(n / (64 segment_chunks)) of them (one if it
+ *                    is shorter, or empty; such a sequence runs as in wyp_chunk_fwd).  When no
+ *                    sequence can have two (batch rows: segment_chunks covers ceil(T / 64)
+ *                    chunks; packed: 64 segment_chunks > T), the call is wyp_chunk_fwd itself
+ *                    and needs no workspace.
  *   workspace        caller-owned device memory of at least
- *                    wyp_chunk_fwd_cp_workspace_bytes(problem, segment_chunks) bytes,
+ *                    wyp_chunk_fwd_cp_workspace_bytes(problem, cu_seqlens, segment_chunks) bytes,
  *                    16-byte aligned; its contents on entry do not matter and on return are
  *                    unspecified.  Calls that share a workspace must not overlap.
  * Supported as wyp_chunk_fwd (bf16, C = 64, dk = dv = 128). */
 wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
                             const void* w_in, const void* u_in, const float* g,
-                            const float* initial_state, float scale, int32_t segment_chunks,
-                            void* workspace, int64_t workspace_bytes, void* o_out,
-                            float* final_state, void* stream);
+                            const float* initial_state, float scale, const int32_t* cu_seqlens,
+                            int32_t segment_chunks, void* workspace, int64_t workspace_bytes,
+                            void* o_out, float* final_state, void* stream);
 
-/* Workspace bytes wyp_chunk_fwd_cp needs: B x Hv x (2 x segments - 1) x dk x dk x 4 (A and M
- * of every segment but the last, and a copy of the initial state); 0 for a single segment; -1
- * for invalid arguments (segment_chunks < 1, chunk_size other than 64, NULL problem). */
-int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t segment_chunks);
+/* Workspace bytes wyp_chunk_fwd_cp needs, with X = 64 segment_chunks tokens per segment:
+ *   batch rows (cu_seqlens NULL): B x Hv x (2 nseg - 1) x dk x dk x 4, nseg = ceil(T / X) (A
+ *     and M of every segment but a row's last, and a copy of the initial state); 0 if nseg = 1;
+ *   packed (cu_seqlens non-NULL; only whether it is NULL matters, it is not read):
+ *     (2 floor(T / X) + N) x Hv x dk x dk x 4, with T the total tokens and N = num_seqs (no
+ *     length mix needs more: a sequence's segments after its first number at most its tokens
+ *     / X); 0 if T < X.
+ * -1 for invalid arguments (segment_chunks < 1, chunk_size other than 64, NULL problem, batch
+ * other than 1 with cu_seqlens). */
+int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, const int32_t* cu_seqlens,
+                                         int32_t segment_chunks);
 
 /* wyp_chunk_fwd_cp for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same passes, results and
@@ -220,7 +231,7 @@ int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t seg
  * copy until the process ends.  The call allocates and frees nothing (no hipMalloc, hipFree or
  * allocating library routine); on its first call on a device it looks up that device's address
  * of the array once.
- *   Limit: wyp_chunk_fwd_cp_workspace_bytes(problem, segment_chunks) must not exceed
+ *   Limit: wyp_chunk_fwd_cp_workspace_bytes(problem, cu_seqlens, segment_chunks) must not exceed
  *   WYP_CP_SCRATCH_BYTES, else WYP_ERR_UNSUPPORTED (checked on the host, nothing launched).
  *   B = 1, T = 8192, Hv = 16 in 8 segments needs 15 MiB.
  *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on different
@@ -230,8 +241,8 @@ int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, int32_t seg
 wyp_status wyp_chunk_fwd_cp_noalloc(const wyp_problem* problem, const void* q, const void* k,
                                     const void* w_in, const void* u_in, const float* g,
                                     const float* initial_state, float scale,
-                                    int32_t segment_chunks, void* o_out, float* final_state,
-                                    void* stream);
+                                    const int32_t* cu_seqlens, int32_t segment_chunks,
+                                    void* o_out, float* final_state, void* stream);
 
 /* Backward of the preparation step (the training path; [QLA] "反向" (backward): FlashQLA fuses
  * bwd_wy with the other backward kernels).  For upstream gradients dT, dW, dU of wyp_wy_prepare's

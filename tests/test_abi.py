@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import chunkwise_gated_deltanet_amd as cg
@@ -38,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.wyp_abi_version() == 7 == cg.ABI_VERSION
+    assert lib.wyp_abi_version() == 8 == cg.ABI_VERSION
     assert lib.wyp_status_string(0) == b"WYP_OK"
     assert lib.wyp_status_string(3) == b"WYP_ERR_HIP"
     assert lib.wyp_status_string(99) == b"WYP_ERR_UNKNOWN"
@@ -192,21 +193,57 @@ def test_wy_backward_rejects(lib):
 
 def test_chunk_fwd_cp_workspace_and_rejects(lib):
     p = good(batch=2, seqlen=1000, num_v_heads=4)       # 16 chunks per row
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 16) == 0   # one segment
+    ws = lib.wyp_chunk_fwd_cp_workspace_bytes
+    assert ws(ctypes.byref(p), None, 16) == 0   # one segment
     # four segments: A and M of three, plus the initial-state copy, per (row, value head)
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 5) == 2 * 4 * 7 * 128 * 128 * 4
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 0) == -1
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(good(chunk_size=32)), 4) == -1
-    need = lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 4)
+    assert ws(ctypes.byref(p), None, 5) == 2 * 4 * 7 * 128 * 128 * 4
+    assert ws(ctypes.byref(p), None, 0) == -1
+    assert ws(ctypes.byref(good(chunk_size=32)), None, 4) == -1
+    need = ws(ctypes.byref(p), None, 4)
 
     def call(seg=4, ws=FAKE, nbytes=need, **kw):
-        return lib.wyp_chunk_fwd_cp(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0.5, seg,
-                                    ws, nbytes, FAKE, None, None)
+        return lib.wyp_chunk_fwd_cp(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0.5, None,
+                                    seg, ws, nbytes, FAKE, None, None)
     assert call(ws=None) == 1
     assert "workspace" in lib.wyp_last_error().decode()
     assert call(nbytes=need - 1) == 1
     assert call(ws=FAKE + 4) == 1
     assert call(seg=0) == 1
+
+
+def test_chunk_fwd_cp_packed_workspace(lib):
+    """Packed sequences: floor(T / X) + N a-slots and floor(T / X) m-slots per value head, X = 64
+    segment_chunks tokens; the pointer is only tested for NULL, never read."""
+    ws = lib.wyp_chunk_fwd_cp_workspace_bytes
+    slot = 128 * 128 * 4
+    p = good(batch=1, seqlen=5000, num_v_heads=8, num_seqs=7)
+    cu = ctypes.c_void_p(FAKE)
+    assert ws(ctypes.byref(p), cu, 4) == (2 * (5000 // 256) + 7) * 8 * slot
+    assert ws(ctypes.byref(p), cu, 78) == (2 * 1 + 7) * 8 * slot     # X = 4992 <= T
+    assert ws(ctypes.byref(p), cu, 79) == 0                          # X > T: never split
+    assert ws(ctypes.byref(p), cu, 0) == -1
+    assert ws(ctypes.byref(good(batch=2, seqlen=5000, num_seqs=7)), cu, 4) == -1
+    # the bound holds for any length mix: brute force over a few, counting the slots the
+    # kernel uses (a-slots floor(cu[n] / X) + n + s, m-slots floor(cu[n] / X) + s)
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        lens = rng.integers(0, 3000, size=int(rng.integers(1, 12)))
+        lens[rng.random(lens.size) < 0.2] = 0
+        T, X = int(lens.sum()), 64 * int(rng.integers(1, 20))
+        cu_h = np.concatenate([[0], np.cumsum(lens)])
+        a_used, m_used = set(), set()
+        for n, ln in enumerate(lens):
+            nseg = max(1, -(-int(ln) // X))
+            for s in range(nseg):
+                a = cu_h[n] // X + n + s
+                assert a not in a_used
+                a_used.add(a)
+            for s in range(nseg - 1):
+                m = cu_h[n] // X + s
+                assert m not in m_used
+                m_used.add(m)
+        assert max(a_used) < T // X + lens.size
+        assert not m_used or max(m_used) < T // X
 
 
 def test_chunk_fwd_cp_noalloc_rejects_before_any_hip_call(lib):
@@ -216,10 +253,10 @@ def test_chunk_fwd_cp_noalloc_rejects_before_any_hip_call(lib):
 
     def call(prob, seg, **kw):
         return lib.wyp_chunk_fwd_cp_noalloc(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, None, None,
-                                            0.5, seg, FAKE, None, None)
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), 16) <= lim      # 8 segments
+                                            0.5, None, seg, FAKE, None, None)
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(p), None, 16) <= lim      # 8 segments
     big = good(batch=4, seqlen=64 * 128, num_qk_heads=32, num_v_heads=32)
-    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(big), 16) > lim
+    assert lib.wyp_chunk_fwd_cp_workspace_bytes(ctypes.byref(big), None, 16) > lim
     assert call(big, 16) == 2
     assert "scratch" in lib.wyp_last_error().decode()
     assert call(p, 0) == 1

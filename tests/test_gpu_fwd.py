@@ -184,19 +184,32 @@ CP_CASES = {
     # 17 segments x 8 value heads: 64-column slices in both kernel passes
     "wide_B1_T2100_H2_8_mu4_h0_seg2": (dict(batch=1, seqlen=2100, num_qk_heads=2, num_v_heads=8,
                                             seed=136, gate_mu=4.0, h0=True), 2),
+    # Packed sequences: segments start at each sequence's first chunk; one-segment, empty and
+    # one-token sequences run beside split ones (segment lengths 1 .. 4 chunks, ragged tails)
+    "packed_mu4_h0_seg2": (dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4, seed=137,
+                                gate_mu=4.0, h0=True,
+                                seqlens=[700, 0, 90, 1, 257, 64, 65, 128, 129]), 2),
+    "packed_one_long_many_short_mu0_h0_seg4": (dict(batch=1, seqlen=0, num_qk_heads=1,
+                                                    num_v_heads=8, seed=138, gate_mu=0.0, h0=True,
+                                                    seqlens=[4000] + [5, 63, 64, 65, 0] * 8), 4),
+    "packed_ungated_seg1": (dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=2, seed=139,
+                                 seqlens=[300, 1, 513]), 1),
+    # 64-column slices: 14 sequences, Hv = 16
+    "wide_packed_mu4_seg3": (dict(batch=1, seqlen=0, num_qk_heads=4, num_v_heads=16, seed=140,
+                                  gate_mu=4.0, seqlens=[1000, 333, 64, 0, 1, 2000, 150] * 2), 3),
 }
 
 
 def run_fwd_cp(inp, h0, device, seg):
     import torch
     import chunkwise_gated_deltanet_amd as cg
-    k, v, beta, _ = to_device(inp, device)
+    k, v, beta, cu = to_device(inp, device)
     q = q_of(inp, device)
     g = gate_of(inp, device)
-    W, U = cg.wu_prepare(k, v, beta, 64, g=g)
+    W, U = cg.wu_prepare(k, v, beta, 64, g=g, cu_seqlens=cu)
     o = torch.full(v.shape, float("nan"), dtype=v.dtype, device=device)
     h0d = None if h0 is None else torch.from_numpy(h0).to(device)
-    o, hT = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=h0d, o_out=o,
+    o, hT = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=h0d, o_out=o, cu_seqlens=cu,
                          output_final_state=True, segment_chunks=seg)
     torch.cuda.synchronize(device)
     return o, hT
@@ -214,6 +227,35 @@ def test_chunk_fwd_cp(name, gpu):
     ro, rh = rel_fro(to_f64(o), o_ref), rel_fro(to_f64(hT), h_ref)
     say(f"[cp {name}] o rel fro {ro:.3e}, final state rel fro {rh:.3e}")
     assert ro <= FWD_TOL and rh <= FWD_TOL, (ro, rh)
+    if inp["cu_seqlens"] is not None:
+        worst = compare_pairs(inp, o, hT, o_ref, h_ref, f"cp {name} per pair")
+        assert worst <= 2 * FWD_TOL, worst
+        for s in np.nonzero(np.diff(inp["cu_seqlens"]) == 0)[0]:  # empty: the initial state back
+            want = np.zeros((inp["beta"].shape[2], 128, 128), np.float32) if h0 is None else h0[s]
+            assert np.array_equal(hT[s].cpu().numpy(), want)
+
+
+def test_chunk_fwd_cp_packed_in_place_state(gpu):
+    """Packed split forward with final_state = initial_state: the split sequences' segment 0
+    reads the combine's copy, the one-segment sequences read and write their own state in one
+    workgroup."""
+    import torch
+    import chunkwise_gated_deltanet_amd as cg
+    spec, seg = CP_CASES["packed_mu4_h0_seg2"]
+    inp, h0 = make_inputs(spec)
+    say("chunk_fwd_cp packed in place, segment_chunks=2")
+    k, v, beta, cu = to_device(inp, gpu)
+    q = q_of(inp, gpu)
+    g = gate_of(inp, gpu)
+    W, U = cg.wu_prepare(k, v, beta, 64, g=g, cu_seqlens=cu)
+    o1, h1 = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=torch.from_numpy(h0).to(gpu),
+                          cu_seqlens=cu, output_final_state=True, segment_chunks=seg)
+    state = torch.from_numpy(h0).to(gpu)
+    o2, h2 = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=state, final_state=state,
+                          cu_seqlens=cu, segment_chunks=seg)
+    torch.cuda.synchronize(gpu)
+    assert h2.data_ptr() == state.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
 def test_chunk_fwd_cp_in_place_state(gpu):
