@@ -57,6 +57,7 @@ struct Params {
     int32_t hq;
     int32_t hv;
     int32_t num_seqs;
+    int32_t group;  // preparation kernel: consecutive units a workgroup takes in turn (divides hv)
 };
 
 // Placement of the fp32 C x C tile (A, then T, then T') in LDS; off(r, c) is the float offset

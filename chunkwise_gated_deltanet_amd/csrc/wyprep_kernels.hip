@@ -1017,28 +1017,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int* info = reinterpret_cast<int*>(smem + L::OFF_INFO);
 
-    // Workgroups are dealt round-robin to the 8 XCDs; in every round give each XCD a
-    // contiguous range of units, so value heads sharing a key head meet in one L2.
+    // A workgroup takes groups of q = p.group consecutive units (the value heads of one key head
+    // of one chunk, or two such at C = 32) one after the other: they read the same key rows and
+    // write neighbouring rows of T, W and U.  Its next group is G groups on.  Workgroups are
+    // dealt round-robin to the 8 XCDs; in every round each XCD gets a contiguous range of
+    // groups.
     const uint32_t G = gridDim.x;  // a multiple of 8
     const int64_t first = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
+    const int64_t q = p.group;
+    const int64_t GS = static_cast<int64_t>(G) * q;  // units from a group to this workgroup's next
+    auto next_unit = [q, GS](int64_t l) { return (l + 1) % q != 0 ? l + 1 : l + 1 - q + GS; };
 
     // Fewer than 64 packed sequences: wave 0 keeps cu_seqlens in registers (lane l: cu[min(l, N)])
     // for the whole launch, so every unit's search is a ballot and two shuffles.
     const bool cached = p.cu != nullptr && p.num_seqs < 64;
     const int cu_lane = cached && threadIdx.x < 64 ? p.cu[min(static_cast<int>(threadIdx.x), p.num_seqs)] : 0;
-    int64_t logical = first;
-    Unit cur = map_unit<C>(p, info, logical, G, threadIdx.x, cached, cu_lane);
+    // A packed slot past its sequence's end is empty for all its value heads, so the search for a
+    // non-empty unit (map_search) starts only at a group's first unit and steps GS at a time.
+    int64_t logical = first * q;
+    Unit cur = map_unit<C>(p, info, logical, GS, threadIdx.x, cached, cu_lane);
     if (cur.n <= 0) return;  // uniform per workgroup
     __syncthreads();  // every wave has read info before the next unit's search rewrites it
     Prefetch<C, L::ESZ, L::KROW, WU || (M & kModeSolve) != 0, (M & kModeGate) != 0> pf;
     pf.issue_k(p, cur, threadIdx.x);
     // The first unit is peeled off the loop: the loop head is then reached only from the end
     // of a unit, so the memory-counter waits inside see one issue history.
-    int64_t next = logical + G;
-    cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G, cached, cu_lane);
+    int64_t next = next_unit(logical);
+    cur = run_unit<C, DT, M>(p, smem, pf, cur, next, GS, cached, cu_lane);
     while (cur.n > 0) {  // uniform
-        next += G;
-        cur = run_unit<C, DT, M>(p, smem, pf, cur, next, G, cached, cu_lane);
+        next = next_unit(next);
+        cur = run_unit<C, DT, M>(p, smem, pf, cur, next, GS, cached, cu_lane);
     }
 }
 
@@ -1104,8 +1112,17 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     int resident = 0;
     if (e == hipSuccess) resident = resident_grid<C, DT, M>(device, &e);
     if (e == hipSuccess) {
-        int64_t grid = (p.units + 7) / 8 * 8;
         const int64_t cap = static_cast<int64_t>(resident) / 8 * 8;
+        // Units in groups: the r = Hv / Hq value heads of one (chunk, key head) in turn on one
+        // workgroup.  Measured on MI355X against one unit per workgroup and round: packed 8
+        // sequences Hq=16 Hv=64 1132 -> 1073 us, B=4 T=16384 Hq=16 Hv=64 1073 -> 931 us, the same
+        // order as before where r = 1.  At C = 32 two key heads per group, where that still
+        // leaves every workgroup two groups: B=4 T=4096 H=32 108 -> 102 us, B=1 T=32768 H=8
+        // 53.7 -> 51.5 us (at C = 64 and 128 it was 1-3% slower).
+        const int r = p.hv / p.hq;
+        p.group = r;
+        if (C == 32 && p.hv % (2 * r) == 0 && p.units / (2 * r) >= 2 * cap) p.group = 2 * r;
+        int64_t grid = (p.units / p.group + 7) / 8 * 8;
         if (cap >= 8 && grid > cap) grid = cap;
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), L::TOTAL,
                            stream, p);
