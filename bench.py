@@ -472,7 +472,7 @@ def main(argv=None):
                          "(W, U, no T in HBM); kkt: wyp_kkt_solve (T only); solve: "
                          "wyp_solve_rhs with v as the one right-hand side (X = U, T never "
                          "formed); fwd: wyp_chunk_fwd "
-                         "(state recurrence and output from prepared W, U; C = 64); gdn: the "
+                         "(state recurrence and output from prepared W, U; C = 32, 64, 128); gdn: the "
                          "whole forward, wyp_wu_prepare then wyp_chunk_fwd; bwd: "
                          "wyp_wy_backward (dk, dv, dbeta, dg from dW, dU; no dT; C = 64)")
     ap.add_argument("--gate-mu", type=float, default=None,

@@ -78,9 +78,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kD = 128;        // dk = dv
-constexpr int kC = 64;         // chunk size
-constexpr int kNB = kC / 16;   // row tiles per chunk (one per wave)
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // the combine's workgroup
 constexpr int kBufferConfig = 0x00020000;
 // Non-temporal policy for what one workgroup alone reads or writes (its U slice, g, o).  Q, K
 // and W keep the default policy: the four dv-slice workgroups of a head each read them, and
@@ -107,6 +105,7 @@ struct Params {
     int32_t split;       // 1: the sequence-parallel form
     int32_t nseg;        // split batch rows: segments per row
     int32_t seg_chunks;  // split: chunks per segment
+    int32_t seg_tokens;  // split: seg_chunks x C tokens per segment
     float* ws_a;         // [a-slot][Hv][dk][dv]: a sequence's first a-slot S_start(0) (pass 2),
                          // a-slot s + 1 A_s (pass 1), then S_start(s + 1) (pass 2)
     float* ws_m;         // [m-slot][Hv][dk][dk]: M_s
@@ -114,7 +113,17 @@ struct Params {
 
 constexpr int QROW = kD + 8;          // bf16 per K row
 constexpr int SROW = kD + 8;          // bf16 per S^T row (one dv column of S)
-constexpr int VROW = kC + 8;          // bf16 per V'^T row (one dv column of V')
+
+// A chunk of C tokens is C / 16 row tiles, one per wave: C / 16 waves of 64 threads.  The state's
+// 8 dk row tiles are shared out over the waves, 128 / C each.
+template <int C>
+struct Geo {
+    static constexpr int NB = C / 16;        // row tiles per chunk (one per wave)
+    static constexpr int THREADS = 4 * C;    // NB waves
+    static constexpr int MT = kD / 16 / NB;  // dk row tiles of the state per wave
+    static constexpr int NG = C > 64 ? 2 : 1;  // gates per lane of wave 0
+    static constexpr int VROW = C + 8;       // bf16 per V'^T row (one dv column of V')
+};
 
 // A workgroup owns DVS of its head's dv columns (a slice: 32 or 64).  LDS plan (bytes): only what
 // several waves read goes through LDS: K (rows padded by 16 bytes, row stride 272 B, so 16-byte
@@ -123,25 +132,27 @@ constexpr int VROW = kC + 8;          // bf16 per V'^T row (one dv column of V')
 // are read by wave w alone, so they go from HBM straight into its MFMA operand registers: this
 // halves the LDS traffic of a chunk step.  45.8 KB at DVS = 32 (three workgroups per CU by LDS;
 // registers allow three ungated, two gated), 71.8 KB at DVS = 64 (two).
-template <int DVS>
+template <int C, int DVS>
 struct Slice {
+    static constexpr int VROW = Geo<C>::VROW;
     static constexpr int NT = DVS / 16;        // 16-column tiles of the slice
     static constexpr int COUNT = kD / DVS;     // slices per head
     static constexpr int PIECES = DVS / 32;    // 16-byte pieces of the U / O slice per thread
     static constexpr int RPC = DVS / 8;        // 16-byte pieces per row of the slice
     static constexpr int UROW = DVS + 8;       // bf16 per U / O slice row
     static constexpr int OFF_K = 0;
-    static constexpr int OFF_U = OFF_K + kC * QROW * 2;
-    static constexpr int OFF_O = OFF_U + kC * UROW * 2;
-    static constexpr int OFF_S = OFF_O + kC * UROW * 2;
+    static constexpr int OFF_U = OFF_K + C * QROW * 2;
+    static constexpr int OFF_O = OFF_U + C * UROW * 2;
+    static constexpr int OFF_S = OFF_O + C * UROW * 2;
     static constexpr int OFF_VN = OFF_S + DVS * SROW * 2;
     static constexpr int OFF_VD = OFF_VN + DVS * VROW * 2;
     static constexpr int OFF_G = OFF_VD + DVS * VROW * 2;
-    static constexpr int LDS_TOTAL = OFF_G + kC * 4;
-    static_assert(kC * RPC == PIECES * kThreads, "the U / O slice splits evenly over the threads");
+    static constexpr int LDS_TOTAL = OFF_G + C * 4;
+    static_assert(C * RPC == PIECES * Geo<C>::THREADS, "the U / O slice splits evenly over the threads");
+    static_assert(LDS_TOTAL <= 160 * 1024, "LDS plan exceeds 160 KiB");
 };
-static_assert(3 * Slice<32>::LDS_TOTAL <= 160 * 1024, "three workgroups per CU by LDS");
-static_assert(2 * Slice<64>::LDS_TOTAL <= 160 * 1024, "two workgroups per CU by LDS");
+static_assert(3 * Slice<64, 32>::LDS_TOTAL <= 160 * 1024, "C = 64: three workgroups per CU by LDS");
+static_assert(2 * Slice<64, 64>::LDS_TOTAL <= 160 * 1024, "C = 64: two workgroups per CU by LDS");
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -160,17 +171,19 @@ __device__ inline uint32_t row_bytes(int n, uint32_t stride, uint32_t width)
     return n > 0 ? static_cast<uint32_t>(n - 1) * stride + width : 0u;
 }
 
-// One chunk's data in flight to registers: K (64 rows x 256 B: four 16-byte pieces per thread),
-// the U slice (64 rows x 64 B: one piece per thread), g (wave 0, one per lane), and for wave w
-// its own Q and W rows 16 w .. 16 w + 15 as 16x16x32 MFMA operands: lane 16 lg + lr holds
-// elements 32 s + 8 lg .. + 7 of row 16 w + lr, s = 0..3.  Rows past the chunk's n tokens read
-// as 0 through the buffer range.
-template <int DVS>
+// One chunk's data in flight to registers: K (C rows x 256 B: four 16-byte pieces per thread),
+// the U slice (C rows x 2 DVS B: DVS / 32 pieces per thread), g (wave 0, one or two per lane), and
+// for wave w its own Q and W rows 16 w .. 16 w + 15 as 16x16x32 MFMA operands: lane 16 lg + lr
+// holds elements 32 s + 8 lg .. + 7 of row 16 w + lr, s = 0..3.  Rows past the chunk's n tokens
+// read as 0 through the buffer range.
+template <int C, int DVS>
 struct Chunk {
-    using F = Slice<DVS>;
+    using F = Slice<C, DVS>;
+    static constexpr int THREADS = Geo<C>::THREADS;
+    static constexpr int NG = Geo<C>::NG;
     u32x4 q[4], k[4], w[4];
     u32x4 u[F::PIECES];
-    float g;
+    float g[NG];
 
     // This wave's Q and W operands.
     __device__ void issue_qw(const Params& p, int64_t tok0, int n, int hk, int hv, int tid, bool want_q)
@@ -199,7 +212,7 @@ struct Chunk {
         const __amdgpu_buffer_rsrc_t kr = rsrc(p.k + (tok0 * p.hq + hk) * kD, row_bytes(n, qstride, kD * 2));
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int pc = tid + it * kThreads;  // row pc / 16, piece pc % 16
+            const int pc = tid + it * THREADS;  // row pc / 16, piece pc % 16
             k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (pc >> 4) * qstride + (pc & 15) * 16, 0, 0);
         }
         // the transition slices of the sequence-parallel pass read no U: an empty range
@@ -207,42 +220,54 @@ struct Chunk {
                                                want_u ? row_bytes(n, wstride, DVS * 2) : 0u);
 #pragma unroll
         for (int it = 0; it < F::PIECES; ++it) {
-            const int pc = tid + it * kThreads;  // row pc / RPC, piece pc % RPC
+            const int pc = tid + it * THREADS;  // row pc / RPC, piece pc % RPC
             u[it] = __builtin_amdgcn_raw_buffer_load_b128(ur, (pc / F::RPC) * wstride + (pc % F::RPC) * 16, 0, kStream);
         }
-        g = 0.f;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) g[i] = 0.f;
         if constexpr (GT) {
-            // every thread loads; rows tid >= n (all of waves 1-3) fall outside the range
-            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, row_bytes(n, p.hv * 4, 4));
-            g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, tid * p.hv * 4, 0, kStream));
+            // wave 0 only (the other waves get an empty range): lane l takes rows l and 64 + l;
+            // rows >= n read as 0
+            const __amdgpu_buffer_rsrc_t gr =
+                rsrc(p.g + tok0 * p.hv + hv, tid < 64 ? row_bytes(n, p.hv * 4, 4) : 0u);
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                g[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                    gr, (64 * i + (tid & 63)) * p.hv * 4, 0, kStream));
         }
         issue_qw(p, tok0, n, hk, hv, tid, want_q);
     }
 
     // K and U to LDS; wave 0 turns g into the chunk-local inclusive prefix sums G (fp64 shuffle
-    // scan, stored as fp32).  Q and W stay in registers.
+    // scan, 64 rows at a time, stored as fp32).  Q and W stay in registers.
     template <bool GT>
     __device__ void commit(unsigned char* smem, int tid) const
     {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int pc = tid + it * kThreads;
+            const int pc = tid + it * THREADS;
             *reinterpret_cast<u32x4*>(smem + F::OFF_K + (pc >> 4) * (QROW * 2) + (pc & 15) * 16) = k[it];
         }
 #pragma unroll
         for (int it = 0; it < F::PIECES; ++it) {
-            const int pc = tid + it * kThreads;
+            const int pc = tid + it * THREADS;
             *reinterpret_cast<u32x4*>(smem + F::OFF_U + (pc / F::RPC) * (F::UROW * 2) + (pc % F::RPC) * 16) = u[it];
         }
         if constexpr (GT) {
             if (tid < 64) {
-                double x = static_cast<double>(g);
+                double carry = 0.0;  // the sum over the rows of the lanes' earlier blocks
 #pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const double t = __shfl_up(x, d);
-                    if (tid >= d) x += t;
+                for (int i = 0; i < NG; ++i) {
+                    double x = static_cast<double>(g[i]);
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const double t = __shfl_up(x, d);
+                        if (tid >= d) x += t;
+                    }
+                    x += carry;
+                    reinterpret_cast<float*>(smem + F::OFF_G)[64 * i + tid] = static_cast<float>(x);
+                    carry = __shfl(x, 63);
                 }
-                reinterpret_cast<float*>(smem + F::OFF_G)[tid] = static_cast<float>(x);
             }
         }
     }
@@ -281,7 +306,7 @@ struct Seg {
 template <bool ASLOT>
 __device__ inline int packed_owner(const Params& p, int idx, int lane)
 {
-    const int X = p.seg_chunks * kC;
+    const int X = p.seg_tokens;
     int lo = 0, span = p.num_seqs;
     while (span > 1) {  // uniform
         const int step = (span + 63) >> 6;
@@ -310,7 +335,7 @@ __device__ inline Seg seq_slots(const Params& p, int n)
         s.abase = n * p.nseg;
         s.mbase = n * (p.nseg - 1);
     } else {
-        const int X = p.seg_chunks * kC;
+        const int X = p.seg_tokens;
         const int c0 = p.cu[n], len = p.cu[n + 1] - c0;
         s.nseg = len > X ? (len + X - 1) / X : 1;
         s.mbase = c0 / X;
@@ -342,18 +367,21 @@ __device__ inline Seg locate(const Params& p, int slot, int lane)
     return s;
 }
 
-template <bool GT, bool LOCAL, int DVS>
-// Two waves per SIMD for the register allocator: the two register sets of the chunk pipeline take
-// 155 (gated: 177) VGPRs; with three the gated instance spills, and the ungated one is slower at
-// one workgroup per CU.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
+template <int C, bool GT, bool LOCAL, int DVS>
+// Two waves per SIMD for the register allocator: at C = 64 the two register sets of the chunk
+// pipeline take 155 (gated: 177) VGPRs; with three the gated instance spills, and the ungated
+// one is slower at one workgroup per CU.
+__global__ __launch_bounds__(Geo<C>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void chunk_fwd_kernel(Params p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // item = (slot * Hv + hv) * NSL + slice over the a-slots (unsplit: the sequences), or in
     // pass 1 (LOCAL) over the m-slots with twice the slices (A's, then M's); no pass-1 item for
     // a sequence's last segment
-    using F = Slice<DVS>;
+    using F = Slice<C, DVS>;
     constexpr int NT = F::NT;
+    constexpr int NB = Geo<C>::NB;
+    constexpr int MT = Geo<C>::MT;
+    constexpr int VROW = Geo<C>::VROW;
     constexpr int NSL = LOCAL ? 2 * F::COUNT : F::COUNT;
     // Workgroups are dealt round-robin to the 8 XCDs (block b to XCD b mod 8).  A group is one
     // (sequence or segment, key head): its value heads' dv slices read the same Q, K and W rows, so
@@ -377,7 +405,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int hk = hv / (p.hv / p.hq);
     int64_t s0, s1;
     seq_range(p, seq, &s0, &s1);
-    const int nchunks_seq = static_cast<int>((s1 - s0 + kC - 1) / kC);
+    const int nchunks_seq = static_cast<int>((s1 - s0 + C - 1) / C);
     const int c_begin = p.split ? seg * p.seg_chunks : 0;
     const int c_end = p.split ? min(c_begin + p.seg_chunks, nchunks_seq) : nchunks_seq;
     const int64_t slot_floats = static_cast<int64_t>(p.hv) * kD * kD;  // one workspace slot
@@ -393,12 +421,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __bf16* Vd = reinterpret_cast<__bf16*>(smem + F::OFF_VD);
     const float* Gs = reinterpret_cast<const float*>(smem + F::OFF_G);
 
-    // State tiles of this wave: S[16 mt + 4 lg + r][16 nt + lr], mt = 2 wave + m, in fp32.
+    // State tiles of this wave: S[16 mt + 4 lg + r][16 nt + lr], mt = MT wave + m, in fp32.
     // Start: pass 1 from zero (A) or from the identity's columns (M); unsplit, the sequence's
     // initial state (also a split launch's one-segment sequences); split, the S_start the combine
     // left in the workspace (segment 0 too: the combine copied the initial state there before
     // this pass, so the last segment may write the final state over the initial state's buffer).
-    f32x4 sacc[2][NT];
+    f32x4 sacc[MT][NT];
     const float* h0 = nullptr;
     if (!LOCAL) {
         if (at.nseg == 1)
@@ -408,25 +436,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     if (h0) h0 += slice * DVS;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * (2 * wave + m) + 4 * lg + r, col = 16 * nt + lr;
+                const int row = 16 * (MT * wave + m) + 4 * lg + r, col = 16 * nt + lr;
                 sacc[m][nt][r] = h0 ? h0[row * kD + col] : (mcols && row == slice * DVS + col ? 1.f : 0.f);
             }
 
     // S^T (bf16) for the first chunk's products: row = dv column, 4 consecutive dk per lane
     auto write_st = [&]() {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 bf16x4 v;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[r] = static_cast<__bf16>(sacc[m][nt][r]);
-                *reinterpret_cast<bf16x4*>(St + (16 * nt + lr) * SROW + 16 * (2 * wave + m) + 4 * lg) = v;
+                *reinterpret_cast<bf16x4*>(St + (16 * nt + lr) * SROW + 16 * (MT * wave + m) + 4 * lg) = v;
             }
     };
     write_st();
@@ -434,11 +462,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // Two register sets take turns (the loop is unrolled by two): chunk c + 1's loads go into the
     // set chunk c does not use, right after chunk c's first barrier, so they have a whole chunk
     // step to arrive, and no register copy makes the compiler wait for them early.
-    Chunk<DVS> ch0, ch1;
+    Chunk<C, DVS> ch0, ch1;
     const bool want_q = !LOCAL, want_u = !mcols;
     {
-        const int64_t t0 = s0 + static_cast<int64_t>(c_begin) * kC;
-        const int n0 = c_begin < c_end ? static_cast<int>(s1 - t0 < kC ? s1 - t0 : kC) : 0;
+        const int64_t t0 = s0 + static_cast<int64_t>(c_begin) * C;
+        const int n0 = c_begin < c_end ? static_cast<int>(s1 - t0 < C ? s1 - t0 : C) : 0;
         ch0.template issue<GT>(p, t0, n0, hk, hv, slice, tid, want_q, want_u);
         // Each chunk step ends with its O store; the loop is entered after a store too (over an
         // empty range: the hardware drops it), so both ways into the loop have the same memory
@@ -446,9 +474,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if constexpr (!LOCAL)
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rsrc(p.o, 0u), 0, 0, kStream);
     }
-    auto step = [&](int c, const Chunk<DVS>& cur, Chunk<DVS>& nxt) {
-        const int64_t tok0 = s0 + static_cast<int64_t>(c) * kC;
-        const int n = static_cast<int>(s1 - tok0 < kC ? s1 - tok0 : kC);
+    auto step = [&](int c, const Chunk<C, DVS>& cur, Chunk<C, DVS>& nxt) {
+        const int64_t tok0 = s0 + static_cast<int64_t>(c) * C;
+        const int n = static_cast<int>(s1 - tok0 < C ? s1 - tok0 : C);
         cur.template commit<GT>(smem, tid);
         // this wave's Q and W operands, straight from the registers they were loaded into
         bf16x8 qa[kD / 32], wa[kD / 32];
@@ -459,11 +487,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         __syncthreads();  // B1: the chunk (and the state's S^T) is in LDS
         // every load of the next chunk goes in flight now, into the other register set
-        const int64_t nt0 = tok0 + kC;
-        const int nn = c + 1 < c_end ? static_cast<int>(s1 - nt0 < kC ? s1 - nt0 : kC) : 0;
+        const int64_t nt0 = tok0 + C;
+        const int nn = c + 1 < c_end ? static_cast<int>(s1 - nt0 < C ? s1 - nt0 : C) : 0;
         nxt.template issue<GT>(p, nt0, nn, hk, hv, slice, tid, want_q, want_u);
         const int I = wave;  // row tile of V' and O
-        const float glast = GT ? Gs[kC - 1] : 0.f;
+        const float glast = GT ? Gs[C - 1] : 0.f;
         float grow[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) grow[r] = GT ? Gs[16 * I + 4 * lg + r] : 0.f;
@@ -502,11 +530,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // P^T tiles K_J Q_I^T, J <= I.  Accumulator element r of lane 16 lg + lr is
         // P[i = 16 I + lr][j = 16 J + 4 lg + r] = q_i . k_j: the A operand of the 16x16x16
         // product with V'.  Causal mask (j <= i) and the decay Gamma[i][j] applied in place.
-        bf16x4 pa[kNB];
+        bf16x4 pa[NB];
         float gi = 0.f;
         if constexpr (GT) gi = Gs[16 * I + lr];
 #pragma unroll
-        for (int J = 0; J < kNB; ++J) {
+        for (int J = 0; J < NB; ++J) {
             if (LOCAL || J > I) break;  // uniform
             f32x4 pt = zero4();
 #pragma unroll
@@ -528,7 +556,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
         // 2a. O += (Gamma o P) V' over the causal k tiles (16x16x16 bf16)
 #pragma unroll
-        for (int J = 0; J < kNB; ++J) {
+        for (int J = 0; J < NB; ++J) {
             if (LOCAL || J > I) break;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -540,15 +568,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // 2b. S = exp(G_last) S + K^T V'_dec; K^T fragments by transposed LDS reads: lane
         // 16 lg + L addresses token row 16 kt + 4 lg + L / 4, dk columns 16 mt + 4 (L % 4) .. +3
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int mt = 2 * wave + m;
+        for (int m = 0; m < MT; ++m) {
+            const int mt = MT * wave + m;
             if constexpr (GT) {
                 const float e = __expf(glast);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) sacc[m][nt] *= e;
             }
 #pragma unroll
-            for (int kt = 0; kt < kNB; ++kt) {
+            for (int kt = 0; kt < NB; ++kt) {
                 const __bf16* p0 = Ks + (16 * kt + 4 * lg + (lr >> 2)) * QROW + 16 * mt + 4 * (lr & 3);
                 const i16x4 kfr = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
 #pragma unroll
@@ -575,7 +603,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 rsrc(p.o + (tok0 * p.hv + hv) * kD + slice * DVS, (n - 1) * ostride + DVS * 2);
 #pragma unroll
             for (int it = 0; it < F::PIECES; ++it) {
-                const int pc = tid + it * kThreads;
+                const int pc = tid + it * Geo<C>::THREADS;
                 const u32x4 val = *reinterpret_cast<const u32x4*>(smem + F::OFF_O + (pc / F::RPC) * (F::UROW * 2) + (pc % F::RPC) * 16);
                 __builtin_amdgcn_raw_buffer_store_b128(val, orr, (pc / F::RPC) * ostride + (pc % F::RPC) * 16, 0, kStream);
             }
@@ -595,12 +623,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (out != nullptr) {
         float* hT = out;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    hT[(16 * (2 * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] = sacc[m][nt][r];
+                    hT[(16 * (MT * wave + m) + 4 * lg + r) * kD + 16 * nt + lr] = sacc[m][nt][r];
     }
 }
 
@@ -707,10 +735,11 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
     }
 }
 
-template <bool GT, int DVS>
+template <int C, bool GT, int DVS>
 int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 {
-    using F = Slice<DVS>;
+    using F = Slice<C, DVS>;
+    constexpr int THREADS = Geo<C>::THREADS;
     static std::once_flag once[64];
     static hipError_t attr_err[64];
     int device = 0;
@@ -718,10 +747,10 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
     if (e == hipSuccess && (device < 0 || device >= 64)) e = hipErrorInvalidDevice;
     if (e == hipSuccess) {
         std::call_once(once[device], [&] {
-            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, false, DVS>),
+            attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<C, GT, false, DVS>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS_TOTAL);
             if (attr_err[device] == hipSuccess)
-                attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<GT, true, DVS>),
+                attr_err[device] = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<C, GT, true, DVS>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS_TOTAL);
         });
         e = attr_err[device];
@@ -745,6 +774,7 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         p.split = a.split;
         p.nseg = a.nseg;
         p.seg_chunks = a.seg_chunks;
+        p.seg_tokens = a.seg_chunks * C;  // a split has a segment boundary inside T
         p.ws_a = a.ws;
         p.ws_m = a.split ? a.ws + static_cast<int64_t>(a.a_slots) * a.num_v_heads * kD * kD : nullptr;
         const int hv = a.num_v_heads;
@@ -756,8 +786,8 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         };
         if (p.split) {
             p.work = a.m_slots * hv * 2 * F::COUNT;  // pass 1
-            hipLaunchKernelGGL((chunk_fwd_kernel<GT, true, DVS>), dim3(grid_of(p.work, 2 * F::COUNT)),
-                               dim3(kThreads), F::LDS_TOTAL, stream, p);
+            hipLaunchKernelGGL((chunk_fwd_kernel<C, GT, true, DVS>), dim3(grid_of(p.work, 2 * F::COUNT)),
+                               dim3(THREADS), F::LDS_TOTAL, stream, p);
             e = hipGetLastError();
             if (e == hipSuccess) {  // pass 2
                 const int groups = a.num_seqs * hv;
@@ -768,14 +798,14 @@ int launch_t(const FwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         }
         if (e == hipSuccess) {  // pass 3 (the whole forward when not split)
             p.work = (p.split ? a.a_slots : a.num_seqs) * hv * F::COUNT;
-            hipLaunchKernelGGL((chunk_fwd_kernel<GT, false, DVS>), dim3(grid_of(p.work, F::COUNT)),
-                               dim3(kThreads), F::LDS_TOTAL, stream, p);
+            hipLaunchKernelGGL((chunk_fwd_kernel<C, GT, false, DVS>), dim3(grid_of(p.work, F::COUNT)),
+                               dim3(THREADS), F::LDS_TOTAL, stream, p);
             e = hipGetLastError();
         }
     }
     if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (chunk_fwd, gated=%d, split=%d, slice=%d)", hipGetErrorString(e), GT ? 1 : 0,
-                      a.split, DVS);
+        std::snprintf(msg, msg_len, "%s (chunk_fwd, C=%d, gated=%d, split=%d, slice=%d)", hipGetErrorString(e), C,
+                      GT ? 1 : 0, a.split, DVS);
         return static_cast<int>(e);
     }
     return 0;
@@ -805,8 +835,9 @@ int cu_count(int* out)
 // workgroup instead of 2x; it wins once the 64-column workgroups (two per (sequence or segment,
 // value head)) give every CU one, and loses below that, where the 32-column grid fills twice as
 // many CUs.  Both widths do the same operations per column in the same order, so the results
-// are identical bit for bit.
-template <bool GT>
+// are identical bit for bit.  C = 32 keeps 32 columns: its two waves hold four dk row tiles of
+// the state each, and the gated 64-column instance would spill.
+template <int C, bool GT>
 int launch_s(const FwdArgs& a, hipStream_t s, char* msg, int len)
 {
     int cus = 0;
@@ -816,8 +847,10 @@ int launch_s(const FwdArgs& a, hipStream_t s, char* msg, int len)
         return e;
     }
     const int64_t items = static_cast<int64_t>(a.split ? a.a_slots : a.num_seqs) * a.num_v_heads;
-    if (items * Slice<64>::COUNT >= cus) return launch_t<GT, 64>(a, s, msg, len);
-    return launch_t<GT, 32>(a, s, msg, len);
+    if constexpr (C > 32) {
+        if (items * Slice<C, 64>::COUNT >= cus) return launch_t<C, GT, 64>(a, s, msg, len);
+    }
+    return launch_t<C, GT, 32>(a, s, msg, len);
 }
 
 }  // namespace
@@ -850,7 +883,15 @@ int cp_scratch(void** ptr, char* msg, int msg_len)
 int launch_fwd(const FwdArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return a.g != nullptr ? fwd::launch_s<true>(a, s, msg, msg_len) : fwd::launch_s<false>(a, s, msg, msg_len);
+    switch (a.chunk_size) {
+    case 32:
+        return a.g != nullptr ? fwd::launch_s<32, true>(a, s, msg, msg_len) : fwd::launch_s<32, false>(a, s, msg, msg_len);
+    case 64:
+        return a.g != nullptr ? fwd::launch_s<64, true>(a, s, msg, msg_len) : fwd::launch_s<64, false>(a, s, msg, msg_len);
+    default:
+        return a.g != nullptr ? fwd::launch_s<128, true>(a, s, msg, msg_len)
+                              : fwd::launch_s<128, false>(a, s, msg, msg_len);
+    }
 }
 
 }  // namespace wyp

@@ -139,8 +139,8 @@ wyp_status validate_fwd(const wyp_problem* p, const void* q, const void* k, cons
     if (p->head_dim_k != 128 || p->head_dim_v != 128)
         return fail(WYP_ERR_UNSUPPORTED, "only head_dim_k = head_dim_v = 128 is built (got %d, %d)",
                     p->head_dim_k, p->head_dim_v);
-    if (p->chunk_size != 64)
-        return fail(WYP_ERR_UNSUPPORTED, "wyp_chunk_fwd is built for chunk_size 64 (got %d)",
+    if (p->chunk_size != 32 && p->chunk_size != 64 && p->chunk_size != 128)
+        return fail(WYP_ERR_UNSUPPORTED, "wyp_chunk_fwd is built for chunk_size 32, 64 and 128 (got %d)",
                     p->chunk_size);
     if (!(scale == scale) || scale == 1.0f / 0.0f || scale == -1.0f / 0.0f)
         return fail(WYP_ERR_INVALID_ARGUMENT, "scale must be finite");
@@ -186,6 +186,7 @@ wyp_status validate_fwd(const wyp_problem* p, const void* q, const void* k, cons
     out->num_qk_heads = p->num_qk_heads;
     out->num_v_heads = p->num_v_heads;
     out->num_seqs = static_cast<int32_t>(nseq);
+    out->chunk_size = p->chunk_size;
     return WYP_OK;
 }
 
@@ -334,7 +335,7 @@ namespace {
 
 // Slots of the split forward.  Batch rows: nseg = ceil(chunks / segment_chunks) segments per row,
 // B nseg a-slots and B (nseg - 1) m-slots.  Packed sequences (segments aligned to each
-// sequence's first chunk, X = 64 segment_chunks tokens each): floor(T / X) + N a-slots and
+// sequence's first chunk, X = C segment_chunks tokens each): floor(T / X) + N a-slots and
 // floor(T / X) m-slots, enough for any length mix.  No m-slot means no split.
 struct CpPlan {
     int64_t nseg, a_slots, m_slots;
@@ -342,17 +343,18 @@ struct CpPlan {
 
 bool cp_plan(const wyp_problem* p, bool packed, int32_t segment_chunks, CpPlan* out)
 {
-    if (!p || segment_chunks < 1 || p->chunk_size != 64 || p->seqlen < 0 || p->num_v_heads < 1)
-        return false;
+    if (!p || segment_chunks < 1 || p->seqlen < 0 || p->num_v_heads < 1) return false;
+    if (p->chunk_size != 32 && p->chunk_size != 64 && p->chunk_size != 128) return false;
+    const int64_t C = p->chunk_size;
     if (packed) {
         if (p->batch != 1 || p->num_seqs < 0) return false;
-        const int64_t e = p->seqlen / (64 * static_cast<int64_t>(segment_chunks));
+        const int64_t e = p->seqlen / (C * segment_chunks);
         out->nseg = 0;
         out->m_slots = e;
         out->a_slots = e > 0 ? e + p->num_seqs : 0;
     } else {
         if (p->batch < 1) return false;
-        const int64_t nchunks = (static_cast<int64_t>(p->seqlen) + 63) / 64;
+        const int64_t nchunks = (static_cast<int64_t>(p->seqlen) + C - 1) / C;
         const int64_t nseg = nchunks == 0 ? 1 : (nchunks + segment_chunks - 1) / segment_chunks;
         out->nseg = nseg;
         out->m_slots = nseg > 1 ? p->batch * (nseg - 1) : 0;

@@ -47,11 +47,12 @@ struct FwdArgs {
     int32_t num_qk_heads;
     int32_t num_v_heads;
     int32_t num_seqs;          // sequences (cu_seqlens) or batch rows
+    int32_t chunk_size;        // C: 32, 64 or 128
     int32_t split;             // 1: the sequence-parallel form (the fields below)
     int32_t nseg;              // batch rows: segments per row
     int32_t seg_chunks;        // chunks per segment
-    int32_t a_slots;           // batch rows: B nseg; packed: floor(T / (64 seg_chunks)) + N
-    int32_t m_slots;           // batch rows: B (nseg - 1); packed: floor(T / (64 seg_chunks))
+    int32_t a_slots;           // batch rows: B nseg; packed: floor(T / (C seg_chunks)) + N
+    int32_t m_slots;           // batch rows: B (nseg - 1); packed: floor(T / (C seg_chunks))
     float* ws;                 // (a_slots + m_slots) x Hv x dk x dk floats
 };
 

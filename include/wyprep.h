@@ -173,8 +173,10 @@ wyp_status wyp_solve_rhs(const wyp_problem* problem, const void* k, const void* 
  *   o_out            [B, T, Hv, dv]   kv_dtype
  *   final_state      [N, Hv, dk, dv] float32, or NULL (not written)
  * The state stays fp32 on chip for the whole sequence; its products with W and Q take it
- * rounded to bf16.  Work is split over (sequence, value head, 32-column slice of dv).
- * Supported: kv_dtype WYP_BF16, chunk_size 64, dk = dv = 128 (else WYP_ERR_UNSUPPORTED).
+ * rounded to bf16.  Work is split over (sequence, value head, 32- or 64-column slice of dv).
+ * chunk_size is the C that W and U were prepared with.
+ * Supported: kv_dtype WYP_BF16, chunk_size 32, 64 or 128, dk = dv = 128 (else
+ * WYP_ERR_UNSUPPORTED).
  * q, k, w_in, u_in and o_out must be 16-byte aligned; g, the states 4-byte aligned.
  * initial_state and final_state may be the same buffer (an in-place state update): each
  * workgroup reads its own slice of the initial state first and writes only that slice last. */
@@ -196,31 +198,31 @@ wyp_status wyp_chunk_fwd(const wyp_problem* problem, const void* q, const void* 
  * may be the same buffer, as for wyp_chunk_fwd.
  * Arguments as for wyp_chunk_fwd, cu_seqlens included, plus:
  *   segment_chunks   chunks per segment, >= 1.  Segments start at a sequence's first chunk, so a
- *                    sequence of n tokens has ceil(n / (64 segment_chunks)) of them (one if it
+ *                    sequence of n tokens has ceil(n / (C segment_chunks)) of them (one if it
  *                    is shorter, or empty; such a sequence runs as in wyp_chunk_fwd).  When no
- *                    sequence can have two (batch rows: segment_chunks covers ceil(T / 64)
- *                    chunks; packed: 64 segment_chunks > T), the call is wyp_chunk_fwd itself
+ *                    sequence can have two (batch rows: segment_chunks covers ceil(T / C)
+ *                    chunks; packed: C segment_chunks > T), the call is wyp_chunk_fwd itself
  *                    and needs no workspace.
  *   workspace        caller-owned device memory of at least
  *                    wyp_chunk_fwd_cp_workspace_bytes(problem, cu_seqlens, segment_chunks) bytes,
  *                    16-byte aligned; its contents on entry do not matter and on return are
  *                    unspecified.  Calls that share a workspace must not overlap.
- * Supported as wyp_chunk_fwd (bf16, C = 64, dk = dv = 128). */
+ * Supported as wyp_chunk_fwd (bf16, C = 32, 64 or 128, dk = dv = 128). */
 wyp_status wyp_chunk_fwd_cp(const wyp_problem* problem, const void* q, const void* k,
                             const void* w_in, const void* u_in, const float* g,
                             const float* initial_state, float scale, const int32_t* cu_seqlens,
                             int32_t segment_chunks, void* workspace, int64_t workspace_bytes,
                             void* o_out, float* final_state, void* stream);
 
-/* Workspace bytes wyp_chunk_fwd_cp needs, with X = 64 segment_chunks tokens per segment:
+/* Workspace bytes wyp_chunk_fwd_cp needs, with X = C segment_chunks tokens per segment:
  *   batch rows (cu_seqlens NULL): B x Hv x (2 nseg - 1) x dk x dk x 4, nseg = ceil(T / X) (A
  *     and M of every segment but a row's last, and a copy of the initial state); 0 if nseg = 1;
  *   packed (cu_seqlens non-NULL; only whether it is NULL matters, it is not read):
  *     (2 floor(T / X) + N) x Hv x dk x dk x 4, with T the total tokens and N = num_seqs (no
  *     length mix needs more: a sequence's segments after its first number at most its tokens
  *     / X); 0 if T < X.
- * -1 for invalid arguments (segment_chunks < 1, chunk_size other than 64, NULL problem, batch
- * other than 1 with cu_seqlens). */
+ * -1 for invalid arguments (segment_chunks < 1, chunk_size other than 32, 64 or 128, NULL
+ * problem, batch other than 1 with cu_seqlens). */
 int64_t wyp_chunk_fwd_cp_workspace_bytes(const wyp_problem* problem, const int32_t* cu_seqlens,
                                          int32_t segment_chunks);
 

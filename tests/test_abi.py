@@ -138,8 +138,8 @@ def call_fwd(lib, p, q=FAKE, k=FAKE, w=FAKE, u=FAKE, g=None, h0=None, scale=0.5,
 
 
 @pytest.mark.parametrize("kw,code,needle", [
-    (dict(chunk_size=32), 2, "chunk_size"),
-    (dict(chunk_size=128), 2, "chunk_size"),
+    (dict(chunk_size=48), 2, "chunk_size"),
+    (dict(chunk_size=256), 2, "chunk_size"),
     (dict(kv_dtype=1), 2, "bf16"),
     (dict(head_dim_v=64), 2, "head_dim"),
     (dict(num_v_heads=3), 1, "multiple"),
@@ -198,7 +198,11 @@ def test_chunk_fwd_cp_workspace_and_rejects(lib):
     # four segments: A and M of three, plus the initial-state copy, per (row, value head)
     assert ws(ctypes.byref(p), None, 5) == 2 * 4 * 7 * 128 * 128 * 4
     assert ws(ctypes.byref(p), None, 0) == -1
-    assert ws(ctypes.byref(good(chunk_size=32)), None, 4) == -1
+    assert ws(ctypes.byref(good(chunk_size=48)), None, 4) == -1
+    # C = 32 and 128: segments of segment_chunks x C tokens
+    assert ws(ctypes.byref(good(batch=2, seqlen=1000, num_v_heads=4, chunk_size=32)), None, 8) == \
+        2 * 4 * (2 * 4 - 1) * 128 * 128 * 4   # 32 chunks of 32 per row: 4 segments
+    assert ws(ctypes.byref(good(batch=2, seqlen=1000, num_v_heads=4, chunk_size=128)), None, 8) == 0
     need = ws(ctypes.byref(p), None, 4)
 
     def call(seg=4, ws=FAKE, nbytes=need, **kw):
@@ -260,7 +264,7 @@ def test_chunk_fwd_cp_noalloc_rejects_before_any_hip_call(lib):
     assert call(big, 16) == 2
     assert "scratch" in lib.wyp_last_error().decode()
     assert call(p, 0) == 1
-    assert call(good(chunk_size=32), 4) == 2
+    assert call(good(chunk_size=48), 4) == 2
     assert call(good(seqlen=0), 4) == 0          # no tokens, no final state: a no-op
 
 

@@ -40,13 +40,30 @@ CASES = {
     "wide_packed_40_mu0_h0": dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4, seed=108,
                                   gate_mu=0.0, h0=True,
                                   seqlens=[1, 0, 64, 65, 127, 129, 200, 31, 33, 63] * 4),
+    # the other chunk sizes the preparation step supports: C = 32 (two waves per workgroup) and
+    # C = 128 (eight waves; gates two per lane)
+    "C32_B2_T333_H4_mu4_h0": dict(C=32, batch=2, seqlen=333, num_qk_heads=4, num_v_heads=4,
+                                  seed=109, gate_mu=4.0, h0=True),
+    "C32_packed_gva_ungated": dict(C=32, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=8,
+                                   seed=110, seqlens=[31, 32, 33, 1, 0, 95, 200]),
+    "C32_wide_B8_T200_H4_16_mu2": dict(C=32, batch=8, seqlen=200, num_qk_heads=4,
+                                       num_v_heads=16, seed=111, gate_mu=2.0),
+    "C128_B2_T333_H2_4_mu4_h0": dict(C=128, batch=2, seqlen=333, num_qk_heads=2, num_v_heads=4,
+                                     seed=112, gate_mu=4.0, h0=True),
+    "C128_packed_mu0_h0": dict(C=128, batch=1, seqlen=0, num_qk_heads=1, num_v_heads=2,
+                               seed=113, gate_mu=0.0, h0=True,
+                               seqlens=[127, 128, 129, 1, 0, 300, 64]),
+    "C128_wide_B8_T300_H4_16_ungated": dict(C=128, batch=8, seqlen=300, num_qk_heads=4,
+                                            num_v_heads=16, seed=114),
 }
 
 
 def make_inputs(spec):
     spec = dict(spec)
     want_h0 = spec.pop("h0", False)
-    inp = synth.custom(chunk_size=64, with_q=True, **spec)
+    C = spec.pop("C", 64)
+    inp = synth.custom(chunk_size=C, with_q=True, **spec)
+    inp["C"] = C
     N = inp["batch"] if inp["cu_seqlens"] is None else len(inp["cu_seqlens"]) - 1
     Hv = inp["beta"].shape[2]
     h0 = None
@@ -68,14 +85,15 @@ def run_fwd(inp, h0, device, in_place=False):
     k, v, beta, cu = to_device(inp, device)
     q = q_of(inp, device)
     g = gate_of(inp, device)
-    W, U = cg.wu_prepare(k, v, beta, 64, cu_seqlens=cu, g=g)
+    C = inp.get("C", 64)
+    W, U = cg.wu_prepare(k, v, beta, C, cu_seqlens=cu, g=g)
     o = torch.full(v.shape, float("nan"), dtype=v.dtype, device=device)
     h0d = None if h0 is None else torch.from_numpy(h0).to(device)
     if in_place:
-        o, hT = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=h0d, cu_seqlens=cu,
+        o, hT = cg.chunk_fwd(q, k, W, U, C, g=g, initial_state=h0d, cu_seqlens=cu,
                              o_out=o, final_state=h0d)
     else:
-        o, hT = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=h0d, cu_seqlens=cu,
+        o, hT = cg.chunk_fwd(q, k, W, U, C, g=g, initial_state=h0d, cu_seqlens=cu,
                              o_out=o, output_final_state=True)
     torch.cuda.synchronize(device)
     return o, hT
@@ -100,7 +118,8 @@ def test_chunk_fwd_small(name, gpu):
     if inp["cu_seqlens"] is not None:
         lens = np.diff(inp["cu_seqlens"])
         for s in np.nonzero(lens == 0)[0]:  # an empty sequence hands its initial state back
-            assert np.array_equal(hT[s].cpu().numpy(), h0[s])
+            want = np.zeros(hT[s].shape, np.float32) if h0 is None else h0[s]
+            assert np.array_equal(hT[s].cpu().numpy(), want)
 
 
 def test_chunk_fwd_in_place_state(gpu):
@@ -126,9 +145,10 @@ def test_chunk_gated_delta_rule_api(gpu):
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
-# Full sizes, C = 64: every (sequence, value head) pair against the oracle, whole tensors, with
-# the worst pair reported; every output entry written.
-FULL = [(2, None), (2, 4.0), (3, None), (5, 4.0)]
+# Full sizes: every (sequence, value head) pair against the oracle, whole tensors, with the worst
+# pair reported; every output entry written.  C = 64, and the other chunk sizes on one workload
+# each.
+FULL = [(2, None, 64), (2, 4.0, 64), (3, None, 64), (5, 4.0, 64), (4, None, 128), (2, 4.0, 32)]
 
 
 def compare_pairs(inp, o, hT, o_ref, h_ref, label):
@@ -154,11 +174,13 @@ def compare_pairs(inp, o, hT, o_ref, h_ref, label):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("idx,mu", FULL, ids=[f"w{i}_{'mu' + str(m) if m else 'ungated'}" for i, m in FULL])
-def test_chunk_fwd_full_size(idx, mu, gpu):
+@pytest.mark.parametrize("idx,mu,C", FULL,
+                         ids=[f"w{i}_{'mu' + str(m) if m else 'ungated'}_C{c}" for i, m, c in FULL])
+def test_chunk_fwd_full_size(idx, mu, C, gpu):
     import torch
-    w = synth.workload(idx, chunk_size=64, gate_mu=mu, with_q=True)
+    w = synth.workload(idx, chunk_size=C, gate_mu=mu, with_q=True)
     inp = synth.generate(w)
+    inp["C"] = C
     say(f"chunk_fwd full {w.name} gate_mu={mu} tokens={inp['batch'] * inp['seqlen']}")
     o, hT = run_fwd(inp, None, gpu)
     assert not torch.isnan(o).any(), "unwritten o entries"
@@ -197,6 +219,15 @@ CP_CASES = {
     # 64-column slices: 14 sequences, Hv = 16
     "wide_packed_mu4_seg3": (dict(batch=1, seqlen=0, num_qk_heads=4, num_v_heads=16, seed=140,
                                   gate_mu=4.0, seqlens=[1000, 333, 64, 0, 1, 2000, 150] * 2), 3),
+    # C = 32 and 128: segments of segment_chunks x C tokens
+    "C32_B1_T1000_H2_mu4_h0_seg5": (dict(C=32, batch=1, seqlen=1000, num_qk_heads=2,
+                                         num_v_heads=2, seed=141, gate_mu=4.0, h0=True), 5),
+    "C32_packed_seg3": (dict(C=32, batch=1, seqlen=0, num_qk_heads=1, num_v_heads=4, seed=142,
+                             seqlens=[500, 0, 33, 1, 250]), 3),
+    "C128_B1_T2100_H2_8_h0_seg3": (dict(C=128, batch=1, seqlen=2100, num_qk_heads=2,
+                                        num_v_heads=8, seed=143, h0=True), 3),
+    "C128_packed_mu4_seg2": (dict(C=128, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4,
+                                  seed=144, gate_mu=4.0, seqlens=[1300, 1, 0, 256, 257, 90]), 2),
 }
 
 
@@ -206,10 +237,11 @@ def run_fwd_cp(inp, h0, device, seg):
     k, v, beta, cu = to_device(inp, device)
     q = q_of(inp, device)
     g = gate_of(inp, device)
-    W, U = cg.wu_prepare(k, v, beta, 64, g=g, cu_seqlens=cu)
+    C = inp.get("C", 64)
+    W, U = cg.wu_prepare(k, v, beta, C, g=g, cu_seqlens=cu)
     o = torch.full(v.shape, float("nan"), dtype=v.dtype, device=device)
     h0d = None if h0 is None else torch.from_numpy(h0).to(device)
-    o, hT = cg.chunk_fwd(q, k, W, U, 64, g=g, initial_state=h0d, o_out=o, cu_seqlens=cu,
+    o, hT = cg.chunk_fwd(q, k, W, U, C, g=g, initial_state=h0d, o_out=o, cu_seqlens=cu,
                          output_final_state=True, segment_chunks=seg)
     torch.cuda.synchronize(device)
     return o, hT
