@@ -41,37 +41,42 @@ namespace {
 
 namespace bwd {
 
-constexpr int kC = 64;
-constexpr int kNB = kC / 16;
-// Eight waves per workgroup: LDS (141 KB) holds one workgroup per CU, and with one wave per SIMD
-// every LDS, MFMA and VALU latency of the unit's long serial chain would be exposed.  Phases
-// that tile over waves run twice as wide; the forward's Gram / substitution / coupling steps
-// keep their four-wave mapping.
-constexpr int kBT = 512;
-constexpr int kBW = kBT / 64;
-constexpr int kCW = kD / 16 / kBW;  // dk column tiles per wave in the transposed products
-constexpr int KROW = kD + 8;                 // bf16 per staged K / V / dW / dU row
-constexpr int TRS = kC + 4;                  // floats per n x n tile row
-constexpr int KB = kC * KROW * 2;            // 17408
-constexpr int TB = kC * TRS * 4;             // 17408
-constexpr int OFF_K = 0;
-constexpr int OFF_V = OFF_K + KB;
-constexpr int OFF_DW = OFF_V + KB;
-constexpr int OFF_DU = OFF_DW + KB;
-constexpr int OFF_T = OFF_DU + KB;           // A -> T (fp32) -> S = R + R^T (hi / lo)
-constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, strict lower (fp32)
-constexpr int OFF_X = OFF_H + TB;            // X -> Y^T -> M (fp32)
-constexpr int OFF_TT = OFF_X + TB;           // T^T as hi / lo chunks
-constexpr int OFF_B = OFF_TT + TB;           // beta (64 floats)
-constexpr int OFF_PART = OFF_B + kC * 4;     // per-wave row partials: kBW waves x 2 x 64 floats
-constexpr int OFF_RED = OFF_PART + kBW * 2 * kC * 4;  // dbeta, dG of this value head (2 x 64)
-constexpr int OFF_GD = OFF_RED + 2 * kC * 4;  // G of the chunk's rows, fp64 (gated instances)
-constexpr int OFF_INFO = OFF_GD + kC * 8;
-constexpr int LDS_TOTAL = OFF_INFO + 16;
-static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
-
-using TL = TLayout<kC>;
-using GR = GateRow<KROW, 2>;
+// Workgroup shape and LDS plan per chunk size.  Eight waves at C = 64: LDS (141 KB) holds one
+// workgroup per CU, and with one wave per SIMD every LDS, MFMA and VALU latency of the unit's long
+// serial chain would be exposed; phases that tile over waves run twice as wide, while the
+// forward's Gram / substitution / coupling steps keep their four-wave mapping.  Four waves at
+// C = 32 (54 KB, two workgroups per CU).  Either way eight threads share a row in the
+// elementwise step.
+template <int C>
+struct BG {
+    static constexpr int NB = C / 16;
+    static constexpr int BT = C == 64 ? 512 : 256;
+    static constexpr int BW = BT / 64;
+    static constexpr int CW = kD / 16 / BW;  // dk column tiles per wave in the transposed products
+    static constexpr int KROW = kD + 8;       // bf16 per staged K / V / dW / dU row
+    static constexpr int TRS = C + 4;         // floats per C x C tile row
+    static constexpr int KB = C * KROW * 2;
+    static constexpr int TB = C * TRS * 4;
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_V = OFF_K + KB;
+    static constexpr int OFF_DW = OFF_V + KB;
+    static constexpr int OFF_DU = OFF_DW + KB;
+    static constexpr int OFF_T = OFF_DU + KB;           // A -> T (fp32) -> S = R + R^T (hi / lo)
+    static constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, strict lower (fp32)
+    static constexpr int OFF_X = OFF_H + TB;            // X -> Y^T -> M (fp32)
+    static constexpr int OFF_TT = OFF_X + TB;           // T^T as hi / lo chunks
+    static constexpr int OFF_B = OFF_TT + TB;           // beta (C floats)
+    static constexpr int OFF_PART = OFF_B + C * 4;      // per-wave row partials: BW waves x 2 x C
+    static constexpr int OFF_RED = OFF_PART + BW * 2 * C * 4;  // dbeta, dG of this value head
+    static constexpr int OFF_GD = OFF_RED + 2 * C * 4;  // G of the chunk's rows, fp64 (gated)
+    static constexpr int OFF_INFO = OFF_GD + C * 8;
+    static constexpr int LDS_TOTAL = OFF_INFO + 16;
+    static constexpr int CPT = C / 8;                   // elementwise step: columns per thread
+    static_assert(BT / C == 8, "eight threads per row in the elementwise step");
+    static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
+    using TL = TLayout<C>;
+    using GR = GateRow<KROW, 2>;
+};
 
 struct Params {
     const __bf16* k;
@@ -96,8 +101,10 @@ struct Params {
 // Rows [0, n) of a [tokens, heads, 128] bf16 tensor in flight to registers (two 16-byte pieces
 // per thread; rows >= n read as 0 through the buffer range), then into LDS rows of KROW
 // elements.  All of a value head's rows are issued before any is waited for.
+template <int C>
 struct Rows {
-    static constexpr int NIT = kC * 16 / kBT;
+    static constexpr int KROW = BG<C>::KROW, kBT = BG<C>::BT;
+    static constexpr int NIT = C * 16 / kBT;
     u32x4 x[NIT];
 
     __device__ void issue(const __bf16* base, int64_t tok0, int n, int heads, int head, int tid)
@@ -126,9 +133,9 @@ struct Rows {
 // The inputs of one job (one value head hv of a unit: first token tok0, n tokens, key head hk)
 // in flight to registers: k (read only for the first value head of a unit), v, dW, dU, beta and
 // g.  n = 0 (past the last job) issues loads over empty ranges, so the issue has no branches.
-template <bool GT>
+template <int C, bool GT>
 struct JobIn {
-    Rows k, v, dw, du;
+    Rows<C> k, v, dw, du;
     float b, g;
 
     __device__ void issue(const Params& p, int64_t tok0, int n, int hk, int hv, bool with_k, int tid)
@@ -178,10 +185,16 @@ __device__ inline f32x4 unpack_hilo(u32x4 c)
 // row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed chunks).  KT_GE_MI
 // skips the k tiles kt < mi (B = T^T is zero there).  Accumulator element r of lane 16 g + c is
 // (.)[16 ni + 4 g + r][16 mi + c].
-template <bool KT_GE_MI>
+template <int C, bool KT_GE_MI>
 __device__ inline void tr_products(const unsigned char* src, const float* bp, int wave, int lr, int lg,
-                                   f32x4 (&acc)[kCW][kNB])
+                                   f32x4 (&acc)[BG<C>::CW][BG<C>::NB])
 {
+    using BGC = BG<C>;
+    constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
+    using TL = typename BGC::TL;
+    using GR = typename BGC::GR;
+
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const __bf16* base = reinterpret_cast<const __bf16*>(src);
@@ -212,9 +225,16 @@ __device__ inline void tr_products(const unsigned char* src, const float* bp, in
 
 // Stages transposed accumulators (element r of lane 16 g + c = X[16 mi + c][16 ni + 4 g + r])
 // as bf16 rows of `dst` and stores rows [0, n) to a [tokens, heads, 128] tensor.
-__device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][kNB], __bf16* out, int64_t tok0,
-                                   int n, int heads, int head, int wave, int lr, int lg, int tid)
+template <int C>
+__device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[BG<C>::CW][BG<C>::NB], __bf16* out,
+                                   int64_t tok0, int n, int heads, int head, int wave, int lr, int lg, int tid)
 {
+    using BGC = BG<C>;
+    constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
+    using TL = typename BGC::TL;
+    using GR = typename BGC::GR;
+
     __bf16* d = reinterpret_cast<__bf16*>(dst);
 #pragma unroll
     for (int c = 0; c < kCW; ++c)
@@ -229,7 +249,7 @@ __device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][k
     const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
     const __amdgpu_buffer_rsrc_t r = rsrc(out + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
 #pragma unroll
-    for (int it = 0; it < Rows::NIT; ++it) {
+    for (int it = 0; it < Rows<C>::NIT; ++it) {
         const int q = tid + it * kBT;
         const u32x4 val = *reinterpret_cast<const u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16);
         __builtin_amdgcn_raw_buffer_store_b128(val, r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
@@ -241,10 +261,16 @@ __device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[kCW][k
 // Gram per lower tile, over the eight waves.  Hs holds H below the diagonal and its transpose
 // above (Hs[j][i] = H[i][j] for i > j; 0 on the diagonal), so row i of Hs lists H_ij for j < i
 // and H_ji for j > i: the elementwise step then reads rows only.
-template <bool GT>
+template <int C, bool GT>
 __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const float* bs, int wave, int lr,
                          int lg)
 {
+    using BGC = BG<C>;
+    constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
+    using TL = typename BGC::TL;
+    using GR = typename BGC::GR;
+
     constexpr int NTILE = kNB * (kNB + 1) / 2;
     for (int t = wave; t < NTILE; t += kBW) {  // uniform
         int I = 0, J = 0;
@@ -284,23 +310,28 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
     }
 }
 
-template <bool GT>
-__global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
+template <int C, bool GT>
+__global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
 {
+    using BGC = BG<C>;
+    constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
+    using TL = typename BGC::TL;
+    using GR = typename BGC::GR;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned char* Kraw = smem + OFF_K;
-    unsigned char* Vraw = smem + OFF_V;
-    unsigned char* dWraw = smem + OFF_DW;
-    unsigned char* dUraw = smem + OFF_DU;
-    float* Ts = reinterpret_cast<float*>(smem + OFF_T);
-    float* Hs = reinterpret_cast<float*>(smem + OFF_H);
-    float* Xs = reinterpret_cast<float*>(smem + OFF_X);
-    float* TT = reinterpret_cast<float*>(smem + OFF_TT);
-    float* bs = reinterpret_cast<float*>(smem + OFF_B);
-    float* part = reinterpret_cast<float*>(smem + OFF_PART);
-    float* red = reinterpret_cast<float*>(smem + OFF_RED);
-    double* Gd = reinterpret_cast<double*>(smem + OFF_GD);
-    int* info = reinterpret_cast<int*>(smem + OFF_INFO);
+    unsigned char* Kraw = smem + BGC::OFF_K;
+    unsigned char* Vraw = smem + BGC::OFF_V;
+    unsigned char* dWraw = smem + BGC::OFF_DW;
+    unsigned char* dUraw = smem + BGC::OFF_DU;
+    float* Ts = reinterpret_cast<float*>(smem + BGC::OFF_T);
+    float* Hs = reinterpret_cast<float*>(smem + BGC::OFF_H);
+    float* Xs = reinterpret_cast<float*>(smem + BGC::OFF_X);
+    float* TT = reinterpret_cast<float*>(smem + BGC::OFF_TT);
+    float* bs = reinterpret_cast<float*>(smem + BGC::OFF_B);
+    float* part = reinterpret_cast<float*>(smem + BGC::OFF_PART);
+    float* red = reinterpret_cast<float*>(smem + BGC::OFF_RED);
+    double* Gd = reinterpret_cast<double*>(smem + BGC::OFF_GD);
+    int* info = reinterpret_cast<int*>(smem + BGC::OFF_INFO);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = uniform(tid >> 6);
@@ -325,7 +356,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
     if (u.n <= 0) return;  // uniform
     int hv = u.hv * r;
     bool new_unit = true;
-    JobIn<GT> in;
+    JobIn<C, GT> in;
     in.issue(p, u.tok0, u.n, u.hv, hv, true, tid);
     f32x4 dk_acc[kCW][kNB];
 #pragma unroll
@@ -345,15 +376,17 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         if (tid < kC) bs[tid] = in.b;
         if constexpr (GT) {
             if (tid < 64) {  // G = inclusive prefix sums of g in fp64 (as the forward)
-                double x = static_cast<double>(in.g);
+                double x = static_cast<double>(in.g);  // 0 past the chunk's rows
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
                     const double t = __shfl_up(x, d);
                     if (tid >= d) x += t;
                 }
-                *GR::Gp(Kraw, tid) = x;
-                *GR::Ep(Kraw, tid) = __expf(static_cast<float>(x));
-                Gd[tid] = x;
+                if (tid < kC) {  // the chunk's C rows
+                    *GR::Gp(Kraw, tid) = x;
+                    *GR::Ep(Kraw, tid) = __expf(static_cast<float>(x));
+                    Gd[tid] = x;
+                }
             }
         }
         __syncthreads();
@@ -371,7 +404,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);
 
         // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs)
-        form_a_h<GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
+        form_a_h<C, GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
         __syncthreads();
         // ---- wave 0 inverts the diagonal blocks of A (its substitutions are one long dependency
         // chain); meanwhile waves 1-7 form X, which does not depend on T
@@ -440,13 +473,13 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         }
         __syncthreads();
         coupling_level<kC, 16, TL>(Ts, tid);
-        coupling_level<kC, 32, TL>(Ts, tid);
+        if constexpr (kC >= 64) coupling_level<kC, 32, TL>(Ts, tid);
 
         // ---- T^T as hi / lo chunks: chunk (i, c4) holds T[4 c4 + e][i], e = 0..3
 #pragma unroll
-        for (int it = 0; it < kC * 16 / kBT; ++it) {
+        for (int it = 0; it < kC * (kC / 4) / kBT; ++it) {
             const int q = tid + it * kBT;
-            const int i = q >> 4, c4 = q & 15;
+            const int i = q / (kC / 4), c4 = q % (kC / 4);
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = Ts[(4 * c4 + e) * TRS + i];
@@ -537,14 +570,15 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         // already carries Gamma).  Row i of Xs and Hs holds M_ij, H_ij for j < i and M_ji, H_ji
         // for j > i, so every read is a 16-byte row chunk.
         {
-            const int i = tid >> 3, seg = tid & 7;  // row i, columns 8 seg .. 8 seg + 7
+            constexpr int CPT = BGC::CPT;
+            const int i = tid >> 3, seg = tid & 7;  // row i, columns CPT seg .. CPT seg + CPT - 1
             const float bi = bs[i];
             double gi = 0.0;
             if constexpr (GT) gi = Gd[i];
             float rowMH = 0.f, rowZ = 0.f, colZ = 0.f;
 #pragma unroll
-            for (int c4 = 0; c4 < 2; ++c4) {
-                const int j0 = 8 * seg + 4 * c4;
+            for (int c4 = 0; c4 < CPT / 4; ++c4) {
+                const int j0 = CPT * seg + 4 * c4;
                 const f32x4 mv = *reinterpret_cast<const f32x4*>(Xs + i * TRS + j0);
                 const f32x4 hv = *reinterpret_cast<const f32x4*>(Hs + i * TRS + j0);
                 const f32x4 bj = *reinterpret_cast<const f32x4*>(bs + j0);
@@ -590,7 +624,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
             for (int c = 0; c < kCW; ++c)
 #pragma unroll
                 for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            tr_products<true>(dWraw, TT, wave, lr, lg, acc);
+            tr_products<C, true>(dWraw, TT, wave, lr, lg, acc);
             // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
             const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
             const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
@@ -617,7 +651,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
             for (int c = 0; c < kCW; ++c)
 #pragma unroll
                 for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            tr_products<true>(dUraw, TT, wave, lr, lg, acc);
+            tr_products<C, true>(dUraw, TT, wave, lr, lg, acc);
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
                 const int i = 16 * mi + lr;
@@ -637,24 +671,28 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
                 if (lg == 0) part[(wave * 2 + 1) * kC + i] = sv;
             }
             __syncthreads();  // every read of dU (and V) done: dV is staged over dU
-            stage_store(dUraw, acc, p.dv, tok0, n, p.hv, hv, wave, lr, lg, tid);
+            stage_store<C>(dUraw, acc, p.dv, tok0, n, p.hv, hv, wave, lr, lg, tid);
         }
         // ---- (R + R^T) K into dK (bf16 MFMA, S hi / lo; S symmetric, so its row chunks are
         // also the column chunks the product needs)
-        tr_products<false>(Kraw, Ts, wave, lr, lg, dk_acc);
+        tr_products<C, false>(Kraw, Ts, wave, lr, lg, dk_acc);
 
-        // ---- dbeta, dG, dg of this value head
+        // ---- dbeta, dG, dg of this value head (lanes past the chunk's C rows hold 0; their stores
+        // fall outside the n-row buffer range)
         if (tid < 64) {
             const int i = tid;
+            const bool row = i < kC;
             float sk = 0.f, sv = 0.f;
+            if (row) {
 #pragma unroll
-            for (int w = 0; w < kBW; ++w) {
-                sk += part[(w * 2 + 0) * kC + i];
-                sv += part[(w * 2 + 1) * kC + i];
+                for (int w = 0; w < kBW; ++w) {
+                    sk += part[(w * 2 + 0) * kC + i];
+                    sv += part[(w * 2 + 1) * kC + i];
+                }
             }
-            const float ei = GT ? GR::E(Kraw, i) : 1.f;
-            const float db = sk * ei + sv + red[i];
-            float dG = bs[i] * ei * sk + red[kC + i];
+            const float ei = GT && row ? GR::E(Kraw, i) : 1.f;
+            const float db = row ? sk * ei + sv + red[i] : 0.f;
+            float dG = row ? bs[i] * ei * sk + red[kC + i] : 0.f;
             const __amdgpu_buffer_rsrc_t br = rsrc(p.dbeta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, db), br, i * p.hv * 4, 0, 0);
             if constexpr (GT) {
@@ -670,7 +708,7 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
         }
         __syncthreads();  // LDS of this value head is rewritten by the next
         if (hv == (hk + 1) * r - 1) {  // uniform: dk of this unit, summed over its value heads
-            stage_store(Vraw, dk_acc, p.dk, tok0, n, p.hq, hk, wave, lr, lg, tid);
+            stage_store<C>(Vraw, dk_acc, p.dk, tok0, n, p.hq, hk, wave, lr, lg, tid);
 #pragma unroll
             for (int c = 0; c < kCW; ++c)
 #pragma unroll
@@ -690,9 +728,10 @@ __global__ __launch_bounds__(kBT) void wy_backward_kernel(Params p)
     }
 }
 
-template <bool GT>
+template <int C, bool GT>
 int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 {
+    constexpr int LDS_TOTAL = BG<C>::LDS_TOTAL, kBT = BG<C>::BT;
     // Per device, once: raise the kernel's dynamic LDS limit and count its resident workgroups
     // (occupancy x CUs), so later launches (also under stream capture) make no attribute calls.
     constexpr int kMaxDevices = 64;
@@ -704,7 +743,7 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
     if (e == hipSuccess && (device < 0 || device >= kMaxDevices)) e = hipErrorInvalidDevice;
     if (e == hipSuccess) {
         std::call_once(once[device], [&] {
-            const void* kern = reinterpret_cast<const void*>(wy_backward_kernel<GT>);
+            const void* kern = reinterpret_cast<const void*>(wy_backward_kernel<C, GT>);
             hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
             int cus = 0, per_cu = 0;
             if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
@@ -737,12 +776,12 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
         int64_t grid = (p.units + 7) / 8 * 8;
         const int64_t cap = static_cast<int64_t>(resident[device]) / 8 * 8;
         if (cap >= 8 && grid > cap) grid = cap;
-        hipLaunchKernelGGL(wy_backward_kernel<GT>, dim3(static_cast<uint32_t>(grid)), dim3(kBT), LDS_TOTAL,
+        hipLaunchKernelGGL((wy_backward_kernel<C, GT>), dim3(static_cast<uint32_t>(grid)), dim3(kBT), LDS_TOTAL,
                            stream, p);
         e = hipGetLastError();
     }
     if (e != hipSuccess) {
-        std::snprintf(msg, msg_len, "%s (wy_backward, gated=%d)", hipGetErrorString(e), GT ? 1 : 0);
+        std::snprintf(msg, msg_len, "%s (wy_backward, C=%d, gated=%d)", hipGetErrorString(e), C, GT ? 1 : 0);
         return static_cast<int>(e);
     }
     return 0;
@@ -755,7 +794,9 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 int launch_bwd(const BwdArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return a.g != nullptr ? bwd::launch_t<true>(a, s, msg, msg_len) : bwd::launch_t<false>(a, s, msg, msg_len);
+    if (a.chunk_size == 32)
+        return a.g != nullptr ? bwd::launch_t<32, true>(a, s, msg, msg_len) : bwd::launch_t<32, false>(a, s, msg, msg_len);
+    return a.g != nullptr ? bwd::launch_t<64, true>(a, s, msg, msg_len) : bwd::launch_t<64, false>(a, s, msg, msg_len);
 }
 
 }  // namespace wyp

@@ -28,18 +28,27 @@ CASES = {
                            gate_mu=0.0, seqlens=[31, 33, 1, 95, 200]),
     "T700_H2_dT": dict(batch=1, seqlen=700, num_qk_heads=2, num_v_heads=2, seed=124, dT=True,
                        beta_sigma=1.5),
+    # C = 32: four waves per workgroup, two workgroups per CU
+    "C32_B2_T333_H4_mu4_dT": dict(C=32, batch=2, seqlen=333, num_qk_heads=4, num_v_heads=4,
+                                  seed=127, gate_mu=4.0, dT=True),
+    "C32_packed_gva_mu0": dict(C=32, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=8, seed=128,
+                               gate_mu=0.0, seqlens=[31, 32, 33, 1, 0, 95, 200]),
+    "C32_T700_H2_ungated_dT": dict(C=32, batch=1, seqlen=700, num_qk_heads=2, num_v_heads=2,
+                                   seed=129, dT=True, beta_sigma=1.5),
 }
 
 
 def make_inputs(spec):
     spec = dict(spec)
     want_dT = spec.pop("dT", False)
-    inp = synth.custom(chunk_size=64, **spec)
+    C = spec.pop("C", 64)
+    inp = synth.custom(chunk_size=C, **spec)
+    inp["C"] = C
     rng = np.random.default_rng(spec["seed"] + 2000)
     B, T, Hv = inp["beta"].shape
     dW = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
     dU = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
-    dT = rng.standard_normal((B, T, Hv, 64)).astype(np.float32) if want_dT else None
+    dT = rng.standard_normal((B, T, Hv, C)).astype(np.float32) if want_dT else None
     return inp, dW, dU, dT
 
 
@@ -48,7 +57,7 @@ def run_bwd(inp, dW, dU, dT, device):
     import chunkwise_gated_deltanet_amd as cg
     k, v, beta, cu = to_device(inp, device)
     bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
-    out = cg.wy_backward(k, v, beta, 64, bf(dW), bf(dU),
+    out = cg.wy_backward(k, v, beta, inp.get("C", 64), bf(dW), bf(dU),
                          dT=None if dT is None else torch.from_numpy(dT).to(device),
                          g=gate_of(inp, device), cu_seqlens=cu)
     torch.cuda.synchronize(device)
@@ -57,8 +66,8 @@ def run_bwd(inp, dW, dU, dT, device):
 
 def check(inp, dW, dU, dT, out, label):
     dk, dv, db, dg = out
-    rk, rv, rb, rg = oracle.wy_backward(inp["k"], inp["v"], inp["beta"], 64, dW, dU, dT=dT,
-                                        g=inp.get("g"), cu_seqlens=inp["cu_seqlens"])
+    rk, rv, rb, rg = oracle.wy_backward(inp["k"], inp["v"], inp["beta"], inp.get("C", 64), dW, dU,
+                                        dT=dT, g=inp.get("g"), cu_seqlens=inp["cu_seqlens"])
     m = {"dk": rel_fro(to_f64(dk), rk), "dv": rel_fro(to_f64(dv), rv),
          "dbeta": rel_fro(to_f64(db), rb)}
     if rg is not None:
@@ -76,29 +85,32 @@ def test_wy_backward_small(name, gpu):
     check(inp, dW, dU, dT, out, name)
 
 
-def test_wy_backward_identical_keys(gpu):
+@pytest.mark.parametrize("C", [32, 64])
+def test_wy_backward_identical_keys(C, gpu):
     """All keys of a chunk equal: the cancellation case that makes a single bf16 rounding of T
     miss the W tolerance in the forward."""
-    inp, dW, dU, dT = make_inputs(dict(batch=1, seqlen=128, num_qk_heads=1, num_v_heads=2,
+    inp, dW, dU, dT = make_inputs(dict(C=C, batch=1, seqlen=128, num_qk_heads=1, num_v_heads=2,
                                        seed=125, dT=True, gate_mu=4.0))
-    inp["k"][0, :64] = inp["k"][0, 0]
-    inp["k"][0, 64:] = inp["k"][0, 64]
-    say("wy_backward identical keys")
+    for c0 in range(0, 128, C):
+        inp["k"][0, c0:c0 + C] = inp["k"][0, c0]
+    say(f"wy_backward identical keys C={C}")
     out = run_bwd(inp, dW, dU, dT, gpu)
     check(inp, dW, dU, dT, out, "identical keys")
 
 
-def test_wy_backward_many_short_sequences(gpu):
-    """1100 packed sequences of 1..65 tokens (a few empty): the work map's search and its empty
+@pytest.mark.parametrize("C", [32, 64])
+def test_wy_backward_many_short_sequences(C, gpu):
+    """1100 packed sequences of 1..C+1 tokens (a few empty): the work map's search and its empty
     slots, on the key-head units of the backward."""
     rng = np.random.default_rng(126)
-    lens = rng.integers(1, 66, size=1100)
+    lens = rng.integers(1, C + 2, size=1100)
     lens[rng.random(1100) < 0.05] = 0
-    inp, dW, dU, dT = make_inputs(dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4, seed=126,
-                                       gate_mu=4.0, dT=True, seqlens=[int(x) for x in lens]))
-    say(f"wy_backward 1100 short sequences, tokens={int(lens.sum())}")
+    inp, dW, dU, dT = make_inputs(dict(C=C, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4,
+                                       seed=126, gate_mu=4.0, dT=True,
+                                       seqlens=[int(x) for x in lens]))
+    say(f"wy_backward 1100 short sequences C={C}, tokens={int(lens.sum())}")
     out = run_bwd(inp, dW, dU, dT, gpu)
-    check(inp, dW, dU, dT, out, "1100 short sequences")
+    check(inp, dW, dU, dT, out, f"1100 short sequences C={C}")
 
 
 def test_wy_backward_deterministic(gpu):
@@ -110,17 +122,18 @@ def test_wy_backward_deterministic(gpu):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("mu", [None, 4.0])
-def test_wy_backward_full_size(mu, gpu):
-    """B=1 T=8192 H=16/16 C=64, whole tensors against the oracle."""
+@pytest.mark.parametrize("mu,C", [(None, 64), (4.0, 64), (None, 32), (4.0, 32)])
+def test_wy_backward_full_size(mu, C, gpu):
+    """B=1 T=8192 H=16/16, whole tensors against the oracle."""
     import torch
-    w = synth.workload(2, chunk_size=64, gate_mu=mu)
+    w = synth.workload(2, chunk_size=C, gate_mu=mu)
     inp = synth.generate(w)
+    inp["C"] = C
     rng = np.random.default_rng(7)
     B, T, Hv = inp["beta"].shape
     dW = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
     dU = synth.f32_to_bf16_bits(rng.standard_normal((B, T, Hv, 128)).astype(np.float32))
-    dT = rng.standard_normal((B, T, Hv, 64)).astype(np.float32)
+    dT = rng.standard_normal((B, T, Hv, C)).astype(np.float32)
     say(f"wy_backward full {w.name} gate_mu={mu}")
     out = run_bwd(inp, dW, dU, dT, gpu)
     check(inp, dW, dU, dT, out, f"full {w.name} mu={mu}")
