@@ -1116,12 +1116,15 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
         // Units in groups: the r = Hv / Hq value heads of one (chunk, key head) in turn on one
         // workgroup.  Measured on MI355X against one unit per workgroup and round: packed 8
         // sequences Hq=16 Hv=64 1132 -> 1073 us, B=4 T=16384 Hq=16 Hv=64 1073 -> 931 us, the same
-        // order as before where r = 1.  At C = 32 two key heads per group, where that still
-        // leaves every workgroup two groups: B=4 T=4096 H=32 108 -> 102 us, B=1 T=32768 H=8
-        // 53.7 -> 51.5 us (at C = 64 and 128 it was 1-3% slower).
+        // order as before where r = 1.  Two key heads per group, where that still leaves every
+        // workgroup two groups, at C = 32 (B=4 T=4096 H=32 108 -> 102 us, B=1 T=32768 H=8
+        // 53.7 -> 51.5 us) and for r >= 4 with W and U (the packed workload 1075 -> 1066 us; T
+        // alone, at up to seven workgroups per CU, went 432 -> 442 us); for r = 1 at C = 64 and
+        // 128 it was 1-3% slower.
         const int r = p.hv / p.hq;
         p.group = r;
-        if (C == 32 && p.hv % (2 * r) == 0 && p.units / (2 * r) >= 2 * cap) p.group = 2 * r;
+        if ((C == 32 || (r >= 4 && (M & kModeWU) != 0)) && p.hv % (2 * r) == 0 && p.units / (2 * r) >= 2 * cap)
+            p.group = 2 * r;
         int64_t grid = (p.units / p.group + 7) / 8 * 8;
         if (cap >= 8 && grid > cap) grid = cap;
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), L::TOTAL,
