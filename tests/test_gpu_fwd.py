@@ -228,6 +228,11 @@ CP_CASES = {
                                         num_v_heads=8, seed=143, h0=True), 3),
     "C128_packed_mu4_seg2": (dict(C=128, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=4,
                                   seed=144, gate_mu=4.0, seqlens=[1300, 1, 0, 256, 257, 90]), 2),
+    # 150 sequences: the owner search over cu_seqlens takes two 64-ary levels
+    "packed_150_mu2_h0_seg2": (dict(batch=1, seqlen=0, num_qk_heads=1, num_v_heads=2, seed=145,
+                                    gate_mu=2.0, h0=True,
+                                    seqlens=[int(x) for x in
+                                             np.random.default_rng(145).integers(0, 300, 150)]), 2),
 }
 
 
