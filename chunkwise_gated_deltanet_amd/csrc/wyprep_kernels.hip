@@ -1112,7 +1112,7 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     int resident = 0;
     if (e == hipSuccess) resident = resident_grid<C, DT, M>(device, &e);
     if (e == hipSuccess) {
-        const int64_t cap = static_cast<int64_t>(resident) / 8 * 8;
+        int64_t cap = static_cast<int64_t>(resident) / 8 * 8;
         // Units in groups: the r = Hv / Hq value heads of one (chunk, key head) in turn on one
         // workgroup.  Measured on MI355X against one unit per workgroup and round: packed 8
         // sequences Hq=16 Hv=64 1132 -> 1073 us, B=4 T=16384 Hq=16 Hv=64 1073 -> 931 us, the same
@@ -1126,6 +1126,13 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
         if ((C == 32 || (r >= 4 && (M & kModeWU) != 0)) && p.hv % (2 * r) == 0 && p.units / (2 * r) >= 2 * cap)
             p.group = 2 * r;
         int64_t grid = (p.units / p.group + 7) / 8 * 8;
+        // bf16 W / U at C = 64 with four or more value heads per key head: three of the four
+        // resident workgroups per CU.  Measured on MI355X against four, one call: packed 8
+        // sequences Hq=16 Hv=64 1061 -> 1041 us, packed 4 sequences of 8k-24k tokens Hq=16 Hv=64
+        // 918 -> 883 us, packed 8 sequences Hq=4 Hv=16 263 -> 246 us, B=4 T=16384 Hq=16 Hv=64
+        // 955 -> 954 us; with one value head per key head it was slower (B=1 T=8192 H=16
+        // 32.2 -> 33.6 us, packed 1024 short sequences 193 -> 220 us).
+        if (C == 64 && DT == 0 && (M & kModeWU) != 0 && r >= 4) cap = cap * 3 / 4 / 8 * 8;
         if (cap >= 8 && grid > cap) grid = cap;
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), L::TOTAL,
                            stream, p);
