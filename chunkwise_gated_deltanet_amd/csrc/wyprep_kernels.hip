@@ -1050,39 +1050,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
     }
 }
 
-// Resident workgroups (occupancy x CUs) for one kernel instance, cached per device.  The first
-// call on a device also raises the instance's dynamic LDS limit where its plan needs more than
-// the default 64 KiB, so later launches (including ones under stream capture) make no
+// Occupancy (resident workgroups per CU) and CU count for one kernel instance, cached per device.
+// The first call on a device also raises the instance's dynamic LDS limit where its plan needs
+// more than the default 64 KiB, so later launches (including ones under stream capture) make no
 // attribute calls.
+struct Residency {
+    int per_cu, cus;
+};
+
 template <int C, int DT, int M>
-int resident_grid(int device, hipError_t* err)
+Residency resident_grid(int device, hipError_t* err)
 {
     constexpr int kMaxDevices = 64;
-    static int cached[kMaxDevices] = {};
+    static Residency cached[kMaxDevices] = {};
     static std::mutex mu;
     if (device < 0 || device >= kMaxDevices) {
         *err = hipErrorInvalidDevice;
-        return 0;
+        return Residency{0, 0};
     }
     std::lock_guard<std::mutex> lock(mu);
-    if (cached[device] == 0) {
+    if (cached[device].cus == 0) {
         using L = Lds<C, DT, (M & kModeWU) != 0>;
         const void* kern = reinterpret_cast<const void*>(wy_prepare_kernel<C, DT, M>);
         if (L::TOTAL > 64 * 1024) {
             *err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-            if (*err != hipSuccess) return 0;
+            if (*err != hipSuccess) return Residency{0, 0};
         }
         int cus = 0, per_cu = 0;
         *err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-        if (*err != hipSuccess) return 0;
+        if (*err != hipSuccess) return Residency{0, 0};
         *err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, L::TOTAL);
-        if (*err != hipSuccess) return 0;
-        // With W and U, more than four resident workgroups per CU only add HBM streams: at C = 32
-        // (seven fit) four were measured faster, e.g. 29.6 vs 34.6 us at B=1 T=8192 H=16, while
-        // T alone gains from all seven.
-        constexpr int kMaxPerCu = (M & (kModeWU | kModeSolve)) != 0 ? 4 : 1 << 10;
-        if (per_cu > kMaxPerCu) per_cu = kMaxPerCu;
-        cached[device] = (per_cu > 0 ? per_cu : 1) * cus;
+        if (*err != hipSuccess) return Residency{0, 0};
+        cached[device] = Residency{per_cu > 0 ? per_cu : 1, cus};
     }
     return cached[device];
 }
@@ -1109,10 +1108,25 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
     auto kern = wy_prepare_kernel<C, DT, M>;
     int device = 0;
     hipError_t e = hipGetDevice(&device);
-    int resident = 0;
-    if (e == hipSuccess) resident = resident_grid<C, DT, M>(device, &e);
+    Residency res{0, 0};
+    if (e == hipSuccess) res = resident_grid<C, DT, M>(device, &e);
     if (e == hipSuccess) {
-        int64_t cap = static_cast<int64_t>(resident) / 8 * 8;
+        const int r = p.hv / p.hq;
+        // Resident workgroups per CU.  With W and U, more than four only add HBM streams: at C =
+        // 32 (seven fit) four were measured faster, e.g. 29.6 vs 34.6 us at B=1 T=8192 H=16, while
+        // T alone gains from all seven.  bf16 W / U with four or more value heads per key head
+        // (groups of two key heads, see below) at C = 64 take three, at C = 32 six.  Measured on
+        // MI355X against four, one call each, bit-identical: at C = 64 packed 8 sequences
+        // Hq=16 Hv=64 1069 -> 1044 us, packed 4 sequences of 8k-24k tokens Hq=16 Hv=64
+        // 899 -> 861 us, packed 8 sequences Hq=4 Hv=16 270 -> 251 us, B=4 T=16384 Hq=16 Hv=64
+        // unchanged; at C = 32 packed 8 sequences Hq=16 Hv=64 942 -> 840 us.  With one value
+        // head per key head both were slower (C = 64: B=1 T=8192 H=16 32.2 -> 33.6 us, 1024
+        // short packed sequences 193 -> 220 us; C = 32 with six: B=4 T=4096 H=32 102 -> 113 us,
+        // B=1 T=32768 H=8 53 -> 56 us), so they keep four.
+        int per_cu = (M & (kModeWU | kModeSolve)) != 0 ? 4 : 1 << 10;
+        if (DT == 0 && (M & kModeWU) != 0 && r >= 4) per_cu = C == 64 ? 3 : (C == 32 ? 6 : per_cu);
+        if (per_cu > res.per_cu) per_cu = res.per_cu;
+        int64_t cap = static_cast<int64_t>(per_cu) * res.cus / 8 * 8;
         // Units in groups: the r = Hv / Hq value heads of one (chunk, key head) in turn on one
         // workgroup.  Measured on MI355X against one unit per workgroup and round: packed 8
         // sequences Hq=16 Hv=64 1132 -> 1073 us, B=4 T=16384 Hq=16 Hv=64 1073 -> 931 us, the same
@@ -1121,18 +1135,10 @@ int launch_t(const LaunchArgs& a, hipStream_t stream, char* msg, int msg_len)
         // 53.7 -> 51.5 us) and for r >= 4 with W and U (the packed workload 1075 -> 1066 us; T
         // alone, at up to seven workgroups per CU, went 432 -> 442 us); for r = 1 at C = 64 and
         // 128 it was 1-3% slower.
-        const int r = p.hv / p.hq;
         p.group = r;
         if ((C == 32 || (r >= 4 && (M & kModeWU) != 0)) && p.hv % (2 * r) == 0 && p.units / (2 * r) >= 2 * cap)
             p.group = 2 * r;
         int64_t grid = (p.units / p.group + 7) / 8 * 8;
-        // bf16 W / U at C = 64 with four or more value heads per key head: three of the four
-        // resident workgroups per CU.  Measured on MI355X against four, one call: packed 8
-        // sequences Hq=16 Hv=64 1061 -> 1041 us, packed 4 sequences of 8k-24k tokens Hq=16 Hv=64
-        // 918 -> 883 us, packed 8 sequences Hq=4 Hv=16 263 -> 246 us, B=4 T=16384 Hq=16 Hv=64
-        // 955 -> 954 us; with one value head per key head it was slower (B=1 T=8192 H=16
-        // 32.2 -> 33.6 us, packed 1024 short sequences 193 -> 220 us).
-        if (C == 64 && DT == 0 && (M & kModeWU) != 0 && r >= 4) cap = cap * 3 / 4 / 8 * 8;
         if (cap >= 8 && grid > cap) grid = cap;
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), L::TOTAL,
                            stream, p);
