@@ -344,11 +344,29 @@ __device__ inline Seg seq_slots(const Params& p, int n)
     return s;
 }
 
+// Unsplit packed batches of 2..64 sequences: the sequence of rank k when they are ordered by length,
+// longest first (ties by index), so the longest sequences' workgroups are dispatched first and
+// the launch does not end on a long sequence that started late.  One wave ranks all lengths; the
+// result is wave-uniform.
+__device__ inline int longest_first(const Params& p, int k, int lane)
+{
+    const int N = p.num_seqs;
+    const int len = lane < N ? p.cu[lane + 1] - p.cu[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < N; ++j) {  // uniform
+        const int lj = __shfl(len, j);
+        rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long b = __ballot(lane < N && rank == k);
+    return b ? uniform(__ffsll(b) - 1) : k;
+}
+
 template <bool ASLOT>
 __device__ inline Seg locate(const Params& p, int slot, int lane)
 {
     Seg s;
     if (!p.split) {
+        if (p.cu != nullptr && p.num_seqs > 1 && p.num_seqs <= 64) slot = longest_first(p, slot, lane);
         s.seq = slot;
         s.seg = 0;
         s.nseg = 1;
