@@ -384,8 +384,10 @@ def chunk_fwd(q, k, w, u, chunk_size=64, g=None, initial_state=None, scale=None,
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            output_final_state=False, cu_seqlens=None, chunk_size=64):
     """The gated DeltaNet chunked forward with the argument list of the FlashQLA usage section:
-    wu_prepare (W, U for every chunk; T stays on chip) followed by chunk_fwd.  g may be None
-    (no gates).  Returns (o, final_state); final_state is None unless output_final_state."""
+    wu_prepare (W, U for every chunk; T stays on chip) followed by chunk_fwd, which splits each
+    sequence into segments run in parallel where sequences x heads would leave CUs idle
+    (auto_segment_chunks; batch rows and packed sequences alike).  g may be None (no gates).
+    Returns (o, final_state); final_state is None unless output_final_state."""
     w, u = wu_prepare(k, v, beta, chunk_size, cu_seqlens=cu_seqlens, g=g)
     # in-GPU sequence parallelism when sequences x heads is small
     return chunk_fwd(q, k, w, u, chunk_size, g=g, initial_state=initial_state, scale=scale,

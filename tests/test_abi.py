@@ -281,3 +281,24 @@ def test_solve_rhs_rejects_before_any_hip_call(lib):
     assert call(good(head_dim_v=64)) == 2
     assert call(good(num_v_heads=3)) == 1
     assert call(good(seqlen=0), k=None, rhs=None, beta=None, X=None) == 0
+
+
+def test_segment_length_choice():
+    """cp_segment_chunks / auto_segment_chunks: no split once the 32-column workgroups of every
+    (sequence, value head) give each of the 256 CUs one; otherwise segments of at least 4 chunks
+    for about 512 such workgroups.  A packed batch counts as num_seqs rows of its mean length,
+    and a choice that would not split comes back as None, so no sequence of a packed batch is
+    cut when the rule says the batch needs no split."""
+    assert cg.cp_segment_chunks(1, 8192, 16) == 16          # 64 items: 8 segments of 16 chunks
+    assert cg.cp_segment_chunks(1, 32768, 8) == 32          # 32 items: 16 segments
+    assert cg.cp_segment_chunks(4, 4096, 32) == 64          # 512 items: no split (all 64 chunks)
+    assert cg.cp_segment_chunks(1, 1024, 2) == 4            # capped at 4 chunks per segment
+    assert cg.auto_segment_chunks(1, 8192, 16) == 16
+    assert cg.auto_segment_chunks(4, 4096, 32) is None
+    assert cg.auto_segment_chunks(1, 100, 16) is None        # two chunks: nothing to split
+    # packed: 2 sequences of 16384 tokens in all are two rows of 8192
+    assert cg.auto_segment_chunks(1, 16384, 16, num_seqs=2) == cg.cp_segment_chunks(2, 8192, 16)
+    # packed, many sequences x heads: no split at all
+    assert cg.auto_segment_chunks(1, 70000, 64, num_seqs=8) is None
+    # the chunk size enters through the chunk count
+    assert cg.auto_segment_chunks(1, 8192, 16, chunk_size=128) == cg.cp_segment_chunks(1, 8192, 16, 128)
