@@ -40,6 +40,17 @@ def test_mid_size_multi_unit(C, gpu):
     check_entry_points(inp, gpu, f"mid C={C}")
 
 
+# Eight value heads per key head with enough units that the W / U instances take groups of two
+# key heads (16 consecutive units per workgroup) and the r >= 4 occupancy (three workgroups per
+# CU at C = 64, six at C = 32): 98304 packed tokens in 6 sequences, Hq=2 / Hv=16, gated.
+@pytest.mark.parametrize("C", [32, 64])
+def test_eight_value_heads_per_key_head(C, gpu):
+    lens = [30000, 1, 20000, 18303, 0, 30000]
+    inp = synth.custom(1, 0, 2, 16, C, seed=70 + C, gate_mu=4.0, seqlens=lens)
+    say(f"Hq=2 Hv=16 packed {len(lens)} seqs, {sum(lens)} tokens, C={C}")
+    check_entry_points(inp, gpu, f"r=8 C={C}")
+
+
 def short_lengths(seed, count, C, zero_frac=0.05):
     """Lengths uniform in [1, C + 1], a few of them 0: most sequences are a single short chunk."""
     rng = np.random.default_rng(seed)
