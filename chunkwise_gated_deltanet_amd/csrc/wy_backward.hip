@@ -52,7 +52,9 @@ struct BG {
     static constexpr int NB = C / 16;
     static constexpr int BT = C == 64 ? 512 : 256;
     static constexpr int BW = BT / 64;
-    static constexpr int CW = kD / 16 / BW;  // dk column tiles per wave in the transposed products
+    static constexpr int YW = BW / 2;        // waves [0, YW): Y and M; waves [YW, BW): products over tokens
+    static constexpr int ZW = BW - YW;
+    static constexpr int CW = kD / 16 / ZW;  // dk column tiles per product wave
     static constexpr int KROW = kD + 8;       // bf16 per staged K / V / dW / dU row
     static constexpr int TRS = C + 4;         // floats per C x C tile row
     static constexpr int KB = C * KROW * 2;
@@ -64,15 +66,16 @@ struct BG {
     static constexpr int OFF_T = OFF_DU + KB;           // A -> T (fp32) -> S = R + R^T (hi / lo)
     static constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, strict lower (fp32)
     static constexpr int OFF_X = OFF_H + TB;            // X -> Y^T -> M (fp32)
-    static constexpr int OFF_TT = OFF_X + TB;           // T^T as hi / lo chunks
-    static constexpr int OFF_B = OFF_TT + TB;           // beta (C floats)
-    static constexpr int OFF_PART = OFF_B + C * 4;      // per-wave row partials: BW waves x 2 x C
-    static constexpr int OFF_RED = OFF_PART + BW * 2 * C * 4;  // dbeta, dG of this value head
+    static constexpr int OFF_M = OFF_X + TB;            // M, with M^T above the diagonal (fp32)
+    static constexpr int OFF_B = OFF_M + TB;            // beta (C floats)
+    static constexpr int OFF_PART = OFF_B + C * 4;      // per-wave row partials: ZW waves x 2 x C
+    static constexpr int OFF_RED = OFF_PART + ZW * 2 * C * 4;  // dbeta, dG of this value head
     static constexpr int OFF_GD = OFF_RED + 2 * C * 4;  // G of the chunk's rows, fp64 (gated)
     static constexpr int OFF_INFO = OFF_GD + C * 8;
     static constexpr int LDS_TOTAL = OFF_INFO + 16;
     static constexpr int CPT = C / 8;                   // elementwise step: columns per thread
     static_assert(BT / C == 8, "eight threads per row in the elementwise step");
+    static_assert(OFF_X == OFF_H + TB && 2 * TB >= KB, "dk is staged as bf16 rows over H and X");
     static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
     using TL = TLayout<C>;
     using GR = GateRow<KROW, 2>;
@@ -168,32 +171,18 @@ __device__ inline u32x4 pack_hilo(f32x4 x)
     return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
-__device__ inline f32x4 unpack_hilo(u32x4 c)
-{
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const bf16x4 h = __builtin_bit_cast(bf16x4, u32x2{c[0], c[1]});
-    const bf16x4 l = __builtin_bit_cast(bf16x4, u32x2{c[2], c[3]});
-    f32x4 x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = static_cast<float>(h[e]) + static_cast<float>(l[e]);
-    return x;
-}
-
-// Transposed products over tokens: acc[c][mi] (+)= sum_kt X^T(ni, kt) B(kt, mi) for the dk
-// column tile ni = wave + 8 c and the four token tiles mi, where X^T fragments come from the
-// staged bf16 rows of `src` by transposed LDS reads and B(kt, mi) is the packed hi / lo chunk of
-// row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed chunks).  KT_GE_MI
-// skips the k tiles kt < mi (B = T^T is zero there).  Accumulator element r of lane 16 g + c is
-// (.)[16 ni + 4 g + r][16 mi + c].
-template <int C, bool KT_GE_MI>
-__device__ inline void tr_products(const unsigned char* src, const float* bp, int wave, int lr, int lg,
+// Transposed products over tokens for the dk column tiles ni = zw + ZW c of product wave zw:
+// acc[c][mi] += sum_kt X^T(ni, kt) B(kt, mi) over the four token tiles mi, where X^T fragments
+// come from the staged bf16 rows of `src` by transposed LDS reads and B(kt, mi) is the packed
+// hi / lo chunk of row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed
+// chunks).  Accumulator element r of lane 16 g + c is (.)[16 ni + 4 g + r][16 mi + c].
+template <int C>
+__device__ inline void tr_products(const unsigned char* src, const float* bp, int zw, int lr, int lg,
                                    f32x4 (&acc)[BG<C>::CW][BG<C>::NB])
 {
     using BGC = BG<C>;
-    constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int kNB = BGC::NB, kZW = BGC::ZW, kCW = BGC::CW;
     constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
-    using TL = typename BGC::TL;
-    using GR = typename BGC::GR;
 
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -203,16 +192,14 @@ __device__ inline void tr_products(const unsigned char* src, const float* bp, in
         u32x4 bch[kNB];
 #pragma unroll
         for (int mi = 0; mi < kNB; ++mi)
-            bch[mi] = (KT_GE_MI && kt < mi) ? u32x4{0u, 0u, 0u, 0u}
-                                            : *reinterpret_cast<const u32x4*>(bp + (16 * mi + lr) * TRS + 16 * kt + 4 * lg);
+            bch[mi] = *reinterpret_cast<const u32x4*>(bp + (16 * mi + lr) * TRS + 16 * kt + 4 * lg);
 #pragma unroll
         for (int c = 0; c < kCW; ++c) {
-            const int ni = wave + kBW * c;
+            const int ni = zw + kZW * c;
             const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
             const i16x4 xf = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
-                if (KT_GE_MI && kt < mi) continue;
                 const u32x4 ch = bch[mi];
                 acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                     xf, __builtin_bit_cast(i16x4, u32x2{ch[0], ch[1]}), acc[c][mi], 0, 0, 0);
@@ -223,18 +210,112 @@ __device__ inline void tr_products(const unsigned char* src, const float* bp, in
     }
 }
 
-// Stages transposed accumulators (element r of lane 16 g + c = X[16 mi + c][16 ni + 4 g + r])
-// as bf16 rows of `dst` and stores rows [0, n) to a [tokens, heads, 128] tensor.
+// T^T X (X = dW or dU) for the dk column tiles of product wave zw: acc[c][mi] element r of
+// lane 16 g + c' is (T^T X)[16 mi + c'][16 ni + 4 g + r].  The B fragments of T^T are read as
+// columns of T (fp32, one 4-byte read per row; 16 consecutive columns of 4 rows 68 floats
+// apart fall in 64 distinct banks) and split into hi / lo bf16.  T[t][i] = 0 for t < i, so k
+// tiles kt < mi are skipped.
 template <int C>
-__device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[BG<C>::CW][BG<C>::NB], __bf16* out,
-                                   int64_t tok0, int n, int heads, int head, int wave, int lr, int lg, int tid)
+__device__ inline void z_products(const unsigned char* src, const float* Ts, int zw, int lr, int lg,
+                                  f32x4 (&acc)[BG<C>::CW][BG<C>::NB])
 {
     using BGC = BG<C>;
-    constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int kNB = BGC::NB, kZW = BGC::ZW, kCW = BGC::CW;
     constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
-    using TL = typename BGC::TL;
-    using GR = typename BGC::GR;
 
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const __bf16* base = reinterpret_cast<const __bf16*>(src);
+#pragma unroll
+    for (int kt = 0; kt < kNB; ++kt) {
+        u32x4 bch[kNB];
+#pragma unroll
+        for (int mi = 0; mi <= kt; ++mi) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = Ts[(16 * kt + 4 * lg + e) * TRS + 16 * mi + lr];
+            bch[mi] = pack_hilo(x);
+        }
+#pragma unroll
+        for (int c = 0; c < kCW; ++c) {
+            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * (zw + kZW * c) + 4 * (lr & 3);
+            const i16x4 xf = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
+#pragma unroll
+            for (int mi = 0; mi <= kt; ++mi) {
+                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    xf, __builtin_bit_cast(i16x4, u32x2{bch[mi][0], bch[mi][1]}), acc[c][mi], 0, 0, 0);
+                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    xf, __builtin_bit_cast(i16x4, u32x2{bch[mi][2], bch[mi][3]}), acc[c][mi], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one k tile's operands in registers at a time
+    }
+}
+
+// Y = X T^T and M = strictLower(-T^T Y) for column tile J of M, rows I0 .. I1, on one wave
+// with no barrier: the Y tiles (Mt, J), Mt >= I0, stay in registers, where an accumulator's
+// element q of lane 16 g + c (row 4 g + q, column c) is exactly the B operand of step q of
+// the product T^T Y.  T^T's A fragments are read as columns of T in fp32.  M goes to Ms below
+// the diagonal and transposed above it (Ms[j][i] = M[i][j] for i > j, 0 on the diagonal).
+template <int C, int J, int I0, int I1>
+__device__ inline void ym_column(const float* Xs, const float* Ts, float* Ms, int lr, int lg)
+{
+    constexpr int NB = C / 16, TRS = BG<C>::TRS;
+    f32x4 y[NB];
+#pragma unroll
+    for (int Mt = I0; Mt < NB; ++Mt) y[Mt] = zero4();
+#pragma unroll
+    for (int L = 0; L <= J; ++L) {  // Y(Mt, J) = sum_{L <= J} X(Mt, L) T(J, L)^T
+        const f32x4 b = *reinterpret_cast<const f32x4*>(Ts + (16 * J + lr) * TRS + 16 * L + 4 * lg);
+#pragma unroll
+        for (int Mt = I0; Mt < NB; ++Mt) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + (16 * Mt + lr) * TRS + 16 * L + 4 * lg);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) y[Mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], y[Mt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one k step's operands in registers at a time
+    }
+    f32x4 m[NB];
+#pragma unroll
+    for (int I = I0; I <= I1; ++I) m[I] = zero4();
+#pragma unroll
+    for (int Mt = I0; Mt < NB; ++Mt) {  // M(I, J) = -sum_{Mt >= I} T(Mt, I)^T Y(Mt, J)
+#pragma unroll
+        for (int I = I0; I <= I1 && I <= Mt; ++I) {
+            f32x4 a;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] = Ts[(16 * Mt + 4 * lg + q) * TRS + 16 * I + lr];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], y[Mt][q], m[I], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int I = I0; I <= I1; ++I) {
+        // element r of lane 16 g + c is M[16 I + 4 g + r][16 J + c] (negated)
+        if (I > J) {  // constant after unrolling
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) Ms[(16 * I + 4 * lg + rr) * TRS + 16 * J + lr] = -m[I][rr];
+            *reinterpret_cast<f32x4*>(Ms + (16 * J + lr) * TRS + 16 * I + 4 * lg) = -m[I];
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
+                if (i >= j) Ms[i * TRS + j] = i > j ? -m[I][rr] : 0.f;
+                if (i > j) Ms[j * TRS + i] = -m[I][rr];
+            }
+        }
+    }
+}
+
+// Accumulators of product wave zw (element r of lane 16 g + c = X[16 mi + c][16 ni + 4 g + r])
+// as bf16 into its own columns of the staged rows at `dst` (rows of KROW elements).
+template <int C>
+__device__ inline void stage_rows(unsigned char* dst, const f32x4 (&acc)[BG<C>::CW][BG<C>::NB], int zw, int lr,
+                                  int lg)
+{
+    using BGC = BG<C>;
+    constexpr int kNB = BGC::NB, kZW = BGC::ZW, kCW = BGC::CW, KROW = BGC::KROW;
     __bf16* d = reinterpret_cast<__bf16*>(dst);
 #pragma unroll
     for (int c = 0; c < kCW; ++c)
@@ -243,15 +324,22 @@ __device__ inline void stage_store(unsigned char* dst, const f32x4 (&acc)[BG<C>:
             bf16x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[c][mi][r]);
-            *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (wave + kBW * c) + 4 * lg) = o;
+            *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * (zw + kZW * c) + 4 * lg) = o;
         }
-    __syncthreads();
+}
+
+// Staged rows [0, n) at `src` to a [tokens, heads, 128] tensor, by every thread.
+template <int C>
+__device__ inline void store_rows(const unsigned char* src, __bf16* out, int64_t tok0, int n, int heads, int head,
+                                  int tid)
+{
+    constexpr int KROW = BG<C>::KROW, kBT = BG<C>::BT;
     const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
     const __amdgpu_buffer_rsrc_t r = rsrc(out + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
 #pragma unroll
     for (int it = 0; it < Rows<C>::NIT; ++it) {
         const int q = tid + it * kBT;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(dst + (q >> 4) * (KROW * 2) + (q & 15) * 16);
+        const u32x4 val = *reinterpret_cast<const u32x4*>(src + (q >> 4) * (KROW * 2) + (q & 15) * 16);
         __builtin_amdgcn_raw_buffer_store_b128(val, r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
     }
 }
@@ -311,10 +399,11 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
 }
 
 template <int C, bool GT>
-__global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
+__global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
 {
     using BGC = BG<C>;
     constexpr int kC = C, kNB = BGC::NB, kBT = BGC::BT, kBW = BGC::BW, kCW = BGC::CW;
+    constexpr int kYW = BGC::YW, kZW = BGC::ZW;
     constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
     using TL = typename BGC::TL;
     using GR = typename BGC::GR;
@@ -326,7 +415,7 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
     float* Ts = reinterpret_cast<float*>(smem + BGC::OFF_T);
     float* Hs = reinterpret_cast<float*>(smem + BGC::OFF_H);
     float* Xs = reinterpret_cast<float*>(smem + BGC::OFF_X);
-    float* TT = reinterpret_cast<float*>(smem + BGC::OFF_TT);
+    float* Ms = reinterpret_cast<float*>(smem + BGC::OFF_M);
     float* bs = reinterpret_cast<float*>(smem + BGC::OFF_B);
     float* part = reinterpret_cast<float*>(smem + BGC::OFF_PART);
     float* red = reinterpret_cast<float*>(smem + BGC::OFF_RED);
@@ -365,6 +454,13 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
         for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
 
     auto job = [&]() -> bool {
+        // The lane indices are made opaque once per job, so the many per-lane LDS addresses
+        // derived from them are formed where they are used instead of being hoisted out of the
+        // persistent loop and held in registers across the whole job.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = uniform(tid >> 6);
+        const int lr = lane & 15, lg = lane >> 4;
         const int hk = u.hv;
         const int64_t tok0 = u.tok0;
         const int n = u.n;
@@ -460,115 +556,98 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
                     x_tiles(std::true_type{});
                 else
                     x_tiles(std::false_type{});
-                for (int t = wave - 1; t < kNB * (kNB - 1) / 2; t += kBW - 1) {
-                    int Iu = 0, rem = t;
-                    while (rem >= kNB - 1 - Iu) {
-                        rem -= kNB - 1 - Iu;
-                        ++Iu;
-                    }
-                    const int Ju = Iu + 1 + rem;
-                    *reinterpret_cast<f32x4*>(Xs + (16 * Iu + lr) * TRS + 16 * Ju + 4 * lg) = zero4();
-                }
             }
         }
         __syncthreads();
         coupling_level<kC, 16, TL>(Ts, tid);
         if constexpr (kC >= 64) coupling_level<kC, 32, TL>(Ts, tid);
+        const bool last_head = hv == (hk + 1) * r - 1;  // uniform
 
-        // ---- T^T as hi / lo chunks: chunk (i, c4) holds T[4 c4 + e][i], e = 0..3
-#pragma unroll
-        for (int it = 0; it < kC * (kC / 4) / kBT; ++it) {
-            const int q = tid + it * kBT;
-            const int i = q / (kC / 4), c4 = q % (kC / 4);
-            f32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = Ts[(4 * c4 + e) * TRS + i];
-            *reinterpret_cast<u32x4*>(TT + i * TRS + 4 * c4) = pack_hilo(x);
-        }
-        __syncthreads();
-
-        // ---- Y = X T^T on the lower tiles (fp32 MFMA): Y(M, J) = sum_{L <= J} X(M, L) T(J, L)^T;
-        // stored transposed over X
-        {
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            constexpr int NT = (NTILE + kBW - 1) / kBW;
-            f32x4 y[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                y[tt] = zero4();
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int Mt = 0, J = 0;
-                tile_of(t, &Mt, &J);
-                for (int L = 0; L <= J; ++L) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + (16 * Mt + lr) * TRS + 16 * L + 4 * lg);
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(Ts + (16 * J + lr) * TRS + 16 * L + 4 * lg);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) y[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], y[tt], 0, 0, 0);
-                }
-            }
-            __syncthreads();  // every read of X done
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int Mt = 0, J = 0;
-                tile_of(t, &Mt, &J);
-                // element r of lane 16 g + c is Y[16 Mt + 4 g + r][16 J + c] -> Y^T row 16 J + c
-                *reinterpret_cast<f32x4*>(Xs + (16 * J + lr) * TRS + 16 * Mt + 4 * lg) = y[tt];
-            }
-        }
-        __syncthreads();
-
-        // ---- M = strictLower(-T^T Y): M(I, J) = -sum_{Mt >= I} T^T(I, Mt) Y(Mt, J); T^T rows from
-        // the hi / lo chunks (hi + lo), Y from Y^T rows
-        {
-            constexpr int NTILE = kNB * (kNB + 1) / 2;
-            constexpr int NT = (NTILE + kBW - 1) / kBW;
-            f32x4 m[NT];
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                m[tt] = zero4();
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-                for (int Mt = I; Mt < kNB; ++Mt) {
-                    const f32x4 a = unpack_hilo(*reinterpret_cast<const u32x4*>(TT + (16 * I + lr) * TRS + 16 * Mt + 4 * lg));
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(Xs + (16 * J + lr) * TRS + 16 * Mt + 4 * lg);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) m[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], m[tt], 0, 0, 0);
-                }
-            }
-            __syncthreads();  // every read of Y^T done
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const int t = wave + kBW * tt;
-                if (t >= NTILE) break;
-                int I = 0, J = 0;
-                tile_of(t, &I, &J);
-                // M below the diagonal and M^T above it (Xs[j][i] = M[i][j] for i > j; 0 on the
-                // diagonal), so that row i of Xs lists M_ij for j < i and M_ji for j > i
-                if (I > J) {  // uniform
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) Xs[(16 * I + 4 * lg + rr) * TRS + 16 * J + lr] = -m[tt][rr];
-                    *reinterpret_cast<f32x4*>(Xs + (16 * J + lr) * TRS + 16 * I + 4 * lg) = -m[tt];
+        // ---- Two independent products at once.  Waves [0, YW): Y = X T^T and M = strictLower(-T^T
+        // Y), by column tiles of M (into Ms).  Waves [YW, BW): T^T dW and T^T dU with their
+        // consumers: dK += D E T^T dW, dV = D T^T dU (staged over dU in the wave's own columns),
+        // and the per-row sums for dbeta and dG.
+        if (wave < kYW) {  // uniform
+            if constexpr (kC == 64) {
+                if (wave == 0) {
+                    ym_column<64, 0, 0, 1>(Xs, Ts, Ms, lr, lg);
+                } else if (wave == 1) {
+                    ym_column<64, 1, 1, 3>(Xs, Ts, Ms, lr, lg);
+                } else if (wave == 2) {
+                    ym_column<64, 2, 2, 3>(Xs, Ts, Ms, lr, lg);
                 } else {
+                    ym_column<64, 0, 2, 3>(Xs, Ts, Ms, lr, lg);
+                    ym_column<64, 3, 3, 3>(Xs, Ts, Ms, lr, lg);
+                }
+            } else {
+                if (wave == 0)
+                    ym_column<32, 0, 0, 1>(Xs, Ts, Ms, lr, lg);
+                else
+                    ym_column<32, 1, 1, 1>(Xs, Ts, Ms, lr, lg);
+            }
+        } else {
+            const int zw = wave - kYW;
+            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+            const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
+            f32x4 acc[kCW][kNB];
+#pragma unroll
+            for (int c = 0; c < kCW; ++c)
+#pragma unroll
+                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
+            z_products<C>(dWraw, Ts, zw, lr, lg, acc);
+            // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
+#pragma unroll
+            for (int mi = 0; mi < kNB; ++mi) {
+                const int i = 16 * mi + lr;
+                const float bi = bs[i];
+                const float ei = GT ? GR::E(Kraw, i) : 1.f;
+                float sk = 0.f;
+#pragma unroll
+                for (int c = 0; c < kCW; ++c) {
+                    const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * (zw + kZW * c) + 4 * lg);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
-                        if (i >= j) Xs[i * TRS + j] = i > j ? -m[tt][rr] : 0.f;
-                        if (i > j) Xs[j * TRS + i] = -m[tt][rr];
+                        sk += acc[c][mi][rr] * static_cast<float>(kv[rr]);
+                        dk_acc[c][mi][rr] += bi * ei * acc[c][mi][rr];
                     }
                 }
+                sk += __shfl_xor(sk, 16);
+                sk += __shfl_xor(sk, 32);
+                if (lg == 0) part[(zw * 2 + 0) * kC + i] = sk;
             }
+#pragma unroll
+            for (int c = 0; c < kCW; ++c)
+#pragma unroll
+                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
+            z_products<C>(dUraw, Ts, zw, lr, lg, acc);
+#pragma unroll
+            for (int mi = 0; mi < kNB; ++mi) {
+                const int i = 16 * mi + lr;
+                const float bi = bs[i];
+                float sv = 0.f;
+#pragma unroll
+                for (int c = 0; c < kCW; ++c) {
+                    const bf16x4 vv = *reinterpret_cast<const bf16x4*>(Vb + i * KROW + 16 * (zw + kZW * c) + 4 * lg);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        sv += acc[c][mi][rr] * static_cast<float>(vv[rr]);
+                        acc[c][mi][rr] *= bi;  // dV
+                    }
+                }
+                sv += __shfl_xor(sv, 16);
+                sv += __shfl_xor(sv, 32);
+                if (lg == 0) part[(zw * 2 + 1) * kC + i] = sv;
+            }
+            // this wave alone reads and writes its columns of dU
+            stage_rows<C>(dUraw, acc, zw, lr, lg);
         }
         __syncthreads();
 
-        // ---- elementwise: S = R + R^T (R = D (Gamma o M)) as hi / lo chunks over Ts;
-        // row sums sum_j M_ij H_ij and sum_j Z_ij, column sums sum_i Z_ij (Z = M o D H; H
-        // already carries Gamma).  Row i of Xs and Hs holds M_ij, H_ij for j < i and M_ji, H_ji
-        // for j > i, so every read is a 16-byte row chunk.
+        // ---- dV out; then elementwise: S = R + R^T (R = D (Gamma o M)) as hi / lo chunks over Ts
+        // (T is no longer read); row sums sum_j M_ij H_ij and sum_j Z_ij, column sums sum_i Z_ij
+        // (Z = M o D H; H already carries Gamma).  Row i of Ms and Hs holds M_ij, H_ij for j < i
+        // and M_ji, H_ji for j > i, so every read is a 16-byte row chunk.
+        store_rows<C>(dUraw, p.dv, tok0, n, p.hv, hv, tid);
         {
             constexpr int CPT = BGC::CPT;
             const int i = tid >> 3, seg = tid & 7;  // row i, columns CPT seg .. CPT seg + CPT - 1
@@ -579,8 +658,8 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
 #pragma unroll
             for (int c4 = 0; c4 < CPT / 4; ++c4) {
                 const int j0 = CPT * seg + 4 * c4;
-                const f32x4 mv = *reinterpret_cast<const f32x4*>(Xs + i * TRS + j0);
-                const f32x4 hv = *reinterpret_cast<const f32x4*>(Hs + i * TRS + j0);
+                const f32x4 mv = *reinterpret_cast<const f32x4*>(Ms + i * TRS + j0);
+                const f32x4 hv4 = *reinterpret_cast<const f32x4*>(Hs + i * TRS + j0);
                 const f32x4 bj = *reinterpret_cast<const f32x4*>(bs + j0);
                 f32x4 sv;
 #pragma unroll
@@ -592,7 +671,7 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
                         const double d = Gd[j] - gi;
                         gam = __expf(static_cast<float>(below ? -d : d));
                     }
-                    const float m = mv[e], h = hv[e];
+                    const float m = mv[e], h = hv4[e];
                     // R_ij (j < i) and R_ji (j > i); Z_ij = M_ij beta_i Gamma_ij (k_i . k_j), and
                     // this thread's column sum runs over column i: Z_ji for rows j > i
                     sv[e] = below ? m * bi * gam : (above ? m * bj[e] * gam : 0.f);
@@ -610,82 +689,33 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
                 colZ += __shfl_xor(colZ, d);
             }
             if (seg == 0) {
-                red[i] = rowMH;            // dbeta part
+                red[i] = rowMH;             // dbeta part
                 red[kC + i] = rowZ - colZ;  // dG part
             }
         }
         __syncthreads();
 
-        // ---- T^T dW and T^T dU (bf16 MFMA, T^T hi / lo): dK += D E T^T dW, dV = D T^T dU, and
-        // the per-row sums for dbeta and dG
-        {
-            f32x4 acc[kCW][kNB];
+        // ---- product waves: (R + R^T) K into dK (bf16 MFMA, S hi / lo; S is symmetric, so its row
+        // chunks are also the column chunks the product needs), and after a unit's last value
+        // head dk staged over H and X.  Wave 0: dbeta, dG, dg of this value head (lanes past the
+        // chunk's C rows hold 0; their stores fall outside the n-row buffer range).
+        if (wave >= kYW) {  // uniform
+            const int zw = wave - kYW;
+            tr_products<C>(Kraw, Ts, zw, lr, lg, dk_acc);
+            if (last_head) {  // uniform
+                stage_rows<C>(smem + BGC::OFF_H, dk_acc, zw, lr, lg);
 #pragma unroll
-            for (int c = 0; c < kCW; ++c)
+                for (int c = 0; c < kCW; ++c)
 #pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            tr_products<C, true>(dWraw, TT, wave, lr, lg, acc);
-            // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
-            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
-            const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
-#pragma unroll
-            for (int mi = 0; mi < kNB; ++mi) {
-                const int i = 16 * mi + lr;
-                const float bi = bs[i];
-                const float ei = GT ? GR::E(Kraw, i) : 1.f;
-                float sk = 0.f;
-#pragma unroll
-                for (int c = 0; c < kCW; ++c) {
-                    const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * (wave + kBW * c) + 4 * lg);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        sk += acc[c][mi][rr] * static_cast<float>(kv[rr]);
-                        dk_acc[c][mi][rr] += bi * ei * acc[c][mi][rr];
-                    }
-                }
-                sk += __shfl_xor(sk, 16);
-                sk += __shfl_xor(sk, 32);
-                if (lg == 0) part[(wave * 2 + 0) * kC + i] = sk;
+                    for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
             }
-#pragma unroll
-            for (int c = 0; c < kCW; ++c)
-#pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            tr_products<C, true>(dUraw, TT, wave, lr, lg, acc);
-#pragma unroll
-            for (int mi = 0; mi < kNB; ++mi) {
-                const int i = 16 * mi + lr;
-                const float bi = bs[i];
-                float sv = 0.f;
-#pragma unroll
-                for (int c = 0; c < kCW; ++c) {
-                    const bf16x4 vv = *reinterpret_cast<const bf16x4*>(Vb + i * KROW + 16 * (wave + kBW * c) + 4 * lg);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        sv += acc[c][mi][rr] * static_cast<float>(vv[rr]);
-                        acc[c][mi][rr] *= bi;  // dV
-                    }
-                }
-                sv += __shfl_xor(sv, 16);
-                sv += __shfl_xor(sv, 32);
-                if (lg == 0) part[(wave * 2 + 1) * kC + i] = sv;
-            }
-            __syncthreads();  // every read of dU (and V) done: dV is staged over dU
-            stage_store<C>(dUraw, acc, p.dv, tok0, n, p.hv, hv, wave, lr, lg, tid);
-        }
-        // ---- (R + R^T) K into dK (bf16 MFMA, S hi / lo; S symmetric, so its row chunks are
-        // also the column chunks the product needs)
-        tr_products<C, false>(Kraw, Ts, wave, lr, lg, dk_acc);
-
-        // ---- dbeta, dG, dg of this value head (lanes past the chunk's C rows hold 0; their stores
-        // fall outside the n-row buffer range)
-        if (tid < 64) {
+        } else if (wave == 0) {
             const int i = tid;
             const bool row = i < kC;
             float sk = 0.f, sv = 0.f;
             if (row) {
 #pragma unroll
-                for (int w = 0; w < kBW; ++w) {
+                for (int w = 0; w < kZW; ++w) {
                     sk += part[(w * 2 + 0) * kC + i];
                     sv += part[(w * 2 + 1) * kC + i];
                 }
@@ -706,15 +736,11 @@ __global__ __launch_bounds__(BG<C>::BT) void wy_backward_kernel(Params p)
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, dG), gr, i * p.hv * 4, 0, 0);
             }
         }
-        __syncthreads();  // LDS of this value head is rewritten by the next
-        if (hv == (hk + 1) * r - 1) {  // uniform: dk of this unit, summed over its value heads
-            stage_store<C>(Vraw, dk_acc, p.dk, tok0, n, p.hq, hk, wave, lr, lg, tid);
-#pragma unroll
-            for (int c = 0; c < kCW; ++c)
-#pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) dk_acc[c][mi] = zero4();
-            __syncthreads();  // the staging rows (V) are rewritten by the next commit
-        }
+        // Every read of this value head's K, V, dW, dU, beta and partial sums is done past this
+        // barrier, so the next commit may overwrite them; the staged dk (over H and X) is
+        // rewritten only after the next job's first barrier.
+        __syncthreads();
+        if (last_head) store_rows<C>(smem + BGC::OFF_H, p.dk, tok0, n, p.hq, hk, tid);  // uniform
         u = nu;
         hv = nhv;
         new_unit = nnew;
