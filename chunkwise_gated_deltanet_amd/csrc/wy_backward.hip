@@ -41,12 +41,10 @@ namespace {
 
 namespace bwd {
 
-// Workgroup shape and LDS plan per chunk size.  Eight waves at C = 64: LDS (141 KB) holds one
-// workgroup per CU, and with one wave per SIMD every LDS, MFMA and VALU latency of the unit's long
-// serial chain would be exposed; phases that tile over waves run twice as wide, while the
-// forward's Gram / substitution / coupling steps keep their four-wave mapping.  Four waves at
-// C = 32 (54 KB, two workgroups per CU).  Either way eight threads share a row in the
-// elementwise step.
+// Workgroup shape and LDS plan per chunk size.  Eight waves at C = 64 (157 KB of LDS, one
+// workgroup per CU), four at C = 32 (58 KB, two per CU).  The forward's Gram / substitution /
+// coupling steps keep their own wave mapping; after them the waves split in two halves that
+// run the two independent products of the reverse step side by side.
 template <int C>
 struct BG {
     static constexpr int NB = C / 16;
@@ -63,19 +61,19 @@ struct BG {
     static constexpr int OFF_V = OFF_K + KB;
     static constexpr int OFF_DW = OFF_V + KB;
     static constexpr int OFF_DU = OFF_DW + KB;
-    static constexpr int OFF_T = OFF_DU + KB;           // A -> T (fp32) -> S = R + R^T (hi / lo)
-    static constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, strict lower (fp32)
-    static constexpr int OFF_X = OFF_H + TB;            // X -> Y^T -> M (fp32)
-    static constexpr int OFF_M = OFF_X + TB;            // M, with M^T above the diagonal (fp32)
-    static constexpr int OFF_B = OFF_M + TB;            // beta (C floats)
-    static constexpr int OFF_PART = OFF_B + C * 4;      // per-wave row partials: ZW waves x 2 x C
-    static constexpr int OFF_RED = OFF_PART + ZW * 2 * C * 4;  // dbeta, dG of this value head
-    static constexpr int OFF_GD = OFF_RED + 2 * C * 4;  // G of the chunk's rows, fp64 (gated)
+    static constexpr int OFF_T = OFF_DU + KB;           // A -> T (fp32)
+    static constexpr int OFF_H = OFF_T + TB;            // H = Gamma o K K^T, with H^T above the diagonal (fp32)
+    static constexpr int OFF_X = OFF_H + TB;            // X, lower tiles (fp32)
+    static constexpr int OFF_S = OFF_X + TB;            // S = R + R^T as hi / lo chunks
+    static constexpr int OFF_B = OFF_S + TB;            // beta (C floats)
+    static constexpr int PSTR = C + 16 > 80 ? C + 16 : 80;  // row-partial slot stride (floats; 16 lg + lr banks)
+    static constexpr int OFF_PART = OFF_B + C * 4;      // row partials: 2 sums x ZW waves x 4 lane groups
+    static constexpr int OFF_PY = OFF_PART + 2 * ZW * 4 * PSTR * 4;  // row / column sums: 2 x YW waves x 4 lane groups
+    static constexpr int OFF_GD = OFF_PY + 2 * YW * 4 * PSTR * 4;  // G of the chunk's rows, fp64 (gated)
     static constexpr int OFF_INFO = OFF_GD + C * 8;
     static constexpr int LDS_TOTAL = OFF_INFO + 16;
-    static constexpr int CPT = C / 8;                   // elementwise step: columns per thread
-    static_assert(BT / C == 8, "eight threads per row in the elementwise step");
     static_assert(OFF_X == OFF_H + TB && 2 * TB >= KB, "dk is staged as bf16 rows over H and X");
+    static_assert(4 * PSTR >= 16 * 20, "a Y / M wave's row-sum slots hold its 16 x 20 transpose tile");
     static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
     using TL = TLayout<C>;
     using GR = GateRow<KROW, 2>;
@@ -158,24 +156,53 @@ struct JobIn {
     }
 };
 
-__device__ inline u32x4 pack_hilo(f32x4 x)
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest even, two
+// values per conversion: hi / lo of x[2p], x[2p + 1] land in 32-bit word p of `hi` / `lo`.
+template <int N>
+__device__ inline void split_hilo(const float (&x)[N], unsigned (&hi)[N / 2], unsigned (&lo)[N / 2])
 {
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    bf16x4 h, l;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        h[e] = static_cast<__bf16>(x[e]);
-        l[e] = static_cast<__bf16>(x[e] - static_cast<float>(h[e]));
+    for (int p = 0; p < N / 2; ++p) {
+        const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[2 * p], x[2 * p + 1]}, bf16x2));
+        const float h0 = __builtin_bit_cast(float, h << 16), h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+        hi[p] = h;
+        lo[p] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x[2 * p] - h0, x[2 * p + 1] - h1}, bf16x2));
     }
-    const u32x2 hp = __builtin_bit_cast(u32x2, h), lp = __builtin_bit_cast(u32x2, l);
-    return u32x4{hp[0], hp[1], lp[0], lp[1]};
 }
 
-// Transposed products over tokens for the dk column tiles ni = zw + ZW c of product wave zw:
-// acc[c][mi] += sum_kt X^T(ni, kt) B(kt, mi) over the four token tiles mi, where X^T fragments
-// come from the staged bf16 rows of `src` by transposed LDS reads and B(kt, mi) is the packed
-// hi / lo chunk of row 16 mi + lr, columns 16 kt + 4 lg of `bp` (a C x C tile of packed
-// chunks).  Accumulator element r of lane 16 g + c is (.)[16 ni + 4 g + r][16 mi + c].
+// Four values as one 16-byte chunk: hi of x[0..3], then lo of x[0..3].
+__device__ inline u32x4 pack_hilo(f32x4 x)
+{
+    const float v[4] = {x[0], x[1], x[2], x[3]};
+    unsigned h[2], l[2];
+    split_hilo<4>(v, h, l);
+    return u32x4{h[0], h[1], l[0], l[1]};
+}
+
+// A fragment of the transposed product over 32 tokens: lane 16 g + c gets column 16 ni + c of
+// rows t0 + 8 g .. t0 + 8 g + 7 of the staged bf16 rows (two transposed 4 x 16 LDS reads).
+template <int KROW>
+__device__ inline bf16x8 tr_frag(const __bf16* base, int t0, int ni, int lr, int lg)
+{
+    const __bf16* p0 = base + (t0 + 8 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * KROW));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline bf16x8 cat_u32(unsigned a, unsigned b, unsigned c, unsigned d)
+{
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8, u32x4v{a, b, c, d});
+}
+
+// (R + R^T) K for the dk column tiles ni = zw + ZW c of product wave zw, over 32 tokens per
+// bf16 MFMA: acc[c][mi] += sum_t K(t, ni)^T S(t, mi), where the K fragments come from transposed
+// LDS reads and S(t, i) is read from the packed hi / lo chunks of row i of `bp` (S is
+// symmetric, so its rows are also its columns).  Accumulator element r of lane 16 g + c is
+// (.)[16 ni + 4 g + r][16 mi + c].
 template <int C>
 __device__ inline void tr_products(const unsigned char* src, const float* bp, int zw, int lr, int lg,
                                    f32x4 (&acc)[BG<C>::CW][BG<C>::NB])
@@ -183,82 +210,91 @@ __device__ inline void tr_products(const unsigned char* src, const float* bp, in
     using BGC = BG<C>;
     constexpr int kNB = BGC::NB, kZW = BGC::ZW, kCW = BGC::CW;
     constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
-
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const __bf16* base = reinterpret_cast<const __bf16*>(src);
 #pragma unroll
-    for (int kt = 0; kt < kNB; ++kt) {
-        u32x4 bch[kNB];
+    for (int ks = 0; ks < C / 32; ++ks) {
+        bf16x8 bh[kNB], bl[kNB];
 #pragma unroll
-        for (int mi = 0; mi < kNB; ++mi)
-            bch[mi] = *reinterpret_cast<const u32x4*>(bp + (16 * mi + lr) * TRS + 16 * kt + 4 * lg);
+        for (int mi = 0; mi < kNB; ++mi) {
+            const float* row = bp + (16 * mi + lr) * TRS + 32 * ks + 8 * lg;
+            const u32x4 c0 = *reinterpret_cast<const u32x4*>(row);
+            const u32x4 c1 = *reinterpret_cast<const u32x4*>(row + 4);
+            bh[mi] = cat_u32(c0[0], c0[1], c1[0], c1[1]);
+            bl[mi] = cat_u32(c0[2], c0[3], c1[2], c1[3]);
+        }
 #pragma unroll
         for (int c = 0; c < kCW; ++c) {
-            const int ni = zw + kZW * c;
-            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * ni + 4 * (lr & 3);
-            const i16x4 xf = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
+            const bf16x8 xa = tr_frag<KROW>(base, 32 * ks, zw + kZW * c, lr, lg);
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
-                const u32x4 ch = bch[mi];
-                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    xf, __builtin_bit_cast(i16x4, u32x2{ch[0], ch[1]}), acc[c][mi], 0, 0, 0);
-                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    xf, __builtin_bit_cast(i16x4, u32x2{ch[2], ch[3]}), acc[c][mi], 0, 0, 0);
+                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh[mi], acc[c][mi], 0, 0, 0);
+                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl[mi], acc[c][mi], 0, 0, 0);
             }
         }
     }
 }
 
-// T^T X (X = dW or dU) for the dk column tiles of product wave zw: acc[c][mi] element r of
-// lane 16 g + c' is (T^T X)[16 mi + c'][16 ni + 4 g + r].  The B fragments of T^T are read as
-// columns of T (fp32, one 4-byte read per row; 16 consecutive columns of 4 rows 68 floats
-// apart fall in 64 distinct banks) and split into hi / lo bf16.  T[t][i] = 0 for t < i, so k
-// tiles kt < mi are skipped.
+// T^T dW and T^T dU for the dk column tiles of product wave zw, over 32 tokens per bf16 MFMA:
+// aw[c][mi] (au) element r of lane 16 g + c' is (T^T dW)[16 mi + c'][16 ni + 4 g + r].  The B
+// fragments of T^T are read as columns of T (fp32, one 4-byte read per row) and split into
+// hi / lo bf16 once for both products.  T[t][i] = 0 for t < i, so token steps entirely above
+// tile mi are skipped.
 template <int C>
-__device__ inline void z_products(const unsigned char* src, const float* Ts, int zw, int lr, int lg,
-                                  f32x4 (&acc)[BG<C>::CW][BG<C>::NB])
+__device__ inline void z_products(const unsigned char* dWraw, const unsigned char* dUraw, const float* Ts, int zw,
+                                  int lr, int lg, f32x4 (&aw)[BG<C>::CW][BG<C>::NB],
+                                  f32x4 (&au)[BG<C>::CW][BG<C>::NB])
 {
     using BGC = BG<C>;
     constexpr int kNB = BGC::NB, kZW = BGC::ZW, kCW = BGC::CW;
     constexpr int KROW = BGC::KROW, TRS = BGC::TRS;
-
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const __bf16* base = reinterpret_cast<const __bf16*>(src);
+    const __bf16* dWb = reinterpret_cast<const __bf16*>(dWraw);
+    const __bf16* dUb = reinterpret_cast<const __bf16*>(dUraw);
 #pragma unroll
-    for (int kt = 0; kt < kNB; ++kt) {
-        u32x4 bch[kNB];
+    for (int ks = 0; ks < C / 32; ++ks) {
+        bf16x8 bh[kNB], bl[kNB];
 #pragma unroll
-        for (int mi = 0; mi <= kt; ++mi) {
-            f32x4 x;
+        for (int mi = 0; mi < kNB; ++mi) {
+            if (16 * mi > 32 * ks + 31) continue;  // constant after unrolling
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = Ts[(16 * kt + 4 * lg + e) * TRS + 16 * mi + lr];
-            bch[mi] = pack_hilo(x);
+            for (int j = 0; j < 8; ++j) x[j] = Ts[(32 * ks + 8 * lg + j) * TRS + 16 * mi + lr];
+            unsigned h[4], l[4];
+            split_hilo<8>(x, h, l);
+            bh[mi] = cat_u32(h[0], h[1], h[2], h[3]);
+            bl[mi] = cat_u32(l[0], l[1], l[2], l[3]);
         }
 #pragma unroll
         for (int c = 0; c < kCW; ++c) {
-            const __bf16* p0 = base + (16 * kt + 4 * lg + (lr >> 2)) * KROW + 16 * (zw + kZW * c) + 4 * (lr & 3);
-            const i16x4 xf = __builtin_bit_cast(i16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0)));
+            const bf16x8 xw = tr_frag<KROW>(dWb, 32 * ks, zw + kZW * c, lr, lg);
+            const bf16x8 xu = tr_frag<KROW>(dUb, 32 * ks, zw + kZW * c, lr, lg);
 #pragma unroll
-            for (int mi = 0; mi <= kt; ++mi) {
-                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    xf, __builtin_bit_cast(i16x4, u32x2{bch[mi][0], bch[mi][1]}), acc[c][mi], 0, 0, 0);
-                acc[c][mi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    xf, __builtin_bit_cast(i16x4, u32x2{bch[mi][2], bch[mi][3]}), acc[c][mi], 0, 0, 0);
+            for (int mi = 0; mi < kNB; ++mi) {
+                if (16 * mi > 32 * ks + 31) continue;
+                aw[c][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, bh[mi], aw[c][mi], 0, 0, 0);
+                au[c][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xu, bh[mi], au[c][mi], 0, 0, 0);
+                aw[c][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, bl[mi], aw[c][mi], 0, 0, 0);
+                au[c][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xu, bl[mi], au[c][mi], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);  // one k tile's operands in registers at a time
     }
 }
 
-// Y = X T^T and M = strictLower(-T^T Y) for column tile J of M, rows I0 .. I1, on one wave
-// with no barrier: the Y tiles (Mt, J), Mt >= I0, stay in registers, where an accumulator's
-// element q of lane 16 g + c (row 4 g + q, column c) is exactly the B operand of step q of
-// the product T^T Y.  T^T's A fragments are read as columns of T in fp32.  M goes to Ms below
-// the diagonal and transposed above it (Ms[j][i] = M[i][j] for i > j, 0 on the diagonal).
-template <int C, int J, int I0, int I1>
-__device__ inline void ym_column(const float* Xs, const float* Ts, float* Ms, int lr, int lg)
+// Y = X T^T, M = strictLower(-T^T Y) and the elementwise step for column tile J of M, rows
+// I0 .. I1, on one wave with no barrier.  The Y tiles (Mt, J), Mt >= I0, stay in registers,
+// where an accumulator's element q of lane 16 g + c (row 4 g + q, column c) is exactly the B
+// operand of step q of T^T Y and the A operand of step q of Y^T T; T's columns (fp32) are the
+// other operand of both.  So each tile of M comes in two layouts at the cost of its MFMAs alone:
+// m (lane 16 g + c holds rows 16 I + 4 g .. + 3 of column 16 J + c) and mt (row 16 I + c,
+// columns 16 J + 4 g .. + 3).  From them, with R = D (Gamma o M) and S = R + R^T:
+//   - mt gives row i's chunk of S left of the diagonal (R_ij) and the row sum sum_j M_ij H_ij;
+//   - m gives row j's chunk of S right of the diagonal (R_ij again, S symmetric) and the column
+//     sum sum_i beta_i M_ij H_ij;
+// a diagonal tile's chunk takes its lower entries from mt and its upper ones from m.  S goes to
+// Ss as hi / lo chunks; the sums accumulate in rowp[I] (row 16 I + c) and colp[J] (row 16 J + c).
+template <int C, bool GT, int J, int I0, int I1>
+__device__ inline void ym_column(const float* Xs, const float* Ts, const float* Hs, const float* bs, const double* Gd,
+                                 float* Ss, float* scratch, int lr, int lg, float (&rowp)[C / 16],
+                                 float (&colp)[C / 16])
 {
     constexpr int NB = C / 16, TRS = BG<C>::TRS;
     f32x4 y[NB];
@@ -275,35 +311,65 @@ __device__ inline void ym_column(const float* Xs, const float* Ts, float* Ms, in
         }
         __builtin_amdgcn_sched_barrier(0);  // one k step's operands in registers at a time
     }
-    f32x4 m[NB];
+    f32x4 m[NB], mt[NB];  // -M in the two layouts
 #pragma unroll
-    for (int I = I0; I <= I1; ++I) m[I] = zero4();
+    for (int I = I0; I <= I1; ++I) mt[I] = zero4();
 #pragma unroll
-    for (int Mt = I0; Mt < NB; ++Mt) {  // M(I, J) = -sum_{Mt >= I} T(Mt, I)^T Y(Mt, J)
+    for (int Mt = I0; Mt < NB; ++Mt) {  // M(I, J)^T = -sum_{Mt >= I} Y(Mt, J)^T T(Mt, I)
 #pragma unroll
         for (int I = I0; I <= I1 && I <= Mt; ++I) {
             f32x4 a;
 #pragma unroll
             for (int q = 0; q < 4; ++q) a[q] = Ts[(16 * Mt + 4 * lg + q) * TRS + 16 * I + lr];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) m[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], y[Mt][q], m[I], 0, 0, 0);
+            for (int q = 0; q < 4; ++q) mt[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(y[Mt][q], a[q], mt[I], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    // m from mt by a transpose through this wave's own 16 x 20 scratch tile (its LDS operations
+    // run in order, so no barrier is needed; 20-float rows keep both sides conflict-free)
 #pragma unroll
     for (int I = I0; I <= I1; ++I) {
-        // element r of lane 16 g + c is M[16 I + 4 g + r][16 J + c] (negated)
-        if (I > J) {  // constant after unrolling
+        *reinterpret_cast<f32x4*>(scratch + lr * 20 + 4 * lg) = mt[I];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) Ms[(16 * I + 4 * lg + rr) * TRS + 16 * J + lr] = -m[I][rr];
-            *reinterpret_cast<f32x4*>(Ms + (16 * J + lr) * TRS + 16 * I + 4 * lg) = -m[I];
-        } else {
+        for (int r = 0; r < 4; ++r) m[I][r] = scratch[(4 * lg + r) * 20 + lr];
+    }
+    const int jc = 16 * J + lr;  // the m layout's column
+    double gjc = 0.0;
+    if constexpr (GT) gjc = Gd[jc];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int i = 16 * I + 4 * lg + rr, j = 16 * J + lr;
-                if (i >= j) Ms[i * TRS + j] = i > j ? -m[I][rr] : 0.f;
-                if (i > j) Ms[j * TRS + i] = -m[I][rr];
+    for (int I = I0; I <= I1; ++I) {
+        const int i = 16 * I + lr;  // the mt layout's row
+        const float bi = bs[i];
+        double gi = 0.0;
+        if constexpr (GT) gi = Gd[i];
+        // row i, columns 16 J + 4 g ..: H_ij (j < i); row jc, columns 16 I + 4 g ..: H_i'jc (i' > jc)
+        const f32x4 hrow = *reinterpret_cast<const f32x4*>(Hs + i * TRS + 16 * J + 4 * lg);
+        const f32x4 hcol = *reinterpret_cast<const f32x4*>(Hs + jc * TRS + 16 * I + 4 * lg);
+        const f32x4 bcol = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);  // beta_i'
+        f32x4 slow, sup;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * J + 4 * lg + r;   // mt: M[i][j]
+            const int ir = 16 * I + 4 * lg + r;  // m: M[ir][jc]
+            const float Mr = -mt[I][r], Mc = -m[I][r];
+            float grow = 1.f, gcol = 1.f;
+            if constexpr (GT) {  // decay from the earlier to the later token
+                grow = __expf(static_cast<float>(gi - Gd[j]));
+                gcol = __expf(static_cast<float>(Gd[ir] - gjc));
             }
+            const bool lo_ok = I > J || j < i;    // constant for I > J
+            const bool up_ok = I > J || ir > jc;
+            slow[r] = lo_ok ? bi * grow * Mr : 0.f;
+            sup[r] = up_ok ? bcol[r] * gcol * Mc : 0.f;
+            rowp[I] += lo_ok ? Mr * hrow[r] : 0.f;
+            colp[J] += up_ok ? bcol[r] * Mc * hcol[r] : 0.f;
+        }
+        if (I > J) {  // constant after unrolling
+            *reinterpret_cast<u32x4*>(Ss + i * TRS + 16 * J + 4 * lg) = pack_hilo(slow);
+            *reinterpret_cast<u32x4*>(Ss + jc * TRS + 16 * I + 4 * lg) = pack_hilo(sup);
+        } else {  // row i = jc: lower entries from mt, upper ones from m, 0 on the diagonal
+            *reinterpret_cast<u32x4*>(Ss + i * TRS + 16 * J + 4 * lg) = pack_hilo(slow + sup);
         }
     }
 }
@@ -415,10 +481,10 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
     float* Ts = reinterpret_cast<float*>(smem + BGC::OFF_T);
     float* Hs = reinterpret_cast<float*>(smem + BGC::OFF_H);
     float* Xs = reinterpret_cast<float*>(smem + BGC::OFF_X);
-    float* Ms = reinterpret_cast<float*>(smem + BGC::OFF_M);
+    float* Ss = reinterpret_cast<float*>(smem + BGC::OFF_S);
     float* bs = reinterpret_cast<float*>(smem + BGC::OFF_B);
     float* part = reinterpret_cast<float*>(smem + BGC::OFF_PART);
-    float* red = reinterpret_cast<float*>(smem + BGC::OFF_RED);
+    float* py = reinterpret_cast<float*>(smem + BGC::OFF_PY);
     double* Gd = reinterpret_cast<double*>(smem + BGC::OFF_GD);
     int* info = reinterpret_cast<int*>(smem + BGC::OFF_INFO);
 
@@ -486,8 +552,10 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
             }
         }
         __syncthreads();
-        // ---- the next job (the next value head of this unit, else the first of the next unit)
-        // goes in flight now
+        // ---- the next job (the next value head of this unit, else the first of the next unit).  Its
+        // loads are issued where the issuing waves would otherwise wait: the product waves before
+        // the coupling levels (which run on waves 0-1), the Y / M waves at the start of their
+        // products (they finish well before the product waves).
         Unit nu = u;
         int nhv = hv + 1;
         bool nnew = false;
@@ -497,7 +565,6 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
             nhv = nu.hv * r;
             nnew = true;
         }
-        in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);
 
         // ---- A (into Ts) and H = Gamma o K K^T (strict lower, into Hs)
         form_a_h<C, GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
@@ -559,42 +626,55 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
             }
         }
         __syncthreads();
+        if (wave >= kYW) in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // uniform
         coupling_level<kC, 16, TL>(Ts, tid);
         if constexpr (kC >= 64) coupling_level<kC, 32, TL>(Ts, tid);
+        const int zw = wave - kYW;
         const bool last_head = hv == (hk + 1) * r - 1;  // uniform
 
-        // ---- Two independent products at once.  Waves [0, YW): Y = X T^T and M = strictLower(-T^T
-        // Y), by column tiles of M (into Ms).  Waves [YW, BW): T^T dW and T^T dU with their
-        // consumers: dK += D E T^T dW, dV = D T^T dU (staged over dU in the wave's own columns),
-        // and the per-row sums for dbeta and dG.
+        // ---- Two independent products at once.  Waves [0, YW): Y = X T^T, M = strictLower(-T^T Y)
+        // and the elementwise step, by column tiles of M: S = R + R^T into Ss, and the row and
+        // column sums into their slots.  Waves [YW, BW): T^T dW and T^T dU with their consumers:
+        // dK += D E T^T dW, dV = D T^T dU (staged over dU in the wave's own columns), and the
+        // per-row sums for dbeta and dG.
         if (wave < kYW) {  // uniform
+            in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);
+            float rowp[kNB], colp[kNB];
+#pragma unroll
+            for (int I = 0; I < kNB; ++I) rowp[I] = colp[I] = 0.f;
             if constexpr (kC == 64) {
                 if (wave == 0) {
-                    ym_column<64, 0, 0, 1>(Xs, Ts, Ms, lr, lg);
+                    ym_column<64, GT, 0, 0, 1>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
                 } else if (wave == 1) {
-                    ym_column<64, 1, 1, 3>(Xs, Ts, Ms, lr, lg);
+                    ym_column<64, GT, 1, 1, 3>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
                 } else if (wave == 2) {
-                    ym_column<64, 2, 2, 3>(Xs, Ts, Ms, lr, lg);
+                    ym_column<64, GT, 2, 2, 3>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
                 } else {
-                    ym_column<64, 0, 2, 3>(Xs, Ts, Ms, lr, lg);
-                    ym_column<64, 3, 3, 3>(Xs, Ts, Ms, lr, lg);
+                    ym_column<64, GT, 0, 2, 3>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
+                    ym_column<64, GT, 3, 3, 3>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
                 }
             } else {
                 if (wave == 0)
-                    ym_column<32, 0, 0, 1>(Xs, Ts, Ms, lr, lg);
+                    ym_column<32, GT, 0, 0, 1>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
                 else
-                    ym_column<32, 1, 1, 1>(Xs, Ts, Ms, lr, lg);
+                    ym_column<32, GT, 1, 1, 1>(Xs, Ts, Hs, bs, Gd, Ss, py + wave * 4 * BGC::PSTR, lr, lg, rowp, colp);
+            }
+            // one slot per (wave, lane group); rows and columns this wave does not touch get 0.  The
+            // row-sum slots of this wave served as its transpose scratch above.
+#pragma unroll
+            for (int I = 0; I < kNB; ++I) {
+                py[((0 * kYW + wave) * 4 + lg) * BGC::PSTR + 16 * I + lr] = rowp[I];
+                py[((1 * kYW + wave) * 4 + lg) * BGC::PSTR + 16 * I + lr] = colp[I];
             }
         } else {
-            const int zw = wave - kYW;
             const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
             const __bf16* Vb = reinterpret_cast<const __bf16*>(Vraw);
-            f32x4 acc[kCW][kNB];
+            f32x4 aw[kCW][kNB], au[kCW][kNB];
 #pragma unroll
             for (int c = 0; c < kCW; ++c)
 #pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            z_products<C>(dWraw, Ts, zw, lr, lg, acc);
+                for (int mi = 0; mi < kNB; ++mi) aw[c][mi] = au[c][mi] = zero4();
+            z_products<C>(dWraw, dUraw, Ts, zw, lr, lg, aw, au);
             // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
@@ -607,19 +687,12 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
                     const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * (zw + kZW * c) + 4 * lg);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        sk += acc[c][mi][rr] * static_cast<float>(kv[rr]);
-                        dk_acc[c][mi][rr] += bi * ei * acc[c][mi][rr];
+                        sk += aw[c][mi][rr] * static_cast<float>(kv[rr]);
+                        dk_acc[c][mi][rr] += bi * ei * aw[c][mi][rr];
                     }
                 }
-                sk += __shfl_xor(sk, 16);
-                sk += __shfl_xor(sk, 32);
-                if (lg == 0) part[(zw * 2 + 0) * kC + i] = sk;
+                part[((0 * kZW + zw) * 4 + lg) * BGC::PSTR + i] = sk;  // one slot per lane group
             }
-#pragma unroll
-            for (int c = 0; c < kCW; ++c)
-#pragma unroll
-                for (int mi = 0; mi < kNB; ++mi) acc[c][mi] = zero4();
-            z_products<C>(dUraw, Ts, zw, lr, lg, acc);
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
                 const int i = 16 * mi + lr;
@@ -630,78 +703,25 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
                     const bf16x4 vv = *reinterpret_cast<const bf16x4*>(Vb + i * KROW + 16 * (zw + kZW * c) + 4 * lg);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        sv += acc[c][mi][rr] * static_cast<float>(vv[rr]);
-                        acc[c][mi][rr] *= bi;  // dV
+                        sv += au[c][mi][rr] * static_cast<float>(vv[rr]);
+                        au[c][mi][rr] *= bi;  // dV
                     }
                 }
-                sv += __shfl_xor(sv, 16);
-                sv += __shfl_xor(sv, 32);
-                if (lg == 0) part[(zw * 2 + 1) * kC + i] = sv;
+                part[((1 * kZW + zw) * 4 + lg) * BGC::PSTR + i] = sv;
             }
             // this wave alone reads and writes its columns of dU
-            stage_rows<C>(dUraw, acc, zw, lr, lg);
+            stage_rows<C>(dUraw, au, zw, lr, lg);
         }
         __syncthreads();
 
-        // ---- dV out; then elementwise: S = R + R^T (R = D (Gamma o M)) as hi / lo chunks over Ts
-        // (T is no longer read); row sums sum_j M_ij H_ij and sum_j Z_ij, column sums sum_i Z_ij
-        // (Z = M o D H; H already carries Gamma).  Row i of Ms and Hs holds M_ij, H_ij for j < i
-        // and M_ji, H_ji for j > i, so every read is a 16-byte row chunk.
-        store_rows<C>(dUraw, p.dv, tok0, n, p.hv, hv, tid);
-        {
-            constexpr int CPT = BGC::CPT;
-            const int i = tid >> 3, seg = tid & 7;  // row i, columns CPT seg .. CPT seg + CPT - 1
-            const float bi = bs[i];
-            double gi = 0.0;
-            if constexpr (GT) gi = Gd[i];
-            float rowMH = 0.f, rowZ = 0.f, colZ = 0.f;
-#pragma unroll
-            for (int c4 = 0; c4 < CPT / 4; ++c4) {
-                const int j0 = CPT * seg + 4 * c4;
-                const f32x4 mv = *reinterpret_cast<const f32x4*>(Ms + i * TRS + j0);
-                const f32x4 hv4 = *reinterpret_cast<const f32x4*>(Hs + i * TRS + j0);
-                const f32x4 bj = *reinterpret_cast<const f32x4*>(bs + j0);
-                f32x4 sv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = j0 + e;
-                    const bool below = j < i, above = j > i;
-                    float gam = 1.f;
-                    if constexpr (GT) {  // decay between the later and the earlier token
-                        const double d = Gd[j] - gi;
-                        gam = __expf(static_cast<float>(below ? -d : d));
-                    }
-                    const float m = mv[e], h = hv4[e];
-                    // R_ij (j < i) and R_ji (j > i); Z_ij = M_ij beta_i Gamma_ij (k_i . k_j), and
-                    // this thread's column sum runs over column i: Z_ji for rows j > i
-                    sv[e] = below ? m * bi * gam : (above ? m * bj[e] * gam : 0.f);
-                    rowMH += below ? m * h : 0.f;
-                    rowZ += below ? m * bi * h : 0.f;
-                    colZ += above ? m * bj[e] * h : 0.f;
-                }
-                *reinterpret_cast<u32x4*>(Ts + i * TRS + j0) = pack_hilo(sv);
-            }
-            // reduce over the eight threads of row i (consecutive lanes), in a fixed order
-#pragma unroll
-            for (int d = 1; d < 8; d <<= 1) {
-                rowMH += __shfl_xor(rowMH, d);
-                rowZ += __shfl_xor(rowZ, d);
-                colZ += __shfl_xor(colZ, d);
-            }
-            if (seg == 0) {
-                red[i] = rowMH;             // dbeta part
-                red[kC + i] = rowZ - colZ;  // dG part
-            }
-        }
-        __syncthreads();
+        store_rows<C>(dUraw, p.dv, tok0, n, p.hv, hv, tid);  // dV out
 
         // ---- product waves: (R + R^T) K into dK (bf16 MFMA, S hi / lo; S is symmetric, so its row
         // chunks are also the column chunks the product needs), and after a unit's last value
         // head dk staged over H and X.  Wave 0: dbeta, dG, dg of this value head (lanes past the
         // chunk's C rows hold 0; their stores fall outside the n-row buffer range).
         if (wave >= kYW) {  // uniform
-            const int zw = wave - kYW;
-            tr_products<C>(Kraw, Ts, zw, lr, lg, dk_acc);
+            tr_products<C>(Kraw, Ss, zw, lr, lg, dk_acc);
             if (last_head) {  // uniform
                 stage_rows<C>(smem + BGC::OFF_H, dk_acc, zw, lr, lg);
 #pragma unroll
@@ -712,17 +732,25 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
         } else if (wave == 0) {
             const int i = tid;
             const bool row = i < kC;
-            float sk = 0.f, sv = 0.f;
-            if (row) {
+            float sk = 0.f, sv = 0.f, mh = 0.f, cz = 0.f;
+            if (row) {  // the (wave, lane group) slots in a fixed order
 #pragma unroll
-                for (int w = 0; w < kZW; ++w) {
-                    sk += part[(w * 2 + 0) * kC + i];
-                    sv += part[(w * 2 + 1) * kC + i];
+                for (int w = 0; w < kZW * 4; ++w) {
+                    sk += part[(0 * kZW * 4 + w) * BGC::PSTR + i];
+                    sv += part[(1 * kZW * 4 + w) * BGC::PSTR + i];
+                }
+#pragma unroll
+                for (int w = 0; w < kYW * 4; ++w) {
+                    mh += py[(0 * kYW * 4 + w) * BGC::PSTR + i];
+                    cz += py[(1 * kYW * 4 + w) * BGC::PSTR + i];
                 }
             }
+            // dbeta_i: sum_d (T^T dW)_id e^{G_i} K_id + sum_d (T^T dU)_id V_id + sum_j M_ij H_ij;
+            // dG_i: beta_i e^{G_i} sum_d (T^T dW)_id K_id + sum_j Z_ij - sum_j Z_ji (Z = M o D H)
+            const float bi = row ? bs[i] : 0.f;
             const float ei = GT && row ? GR::E(Kraw, i) : 1.f;
-            const float db = row ? sk * ei + sv + red[i] : 0.f;
-            float dG = row ? bs[i] * ei * sk + red[kC + i] : 0.f;
+            const float db = row ? sk * ei + sv + mh : 0.f;
+            float dG = row ? bi * ei * sk + bi * mh - cz : 0.f;
             const __amdgpu_buffer_rsrc_t br = rsrc(p.dbeta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, db), br, i * p.hv * 4, 0, 0);
             if constexpr (GT) {
