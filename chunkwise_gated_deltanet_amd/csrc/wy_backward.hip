@@ -464,6 +464,51 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
     }
 }
 
+// Batch rows: the units logical, logical + G, logical + 2 G, ... of one workgroup, walked without
+// a division per step.  logical = slot * H + head and slot = b * cps + c, so a step of G adds
+// G mod H to the head (carrying one slot) and G div H (or one more) slots, split once per
+// workgroup into whole rows and chunks.
+struct BatchWalk {
+    uint32_t head, c, b, H, cps, dhead, dq0, dr0, dq1, dr1;
+
+    __device__ void init(uint32_t logical, uint32_t G, uint32_t heads, uint32_t chunks_per_row)
+    {
+        H = heads;
+        cps = chunks_per_row;
+        const uint32_t slot = logical / H;
+        head = logical % H;
+        b = slot / cps;
+        c = slot % cps;
+        dhead = G % H;
+        const uint32_t dslot = G / H;
+        dq0 = dslot / cps;
+        dr0 = dslot % cps;
+        dq1 = (dslot + 1) / cps;
+        dr1 = (dslot + 1) % cps;
+    }
+    __device__ void step()
+    {
+        head += dhead;
+        const bool carry = head >= H;
+        head = carry ? head - H : head;
+        c += carry ? dr1 : dr0;
+        b += carry ? dq1 : dq0;
+        if (c >= cps) {
+            c -= cps;
+            ++b;
+        }
+    }
+    template <int C>
+    __device__ Unit unit(int seqlen, bool valid) const
+    {
+        Unit u;
+        u.tok0 = static_cast<int64_t>(b) * seqlen + static_cast<int64_t>(c) * C;
+        u.n = valid ? min(C, seqlen - static_cast<int>(c) * C) : 0;
+        u.hv = static_cast<int>(head);
+        return u;
+    }
+};
+
 template <int C, bool GT>
 __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
 {
@@ -507,7 +552,15 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
     // and the next job's inputs are in flight while the current one computes.
     const uint32_t G = gridDim.x;  // a multiple of 8
     int64_t logical = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
-    Unit u = map_unit<kC>(mp, info, logical, G, tid);
+    BatchWalk walk{};
+    Unit u;
+    if (p.cu == nullptr) {  // uniform
+        walk.init(static_cast<uint32_t>(logical), G, static_cast<uint32_t>(p.hq),
+                  static_cast<uint32_t>((p.seqlen + kC - 1) / kC));
+        u = walk.unit<kC>(p.seqlen, logical < p.units);
+    } else {
+        u = map_unit<kC>(mp, info, logical, G, tid);
+    }
     if (u.n <= 0) return;  // uniform
     int hv = u.hv * r;
     bool new_unit = true;
@@ -561,7 +614,12 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
         bool nnew = false;
         if (nhv == (hk + 1) * r) {  // uniform
             logical += G;
-            nu = map_unit<kC>(mp, info, logical, G, tid);
+            if (p.cu == nullptr) {  // uniform
+                walk.step();
+                nu = walk.unit<kC>(p.seqlen, logical < p.units);
+            } else {
+                nu = map_unit<kC>(mp, info, logical, G, tid);
+            }
             nhv = nu.hv * r;
             nnew = true;
         }
