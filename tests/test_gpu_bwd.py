@@ -113,6 +113,19 @@ def test_wy_backward_many_short_sequences(C, gpu):
     check(inp, dW, dU, dT, out, f"1100 short sequences C={C}")
 
 
+@pytest.mark.parametrize("C", [32, 64])
+def test_wy_backward_batch_walk(C, gpu):
+    """Batch rows with more units than resident workgroups (432 at C = 64, 846 at C = 32) and 3 key
+    heads, which divides neither grid: each workgroup's division-free walk over its units carries
+    the head into the chunk slot and the chunk slot into the next row, on ragged rows (T = 1500),
+    with two value heads per key head summed into dk."""
+    inp, dW, dU, dT = make_inputs(dict(C=C, batch=6, seqlen=1500, num_qk_heads=3, num_v_heads=6,
+                                       seed=130, gate_mu=4.0, dT=True))
+    say(f"wy_backward batch walk C={C}")
+    out = run_bwd(inp, dW, dU, dT, gpu)
+    check(inp, dW, dU, dT, out, f"batch walk C={C}")
+
+
 def test_wy_backward_deterministic(gpu):
     import torch
     inp, dW, dU, dT = make_inputs(CASES["packed_gva_mu4_dT"])
