@@ -218,19 +218,29 @@ def cpu_baseline_fwd(inp, seconds=10.0):
 
 
 # Extra workloads timed after the headline (each with its own roofline): the other C = 64
-# configurations, the chunk-size study on B=4 T=4096 H=32, and 1024 short packed sequences (the
-# packed-sequence work map under load).
-DEFAULT_EXTRAS = "3:32,3:64,3:128,5:64,6:64"
+# configurations, the chunk-size study on B=4 T=4096 H=32, 1024 short packed sequences (the
+# packed-sequence work map under load), and on the headline's shape the backward at C = 64 and
+# 32 and the chunk recurrence in its sequence-parallel form.
+DEFAULT_EXTRAS = "3:32,3:64,3:128,5:64,6:64,bwd/2:64,bwd/2:32,fwd/2:64/auto"
 
 
-def parse_extras(text):
-    """'3:32,5:64' -> [(3, 32), (5, 64)]; 'none' or '' -> []."""
+def parse_extras(text, entry="wy"):
+    """'[entry/]workload:C[/segments]' items, comma-separated, -> (entry, workload, C, segments)
+    tuples; the entry defaults to `entry`, segments (fwd / gdn: an int or 'auto') to None.
+    'none' or '' -> []."""
     if not text or text == "none":
         return []
     out = []
     for item in text.split(","):
-        idx, c = item.split(":")
-        out.append((int(idx), int(c)))
+        parts = item.split("/")
+        e = entry
+        if not parts[0][:1].isdigit():
+            e = parts.pop(0)
+            if e not in ENTRY_NAMES:
+                raise ValueError(f"unknown entry point in extras item {item!r}")
+        idx, c = parts[0].split(":")
+        seg = parts[1] if len(parts) > 1 else None
+        out.append((e, int(idx), int(c), seg))
     return out
 
 
@@ -483,9 +493,10 @@ def main(argv=None):
                          "chunks run in parallel (wyp_chunk_fwd_cp); 'auto' picks it from the "
                          "shape")
     ap.add_argument("--extras", default=None,
-                    help="extra workloads timed after the main one with the same entry point, "
-                         "as workload:C pairs (default for the headline: "
-                         f"{DEFAULT_EXTRAS}; 'none' for none)")
+                    help="extra workloads timed after the main one, comma-separated "
+                         "[entry/]workload:C[/segments] items (the entry defaults to --entry; "
+                         "segments for fwd / gdn: chunks per segment or 'auto'); default for "
+                         f"the headline: {DEFAULT_EXTRAS}; 'none' for none")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed step from Python instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -555,22 +566,27 @@ def main(argv=None):
                                    "their summed algorithmic bytes over the step time")
     extras = parse_extras(args.extras if args.extras is not None else
                           (DEFAULT_EXTRAS if args.entry == "wy" and args.workload == 2 and
-                           args.chunk_size in (None, 64) and not gated else "none"))
+                           args.chunk_size in (None, 64) and not gated else "none"), args.entry)
     if extras:
         out["workloads"] = []
         cache = {}
-        for idx, c in extras:
-            we = synth.workload(idx, chunk_size=c, gate_mu=args.gate_mu, with_q=fwd_entry)
+        for e, idx, c, seg in extras:
+            e_fwd = e in ("fwd", "gdn")
+            we = synth.workload(idx, chunk_size=c, gate_mu=args.gate_mu, with_q=e_fwd)
             # the chunk size changes only a packed workload's lengths
-            key = (idx, c if we.seq_range is not None else None)
+            key = (idx, c if we.seq_range is not None else None, e_fwd)
             if key not in cache:
                 cache.clear()
                 cache[key] = synth.generate(we)
             ie = dict(cache[key], chunk_size=c)
+            args_e = argparse.Namespace(**vars(args))
+            args_e.workload, args_e.segment_chunks = idx, (seg if e_fwd else None)
             # each gets its own clock ramp: the GPU idles while the host draws its inputs
-            re_ = measure(args, args.entry, we, ie, dev, lib, ramp=True)
+            re_ = measure(args_e, e, we, ie, dev, lib, ramp=True)
             out["workloads"].append({
-                "workload": we.name, "chunk_size": c, "units_per_step": re_["units"],
+                "workload": we.name, "entry": ENTRY_NAMES[e], "chunk_size": c,
+                "segment_chunks": re_["seg_chunks"] if e_fwd else None,
+                "units_per_step": re_["units"],
                 "tokens_per_step": re_["tokens"], "ms_per_step": re_["step_s"] * 1e3,
                 "value": re_["units"] / re_["step_s"], "unit": "chunks/s",
                 "tokens_per_s": re_["tokens"] / re_["step_s"],

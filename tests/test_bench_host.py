@@ -82,9 +82,17 @@ def test_committed_headline_counters_are_near_the_algorithmic_bytes():
 
 def test_extra_workloads_cover_the_c64_configs_and_the_chunk_study():
     extras = bench.parse_extras(bench.DEFAULT_EXTRAS)
-    assert (3, 64) in extras and (5, 64) in extras
-    assert {c for i, c in extras if i == 3} == {32, 64, 128}
-    assert bench.parse_extras("none") == [] and bench.parse_extras("2:32") == [(2, 32)]
+    wy = [(i, c) for e, i, c, seg in extras if e == "wy"]
+    assert (3, 64) in wy and (5, 64) in wy
+    assert {c for i, c in wy if i == 3} == {32, 64, 128}
+    # the backward and the sequence-parallel recurrence on the headline's shape ride along
+    assert ("bwd", 2, 64, None) in extras and ("bwd", 2, 32, None) in extras
+    assert ("fwd", 2, 64, "auto") in extras
+    assert bench.parse_extras("none") == [] and bench.parse_extras("2:32") == [("wy", 2, 32, None)]
+    assert bench.parse_extras("2:32", "kkt") == [("kkt", 2, 32, None)]
+    assert bench.parse_extras("gdn/2:64/16") == [("gdn", 2, 64, "16")]
+    with pytest.raises(ValueError):
+        bench.parse_extras("nope/2:64")
 
 
 def test_cpu_threads_are_capped_and_host_cores_recorded():
