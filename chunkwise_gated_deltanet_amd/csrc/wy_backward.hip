@@ -6,7 +6,7 @@
 //         lower-triangular matrix).
 //   [QLA] The FlashQLA announcement, sections "使用方式" (usage) and the backward (bwd_wy).
 //
-// Backward of the preparation step (bf16 k / v, C = 64): the gradient of
+// Backward of the preparation step (bf16 k / v, C = 32 and 64): the gradient of
 //     L = <dT, T> + <dW, W> + <dU, U>
 // with respect to k, v, beta and g.  Forward per chunk and value head (D = diag(beta),
 // E = diag(exp(G)), Gamma[i][j] = exp(G_i - G_j), H = Gamma o K K^T on the strict lower
@@ -21,9 +21,11 @@
 // A unit is one (chunk, key head); a workgroup handles the value heads of a unit in turn (one
 // job each) and sums their dK in registers, so dk is written once, without atomics.  Workgroups
 // are persistent and walk a strided list of units; the next job's inputs are loaded while the
-// current job computes.  T is recomputed with
-// the forward's own steps (bit-identical to the T that wy_prepare returns).  T and R + R^T
-// enter the bf16 products as hi + lo pairs, so dbeta and dg keep fp32 accuracy.
+// current job computes.  T is recomputed with the forward's own steps (bit-identical to the T
+// that wy_prepare returns).  After it the waves split in two halves that run the two
+// independent products side by side: Y, M and the elementwise step on one, T^T dW and T^T dU
+// with their consumers on the other.  T and R + R^T enter the bf16 products as hi + lo pairs,
+// so dbeta and dg keep fp32 accuracy.
 //
 // Device helpers shared with the forward preparation step (unit map, T-tile layout, Gram
 // fragments, block inversion, MFMA operand convention) live in wyprep_device.h.
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
         form_a_h<C, GT>(Kraw, Ts, Hs, bs, wave, lr, lg);
         __syncthreads();
         // ---- wave 0 inverts the diagonal blocks of A (its substitutions are one long dependency
-        // chain); meanwhile waves 1-7 form X, which does not depend on T
+        // chain); meanwhile the other waves form X, which does not depend on T
         if (wave == 0) {  // uniform
             invert_diagonal_blocks<kC, TL>(Ts, tid);
         } else {
