@@ -78,7 +78,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kD = 128;        // dk = dv
-constexpr int kThreads = 256;  // the combine's workgroup
+constexpr int kThreads = 512;  // the combine's workgroup: one wave per 16-row tile of the state
 constexpr int kBufferConfig = 0x00020000;
 // Non-temporal policy for what one workgroup alone reads or writes (its U slice, g, o).  Q, K
 // and W keep the default policy: the four dv-slice workgroups of a head each read them, and
@@ -655,15 +655,19 @@ __global__ __launch_bounds__(Geo<C>::THREADS) __attribute__((amdgpu_waves_per_eu
 // and S_start(s + 1) = M_s S_start(s) + A_s for s = 0 .. nseg_n - 2, each written over A_s
 // (pass 3 reads them there).  Each step is 128 x 128 x 16 fp32
 // multiply-adds on fp32 MFMA 16x16x4.  The steps of one slice form a chain, so the slices are
-// 16 columns wide (eight workgroups per head: more chains, each step shorter); wave w owns row
-// tiles 2w, 2w + 1; S^T sits in LDS so every B operand is one 16-byte read.  M_{s+1} and A_{s+1}
-// do not depend on S and are in flight while step s computes.
+// 16 columns wide (eight workgroups per head: more chains, each step shorter) and each of the
+// eight waves owns one row tile (a chain of 32 dependent MFMAs per step); S^T sits in LDS so
+// every B operand is one 16-byte read.  M_{s+1} and A_{s+1} do not depend on S and are in
+// flight while step s computes.
 constexpr int kCombCols = 16;
 constexpr int kCombSlices = kD / kCombCols;
 
+constexpr int kCombTiles = kD / 16 / (kThreads / 64);  // row tiles per wave
+static_assert(kCombTiles >= 1 && kCombTiles * (kThreads / 64) * 16 == kD, "the waves cover the state's rows");
+
 struct CombineOperands {
-    f32x4 m[2][kD / 16];  // M rows 16 mt + lr, columns 16 kt + 4 lg .. + 3 (A operands)
-    f32x4 a[2];           // A elements [16 mt + 4 lg + r][lr] of the slice (accumulator start)
+    f32x4 m[kCombTiles][kD / 16];  // M rows 16 mt + lr, columns 16 kt + 4 lg .. + 3 (A operands)
+    f32x4 a[kCombTiles];           // A elements [16 mt + 4 lg + r][lr] of the slice (accumulator start)
 
     // Step s of value head hv of a sequence: A_s sits in a-slot abase + s + 1, M_s in m-slot
     // mbase + s.
@@ -673,8 +677,8 @@ struct CombineOperands {
         const float* A = p.ws_a + static_cast<int64_t>(at.abase + s + 1) * p.hv * kD * kD + head + slice * kCombCols;
         const float* M = p.ws_m + static_cast<int64_t>(at.mbase + s) * p.hv * kD * kD + head;
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            const int mt = 2 * wave + mm;
+        for (int mm = 0; mm < kCombTiles; ++mm) {
+            const int mt = kCombTiles * wave + mm;
 #pragma unroll
             for (int kt = 0; kt < kD / 16; ++kt)
                 m[mm][kt] = *reinterpret_cast<const f32x4*>(M + (16 * mt + lr) * kD + 16 * kt + 4 * lg);
@@ -724,9 +728,9 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
         // compiler's wait for `cur` conservative, and that wait would then cover these loads.
         nxt.load(p, at, hv, sg + 2 < at.nseg ? sg + 1 : sg, slice, wave, lr, lg);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads here, ahead of this step's products
-        f32x4 acc[2];
+        f32x4 acc[kCombTiles];
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
+        for (int mm = 0; mm < kCombTiles; ++mm) {
             acc[mm] = cur.a[mm];
 #pragma unroll
             for (int kt = 0; kt < kD / 16; ++kt) {
@@ -739,10 +743,11 @@ __global__ __launch_bounds__(kThreads) void cp_combine_kernel(Params p)
         __syncthreads();  // every read of S_start(s) done
         float* A = s0 + (sg + 1) * slot_floats;
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            *reinterpret_cast<f32x4*>(&St[lr][16 * (2 * wave + mm) + 4 * lg]) = acc[mm];
+        for (int mm = 0; mm < kCombTiles; ++mm) {
+            const int mt = kCombTiles * wave + mm;
+            *reinterpret_cast<f32x4*>(&St[lr][16 * mt + 4 * lg]) = acc[mm];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) A[(16 * (2 * wave + mm) + 4 * lg + r) * kD + lr] = acc[mm][r];
+            for (int r = 0; r < 4; ++r) A[(16 * mt + 4 * lg + r) * kD + lr] = acc[mm][r];
         }
         __syncthreads();
     };
