@@ -82,10 +82,11 @@ def kernel_source_sha(entry="wy"):
     return h.hexdigest()
 
 
-def profile_name(entry, w, batch, seqlen, num_seqs):
+def profile_name(entry, w, batch, seqlen, num_seqs, seg_chunks=None):
     """Name of the profiles/ summaries for one entry point and workload, e.g.
-    wy_prepare_bf16_c64_b1t8192h16, wy_prepare_bf16_c64_packed8_hq16hv64 or, with log gates,
-    wy_prepare_gated_bf16_c64_b1t8192h16."""
+    wy_prepare_bf16_c64_b1t8192h16, wy_prepare_bf16_c64_packed8_hq16hv64, with log gates
+    wy_prepare_gated_bf16_c64_b1t8192h16, or for the split forward (segments of 16 chunks)
+    chunk_fwd_cp16_bf16_c64_b1t8192h16."""
     if num_seqs:
         shape = f"packed{num_seqs}_hq{w.num_qk_heads}hv{w.num_v_heads}"
     elif w.num_qk_heads == w.num_v_heads:
@@ -93,7 +94,8 @@ def profile_name(entry, w, batch, seqlen, num_seqs):
     else:
         shape = f"b{batch}t{seqlen}hq{w.num_qk_heads}hv{w.num_v_heads}"
     gated = "_gated" if w.gate_mu is not None else ""
-    return f"{ENTRY_NAMES[entry]}{gated}_{w.dtype}_c{w.chunk_size}_{shape}"
+    split = f"_cp{seg_chunks}" if seg_chunks is not None and entry in ("fwd", "gdn") else ""
+    return f"{ENTRY_NAMES[entry]}{split}{gated}_{w.dtype}_c{w.chunk_size}_{shape}"
 
 
 def counter_traffic(name, entry="wy"):
@@ -444,7 +446,7 @@ def measure(args, entry, w, inp, dev, lib, ramp=True):
     durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
 
     achieved = alg / step_s / 1e9
-    pname = profile_name(entry, w, B, T, 0 if cu is None else cu.numel() - 1)
+    pname = profile_name(entry, w, B, T, 0 if cu is None else cu.numel() - 1, seg_chunks)
     traffic = counter_traffic(pname, entry) if entry != "gdn" else None
     res = {
         "units": units, "tokens": tokens, "alg": alg, "nsets": nsets, "seg_chunks": seg_chunks,

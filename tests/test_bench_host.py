@@ -105,3 +105,16 @@ def test_solve_bytes():
     assert bench.algorithmic_bytes(tok, hq, hv, d, d, 64, 2, entry="solve") == \
         tok * (hq * d * 2 + hv * (d * 2 + 4 + d * 2))
     assert bench.profile_name("solve", synth.workload(2), 1, 8192, 0) == "solve_rhs_bf16_c64_b1t8192h16"
+
+
+def test_split_forward_reads_its_own_profile():
+    # the split form's summary covers its three kernels; the unsplit one is another file
+    w = synth.workload(2)
+    assert bench.profile_name("fwd", w, 1, 8192, 0) == "chunk_fwd_bf16_c64_b1t8192h16"
+    assert bench.profile_name("fwd", w, 1, 8192, 0, 16) == "chunk_fwd_cp16_bf16_c64_b1t8192h16"
+    assert bench.profile_name("wy", w, 1, 8192, 0, 16) == "wy_prepare_bf16_c64_b1t8192h16"
+    t = bench.counter_traffic("chunk_fwd_cp16_bf16_c64_b1t8192h16", "fwd")
+    if t is None:
+        pytest.skip("split forward counter summary was taken on another kernel source")
+    alg = bench.fwd_bytes(8192, 1, 16, 16, 128, 128, 2, False)
+    assert 1.5 * alg < t < 2.0 * alg  # two passes over K, W, U and the workspace round trip
