@@ -632,7 +632,9 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
         // ---- wave 0 inverts the diagonal blocks of A (its substitutions are one long dependency
         // chain); meanwhile the other waves form X, which does not depend on T
         if (wave == 0) {  // uniform
+            __builtin_amdgcn_s_setprio(2);  // the chain: its instructions go first on the SIMD
             invert_diagonal_blocks<kC, TL>(Ts, tid);
+            __builtin_amdgcn_s_setprio(0);
         } else {
             // ---- X = strictLower(dT + (dW K^T) D E + (dU V^T) D), lower tiles on bf16 MFMA.  The dT
             // reads sit in their own instance of the tile loop: without dT the loop issues no memory
