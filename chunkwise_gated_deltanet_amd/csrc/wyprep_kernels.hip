@@ -982,15 +982,18 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     // other workgroups' waves share the SIMDs.  With T alone (up to seven workgroups per CU) and
     // at C = 128 (three coupling levels) their raised priority shortens it; with W and U at
     // C <= 64 the other workgroups' product waves should not wait, and it stays even.
+    // At C = 64 with four or more value heads per key head (three workgroups per CU) the chain
+    // goes first too.
     constexpr bool kChainFirst = !WU || C == 128;
-    if constexpr (kChainFirst) __builtin_amdgcn_s_setprio(2);
+    const bool chain_first = kChainFirst || (C == 64 && p.hv >= 4 * p.hq);  // uniform
+    if (chain_first) __builtin_amdgcn_s_setprio(2);
     invert_diagonal_blocks<C, TL>(Ts, tid);
     if constexpr (C >= 64) {
         if (nxt.n > 0) pf.issue_k(p, nxt, tid);
     }
     __syncthreads();
     if constexpr (SOLVE) {
-        if constexpr (kChainFirst) __builtin_amdgcn_s_setprio(0);
+        if (chain_first) __builtin_amdgcn_s_setprio(0);
         // K is no longer read (form_a finished before the last barrier but one): the right-hand
         // side takes its place, and X is staged over it
         pf.commit_v(Kraw, tid);
@@ -1004,7 +1007,7 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
     if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
     if constexpr (C >= 64) coupling_level<C, 32, TL>(Ts, tid);
     if constexpr (C >= 128) coupling_level<C, 64, TL>(Ts, tid);
-    if constexpr (kChainFirst) __builtin_amdgcn_s_setprio(0);
+    if (chain_first) __builtin_amdgcn_s_setprio(0);
     store_t<C, TL, DT == 0 && WU, (M & kModeT) != 0>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
         __syncthreads();  // T (packed T' for bf16) of all threads is in place
