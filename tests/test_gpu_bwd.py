@@ -35,6 +35,11 @@ CASES = {
                                gate_mu=0.0, seqlens=[31, 32, 33, 1, 0, 95, 200]),
     "C32_T700_H2_ungated_dT": dict(C=32, batch=1, seqlen=700, num_qk_heads=2, num_v_heads=2,
                                    seed=129, dT=True, beta_sigma=1.5),
+    # eight value heads per key head: dk sums eight jobs in registers before its one store
+    "gva8_mu4_dT": dict(batch=1, seqlen=0, num_qk_heads=2, num_v_heads=16, seed=131, gate_mu=4.0,
+                        dT=True, seqlens=[200, 333, 64, 1, 129]),
+    "C32_gva8_mu4_dT": dict(C=32, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=16, seed=132,
+                            gate_mu=4.0, dT=True, seqlens=[200, 333, 32, 1, 65]),
 }
 
 
