@@ -6,7 +6,7 @@
 //         lower-triangular matrix).
 //   [QLA] The FlashQLA announcement, sections "使用方式" (usage) and the backward (bwd_wy).
 //
-// Backward of the preparation step (bf16 k / v, C = 32 and 64): the gradient of
+// Backward of the preparation step (bf16 k / v, C = 32, 64 and 128): the gradient of
 //     L = <dT, T> + <dW, W> + <dU, U>
 // with respect to k, v, beta and g.  Forward per chunk and value head (D = diag(beta),
 // E = diag(exp(G)), Gamma[i][j] = exp(G_i - G_j), H = Gamma o K K^T on the strict lower
@@ -903,6 +903,726 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
     return 0;
 }
 
+
+// ---- C = 128 ---------------------------------------------------------------------------------
+// The plan above (K, V, dW, dU, T, H, X and S of one job all in LDS) would take about 390 KB at
+// C = 128.  Here only K, T and one C x C region stay in LDS.  The region holds X, then Y, then R
+// in turn, each hand-over behind a barrier.  V is staged (256-byte rows, 16-byte chunks XOR-
+// swizzled by row) over the scratch that later holds the row sums and the per-wave panels, for
+// as long as X is formed.  The rows of dW and dU enter the X tiles straight from memory.  The
+// products over tokens (T^T dW, T^T dU) stream each wave's own 16 columns of dW and dU through
+// a 32-token panel of that wave.  H is not kept: the elementwise step forms its tiles again
+// from K.  Eight waves, one workgroup per CU; every phase runs on all eight waves, with the
+// fp32 Y and M tiles dealt so that each SIMD gets the same number of MFMAs.
+namespace c128 {
+
+constexpr int kC = 128;
+constexpr int kNB = kC / 16;
+constexpr int kBT = 512;
+constexpr int kBW = kBT / 64;
+constexpr int KROW = kD + 8;  // bf16 per staged K row (and per dv / dk staging row)
+using TL = TLayout<kC>;       // the 36 lower 16 x 16 tiles, 16 rows of 20 floats each
+using GR = GateRow<KROW, 2>;
+constexpr int KB = kC * KROW * 2;
+constexpr int OFF_K = 0;
+constexpr int OFF_T = OFF_K + KB;             // A -> T (tile-packed fp32); then dv as bf16 rows
+constexpr int OFF_XR = OFF_T + TL::BYTES;     // X -> Y -> R (tile-packed); then dk as bf16 rows
+constexpr int OFF_B = OFF_XR + TL::BYTES;     // beta
+constexpr int OFF_GD = OFF_B + kC * 4;        // G, fp64 (gated)
+constexpr int OFF_INFO = OFF_GD + kC * 8;
+constexpr int OFF_V = OFF_INFO + 16;          // V rows while X is formed; after that:
+constexpr int OFF_SUM = OFF_V;                //   row sums, 4 kinds x 8 waves x C floats
+constexpr int OFF_PAN = OFF_SUM + 4 * kBW * kC * 4;  //   2 KB per wave: transpose tile; dW / dU panels
+constexpr int LDS_TOTAL = OFF_PAN + kBW * 2048;
+static_assert(LDS_TOTAL - OFF_V >= kC * kD * 2, "V rows fit over the sums and the panels");
+static_assert(KB <= TL::BYTES, "dv and dk are staged as bf16 rows over T and XR");
+static_assert(OFF_V % 16 == 0 && OFF_PAN % 16 == 0, "16-byte aligned regions");
+static_assert(LDS_TOTAL <= 160 * 1024, "C = 128 backward LDS plan exceeds 160 KiB");
+
+// Sum slots: kind 0 = sum_j M_ij H_ij (row i), 1 = sum_i beta_i M_ij H_ij (column j), 2 = sum_d
+// (T^T dW)_id K_id, 3 = sum_d (T^T dU)_id V_id; one row of C floats per (kind, wave).
+__device__ inline float* sum_slot(unsigned char* smem, int kind, int wave)
+{
+    return reinterpret_cast<float*>(smem + OFF_SUM) + (kind * kBW + wave) * kC;
+}
+
+// Lower tiles (Mt, J) of Y = X T^T per wave, as 8 Mt + J (255 ends a list).  Tile (Mt, J) costs
+// J + 1 steps of four fp32 MFMAs, so every wave gets 15 steps and each SIMD (waves w and w + 4)
+// 30.  The M tiles use the same lists mirrored: entry (Mt, J) stands for M tile (7 - J, 7 - Mt),
+// whose cost 8 - I is again J + 1.
+__constant__ unsigned char kYTiles[kBW][8] = {
+    {63, 54, 255, 255, 255, 255, 255, 255},  // (7,7) (6,6)
+    {62, 45, 9, 255, 255, 255, 255, 255},    // (7,6) (5,5) (1,1)
+    {53, 61, 17, 0, 255, 255, 255, 255},     // (6,5) (7,5) (2,1) (0,0)
+    {36, 44, 52, 255, 255, 255, 255, 255},   // (4,4) (5,4) (6,4)
+    {60, 27, 35, 25, 255, 255, 255, 255},    // (7,4) (3,3) (4,3) (3,1)
+    {43, 51, 59, 33, 8, 255, 255, 255},      // (5,3) (6,3) (7,3) (4,1) (1,0)
+    {18, 26, 34, 41, 49, 16, 24, 255},       // (2,2) (3,2) (4,2) (5,1) (6,1) (2,0) (3,0)
+    {42, 50, 58, 57, 32, 40, 48, 56},        // (5,2) (6,2) (7,2) (7,1) (4,0) (5,0) (6,0) (7,0)
+};
+
+// X tiles while waves 0-1 invert the diagonal blocks: waves 2-7 take row segments (I, J0, J1),
+// seven tiles or fewer each (255: none).
+__constant__ unsigned char kXSeg[kBW - 2][2][3] = {
+    {{7, 0, 3}, {255, 0, 0}}, {{6, 0, 6}, {255, 0, 0}}, {{5, 0, 5}, {0, 0, 0}},
+    {{4, 0, 4}, {1, 0, 1}},   {{3, 0, 3}, {2, 0, 2}},   {{7, 4, 7}, {255, 0, 0}},
+};
+
+// The next job's K (read only for the first value head of a unit), beta and g in flight.
+template <bool GT>
+struct Next {
+    static constexpr int NIT = kC * 16 / kBT;
+    u32x4 k[NIT];
+    float b;
+    float g[2];  // wave 0 lane l: g of rows l and l + 64
+
+    __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hk, int hv, bool with_k, int tid)
+    {
+        const uint32_t kstride = static_cast<uint32_t>(p.hq) * kD * 2;
+        const int nk = with_k ? n : 0;  // n = 0 (no job): empty ranges, every load reads 0
+        const __amdgpu_buffer_rsrc_t kr =
+            rsrc(p.k + (tok0 * p.hq + hk) * kD, nk > 0 ? (nk - 1) * kstride + kD * 2 : 0u);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kBT;
+            k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (q >> 4) * kstride + (q & 15) * 16, 0, kStream);
+        }
+        const uint32_t bytes = n > 0 ? ((n - 1) * p.hv + 1) * 4 : 0u;
+        const __amdgpu_buffer_rsrc_t br = rsrc(p.beta + tok0 * p.hv + hv, bytes);
+        b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (tid & (kC - 1)) * p.hv * 4, 0, 0));
+        g[0] = g[1] = 0.f;
+        if constexpr (GT) {
+            const __amdgpu_buffer_rsrc_t gr = rsrc(p.g + tok0 * p.hv + hv, bytes);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                g[e] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(gr, ((tid & 63) + 64 * e) * p.hv * 4, 0, 0));
+        }
+    }
+
+    // K rows (new unit only), beta, and G = inclusive prefix sums of g in fp64 by wave 0, in the
+    // forward's order (each half of the chunk scanned, the first half's total added to the second)
+    __device__ __attribute__((always_inline)) void commit(unsigned char* Kraw, float* bs, double* Gd, bool with_k, int tid) const
+    {
+        if (with_k) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int q = tid + it * kBT;
+                *reinterpret_cast<u32x4*>(Kraw + (q >> 4) * (KROW * 2) + (q & 15) * 16) = k[it];
+            }
+        }
+        if (tid < kC) bs[tid] = b;
+        if constexpr (GT) {
+            if (tid < 64) {
+                double run = 0.0;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    double x = static_cast<double>(g[e]);
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const double t = __shfl_up(x, d);
+                        if (tid >= d) x += t;
+                    }
+                    x += run;
+                    const int r = tid + 64 * e;
+                    *GR::Gp(Kraw, r) = x;
+                    *GR::Ep(Kraw, r) = __expf(static_cast<float>(x));
+                    Gd[r] = x;
+                    run = __shfl(x, 63);
+                }
+            }
+        }
+    }
+};
+
+// This job's V rows, in flight and then staged: row r's 16-byte chunk q at r * 256 + 16 (q ^ (r & 15)).
+struct VRows {
+    static constexpr int NIT = kC * 16 / kBT;
+    u32x4 x[NIT];
+
+    __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hv, int tid)
+    {
+        const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
+        const __amdgpu_buffer_rsrc_t vr = rsrc(p.v + (tok0 * p.hv + hv) * kD, (n - 1) * stride + kD * 2);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kBT;
+            x[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, (q >> 4) * stride + (q & 15) * 16, 0, 0);
+        }
+    }
+    __device__ __attribute__((always_inline)) void commit(unsigned char* dst, int tid) const
+    {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kBT;
+            const int r = q >> 4, c = q & 15;
+            *reinterpret_cast<u32x4*>(dst + r * 256 + 16 * (c ^ (r & 15))) = x[it];
+        }
+    }
+};
+
+// A fragments of rows 16 I .. 16 I + 15 of dW and dU (lane 16 g + c: row 16 I + c, dk 32 s + 8 g
+// .. + 7), straight from memory; I < 0 reads nothing.
+struct RowFrags {
+    bf16x8 w[kD / 32], u[kD / 32];
+
+    __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hv, int I, int lr, int lg)
+    {
+        const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
+        const uint32_t bytes = I >= 0 ? (n - 1) * stride + kD * 2 : 0u;
+        const __amdgpu_buffer_rsrc_t wr = rsrc(p.dW + (tok0 * p.hv + hv) * kD, bytes);
+        const __amdgpu_buffer_rsrc_t ur = rsrc(p.dU + (tok0 * p.hv + hv) * kD, bytes);
+        const uint32_t off = (16 * (I >= 0 ? I : 0) + lr) * stride + 16 * lg;
+#pragma unroll
+        for (int s = 0; s < kD / 32; ++s) {
+            w[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, off + 64 * s, 0, 0));
+            u[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ur, off + 64 * s, 0, 0));
+        }
+    }
+};
+
+// a2 + a3: A = I + strictLower(D H) into the tile-packed Ts, entry for entry as the forward
+// forms it (same Gram fragments and MFMA order, same decay and products), so T is bit-identical.
+template <bool GT>
+__device__ __attribute__((always_inline)) void form_a(const unsigned char* Kraw, float* Ts, const float* bs, int wave, int lr, int lg)
+{
+    constexpr int NTILE = kNB * (kNB + 1) / 2;
+    for (int t = wave; t < NTILE; t += kBW) {  // uniform
+        int I = 0, J = 0;
+        tile_of(t, &I, &J);
+        GramFrags<0, KROW> f;
+        f.load(Kraw, I, J, lr, lg);
+        const f32x4 acc = f.product();
+        const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
+        const float bcol = bs[16 * J + lr];
+        double gcol = 0.0;
+        if constexpr (GT) gcol = GR::G(Kraw, 16 * J + lr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * I + 4 * lg + r, j = 16 * J + lr;
+            float a = acc[r];
+            if constexpr (GT) {
+                const double d = GR::G(Kraw, i) - gcol;
+                a *= __expf(static_cast<float>(i > j ? d : -d));
+            }
+            Ts[TL::off(i, j)] = (i > j) ? bet[r] * a : (i == j ? 1.f : bcol * a);
+        }
+    }
+}
+
+// X(i, j) = dT_ij + (dW K^T)_ij beta_j e^{G_j} + (dU V^T)_ij beta_j for i > j, 0 otherwise, for
+// the tiles (I, J0 .. J1); K rows from LDS, V rows from the swizzled staging.
+template <bool GT, bool DT>
+__device__ __attribute__((always_inline)) void x_row(const Params& p, const RowFrags& f, int I, int J0, int J1, const unsigned char* Kraw,
+                      const unsigned char* Vst, const float* bs, float* Xs, int64_t tok0, int n, int hv, int lr,
+                      int lg)
+{
+    const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+    const __amdgpu_buffer_rsrc_t dtr = rsrc(DT ? p.dT + (tok0 * p.hv + hv) * kC : nullptr,
+                                            DT ? (n - 1) * static_cast<uint32_t>(p.hv) * kC * 4 + kC * 4 : 0u);
+    for (int J = J0; J <= J1; ++J) {  // uniform
+        f32x4 pw = zero4(), pu = zero4();
+#pragma unroll
+        for (int s = 0; s < kD / 32; ++s) {
+            const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Kb + (16 * J + lr) * KROW + 32 * s + 8 * lg);
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Vst + (16 * J + lr) * 256 + 16 * ((4 * s + lg) ^ lr));
+            pw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[s], bk, pw, 0, 0, 0);
+            pu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.u[s], bv, pu, 0, 0, 0);
+        }
+        const int j = 16 * J + lr;
+        const float bj = bs[j];
+        const float ej = GT ? GR::E(Kraw, j) : 1.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int i = 16 * I + 4 * lg + rr;
+            float x = 0.f;
+            if (i > j) {
+                float dt = 0.f;
+                if constexpr (DT)
+                    dt = __builtin_bit_cast(float,
+                                            __builtin_amdgcn_raw_buffer_load_b32(dtr, i * p.hv * kC * 4 + j * 4, 0, 0));
+                x = dt + pw[rr] * bj * ej + pu[rr] * bj;
+            }
+            Xs[TL::off(i, j)] = x;
+        }
+    }
+}
+
+// Rows [0, n) of C staged bf16 rows (KROW elements) at `src` to a [tokens, heads, 128] tensor.
+__device__ __attribute__((always_inline)) void store_rows(const unsigned char* src, __bf16* out, int64_t tok0, int n, int heads, int head,
+                                  int tid)
+{
+    const uint32_t stride = static_cast<uint32_t>(heads) * kD * 2;
+    const __amdgpu_buffer_rsrc_t r = rsrc(out + (tok0 * heads + head) * kD, (n - 1) * stride + kD * 2);
+#pragma unroll
+    for (int it = 0; it < kC * 16 / kBT; ++it) {
+        const int q = tid + it * kBT;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(src + (q >> 4) * (KROW * 2) + (q & 15) * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(val, r, (q >> 4) * stride + (q & 15) * 16, 0, kStream);
+    }
+}
+
+// Accumulators acc[mi] of wave ni (element r of lane 16 g + c: row 16 mi + c, column 16 ni + 4 g
+// + r) as bf16 into staged rows at `dst`.
+__device__ __attribute__((always_inline)) void stage_cols(unsigned char* dst, const f32x4 (&acc)[kNB], int ni, int lr, int lg)
+{
+    __bf16* d = reinterpret_cast<__bf16*>(dst);
+#pragma unroll
+    for (int mi = 0; mi < kNB; ++mi) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[mi][r]);
+        *reinterpret_cast<bf16x4*>(d + (16 * mi + lr) * KROW + 16 * ni + 4 * lg) = o;
+    }
+}
+
+__device__ inline float sum_lane_groups(float x)
+{
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <bool GT>
+__global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char* Kraw = smem + OFF_K;
+    float* Ts = reinterpret_cast<float*>(smem + OFF_T);
+    float* Xs = reinterpret_cast<float*>(smem + OFF_XR);
+    float* bs = reinterpret_cast<float*>(smem + OFF_B);
+    double* Gd = reinterpret_cast<double*>(smem + OFF_GD);
+    int* info = reinterpret_cast<int*>(smem + OFF_INFO);
+
+    const int tid = threadIdx.x;
+
+    wyp::Params mp{};
+    mp.cu = p.cu;
+    mp.units = p.units;
+    mp.seqlen = p.seqlen;
+    mp.hq = p.hq;
+    mp.hv = p.hq;
+    mp.num_seqs = p.num_seqs;
+    const int r = p.hv / p.hq;
+    // Persistent, one resident round dealt round-robin to the 8 XCDs (as the C = 32 / 64 kernel).
+    const uint32_t G = gridDim.x;  // a multiple of 8
+    int64_t logical = static_cast<int64_t>(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3);
+    BatchWalk walk{};
+    Unit u;
+    if (p.cu == nullptr) {  // uniform
+        walk.init(static_cast<uint32_t>(logical), G, static_cast<uint32_t>(p.hq),
+                  static_cast<uint32_t>((p.seqlen + kC - 1) / kC));
+        u = walk.unit<kC>(p.seqlen, logical < p.units);
+    } else {
+        u = map_unit<kC>(mp, info, logical, G, tid);
+    }
+    if (u.n <= 0) return;  // uniform
+    int hv = u.hv * r;
+    bool new_unit = true;
+    Next<GT> in;
+    in.issue(p, u.tok0, u.n, u.hv, hv, true, tid);
+    f32x4 dk_acc[kNB];
+#pragma unroll
+    for (int mi = 0; mi < kNB; ++mi) dk_acc[mi] = zero4();
+
+    // inlined at both calls: a call would keep every captured array in scratch memory
+    auto job = [&]() __attribute__((always_inline)) -> bool {
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));  // per-lane LDS addresses are formed where used, not held
+        const int lane = tid & 63, wave = uniform(tid >> 6);
+        const int lr = lane & 15, lg = lane >> 4;
+        const int hk = u.hv;
+        const int64_t tok0 = u.tok0;
+        const int n = u.n;
+        const bool last_head = hv == (hk + 1) * r - 1;  // uniform
+
+        in.commit(Kraw, bs, Gd, new_unit, tid);
+        __syncthreads();
+        Unit nu = u;
+        int nhv = hv + 1;
+        bool nnew = false;
+        if (nhv == (hk + 1) * r) {  // uniform
+            logical += G;
+            if (p.cu == nullptr) {  // uniform
+                walk.step();
+                nu = walk.unit<kC>(p.seqlen, logical < p.units);
+            } else {
+                nu = map_unit<kC>(mp, info, logical, G, tid);
+            }
+            nhv = nu.hv * r;
+            nnew = true;
+        }
+
+        // ---- this job's V rows and the X waves' dW / dU row fragments in flight; A meanwhile
+        VRows vin;
+        vin.issue(p, tok0, n, hv, tid);
+        RowFrags fa, fb;
+        int segI[2] = {-1, -1}, segJ0[2] = {0, 0}, segJ1[2] = {0, 0};
+        if (wave >= 2) {  // uniform
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int I = kXSeg[wave - 2][s][0];
+                segI[s] = I == 255 ? -1 : I;
+                segJ0[s] = kXSeg[wave - 2][s][1];
+                segJ1[s] = kXSeg[wave - 2][s][2];
+            }
+            fa.issue(p, tok0, n, hv, segI[0], lr, lg);
+            fb.issue(p, tok0, n, hv, segI[1], lr, lg);
+        }
+        form_a<GT>(Kraw, Ts, bs, wave, lr, lg);
+        vin.commit(smem + OFF_V, tid);
+        __syncthreads();
+
+        // ---- waves 0-1 invert the diagonal blocks (the chain, at raised priority); waves 2-7 form X
+        if (wave < 2) {  // uniform
+            __builtin_amdgcn_s_setprio(2);
+            invert_diagonal_blocks<kC, TL>(Ts, tid);
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            auto xs = [&](auto with_dt) {
+                constexpr bool DT = decltype(with_dt)::value;
+                x_row<GT, DT>(p, fa, segI[0], segJ0[0], segJ1[0], Kraw, smem + OFF_V, bs, Xs, tok0, n, hv, lr, lg);
+                if (segI[1] >= 0)  // uniform
+                    x_row<GT, DT>(p, fb, segI[1], segJ0[1], segJ1[1], Kraw, smem + OFF_V, bs, Xs, tok0, n, hv, lr,
+                                  lg);
+            };
+            if (p.dT != nullptr)  // uniform
+                xs(std::true_type{});
+            else
+                xs(std::false_type{});
+        }
+        __syncthreads();
+        // ---- coupling levels on waves 0-3; the others issue the next job's loads meanwhile
+        if (wave >= 4) in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // uniform
+        coupling_level<kC, 16, TL>(Ts, tid);
+        coupling_level<kC, 32, TL>(Ts, tid);
+        coupling_level<kC, 64, TL>(Ts, tid);
+        if (wave < 4) in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // uniform
+
+        // ---- Y = X T^T, lower tiles, in registers; then over X as one 16-byte chunk per lane
+        f32x4 yt[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            yt[s] = zero4();
+            const int code = kYTiles[wave][s];
+            if (code != 255) {  // uniform
+                const int Mt = code >> 3, J = code & 7;
+                for (int L = 0; L <= J; ++L) {  // Y(Mt, J) = sum_{L <= J} X(Mt, L) T(J, L)^T
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(Xs + TL::off(16 * Mt + lr, 16 * L + 4 * lg));
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(Ts + TL::off(16 * J + lr, 16 * L + 4 * lg));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) yt[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], yt[s], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int code = kYTiles[wave][s];
+            if (code != 255)  // uniform
+                *reinterpret_cast<f32x4*>(Xs + TL::off(16 * (code >> 3), 16 * (code & 7)) + 4 * lane) = yt[s];
+        }
+        __syncthreads();
+
+        // ---- M = strictLower(-T^T Y) by tiles, and the elementwise step: R = D (Gamma o M) kept in
+        // registers, the row and column sums of Q = M o H (H formed again from K) into this wave's
+        // slots.  Tile element r of lane 16 g + c is (16 I + 4 g + r, 16 J + c).
+        {
+            float* srow = sum_slot(smem, 0, wave);
+            float* scol = sum_slot(smem, 1, wave);
+            float* scr = reinterpret_cast<float*>(smem + OFF_PAN + wave * 2048);
+            srow[lane] = srow[lane + 64] = 0.f;
+            scol[lane] = scol[lane + 64] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                yt[s] = zero4();  // R of this slot
+                const int code = kYTiles[wave][s];
+                if (code != 255) {  // uniform
+                    const int I = 7 - (code & 7), J = 7 - (code >> 3);
+                    f32x4 acc = zero4();
+                    for (int Mt = I; Mt < kNB; ++Mt) {  // (T^T Y)(I, J) = sum_{Mt >= I} T(Mt, I)^T Y(Mt, J)
+                        f32x4 a;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) a[q] = Ts[TL::off(16 * Mt + 4 * lg + q, 16 * I + lr)];
+                        const f32x4 b = *reinterpret_cast<const f32x4*>(Xs + TL::off(16 * Mt, 16 * J) + 4 * lane);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
+                    }
+                    GramFrags<0, KROW> gf;
+                    gf.load(Kraw, I, J, lr, lg);
+                    const f32x4 gr = gf.product();
+                    const f32x4 bi = *reinterpret_cast<const f32x4*>(bs + 16 * I + 4 * lg);
+                    const int j = 16 * J + lr;
+                    double gj = 0.0;
+                    if constexpr (GT) gj = Gd[j];
+                    f32x4 q4;
+                    float colp = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = 16 * I + 4 * lg + rr;
+                        const bool ok = I > J || i > j;
+                        float gam = 1.f;
+                        if constexpr (GT) gam = __expf(static_cast<float>(Gd[i] - gj));
+                        const float m = -acc[rr];
+                        yt[s][rr] = ok ? bi[rr] * gam * m : 0.f;
+                        q4[rr] = ok ? m * (gam * gr[rr]) : 0.f;
+                        colp += bi[rr] * q4[rr];
+                    }
+                    // row sums through this wave's 16 x 20 transpose tile (its LDS operations run in order)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) scr[(4 * lg + rr) * 20 + lr] = q4[rr];
+                    const f32x4 qt = *reinterpret_cast<const f32x4*>(scr + lr * 20 + 4 * lg);
+                    const float rowp = sum_lane_groups(qt[0] + qt[1] + qt[2] + qt[3]);
+                    colp = sum_lane_groups(colp);
+                    if (lg == 0) {
+                        srow[16 * I + lr] += rowp;
+                        scol[16 * J + lr] += colp;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {  // R over Y
+            const int code = kYTiles[wave][s];
+            if (code != 255) {  // uniform
+                const int I = 7 - (code & 7), J = 7 - (code >> 3);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Xs[TL::off(16 * I + 4 * lg + rr, 16 * J + lr)] = yt[s][rr];
+            }
+        }
+        __syncthreads();
+
+        // ---- wave ni: T^T dW and T^T dU for dk columns 16 ni .. + 15, over 32-token panels of its
+        // own columns of dW and dU; then dK += D E T^T dW, dV = D T^T dU and the per-row sums
+        const int ni = wave;
+        {
+            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+            unsigned char* pan = smem + OFF_PAN + wave * 2048;  // [0, 1 KB): dW, [1 KB, 2 KB): dU
+            const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
+            const uint32_t bytes = (n - 1) * stride + kD * 2;
+            const __amdgpu_buffer_rsrc_t vr = rsrc(p.v + (tok0 * p.hv + hv) * kD, bytes);
+            const __amdgpu_buffer_rsrc_t wr = rsrc(p.dW + (tok0 * p.hv + hv) * kD, bytes);
+            const __amdgpu_buffer_rsrc_t ur = rsrc(p.dU + (tok0 * p.hv + hv) * kD, bytes);
+            u32x2 vv[kNB];
+#pragma unroll
+            for (int mi = 0; mi < kNB; ++mi)
+                vv[mi] = __builtin_amdgcn_raw_buffer_load_b64(vr, (16 * mi + lr) * stride + (16 * ni + 4 * lg) * 2, 0,
+                                                              kStream);
+            const uint32_t poff = (lane >> 1) * stride + (16 * ni + 8 * (lane & 1)) * 2;
+            u32x4 pw = __builtin_amdgcn_raw_buffer_load_b128(wr, poff, 0, kStream);
+            u32x4 pu = __builtin_amdgcn_raw_buffer_load_b128(ur, poff, 0, kStream);
+            f32x4 aw[kNB], au[kNB];
+#pragma unroll
+            for (int mi = 0; mi < kNB; ++mi) aw[mi] = au[mi] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < kC / 32; ++ks) {
+                *reinterpret_cast<u32x4*>(pan + (lane >> 1) * 32 + (lane & 1) * 16) = pw;
+                *reinterpret_cast<u32x4*>(pan + 1024 + (lane >> 1) * 32 + (lane & 1) * 16) = pu;
+                if (ks + 1 < kC / 32) {
+                    pw = __builtin_amdgcn_raw_buffer_load_b128(wr, poff + 32 * (ks + 1) * stride, 0, kStream);
+                    pu = __builtin_amdgcn_raw_buffer_load_b128(ur, poff + 32 * (ks + 1) * stride, 0, kStream);
+                }
+                const bf16x8 xw = tr_frag<16>(reinterpret_cast<const __bf16*>(pan), 0, 0, lr, lg);
+                const bf16x8 xu = tr_frag<16>(reinterpret_cast<const __bf16*>(pan + 1024), 0, 0, lr, lg);
+                const int t0 = 32 * ks + 8 * lg;
+#pragma unroll
+                for (int mi = 0; mi <= 2 * ks + 1; ++mi) {
+                    // B fragment: T(t0 .. t0 + 7, 16 mi + c); rows of a tile above the diagonal are 0
+                    const bool in = (t0 >> 4) >= mi;
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const float tv = Ts[TL::off(in ? t0 + jj : 16 * mi, 16 * mi + lr)];
+                        x[jj] = in ? tv : 0.f;
+                    }
+                    unsigned h[4], l[4];
+                    split_hilo<8>(x, h, l);
+                    const bf16x8 bh = cat_u32(h[0], h[1], h[2], h[3]);
+                    const bf16x8 bl = cat_u32(l[0], l[1], l[2], l[3]);
+                    aw[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, bh, aw[mi], 0, 0, 0);
+                    au[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xu, bh, au[mi], 0, 0, 0);
+                    aw[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, bl, aw[mi], 0, 0, 0);
+                    au[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xu, bl, au[mi], 0, 0, 0);
+                }
+            }
+            // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
+            float* ssk = sum_slot(smem, 2, wave);
+            float* ssv = sum_slot(smem, 3, wave);
+#pragma unroll
+            for (int mi = 0; mi < kNB; ++mi) {
+                const int i = 16 * mi + lr;
+                const float bi = bs[i];
+                const float ei = GT ? GR::E(Kraw, i) : 1.f;
+                const bf16x4 kv = *reinterpret_cast<const bf16x4*>(Kb + i * KROW + 16 * ni + 4 * lg);
+                const bf16x4 vb = __builtin_bit_cast(bf16x4, vv[mi]);
+                float sk = 0.f, sv = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    sk += aw[mi][rr] * static_cast<float>(kv[rr]);
+                    sv += au[mi][rr] * static_cast<float>(vb[rr]);
+                    dk_acc[mi][rr] += bi * ei * aw[mi][rr];
+                    au[mi][rr] *= bi;  // dV
+                }
+                sk = sum_lane_groups(sk);
+                sv = sum_lane_groups(sv);
+                if (lg == 0) {
+                    ssk[i] = sk;
+                    ssv[i] = sv;
+                }
+            }
+            __syncthreads();  // every read of T is done
+            stage_cols(smem + OFF_T, au, ni, lr, lg);  // dV rows over T
+        }
+
+        // ---- (R + R^T) K into dK: S(t, i) = R(t, i) below the diagonal and R(i, t) above, read
+        // from the tile-packed R (fp32) and split into hi / lo bf16
+        {
+            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+#pragma unroll
+            for (int ks = 0; ks < kC / 32; ++ks) {
+                const bf16x8 xk = tr_frag<KROW>(Kb, 32 * ks, ni, lr, lg);
+                const int t0 = 32 * ks + 8 * lg;
+#pragma unroll
+                for (int mi = 0; mi < kNB; ++mi) {
+                    const int i = 16 * mi + lr;
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int t = t0 + jj;
+                        x[jj] = Xs[TL::off(t > i ? t : i, t > i ? i : t)];  // R(i, i) = 0
+                    }
+                    unsigned h[4], l[4];
+                    split_hilo<8>(x, h, l);
+                    dk_acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xk, cat_u32(h[0], h[1], h[2], h[3]), dk_acc[mi], 0, 0, 0);
+                    dk_acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xk, cat_u32(l[0], l[1], l[2], l[3]), dk_acc[mi], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+
+        store_rows(smem + OFF_T, p.dv, tok0, n, p.hv, hv, tid);  // dV out
+        if (last_head) {  // uniform: dK of the unit staged over R
+            stage_cols(smem + OFF_XR, dk_acc, ni, lr, lg);
+#pragma unroll
+            for (int mi = 0; mi < kNB; ++mi) dk_acc[mi] = zero4();
+        }
+        if (wave == 0) {
+            // dbeta_i = sum_d (T^T dW)_id e^{G_i} K_id + sum_d (T^T dU)_id V_id + sum_j M_ij H_ij;
+            // dG_i = beta_i e^{G_i} sum_d (T^T dW)_id K_id + beta_i sum_j M_ij H_ij - sum_j beta_j M_ji H_ji;
+            // lane l takes rows l and l + 64
+            float dG[2];
+            const __amdgpu_buffer_rsrc_t br = rsrc(p.dbeta + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = lane + 64 * h;
+                float sk = 0.f, sv = 0.f, mh = 0.f, cz = 0.f;
+#pragma unroll
+                for (int w = 0; w < kBW; ++w) {  // the waves' slots in a fixed order
+                    mh += sum_slot(smem, 0, w)[i];
+                    cz += sum_slot(smem, 1, w)[i];
+                    sk += sum_slot(smem, 2, w)[i];
+                    sv += sum_slot(smem, 3, w)[i];
+                }
+                const float bi = bs[i];
+                const float ei = GT ? GR::E(Kraw, i) : 1.f;
+                const float db = sk * ei + sv + mh;
+                dG[h] = bi * ei * sk + bi * mh - cz;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, db), br, i * p.hv * 4, 0, 0);
+            }
+            if constexpr (GT) {
+                // dg_t = sum_{i >= t} dG_i: reverse inclusive scans of the two halves, the second
+                // half's total added to the first
+#pragma unroll
+                for (int h = 1; h >= 0; --h) {
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const float t = __shfl_down(dG[h], d);
+                        if (lane + d < 64) dG[h] += t;
+                    }
+                }
+                dG[0] += __shfl(dG[1], 0);
+                const __amdgpu_buffer_rsrc_t gr = rsrc(p.dg + tok0 * p.hv + hv, ((n - 1) * p.hv + 1) * 4);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, dG[h]), gr,
+                                                          (lane + 64 * h) * p.hv * 4, 0, 0);
+            }
+        }
+        // every read of this job's LDS (T, XR, sums, K, beta) is done past this barrier, so the next
+        // job's commit and V staging may overwrite them; the staged dk is read below and only
+        // rewritten after the next job's second barrier
+        __syncthreads();
+        if (last_head) store_rows(smem + OFF_XR, p.dk, tok0, n, p.hq, hk, tid);  // uniform
+        u = nu;
+        hv = nhv;
+        new_unit = nnew;
+        return u.n > 0;
+    };
+    if (job()) {
+        while (job()) {
+        }
+    }
+}
+
+template <bool GT>
+int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
+{
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t setup_err[kMaxDevices];
+    static int resident[kMaxDevices];
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e == hipSuccess && (device < 0 || device >= kMaxDevices)) e = hipErrorInvalidDevice;
+    if (e == hipSuccess) {
+        std::call_once(once[device], [&] {
+            const void* kern = reinterpret_cast<const void*>(wy_backward128_kernel<GT>);
+            hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+            int cus = 0, per_cu = 0;
+            if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+            if (err == hipSuccess) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBT, LDS_TOTAL);
+            resident[device] = (per_cu > 0 ? per_cu : 1) * cus;
+            setup_err[device] = err;
+        });
+        e = setup_err[device];
+    }
+    if (e == hipSuccess) {
+        Params p;
+        p.k = static_cast<const __bf16*>(a.k);
+        p.v = static_cast<const __bf16*>(a.v);
+        p.beta = a.beta;
+        p.g = a.g;
+        p.cu = a.cu_seqlens;
+        p.dT = a.dT;
+        p.dW = static_cast<const __bf16*>(a.dW);
+        p.dU = static_cast<const __bf16*>(a.dU);
+        p.dk = static_cast<__bf16*>(a.dk);
+        p.dv = static_cast<__bf16*>(a.dv);
+        p.dbeta = a.dbeta;
+        p.dg = a.dg;
+        p.units = a.chunk_slots * a.num_qk_heads;
+        p.seqlen = a.seqlen;
+        p.hq = a.num_qk_heads;
+        p.hv = a.num_v_heads;
+        p.num_seqs = a.num_seqs;
+        int64_t grid = (p.units + 7) / 8 * 8;
+        const int64_t cap = static_cast<int64_t>(resident[device]) / 8 * 8;
+        if (cap >= 8 && grid > cap) grid = cap;
+        hipLaunchKernelGGL((wy_backward128_kernel<GT>), dim3(static_cast<uint32_t>(grid)), dim3(kBT), LDS_TOTAL,
+                           stream, p);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) {
+        std::snprintf(msg, msg_len, "%s (wy_backward, C=128, gated=%d)", hipGetErrorString(e), GT ? 1 : 0);
+        return static_cast<int>(e);
+    }
+    return 0;
+}
+
+}  // namespace c128
+
 }  // namespace bwd
 
 }  // namespace
@@ -910,6 +1630,8 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 int launch_bwd(const BwdArgs& a, void* stream, char* msg, int msg_len)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.chunk_size == 128)
+        return a.g != nullptr ? bwd::c128::launch_t<true>(a, s, msg, msg_len) : bwd::c128::launch_t<false>(a, s, msg, msg_len);
     if (a.chunk_size == 32)
         return a.g != nullptr ? bwd::launch_t<32, true>(a, s, msg, msg_len) : bwd::launch_t<32, false>(a, s, msg, msg_len);
     return a.g != nullptr ? bwd::launch_t<64, true>(a, s, msg, msg_len) : bwd::launch_t<64, false>(a, s, msg, msg_len);

@@ -201,9 +201,6 @@ wyp_status validate_bwd(const wyp_problem* p, const void* k, const void* v, cons
     if (st != WYP_OK || *empty) return st;
     if (p->kv_dtype != WYP_BF16)
         return fail(WYP_ERR_UNSUPPORTED, "wyp_wy_backward is built for bf16 k, v only");
-    if (p->chunk_size != 32 && p->chunk_size != 64)
-        return fail(WYP_ERR_UNSUPPORTED, "wyp_wy_backward is built for chunk_size 32 and 64 (got %d)",
-                    p->chunk_size);
     if (!dk || !dv || !dbeta) return fail(WYP_ERR_INVALID_ARGUMENT, "dk, dv and dbeta must be non-NULL");
     if (g && !dg) return fail(WYP_ERR_INVALID_ARGUMENT, "dg must be non-NULL when g is given");
     if (!aligned(dk, 16) || !aligned(dv, 16))

@@ -80,7 +80,7 @@ struct BwdArgs {
     int32_t num_qk_heads;
     int32_t num_v_heads;
     int32_t num_seqs;
-    int32_t chunk_size;        // C: 32 or 64
+    int32_t chunk_size;        // C: 32, 64 or 128
     int64_t chunk_slots;
 };
 

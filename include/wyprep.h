@@ -265,9 +265,8 @@ wyp_status wyp_chunk_fwd_cp_noalloc(const wyp_problem* problem, const void* q, c
  *   dk_out  [B, T, Hq, dk], dv_out [B, T, Hv, dv]   kv_dtype
  *   dbeta_out [B, T, Hv] float32;  dg_out [B, T, Hv] float32, required when g is given (else
  *           ignored)
- * Supported: kv_dtype WYP_BF16, chunk_size 32 or 64, dk = dv = 128 (else WYP_ERR_UNSUPPORTED;
- * at C = 128 the operands of one job do not fit a workgroup's 160 KiB of LDS in this kernel's
- * plan).  Alignment: k, v, dW, dU, dk_out, dv_out 16 bytes; beta, g, dT, dbeta_out, dg_out 4
+ * Supported: kv_dtype WYP_BF16, chunk_size 32, 64 or 128, dk = dv = 128 (else
+ * WYP_ERR_UNSUPPORTED).  Alignment: k, v, dW, dU, dk_out, dv_out 16 bytes; beta, g, dT, dbeta_out, dg_out 4
  * bytes.  Results are deterministic (fixed reduction order, no atomics). */
 wyp_status wyp_wy_backward(const wyp_problem* problem, const void* k, const void* v,
                            const float* g, const float* beta, const int32_t* cu_seqlens,

@@ -40,6 +40,17 @@ CASES = {
                         dT=True, seqlens=[200, 333, 64, 1, 129]),
     "C32_gva8_mu4_dT": dict(C=32, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=16, seed=132,
                             gate_mu=4.0, dT=True, seqlens=[200, 333, 32, 1, 65]),
+    # C = 128: K, T and one C x C region in LDS, V staged while X is formed, dW / dU streamed
+    "C128_B2_T333_H4_mu4_dT": dict(C=128, batch=2, seqlen=333, num_qk_heads=4, num_v_heads=4,
+                                   seed=133, gate_mu=4.0, dT=True),
+    "C128_packed_gva_mu0": dict(C=128, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=8, seed=134,
+                                gate_mu=0.0, seqlens=[127, 128, 129, 1, 0, 95, 300]),
+    "C128_T700_H2_ungated_dT": dict(C=128, batch=1, seqlen=700, num_qk_heads=2, num_v_heads=2,
+                                    seed=135, dT=True, beta_sigma=1.5),
+    "C128_gva8_mu4_dT": dict(C=128, batch=1, seqlen=0, num_qk_heads=2, num_v_heads=16, seed=136,
+                             gate_mu=4.0, dT=True, seqlens=[200, 333, 128, 1, 129]),
+    "C128_B1_T512_H2_ungated": dict(C=128, batch=1, seqlen=512, num_qk_heads=2, num_v_heads=2,
+                                    seed=137),
 }
 
 
@@ -90,7 +101,7 @@ def test_wy_backward_small(name, gpu):
     check(inp, dW, dU, dT, out, name)
 
 
-@pytest.mark.parametrize("C", [32, 64])
+@pytest.mark.parametrize("C", [32, 64, 128])
 def test_wy_backward_identical_keys(C, gpu):
     """All keys of a chunk equal: the cancellation case that makes a single bf16 rounding of T
     miss the W tolerance in the forward."""
@@ -103,7 +114,7 @@ def test_wy_backward_identical_keys(C, gpu):
     check(inp, dW, dU, dT, out, "identical keys")
 
 
-@pytest.mark.parametrize("C", [32, 64])
+@pytest.mark.parametrize("C", [32, 64, 128])
 def test_wy_backward_many_short_sequences(C, gpu):
     """1100 packed sequences of 1..C+1 tokens (a few empty): the work map's search and its empty
     slots, on the key-head units of the backward."""
@@ -118,14 +129,15 @@ def test_wy_backward_many_short_sequences(C, gpu):
     check(inp, dW, dU, dT, out, f"1100 short sequences C={C}")
 
 
-@pytest.mark.parametrize("C", [32, 64])
+@pytest.mark.parametrize("C", [32, 64, 128])
 def test_wy_backward_batch_walk(C, gpu):
-    """Batch rows with more units than resident workgroups (432 at C = 64, 846 at C = 32) and 3 key
-    heads, which divides neither grid: each workgroup's division-free walk over its units carries
-    the head into the chunk slot and the chunk slot into the next row, on ragged rows (T = 1500),
-    with two value heads per key head summed into dk."""
-    inp, dW, dU, dT = make_inputs(dict(C=C, batch=6, seqlen=1500, num_qk_heads=3, num_v_heads=6,
-                                       seed=130, gate_mu=4.0, dT=True))
+    """Batch rows with more units than resident workgroups (432 at C = 64 and 128, 846 at C = 32)
+    and 3 key heads, which divides neither grid: each workgroup's division-free walk over its
+    units carries the head into the chunk slot and the chunk slot into the next row, on ragged
+    rows (T = 1500, 3000 at C = 128), with two value heads per key head summed into dk."""
+    inp, dW, dU, dT = make_inputs(dict(C=C, batch=6, seqlen=3000 if C == 128 else 1500,
+                                       num_qk_heads=3, num_v_heads=6, seed=130, gate_mu=4.0,
+                                       dT=True))
     say(f"wy_backward batch walk C={C}")
     out = run_bwd(inp, dW, dU, dT, gpu)
     check(inp, dW, dU, dT, out, f"batch walk C={C}")
@@ -140,7 +152,8 @@ def test_wy_backward_deterministic(gpu):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("mu,C", [(None, 64), (4.0, 64), (None, 32), (4.0, 32)])
+@pytest.mark.parametrize("mu,C", [(None, 64), (4.0, 64), (None, 32), (4.0, 32), (None, 128),
+                                  (4.0, 128)])
 def test_wy_backward_full_size(mu, C, gpu):
     """B=1 T=8192 H=16/16, whole tensors against the oracle."""
     import torch
