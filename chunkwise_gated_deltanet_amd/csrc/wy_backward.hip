@@ -908,12 +908,15 @@ int launch_t(const BwdArgs& a, hipStream_t stream, char* msg, int msg_len)
 // The plan above (K, V, dW, dU, T, H, X and S of one job all in LDS) would take about 390 KB at
 // C = 128.  Here only K, T and one C x C region stay in LDS.  The region holds X, then Y, then R
 // in turn, each hand-over behind a barrier.  V is staged (256-byte rows, 16-byte chunks XOR-
-// swizzled by row) over the scratch that later holds the row sums and the per-wave panels, for
-// as long as X is formed.  The rows of dW and dU enter the X tiles straight from memory.  The
-// products over tokens (T^T dW, T^T dU) stream each wave's own 16 columns of dW and dU through
-// a 32-token panel of that wave.  H is not kept: the elementwise step forms its tiles again
-// from K.  Eight waves, one workgroup per CU; every phase runs on all eight waves, with the
-// fp32 Y and M tiles dealt so that each SIMD gets the same number of MFMAs.
+// swizzled by row) over the scratch that later holds the sums and the per-wave panels, for as
+// long as X is formed; the rows of dW and dU enter the X tiles straight from memory.  H is not
+// kept: the elementwise step forms its tiles again from K.  Once M is known, R and T are written
+// once more as bf16 hi / lo tiles (16 x 16, row-major), so that every operand of the products
+// over tokens (T^T dW, T^T dU and (R + R^T) K) is one or two LDS reads: a transposed read for 8
+// rows of a column, a plain one for 8 entries of a row.  Those products stream each wave's own
+// 16 columns of dW and dU through a 32-token panel of that wave.  Eight waves, one workgroup per
+// CU; every phase runs on all eight waves, the fp32 Y and M tiles dealt so that the waves (and
+// the SIMDs) get equal shares.
 namespace c128 {
 
 constexpr int kC = 128;
@@ -931,25 +934,35 @@ constexpr int OFF_B = OFF_XR + TL::BYTES;     // beta
 constexpr int OFF_GD = OFF_B + kC * 4;        // G, fp64 (gated)
 constexpr int OFF_INFO = OFF_GD + kC * 8;
 constexpr int OFF_V = OFF_INFO + 16;          // V rows while X is formed; after that:
-constexpr int OFF_SUM = OFF_V;                //   row sums, 4 kinds x 8 waves x C floats
-constexpr int OFF_PAN = OFF_SUM + 4 * kBW * kC * 4;  //   2 KB per wave: transpose tile; dW / dU panels
-constexpr int LDS_TOTAL = OFF_PAN + kBW * 2048;
+constexpr int OFF_QS = OFF_V;                 //   per lower tile of Q = M o H: 16 row and 16 column sums
+constexpr int OFF_SUM = OFF_QS + 36 * 32 * 4; //   per wave: sum_d (T^T dW) K and sum_d (T^T dU) V per row
+constexpr int OFF_PAN = OFF_SUM + 2 * kBW * kC * 4;  //   per wave: two 16 x 20 transpose tiles; dW / dU panels
+constexpr int PAN_BYTES = 2 * 16 * 20 * 4;
+constexpr int LDS_TOTAL = OFF_PAN + kBW * PAN_BYTES;
 static_assert(LDS_TOTAL - OFF_V >= kC * kD * 2, "V rows fit over the sums and the panels");
+static_assert(PAN_BYTES >= 2048, "a wave's dW and dU panels fit its transpose tiles");
 static_assert(KB <= TL::BYTES, "dv and dk are staged as bf16 rows over T and XR");
 static_assert(OFF_V % 16 == 0 && OFF_PAN % 16 == 0, "16-byte aligned regions");
 static_assert(LDS_TOTAL <= 160 * 1024, "C = 128 backward LDS plan exceeds 160 KiB");
+static_assert(2 * 36 * 512 <= TL::BYTES, "T and R fit as bf16 hi / lo tiles over their fp32 regions");
 
-// Sum slots: kind 0 = sum_j M_ij H_ij (row i), 1 = sum_i beta_i M_ij H_ij (column j), 2 = sum_d
-// (T^T dW)_id K_id, 3 = sum_d (T^T dU)_id V_id; one row of C floats per (kind, wave).
+// Row sums of the products over tokens: kind 0 = sum_d (T^T dW)_id K_id, 1 = sum_d (T^T dU)_id V_id;
+// one row of C floats per (kind, wave).
 __device__ inline float* sum_slot(unsigned char* smem, int kind, int wave)
 {
     return reinterpret_cast<float*>(smem + OFF_SUM) + (kind * kBW + wave) * kC;
 }
 
+// Sums of the lower tile t = I (I + 1) / 2 + J of Q = M o H: [0, 16) row sums sum_j Q_ij over the
+// tile's columns, [16, 32) column sums sum_i beta_i Q_ij over its rows.
+__device__ inline float* q_slot(unsigned char* smem, int t)
+{
+    return reinterpret_cast<float*>(smem + OFF_QS) + t * 32;
+}
+
 // Lower tiles (Mt, J) of Y = X T^T per wave, as 8 Mt + J (255 ends a list).  Tile (Mt, J) costs
 // J + 1 steps of four fp32 MFMAs, so every wave gets 15 steps and each SIMD (waves w and w + 4)
-// 30.  The M tiles use the same lists mirrored: entry (Mt, J) stands for M tile (7 - J, 7 - Mt),
-// whose cost 8 - I is again J + 1.
+// 30.
 __constant__ unsigned char kYTiles[kBW][8] = {
     {63, 54, 255, 255, 255, 255, 255, 255},  // (7,7) (6,6)
     {62, 45, 9, 255, 255, 255, 255, 255},    // (7,6) (5,5) (1,1)
@@ -959,6 +972,20 @@ __constant__ unsigned char kYTiles[kBW][8] = {
     {43, 51, 59, 33, 8, 255, 255, 255},      // (5,3) (6,3) (7,3) (4,1) (1,0)
     {18, 26, 34, 41, 49, 16, 24, 255},       // (2,2) (3,2) (4,2) (5,1) (6,1) (2,0) (3,0)
     {42, 50, 58, 57, 32, 40, 48, 56},        // (5,2) (6,2) (7,2) (7,1) (4,0) (5,0) (6,0) (7,0)
+};
+
+// Lower tiles (I, J) of M per wave, as 8 I + J (255 ends a list).  Tile (I, J) costs 8 - I steps of
+// four fp32 MFMAs plus a fixed cost of about four steps (its Gram, the elementwise step and the
+// transposes); four or five tiles per wave, 30 to 34 of these units each.
+__constant__ unsigned char kMTiles[kBW][5] = {
+    {52, 53, 45, 0, 255},  // (6,4) (6,5) (5,5) (0,0)
+    {58, 41, 33, 9, 255},  // (7,2) (5,1) (4,1) (1,1)
+    {61, 40, 35, 8, 255},  // (7,5) (5,0) (4,3) (1,0)
+    {48, 44, 34, 17, 255}, // (6,0) (5,4) (4,2) (2,1)
+    {62, 50, 54, 36, 18},  // (7,6) (6,2) (6,6) (4,4) (2,2)
+    {57, 60, 42, 32, 16},  // (7,1) (7,4) (5,2) (4,0) (2,0)
+    {59, 63, 43, 24, 27},  // (7,3) (7,7) (5,3) (3,0) (3,3)
+    {56, 49, 51, 25, 26},  // (7,0) (6,1) (6,3) (3,1) (3,2)
 };
 
 // X tiles while waves 0-1 invert the diagonal blocks: waves 2-7 take row segments (I, J0, J1),
@@ -976,7 +1003,8 @@ struct Next {
     float b;
     float g[2];  // wave 0 lane l: g of rows l and l + 64
 
-    __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hk, int hv, bool with_k, int tid)
+    __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hk, int hv,
+                                                         bool with_k, int tid)
     {
         const uint32_t kstride = static_cast<uint32_t>(p.hq) * kD * 2;
         const int nk = with_k ? n : 0;  // n = 0 (no job): empty ranges, every load reads 0
@@ -1002,7 +1030,8 @@ struct Next {
 
     // K rows (new unit only), beta, and G = inclusive prefix sums of g in fp64 by wave 0, in the
     // forward's order (each half of the chunk scanned, the first half's total added to the second)
-    __device__ __attribute__((always_inline)) void commit(unsigned char* Kraw, float* bs, double* Gd, bool with_k, int tid) const
+    __device__ __attribute__((always_inline)) void commit(unsigned char* Kraw, float* bs, double* Gd, bool with_k,
+                                                          int tid) const
     {
         if (with_k) {
 #pragma unroll
@@ -1043,7 +1072,8 @@ struct VRows {
     __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hv, int tid)
     {
         const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
-        const __amdgpu_buffer_rsrc_t vr = rsrc(p.v + (tok0 * p.hv + hv) * kD, (n - 1) * stride + kD * 2);
+        const __amdgpu_buffer_rsrc_t vr =
+            rsrc(p.v + (tok0 * p.hv + hv) * kD, n > 0 ? (n - 1) * stride + kD * 2 : 0u);  // n = 0: reads 0
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int q = tid + it * kBT;
@@ -1062,14 +1092,14 @@ struct VRows {
 };
 
 // A fragments of rows 16 I .. 16 I + 15 of dW and dU (lane 16 g + c: row 16 I + c, dk 32 s + 8 g
-// .. + 7), straight from memory; I < 0 reads nothing.
+// .. + 7), straight from memory; I < 0 or n = 0 reads nothing.
 struct RowFrags {
     bf16x8 w[kD / 32], u[kD / 32];
 
     __device__ __attribute__((always_inline)) void issue(const Params& p, int64_t tok0, int n, int hv, int I, int lr, int lg)
     {
         const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
-        const uint32_t bytes = I >= 0 ? (n - 1) * stride + kD * 2 : 0u;
+        const uint32_t bytes = I >= 0 && n > 0 ? (n - 1) * stride + kD * 2 : 0u;
         const __amdgpu_buffer_rsrc_t wr = rsrc(p.dW + (tok0 * p.hv + hv) * kD, bytes);
         const __amdgpu_buffer_rsrc_t ur = rsrc(p.dU + (tok0 * p.hv + hv) * kD, bytes);
         const uint32_t off = (16 * (I >= 0 ? I : 0) + lr) * stride + 16 * lg;
@@ -1176,6 +1206,23 @@ __device__ __attribute__((always_inline)) void stage_cols(unsigned char* dst, co
     }
 }
 
+// 16 x 16 bf16 tiles with rows of 32 bytes.  tile_col8: lane 16 g + c gets column c of rows
+// 8 (g & 1) .. + 7 (two transposed LDS reads); tile_row8: row c, columns 8 (g & 1) .. + 7.
+constexpr int kTileBf = 16 * 16 * 2;
+
+__device__ inline bf16x8 tile_col8(const unsigned char* tile, int lr, int lg)
+{
+    const unsigned char* p0 = tile + (8 * (lg & 1) + (lr >> 2)) * 32 + 8 * (lr & 3);
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * 32));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline bf16x8 tile_row8(const unsigned char* tile, int lr, int lg)
+{
+    return *reinterpret_cast<const bf16x8*>(tile + lr * 32 + 16 * (lg & 1));
+}
+
 __device__ inline float sum_lane_groups(float x)
 {
     x += __shfl_xor(x, 16);
@@ -1222,11 +1269,25 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
     bool new_unit = true;
     Next<GT> in;
     in.issue(p, u.tok0, u.n, u.hv, hv, true, tid);
+    // The X waves' row segments (fixed per wave).
+    int segI[2] = {-1, -1}, segJ0[2] = {0, 0}, segJ1[2] = {0, 0};
+    {
+        const int wave = uniform(tid >> 6);
+        if (wave >= 2) {  // uniform
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int I = kXSeg[wave - 2][s][0];
+                segI[s] = I == 255 ? -1 : I;
+                segJ0[s] = kXSeg[wave - 2][s][1];
+                segJ1[s] = kXSeg[wave - 2][s][2];
+            }
+        }
+    }
     f32x4 dk_acc[kNB];
 #pragma unroll
     for (int mi = 0; mi < kNB; ++mi) dk_acc[mi] = zero4();
 
-    // inlined at both calls: a call would keep every captured array in scratch memory
+    // inlined (one call): a call would keep every captured array in scratch memory
     auto job = [&]() __attribute__((always_inline)) -> bool {
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));  // per-lane LDS addresses are formed where used, not held
@@ -1254,22 +1315,15 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
             nnew = true;
         }
 
-        // ---- this job's V rows and the X waves' dW / dU row fragments in flight; A meanwhile
+        // ---- this job's V rows and the X waves' dW / dU fragments in flight; A meanwhile.  (Issued
+        // a job ahead instead, from the previous job's end, they measured 3.5% slower: every
+        // workgroup then waits for them at the commit of K, and the registers they hold cost the
+        // last phases more than the head start gains.)
         VRows vin;
         vin.issue(p, tok0, n, hv, tid);
         RowFrags fa, fb;
-        int segI[2] = {-1, -1}, segJ0[2] = {0, 0}, segJ1[2] = {0, 0};
-        if (wave >= 2) {  // uniform
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int I = kXSeg[wave - 2][s][0];
-                segI[s] = I == 255 ? -1 : I;
-                segJ0[s] = kXSeg[wave - 2][s][1];
-                segJ1[s] = kXSeg[wave - 2][s][2];
-            }
-            fa.issue(p, tok0, n, hv, segI[0], lr, lg);
-            fb.issue(p, tok0, n, hv, segI[1], lr, lg);
-        }
+        if (wave >= 2) fa.issue(p, tok0, n, hv, segI[0], lr, lg);  // uniform
+        if (wave >= 4) fb.issue(p, tok0, n, hv, segI[1], lr, lg);  // uniform: waves 4-6 have a second segment
         form_a<GT>(Kraw, Ts, bs, wave, lr, lg);
         vin.commit(smem + OFF_V, tid);
         __syncthreads();
@@ -1293,12 +1347,10 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
                 xs(std::false_type{});
         }
         __syncthreads();
-        // ---- coupling levels on waves 0-3; the others issue the next job's loads meanwhile
-        if (wave >= 4) in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // uniform
+        // ---- coupling levels on waves 0-3
         coupling_level<kC, 16, TL>(Ts, tid);
         coupling_level<kC, 32, TL>(Ts, tid);
         coupling_level<kC, 64, TL>(Ts, tid);
-        if (wave < 4) in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // uniform
 
         // ---- Y = X T^T, lower tiles, in registers; then over X as one 16-byte chunk per lane
         f32x4 yt[8];
@@ -1327,27 +1379,25 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
 
         // ---- M = strictLower(-T^T Y) by tiles, and the elementwise step: R = D (Gamma o M) kept in
         // registers, the row and column sums of Q = M o H (H formed again from K) into this wave's
-        // slots.  Tile element r of lane 16 g + c is (16 I + 4 g + r, 16 J + c).
+        // slots.  Tile element r of lane 16 g + c is (16 I + 4 g + r, 16 J + c) (the m layout);
+        // R leaves the tile transposed (row 16 I + c, columns 16 J + 4 g ..; a diagonal tile
+        // as the symmetric S = R + R^T) and packed into bf16 hi / lo, ready for its row-major
+        // store.
         {
-            float* srow = sum_slot(smem, 0, wave);
-            float* scol = sum_slot(smem, 1, wave);
-            float* scr = reinterpret_cast<float*>(smem + OFF_PAN + wave * 2048);
-            srow[lane] = srow[lane + 64] = 0.f;
-            scol[lane] = scol[lane + 64] = 0.f;
+            float* scr = reinterpret_cast<float*>(smem + OFF_PAN + wave * PAN_BYTES);  // two 16 x 20 tiles
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
+            for (int s = 0; s < 5; ++s) {
                 yt[s] = zero4();  // R of this slot
-                const int code = kYTiles[wave][s];
+                const int code = kMTiles[wave][s];
                 if (code != 255) {  // uniform
-                    const int I = 7 - (code & 7), J = 7 - (code >> 3);
+                    const int I = code >> 3, J = code & 7;
                     f32x4 acc = zero4();
                     for (int Mt = I; Mt < kNB; ++Mt) {  // (T^T Y)(I, J) = sum_{Mt >= I} T(Mt, I)^T Y(Mt, J)
-                        f32x4 a;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) a[q] = Ts[TL::off(16 * Mt + 4 * lg + q, 16 * I + lr)];
+                        const float* tcol = Ts + TL::off(16 * Mt + 4 * lg, 16 * I + lr);
                         const f32x4 b = *reinterpret_cast<const f32x4*>(Xs + TL::off(16 * Mt, 16 * J) + 4 * lane);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], b[q], acc, 0, 0, 0);
+                        for (int q = 0; q < 4; ++q)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tcol[q * TL::RS], b[q], acc, 0, 0, 0);
                     }
                     GramFrags<0, KROW> gf;
                     gf.load(Kraw, I, J, lr, lg);
@@ -1356,7 +1406,7 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
                     const int j = 16 * J + lr;
                     double gj = 0.0;
                     if constexpr (GT) gj = Gd[j];
-                    f32x4 q4;
+                    f32x4 q4, rm;
                     float colp = 0.f;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
@@ -1365,82 +1415,114 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
                         float gam = 1.f;
                         if constexpr (GT) gam = __expf(static_cast<float>(Gd[i] - gj));
                         const float m = -acc[rr];
-                        yt[s][rr] = ok ? bi[rr] * gam * m : 0.f;
+                        rm[rr] = ok ? bi[rr] * gam * m : 0.f;
                         q4[rr] = ok ? m * (gam * gr[rr]) : 0.f;
                         colp += bi[rr] * q4[rr];
                     }
-                    // row sums through this wave's 16 x 20 transpose tile (its LDS operations run in order)
+                    // both tiles transposed through this wave's scratch (its LDS operations run in order)
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) scr[(4 * lg + rr) * 20 + lr] = q4[rr];
+                    for (int rr = 0; rr < 4; ++rr) {
+                        scr[(4 * lg + rr) * 20 + lr] = q4[rr];
+                        scr[320 + (4 * lg + rr) * 20 + lr] = rm[rr];
+                    }
                     const f32x4 qt = *reinterpret_cast<const f32x4*>(scr + lr * 20 + 4 * lg);
+                    f32x4 rt = *reinterpret_cast<const f32x4*>(scr + 320 + lr * 20 + 4 * lg);
                     const float rowp = sum_lane_groups(qt[0] + qt[1] + qt[2] + qt[3]);
                     colp = sum_lane_groups(colp);
                     if (lg == 0) {
-                        srow[16 * I + lr] += rowp;
-                        scol[16 * J + lr] += colp;
+                        float* qs = q_slot(smem, I * (I + 1) / 2 + J);
+                        qs[lr] = rowp;
+                        qs[16 + lr] = colp;
                     }
+                    if (I == J) rt += rm;  // uniform: the diagonal tile as S = R + R^T
+                    yt[s] = __builtin_bit_cast(f32x4, pack_hilo(rt));
                 }
             }
         }
-        __syncthreads();
+        // ---- the products over tokens read T and R as bf16 hi / lo tiles (16 x 16, rows of 32 bytes,
+        // row-major), where a fragment of 8 rows of one column is one transposed LDS read: this
+        // thread's share of T in registers now, written over T past the barrier.
+        f32x4 tpart[5];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {  // R over Y
-            const int code = kYTiles[wave][s];
-            if (code != 255) {  // uniform
-                const int I = 7 - (code & 7), J = 7 - (code >> 3);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) Xs[TL::off(16 * I + 4 * lg + rr, 16 * J + lr)] = yt[s][rr];
-            }
+        for (int it = 0; it < 5; ++it) {
+            const int q = tid + it * kBT;  // 16-byte chunk q of T: tile q >> 6, row (q >> 2) & 15, chunk q & 3
+            tpart[it] = q < 36 * 64 ? *reinterpret_cast<const f32x4*>(Ts + (q >> 6) * TL::TILE + ((q >> 2) & 15) * TL::RS + 4 * (q & 3))
+                                    : zero4();
         }
-        __syncthreads();
-
-        // ---- wave ni: T^T dW and T^T dU for dk columns 16 ni .. + 15, over 32-token panels of its
-        // own columns of dW and dU; then dK += D E T^T dW, dV = D T^T dU and the per-row sums
+        // wave ni's 16 columns of dW and dU for all four 32-token panels, and the V chunks for sv
         const int ni = wave;
+        const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
+        const uint32_t bytes = (n - 1) * stride + kD * 2;
+        u32x4 pw[kC / 32], pu[kC / 32];
+        u32x2 vv[kNB];
         {
-            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
-            unsigned char* pan = smem + OFF_PAN + wave * 2048;  // [0, 1 KB): dW, [1 KB, 2 KB): dU
-            const uint32_t stride = static_cast<uint32_t>(p.hv) * kD * 2;
-            const uint32_t bytes = (n - 1) * stride + kD * 2;
-            const __amdgpu_buffer_rsrc_t vr = rsrc(p.v + (tok0 * p.hv + hv) * kD, bytes);
             const __amdgpu_buffer_rsrc_t wr = rsrc(p.dW + (tok0 * p.hv + hv) * kD, bytes);
             const __amdgpu_buffer_rsrc_t ur = rsrc(p.dU + (tok0 * p.hv + hv) * kD, bytes);
-            u32x2 vv[kNB];
+            const __amdgpu_buffer_rsrc_t vr = rsrc(p.v + (tok0 * p.hv + hv) * kD, bytes);
+            const uint32_t poff = (lane >> 1) * stride + (16 * ni + 8 * (lane & 1)) * 2;
+#pragma unroll
+            for (int ks = 0; ks < kC / 32; ++ks) {
+                pw[ks] = __builtin_amdgcn_raw_buffer_load_b128(wr, poff + 32 * ks * stride, 0, kStream);
+                pu[ks] = __builtin_amdgcn_raw_buffer_load_b128(ur, poff + 32 * ks * stride, 0, kStream);
+            }
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi)
                 vv[mi] = __builtin_amdgcn_raw_buffer_load_b64(vr, (16 * mi + lr) * stride + (16 * ni + 4 * lg) * 2, 0,
                                                               kStream);
-            const uint32_t poff = (lane >> 1) * stride + (16 * ni + 8 * (lane & 1)) * 2;
-            u32x4 pw = __builtin_amdgcn_raw_buffer_load_b128(wr, poff, 0, kStream);
-            u32x4 pu = __builtin_amdgcn_raw_buffer_load_b128(ur, poff, 0, kStream);
+        }
+        __syncthreads();
+        {
+            unsigned char* Rb = smem + OFF_XR;  // R hi tiles, then R lo tiles (36 x 512 bytes each)
+#pragma unroll
+            for (int s = 0; s < 5; ++s) {
+                const int code = kMTiles[wave][s];
+                if (code != 255) {  // uniform
+                    const int I = code >> 3, J = code & 7;
+                    const int off = (I * (I + 1) / 2 + J) * 512 + lr * 32 + 8 * lg;
+                    const u32x4 h = __builtin_bit_cast(u32x4, yt[s]);
+                    *reinterpret_cast<u32x2*>(Rb + off) = u32x2{h[0], h[1]};
+                    *reinterpret_cast<u32x2*>(Rb + kTileBf * 36 + off) = u32x2{h[2], h[3]};
+                }
+            }
+            unsigned char* Tb = smem + OFF_T;  // T hi tiles, then T lo tiles
+#pragma unroll
+            for (int it = 0; it < 5; ++it) {
+                const int q = tid + it * kBT;
+                if (q < 36 * 64) {
+                    const u32x4 h = pack_hilo(tpart[it]);
+                    const int off = (q >> 6) * 512 + ((q >> 2) & 15) * 32 + 8 * (q & 3);
+                    *reinterpret_cast<u32x2*>(Tb + off) = u32x2{h[0], h[1]};
+                    *reinterpret_cast<u32x2*>(Tb + kTileBf * 36 + off) = u32x2{h[2], h[3]};
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- wave ni: T^T dW and T^T dU for dk columns 16 ni .. + 15, over the four 32-token panels
+        // of its own columns of dW and dU (staged in its own 2 KB); then dK += D E T^T dW,
+        // dV = D T^T dU and the per-row sums
+        {
+            const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+            unsigned char* pan = smem + OFF_PAN + wave * PAN_BYTES;  // [0, 1 KB): dW, [1 KB, 2 KB): dU
+            const unsigned char* Tb = smem + OFF_T;
             f32x4 aw[kNB], au[kNB];
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) aw[mi] = au[mi] = zero4();
 #pragma unroll
             for (int ks = 0; ks < kC / 32; ++ks) {
-                *reinterpret_cast<u32x4*>(pan + (lane >> 1) * 32 + (lane & 1) * 16) = pw;
-                *reinterpret_cast<u32x4*>(pan + 1024 + (lane >> 1) * 32 + (lane & 1) * 16) = pu;
-                if (ks + 1 < kC / 32) {
-                    pw = __builtin_amdgcn_raw_buffer_load_b128(wr, poff + 32 * (ks + 1) * stride, 0, kStream);
-                    pu = __builtin_amdgcn_raw_buffer_load_b128(ur, poff + 32 * (ks + 1) * stride, 0, kStream);
-                }
+                *reinterpret_cast<u32x4*>(pan + (lane >> 1) * 32 + (lane & 1) * 16) = pw[ks];
+                *reinterpret_cast<u32x4*>(pan + 1024 + (lane >> 1) * 32 + (lane & 1) * 16) = pu[ks];
                 const bf16x8 xw = tr_frag<16>(reinterpret_cast<const __bf16*>(pan), 0, 0, lr, lg);
                 const bf16x8 xu = tr_frag<16>(reinterpret_cast<const __bf16*>(pan + 1024), 0, 0, lr, lg);
-                const int t0 = 32 * ks + 8 * lg;
+                const int Tt = 2 * ks + (lg >> 1);  // the 16-row tile of this lane group's 8 tokens
 #pragma unroll
                 for (int mi = 0; mi <= 2 * ks + 1; ++mi) {
-                    // B fragment: T(t0 .. t0 + 7, 16 mi + c); rows of a tile above the diagonal are 0
-                    const bool in = (t0 >> 4) >= mi;
-                    float x[8];
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const float tv = Ts[TL::off(in ? t0 + jj : 16 * mi, 16 * mi + lr)];
-                        x[jj] = in ? tv : 0.f;
-                    }
-                    unsigned h[4], l[4];
-                    split_hilo<8>(x, h, l);
-                    const bf16x8 bh = cat_u32(h[0], h[1], h[2], h[3]);
-                    const bf16x8 bl = cat_u32(l[0], l[1], l[2], l[3]);
+                    // B fragment: T(32 ks + 8 g .. + 7, 16 mi + c), 0 for a tile above the diagonal
+                    const bool in = Tt >= mi;
+                    const int tile = in ? Tt * (Tt + 1) / 2 + mi : mi * (mi + 1) / 2 + mi;
+                    bf16x8 bh = tile_col8(Tb + tile * 512, lr, lg);
+                    bf16x8 bl = tile_col8(Tb + kTileBf * 36 + tile * 512, lr, lg);
+                    if (!in) bh = bl = bf16x8{};
                     aw[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, bh, aw[mi], 0, 0, 0);
                     au[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xu, bh, au[mi], 0, 0, 0);
                     aw[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xw, bl, aw[mi], 0, 0, 0);
@@ -1448,8 +1530,8 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
                 }
             }
             // element r of lane 16 g + c: (T^T dW)[i = 16 mi + c][d = 16 ni + 4 g + r]
-            float* ssk = sum_slot(smem, 2, wave);
-            float* ssv = sum_slot(smem, 3, wave);
+            float* ssk = sum_slot(smem, 0, wave);
+            float* ssv = sum_slot(smem, 1, wave);
 #pragma unroll
             for (int mi = 0; mi < kNB; ++mi) {
                 const int i = 16 * mi + lr;
@@ -1476,27 +1558,41 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
             stage_cols(smem + OFF_T, au, ni, lr, lg);  // dV rows over T
         }
 
-        // ---- (R + R^T) K into dK: S(t, i) = R(t, i) below the diagonal and R(i, t) above, read
-        // from the tile-packed R (fp32) and split into hi / lo bf16
+        in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // the next job's K, beta and g
+        // ---- (R + R^T) K into dK.  S(t, i) is R(t, i) below the diagonal tiles (8 rows of one
+        // column of tile (t, i): a transposed read) and R(i, t) above them (8 entries of one row of
+        // tile (i, t)); the diagonal tiles hold S itself, read by rows.
         {
             const __bf16* Kb = reinterpret_cast<const __bf16*>(Kraw);
+            const unsigned char* Rb = smem + OFF_XR;
 #pragma unroll
             for (int ks = 0; ks < kC / 32; ++ks) {
                 const bf16x8 xk = tr_frag<KROW>(Kb, 32 * ks, ni, lr, lg);
-                const int t0 = 32 * ks + 8 * lg;
+                const int Tt = 2 * ks + (lg >> 1);
 #pragma unroll
                 for (int mi = 0; mi < kNB; ++mi) {
-                    const int i = 16 * mi + lr;
-                    float x[8];
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const int t = t0 + jj;
-                        x[jj] = Xs[TL::off(t > i ? t : i, t > i ? i : t)];  // R(i, i) = 0
+                    bf16x8 sh, sl;
+                    if (mi < 2 * ks) {  // every lane group below the diagonal: columns of tiles (Tt, mi)
+                        const int tile = Tt * (Tt + 1) / 2 + mi;
+                        sh = tile_col8(Rb + tile * 512, lr, lg);
+                        sl = tile_col8(Rb + kTileBf * 36 + tile * 512, lr, lg);
+                    } else if (mi > 2 * ks + 1) {  // every lane group above: rows of tiles (mi, Tt)
+                        const int tile = mi * (mi + 1) / 2 + Tt;
+                        sh = tile_row8(Rb + tile * 512, lr, lg);
+                        sl = tile_row8(Rb + kTileBf * 36 + tile * 512, lr, lg);
+                    } else {  // the lane groups of tile mi read rows of the diagonal tile, the others columns
+                        const bool below = Tt > mi;
+                        const int tc = below ? Tt * (Tt + 1) / 2 + mi : mi * (mi + 1) / 2 + mi;
+                        const int tr = mi * (mi + 1) / 2 + (below ? mi : Tt);
+                        const bf16x8 ch = tile_col8(Rb + tc * 512, lr, lg);
+                        const bf16x8 cl = tile_col8(Rb + kTileBf * 36 + tc * 512, lr, lg);
+                        const bf16x8 rh = tile_row8(Rb + tr * 512, lr, lg);
+                        const bf16x8 rl = tile_row8(Rb + kTileBf * 36 + tr * 512, lr, lg);
+                        sh = below ? ch : rh;
+                        sl = below ? cl : rl;
                     }
-                    unsigned h[4], l[4];
-                    split_hilo<8>(x, h, l);
-                    dk_acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xk, cat_u32(h[0], h[1], h[2], h[3]), dk_acc[mi], 0, 0, 0);
-                    dk_acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xk, cat_u32(l[0], l[1], l[2], l[3]), dk_acc[mi], 0, 0, 0);
+                    dk_acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xk, sh, dk_acc[mi], 0, 0, 0);
+                    dk_acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xk, sl, dk_acc[mi], 0, 0, 0);
                 }
             }
         }
@@ -1520,11 +1616,12 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
                 float sk = 0.f, sv = 0.f, mh = 0.f, cz = 0.f;
 #pragma unroll
                 for (int w = 0; w < kBW; ++w) {  // the waves' slots in a fixed order
-                    mh += sum_slot(smem, 0, w)[i];
-                    cz += sum_slot(smem, 1, w)[i];
-                    sk += sum_slot(smem, 2, w)[i];
-                    sv += sum_slot(smem, 3, w)[i];
+                    sk += sum_slot(smem, 0, w)[i];
+                    sv += sum_slot(smem, 1, w)[i];
                 }
+                const int Ib = i >> 4, ir = i & 15;
+                for (int J = 0; J <= Ib; ++J) mh += q_slot(smem, Ib * (Ib + 1) / 2 + J)[ir];  // row i
+                for (int I = Ib; I < kNB; ++I) cz += q_slot(smem, I * (I + 1) / 2 + Ib)[16 + ir];  // column i
                 const float bi = bs[i];
                 const float ei = GT ? GR::E(Kraw, i) : 1.f;
                 const float db = sk * ei + sv + mh;
@@ -1560,9 +1657,7 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
         new_unit = nnew;
         return u.n > 0;
     };
-    if (job()) {
-        while (job()) {
-        }
+    while (job()) {
     }
 }
 
