@@ -941,6 +941,7 @@ constexpr int PAN_BYTES = 2 * 16 * 20 * 4;
 constexpr int LDS_TOTAL = OFF_PAN + kBW * PAN_BYTES;
 static_assert(LDS_TOTAL - OFF_V >= kC * kD * 2, "V rows fit over the sums and the panels");
 static_assert(PAN_BYTES >= 2048, "a wave's dW and dU panels fit its transpose tiles");
+static_assert(LDS_TOTAL - OFF_V >= 16 * 1024, "the coupling's tmp tiles fit over the V rows");
 static_assert(KB <= TL::BYTES, "dv and dk are staged as bf16 rows over T and XR");
 static_assert(OFF_V % 16 == 0 && OFF_PAN % 16 == 0, "16-byte aligned regions");
 static_assert(LDS_TOTAL <= 160 * 1024, "C = 128 backward LDS plan exceeds 160 KiB");
@@ -1178,6 +1179,57 @@ __device__ __attribute__((always_inline)) void x_row(const Params& p, const RowF
     }
 }
 
+// a6 for block size S = 32 or 64 on all eight waves (coupling_level runs a pair's column tile on
+// one wave, which at S = 64 makes one wave's chain 104 fp32 MFMAs long).  Two passes, a barrier
+// between them: tmp = L10 X00 tile by tile into `tmpb` (one 16-byte chunk per lane and tile),
+// then X10 = -X11 tmp written over L10, which no wave reads any more.  Pass A's tile (mr, nc)
+// costs TS - nc steps of four MFMAs and pass B's mr + 1, so at S = 64 each wave takes two tiles
+// whose costs add up to 5 in each pass, and at S = 32 one tile.  Every tile's sum runs in
+// coupling_level's order, so T is bit-identical to it.
+template <int S>
+__device__ __attribute__((always_inline)) void coupling8(float* Ts, float* tmpb, int wave, int lane, int lr, int lg)
+{
+    constexpr int TS = S / 16;
+    constexpr int PER = TS * TS * (kC / (2 * S)) / kBW;  // tiles per wave and pass
+    static_assert((S == 64 && PER == 2) || (S == 32 && PER == 1), "tile dealing below");
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {  // pass A: tmp(mr, nc) = sum_{kt >= nc} L10(mr, kt) X00(kt, nc)
+        const int pr = S == 64 ? 0 : wave >> 2;
+        const int mr = S == 64 ? wave >> 1 : (wave >> 1) & 1;
+        const int nc = S == 64 ? (t == 0 ? (wave & 1) : 3 - (wave & 1)) : wave & 1;
+        const int base = 2 * S * pr;
+        f32x4 acc = zero4();
+        for (int kt = nc; kt < TS; ++kt) {  // uniform
+            float bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bq[q] = Ts[TL::off(base + 16 * kt + 4 * lg + q, base + 16 * nc + lr)];
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(base + S + 16 * mr + lr, base + 16 * kt + 4 * lg));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bq[q], acc, 0, 0, 0);
+        }
+        *reinterpret_cast<f32x4*>(tmpb + ((pr * TS + mr) * TS + nc) * 256 + 4 * lane) = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {  // pass B: X10(mr, nc) = -sum_{kt <= mr} X11(mr, kt) tmp(kt, nc)
+        const int pr = S == 64 ? 0 : wave >> 2;
+        const int nc = S == 64 ? wave >> 1 : (wave >> 1) & 1;
+        const int mr = S == 64 ? (t == 0 ? (wave & 1) : 3 - (wave & 1)) : wave & 1;
+        const int base = 2 * S * pr;
+        f32x4 acc = zero4();
+        for (int kt = 0; kt <= mr; ++kt) {  // uniform
+            const f32x4 av =
+                *reinterpret_cast<const f32x4*>(Ts + TL::off(base + S + 16 * mr + lr, base + S + 16 * kt + 4 * lg));
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(tmpb + ((pr * TS + kt) * TS + nc) * 256 + 4 * lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[TL::off(base + S + 16 * mr + 4 * lg + r, base + 16 * nc + lr)] = -acc[r];
+    }
+    __syncthreads();
+}
+
 // Rows [0, n) of C staged bf16 rows (KROW elements) at `src` to a [tokens, heads, 128] tensor.
 __device__ __attribute__((always_inline)) void store_rows(const unsigned char* src, __bf16* out, int64_t tok0, int n, int heads, int head,
                                   int tid)
@@ -1347,10 +1399,10 @@ __global__ __launch_bounds__(kBT, 2) void wy_backward128_kernel(Params p)
                 xs(std::false_type{});
         }
         __syncthreads();
-        // ---- coupling levels on waves 0-3
+        // ---- coupling levels: 16 rows on waves 0-3, 32 and 64 rows on all eight (tmp over the V rows)
         coupling_level<kC, 16, TL>(Ts, tid);
-        coupling_level<kC, 32, TL>(Ts, tid);
-        coupling_level<kC, 64, TL>(Ts, tid);
+        coupling8<32>(Ts, reinterpret_cast<float*>(smem + OFF_V), wave, lane, lr, lg);
+        coupling8<64>(Ts, reinterpret_cast<float*>(smem + OFF_V), wave, lane, lr, lg);
 
         // ---- Y = X T^T, lower tiles, in registers; then over X as one 16-byte chunk per lane
         f32x4 yt[8];
