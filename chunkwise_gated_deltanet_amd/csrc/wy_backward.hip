@@ -77,6 +77,7 @@ struct BG {
     static_assert(OFF_X == OFF_H + TB && 2 * TB >= KB, "dk is staged as bf16 rows over H and X");
     static_assert(4 * PSTR >= 16 * 20, "a Y / M wave's row-sum slots hold its 16 x 20 transpose tile");
     static_assert(LDS_TOTAL <= 160 * 1024, "backward LDS plan exceeds 160 KiB");
+    static_assert(C != 64 || 2 * ZW * 4 * PSTR >= 4 * 256, "the 32-row coupling's tmp tiles fit over the row partials");
     using TL = TLayout<C>;
     using GR = GateRow<KROW, 2>;
 };
@@ -466,6 +467,48 @@ __device__ void form_a_h(const unsigned char* Kraw, float* Ts, float* Hs, const 
     }
 }
 
+// a6 at S = 32 for C = 64 on waves 0-3 (coupling_level runs it on two waves, one of them with 28
+// dependent fp32 MFMAs), in two passes: tmp = L10 X00 tile by tile into `tmpb` (one 16-byte
+// chunk per lane and tile), barrier, X10 = -X11 tmp over L10, which no wave reads any more.
+// Each wave takes one tile of each pass, three MFMA steps in all; every sum runs in
+// coupling_level's order (its products with the zero tiles above X00's diagonal skipped), so T
+// is the same.
+template <int C>
+__device__ __attribute__((always_inline)) void coupling32_4w(float* Ts, float* tmpb, int wave, int lane, int lr,
+                                                             int lg)
+{
+    using TL = typename BG<C>::TL;
+    static_assert(C == 64, "one 32-row pair");
+    constexpr int S = 32, TS = 2;
+    if (wave < 4) {  // uniform; pass A: tmp(mr, nc) = sum_{kt >= nc} L10(mr, kt) X00(kt, nc)
+        const int mr = wave >> 1, nc = wave & 1;
+        f32x4 acc = zero4();
+        for (int kt = nc; kt < TS; ++kt) {
+            float bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bq[q] = Ts[TL::off(16 * kt + 4 * lg + q, 16 * nc + lr)];
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(S + 16 * mr + lr, 16 * kt + 4 * lg));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bq[q], acc, 0, 0, 0);
+        }
+        *reinterpret_cast<f32x4*>(tmpb + (mr * TS + nc) * 256 + 4 * lane) = acc;
+    }
+    __syncthreads();
+    if (wave < 4) {  // uniform; pass B: X10(mr, nc) = -sum_{kt <= mr} X11(mr, kt) tmp(kt, nc)
+        const int nc = wave >> 1, mr = wave & 1;
+        f32x4 acc = zero4();
+        for (int kt = 0; kt <= mr; ++kt) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(S + 16 * mr + lr, S + 16 * kt + 4 * lg));
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(tmpb + (kt * TS + nc) * 256 + 4 * lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[TL::off(S + 16 * mr + 4 * lg + r, 16 * nc + lr)] = -acc[r];
+    }
+    __syncthreads();
+}
+
 // Batch rows: the units logical, logical + G, logical + 2 G, ... of one workgroup, walked without
 // a division per step.  logical = slot * H + head and slot = b * cps + c, so a step of G adds
 // G mod H to the head (carrying one slot) and G div H (or one more) slots, split once per
@@ -690,7 +733,7 @@ __global__ __launch_bounds__(BG<C>::BT, 2) void wy_backward_kernel(Params p)
         __syncthreads();
         if (wave >= kYW) in.issue(p, nu.tok0, nu.n, nu.hv, nhv, nnew, tid);  // uniform
         coupling_level<kC, 16, TL>(Ts, tid);
-        if constexpr (kC >= 64) coupling_level<kC, 32, TL>(Ts, tid);
+        if constexpr (kC >= 64) coupling32_4w<kC>(Ts, part, wave, lane, lr, lg);  // tmp over the row partials
         const int zw = wave - kYW;
         const bool last_head = hv == (hk + 1) * r - 1;  // uniform
 
