@@ -143,9 +143,10 @@ def test_wy_backward_batch_walk(C, gpu):
     check(inp, dW, dU, dT, out, f"batch walk C={C}")
 
 
-def test_wy_backward_deterministic(gpu):
+@pytest.mark.parametrize("case", ["packed_gva_mu4_dT", "C128_gva8_mu4_dT"])
+def test_wy_backward_deterministic(case, gpu):
     import torch
-    inp, dW, dU, dT = make_inputs(CASES["packed_gva_mu4_dT"])
+    inp, dW, dU, dT = make_inputs(CASES[case])
     a = run_bwd(inp, dW, dU, dT, gpu)
     b = run_bwd(inp, dW, dU, dT, gpu)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
