@@ -884,16 +884,76 @@ __device__ void wu_f32(unsigned char* Kraw, float* Ts, const float* bs, PF& pf, 
 // with L_ii^{-1} the inverted diagonal blocks (a5) and A_ij the sub-diagonal blocks of A as
 // form_a left them; the coupling levels that would fill in T are never run.  Wave w owns the 32
 // columns 32 w .. 32 w + 31 of R and X (two column tiles) for every row block, so the waves never
-// wait for each other.  Both products run on fp32 MFMA 16x16x4: the accumulator of X_j (element r
-// of lane 16 g + c is X_j[4 g + r][c]) is exactly the B operand the later products take, so X
-// stays in registers; R_i is read from LDS in that layout and X_i written back over it (same
-// wave, same columns), as bf16 (or fp32) for the row store.
+// wait for each other.  The fp32 instance runs both products on fp32 MFMA 16x16x4: the
+// accumulator of X_j (element r of lane 16 g + c is X_j[4 g + r][c]) is exactly the B operand the
+// later products take, so X stays in registers; the bf16 instance splits the same operands into
+// bf16 hi / lo halves for the 16x16x16 bf16 MFMA.  R_i is read from LDS in that layout and X_i
+// written back over it (same wave, same columns), as bf16 (or fp32) for the row store.
 template <int C, int DT, int KROW, class TL>
 __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs, int tid)
 {
     constexpr int NB = C / 16;
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
+    if constexpr (DT == 0) {
+        // bf16 right-hand side and output: the sums A_ij X_j run as three bf16 MFMA 16x16x16
+        // products of the hi / lo halves of A_ij and X_j (hi*hi + hi*lo + lo*hi; the dropped
+        // lo*lo term is below 2^-17 of the product), a third of the fp32 16x16x4 MFMA time.  The
+        // 16x16x16 operands take the same lane layout as the 16x16x4 steps (lane 16 g + c: row or
+        // column c, k = 4 g .. 4 g + 3), so X_j's accumulator is split in place once and kept
+        // as its two bf16 halves.  The product with L_ii^{-1} stays on fp32 MFMA, so where A is
+        // the identity X = diag(beta) R is rounded once.
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        auto split = [](const f32x4& x, i16x4& h, i16x4& l) {
+            bf16x4 hb, lb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hb[e] = static_cast<__bf16>(x[e]);
+                lb[e] = static_cast<__bf16>(x[e] - static_cast<float>(hb[e]));
+            }
+            h = __builtin_bit_cast(i16x4, hb);
+            l = __builtin_bit_cast(i16x4, lb);
+        };
+        i16x4 xh[NB][2], xl[NB][2];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int j = 0; j < i; ++j) {
+                i16x4 ah, al;
+                split(*reinterpret_cast<const f32x4*>(Ts + TL::off(16 * i + lr, 16 * j + 4 * lg)), ah, al);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, xh[j][c], acc[c], 0, 0, 0);
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, xl[j][c], acc[c], 0, 0, 0);
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, xh[j][c], acc[c], 0, 0, 0);
+                }
+            }
+            const f32x4 inv = *reinterpret_cast<const f32x4*>(Ts + TL::off(16 * i + lr, 16 * i + 4 * lg));
+            const f32x4 bet = *reinterpret_cast<const f32x4*>(bs + 16 * i + 4 * lg);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int col = 32 * wave + 16 * c + lr;
+                f32x4 y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * i + 4 * lg + r;
+                    y[r] = bet[r] * static_cast<float>(reinterpret_cast<const __bf16*>(Rraw)[row * KROW + col]) -
+                           acc[c][r];
+                }
+                f32x4 x = zero4();
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x = __builtin_amdgcn_mfma_f32_16x16x4f32(inv[q], y[q], x, 0, 0, 0);
+                split(x, xh[i][c], xl[i][c]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * i + 4 * lg + r;
+                    reinterpret_cast<__bf16*>(Rraw)[row * KROW + col] = static_cast<__bf16>(x[r]);
+                }
+            }
+        }
+        return;
+    }
     f32x4 X[NB][2];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -917,12 +977,7 @@ __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * i + 4 * lg + r;
-                float rv;
-                if constexpr (DT == 0)
-                    rv = static_cast<float>(reinterpret_cast<const __bf16*>(Rraw)[row * KROW + col]);
-                else
-                    rv = reinterpret_cast<const float*>(Rraw)[row * KROW + col];
-                y[r] = bet[r] * rv - acc[c][r];
+                y[r] = bet[r] * reinterpret_cast<const float*>(Rraw)[row * KROW + col] - acc[c][r];
             }
             f32x4 x = zero4();
 #pragma unroll
@@ -931,10 +986,7 @@ __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * i + 4 * lg + r;
-                if constexpr (DT == 0)
-                    reinterpret_cast<__bf16*>(Rraw)[row * KROW + col] = static_cast<__bf16>(x[r]);
-                else
-                    reinterpret_cast<float*>(Rraw)[row * KROW + col] = x[r];
+                reinterpret_cast<float*>(Rraw)[row * KROW + col] = x[r];
             }
         }
     }
