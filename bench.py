@@ -221,8 +221,8 @@ def cpu_baseline_fwd(inp, seconds=10.0):
 
 # Extra workloads timed after the headline (each with its own roofline): the other C = 64
 # configurations, the chunk-size study on B=4 T=4096 H=32, 1024 short packed sequences (the
-# packed-sequence work map under load), and on the headline's shape the backward at C = 64 and
-# 32 and the chunk recurrence in its sequence-parallel form.
+# packed-sequence work map under load), and on the headline's shape the backward at C = 64, 32
+# and 128 and the chunk recurrence in its sequence-parallel form.
 DEFAULT_EXTRAS = "3:32,3:64,3:128,5:64,6:64,bwd/2:64,bwd/2:32,bwd/2:128,fwd/2:64/auto"
 
 
