@@ -992,6 +992,55 @@ __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs,
     }
 }
 
+// a6 for T alone (kkt_solve) at S = 32 (C = 64) and S = 64 (C = 128).  coupling_level gives a
+// pair's column tile to one wave, and that wave's chain (28 and 104 fp32 MFMAs) is the unit's
+// longest.  Here every wave takes tiles of both passes: tmp = L10 X00 into `tmpb` (K's region,
+// which T alone no longer reads; one 16-byte chunk per lane and tile), a barrier, then
+// X10 = -X11 tmp over L10.  Pass A's tile (mr, nc) costs TS - nc steps of four MFMAs and pass B's
+// mr + 1: at S = 64 wave w takes row mr = w of pass A and column nc = w of pass B (ten steps
+// each), at S = 32 tile (w >> 1, w & 1) of A and (w & 1, w >> 1) of B (three in all).  Each sum
+// keeps coupling_level's order (the zero tiles above X00's diagonal skipped), so T is the same.
+template <int C, int S, class TL>
+__device__ void coupling_2pass(float* Ts, float* tmpb, int tid)
+{
+    constexpr int TS = S / 16;
+    constexpr int PER = TS * TS / kWaves;  // tiles per wave and pass: 1 at S = 32, 4 at S = 64
+    static_assert(C == 2 * S && kWaves == 4 && (S == 32 || S == 64), "one pair of blocks, four waves");
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {  // pass A: tmp(mr, nc) = sum_{kt >= nc} L10(mr, kt) X00(kt, nc)
+        const int mr = S == 64 ? wave : wave >> 1;
+        const int nc = S == 64 ? t : wave & 1;
+        f32x4 acc = zero4();
+        for (int kt = nc; kt < TS; ++kt) {  // uniform
+            float bq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bq[q] = Ts[TL::off(16 * kt + 4 * lg + q, 16 * nc + lr)];
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(S + 16 * mr + lr, 16 * kt + 4 * lg));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bq[q], acc, 0, 0, 0);
+        }
+        *reinterpret_cast<f32x4*>(tmpb + (mr * TS + nc) * 256 + 4 * lane) = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {  // pass B: X10(mr, nc) = -sum_{kt <= mr} X11(mr, kt) tmp(kt, nc)
+        const int nc = S == 64 ? wave : wave >> 1;
+        const int mr = S == 64 ? t : wave & 1;
+        f32x4 acc = zero4();
+        for (int kt = 0; kt <= mr; ++kt) {  // uniform
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(S + 16 * mr + lr, S + 16 * kt + 4 * lg));
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(tmpb + (kt * TS + nc) * 256 + 4 * lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ts[TL::off(S + 16 * mr + 4 * lg + r, 16 * nc + lr)] = -acc[r];
+    }
+    __syncthreads();
+}
+
 // One unit, from committing its prefetched K to storing its outputs; its own V and the next
 // unit's K are issued on the way.  Returns the next unit.
 template <int C, int DT, int M, class PF>
@@ -1057,8 +1106,18 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
         return nxt;
     }
     if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
-    if constexpr (C >= 64) coupling_level<C, 32, TL>(Ts, tid);
-    if constexpr (C >= 128) coupling_level<C, 64, TL>(Ts, tid);
+    // T alone: K is no longer read, so the level whose single-wave chain is the longest runs on
+    // all four waves in two passes with its tmp tiles over K
+    if constexpr (!WU && C == 64) {
+        coupling_2pass<C, 32, TL>(Ts, reinterpret_cast<float*>(Kraw), tid);
+    } else if constexpr (C >= 64) {
+        coupling_level<C, 32, TL>(Ts, tid);
+    }
+    if constexpr (!WU && C == 128) {
+        coupling_2pass<C, 64, TL>(Ts, reinterpret_cast<float*>(Kraw), tid);
+    } else if constexpr (C >= 128) {
+        coupling_level<C, 64, TL>(Ts, tid);
+    }
     if (chain_first) __builtin_amdgcn_s_setprio(0);
     store_t<C, TL, DT == 0 && WU, (M & kModeT) != 0>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
