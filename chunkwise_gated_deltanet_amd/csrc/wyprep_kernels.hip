@@ -1000,7 +1000,7 @@ __device__ void solve_rhs(unsigned char* Rraw, const float* Ts, const float* bs,
 // mr + 1: at S = 64 wave w takes row mr = w of pass A and column nc = w of pass B (ten steps
 // each), at S = 32 tile (w >> 1, w & 1) of A and (w & 1, w >> 1) of B (three in all).  Each sum
 // keeps coupling_level's order (the zero tiles above X00's diagonal skipped), so T is the same.
-template <int C, int S, class TL>
+template <int C, int S, class TL, bool INPLACE>
 __device__ void coupling_2pass(float* Ts, float* tmpb, int tid)
 {
     constexpr int TS = S / 16;
@@ -1008,35 +1008,64 @@ __device__ void coupling_2pass(float* Ts, float* tmpb, int tid)
     static_assert(C == 2 * S && kWaves == 4 && (S == 32 || S == 64), "one pair of blocks, four waves");
     const int lane = tid & 63, wave = uniform(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
+    f32x4 acc[PER];
 #pragma unroll
     for (int t = 0; t < PER; ++t) {  // pass A: tmp(mr, nc) = sum_{kt >= nc} L10(mr, kt) X00(kt, nc)
         const int mr = S == 64 ? wave : wave >> 1;
         const int nc = S == 64 ? t : wave & 1;
-        f32x4 acc = zero4();
+        acc[t] = zero4();
         for (int kt = nc; kt < TS; ++kt) {  // uniform
             float bq[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) bq[q] = Ts[TL::off(16 * kt + 4 * lg + q, 16 * nc + lr)];
             const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(S + 16 * mr + lr, 16 * kt + 4 * lg));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bq[q], acc, 0, 0, 0);
+            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bq[q], acc[t], 0, 0, 0);
         }
-        *reinterpret_cast<f32x4*>(tmpb + (mr * TS + nc) * 256 + 4 * lane) = acc;
+        if constexpr (!INPLACE) *reinterpret_cast<f32x4*>(tmpb + (mr * TS + nc) * 256 + 4 * lane) = acc[t];
+    }
+    if constexpr (INPLACE) {  // tmp over L10, once every wave has read L10 for the last time
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            const int mr = S == 64 ? wave : wave >> 1;
+            const int nc = S == 64 ? t : wave & 1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ts[TL::off(S + 16 * mr + 4 * lg + r, 16 * nc + lr)] = acc[t][r];
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < PER; ++t) {  // pass B: X10(mr, nc) = -sum_{kt <= mr} X11(mr, kt) tmp(kt, nc)
         const int nc = S == 64 ? wave : wave >> 1;
         const int mr = S == 64 ? t : wave & 1;
-        f32x4 acc = zero4();
+        acc[t] = zero4();
         for (int kt = 0; kt <= mr; ++kt) {  // uniform
             const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + TL::off(S + 16 * mr + lr, S + 16 * kt + 4 * lg));
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(tmpb + (kt * TS + nc) * 256 + 4 * lane);
+            f32x4 bv;
+            if constexpr (INPLACE) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+                for (int q = 0; q < 4; ++q) bv[q] = Ts[TL::off(S + 16 * kt + 4 * lg + q, 16 * nc + lr)];
+            } else {
+                bv = *reinterpret_cast<const f32x4*>(tmpb + (kt * TS + nc) * 256 + 4 * lane);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[t], 0, 0, 0);
         }
+        if constexpr (!INPLACE) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Ts[TL::off(S + 16 * mr + 4 * lg + r, 16 * nc + lr)] = -acc[r];
+            for (int r = 0; r < 4; ++r) Ts[TL::off(S + 16 * mr + 4 * lg + r, 16 * nc + lr)] = -acc[t][r];
+        }
+    }
+    if constexpr (INPLACE) {  // X10 over tmp, once every wave has read tmp for the last time
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            const int nc = S == 64 ? wave : wave >> 1;
+            const int mr = S == 64 ? t : wave & 1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ts[TL::off(S + 16 * mr + 4 * lg + r, 16 * nc + lr)] = -acc[t][r];
+        }
     }
     __syncthreads();
 }
@@ -1106,18 +1135,11 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
         return nxt;
     }
     if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
-    // T alone: K is no longer read, so the level whose single-wave chain is the longest runs on
-    // all four waves in two passes with its tmp tiles over K
-    if constexpr (!WU && C == 64) {
-        coupling_2pass<C, 32, TL>(Ts, reinterpret_cast<float*>(Kraw), tid);
-    } else if constexpr (C >= 64) {
-        coupling_level<C, 32, TL>(Ts, tid);
-    }
-    if constexpr (!WU && C == 128) {
-        coupling_2pass<C, 64, TL>(Ts, reinterpret_cast<float*>(Kraw), tid);
-    } else if constexpr (C >= 128) {
-        coupling_level<C, 64, TL>(Ts, tid);
-    }
+    // The level whose single-wave chain is the longest runs on all four waves in two passes: for
+    // T alone with its tmp tiles over K (no longer read), with W and U in place over L10
+    if constexpr (C == 64) coupling_2pass<C, 32, TL, WU>(Ts, reinterpret_cast<float*>(Kraw), tid);
+    if constexpr (C >= 128) coupling_level<C, 32, TL>(Ts, tid);
+    if constexpr (C == 128) coupling_2pass<C, 64, TL, WU>(Ts, reinterpret_cast<float*>(Kraw), tid);
     if (chain_first) __builtin_amdgcn_s_setprio(0);
     store_t<C, TL, DT == 0 && WU, (M & kModeT) != 0>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
