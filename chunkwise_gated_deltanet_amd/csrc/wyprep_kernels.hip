@@ -1134,12 +1134,27 @@ __device__ __forceinline__ Unit run_unit(const Params& p, unsigned char* smem, P
         __syncthreads();  // LDS is rewritten by the next unit
         return nxt;
     }
-    if constexpr (C >= 32) coupling_level<C, 16, TL>(Ts, tid);
+    // Level s writes only rows s and past (the X10 blocks).  Rows at or past n are never stored,
+    // and the stored rows of T, W and U depend on T's rows below n alone, so a unit of n <= s
+    // rows (a sequence's last chunk, short sequences) skips level s and the ones above it.  Not
+    // at C = 64 with W and U: there it gained 5% on short sequences, but the check alone moved
+    // the code of the full-chunk case and cost 1.5% on it.
+    constexpr bool kSkip = !(C == 64 && WU);
+    const int nrows = kSkip ? __builtin_amdgcn_readfirstlane(cur.n) : C;
+    if constexpr (C >= 32) {
+        if (nrows > 16) coupling_level<C, 16, TL>(Ts, tid);  // uniform
+    }
     // The level whose single-wave chain is the longest runs on all four waves in two passes: for
     // T alone with its tmp tiles over K (no longer read), with W and U in place over L10
-    if constexpr (C == 64) coupling_2pass<C, 32, TL, WU>(Ts, reinterpret_cast<float*>(Kraw), tid);
-    if constexpr (C >= 128) coupling_level<C, 32, TL>(Ts, tid);
-    if constexpr (C == 128) coupling_2pass<C, 64, TL, WU>(Ts, reinterpret_cast<float*>(Kraw), tid);
+    if constexpr (C == 64) {
+        if (nrows > 32) coupling_2pass<C, 32, TL, WU>(Ts, reinterpret_cast<float*>(Kraw), tid);  // uniform
+    }
+    if constexpr (C >= 128) {
+        if (nrows > 32) coupling_level<C, 32, TL>(Ts, tid);  // uniform
+    }
+    if constexpr (C == 128) {
+        if (nrows > 64) coupling_2pass<C, 64, TL, WU>(Ts, reinterpret_cast<float*>(Kraw), tid);  // uniform
+    }
     if (chain_first) __builtin_amdgcn_s_setprio(0);
     store_t<C, TL, DT == 0 && WU, (M & kModeT) != 0>(Ts, bs, p.T, cur, p.hv, tid);
     if constexpr (WU) {
